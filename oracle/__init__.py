@@ -1,0 +1,303 @@
+"""CPU oracle for the HGRNBit layer forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package. The product path (the HIP
+library and its binding) never does; the two share no code.
+
+What it computes, and where each step comes from (web pages about the
+MatMul-free LM project):
+
+* [R1] "MatMul-Free LLM 深度分析报告" (nightvoyager.top), section "核心价值提炼":
+  table "创新之处" -- ternary ``weight_quant`` (round to nearest {-1,0,+1}),
+  the HGRN recurrence h_t = gate_t * h_{t-1} + x_t (elementwise); list
+  "可复用的模式与技巧" -- RMSNorm fused with INT8 activation quantisation,
+  RMSNorm fused with a Swish gate.
+* [R3] "MatMul-Free LM：把矩陣乘法從語言模型裡拿掉之後，剩下什麼" (hysenlabs.com),
+  section "HGRNBitBlock 的結構": a block is a token mixer with four
+  FusedBitLinear projections i/f/g/o (each with an eps = 1e-8 RMSNorm) and a
+  g_norm RMSNorm-Swish gate, followed by an MLP of gate_proj (2x inner
+  outputs), a SiLU and down_proj.
+* [R4] mooersco.com article, section 4.1: a ternary matrix-vector product is a
+  conditional add / subtract per weight.
+
+Where the pages are silent the stated problem fixes the reading: per-token
+absmax int8 scale (127 / amax), per-tensor mean-|W| weight scale, forget gate
+f = sigmoid(f_proj), input x~ = (1 - f) * SiLU(i_proj), SiLU-gated MLP over the
+two halves of gate_proj. Further readings (the 1e-5 floors, round half to
+even, g_norm's eps, the residual wiring, which half of gate_proj is gated)
+are listed in the project's design notes.
+
+Precision: every step is binary64 except the two quantisers, which decide
+integers and therefore run in the kernel's precision (binary32 operations,
+binary64 sum of squares); their input vector is rounded to binary32 first.
+The ternary contraction is exact integer arithmetic.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmmf_oracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_quant_rows.argtypes = [P, I64, I64, P, ctypes.c_float, P, P, P]
+    lib.oracle_ternarize.argtypes = [P, I64, I64, P, P]
+    lib.oracle_pack.argtypes = [P, I64, I64, P]
+    lib.oracle_unpack.argtypes = [P, I64, I64, P]
+    lib.oracle_ternary_matmul.argtypes = [P, P, I64, I64, I64, P]
+    lib.oracle_hgrn_scan.argtypes = [P, P, P, I64, I64, I64, P]
+    for fn in (lib.oracle_quant_rows, lib.oracle_ternarize, lib.oracle_pack, lib.oracle_unpack,
+               lib.oracle_ternary_matmul, lib.oracle_hgrn_scan, lib.oracle_num_threads):
+        fn.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
+
+
+# ---------------------------------------------------------------------------
+# Quantisers (binary32 decisions)
+# ---------------------------------------------------------------------------
+
+def quantize(v: np.ndarray, gain: Optional[np.ndarray] = None, eps: float = 1e-8):
+    """RMSNorm (eps inside the square root) + per-row absmax int8 codes.
+
+    [R1] fused RMSNorm + INT8 quantisation; [R3] eps = 1e-8. ``v`` is rounded
+    to binary32 first (the kernel's precision). Returns (q int8 [m,k],
+    s float32 [m], sumq int32 [m]) with q ~= RMSNorm(v)*gain*s.
+    """
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    k = v.shape[-1]
+    m = v.size // k
+    g = None if gain is None else np.ascontiguousarray(np.asarray(gain, dtype=np.float32))
+    if g is not None and g.shape != (k,):
+        raise ValueError("gain must have shape (k,)")
+    q = np.empty(v.shape, dtype=np.int8)
+    s = np.empty(v.shape[:-1], dtype=np.float32)
+    sq = np.empty(v.shape[:-1], dtype=np.int32)
+    rc = _load().oracle_quant_rows(_ptr(v), m, k, _ptr(g), ctypes.c_float(eps), _ptr(q), _ptr(s), _ptr(sq))
+    if rc != 0:
+        raise ValueError("oracle_quant_rows failed")
+    return q, s, sq
+
+
+def ternarize(w: np.ndarray):
+    """Round-to-nearest ternary codes with a per-tensor mean-|W| scale ([R1] weight_quant).
+
+    Returns (t int8 [n,k] in {-1,0,1}, mu float32).
+    """
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.float32))
+    n, k = w.shape
+    t = np.empty((n, k), dtype=np.int8)
+    mu = np.zeros(1, dtype=np.float32)
+    if _load().oracle_ternarize(_ptr(w), n, k, _ptr(t), _ptr(mu)) != 0:
+        raise ValueError("oracle_ternarize failed")
+    return t, np.float32(mu[0])
+
+
+def weight_scale(mu) -> np.float32:
+    """sw = 1 / max(mu, 1e-5) in binary32: ternary t approximates W * sw."""
+    return np.float32(np.float32(1.0) / np.maximum(np.float32(mu), np.float32(1e-5)))
+
+
+def pack(t: np.ndarray) -> np.ndarray:
+    """2-bit packing of codes c = t + 1, 16 per uint32 word ([R4] section 5.1)."""
+    t = np.ascontiguousarray(np.asarray(t, dtype=np.int8))
+    n, k = t.shape
+    if k % 16:
+        raise ValueError("k must be a multiple of 16")
+    words = np.empty((n, k // 16), dtype=np.uint32)
+    if _load().oracle_pack(_ptr(t), n, k, _ptr(words)) != 0:
+        raise ValueError("oracle_pack failed (k % 16 or a code outside {-1,0,1})")
+    return words
+
+
+def unpack(words: np.ndarray, k: int) -> np.ndarray:
+    words = np.ascontiguousarray(np.asarray(words, dtype=np.uint32))
+    n = words.shape[0]
+    t = np.empty((n, k), dtype=np.int8)
+    if _load().oracle_unpack(_ptr(words), n, k, _ptr(t)) != 0:
+        raise ValueError("oracle_unpack failed")
+    return t
+
+
+def ternary_matmul(q: np.ndarray, t: np.ndarray) -> np.ndarray:
+    """Exact acc[i, o] = sum_k q[i, k] * t[o, k] ([R4] section 4.1), int32."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.int8))
+    t = np.ascontiguousarray(np.asarray(t, dtype=np.int8))
+    k = q.shape[-1]
+    m = q.size // k
+    n = t.shape[0]
+    if t.shape[1] != k:
+        raise ValueError("inner dimensions differ")
+    acc = np.empty(q.shape[:-1] + (n,), dtype=np.int32)
+    rc = _load().oracle_ternary_matmul(_ptr(q), _ptr(t), m, n, k, _ptr(acc))
+    if rc != 0:
+        raise ValueError("oracle_ternary_matmul failed (%d)" % rc)
+    return acc
+
+
+def dequant(acc: np.ndarray, s: np.ndarray, mu) -> np.ndarray:
+    """acc / (s * sw) in binary64: the float contraction of the dequantised operands."""
+    sw = np.float64(weight_scale(mu))
+    return np.asarray(acc, dtype=np.float64) / (np.asarray(s, dtype=np.float64)[..., None] * sw)
+
+
+# ---------------------------------------------------------------------------
+# binary64 elementwise pieces
+# ---------------------------------------------------------------------------
+
+def sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z * sigmoid(z)
+
+
+def bitlinear(x: np.ndarray, t: np.ndarray, mu, gain=None, eps: float = 1e-8):
+    """FusedBitLinear: RMSNorm + int8 quant of x, exact ternary contraction, dequant; no bias."""
+    q, s, sq = quantize(x, gain, eps)
+    acc = ternary_matmul(q, t)
+    return dict(y=dequant(acc, s, mu), q=q, s=s, sumq=sq, acc=acc)
+
+
+def mixer_gates(i_hat, f_hat):
+    """f = sigmoid(f_proj); x~ = (1 - f) * SiLU(i_proj)."""
+    f = sigmoid(f_hat)
+    return f, (1.0 - f) * silu(i_hat)
+
+
+def hgrn_scan(x: np.ndarray, f: np.ndarray, h0: Optional[np.ndarray] = None) -> np.ndarray:
+    """h_t = f_t * h_{t-1} + x_t per (batch, channel), binary64, sequential ([R1])."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    f = np.ascontiguousarray(np.asarray(f, dtype=np.float64))
+    if x.shape != f.shape or x.ndim != 3:
+        raise ValueError("x and f must both be [b, t, d]")
+    b, t, d = x.shape
+    h0a = None if h0 is None else np.ascontiguousarray(np.asarray(h0, dtype=np.float64).reshape(b, d))
+    h = np.empty_like(x)
+    if _load().oracle_hgrn_scan(_ptr(x), _ptr(f), _ptr(h0a), b, t, d, _ptr(h)) != 0:
+        raise ValueError("oracle_hgrn_scan failed")
+    return h
+
+
+def gnorm_swish(h, g, weight=None, eps: float = 1e-8):
+    """g_norm: RMSNorm(h) * weight, gated by Swish(g) ([R1] RMSNorm + Swish gate)."""
+    h = np.asarray(h, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + np.float64(np.float32(eps)))
+    u = h * r
+    if weight is not None:
+        u = u * np.asarray(weight, dtype=np.float64)
+    return u * silu(g)
+
+
+# ---------------------------------------------------------------------------
+# Layer
+# ---------------------------------------------------------------------------
+
+@dataclass
+class TernaryLinear:
+    """One FusedBitLinear: ternary codes t [n,k], their scale mu, the RMSNorm gain."""
+    t: np.ndarray
+    mu: np.float32
+    gain: Optional[np.ndarray] = None
+
+    @classmethod
+    def from_latent(cls, w: np.ndarray, gain: Optional[np.ndarray] = None) -> "TernaryLinear":
+        t, mu = ternarize(w)
+        return cls(t=t, mu=mu, gain=None if gain is None else np.asarray(gain, np.float32))
+
+    def __call__(self, v, eps):
+        return bitlinear(v, self.t, self.mu, self.gain, eps)
+
+
+@dataclass
+class Layer:
+    """HGRNBit block weights ([R3] section "HGRNBitBlock 的結構")."""
+    i: TernaryLinear
+    f: TernaryLinear
+    g: TernaryLinear
+    o: TernaryLinear
+    gate: TernaryLinear          # [2*inner, d]; rows [0, inner) are the SiLU branch
+    down: TernaryLinear          # [d, inner]
+    g_norm_w: Optional[np.ndarray] = None
+    eps: float = 1e-8
+
+    @property
+    def d(self) -> int:
+        return self.i.t.shape[1]
+
+    @property
+    def inner(self) -> int:
+        return self.down.t.shape[1]
+
+
+def layer_forward(L: Layer, x: np.ndarray, h0: Optional[np.ndarray] = None) -> dict:
+    """HGRNBit block over a [b, t, d] sequence.
+
+    Token mixer: i/f/g FusedBitLinear of x, gates, HGRN recurrence along t,
+    g_norm, o_proj; residual x1 = x + o. MLP: gate_proj of x1, SiLU(first
+    half) * second half, down_proj; out = x1 + mlp. No extra block-level norm:
+    each FusedBitLinear normalises its own input. Returns every stage.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    b, t, d = x.shape
+    eps = L.eps
+    ri, rf, rg = L.i(x, eps), L.f(x, eps), L.g(x, eps)
+    f, xt = mixer_gates(ri["y"], rf["y"])
+    h = hgrn_scan(xt, f, h0)
+    u = gnorm_swish(h, rg["y"], L.g_norm_w, eps)
+    ro = L.o(u, eps)
+    x1 = x + ro["y"]
+    rgate = L.gate(x1, eps)
+    inner = L.inner
+    a, bb = rgate["y"][..., :inner], rgate["y"][..., inner:]
+    z = silu(a) * bb
+    rd = L.down(z, eps)
+    out = x1 + rd["y"]
+    return dict(out=out, h=h, h_last=h[:, -1, :] if t > 0 else None, f=f, xt=xt,
+                i_hat=ri["y"], f_hat=rf["y"], g_hat=rg["y"], u=u, x1=x1, z=z,
+                q_i=ri["q"], s_i=ri["s"], q_f=rf["q"], s_f=rf["s"], q_g=rg["q"], s_g=rg["s"],
+                acc_i=ri["acc"], acc_f=rf["acc"], acc_g=rg["acc"],
+                q_u=ro["q"], s_u=ro["s"], acc_o=ro["acc"],
+                q_x1=rgate["q"], s_x1=rgate["s"], acc_gate=rgate["acc"],
+                q_z=rd["q"], s_z=rd["s"], acc_down=rd["acc"])
+
+
+def layer_decode_step(L: Layer, x: np.ndarray, h: np.ndarray) -> dict:
+    """One token per sequence ([b, d]) with the carried state h [b, d]."""
+    r = layer_forward(L, np.asarray(x, np.float64)[:, None, :], h0=h)
+    return dict(out=r["out"][:, 0, :], h=r["h_last"], stages=r)
+
+
+def make_layer(latent: dict, gains: Optional[dict] = None, eps: float = 1e-8) -> Layer:
+    """Ternarise a dict of latent fp32 weights {i,f,g,o,gate,down} (+ optional gains)."""
+    gains = gains or {}
+    parts = {k: TernaryLinear.from_latent(latent[k], gains.get(k)) for k in ("i", "f", "g", "o", "gate", "down")}
+    return Layer(g_norm_w=gains.get("g_norm"), eps=eps, **parts)
