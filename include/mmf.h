@@ -1,0 +1,215 @@
+/*
+ * mmf.h -- C ABI of the MI355X (gfx950) HGRNBit layer forward library, libmmf.so.
+ *
+ * The operations follow the MatMul-free LM model as described on:
+ *   [R1] "MatMul-Free LLM 深度分析报告" (nightvoyager.top), section "核心价值提炼":
+ *        table "创新之处" (ternary weight_quant, round to nearest {-1,0,+1};
+ *        HGRN recurrence h_t = gate_t * h_{t-1} + x_t with a step-wise and a
+ *        chunked form) and list "可复用的模式与技巧" (RMSNorm fused with INT8
+ *        activation quantisation; RMSNorm fused with a Swish gate).
+ *   [R3] "MatMul-Free LM：把矩陣乘法從語言模型裡拿掉之後，剩下什麼" (hysenlabs.com),
+ *        section "HGRNBitBlock 的結構": i/f/g/o FusedBitLinear projections, each
+ *        with an eps = 1e-8 RMSNorm, a g_norm RMSNorm-Swish gate, an MLP of
+ *        gate_proj (2 x inner outputs), SiLU and down_proj; section
+ *        "什麼情況下這個工具是錯的選擇" (a FusedBitLinear that silently falls back to
+ *        a slow path is a failure mode: here every call reports its path).
+ *   [R4] mooersco.com article, sections 4.1 and 5.1 (ternary product as
+ *        conditional add/subtract; pack low-bit weights into words).
+ * Readings where the pages are silent (stated with the operations below):
+ * per-token absmax int8 scale 127/amax, per-tensor mean-|W| weight scale,
+ * f = sigmoid(f_proj), x~ = (1 - f) * SiLU(i_proj), SiLU(first half of
+ * gate_proj) * second half, plain residual adds, no bias.
+ *
+ * Conventions (all entry points):
+ *  - Every tensor pointer is DEVICE memory owned by the caller; struct
+ *    arguments are host memory read during the call only. The library
+ *    allocates nothing, keeps no state between calls and never synchronises:
+ *    all work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *    Scratch memory comes from the caller's workspace (`ws`, `ws_bytes`,
+ *    256-byte aligned), sized by the matching *_workspace_size call.
+ *  - Layouts are row-major with the last dimension contiguous. Activation
+ *    tensors are [rows][features]; sequences are [b][t][d].
+ *  - Arguments are validated on the host before any HIP call. A failure
+ *    returns a status other than MMF_OK, enqueues nothing and sets the
+ *    thread-local message read by mmf_last_error(). A failed kernel launch
+ *    returns MMF_ERR_HIP; faults during execution surface at the caller's
+ *    next synchronisation.
+ *  - Inputs and outputs must not overlap, except where an entry point says so.
+ *  - mmf_last_path() names the kernel variants the last successful call on
+ *    this thread launched (there is no silent fallback to another path).
+ */
+#ifndef MMF_H
+#define MMF_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MMF_OK = 0,
+    MMF_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad enum value      */
+    MMF_ERR_UNSUPPORTED = 2,   /* valid but not handled (e.g. k % 16 != 0)     */
+    MMF_ERR_WORKSPACE = 3,     /* workspace missing, too small or misaligned   */
+    MMF_ERR_HIP = 4            /* a HIP launch or runtime call failed          */
+} mmf_status;
+
+typedef enum { MMF_F32 = 0, MMF_BF16 = 1 } mmf_dtype;
+
+/* [R1] the recurrence has a step-wise and a chunked implementation. */
+typedef enum {
+    MMF_SCAN_AUTO = 0,         /* library picks from b*d and t                 */
+    MMF_SCAN_RECURRENT = 1,    /* sequential in t per channel: same order as the definition */
+    MMF_SCAN_CHUNK = 2         /* t split in chunks, carries composed as (a,b) pairs */
+} mmf_scan_mode;
+
+/*
+ * One packed ternary weight ([R1] weight_quant; [R4] section 5.1 packing).
+ *  packed : [n][k/16] uint32. Word w of row r holds the codes c = t + 1 in
+ *           {0,1,2} of t[r][16w .. 16w+15]; t[r][16w + 4j + b] sits at bits
+ *           [8b + 2j, 8b + 2j + 2) (j, b in 0..3), so (word >> 2j) & 0x03030303
+ *           is four int8 codes in k order. Code 3 is never written.
+ *  mu     : device scalar, mean |W| of the latent tensor (binary32).
+ *           The weight approximates W ~ t / sw with sw = 1 / max(mu, 1e-5).
+ *  norm_w : [k] gain of this projection's input RMSNorm, or NULL for ones.
+ *  n, k   : output and input features; k % 16 == 0.
+ */
+typedef struct {
+    const uint32_t *packed;
+    const float *mu;
+    const float *norm_w;
+    int32_t n, k;
+} mmf_ternary_weight;
+
+/*
+ * One HGRNBit block ([R3] section "HGRNBitBlock 的結構").
+ *  i, f, g, o : n = k = d.  gate : n = 2*inner, k = d (rows [0, inner) are the
+ *  SiLU branch, rows [inner, 2*inner) the linear branch, one mu for the whole
+ *  tensor).  down : n = d, k = inner.  g_norm_w : [d] or NULL.
+ *  eps : RMSNorm epsilon of every norm in the block (1e-8 on [R3]).
+ */
+typedef struct {
+    mmf_ternary_weight i, f, g, o, gate, down;
+    const float *g_norm_w;
+    int32_t d, inner;
+    float eps;
+} mmf_layer_weights;
+
+/*
+ * Optional stage outputs of a layer call, for validation. Every pointer may be
+ * NULL; non-NULL ones receive the named stage over all m = b*t rows (decode:
+ * m = b). Element types are fixed (fp32 for real-valued stages) whatever the
+ * activation dtype. When the i/f/g gains are the same pointer (or all NULL)
+ * x is quantised once and only codes_x[0] / scale_x[0] are written.
+ */
+typedef struct {
+    int8_t *codes_x[3];  float *scale_x[3];    /* quantised x for i, f, g: [m][d], [m] */
+    int32_t *acc_ifg;                          /* [m][3][d] exact sum t*q for i, f, g   */
+    float *f, *xt, *g;                         /* forget gate, scan input, g_proj output [m][d] */
+    float *h;                                  /* recurrent state after each token [m][d] */
+    float *u;                                  /* g_norm output, o_proj's input [m][d]  */
+    int8_t *codes_u;     float *scale_u;
+    int32_t *acc_o;                            /* [m][d] */
+    float *x1;                                 /* x + o_proj(u) [m][d] */
+    int8_t *codes_x1;    float *scale_x1;
+    int32_t *acc_gate;                         /* [m][2*inner] */
+    float *z;                                  /* SiLU(a) * b [m][inner] */
+    int8_t *codes_z;     float *scale_z;
+    int32_t *acc_down;                         /* [m][d] */
+} mmf_layer_probe;
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char *mmf_last_error(void);
+
+/* Kernel variants launched by the last successful call on this thread. */
+const char *mmf_last_path(void);
+
+/*
+ * mmf_ternary_pack -- ternarise and pack a latent weight ([R1] weight_quant).
+ *  w      : [n][k] fp32 device input.
+ *  packed : [n][k/16] uint32 device output (layout above).
+ *  mu     : device scalar output, (float)(sum |w| / (n*k)) with the sum in
+ *           binary64; then t = clamp(rint(w * sw), -1, 1), rint = round half
+ *           to even, sw = 1 / max(mu, 1e-5) in binary32.
+ *  Deterministic: the reduction order is fixed for given n, k.
+ *  Errors: INVALID_ARG (null, n <= 0, k <= 0), UNSUPPORTED (k % 16),
+ *  WORKSPACE (ws_bytes < mmf_ternary_pack_workspace_size).
+ */
+mmf_status mmf_ternary_pack_workspace_size(int32_t n, int32_t k, size_t *bytes);
+mmf_status mmf_ternary_pack(const float *w, int32_t n, int32_t k, uint32_t *packed, float *mu,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * mmf_bitlinear_fwd -- one FusedBitLinear ([R1] RMSNorm + INT8 quantisation
+ * fused; [R3] eps; [R4] section 4.1 ternary contraction), no bias:
+ *   r     = (float)(1 / sqrt(sum_k x_k^2 / k + eps))   (binary64 inside)
+ *   y_k   = (x_k * r) * norm_w_k                       (binary32)
+ *   s     = 127 / max(max_k |y_k|, 1e-5)
+ *   q_k   = clamp(rint(y_k * s), -128, 127)
+ *   acc_n = sum_k q_k * t[n][k]                        (exact int32)
+ *   out_n = acc_n / (s * sw)
+ *  x : [m][k] in dtype xt.  y : [m][n] in dtype yt.
+ *  codes_out [m][k] int8, scale_out [m] fp32 (s), acc_out [m][n] int32: optional.
+ *  m may be 0 (nothing is launched). Errors: INVALID_ARG, UNSUPPORTED
+ *  (k % 16), WORKSPACE.
+ */
+mmf_status mmf_bitlinear_workspace_size(int64_t m, int32_t k, size_t *bytes);
+mmf_status mmf_bitlinear_fwd(const void *x, mmf_dtype xt, int64_t m, const mmf_ternary_weight *w,
+                             float eps, void *y, mmf_dtype yt, int8_t *codes_out, float *scale_out,
+                             int32_t *acc_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * mmf_hgrn_scan_fwd -- the HGRN recurrence ([R1] table "创新之处"), fp32:
+ *   h[b][t][c] = f[b][t][c] * h[b][t-1][c] + x[b][t][c],   h[b][-1][c] = h0[b][c]
+ *  x, f, h : [b][t][d] fp32; h0 : [b][d] or NULL (zeros); h_last : [b][d] or NULL.
+ *  h may equal x (in place). RECURRENT evaluates in the definition's order;
+ *  CHUNK splits t into chunks, composes chunk carries as (prod f, partial h)
+ *  pairs and re-runs each chunk from its carry (same value up to rounding).
+ *  t may be 0 (h_last = h0). Errors: INVALID_ARG, WORKSPACE.
+ */
+mmf_status mmf_hgrn_scan_workspace_size(int64_t b, int64_t t, int64_t d, mmf_scan_mode mode,
+                                        size_t *bytes);
+mmf_status mmf_hgrn_scan_fwd(const float *x, const float *f, const float *h0, float *h,
+                             float *h_last, int64_t b, int64_t t, int64_t d, mmf_scan_mode mode,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * mmf_layer_fwd -- one HGRNBit block over b sequences of t tokens ([R3]):
+ *   i^, f^, g^ = BitLinear_{i,f,g}(x)
+ *   f  = sigmoid(f^);  x~ = (1 - f) * SiLU(i^)
+ *   h_t = f_t * h_{t-1} + x~_t                      (fp32 state; h_{-1} = h0 or 0)
+ *   u  = RMSNorm(h) * g_norm_w * SiLU(g^)           ([R1] RMSNorm + Swish gate)
+ *   x1 = x + BitLinear_o(u)
+ *   [a | b] = BitLinear_gate(x1);  z = SiLU(a) * b
+ *   out = x1 + BitLinear_down(z)
+ *  x, out : [b][t][d] in dtype act (fp32 or bf16); everything inside is fp32
+ *  (quantised codes int8, contractions exact int32).
+ *  h0 : [b][d] fp32 or NULL; h_last : [b][d] fp32 output or NULL.
+ *  probe : NULL or stage outputs (above).
+ *  Errors: INVALID_ARG (shapes inconsistent with d/inner, null weights),
+ *  UNSUPPORTED (d or inner % 16), WORKSPACE.
+ */
+mmf_status mmf_layer_workspace_size(const mmf_layer_weights *w, int64_t b, int64_t t, size_t *bytes);
+mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype act,
+                         int64_t b, int64_t t, const float *h0, float *h_last, mmf_scan_mode mode,
+                         void *ws, size_t ws_bytes, const mmf_layer_probe *probe, hipStream_t stream);
+
+/*
+ * mmf_layer_decode_step -- the same block for one new token per sequence,
+ * with the recurrent state carried by the caller ([R1] step-wise recurrence):
+ *  x, out : [b][d] in dtype act.  h : [b][d] fp32, read as h_{t-1} and
+ *  overwritten with h_t.  Equivalent to mmf_layer_fwd with t = 1, h0 = h.
+ *  Errors as mmf_layer_fwd (workspace from mmf_layer_workspace_size(w, b, 1)).
+ */
+mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype act,
+                                 int64_t b, float *h, void *ws, size_t ws_bytes,
+                                 const mmf_layer_probe *probe, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMF_H */

@@ -1,5 +1,322 @@
-"""Placeholder; replaced by the ctypes binding of libmmf.so."""
+"""ctypes binding of libmmf.so (the C ABI in include/mmf.h).
+
+Argument marshalling only: tensors are passed as device pointers with the
+current torch stream; every step of the computation runs in the HIP kernels.
+There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmmf.so")
+
+__all__ = [
+    "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
+    "ternary_pack", "bitlinear_fwd", "hgrn_scan_fwd", "layer_fwd", "layer_decode_step",
+    "layer_workspace_size", "last_path", "last_error", "SCAN_MODES",
+]
+
+# Every entry point declared in include/mmf.h.
+SYMBOLS = [
+    "mmf_last_error", "mmf_last_path",
+    "mmf_ternary_pack_workspace_size", "mmf_ternary_pack",
+    "mmf_bitlinear_workspace_size", "mmf_bitlinear_fwd",
+    "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd",
+    "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
+]
+
+SCAN_MODES = {"auto": 0, "recurrent": 1, "chunk": 2}
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP"}
+
+
+class MMFError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), msg))
+        self.status = status
+
+
+P = ctypes.c_void_p
+I32, I64, F32, SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class CTernaryWeight(ctypes.Structure):
+    _fields_ = [("packed", P), ("mu", P), ("norm_w", P), ("n", I32), ("k", I32)]
+
+
+class CLayerWeights(ctypes.Structure):
+    _fields_ = [("i", CTernaryWeight), ("f", CTernaryWeight), ("g", CTernaryWeight),
+                ("o", CTernaryWeight), ("gate", CTernaryWeight), ("down", CTernaryWeight),
+                ("g_norm_w", P), ("d", I32), ("inner", I32), ("eps", F32)]
+
+
+PROBE_FIELDS = ["acc_ifg", "f", "xt", "g", "h", "u", "codes_u", "scale_u", "acc_o", "x1",
+                "codes_x1", "scale_x1", "acc_gate", "z", "codes_z", "scale_z", "acc_down"]
+
+
+class CLayerProbe(ctypes.Structure):
+    _fields_ = [("codes_x", P * 3), ("scale_x", P * 3)] + [(n, P) for n in PROBE_FIELDS]
+
+
+_lib = None
 
 
 def load():
-    raise RuntimeError("libmmf.so binding not built yet")
+    """Open libmmf.so (built by ternary_weight_matmul_amd/build.py); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmmf.so not built at %s (run __graft_entry__.build())" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.mmf_last_error.restype = ctypes.c_char_p
+    lib.mmf_last_path.restype = ctypes.c_char_p
+    lib.mmf_ternary_pack_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
+    lib.mmf_ternary_pack.argtypes = [P, I32, I32, P, P, P, SZ, P]
+    lib.mmf_bitlinear_workspace_size.argtypes = [I64, I32, ctypes.POINTER(SZ)]
+    lib.mmf_bitlinear_fwd.argtypes = [P, ctypes.c_int, I64, ctypes.POINTER(CTernaryWeight), F32, P,
+                                      ctypes.c_int, P, P, P, P, SZ, P]
+    lib.mmf_hgrn_scan_workspace_size.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
+    lib.mmf_hgrn_scan_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P, SZ, P]
+    lib.mmf_layer_workspace_size.argtypes = [ctypes.POINTER(CLayerWeights), I64, I64, ctypes.POINTER(SZ)]
+    lib.mmf_layer_fwd.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, I64, P, P,
+                                  ctypes.c_int, P, SZ, ctypes.POINTER(CLayerProbe), P]
+    lib.mmf_layer_decode_step.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, P, P, SZ,
+                                          ctypes.POINTER(CLayerProbe), P]
+    for name in SYMBOLS[2:]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().mmf_last_error().decode()
+
+
+def last_path() -> str:
+    return load().mmf_last_path().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise MMFError(status, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return 0
+    if dt == torch.bfloat16:
+        return 1
+    raise TypeError("activation dtype must be float32 or bfloat16, got %s" % dt)
+
+
+def _workspace(nbytes: int, device, ws=None):
+    torch = _torch()
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class PackedLinear:
+    """A packed ternary weight on the device: words [n, k/16] (int32 storage), mu [1], RMSNorm gain [k] or None."""
+    packed: object
+    mu: object
+    norm_w: Optional[object]
+    n: int
+    k: int
+
+    def c(self) -> CTernaryWeight:
+        return CTernaryWeight(_ptr(self.packed), _ptr(self.mu), _ptr(self.norm_w), self.n, self.k)
+
+
+def ternary_pack(w, norm_w=None) -> PackedLinear:
+    """Ternarise and pack a latent fp32 weight [n, k] on the device (mmf_ternary_pack)."""
+    torch = _torch()
+    lib = load()
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+        raise TypeError("w must be a contiguous 2-d float32 tensor")
+    n, k = w.shape
+    need = SZ(0)
+    _check(lib.mmf_ternary_pack_workspace_size(n, k, ctypes.byref(need)))
+    packed = torch.empty((n, k // 16), dtype=torch.int32, device=w.device)
+    mu = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = _workspace(need.value, w.device)
+    _check(lib.mmf_ternary_pack(_ptr(w), n, k, _ptr(packed), _ptr(mu), _ptr(ws), need.value, _stream()))
+    return PackedLinear(packed, mu, norm_w, n, k)
+
+
+def bitlinear_fwd(x, w: PackedLinear, eps: float = 1e-8, out_dtype=None, codes_out=None, scale_out=None,
+                  acc_out=None, ws=None):
+    """FusedBitLinear on rows of x [..., k] (mmf_bitlinear_fwd); returns y [..., n]."""
+    torch = _torch()
+    lib = load()
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    k = x.shape[-1]
+    m = x.numel() // k if k else 0
+    out_dtype = out_dtype or x.dtype
+    y = torch.empty(x.shape[:-1] + (w.n,), dtype=out_dtype, device=x.device)
+    need = SZ(0)
+    _check(lib.mmf_bitlinear_workspace_size(m, k, ctypes.byref(need)))
+    ws = _workspace(need.value, x.device, ws)
+    cw = w.c()
+    _check(lib.mmf_bitlinear_fwd(_ptr(x), _dtype_code(x.dtype), m, ctypes.byref(cw), F32(eps), _ptr(y),
+                                 _dtype_code(out_dtype), _ptr(codes_out), _ptr(scale_out), _ptr(acc_out),
+                                 _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+def hgrn_scan_fwd(x, f, h0=None, mode: str = "auto", out=None, h_last=None, ws=None):
+    """h_t = f_t * h_{t-1} + x_t over x, f [b, t, d] fp32 (mmf_hgrn_scan_fwd); returns h."""
+    torch = _torch()
+    lib = load()
+    if x.shape != f.shape or x.dim() != 3:
+        raise ValueError("x and f must both be [b, t, d]")
+    for t_ in (x, f):
+        if t_.dtype != torch.float32 or not t_.is_contiguous():
+            raise TypeError("x and f must be contiguous float32")
+    b, t, d = x.shape
+    h = out if out is not None else torch.empty_like(x)
+    need = SZ(0)
+    _check(lib.mmf_hgrn_scan_workspace_size(b, t, d, SCAN_MODES[mode], ctypes.byref(need)))
+    wsb = _workspace(need.value, x.device, ws)
+    _check(lib.mmf_hgrn_scan_fwd(_ptr(x), _ptr(f), _ptr(h0), _ptr(h), _ptr(h_last), b, t, d, SCAN_MODES[mode],
+                                 _ptr(wsb), wsb.numel(), _stream()))
+    return h
+
+
+@dataclass
+class LayerParams:
+    """Packed weights of one HGRNBit block."""
+    i: PackedLinear
+    f: PackedLinear
+    g: PackedLinear
+    o: PackedLinear
+    gate: PackedLinear
+    down: PackedLinear
+    g_norm_w: Optional[object] = None
+    eps: float = 1e-8
+
+    @property
+    def d(self) -> int:
+        return self.i.k
+
+    @property
+    def inner(self) -> int:
+        return self.down.k
+
+    def c(self) -> CLayerWeights:
+        return CLayerWeights(self.i.c(), self.f.c(), self.g.c(), self.o.c(), self.gate.c(), self.down.c(),
+                             _ptr(self.g_norm_w), self.d, self.inner, self.eps)
+
+    @classmethod
+    def pack(cls, latent: dict, gains: Optional[dict] = None, eps: float = 1e-8) -> "LayerParams":
+        """Pack latent device weights {i,f,g,o,gate,down} (+ optional device gains) with mmf_ternary_pack."""
+        gains = gains or {}
+        parts = {k: ternary_pack(latent[k], gains.get(k)) for k in ("i", "f", "g", "o", "gate", "down")}
+        return cls(g_norm_w=gains.get("g_norm"), eps=eps, **parts)
+
+
+class LayerProbe:
+    """Device buffers receiving every stage of a layer call (validation only)."""
+
+    def __init__(self, m: int, d: int, inner: int, device, shared_ifg: bool = True):
+        torch = _torch()
+        e = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+        nq = 1 if shared_ifg else 3
+        self.codes_x = [e(m, d, dt=torch.int8) for _ in range(nq)]
+        self.scale_x = [e(m) for _ in range(nq)]
+        self.acc_ifg = e(m, 3, d, dt=torch.int32)
+        self.f, self.xt, self.g, self.h, self.u = (e(m, d) for _ in range(5))
+        self.codes_u, self.scale_u, self.acc_o = e(m, d, dt=torch.int8), e(m), e(m, d, dt=torch.int32)
+        self.x1 = e(m, d)
+        self.codes_x1, self.scale_x1 = e(m, d, dt=torch.int8), e(m)
+        self.acc_gate = e(m, 2 * inner, dt=torch.int32)
+        self.z = e(m, inner)
+        self.codes_z, self.scale_z = e(m, inner, dt=torch.int8), e(m)
+        self.acc_down = e(m, d, dt=torch.int32)
+
+    def c(self) -> CLayerProbe:
+        p = CLayerProbe()
+        for q in range(3):
+            p.codes_x[q] = _ptr(self.codes_x[q]) if q < len(self.codes_x) else None
+            p.scale_x[q] = _ptr(self.scale_x[q]) if q < len(self.scale_x) else None
+        for name in PROBE_FIELDS:
+            setattr(p, name, _ptr(getattr(self, name)))
+        return p
+
+    def host(self) -> dict:
+        out = {}
+        for name in ["codes_x", "scale_x"]:
+            out[name] = [t.cpu().numpy() for t in getattr(self, name)]
+        for name in PROBE_FIELDS:
+            out[name] = getattr(self, name).cpu().numpy()
+        return out
+
+
+def layer_workspace_size(params: LayerParams, b: int, t: int) -> int:
+    need = SZ(0)
+    cw = params.c()
+    _check(load().mmf_layer_workspace_size(ctypes.byref(cw), b, t, ctypes.byref(need)))
+    return need.value
+
+
+def layer_fwd(params: LayerParams, x, h0=None, want_h_last: bool = True, mode: str = "auto",
+              probe: Optional[LayerProbe] = None, out=None, h_last=None, ws=None):
+    """One HGRNBit block over x [b, t, d] (mmf_layer_fwd); returns (out, h_last)."""
+    torch = _torch()
+    lib = load()
+    if x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [b, t, d] tensor")
+    b, t, d = x.shape
+    out = out if out is not None else torch.empty_like(x)
+    if h_last is None and want_h_last:
+        h_last = torch.empty((b, d), dtype=torch.float32, device=x.device)
+    cw = params.c()
+    need = SZ(0)
+    _check(lib.mmf_layer_workspace_size(ctypes.byref(cw), b, t, ctypes.byref(need)))
+    wsb = _workspace(need.value, x.device, ws)
+    cp = probe.c() if probe is not None else None
+    _check(lib.mmf_layer_fwd(ctypes.byref(cw), _ptr(x), _ptr(out), _dtype_code(x.dtype), b, t, _ptr(h0),
+                             _ptr(h_last), SCAN_MODES[mode], _ptr(wsb), wsb.numel(),
+                             ctypes.byref(cp) if cp is not None else None, _stream()))
+    return out, h_last
+
+
+def layer_decode_step(params: LayerParams, x, h, probe: Optional[LayerProbe] = None, out=None, ws=None):
+    """One token per sequence, x [b, d], state h [b, d] fp32 updated in place (mmf_layer_decode_step)."""
+    torch = _torch()
+    lib = load()
+    if x.dim() != 2 or not x.is_contiguous() or not h.is_contiguous() or h.dtype != torch.float32:
+        raise ValueError("x must be contiguous [b, d]; h contiguous float32 [b, d]")
+    b, d = x.shape
+    out = out if out is not None else torch.empty_like(x)
+    cw = params.c()
+    need = SZ(0)
+    _check(lib.mmf_layer_workspace_size(ctypes.byref(cw), b, 1, ctypes.byref(need)))
+    wsb = _workspace(need.value, x.device, ws)
+    cp = probe.c() if probe is not None else None
+    _check(lib.mmf_layer_decode_step(ctypes.byref(cw), _ptr(x), _ptr(out), _dtype_code(x.dtype), b, _ptr(h),
+                                     _ptr(wsb), wsb.numel(), ctypes.byref(cp) if cp is not None else None,
+                                     _stream()))
+    return out

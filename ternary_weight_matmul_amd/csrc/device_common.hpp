@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 kernels of libmmf.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmf {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ---- activation element types -------------------------------------------------
+// fp32 and bf16 (stored as raw uint16 bits). bf16 -> fp32 is exact; fp32 -> bf16
+// rounds to nearest even.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float load_act(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_act(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ void store_act(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_act(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+// Four consecutive elements starting at p[i] (i % 4 == 0).
+__device__ __forceinline__ float4 load_act4(const float *p, int64_t i) {
+    return *reinterpret_cast<const float4 *>(p + i);
+}
+__device__ __forceinline__ float4 load_act4(const uint16_t *p, int64_t i) {
+    uint2 v = *reinterpret_cast<const uint2 *>(p + i);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+
+// ---- wave reductions (wave64) -------------------------------------------------
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// ---- activations ---------------------------------------------------------------
+// sigmoid(z) = 1 / (1 + e^-z) with the hardware exp2 and reciprocal (about 2 ulp).
+__device__ __forceinline__ float sigmoid_fast(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+__device__ __forceinline__ float silu_fast(float z) { return z * sigmoid_fast(z); }
+
+// ---- the row quantiser's binary32 decision steps ----------------------------------
+// r = (float)(1 / sqrt(ss / k + eps)), binary64 inside.
+__device__ __forceinline__ float rms_factor(double ss, int k, float eps) {
+    return (float)(1.0 / sqrt(ss / (double)k + (double)eps));
+}
+// s = 127 / max(amax, 1e-5), a correctly rounded binary32 division.
+__device__ __forceinline__ float quant_scale(float amax) {
+    return __fdiv_rn(127.0f, fmaxf(amax, 1e-5f));
+}
+__device__ __forceinline__ int quant_code(float y, float s) {
+    float p = rintf(__fmul_rn(y, s));
+    p = fminf(fmaxf(p, -128.0f), 127.0f);
+    return (int)p;
+}
+__device__ __forceinline__ uint32_t pack_codes4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+// ---- ternary words ----------------------------------------------------------------
+// A word holds 16 offset codes c = t + 1; (w >> 2j) & 0x03030303 gives the four
+// codes of k = 4j .. 4j+3 as int8 lanes, so one word is one 16-byte MFMA operand.
+__device__ __forceinline__ i32x4 decode_word(uint32_t w) {
+    i32x4 r;
+    r[0] = (int32_t)(w & 0x03030303u);
+    r[1] = (int32_t)((w >> 2) & 0x03030303u);
+    r[2] = (int32_t)((w >> 4) & 0x03030303u);
+    r[3] = (int32_t)((w >> 6) & 0x03030303u);
+    return r;
+}
+
+}  // namespace mmf

@@ -1,0 +1,336 @@
+// Row quantisers and the ternary weight packer (gfx950).
+//
+// RMSNorm fused with per-token absmax int8 quantisation, as the FusedBitLinear
+// of the MatMul-free LM does ("MatMul-Free LLM 深度分析报告", list
+// "可复用的模式与技巧"); eps of the RMSNorm from "MatMul-Free LM：把矩陣乘法從語言
+// 模型裡拿掉之後，剩下什麼", section "HGRNBitBlock 的結構". The g_norm RMSNorm-Swish
+// gate is fused with the o_proj quantiser in one pass over the row.
+//
+// One wavefront owns one row: the row is read once from HBM with 16-byte
+// (fp32) or 8-byte (bf16) coalesced loads and kept in registers, the sum of
+// squares is reduced in binary64 and the absmax in binary32 with cross-lane
+// shuffles, and the int8 codes leave as one 32-bit store per 4 elements.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mmf {
+
+// ----------------------------------------------------------------------------
+// norm_quant: q = clamp(rint(((x * r) * gain) * s)), r = rms factor, s = 127/amax
+// ----------------------------------------------------------------------------
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void norm_quant_kernel(const T *__restrict__ x, int64_t m, int k,
+                                                         const float *__restrict__ gain, float eps,
+                                                         int8_t *__restrict__ q, float *__restrict__ s,
+                                                         int32_t *__restrict__ sumq) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= m) return;
+    const int nch = k >> 2;
+    const T *xr = x + row * (int64_t)k;
+    float v[NV][4];
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + kWave * j;
+        float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < nch) t = load_act4(xr, 4 * (int64_t)c);
+        v[j][0] = t.x; v[j][1] = t.y; v[j][2] = t.z; v[j][3] = t.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += (double)v[j][e] * (double)v[j][e];
+    }
+    ss = wave_sum(ss);
+    const float r = rms_factor(ss, k, eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + kWave * j;
+        if (c < nch) {
+            float4 gv = gain ? *reinterpret_cast<const float4 *>(gain + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
+            const float ge[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float y = __fmul_rn(v[j][e], r);
+                if (gain) y = __fmul_rn(y, ge[e]);
+                v[j][e] = y;
+                amax = fmaxf(amax, fabsf(y));
+            }
+        }
+    }
+    amax = wave_max(amax);
+    const float sc = quant_scale(amax);
+    int tot = 0;
+    uint32_t *qr = reinterpret_cast<uint32_t *>(q + row * (int64_t)k);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + kWave * j;
+        if (c < nch) {
+            const int a0 = quant_code(v[j][0], sc), a1 = quant_code(v[j][1], sc);
+            const int a2 = quant_code(v[j][2], sc), a3 = quant_code(v[j][3], sc);
+            tot += a0 + a1 + a2 + a3;
+            qr[c] = pack_codes4(a0, a1, a2, a3);
+        }
+    }
+    tot = wave_sum_int(tot);
+    if (lane == 0) {
+        s[row] = sc;
+        sumq[row] = tot;
+    }
+}
+
+// Rows longer than the register cache: three passes over the row (the later
+// passes hit L2).
+template <typename T>
+__global__ __launch_bounds__(256) void norm_quant_long_kernel(const T *__restrict__ x, int64_t m, int k,
+                                                              const float *__restrict__ gain, float eps,
+                                                              int8_t *__restrict__ q, float *__restrict__ s,
+                                                              int32_t *__restrict__ sumq) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= m) return;
+    const T *xr = x + row * (int64_t)k;
+    double ss = 0.0;
+    for (int i = lane; i < k; i += kWave) {
+        const float a = load_act(xr, i);
+        ss += (double)a * (double)a;
+    }
+    const float r = rms_factor(wave_sum(ss), k, eps);
+    float amax = 0.0f;
+    for (int i = lane; i < k; i += kWave) {
+        float y = __fmul_rn(load_act(xr, i), r);
+        if (gain) y = __fmul_rn(y, gain[i]);
+        amax = fmaxf(amax, fabsf(y));
+    }
+    const float sc = quant_scale(wave_max(amax));
+    int tot = 0;
+    int8_t *qr = q + row * (int64_t)k;
+    for (int i = lane; i < k; i += kWave) {
+        float y = __fmul_rn(load_act(xr, i), r);
+        if (gain) y = __fmul_rn(y, gain[i]);
+        const int c = quant_code(y, sc);
+        tot += c;
+        qr[i] = (int8_t)c;
+    }
+    tot = wave_sum_int(tot);
+    if (lane == 0) {
+        s[row] = sc;
+        sumq[row] = tot;
+    }
+}
+
+constexpr int kMaxCachedChunks = 32;  // 64 lanes * 32 chunks * 4 = 8192 elements per row
+
+static int chunk_bucket(int k) {
+    const int nch = (k / 4 + kWave - 1) / kWave;
+    int b = 1;
+    while (b < nch) b *= 2;
+    return b;
+}
+
+template <typename T>
+static void norm_quant_dispatch(const T *x, int64_t m, int k, const float *gain, float eps, int8_t *q,
+                                float *s, int32_t *sumq, hipStream_t st, std::string *path) {
+    const dim3 grid((unsigned)((m + 3) / 4)), block(256);
+    const int nv = chunk_bucket(k);
+    const char *tn = sizeof(T) == 4 ? "f32" : "bf16";
+    if (nv > kMaxCachedChunks) {
+        norm_quant_long_kernel<T><<<grid, block, 0, st>>>(x, m, k, gain, eps, q, s, sumq);
+        if (path) *path += std::string("norm_quant_long<") + tn + ">;";
+        return;
+    }
+    switch (nv) {
+#define MMF_NQ(NV) case NV: norm_quant_kernel<T, NV><<<grid, block, 0, st>>>(x, m, k, gain, eps, q, s, sumq); break;
+        MMF_NQ(1) MMF_NQ(2) MMF_NQ(4) MMF_NQ(8) MMF_NQ(16) MMF_NQ(32)
+#undef MMF_NQ
+    }
+    if (path) *path += std::string("norm_quant<") + tn + "," + std::to_string(nv) + ">;";
+}
+
+hipError_t launch_norm_quant(const void *x, ActType xt, int64_t m, int k, const float *gain, float eps,
+                             int8_t *q, float *s, int32_t *sumq, hipStream_t stream, std::string *path) {
+    if (m <= 0) return hipSuccess;
+    if (xt == ACT_F32)
+        norm_quant_dispatch(static_cast<const float *>(x), m, k, gain, eps, q, s, sumq, stream, path);
+    else
+        norm_quant_dispatch(static_cast<const uint16_t *>(x), m, k, gain, eps, q, s, sumq, stream, path);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// gnorm_quant: u = ((h * r_h) * g_norm_w) * SiLU(g), then the o_proj quantiser of u
+// ----------------------------------------------------------------------------
+template <int NV>
+__global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restrict__ h, const float *__restrict__ g,
+                                                          int64_t m, int d, const float *__restrict__ gnw,
+                                                          const float *__restrict__ ogain, float eps,
+                                                          int8_t *__restrict__ q, float *__restrict__ s,
+                                                          int32_t *__restrict__ sumq, float *__restrict__ u_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= m) return;
+    const int nch = d >> 2;
+    const float *hr = h + row * (int64_t)d;
+    const float *gr = g + row * (int64_t)d;
+    float u[NV][4], gs[NV][4];
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + kWave * j;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (c < nch) {
+            a = *reinterpret_cast<const float4 *>(hr + 4 * c);
+            b = *reinterpret_cast<const float4 *>(gr + 4 * c);
+        }
+        u[j][0] = a.x; u[j][1] = a.y; u[j][2] = a.z; u[j][3] = a.w;
+        gs[j][0] = silu_fast(b.x); gs[j][1] = silu_fast(b.y); gs[j][2] = silu_fast(b.z); gs[j][3] = silu_fast(b.w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += (double)u[j][e] * (double)u[j][e];
+    }
+    const float rh = rms_factor(wave_sum(ss), d, eps);
+    double su = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + kWave * j;
+        float4 wv = (gnw && c < nch) ? *reinterpret_cast<const float4 *>(gnw + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
+        const float we[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float y = u[j][e] * rh;
+            if (gnw) y = y * we[e];
+            y = y * gs[j][e];
+            u[j][e] = y;
+            su += (double)y * (double)y;
+        }
+        if (u_out && c < nch)
+            *reinterpret_cast<float4 *>(u_out + row * (int64_t)d + 4 * c) = make_float4(u[j][0], u[j][1], u[j][2], u[j][3]);
+    }
+    const float r = rms_factor(wave_sum(su), d, eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + kWave * j;
+        if (c < nch) {
+            float4 gv = ogain ? *reinterpret_cast<const float4 *>(ogain + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
+            const float ge[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float y = __fmul_rn(u[j][e], r);
+                if (ogain) y = __fmul_rn(y, ge[e]);
+                u[j][e] = y;
+                amax = fmaxf(amax, fabsf(y));
+            }
+        }
+    }
+    const float sc = quant_scale(wave_max(amax));
+    int tot = 0;
+    uint32_t *qr = reinterpret_cast<uint32_t *>(q + row * (int64_t)d);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + kWave * j;
+        if (c < nch) {
+            const int a0 = quant_code(u[j][0], sc), a1 = quant_code(u[j][1], sc);
+            const int a2 = quant_code(u[j][2], sc), a3 = quant_code(u[j][3], sc);
+            tot += a0 + a1 + a2 + a3;
+            qr[c] = pack_codes4(a0, a1, a2, a3);
+        }
+    }
+    tot = wave_sum_int(tot);
+    if (lane == 0) {
+        s[row] = sc;
+        sumq[row] = tot;
+    }
+}
+
+hipError_t launch_gnorm_quant(const float *h, const float *g, int64_t m, int d, const float *g_norm_w,
+                              const float *o_gain, float eps, int8_t *q, float *s, int32_t *sumq,
+                              float *u_out, hipStream_t stream, std::string *path) {
+    if (m <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((m + 3) / 4)), block(256);
+    const int nv = chunk_bucket(d);
+    switch (nv) {
+#define MMF_GQ(NV) case NV: gnorm_quant_kernel<NV><<<grid, block, 0, stream>>>(h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
+        MMF_GQ(1) MMF_GQ(2) MMF_GQ(4) MMF_GQ(8) MMF_GQ(16) MMF_GQ(32)
+#undef MMF_GQ
+        default: return hipErrorInvalidValue;  // d > 8192 is rejected by the ABI layer
+    }
+    if (path) *path += "gnorm_quant<" + std::to_string(nv) + ">;";
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Ternary packer: mu = (float)(sum |w| / (n k)) (binary64, fixed order), then
+// t = clamp(rint(w * sw), -1, 1), sw = 1 / max(mu, 1e-5), 16 codes t+1 per word.
+// ----------------------------------------------------------------------------
+constexpr int kPackPartials = 512;
+
+size_t pack_workspace_bytes() { return kPackPartials * sizeof(double); }
+
+__global__ __launch_bounds__(256) void abs_sum_partial_kernel(const float *__restrict__ w, int64_t count,
+                                                              int64_t per_block, double *__restrict__ partial) {
+    __shared__ double red[256];
+    const int64_t lo = (int64_t)blockIdx.x * per_block;
+    const int64_t hi = lo + per_block < count ? lo + per_block : count;
+    double acc = 0.0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) acc += fabs((double)w[i]);
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const float *__restrict__ w, int n, int k,
+                                                   const double *__restrict__ partial, int nparts,
+                                                   uint32_t *__restrict__ packed, float *__restrict__ mu) {
+    __shared__ double red[256];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < nparts; i += 256) acc += partial[i];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    const float m = (float)(red[0] / ((double)n * (double)k));
+    if (blockIdx.x == 0 && threadIdx.x == 0) *mu = m;
+    const float sw = __fdiv_rn(1.0f, fmaxf(m, 1e-5f));
+    const int kw = k >> 4;
+    const int64_t word = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (word >= (int64_t)n * kw) return;
+    const int64_t row = word / kw;
+    const int wi = (int)(word % kw);
+    const float4 *src = reinterpret_cast<const float4 *>(w + row * (int64_t)k + 16 * wi);
+    uint32_t out = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float4 v = src[j];
+        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float p = rintf(__fmul_rn(e[b], sw));
+            p = fminf(fmaxf(p, -1.0f), 1.0f);
+            const uint32_t c = (uint32_t)((int)p + 1);
+            // element 4j + b of the word: j-th code of byte b
+            out |= c << (8 * b + 2 * j);
+        }
+    }
+    packed[word] = out;
+}
+
+hipError_t launch_pack(const float *w, int n, int k, uint32_t *packed, float *mu, void *ws,
+                       hipStream_t stream, std::string *path) {
+    const int64_t count = (int64_t)n * k;
+    int64_t per = (count + kPackPartials - 1) / kPackPartials;
+    per = (per + 255) / 256 * 256;
+    const int nparts = (int)((count + per - 1) / per);
+    double *partial = static_cast<double *>(ws);
+    abs_sum_partial_kernel<<<nparts, 256, 0, stream>>>(w, count, per, partial);
+    const int64_t words = (int64_t)n * (k >> 4);
+    pack_kernel<<<(unsigned)((words + 255) / 256), 256, 0, stream>>>(w, n, k, partial, nparts, packed, mu);
+    if (path) *path += "abs_sum_partial;pack;";
+    return hipGetLastError();
+}
+
+}  // namespace mmf

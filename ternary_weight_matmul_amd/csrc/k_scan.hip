@@ -1,0 +1,174 @@
+// HGRN recurrence h_t = f_t * h_{t-1} + x_t per (batch, channel), fp32 (gfx950).
+//
+// The recurrence and its two implementations -- step-wise and chunked -- are
+// those of the MatMul-free LM ("MatMul-Free LLM 深度分析报告", section
+// "核心价值提炼", table "创新之处" and list "可复用的模式与技巧").
+//
+// The scan is HBM-bound: 12 bytes per (b, t, c) (read x and f, write h).
+// Channels are contiguous, so one lane per channel gives fully coalesced
+// 256-byte wave accesses at every step; loads of a block of U steps are issued
+// before the dependent chain of that block runs.
+//  * recurrent: one lane runs the whole sequence of its channel.
+//  * chunked:   t is split into C chunks. Pass 1 reduces each chunk but the last
+//    to its pair (A = prod f, B = the chunk's h started from 0). Pass 2 lane
+//    (b, j, c) folds the pairs of chunks < j into its carry h_in = A*h_in + B
+//    and re-runs chunk j from it. C lanes per channel fill the GPU when b*d is
+//    small; the price is re-reading the first C-1 chunks once more.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mmf {
+
+constexpr int kScanU = 8;
+
+// Runs steps [t0, t1) of one channel from state h (strided by d), writing h
+// when out != nullptr. Returns the state after step t1-1.
+__device__ __forceinline__ float scan_run(const float *x, const float *f, float *out, int64_t d, int64_t t0,
+                                          int64_t t1, float h) {
+    int64_t t = t0;
+    for (; t + kScanU <= t1; t += kScanU) {
+        float xa[kScanU], fa[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            xa[u] = x[(t + u) * d];
+            fa[u] = f[(t + u) * d];
+        }
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            h = fa[u] * h + xa[u];
+            if (out) out[(t + u) * d] = h;
+        }
+    }
+    for (; t < t1; ++t) {
+        h = f[t * d] * h + x[t * d];
+        if (out) out[t * d] = h;
+    }
+    return h;
+}
+
+__global__ __launch_bounds__(256) void scan_recurrent_kernel(const float *x, const float *f, const float *h0,
+                                                             float *h, float *h_last, int64_t b, int64_t t,
+                                                             int64_t d) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= b * d) return;
+    const int64_t bi = gid / d, c = gid % d;
+    const int64_t base = bi * t * d + c;
+    float state = h0 ? h0[gid] : 0.0f;
+    state = scan_run(x + base, f + base, h + base, d, 0, t, state);
+    if (h_last) h_last[gid] = state;
+}
+
+// Pass 1: pair (prod f, h from 0) of chunk j < C-1.
+__global__ __launch_bounds__(256) void scan_chunk_reduce_kernel(const float *__restrict__ x,
+                                                                const float *__restrict__ f, int64_t b,
+                                                                int64_t t, int64_t d, int chunks, int64_t clen,
+                                                                float2 *__restrict__ agg) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_b = (int64_t)(chunks - 1) * d;
+    if (gid >= b * per_b) return;
+    const int64_t bi = gid / per_b;
+    const int64_t j = (gid % per_b) / d;
+    const int64_t c = gid % d;
+    const int64_t t0 = j * clen;
+    const int64_t t1 = t0 + clen < t ? t0 + clen : t;
+    const float *xp = x + bi * t * d + c;
+    const float *fp = f + bi * t * d + c;
+    float a = 1.0f, hb = 0.0f;
+    int64_t s = t0;
+    for (; s + kScanU <= t1; s += kScanU) {
+        float xa[kScanU], fa[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            xa[u] = xp[(s + u) * d];
+            fa[u] = fp[(s + u) * d];
+        }
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            hb = fa[u] * hb + xa[u];
+            a = a * fa[u];
+        }
+    }
+    for (; s < t1; ++s) {
+        const float fv = fp[s * d];
+        hb = fv * hb + xp[s * d];
+        a = a * fv;
+    }
+    agg[(bi * (chunks - 1) + j) * d + c] = make_float2(a, hb);
+}
+
+// Pass 2: carry into chunk j, then chunk j itself.
+__global__ __launch_bounds__(256) void scan_chunk_apply_kernel(const float *x, const float *f, const float *h0,
+                                                               float *h, float *h_last, int64_t b, int64_t t,
+                                                               int64_t d, int chunks, int64_t clen,
+                                                               const float2 *__restrict__ agg) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_b = (int64_t)chunks * d;
+    if (gid >= b * per_b) return;
+    const int64_t bi = gid / per_b;
+    const int j = (int)((gid % per_b) / d);
+    const int64_t c = gid % d;
+    float state = h0 ? h0[bi * d + c] : 0.0f;
+    const float2 *ag = agg + bi * (int64_t)(chunks - 1) * d + c;
+    for (int jj = 0; jj < j; ++jj) {
+        const float2 p = ag[(int64_t)jj * d];
+        state = p.x * state + p.y;
+    }
+    const int64_t t0 = (int64_t)j * clen;
+    const int64_t t1 = t0 + clen < t ? t0 + clen : t;
+    const int64_t base = bi * t * d + c;
+    state = scan_run(x + base, f + base, h + base, d, t0, t1, state);
+    if (h_last && j == chunks - 1) h_last[bi * d + c] = state;
+}
+
+__global__ void copy_state_kernel(const float *h0, float *h_last, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) h_last[i] = h0 ? h0[i] : 0.0f;
+}
+
+size_t scan_workspace_bytes(int64_t b, int64_t d, int chunks) {
+    return chunks > 1 ? (size_t)b * (size_t)(chunks - 1) * (size_t)d * sizeof(float2) : 0;
+}
+
+// Recurrent when b*d lanes already fill the GPU or t is short; otherwise enough
+// chunks for ~128k lanes, each chunk at least 64 steps.
+int scan_pick_chunks(int64_t b, int64_t t, int64_t d, int mode) {
+    if (mode == 1 || t <= 1) return 1;
+    const int64_t lanes = b * d;
+    int64_t c = (131072 + lanes - 1) / lanes;
+    if (mode == 2 && c < 2) c = 2;
+    const int64_t max_c = t / 64 > 1 ? t / 64 : (mode == 2 ? t : 1);
+    if (c > max_c) c = max_c;
+    if (c > 256) c = 256;
+    if (c < 1) c = 1;
+    if (mode == 2 && c < 2 && t >= 2) c = 2;
+    return (int)c;
+}
+
+hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h, float *h_last, int64_t b,
+                       int64_t t, int64_t d, int chunks, void *ws, hipStream_t stream, std::string *path) {
+    if (b <= 0) return hipSuccess;
+    if (t == 0) {
+        if (h_last) copy_state_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(h0, h_last, b * d);
+        if (path) *path += "scan_empty;";
+        return hipGetLastError();
+    }
+    if (chunks <= 1) {
+        scan_recurrent_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(x, f, h0, h, h_last, b, t, d);
+        if (path) *path += "scan_recurrent;";
+        return hipGetLastError();
+    }
+    const int64_t clen = (t + chunks - 1) / chunks;
+    const int c_eff = (int)((t + clen - 1) / clen);
+    float2 *agg = static_cast<float2 *>(ws);
+    if (c_eff > 1) {
+        const int64_t n1 = b * (int64_t)(c_eff - 1) * d;
+        scan_chunk_reduce_kernel<<<(unsigned)((n1 + 255) / 256), 256, 0, stream>>>(x, f, b, t, d, c_eff, clen, agg);
+    }
+    const int64_t n2 = b * (int64_t)c_eff * d;
+    scan_chunk_apply_kernel<<<(unsigned)((n2 + 255) / 256), 256, 0, stream>>>(x, f, h0, h, h_last, b, t, d, c_eff,
+                                                                              clen, agg);
+    if (path) *path += "scan_chunk(" + std::to_string(c_eff) + "x" + std::to_string(clen) + ");";
+    return hipGetLastError();
+}
+
+}  // namespace mmf

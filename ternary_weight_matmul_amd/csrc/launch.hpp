@@ -1,0 +1,63 @@
+// Host-side launchers of the libmmf kernels (internal to the library).
+// Every launcher enqueues on `stream` and returns hipGetLastError()'s result;
+// arguments are validated by the C-ABI layer before these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+namespace mmf {
+
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+
+// Row RMSNorm + absmax int8 quantiser over m rows of k elements.
+hipError_t launch_norm_quant(const void *x, ActType xt, int64_t m, int k, const float *gain, float eps,
+                             int8_t *q, float *s, int32_t *sumq, hipStream_t stream, std::string *path);
+
+// g_norm (RMSNorm(h) * w * SiLU(g)) followed by the o_proj quantiser; u_out optional.
+hipError_t launch_gnorm_quant(const float *h, const float *g, int64_t m, int d, const float *g_norm_w,
+                              const float *o_gain, float eps, int8_t *q, float *s, int32_t *sumq,
+                              float *u_out, hipStream_t stream, std::string *path);
+
+// Ternarise + pack. ws must hold pack_workspace_bytes().
+size_t pack_workspace_bytes();
+hipError_t launch_pack(const float *w, int n, int k, uint32_t *packed, float *mu, void *ws,
+                       hipStream_t stream, std::string *path);
+
+// Epilogues of the ternary contraction.
+enum EpiKind {
+    EPI_LINEAR = 0,      // NG=1: y = acc * dq                      (out0, dtype out_type)
+    EPI_RESID = 1,       // NG=1: y = res + acc * dq                (out0, dtype out_type; res dtype res_type)
+    EPI_GATES = 2,       // NG=3: f = sig(f^), xt = (1-f) SiLU(i^), g = g^   (out0 f, out1 xt, out2 g; fp32)
+    EPI_GATES_STEP = 3,  // NG=3: h = f h + xt in place on out0; g to out1; f/xt probes out2/out3
+    EPI_GLU = 4          // NG=2: z = SiLU(a) * b                   (out0 fp32)
+};
+
+struct ContractArgs {
+    // per group (i/f/g, or the two halves of gate_proj, or one tensor)
+    const int8_t *A[3];      // codes [m][k]
+    const float *s[3];       // activation scale per row
+    const int32_t *sumq[3];  // sum of codes per row
+    const uint32_t *B[3];    // packed rows [nc][k/16]
+    const float *mu[3];      // device scalar per group
+    int64_t m;
+    int nc;                  // output channels per group
+    int k;
+    void *out0, *out1, *out2, *out3;
+    const void *res;
+    int32_t *acc_probe;      // [m][ng*nc] (group-major within a row) or NULL
+    ActType out_type, res_type;
+};
+
+// Prefill-shaped contraction (int8 MFMA tiles) and decode-shaped one (m <= 64).
+hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a,
+                           hipStream_t stream, std::string *path);
+
+// HGRN scan. chunks == 1 means the recurrent (sequential) kernel.
+size_t scan_workspace_bytes(int64_t b, int64_t d, int chunks);
+int scan_pick_chunks(int64_t b, int64_t t, int64_t d, int mode);
+hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h, float *h_last,
+                       int64_t b, int64_t t, int64_t d, int chunks, void *ws, hipStream_t stream,
+                       std::string *path);
+
+}  // namespace mmf

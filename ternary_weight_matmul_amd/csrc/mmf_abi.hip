@@ -1,0 +1,427 @@
+// C ABI of libmmf (declared in include/mmf.h): argument validation, workspace
+// carving and the order of kernel launches for a FusedBitLinear, the HGRN
+// scan and one HGRNBit block ("MatMul-Free LM：把矩陣乘法從語言模型裡拿掉之後，
+// 剩下什麼", section "HGRNBitBlock 的結構").
+//
+// Validation happens on the host before any HIP call; errors set a
+// thread-local message. Each call records the kernel variants it launched
+// (mmf_last_path), so a caller can see which path ran: the same page, section
+// "什麼情況下這個工具是錯的選擇", names a silent fallback to a slow path as a
+// failure mode.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "mmf.h"
+#include "launch.hpp"
+
+using namespace mmf;
+
+namespace {
+
+thread_local std::string g_err;
+thread_local std::string g_path;
+
+mmf_status fail(mmf_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+mmf_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MMF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    g_err.clear();
+    return MMF_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxK = 65536;       // |sum t*q| <= 128*k stays exact in binary32
+constexpr int kMaxNormRow = 8192;  // g_norm keeps a row in registers
+
+// Carves 256-byte aligned buffers out of a workspace; with base == nullptr it
+// only measures.
+struct Carver {
+    char *base;
+    size_t off = 0;
+    explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+    template <typename T>
+    T *take(size_t count) {
+        off = (off + 255) & ~size_t(255);
+        T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+mmf_status check_weight(const mmf_ternary_weight *w, const char *name) {
+    if (!w) return fail(MMF_ERR_INVALID_ARG, "%s: weight is NULL", name);
+    if (!w->packed || !w->mu) return fail(MMF_ERR_INVALID_ARG, "%s: packed or mu is NULL", name);
+    if (w->n <= 0 || w->k <= 0) return fail(MMF_ERR_INVALID_ARG, "%s: n=%d k=%d must be positive", name, w->n, w->k);
+    if (w->k % 16) return fail(MMF_ERR_UNSUPPORTED, "%s: k=%d is not a multiple of 16", name, w->k);
+    if (w->k > kMaxK) return fail(MMF_ERR_UNSUPPORTED, "%s: k=%d exceeds %d", name, w->k, kMaxK);
+    if (!aligned16(w->packed) || (w->norm_w && !aligned16(w->norm_w)))
+        return fail(MMF_ERR_INVALID_ARG, "%s: packed / norm_w must be 16-byte aligned", name);
+    return MMF_OK;
+}
+
+bool valid_dtype(mmf_dtype t) { return t == MMF_F32 || t == MMF_BF16; }
+ActType act(mmf_dtype t) { return t == MMF_F32 ? ACT_F32 : ACT_BF16; }
+
+// ---------------------------------------------------------------- bitlinear --
+struct BitlinearWs {
+    int8_t *codes;
+    float *s;
+    int32_t *sumq;
+};
+
+size_t bitlinear_plan(Carver &c, int64_t m, int k, BitlinearWs *o) {
+    BitlinearWs w;
+    w.codes = c.take<int8_t>((size_t)m * k);
+    w.s = c.take<float>((size_t)m);
+    w.sumq = c.take<int32_t>((size_t)m);
+    if (o) *o = w;
+    return c.off;
+}
+
+// -------------------------------------------------------------------- layer --
+struct LayerWs {
+    int8_t *codes_x[3];
+    float *s_x[3];
+    int32_t *sq_x[3];
+    float *f, *xt, *g, *h, *x1, *z;
+    int8_t *codes_b;
+    float *s_b;
+    int32_t *sq_b;
+    void *scan;
+};
+
+bool shared_ifg(const mmf_layer_weights *w) {
+    return w->i.norm_w == w->f.norm_w && w->f.norm_w == w->g.norm_w;
+}
+
+size_t layer_plan(Carver &c, const mmf_layer_weights *w, int64_t b, int64_t t, int chunks, LayerWs *o) {
+    const int64_t m = b * t;
+    const size_t d = (size_t)w->d, inner = (size_t)w->inner;
+    const int nq = shared_ifg(w) ? 1 : 3;
+    LayerWs L{};
+    for (int q = 0; q < nq; ++q) {
+        L.codes_x[q] = c.take<int8_t>(m * d);
+        L.s_x[q] = c.take<float>(m);
+        L.sq_x[q] = c.take<int32_t>(m);
+    }
+    for (int q = nq; q < 3; ++q) {
+        L.codes_x[q] = L.codes_x[0];
+        L.s_x[q] = L.s_x[0];
+        L.sq_x[q] = L.sq_x[0];
+    }
+    L.f = c.take<float>(m * d);
+    L.xt = c.take<float>(m * d);
+    L.g = c.take<float>(m * d);
+    L.h = c.take<float>(m * d);
+    L.x1 = c.take<float>(m * d);
+    L.z = c.take<float>(m * inner);
+    L.codes_b = c.take<int8_t>(m * (d > inner ? d : inner));
+    L.s_b = c.take<float>(m);
+    L.sq_b = c.take<int32_t>(m);
+    L.scan = c.take<char>(scan_workspace_bytes(b, w->d, chunks));
+    if (o) *o = L;
+    return c.off;
+}
+
+mmf_status check_layer(const mmf_layer_weights *w) {
+    if (!w) return fail(MMF_ERR_INVALID_ARG, "layer weights are NULL");
+    const int d = w->d, inner = w->inner;
+    if (d <= 0 || inner <= 0) return fail(MMF_ERR_INVALID_ARG, "d=%d inner=%d must be positive", d, inner);
+    if (d % 16 || inner % 16) return fail(MMF_ERR_UNSUPPORTED, "d=%d and inner=%d must be multiples of 16", d, inner);
+    if (d > kMaxNormRow) return fail(MMF_ERR_UNSUPPORTED, "d=%d exceeds %d", d, kMaxNormRow);
+    if (!(w->eps >= 0.0f)) return fail(MMF_ERR_INVALID_ARG, "eps must be >= 0");
+    const struct { const mmf_ternary_weight *p; const char *name; int n, k; } ws[] = {
+        {&w->i, "i_proj", d, d}, {&w->f, "f_proj", d, d}, {&w->g, "g_proj", d, d},
+        {&w->o, "o_proj", d, d}, {&w->gate, "gate_proj", 2 * inner, d}, {&w->down, "down_proj", d, inner}};
+    for (const auto &e : ws) {
+        mmf_status st = check_weight(e.p, e.name);
+        if (st != MMF_OK) return st;
+        if (e.p->n != e.n || e.p->k != e.k)
+            return fail(MMF_ERR_INVALID_ARG, "%s: shape [%d][%d], expected [%d][%d]", e.name, e.p->n, e.p->k, e.n, e.k);
+    }
+    if (w->g_norm_w && !aligned16(w->g_norm_w)) return fail(MMF_ERR_INVALID_ARG, "g_norm_w must be 16-byte aligned");
+    return MMF_OK;
+}
+
+template <typename T>
+T *pick(T *probe_ptr, T *ws_ptr) { return probe_ptr ? probe_ptr : ws_ptr; }
+
+// The block after the mixer's gates: g_norm, o_proj + residual, MLP + residual.
+hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t m,
+                      const LayerWs &L, const float *h, const float *g, const mmf_layer_probe *pr,
+                      hipStream_t st, std::string *path) {
+    const int d = w->d, inner = w->inner;
+    const float eps = w->eps;
+    hipError_t e;
+    int8_t *cu = pick(pr ? pr->codes_u : nullptr, L.codes_b);
+    float *su = pick(pr ? pr->scale_u : nullptr, L.s_b);
+    e = launch_gnorm_quant(h, g, m, d, w->g_norm_w, w->o.norm_w, eps, cu, su, L.sq_b, pr ? pr->u : nullptr, st, path);
+    if (e != hipSuccess) return e;
+
+    float *x1 = pick(pr ? pr->x1 : nullptr, L.x1);
+    ContractArgs co{};
+    for (int q = 0; q < 3; ++q) { co.A[q] = cu; co.s[q] = su; co.sumq[q] = L.sq_b; co.B[q] = w->o.packed; co.mu[q] = w->o.mu; }
+    co.m = m; co.nc = d; co.k = d;
+    co.out0 = x1; co.res = x; co.res_type = act(actt); co.out_type = ACT_F32;
+    co.acc_probe = pr ? pr->acc_o : nullptr;
+    if ((e = launch_contract(co, EPI_RESID, 1, true, st, path)) != hipSuccess) return e;
+
+    int8_t *c1 = pick(pr ? pr->codes_x1 : nullptr, L.codes_b);
+    float *s1 = pick(pr ? pr->scale_x1 : nullptr, L.s_b);
+    if ((e = launch_norm_quant(x1, ACT_F32, m, d, w->gate.norm_w, eps, c1, s1, L.sq_b, st, path)) != hipSuccess) return e;
+
+    float *z = pick(pr ? pr->z : nullptr, L.z);
+    ContractArgs cg{};
+    for (int q = 0; q < 3; ++q) { cg.A[q] = c1; cg.s[q] = s1; cg.sumq[q] = L.sq_b; cg.mu[q] = w->gate.mu; }
+    cg.B[0] = w->gate.packed;
+    cg.B[1] = w->gate.packed + (size_t)inner * (d / 16);
+    cg.B[2] = cg.B[1];
+    cg.m = m; cg.nc = inner; cg.k = d;
+    cg.out0 = z; cg.out_type = ACT_F32;
+    cg.acc_probe = pr ? pr->acc_gate : nullptr;
+    if ((e = launch_contract(cg, EPI_GLU, 2, true, st, path)) != hipSuccess) return e;
+
+    int8_t *cz = pick(pr ? pr->codes_z : nullptr, L.codes_b);
+    float *sz = pick(pr ? pr->scale_z : nullptr, L.s_b);
+    if ((e = launch_norm_quant(z, ACT_F32, m, inner, w->down.norm_w, eps, cz, sz, L.sq_b, st, path)) != hipSuccess) return e;
+
+    ContractArgs cd{};
+    for (int q = 0; q < 3; ++q) { cd.A[q] = cz; cd.s[q] = sz; cd.sumq[q] = L.sq_b; cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
+    cd.m = m; cd.nc = d; cd.k = inner;
+    cd.out0 = out; cd.out_type = act(actt); cd.res = x1; cd.res_type = ACT_F32;
+    cd.acc_probe = pr ? pr->acc_down : nullptr;
+    return launch_contract(cd, EPI_RESID, 1, true, st, path);
+}
+
+// Quantise x for i/f/g (once when their gains coincide) and fill the contraction's A side.
+hipError_t quant_ifg(const mmf_layer_weights *w, const void *x, mmf_dtype actt, int64_t m, LayerWs &L,
+                     const mmf_layer_probe *pr, ContractArgs &ca, bool *shared, hipStream_t st, std::string *path) {
+    *shared = shared_ifg(w);
+    const int nq = *shared ? 1 : 3;
+    const float *gains[3] = {w->i.norm_w, w->f.norm_w, w->g.norm_w};
+    int8_t *codes[3];
+    float *scales[3];
+    for (int q = 0; q < nq; ++q) {
+        codes[q] = pick(pr ? pr->codes_x[q] : nullptr, L.codes_x[q]);
+        scales[q] = pick(pr ? pr->scale_x[q] : nullptr, L.s_x[q]);
+        hipError_t e = launch_norm_quant(x, act(actt), m, w->d, gains[q], w->eps, codes[q], scales[q], L.sq_x[q], st, path);
+        if (e != hipSuccess) return e;
+    }
+    const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
+    for (int q = 0; q < 3; ++q) {
+        const int src = *shared ? 0 : q;
+        ca.A[q] = codes[src];
+        ca.s[q] = scales[src];
+        ca.sumq[q] = L.sq_x[src];
+        ca.B[q] = tw[q]->packed;
+        ca.mu[q] = tw[q]->mu;
+    }
+    ca.m = m; ca.nc = w->d; ca.k = w->d;
+    ca.acc_probe = pr ? pr->acc_ifg : nullptr;
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mmf_last_error(void) { return g_err.c_str(); }
+const char *mmf_last_path(void) { return g_path.c_str(); }
+
+mmf_status mmf_ternary_pack_workspace_size(int32_t n, int32_t k, size_t *bytes) {
+    if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
+    if (n <= 0 || k <= 0) return fail(MMF_ERR_INVALID_ARG, "n=%d k=%d must be positive", n, k);
+    if (k % 16) return fail(MMF_ERR_UNSUPPORTED, "k=%d is not a multiple of 16", k);
+    *bytes = pack_workspace_bytes();
+    return MMF_OK;
+}
+
+mmf_status mmf_ternary_pack(const float *w, int32_t n, int32_t k, uint32_t *packed, float *mu, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    size_t need = 0;
+    mmf_status st = mmf_ternary_pack_workspace_size(n, k, &need);
+    if (st != MMF_OK) return st;
+    if (!w || !packed || !mu) return fail(MMF_ERR_INVALID_ARG, "w, packed and mu must be non-NULL");
+    if (!aligned16(w) || !aligned16(packed)) return fail(MMF_ERR_INVALID_ARG, "w and packed must be 16-byte aligned");
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    std::string path;
+    mmf_status r = hip_status(launch_pack(w, n, k, packed, mu, ws, stream, &path), "mmf_ternary_pack");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+mmf_status mmf_bitlinear_workspace_size(int64_t m, int32_t k, size_t *bytes) {
+    if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
+    if (m < 0 || k <= 0) return fail(MMF_ERR_INVALID_ARG, "m=%lld k=%d invalid", (long long)m, k);
+    Carver c(nullptr);
+    *bytes = bitlinear_plan(c, m, k, nullptr);
+    return MMF_OK;
+}
+
+mmf_status mmf_bitlinear_fwd(const void *x, mmf_dtype xt, int64_t m, const mmf_ternary_weight *w, float eps,
+                             void *y, mmf_dtype yt, int8_t *codes_out, float *scale_out, int32_t *acc_out,
+                             void *ws, size_t ws_bytes, hipStream_t stream) {
+    mmf_status st = check_weight(w, "weight");
+    if (st != MMF_OK) return st;
+    if (!valid_dtype(xt) || !valid_dtype(yt)) return fail(MMF_ERR_INVALID_ARG, "bad dtype");
+    if (m < 0) return fail(MMF_ERR_INVALID_ARG, "m=%lld < 0", (long long)m);
+    if (!(eps >= 0.0f)) return fail(MMF_ERR_INVALID_ARG, "eps must be >= 0");
+    if (m > 0 && (!x || !y)) return fail(MMF_ERR_INVALID_ARG, "x and y must be non-NULL");
+    if (!aligned16(x) || !aligned16(codes_out)) return fail(MMF_ERR_INVALID_ARG, "x and codes_out must be 16-byte aligned");
+    size_t need = 0;
+    mmf_bitlinear_workspace_size(m, w->k, &need);
+    if (m > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    std::string path;
+    if (m == 0) {
+        g_path = "empty";
+        g_err.clear();
+        return MMF_OK;
+    }
+    Carver c(ws);
+    BitlinearWs B;
+    bitlinear_plan(c, m, w->k, &B);
+    int8_t *codes = codes_out ? codes_out : B.codes;
+    float *s = scale_out ? scale_out : B.s;
+    hipError_t e = launch_norm_quant(x, act(xt), m, w->k, w->norm_w, eps, codes, s, B.sumq, stream, &path);
+    if (e == hipSuccess) {
+        ContractArgs a{};
+        for (int q = 0; q < 3; ++q) { a.A[q] = codes; a.s[q] = s; a.sumq[q] = B.sumq; a.B[q] = w->packed; a.mu[q] = w->mu; }
+        a.m = m; a.nc = w->n; a.k = w->k;
+        a.out0 = y; a.out_type = act(yt);
+        a.acc_probe = acc_out;
+        e = launch_contract(a, EPI_LINEAR, 1, true, stream, &path);
+    }
+    mmf_status r = hip_status(e, "mmf_bitlinear_fwd");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+mmf_status mmf_hgrn_scan_workspace_size(int64_t b, int64_t t, int64_t d, mmf_scan_mode mode, size_t *bytes) {
+    if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
+    if (b < 0 || t < 0 || d <= 0) return fail(MMF_ERR_INVALID_ARG, "b, t >= 0 and d > 0 required");
+    if (mode != MMF_SCAN_AUTO && mode != MMF_SCAN_RECURRENT && mode != MMF_SCAN_CHUNK)
+        return fail(MMF_ERR_INVALID_ARG, "bad scan mode %d", (int)mode);
+    *bytes = scan_workspace_bytes(b, d, scan_pick_chunks(b, t, d, (int)mode));
+    return MMF_OK;
+}
+
+mmf_status mmf_hgrn_scan_fwd(const float *x, const float *f, const float *h0, float *h, float *h_last, int64_t b,
+                             int64_t t, int64_t d, mmf_scan_mode mode, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    size_t need = 0;
+    mmf_status st = mmf_hgrn_scan_workspace_size(b, t, d, mode, &need);
+    if (st != MMF_OK) return st;
+    if (b > 0 && t > 0 && (!x || !f || !h)) return fail(MMF_ERR_INVALID_ARG, "x, f and h must be non-NULL");
+    if (need && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    std::string path;
+    const int chunks = scan_pick_chunks(b, t, d, (int)mode);
+    mmf_status r = hip_status(launch_scan(x, f, h0, h, h_last, b, t, d, chunks, ws, stream, &path), "mmf_hgrn_scan_fwd");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+mmf_status mmf_layer_workspace_size(const mmf_layer_weights *w, int64_t b, int64_t t, size_t *bytes) {
+    if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
+    mmf_status st = check_layer(w);
+    if (st != MMF_OK) return st;
+    if (b < 0 || t < 0) return fail(MMF_ERR_INVALID_ARG, "b, t must be >= 0");
+    const int chunks = scan_pick_chunks(b, t, w->d, MMF_SCAN_CHUNK);
+    Carver c(nullptr);
+    *bytes = layer_plan(c, w, b, t > 0 ? t : 1, chunks, nullptr);
+    return MMF_OK;
+}
+
+mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b, int64_t t,
+                         const float *h0, float *h_last, mmf_scan_mode mode, void *ws, size_t ws_bytes,
+                         const mmf_layer_probe *probe, hipStream_t stream) {
+    size_t need = 0;
+    mmf_status st = mmf_layer_workspace_size(w, b, t, &need);
+    if (st != MMF_OK) return st;
+    if (!valid_dtype(actt)) return fail(MMF_ERR_INVALID_ARG, "bad activation dtype");
+    if (mode != MMF_SCAN_AUTO && mode != MMF_SCAN_RECURRENT && mode != MMF_SCAN_CHUNK)
+        return fail(MMF_ERR_INVALID_ARG, "bad scan mode %d", (int)mode);
+    const int64_t m = b * t;
+    if (m > 0 && (!x || !out)) return fail(MMF_ERR_INVALID_ARG, "x and out must be non-NULL");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(h0) || !aligned16(h_last))
+        return fail(MMF_ERR_INVALID_ARG, "x, out, h0, h_last must be 16-byte aligned");
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    std::string path;
+    hipError_t e = hipSuccess;
+    if (m == 0) {
+        e = launch_scan(nullptr, nullptr, h0, nullptr, h_last, b, 0, w->d, 1, nullptr, stream, &path);
+    } else {
+        const int chunks = scan_pick_chunks(b, t, w->d, (int)mode);
+        Carver c(ws);
+        LayerWs L;
+        layer_plan(c, w, b, t, scan_pick_chunks(b, t, w->d, MMF_SCAN_CHUNK), &L);
+        ContractArgs ca{};
+        bool shared = true;
+        e = quant_ifg(w, x, actt, m, L, probe, ca, &shared, stream, &path);
+        float *f = pick(probe ? probe->f : nullptr, L.f);
+        float *xt = pick(probe ? probe->xt : nullptr, L.xt);
+        float *g = pick(probe ? probe->g : nullptr, L.g);
+        float *h = pick(probe ? probe->h : nullptr, L.h);
+        if (e == hipSuccess) {
+            ca.out0 = f; ca.out1 = xt; ca.out2 = g; ca.out_type = ACT_F32;
+            e = launch_contract(ca, EPI_GATES, 3, shared, stream, &path);
+        }
+        if (e == hipSuccess) e = launch_scan(xt, f, h0, h, h_last, b, t, w->d, chunks, L.scan, stream, &path);
+        if (e == hipSuccess) e = block_tail(w, x, out, actt, m, L, h, g, probe, stream, &path);
+    }
+    mmf_status r = hip_status(e, "mmf_layer_fwd");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b,
+                                 float *h, void *ws, size_t ws_bytes, const mmf_layer_probe *probe,
+                                 hipStream_t stream) {
+    size_t need = 0;
+    mmf_status st = mmf_layer_workspace_size(w, b, 1, &need);
+    if (st != MMF_OK) return st;
+    if (!valid_dtype(actt)) return fail(MMF_ERR_INVALID_ARG, "bad activation dtype");
+    if (b > 0 && (!x || !out || !h)) return fail(MMF_ERR_INVALID_ARG, "x, out and h must be non-NULL");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(h))
+        return fail(MMF_ERR_INVALID_ARG, "x, out and h must be 16-byte aligned");
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    std::string path;
+    hipError_t e = hipSuccess;
+    if (b > 0) {
+        Carver c(ws);
+        LayerWs L;
+        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
+        ContractArgs ca{};
+        bool shared = true;
+        e = quant_ifg(w, x, actt, b, L, probe, ca, &shared, stream, &path);
+        float *g = pick(probe ? probe->g : nullptr, L.g);
+        if (e == hipSuccess) {
+            ca.out0 = h; ca.out1 = g; ca.out_type = ACT_F32;
+            ca.out2 = probe ? probe->f : nullptr;
+            ca.out3 = probe ? probe->xt : nullptr;
+            e = launch_contract(ca, EPI_GATES_STEP, 3, shared, stream, &path);
+        }
+        if (e == hipSuccess && probe && probe->h)
+            e = hipMemcpyAsync(probe->h, h, (size_t)b * w->d * sizeof(float), hipMemcpyDeviceToDevice, stream);
+        if (e == hipSuccess) e = block_tail(w, x, out, actt, b, L, h, g, probe, stream, &path);
+    }
+    mmf_status r = hip_status(e, "mmf_layer_decode_step");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+"""C-ABI contract checks that run without a GPU.
+
+The library must load, export every entry point include/mmf.h declares, and
+reject bad arguments on the host -- with a status code and a message --
+before it makes any HIP call. Fake device addresses are used only where
+validation fails before they could be touched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ternary_weight_matmul_amd as mmf
+from ternary_weight_matmul_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x7f0000000000  # 256-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libmmf.so not built")
+    return mmf.load()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "mmf.h")).read()
+    return sorted(set(re.findall(r"\b(mmf_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(B.SYMBOLS)
+
+
+def test_every_declared_symbol_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mmf_[a-z_0-9]+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def _weight(n=64, k=64, packed=FAKE, mu=FAKE + 4096, norm=None):
+    return B.CTernaryWeight(packed, mu, norm, n, k)
+
+
+def _layer(d=64, inner=96):
+    w = lambda n, k: _weight(n, k)  # noqa: E731
+    return B.CLayerWeights(w(d, d), w(d, d), w(d, d), w(d, d), w(2 * inner, d), w(d, inner), None, d, inner, 1e-8)
+
+
+def _err(lib):
+    return lib.mmf_last_error().decode()
+
+
+def test_pack_validation(lib):
+    sz = ctypes.c_size_t(0)
+    assert lib.mmf_ternary_pack_workspace_size(8, 20, ctypes.byref(sz)) == UNSUPPORTED
+    assert "multiple of 16" in _err(lib)
+    assert lib.mmf_ternary_pack_workspace_size(0, 32, ctypes.byref(sz)) == INVALID
+    assert lib.mmf_ternary_pack_workspace_size(8, 32, ctypes.byref(sz)) == OK and sz.value > 0
+    assert lib.mmf_ternary_pack(None, 8, 32, FAKE, FAKE, FAKE, sz.value, None) == INVALID
+    assert lib.mmf_ternary_pack(FAKE, 8, 32, FAKE, FAKE, FAKE, sz.value - 1, None) == WORKSPACE
+    assert lib.mmf_ternary_pack(FAKE + 4, 8, 32, FAKE, FAKE, FAKE, sz.value, None) == INVALID
+
+
+def test_bitlinear_validation(lib):
+    sz = ctypes.c_size_t(0)
+    assert lib.mmf_bitlinear_workspace_size(16, 64, ctypes.byref(sz)) == OK
+    need = sz.value
+    assert need >= 16 * 64 + 16 * 8
+    w = _weight()
+    args = lambda **kw: dict(dict(x=FAKE, xt=0, m=16, w=ctypes.byref(w), eps=1e-8, y=FAKE, yt=0, c=None, s=None,  # noqa: E731
+                                  a=None, ws=FAKE, wsb=need, st=None), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return lib.mmf_bitlinear_fwd(a["x"], a["xt"], a["m"], a["w"], ctypes.c_float(a["eps"]), a["y"], a["yt"],
+                                     a["c"], a["s"], a["a"], a["ws"], a["wsb"], a["st"])
+    assert call(w=None) == INVALID
+    assert call(xt=7) == INVALID
+    assert call(m=-1) == INVALID
+    assert call(x=None) == INVALID
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 16) == WORKSPACE
+    assert call(eps=-1.0) == INVALID
+    bad = _weight(k=40)
+    assert call(w=ctypes.byref(bad)) == UNSUPPORTED
+    big = _weight(k=65536 + 16)
+    assert call(w=ctypes.byref(big)) == UNSUPPORTED
+    nomu = _weight(mu=None)
+    assert call(w=ctypes.byref(nomu)) == INVALID
+    # m == 0 is valid and launches nothing
+    assert call(m=0, x=None, y=None, ws=None, wsb=0) == OK
+    assert lib.mmf_last_path().decode() == "empty"
+
+
+def test_scan_validation(lib):
+    sz = ctypes.c_size_t(0)
+    assert lib.mmf_hgrn_scan_workspace_size(2, 10, 0, 0, ctypes.byref(sz)) == INVALID
+    assert lib.mmf_hgrn_scan_workspace_size(2, 10, 64, 9, ctypes.byref(sz)) == INVALID
+    assert lib.mmf_hgrn_scan_workspace_size(1, 4096, 64, 1, ctypes.byref(sz)) == OK and sz.value == 0
+    assert lib.mmf_hgrn_scan_workspace_size(1, 4096, 64, 2, ctypes.byref(sz)) == OK and sz.value > 0
+    assert lib.mmf_hgrn_scan_fwd(None, FAKE, None, FAKE, None, 1, 4, 64, 1, None, 0, None) == INVALID
+    assert lib.mmf_hgrn_scan_fwd(FAKE, FAKE, None, FAKE, None, 1, 4096, 64, 2, None, 0, None) == WORKSPACE
+
+
+def test_layer_validation(lib):
+    L = _layer()
+    sz = ctypes.c_size_t(0)
+    assert lib.mmf_layer_workspace_size(ctypes.byref(L), 2, 8, ctypes.byref(sz)) == OK
+    need = sz.value
+    assert need > 0
+    bad = _layer()
+    bad.gate = _weight(96, 64)  # must be [2*inner][d]
+    assert lib.mmf_layer_workspace_size(ctypes.byref(bad), 2, 8, ctypes.byref(sz)) == INVALID
+    assert "gate_proj" in _err(lib)
+    odd = _layer(d=72)
+    assert lib.mmf_layer_workspace_size(ctypes.byref(odd), 2, 8, ctypes.byref(sz)) == UNSUPPORTED
+    wide = _layer(d=8192 + 16)
+    assert lib.mmf_layer_workspace_size(ctypes.byref(wide), 1, 1, ctypes.byref(sz)) == UNSUPPORTED
+    assert lib.mmf_layer_fwd(ctypes.byref(L), FAKE, FAKE, 0, 2, 8, None, None, 0, FAKE, need - 1, None, None) == WORKSPACE
+    assert lib.mmf_layer_fwd(ctypes.byref(L), FAKE, FAKE, 5, 2, 8, None, None, 0, FAKE, need, None, None) == INVALID
+    assert lib.mmf_layer_fwd(ctypes.byref(L), FAKE, FAKE, 0, 2, 8, None, None, 7, FAKE, need, None, None) == INVALID
+    assert lib.mmf_layer_fwd(ctypes.byref(L), FAKE + 8, FAKE, 0, 2, 8, None, None, 0, FAKE, need, None, None) == INVALID
+    assert lib.mmf_layer_decode_step(ctypes.byref(L), FAKE, FAKE, 0, 2, None, FAKE, need, None, None) == INVALID
+    assert lib.mmf_layer_workspace_size(ctypes.byref(L), 4, 1, ctypes.byref(sz)) == OK
+    assert lib.mmf_layer_decode_step(ctypes.byref(L), FAKE, FAKE, 0, 4, FAKE, FAKE, sz.value - 256, None, None) == WORKSPACE
+
+
+def test_workspace_grows_with_tokens(lib):
+    L = _layer()
+    sizes = []
+    for t in (1, 16, 256):
+        sz = ctypes.c_size_t(0)
+        assert lib.mmf_layer_workspace_size(ctypes.byref(L), 2, t, ctypes.byref(sz)) == OK
+        sizes.append(sz.value)
+    assert sizes[0] < sizes[1] < sizes[2]
+    # distinct i/f/g gains need three quantised copies of x
+    L2 = _layer()
+    L2.f.norm_w = FAKE + 8192
+    sz2 = ctypes.c_size_t(0)
+    assert lib.mmf_layer_workspace_size(ctypes.byref(L2), 2, 256, ctypes.byref(sz2)) == OK
+    assert sz2.value > sizes[2]
