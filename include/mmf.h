@@ -208,6 +208,33 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
                                  int64_t b, float *h, void *ws, size_t ws_bytes,
                                  const mmf_layer_probe *probe, hipStream_t stream);
 
+/*
+ * Measurement support (not part of the computation). While enabled on a
+ * thread, every kernel launch made by the entry points above on that thread
+ * is bracketed by two HIP events recorded on the call's stream, and one
+ * record per launch is kept: the kernel variant, its shape and the event
+ * pair. This is the only part of the library that allocates (HIP events,
+ * host records), and it must stay off while a stream is being captured into
+ * a HIP graph.
+ *  mmf_timing_enable(1) clears earlier records; mmf_timing_enable(0) stops
+ *  recording and keeps the records.
+ *  mmf_timing_collect synchronises on the recorded events, copies up to
+ *  `capacity` records into `out` (which may be NULL when capacity is 0) and
+ *  returns the number recorded in *count.
+ *  kernel : variant name, e.g. "tgemm<gates>", "tgemv<resid>", "norm_quant".
+ *  m, n, k: rows, total output columns (all groups) and reduction length of a
+ *  contraction; rows and row length of a quantiser; b*t, d of a scan.
+ */
+typedef struct {
+    char kernel[40];
+    int64_t m;
+    int32_t n, k;
+    float ms;
+} mmf_kernel_timing;
+
+mmf_status mmf_timing_enable(int on);
+mmf_status mmf_timing_collect(mmf_kernel_timing *out, int32_t capacity, int32_t *count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmmf.so")
 __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
     "ternary_pack", "bitlinear_fwd", "hgrn_scan_fwd", "layer_fwd", "layer_decode_step",
-    "layer_workspace_size", "last_path", "last_error", "SCAN_MODES",
+    "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
 ]
 
 # Every entry point declared in include/mmf.h.
@@ -28,6 +28,7 @@ SYMBOLS = [
     "mmf_bitlinear_workspace_size", "mmf_bitlinear_fwd",
     "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd",
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
+    "mmf_timing_enable", "mmf_timing_collect",
 ]
 
 SCAN_MODES = {"auto": 0, "recurrent": 1, "chunk": 2}
@@ -56,6 +57,10 @@ class CLayerWeights(ctypes.Structure):
 
 PROBE_FIELDS = ["acc_ifg", "f", "xt", "g", "h", "u", "codes_u", "scale_u", "acc_o", "x1",
                 "codes_x1", "scale_x1", "acc_gate", "z", "codes_z", "scale_z", "acc_down"]
+
+
+class CKernelTiming(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char * 40), ("m", I64), ("n", I32), ("k", I32), ("ms", F32)]
 
 
 class CLayerProbe(ctypes.Structure):
@@ -87,6 +92,8 @@ def load():
                                   ctypes.c_int, P, SZ, ctypes.POINTER(CLayerProbe), P]
     lib.mmf_layer_decode_step.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, P, P, SZ,
                                           ctypes.POINTER(CLayerProbe), P]
+    lib.mmf_timing_enable.argtypes = [ctypes.c_int]
+    lib.mmf_timing_collect.argtypes = [ctypes.POINTER(CKernelTiming), I32, ctypes.POINTER(I32)]
     for name in SYMBOLS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -99,6 +106,21 @@ def last_error() -> str:
 
 def last_path() -> str:
     return load().mmf_last_path().decode()
+
+
+def timing_enable(on: bool = True):
+    """Bracket every kernel launch of this thread's library calls with HIP events (measurement only)."""
+    _check(load().mmf_timing_enable(1 if on else 0))
+
+
+def timing_collect() -> list:
+    """[(kernel, m, n, k, ms)] for every launch recorded since timing_enable(True)."""
+    lib = load()
+    count = I32(0)
+    _check(lib.mmf_timing_collect(None, 0, ctypes.byref(count)))
+    recs = (CKernelTiming * max(count.value, 1))()
+    _check(lib.mmf_timing_collect(recs, count.value, ctypes.byref(count)))
+    return [(r.kernel.decode(), r.m, r.n, r.k, r.ms) for r in recs[:count.value]]
 
 
 def _check(status: int):

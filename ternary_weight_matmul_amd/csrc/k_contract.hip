@@ -10,8 +10,8 @@
 // computes sum c*q; sum t*q = sum c*q - sum q is exact (|acc| < 2^24), with
 // sum q a by-product of the activation quantiser.
 //
-// Prefill (m > 64): 128 x (NG * 64 * JN) output tiles, four waves of 64 x
-// (NG * 32 * JN), v_mfma_i32_32x32x32_i8, K staged 128 bytes at a time through
+// Prefill (m > 64): 128 x (NG * 64 * JN) output tiles (JN = 4, 2, 1 for one,
+// two, three groups), four waves of 64 x (NG * 32 * JN), v_mfma_i32_32x32x32_i8, K staged 128 bytes at a time through
 // double-buffered LDS (activation tile XOR-swizzled, packed weights padded to
 // a 48-byte row stride: both conflict-free for 16-lane groups). Tiles are
 // assigned XCD-major so that the workgroups of one XCD share activation rows
@@ -26,58 +26,9 @@
 // "HGRNBitBlock 的結構").
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "epilogue.hpp"
 
 namespace mmf {
-
-template <typename T>
-__device__ __forceinline__ float load_any(const void *p, ActType t, int64_t i) {
-    return t == ACT_F32 ? static_cast<const float *>(p)[i] : bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
-}
-__device__ __forceinline__ void store_any(void *p, ActType t, int64_t i, float v) {
-    if (t == ACT_F32)
-        static_cast<float *>(p)[i] = v;
-    else
-        static_cast<uint16_t *>(p)[i] = f32_to_bf16(v);
-}
-
-__device__ __forceinline__ float weight_sw(const float *mu) { return __fdiv_rn(1.0f, fmaxf(*mu, 1e-5f)); }
-
-// raw[g] = sum c*q of output (m, c) for group g. Corrects by sum q, dequantises
-// with 1 / (s * sw) and applies the epilogue.
-template <int EPI, int NG>
-__device__ __forceinline__ void epilogue(const ContractArgs &p, const float (&sw)[3], int64_t m, int c,
-                                         const int32_t (&raw)[NG]) {
-    float y[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int32_t v = raw[g] - p.sumq[g][m];
-        y[g] = (float)v * __builtin_amdgcn_rcpf(p.s[g][m] * sw[g]);
-        if (p.acc_probe) p.acc_probe[m * (int64_t)(NG * p.nc) + (int64_t)g * p.nc + c] = v;
-    }
-    const int64_t o = m * (int64_t)p.nc + c;
-    if constexpr (EPI == EPI_LINEAR) {
-        store_any(p.out0, p.out_type, o, y[0]);
-    } else if constexpr (EPI == EPI_RESID) {
-        const float r = load_any<float>(p.res, p.res_type, o);
-        store_any(p.out0, p.out_type, o, r + y[0]);
-    } else if constexpr (EPI == EPI_GATES) {
-        const float f = sigmoid_fast(y[1]);
-        const float xt = (1.0f - f) * silu_fast(y[0]);
-        static_cast<float *>(p.out0)[o] = f;
-        static_cast<float *>(p.out1)[o] = xt;
-        static_cast<float *>(p.out2)[o] = y[2];
-    } else if constexpr (EPI == EPI_GATES_STEP) {
-        const float f = sigmoid_fast(y[1]);
-        const float xt = (1.0f - f) * silu_fast(y[0]);
-        float *h = static_cast<float *>(p.out0);
-        h[o] = f * h[o] + xt;
-        static_cast<float *>(p.out1)[o] = y[2];
-        if (p.out2) static_cast<float *>(p.out2)[o] = f;
-        if (p.out3) static_cast<float *>(p.out3)[o] = xt;
-    } else if constexpr (EPI == EPI_GLU) {
-        static_cast<float *>(p.out0)[o] = silu_fast(y[0]) * y[1];
-    }
-}
 
 // ----------------------------------------------------------------------------
 // Prefill: tiled int8 MFMA contraction
@@ -236,44 +187,58 @@ __global__ __launch_bounds__(256, 2) void tgemm_kernel(const ContractArgs p, con
         __syncthreads();
     }
 
-    float sw[3];
+    float sw[NG];
 #pragma unroll
-    for (int g = 0; g < 3; ++g) sw[g] = g < NG ? weight_sw(p.mu[g]) : 1.0f;
+    for (int g = 0; g < NG; ++g) sw[g] = weight_sw(p.mu[g]);
+    // per output row: the row's dequant factors once, then its JN column subtiles
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < JN; ++j) {
-            const int c = n0 + wn * (32 * JN) + j * 32 + lr;
+        for (int r = 0; r < 16; ++r) {
+            const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+            if (m >= M) continue;
+            int32_t sq[NG];
+            float dq[NG];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-                if (m < M && c < p.nc) {
-                    int32_t raw[NG];
+            for (int g = 0; g < NG; ++g) {
+                sq[g] = p.sumq[g][m];
+                dq[g] = __builtin_amdgcn_rcpf(p.s[g][m] * sw[g]);
+            }
 #pragma unroll
-                    for (int g = 0; g < NG; ++g) raw[g] = acc[i][g][j][r];
-                    epilogue<EPI, NG>(p, sw, m, c, raw);
+            for (int j = 0; j < JN; ++j) {
+                const int c = n0 + wn * (32 * JN) + j * 32 + lr;
+                if (c < p.nc) {
+                    int32_t v[NG];
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) v[g] = acc[i][g][j][r] - sq[g];
+                    epilogue_vals<EPI, NG>(p, m, c, v, dq);
                 }
             }
         }
 }
 
 // ----------------------------------------------------------------------------
-// Decode: m <= 64 rows, weight streaming
+// Decode: m <= 64 rows, latency-bound weight streaming
 // ----------------------------------------------------------------------------
-template <int NG, int MB, bool SHARED_A, int EPI>
-__global__ __launch_bounds__(256) void tgemv_kernel(const ContractArgs p) {
+// One workgroup per 16 output channels (x NG groups). K is cut into slices of
+// 4*WPL words; one wave per slice (up to 16 waves; further slices loop). A lane
+// (column lc, word group lg) owns WPL consecutive words of its column in the
+// slice and issues every load of the slice -- weights as 16-byte runs,
+// activation codes of its row block as 16-byte chunks -- before its first
+// MFMA, so a GEMV costs about one memory round trip. Wave partial sums are
+// combined with LDS integer atomics (exact, order-free).
+template <int NG, int MB, bool SHARED_A, int EPI, int WPL>
+__global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const int nslices) {
     constexpr int NA = SHARED_A ? 1 : NG;
-    __shared__ i32x4 red[3][MB][NG][64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ int32_t red[MB * NG * 256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int lc = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int K = p.k, KW = K >> 4;
     const int64_t M = p.m;
-    const int per_wave = (KW + 3) / 4;
-    const int w0 = wave * per_wave;
-    const int w1 = w0 + per_wave < KW ? w0 + per_wave : KW;
-    const int steps = (per_wave + 3) / 4;
     const int gn = n0 + lc;
+    const bool bvec = (KW & 3) == 0;
+    for (int i = tid; i < MB * NG * 256; i += blockDim.x) red[i] = 0;
 
     i32x4 acc[MB][NG];
 #pragma unroll
@@ -281,53 +246,63 @@ __global__ __launch_bounds__(256) void tgemv_kernel(const ContractArgs p) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) acc[mb][g] = i32x4{};
 
-    for (int s = 0; s < steps; ++s) {
-        const int wi = w0 + 4 * s + lg;
-        const bool valid = wi < w1;
-        i32x4 b[NG];
+    for (int sl = wave; sl < nslices; sl += nw) {
+        const int w0 = sl * 4 * WPL + lg * WPL;
+        uint32_t bw[NG][WPL];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            const uint32_t w = (valid && gn < p.nc) ? p.B[g][(int64_t)gn * KW + wi] : 0u;
-            b[g] = decode_word(w);
+            const uint32_t *src = p.B[g] + (int64_t)gn * KW + w0;
+            if (gn < p.nc && bvec && w0 + WPL <= KW) {
+#pragma unroll
+                for (int q = 0; q < WPL / 4; ++q) {
+                    const uint4 v = reinterpret_cast<const uint4 *>(src)[q];
+                    bw[g][4 * q] = v.x; bw[g][4 * q + 1] = v.y; bw[g][4 * q + 2] = v.z; bw[g][4 * q + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < WPL; ++j) bw[g][j] = (gn < p.nc && w0 + j < KW) ? src[j] : 0u;
+            }
         }
+        i32x4 a[MB][NA][WPL];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int64_t row = mb * 16 + lc;
-            i32x4 a[NA];
 #pragma unroll
-            for (int q = 0; q < NA; ++q)
-                a[q] = (valid && row < M) ? *reinterpret_cast<const i32x4 *>(p.A[q] + row * K + 16 * wi) : i32x4{};
+            for (int q = 0; q < NA; ++q) {
+                const i32x4 *src = reinterpret_cast<const i32x4 *>(p.A[q] + row * K) + w0;
 #pragma unroll
-            for (int g = 0; g < NG; ++g)
-                acc[mb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[SHARED_A ? 0 : g], b[g], acc[mb][g], 0, 0, 0);
+                for (int j = 0; j < WPL; ++j) a[mb][q][j] = (row < M && w0 + j < KW) ? src[j] : i32x4{};
+            }
         }
-    }
-    if (wave > 0) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int j = 0; j < WPL; ++j)
 #pragma unroll
-            for (int g = 0; g < NG; ++g) red[wave - 1][mb][g][lane] = acc[mb][g];
+            for (int g = 0; g < NG; ++g) {
+                const i32x4 b = decode_word(bw[g][j]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][SHARED_A ? 0 : g][j], b, acc[mb][g], 0, 0, 0);
+            }
     }
     __syncthreads();
-    if (wave != 0) return;
-    float sw[3];
 #pragma unroll
-    for (int g = 0; g < 3; ++g) sw[g] = g < NG ? weight_sw(p.mu[g]) : 1.0f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
-            for (int w = 0; w < 3; ++w) acc[mb][g] += red[w][mb][g][lane];
+            for (int i = 0; i < 4; ++i) atomicAdd(&red[(mb * NG + g) * 256 + (4 * lg + i) * 16 + lc], acc[mb][g][i]);
+    __syncthreads();
+    float sw[3];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t m = mb * 16 + lg * 4 + r;
-            if (m < M && gn < p.nc) {
-                int32_t raw[NG];
+    for (int g = 0; g < 3; ++g) sw[g] = g < NG ? weight_sw(p.mu[g]) : 1.0f;
+    for (int idx = tid; idx < MB * 256; idx += blockDim.x) {
+        const int mb = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+        const int64_t m = mb * 16 + r;
+        if (m < M && n0 + c < p.nc) {
+            int32_t raw[NG];
 #pragma unroll
-                for (int g = 0; g < NG; ++g) raw[g] = acc[mb][g][r];
-                epilogue<EPI, NG>(p, sw, m, gn, raw);
-            }
+            for (int g = 0; g < NG; ++g) raw[g] = red[(mb * NG + g) * 256 + r * 16 + c];
+            epilogue<EPI, NG>(p, sw, m, n0 + c, raw);
         }
     }
 }
@@ -354,22 +329,35 @@ static void run_gemm(const ContractArgs &a, hipStream_t st) {
     tgemm_kernel<NG, JN, SH, EPI><<<(unsigned)(tiles_m * tiles_n), 256, 0, st>>>(a, tiles_n);
 }
 
+template <int NG, int MB, bool SH, int EPI, int WPL>
+static void run_gemv_mb(const ContractArgs &a, hipStream_t st) {
+    const int kw = a.k >> 4;
+    const int nslices = (kw + 4 * WPL - 1) / (4 * WPL);
+    const int waves = nslices < 16 ? nslices : 16;
+    tgemv_kernel<NG, MB, SH, EPI, WPL><<<(unsigned)((a.nc + 15) / 16), waves * 64, 0, st>>>(a, nslices);
+}
+
 template <int NG, bool SH, int EPI>
 static void run_gemv(const ContractArgs &a, hipStream_t st) {
-    const unsigned grid = (unsigned)((a.nc + 15) / 16);
-    const int mb = (int)((a.m + 15) / 16);
-    switch (mb) {
-        case 1: tgemv_kernel<NG, 1, SH, EPI><<<grid, 256, 0, st>>>(a); break;
-        case 2: tgemv_kernel<NG, 2, SH, EPI><<<grid, 256, 0, st>>>(a); break;
-        case 3: tgemv_kernel<NG, 3, SH, EPI><<<grid, 256, 0, st>>>(a); break;
-        default: tgemv_kernel<NG, 4, SH, EPI><<<grid, 256, 0, st>>>(a); break;
+    constexpr int NA = SH ? 1 : NG;
+    switch ((int)((a.m + 15) / 16)) {
+        case 1: run_gemv_mb<NG, 1, SH, EPI, (NA <= 2 ? 8 : 4)>(a, st); break;
+        case 2: run_gemv_mb<NG, 2, SH, EPI, (NA <= 1 ? 8 : 4)>(a, st); break;
+        case 3: run_gemv_mb<NG, 3, SH, EPI, 4>(a, st); break;
+        default: run_gemv_mb<NG, 4, SH, EPI, 4>(a, st); break;
     }
+}
+
+static bool use_gemv(int64_t m) { return m <= 64; }
+
+std::string contract_variant(int64_t m, EpiKind epi, bool shared_a) {
+    return std::string(use_gemv(m) ? "tgemv<" : "tgemm<") + epi_name(epi) + (shared_a ? "" : ",split_a") + ">";
 }
 
 hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a, hipStream_t st,
                            std::string *path) {
     if (a.m <= 0 || a.nc <= 0) return hipSuccess;
-    const bool gemv = a.m <= 64;
+    const bool gemv = use_gemv(a.m);
     if (gemv) {
         switch (epi) {
             case EPI_LINEAR: run_gemv<1, true, EPI_LINEAR>(a, st); break;
@@ -384,9 +372,9 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
         }
     } else {
         switch (epi) {
-            case EPI_LINEAR: run_gemm<1, 2, true, EPI_LINEAR>(a, st); break;
-            case EPI_RESID: run_gemm<1, 2, true, EPI_RESID>(a, st); break;
-            case EPI_GLU: run_gemm<2, 1, true, EPI_GLU>(a, st); break;
+            case EPI_LINEAR: run_gemm<1, 4, true, EPI_LINEAR>(a, st); break;
+            case EPI_RESID: run_gemm<1, 4, true, EPI_RESID>(a, st); break;
+            case EPI_GLU: run_gemm<2, 2, true, EPI_GLU>(a, st); break;
             case EPI_GATES:
                 if (shared_a) run_gemm<3, 1, true, EPI_GATES>(a, st); else run_gemm<3, 1, false, EPI_GATES>(a, st);
                 break;
@@ -396,9 +384,7 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
         }
     }
     (void)ng;
-    if (path)
-        *path += std::string(gemv ? "tgemv_mfma16x16x64<" : "tgemm_mfma32x32x32<") + epi_name(epi) +
-                 (shared_a ? "" : ",split_a") + ">;";
+    if (path) *path += contract_variant(a.m, epi, shared_a) + ";";
     return hipGetLastError();
 }
 

@@ -118,6 +118,92 @@ __global__ __launch_bounds__(256) void norm_quant_long_kernel(const T *__restric
     }
 }
 
+// Few rows (decode): one 256-thread workgroup per row; the four waves'
+// partial reductions meet in LDS.
+__device__ __forceinline__ double block_sum(double v, double *sh) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+__device__ __forceinline__ float block_max(float v, float *sh) {
+    v = wave_max(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+__device__ __forceinline__ int block_sum_int(int v, int *sh) {
+    v = wave_sum_int(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void norm_quant_row_kernel(const T *__restrict__ x, int64_t m, int k,
+                                                             const float *__restrict__ gain, float eps,
+                                                             int8_t *__restrict__ q, float *__restrict__ s,
+                                                             int32_t *__restrict__ sumq) {
+    __shared__ double shd[4];
+    __shared__ float shf[4];
+    __shared__ int shi[4];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nch = k >> 2;
+    const T *xr = x + row * (int64_t)k;
+    float v[NV][4];
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
+        float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < nch) t = load_act4(xr, 4 * (int64_t)c);
+        v[j][0] = t.x; v[j][1] = t.y; v[j][2] = t.z; v[j][3] = t.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += (double)v[j][e] * (double)v[j][e];
+    }
+    const float r = rms_factor(block_sum(ss, shd), k, eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
+        if (c < nch) {
+            float4 gv = gain ? *reinterpret_cast<const float4 *>(gain + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
+            const float ge[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float y = __fmul_rn(v[j][e], r);
+                if (gain) y = __fmul_rn(y, ge[e]);
+                v[j][e] = y;
+                amax = fmaxf(amax, fabsf(y));
+            }
+        }
+    }
+    const float sc = quant_scale(block_max(amax, shf));
+    int tot = 0;
+    uint32_t *qr = reinterpret_cast<uint32_t *>(q + row * (int64_t)k);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
+        if (c < nch) {
+            const int a0 = quant_code(v[j][0], sc), a1 = quant_code(v[j][1], sc);
+            const int a2 = quant_code(v[j][2], sc), a3 = quant_code(v[j][3], sc);
+            tot += a0 + a1 + a2 + a3;
+            qr[c] = pack_codes4(a0, a1, a2, a3);
+        }
+    }
+    tot = block_sum_int(tot, shi);
+    if (tid == 0) {
+        s[row] = sc;
+        sumq[row] = tot;
+    }
+}
+
+constexpr int kFewRows = 2048;  // below this many rows a row gets a whole workgroup
+
 constexpr int kMaxCachedChunks = 32;  // 64 lanes * 32 chunks * 4 = 8192 elements per row
 
 static int chunk_bucket(int k) {
@@ -127,12 +213,30 @@ static int chunk_bucket(int k) {
     return b;
 }
 
+// float4 chunks per thread when a 256-thread workgroup owns the row
+static int block_bucket(int k) {
+    const int nch = (k / 4 + 255) / 256;
+    int b = 1;
+    while (b < nch) b *= 2;
+    return b;
+}
+
 template <typename T>
 static void norm_quant_dispatch(const T *x, int64_t m, int k, const float *gain, float eps, int8_t *q,
                                 float *s, int32_t *sumq, hipStream_t st, std::string *path) {
+    const char *tn = sizeof(T) == 4 ? "f32" : "bf16";
+    const int nvb = block_bucket(k);
+    if (m < kFewRows && nvb <= 8) {
+        switch (nvb) {
+#define MMF_NQB(NV) case NV: norm_quant_row_kernel<T, NV><<<(unsigned)m, 256, 0, st>>>(x, m, k, gain, eps, q, s, sumq); break;
+            MMF_NQB(1) MMF_NQB(2) MMF_NQB(4) MMF_NQB(8)
+#undef MMF_NQB
+        }
+        if (path) *path += std::string("norm_quant_row<") + tn + "," + std::to_string(nvb) + ">;";
+        return;
+    }
     const dim3 grid((unsigned)((m + 3) / 4)), block(256);
     const int nv = chunk_bucket(k);
-    const char *tn = sizeof(T) == 4 ? "f32" : "bf16";
     if (nv > kMaxCachedChunks) {
         norm_quant_long_kernel<T><<<grid, block, 0, st>>>(x, m, k, gain, eps, q, s, sumq);
         if (path) *path += std::string("norm_quant_long<") + tn + ">;";
@@ -241,10 +345,105 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restric
     }
 }
 
+// Few rows (decode): one 256-thread workgroup per row.
+template <int NV>
+__global__ __launch_bounds__(256) void gnorm_quant_row_kernel(const float *__restrict__ h, const float *__restrict__ g,
+                                                              int64_t m, int d, const float *__restrict__ gnw,
+                                                              const float *__restrict__ ogain, float eps,
+                                                              int8_t *__restrict__ q, float *__restrict__ s,
+                                                              int32_t *__restrict__ sumq, float *__restrict__ u_out) {
+    __shared__ double shd[2][4];
+    __shared__ float shf[4];
+    __shared__ int shi[4];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nch = d >> 2;
+    const float *hr = h + row * (int64_t)d;
+    const float *gr = g + row * (int64_t)d;
+    float u[NV][4], gs[NV][4];
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (c < nch) {
+            a = *reinterpret_cast<const float4 *>(hr + 4 * c);
+            b = *reinterpret_cast<const float4 *>(gr + 4 * c);
+        }
+        u[j][0] = a.x; u[j][1] = a.y; u[j][2] = a.z; u[j][3] = a.w;
+        gs[j][0] = silu_fast(b.x); gs[j][1] = silu_fast(b.y); gs[j][2] = silu_fast(b.z); gs[j][3] = silu_fast(b.w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += (double)u[j][e] * (double)u[j][e];
+    }
+    const float rh = rms_factor(block_sum(ss, shd[0]), d, eps);
+    double su = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
+        float4 wv = (gnw && c < nch) ? *reinterpret_cast<const float4 *>(gnw + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
+        const float we[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float y = u[j][e] * rh;
+            if (gnw) y = y * we[e];
+            y = y * gs[j][e];
+            u[j][e] = y;
+            su += (double)y * (double)y;
+        }
+        if (u_out && c < nch)
+            *reinterpret_cast<float4 *>(u_out + row * (int64_t)d + 4 * c) = make_float4(u[j][0], u[j][1], u[j][2], u[j][3]);
+    }
+    const float r = rms_factor(block_sum(su, shd[1]), d, eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
+        if (c < nch) {
+            float4 gv = ogain ? *reinterpret_cast<const float4 *>(ogain + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
+            const float ge[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float y = __fmul_rn(u[j][e], r);
+                if (ogain) y = __fmul_rn(y, ge[e]);
+                u[j][e] = y;
+                amax = fmaxf(amax, fabsf(y));
+            }
+        }
+    }
+    const float sc = quant_scale(block_max(amax, shf));
+    int tot = 0;
+    uint32_t *qr = reinterpret_cast<uint32_t *>(q + row * (int64_t)d);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
+        if (c < nch) {
+            const int a0 = quant_code(u[j][0], sc), a1 = quant_code(u[j][1], sc);
+            const int a2 = quant_code(u[j][2], sc), a3 = quant_code(u[j][3], sc);
+            tot += a0 + a1 + a2 + a3;
+            qr[c] = pack_codes4(a0, a1, a2, a3);
+        }
+    }
+    tot = block_sum_int(tot, shi);
+    if (tid == 0) {
+        s[row] = sc;
+        sumq[row] = tot;
+    }
+}
+
 hipError_t launch_gnorm_quant(const float *h, const float *g, int64_t m, int d, const float *g_norm_w,
                               const float *o_gain, float eps, int8_t *q, float *s, int32_t *sumq,
                               float *u_out, hipStream_t stream, std::string *path) {
     if (m <= 0) return hipSuccess;
+    const int nvb = block_bucket(d);
+    if (m < kFewRows && nvb <= 8) {
+        switch (nvb) {
+#define MMF_GQB(NV) case NV: gnorm_quant_row_kernel<NV><<<(unsigned)m, 256, 0, stream>>>(h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
+            MMF_GQB(1) MMF_GQB(2) MMF_GQB(4) MMF_GQB(8)
+#undef MMF_GQB
+        }
+        if (path) *path += "gnorm_quant_row<" + std::to_string(nvb) + ">;";
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((m + 3) / 4)), block(256);
     const int nv = chunk_bucket(d);
     switch (nv) {

@@ -53,6 +53,31 @@ struct ContractArgs {
 hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a,
                            hipStream_t stream, std::string *path);
 
+// Variant name of the kernel launch_contract picks, e.g. "tgemm<gates>".
+std::string contract_variant(int64_t m, EpiKind epi, bool shared_a);
+
+// Fused decode stage (m <= 16): quantise the input rows inside the kernel,
+// then the contraction and its epilogue. All groups share the quantised input.
+enum QuantIn { QIN_F32 = 0, QIN_BF16 = 1, QIN_GNORM = 2 };
+constexpr int kDecMaxK = 8192;
+
+struct DecodeArgs {
+    ContractArgs c;       // B, mu, m, nc, k, outputs, res, acc_probe (A / s / sumq unused)
+    const void *qin;      // quantiser input rows [m][k]: activations, or h for QIN_GNORM
+    const float *g;       // QIN_GNORM: g_proj output [m][k]
+    const float *gnw;     // QIN_GNORM: g_norm gain [k] or NULL
+    const float *gain;    // quantiser RMSNorm gain [k] or NULL
+    float eps;
+    int8_t *codes_out;    // optional copy of the codes [m][k]
+    float *scale_out;     // optional copy of the scales [m]
+    float *u_out;         // optional g_norm output [m][k] (QIN_GNORM)
+};
+
+bool decode_fused_ok(int64_t m, int k);
+bool decode_fused_supports(int k, QuantIn qin);  // shape limits of the in-kernel quantiser
+hipError_t launch_decode_fused(const DecodeArgs &a, EpiKind epi, QuantIn qin, hipStream_t stream,
+                               std::string *path);
+
 // HGRN scan. chunks == 1 means the recurrent (sequential) kernel.
 size_t scan_workspace_bytes(int64_t b, int64_t d, int chunks);
 int scan_pick_chunks(int64_t b, int64_t t, int64_t d, int mode);

@@ -11,6 +11,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
+#include <cstring>
 
 #include "mmf.h"
 #include "launch.hpp"
@@ -39,6 +41,72 @@ mmf_status hip_status(hipError_t e, const char *what) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- optional per-launch timing (mmf_timing_enable) ----------------------------
+struct TimingRec {
+    std::string kernel;
+    int64_t m;
+    int n, k;
+    hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimingRec> g_recs;
+thread_local std::vector<hipEvent_t> g_events;
+thread_local size_t g_events_used = 0;
+
+hipEvent_t timing_event() {
+    if (g_events_used == g_events.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        g_events.push_back(e);
+    }
+    return g_events[g_events_used++];
+}
+
+template <class F>
+hipError_t timed(const std::string &kernel, int64_t m, int n, int k, hipStream_t st, F &&launch) {
+    if (!g_timing) return launch();
+    hipEvent_t a = timing_event(), b = timing_event();
+    if (!a || !b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, st);
+    if (e != hipSuccess) return e;
+    if ((e = launch()) != hipSuccess) return e;
+    if ((e = hipEventRecord(b, st)) != hipSuccess) return e;
+    g_recs.push_back(TimingRec{kernel, m, n, k, a, b});
+    return hipSuccess;
+}
+
+hipError_t t_norm_quant(const void *x, ActType xt, int64_t m, int k, const float *gain, float eps, int8_t *q,
+                        float *s, int32_t *sumq, hipStream_t st, std::string *path) {
+    if (m <= 0) return hipSuccess;
+    return timed("norm_quant", m, k, k, st,
+                 [&] { return launch_norm_quant(x, xt, m, k, gain, eps, q, s, sumq, st, path); });
+}
+
+hipError_t t_gnorm_quant(const float *h, const float *g, int64_t m, int d, const float *gw, const float *og,
+                         float eps, int8_t *q, float *s, int32_t *sumq, float *u, hipStream_t st, std::string *path) {
+    if (m <= 0) return hipSuccess;
+    return timed("gnorm_quant", m, d, d, st,
+                 [&] { return launch_gnorm_quant(h, g, m, d, gw, og, eps, q, s, sumq, u, st, path); });
+}
+
+hipError_t t_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared, hipStream_t st, std::string *path) {
+    if (a.m <= 0 || a.nc <= 0) return hipSuccess;
+    return timed(contract_variant(a.m, epi, shared), a.m, ng * a.nc, a.k, st,
+                 [&] { return launch_contract(a, epi, ng, shared, st, path); });
+}
+
+hipError_t t_decode(const DecodeArgs &a, EpiKind epi, QuantIn qin, int ng, hipStream_t st, std::string *path) {
+    static const char *names[] = {"linear", "resid", "gates", "gates_step", "glu"};
+    return timed(std::string("decode_fused<") + names[epi] + ">", a.c.m, ng * a.c.nc, a.c.k, st,
+                 [&] { return launch_decode_fused(a, epi, qin, st, path); });
+}
+
+hipError_t t_scan(const float *x, const float *f, const float *h0, float *h, float *hl, int64_t b, int64_t t,
+                  int64_t d, int chunks, void *ws, hipStream_t st, std::string *path) {
+    return timed(chunks > 1 ? "scan_chunk" : "scan_recurrent", b * t, (int)d, (int)d, st,
+                 [&] { return launch_scan(x, f, h0, h, hl, b, t, d, chunks, ws, st, path); });
+}
 
 constexpr int kMaxK = 65536;       // |sum t*q| <= 128*k stays exact in binary32
 constexpr int kMaxNormRow = 8192;  // g_norm keeps a row in registers
@@ -165,7 +233,7 @@ hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_
     hipError_t e;
     int8_t *cu = pick(pr ? pr->codes_u : nullptr, L.codes_b);
     float *su = pick(pr ? pr->scale_u : nullptr, L.s_b);
-    e = launch_gnorm_quant(h, g, m, d, w->g_norm_w, w->o.norm_w, eps, cu, su, L.sq_b, pr ? pr->u : nullptr, st, path);
+    e = t_gnorm_quant(h, g, m, d, w->g_norm_w, w->o.norm_w, eps, cu, su, L.sq_b, pr ? pr->u : nullptr, st, path);
     if (e != hipSuccess) return e;
 
     float *x1 = pick(pr ? pr->x1 : nullptr, L.x1);
@@ -174,11 +242,11 @@ hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_
     co.m = m; co.nc = d; co.k = d;
     co.out0 = x1; co.res = x; co.res_type = act(actt); co.out_type = ACT_F32;
     co.acc_probe = pr ? pr->acc_o : nullptr;
-    if ((e = launch_contract(co, EPI_RESID, 1, true, st, path)) != hipSuccess) return e;
+    if ((e = t_contract(co, EPI_RESID, 1, true, st, path)) != hipSuccess) return e;
 
     int8_t *c1 = pick(pr ? pr->codes_x1 : nullptr, L.codes_b);
     float *s1 = pick(pr ? pr->scale_x1 : nullptr, L.s_b);
-    if ((e = launch_norm_quant(x1, ACT_F32, m, d, w->gate.norm_w, eps, c1, s1, L.sq_b, st, path)) != hipSuccess) return e;
+    if ((e = t_norm_quant(x1, ACT_F32, m, d, w->gate.norm_w, eps, c1, s1, L.sq_b, st, path)) != hipSuccess) return e;
 
     float *z = pick(pr ? pr->z : nullptr, L.z);
     ContractArgs cg{};
@@ -189,18 +257,18 @@ hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_
     cg.m = m; cg.nc = inner; cg.k = d;
     cg.out0 = z; cg.out_type = ACT_F32;
     cg.acc_probe = pr ? pr->acc_gate : nullptr;
-    if ((e = launch_contract(cg, EPI_GLU, 2, true, st, path)) != hipSuccess) return e;
+    if ((e = t_contract(cg, EPI_GLU, 2, true, st, path)) != hipSuccess) return e;
 
     int8_t *cz = pick(pr ? pr->codes_z : nullptr, L.codes_b);
     float *sz = pick(pr ? pr->scale_z : nullptr, L.s_b);
-    if ((e = launch_norm_quant(z, ACT_F32, m, inner, w->down.norm_w, eps, cz, sz, L.sq_b, st, path)) != hipSuccess) return e;
+    if ((e = t_norm_quant(z, ACT_F32, m, inner, w->down.norm_w, eps, cz, sz, L.sq_b, st, path)) != hipSuccess) return e;
 
     ContractArgs cd{};
     for (int q = 0; q < 3; ++q) { cd.A[q] = cz; cd.s[q] = sz; cd.sumq[q] = L.sq_b; cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
     cd.m = m; cd.nc = d; cd.k = inner;
     cd.out0 = out; cd.out_type = act(actt); cd.res = x1; cd.res_type = ACT_F32;
     cd.acc_probe = pr ? pr->acc_down : nullptr;
-    return launch_contract(cd, EPI_RESID, 1, true, st, path);
+    return t_contract(cd, EPI_RESID, 1, true, st, path);
 }
 
 // Quantise x for i/f/g (once when their gains coincide) and fill the contraction's A side.
@@ -214,7 +282,7 @@ hipError_t quant_ifg(const mmf_layer_weights *w, const void *x, mmf_dtype actt, 
     for (int q = 0; q < nq; ++q) {
         codes[q] = pick(pr ? pr->codes_x[q] : nullptr, L.codes_x[q]);
         scales[q] = pick(pr ? pr->scale_x[q] : nullptr, L.s_x[q]);
-        hipError_t e = launch_norm_quant(x, act(actt), m, w->d, gains[q], w->eps, codes[q], scales[q], L.sq_x[q], st, path);
+        hipError_t e = t_norm_quant(x, act(actt), m, w->d, gains[q], w->eps, codes[q], scales[q], L.sq_x[q], st, path);
         if (e != hipSuccess) return e;
     }
     const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
@@ -229,6 +297,64 @@ hipError_t quant_ifg(const mmf_layer_weights *w, const void *x, mmf_dtype actt, 
     ca.m = m; ca.nc = w->d; ca.k = w->d;
     ca.acc_probe = pr ? pr->acc_ifg : nullptr;
     return hipSuccess;
+}
+
+// Decode step with at most 16 rows: four fused kernels, each quantising its
+// own input rows.
+hipError_t decode_fused_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b,
+                             float *h, const LayerWs &L, const mmf_layer_probe *pr, hipStream_t st, std::string *path) {
+    const int d = w->d, inner = w->inner;
+    hipError_t e;
+    float *g = pick(pr ? pr->g : nullptr, L.g);
+    DecodeArgs a{};
+    const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
+    for (int q = 0; q < 3; ++q) { a.c.B[q] = tw[q]->packed; a.c.mu[q] = tw[q]->mu; }
+    a.c.m = b; a.c.nc = d; a.c.k = d;
+    a.c.out0 = h; a.c.out1 = g; a.c.out_type = ACT_F32;
+    a.c.out2 = pr ? pr->f : nullptr;
+    a.c.out3 = pr ? pr->xt : nullptr;
+    a.c.acc_probe = pr ? pr->acc_ifg : nullptr;
+    a.qin = x; a.gain = w->i.norm_w; a.eps = w->eps;
+    a.codes_out = pr ? pr->codes_x[0] : nullptr;
+    a.scale_out = pr ? pr->scale_x[0] : nullptr;
+    if ((e = t_decode(a, EPI_GATES_STEP, actt == MMF_F32 ? QIN_F32 : QIN_BF16, 3, st, path)) != hipSuccess) return e;
+    if (pr && pr->h && (e = hipMemcpyAsync(pr->h, h, (size_t)b * d * sizeof(float), hipMemcpyDeviceToDevice, st)) != hipSuccess)
+        return e;
+
+    float *x1 = pick(pr ? pr->x1 : nullptr, L.x1);
+    a = DecodeArgs{};
+    for (int q = 0; q < 3; ++q) { a.c.B[q] = w->o.packed; a.c.mu[q] = w->o.mu; }
+    a.c.m = b; a.c.nc = d; a.c.k = d;
+    a.c.out0 = x1; a.c.out_type = ACT_F32; a.c.res = x; a.c.res_type = act(actt);
+    a.c.acc_probe = pr ? pr->acc_o : nullptr;
+    a.qin = h; a.g = g; a.gnw = w->g_norm_w; a.gain = w->o.norm_w; a.eps = w->eps;
+    a.codes_out = pr ? pr->codes_u : nullptr;
+    a.scale_out = pr ? pr->scale_u : nullptr;
+    a.u_out = pr ? pr->u : nullptr;
+    if ((e = t_decode(a, EPI_RESID, QIN_GNORM, 1, st, path)) != hipSuccess) return e;
+
+    float *z = pick(pr ? pr->z : nullptr, L.z);
+    a = DecodeArgs{};
+    for (int q = 0; q < 3; ++q) a.c.mu[q] = w->gate.mu;
+    a.c.B[0] = w->gate.packed;
+    a.c.B[1] = a.c.B[2] = w->gate.packed + (size_t)inner * (d / 16);
+    a.c.m = b; a.c.nc = inner; a.c.k = d;
+    a.c.out0 = z; a.c.out_type = ACT_F32;
+    a.c.acc_probe = pr ? pr->acc_gate : nullptr;
+    a.qin = x1; a.gain = w->gate.norm_w; a.eps = w->eps;
+    a.codes_out = pr ? pr->codes_x1 : nullptr;
+    a.scale_out = pr ? pr->scale_x1 : nullptr;
+    if ((e = t_decode(a, EPI_GLU, QIN_F32, 2, st, path)) != hipSuccess) return e;
+
+    a = DecodeArgs{};
+    for (int q = 0; q < 3; ++q) { a.c.B[q] = w->down.packed; a.c.mu[q] = w->down.mu; }
+    a.c.m = b; a.c.nc = d; a.c.k = inner;
+    a.c.out0 = out; a.c.out_type = act(actt); a.c.res = x1; a.c.res_type = ACT_F32;
+    a.c.acc_probe = pr ? pr->acc_down : nullptr;
+    a.qin = z; a.gain = w->down.norm_w; a.eps = w->eps;
+    a.codes_out = pr ? pr->codes_z : nullptr;
+    a.scale_out = pr ? pr->scale_z : nullptr;
+    return t_decode(a, EPI_RESID, QIN_F32, 1, st, path);
 }
 
 }  // namespace
@@ -294,14 +420,14 @@ mmf_status mmf_bitlinear_fwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
     bitlinear_plan(c, m, w->k, &B);
     int8_t *codes = codes_out ? codes_out : B.codes;
     float *s = scale_out ? scale_out : B.s;
-    hipError_t e = launch_norm_quant(x, act(xt), m, w->k, w->norm_w, eps, codes, s, B.sumq, stream, &path);
+    hipError_t e = t_norm_quant(x, act(xt), m, w->k, w->norm_w, eps, codes, s, B.sumq, stream, &path);
     if (e == hipSuccess) {
         ContractArgs a{};
         for (int q = 0; q < 3; ++q) { a.A[q] = codes; a.s[q] = s; a.sumq[q] = B.sumq; a.B[q] = w->packed; a.mu[q] = w->mu; }
         a.m = m; a.nc = w->n; a.k = w->k;
         a.out0 = y; a.out_type = act(yt);
         a.acc_probe = acc_out;
-        e = launch_contract(a, EPI_LINEAR, 1, true, stream, &path);
+        e = t_contract(a, EPI_LINEAR, 1, true, stream, &path);
     }
     mmf_status r = hip_status(e, "mmf_bitlinear_fwd");
     if (r == MMF_OK) g_path = path;
@@ -328,7 +454,7 @@ mmf_status mmf_hgrn_scan_fwd(const float *x, const float *f, const float *h0, fl
         return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
     std::string path;
     const int chunks = scan_pick_chunks(b, t, d, (int)mode);
-    mmf_status r = hip_status(launch_scan(x, f, h0, h, h_last, b, t, d, chunks, ws, stream, &path), "mmf_hgrn_scan_fwd");
+    mmf_status r = hip_status(t_scan(x, f, h0, h, h_last, b, t, d, chunks, ws, stream, &path), "mmf_hgrn_scan_fwd");
     if (r == MMF_OK) g_path = path;
     return r;
 }
@@ -362,7 +488,7 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
     std::string path;
     hipError_t e = hipSuccess;
     if (m == 0) {
-        e = launch_scan(nullptr, nullptr, h0, nullptr, h_last, b, 0, w->d, 1, nullptr, stream, &path);
+        e = t_scan(nullptr, nullptr, h0, nullptr, h_last, b, 0, w->d, 1, nullptr, stream, &path);
     } else {
         const int chunks = scan_pick_chunks(b, t, w->d, (int)mode);
         Carver c(ws);
@@ -377,9 +503,9 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
         float *h = pick(probe ? probe->h : nullptr, L.h);
         if (e == hipSuccess) {
             ca.out0 = f; ca.out1 = xt; ca.out2 = g; ca.out_type = ACT_F32;
-            e = launch_contract(ca, EPI_GATES, 3, shared, stream, &path);
+            e = t_contract(ca, EPI_GATES, 3, shared, stream, &path);
         }
-        if (e == hipSuccess) e = launch_scan(xt, f, h0, h, h_last, b, t, w->d, chunks, L.scan, stream, &path);
+        if (e == hipSuccess) e = t_scan(xt, f, h0, h, h_last, b, t, w->d, chunks, L.scan, stream, &path);
         if (e == hipSuccess) e = block_tail(w, x, out, actt, m, L, h, g, probe, stream, &path);
     }
     mmf_status r = hip_status(e, "mmf_layer_fwd");
@@ -401,7 +527,13 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
         return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
     std::string path;
     hipError_t e = hipSuccess;
-    if (b > 0) {
+    if (b > 0 && decode_fused_ok(b, w->d) && decode_fused_ok(b, w->inner) && shared_ifg(w) &&
+        decode_fused_supports(w->d, QIN_GNORM)) {
+        Carver c(ws);
+        LayerWs L;
+        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
+        e = decode_fused_step(w, x, out, actt, b, h, L, probe, stream, &path);
+    } else if (b > 0) {
         Carver c(ws);
         LayerWs L;
         layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
@@ -413,7 +545,7 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
             ca.out0 = h; ca.out1 = g; ca.out_type = ACT_F32;
             ca.out2 = probe ? probe->f : nullptr;
             ca.out3 = probe ? probe->xt : nullptr;
-            e = launch_contract(ca, EPI_GATES_STEP, 3, shared, stream, &path);
+            e = t_contract(ca, EPI_GATES_STEP, 3, shared, stream, &path);
         }
         if (e == hipSuccess && probe && probe->h)
             e = hipMemcpyAsync(probe->h, h, (size_t)b * w->d * sizeof(float), hipMemcpyDeviceToDevice, stream);
@@ -422,6 +554,37 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
     mmf_status r = hip_status(e, "mmf_layer_decode_step");
     if (r == MMF_OK) g_path = path;
     return r;
+}
+
+mmf_status mmf_timing_enable(int on) {
+    if (on) {
+        g_recs.clear();
+        g_events_used = 0;
+    }
+    g_timing = on != 0;
+    g_err.clear();
+    return MMF_OK;
+}
+
+mmf_status mmf_timing_collect(mmf_kernel_timing *out, int32_t capacity, int32_t *count) {
+    if (!count || capacity < 0 || (capacity > 0 && !out)) return fail(MMF_ERR_INVALID_ARG, "bad timing buffer");
+    *count = (int32_t)g_recs.size();
+    for (size_t i = 0; i < g_recs.size() && (int32_t)i < capacity; ++i) {
+        const TimingRec &r = g_recs[i];
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return hip_status(e, "mmf_timing_collect");
+        float ms = 0.0f;
+        if ((e = hipEventElapsedTime(&ms, r.start, r.stop)) != hipSuccess) return hip_status(e, "mmf_timing_collect");
+        mmf_kernel_timing &o = out[i];
+        std::memset(&o, 0, sizeof o);
+        std::strncpy(o.kernel, r.kernel.c_str(), sizeof(o.kernel) - 1);
+        o.m = r.m;
+        o.n = r.n;
+        o.k = r.k;
+        o.ms = ms;
+    }
+    g_err.clear();
+    return MMF_OK;
 }
 
 }  // extern "C"

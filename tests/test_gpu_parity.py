@@ -205,21 +205,37 @@ def test_layer_c1_end_to_end(gpu):
     assert rel < 1e-3, rel
 
 
-@pytest.mark.parametrize("b", [1, 16, 64, 65])
-def test_decode_step_stages(gpu, b):
+DECODE_CASES = [
+    # b, act, gains, d, inner, expected kernel family
+    (1, "bf16", "shared", 256, 512, "decode_fused"),
+    (5, "f32", None, 272, 1040, "decode_fused"),
+    (16, "bf16", "shared", 256, 512, "decode_fused"),
+    (16, "bf16", "distinct", 256, 512, "tgemv"),
+    (17, "f32", "shared", 256, 512, "tgemv"),
+    (64, "bf16", "shared", 256, 512, "tgemv"),
+    (65, "bf16", "shared", 256, 512, "tgemm"),
+    (3, "bf16", "shared", 256, 4160, "decode_fused"),      # down_proj K > 4096: streamed quantiser rows
+    (16, "bf16", None, 2048, 5632, "decode_fused"),        # the 1.3B decode shape
+    (8, "bf16", None, 2560, 6912, "tgemv"),                # 2.7B width: g_norm row beyond the fused limit
+]
+
+
+@pytest.mark.parametrize("b,act,gains,d,inner,family", DECODE_CASES)
+def test_decode_step_stages(gpu, b, act, gains, d, inner, family):
     import torch
     mmf = _mmf()
-    d, inner = 256, 512
-    L, P = make_pair(d, inner, 600 + b, gpu, "shared")
-    x = synth.activations((b, d), 601, "bf16")
+    L, P = make_pair(d, inner, 600 + b, gpu, gains)
+    x = synth.activations((b, d), 601, act)
     h0 = synth.activations((b, d), 602)
     hd = dev(h0, gpu)
-    probe = mmf.LayerProbe(b, d, inner, gpu)
-    out = mmf.layer_decode_step(P, bf16_tensor(x, gpu), hd, probe=probe)
+    shared = gains != "distinct"
+    probe = mmf.LayerProbe(b, d, inner, gpu, shared_ifg=shared)
+    xd = bf16_tensor(x, gpu) if act == "bf16" else dev(x, gpu)
+    out = mmf.layer_decode_step(P, xd, hd, probe=probe)
     torch.cuda.synchronize()
-    assert ("tgemv" if b <= 64 else "tgemm") in mmf.last_path()
+    assert family in mmf.last_path(), mmf.last_path()
     pr = probe.host()
-    check_layer_stages(L, x[:, None, :], h0, pr, host(out), "bf16")
+    check_layer_stages(L, x[:, None, :], h0, pr, host(out), act, shared=shared)
     assert np.array_equal(host(hd), pr["h"])
 
 
