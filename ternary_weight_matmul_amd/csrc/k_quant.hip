@@ -263,8 +263,8 @@ hipError_t launch_norm_quant(const void *x, ActType xt, int64_t m, int k, const 
 // ----------------------------------------------------------------------------
 // gnorm_quant: u = ((h * r_h) * g_norm_w) * SiLU(g), then the o_proj quantiser of u
 // ----------------------------------------------------------------------------
-template <int NV>
-__global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restrict__ h, const float *__restrict__ g,
+template <typename TG, int NV>
+__global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restrict__ h, const TG *__restrict__ g,
                                                           int64_t m, int d, const float *__restrict__ gnw,
                                                           const float *__restrict__ ogain, float eps,
                                                           int8_t *__restrict__ q, float *__restrict__ s,
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restric
     if (row >= m) return;
     const int nch = d >> 2;
     const float *hr = h + row * (int64_t)d;
-    const float *gr = g + row * (int64_t)d;
+    const TG *gr = g + row * (int64_t)d;
     float u[NV][4], gs[NV][4];
     double ss = 0.0;
 #pragma unroll
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restric
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
         if (c < nch) {
             a = *reinterpret_cast<const float4 *>(hr + 4 * c);
-            b = *reinterpret_cast<const float4 *>(gr + 4 * c);
+            b = load_act4(gr, 4 * (int64_t)c);
         }
         u[j][0] = a.x; u[j][1] = a.y; u[j][2] = a.z; u[j][3] = a.w;
         gs[j][0] = silu_fast(b.x); gs[j][1] = silu_fast(b.y); gs[j][2] = silu_fast(b.z); gs[j][3] = silu_fast(b.w);
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restric
 }
 
 // Few rows (decode): one 256-thread workgroup per row.
-template <int NV>
-__global__ __launch_bounds__(256) void gnorm_quant_row_kernel(const float *__restrict__ h, const float *__restrict__ g,
+template <typename TG, int NV>
+__global__ __launch_bounds__(256) void gnorm_quant_row_kernel(const float *__restrict__ h, const TG *__restrict__ g,
                                                               int64_t m, int d, const float *__restrict__ gnw,
                                                               const float *__restrict__ ogain, float eps,
                                                               int8_t *__restrict__ q, float *__restrict__ s,
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void gnorm_quant_row_kernel(const float *__res
     const int tid = threadIdx.x;
     const int nch = d >> 2;
     const float *hr = h + row * (int64_t)d;
-    const float *gr = g + row * (int64_t)d;
+    const TG *gr = g + row * (int64_t)d;
     float u[NV][4], gs[NV][4];
     double ss = 0.0;
 #pragma unroll
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void gnorm_quant_row_kernel(const float *__res
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
         if (c < nch) {
             a = *reinterpret_cast<const float4 *>(hr + 4 * c);
-            b = *reinterpret_cast<const float4 *>(gr + 4 * c);
+            b = load_act4(gr, 4 * (int64_t)c);
         }
         u[j][0] = a.x; u[j][1] = a.y; u[j][2] = a.z; u[j][3] = a.w;
         gs[j][0] = silu_fast(b.x); gs[j][1] = silu_fast(b.y); gs[j][2] = silu_fast(b.z); gs[j][3] = silu_fast(b.w);
@@ -430,14 +430,14 @@ __global__ __launch_bounds__(256) void gnorm_quant_row_kernel(const float *__res
     }
 }
 
-hipError_t launch_gnorm_quant(const float *h, const float *g, int64_t m, int d, const float *g_norm_w,
-                              const float *o_gain, float eps, int8_t *q, float *s, int32_t *sumq,
-                              float *u_out, hipStream_t stream, std::string *path) {
-    if (m <= 0) return hipSuccess;
+template <typename TG>
+static hipError_t gnorm_dispatch(const float *h, const TG *g, int64_t m, int d, const float *g_norm_w,
+                                 const float *o_gain, float eps, int8_t *q, float *s, int32_t *sumq, float *u_out,
+                                 hipStream_t stream, std::string *path) {
     const int nvb = block_bucket(d);
     if (m < kFewRows && nvb <= 8) {
         switch (nvb) {
-#define MMF_GQB(NV) case NV: gnorm_quant_row_kernel<NV><<<(unsigned)m, 256, 0, stream>>>(h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
+#define MMF_GQB(NV) case NV: gnorm_quant_row_kernel<TG, NV><<<(unsigned)m, 256, 0, stream>>>(h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
             MMF_GQB(1) MMF_GQB(2) MMF_GQB(4) MMF_GQB(8)
 #undef MMF_GQB
         }
@@ -447,13 +447,22 @@ hipError_t launch_gnorm_quant(const float *h, const float *g, int64_t m, int d, 
     const dim3 grid((unsigned)((m + 3) / 4)), block(256);
     const int nv = chunk_bucket(d);
     switch (nv) {
-#define MMF_GQ(NV) case NV: gnorm_quant_kernel<NV><<<grid, block, 0, stream>>>(h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
+#define MMF_GQ(NV) case NV: gnorm_quant_kernel<TG, NV><<<grid, block, 0, stream>>>(h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
         MMF_GQ(1) MMF_GQ(2) MMF_GQ(4) MMF_GQ(8) MMF_GQ(16) MMF_GQ(32)
 #undef MMF_GQ
         default: return hipErrorInvalidValue;  // d > 8192 is rejected by the ABI layer
     }
     if (path) *path += "gnorm_quant<" + std::to_string(nv) + ">;";
     return hipGetLastError();
+}
+
+hipError_t launch_gnorm_quant(const float *h, const void *g, ActType g_type, int64_t m, int d, const float *g_norm_w,
+                              const float *o_gain, float eps, int8_t *q, float *s, int32_t *sumq,
+                              float *u_out, hipStream_t stream, std::string *path) {
+    if (m <= 0) return hipSuccess;
+    if (g_type == ACT_F32)
+        return gnorm_dispatch(h, static_cast<const float *>(g), m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out, stream, path);
+    return gnorm_dispatch(h, static_cast<const uint16_t *>(g), m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out, stream, path);
 }
 
 // ----------------------------------------------------------------------------

@@ -15,7 +15,7 @@ hipError_t launch_norm_quant(const void *x, ActType xt, int64_t m, int k, const 
                              int8_t *q, float *s, int32_t *sumq, hipStream_t stream, std::string *path);
 
 // g_norm (RMSNorm(h) * w * SiLU(g)) followed by the o_proj quantiser; u_out optional.
-hipError_t launch_gnorm_quant(const float *h, const float *g, int64_t m, int d, const float *g_norm_w,
+hipError_t launch_gnorm_quant(const float *h, const void *g, ActType g_type, int64_t m, int d, const float *g_norm_w,
                               const float *o_gain, float eps, int8_t *q, float *s, int32_t *sumq,
                               float *u_out, hipStream_t stream, std::string *path);
 
@@ -28,9 +28,9 @@ hipError_t launch_pack(const float *w, int n, int k, uint32_t *packed, float *mu
 enum EpiKind {
     EPI_LINEAR = 0,      // NG=1: y = acc * dq                      (out0, dtype out_type)
     EPI_RESID = 1,       // NG=1: y = res + acc * dq                (out0, dtype out_type; res dtype res_type)
-    EPI_GATES = 2,       // NG=3: f = sig(f^), xt = (1-f) SiLU(i^), g = g^   (out0 f, out1 xt, out2 g; fp32)
-    EPI_GATES_STEP = 3,  // NG=3: h = f h + xt in place on out0; g to out1; f/xt probes out2/out3
-    EPI_GLU = 4          // NG=2: z = SiLU(a) * b                   (out0 fp32)
+    EPI_GATES = 2,       // NG=3: f = sig(f^), xt = (1-f) SiLU(i^), g = g^   (out0 f, out1 xt fp32; out2 g, aux)
+    EPI_GATES_STEP = 3,  // NG=3: h = f h + xt in place on out0; g to out1 (aux); f/xt probes out2/out3
+    EPI_GLU = 4          // NG=2: z = SiLU(a) * b                   (out0, aux)
 };
 
 struct ContractArgs {
@@ -47,6 +47,8 @@ struct ContractArgs {
     const void *res;
     int32_t *acc_probe;      // [m][ng*nc] (group-major within a row) or NULL
     ActType out_type, res_type;
+    ActType aux_type;        // storage type of the g (gates) or z (GLU) output
+    float *aux_probe;        // optional fp32 copy of g / z as stored (after rounding to aux_type)
 };
 
 // Prefill-shaped contraction (int8 MFMA tiles) and decode-shaped one (m <= 64).
@@ -55,28 +57,6 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
 
 // Variant name of the kernel launch_contract picks, e.g. "tgemm<gates>".
 std::string contract_variant(int64_t m, EpiKind epi, bool shared_a);
-
-// Fused decode stage (m <= 16): quantise the input rows inside the kernel,
-// then the contraction and its epilogue. All groups share the quantised input.
-enum QuantIn { QIN_F32 = 0, QIN_BF16 = 1, QIN_GNORM = 2 };
-constexpr int kDecMaxK = 8192;
-
-struct DecodeArgs {
-    ContractArgs c;       // B, mu, m, nc, k, outputs, res, acc_probe (A / s / sumq unused)
-    const void *qin;      // quantiser input rows [m][k]: activations, or h for QIN_GNORM
-    const float *g;       // QIN_GNORM: g_proj output [m][k]
-    const float *gnw;     // QIN_GNORM: g_norm gain [k] or NULL
-    const float *gain;    // quantiser RMSNorm gain [k] or NULL
-    float eps;
-    int8_t *codes_out;    // optional copy of the codes [m][k]
-    float *scale_out;     // optional copy of the scales [m]
-    float *u_out;         // optional g_norm output [m][k] (QIN_GNORM)
-};
-
-bool decode_fused_ok(int64_t m, int k);
-bool decode_fused_supports(int k, QuantIn qin);  // shape limits of the in-kernel quantiser
-hipError_t launch_decode_fused(const DecodeArgs &a, EpiKind epi, QuantIn qin, hipStream_t stream,
-                               std::string *path);
 
 // HGRN scan. chunks == 1 means the recurrent (sequential) kernel.
 size_t scan_workspace_bytes(int64_t b, int64_t d, int chunks);

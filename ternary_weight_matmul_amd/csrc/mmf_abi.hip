@@ -83,23 +83,17 @@ hipError_t t_norm_quant(const void *x, ActType xt, int64_t m, int k, const float
                  [&] { return launch_norm_quant(x, xt, m, k, gain, eps, q, s, sumq, st, path); });
 }
 
-hipError_t t_gnorm_quant(const float *h, const float *g, int64_t m, int d, const float *gw, const float *og,
+hipError_t t_gnorm_quant(const float *h, const void *g, ActType gt, int64_t m, int d, const float *gw, const float *og,
                          float eps, int8_t *q, float *s, int32_t *sumq, float *u, hipStream_t st, std::string *path) {
     if (m <= 0) return hipSuccess;
     return timed("gnorm_quant", m, d, d, st,
-                 [&] { return launch_gnorm_quant(h, g, m, d, gw, og, eps, q, s, sumq, u, st, path); });
+                 [&] { return launch_gnorm_quant(h, g, gt, m, d, gw, og, eps, q, s, sumq, u, st, path); });
 }
 
 hipError_t t_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared, hipStream_t st, std::string *path) {
     if (a.m <= 0 || a.nc <= 0) return hipSuccess;
     return timed(contract_variant(a.m, epi, shared), a.m, ng * a.nc, a.k, st,
                  [&] { return launch_contract(a, epi, ng, shared, st, path); });
-}
-
-hipError_t t_decode(const DecodeArgs &a, EpiKind epi, QuantIn qin, int ng, hipStream_t st, std::string *path) {
-    static const char *names[] = {"linear", "resid", "gates", "gates_step", "glu"};
-    return timed(std::string("decode_fused<") + names[epi] + ">", a.c.m, ng * a.c.nc, a.c.k, st,
-                 [&] { return launch_decode_fused(a, epi, qin, st, path); });
 }
 
 hipError_t t_scan(const float *x, const float *f, const float *h0, float *h, float *hl, int64_t b, int64_t t,
@@ -161,7 +155,8 @@ struct LayerWs {
     int8_t *codes_x[3];
     float *s_x[3];
     int32_t *sq_x[3];
-    float *f, *xt, *g, *h, *x1, *z;
+    float *f, *xt, *h, *x1;
+    void *g, *z;  // stored in the activation dtype (room for fp32)
     int8_t *codes_b;
     float *s_b;
     int32_t *sq_b;
@@ -189,7 +184,7 @@ size_t layer_plan(Carver &c, const mmf_layer_weights *w, int64_t b, int64_t t, i
     }
     L.f = c.take<float>(m * d);
     L.xt = c.take<float>(m * d);
-    L.g = c.take<float>(m * d);
+    L.g = c.take<float>(m * d);  // fp32-sized; holds activation-dtype values
     L.h = c.take<float>(m * d);
     L.x1 = c.take<float>(m * d);
     L.z = c.take<float>(m * inner);
@@ -226,14 +221,15 @@ T *pick(T *probe_ptr, T *ws_ptr) { return probe_ptr ? probe_ptr : ws_ptr; }
 
 // The block after the mixer's gates: g_norm, o_proj + residual, MLP + residual.
 hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t m,
-                      const LayerWs &L, const float *h, const float *g, const mmf_layer_probe *pr,
+                      const LayerWs &L, const float *h, const void *g, const mmf_layer_probe *pr,
                       hipStream_t st, std::string *path) {
     const int d = w->d, inner = w->inner;
     const float eps = w->eps;
     hipError_t e;
     int8_t *cu = pick(pr ? pr->codes_u : nullptr, L.codes_b);
     float *su = pick(pr ? pr->scale_u : nullptr, L.s_b);
-    e = t_gnorm_quant(h, g, m, d, w->g_norm_w, w->o.norm_w, eps, cu, su, L.sq_b, pr ? pr->u : nullptr, st, path);
+    e = t_gnorm_quant(h, g, act(actt), m, d, w->g_norm_w, w->o.norm_w, eps, cu, su, L.sq_b, pr ? pr->u : nullptr, st,
+                      path);
     if (e != hipSuccess) return e;
 
     float *x1 = pick(pr ? pr->x1 : nullptr, L.x1);
@@ -248,20 +244,20 @@ hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_
     float *s1 = pick(pr ? pr->scale_x1 : nullptr, L.s_b);
     if ((e = t_norm_quant(x1, ACT_F32, m, d, w->gate.norm_w, eps, c1, s1, L.sq_b, st, path)) != hipSuccess) return e;
 
-    float *z = pick(pr ? pr->z : nullptr, L.z);
+    void *z = L.z;
     ContractArgs cg{};
     for (int q = 0; q < 3; ++q) { cg.A[q] = c1; cg.s[q] = s1; cg.sumq[q] = L.sq_b; cg.mu[q] = w->gate.mu; }
     cg.B[0] = w->gate.packed;
     cg.B[1] = w->gate.packed + (size_t)inner * (d / 16);
     cg.B[2] = cg.B[1];
     cg.m = m; cg.nc = inner; cg.k = d;
-    cg.out0 = z; cg.out_type = ACT_F32;
+    cg.out0 = z; cg.aux_type = act(actt); cg.aux_probe = pr ? pr->z : nullptr;
     cg.acc_probe = pr ? pr->acc_gate : nullptr;
     if ((e = t_contract(cg, EPI_GLU, 2, true, st, path)) != hipSuccess) return e;
 
     int8_t *cz = pick(pr ? pr->codes_z : nullptr, L.codes_b);
     float *sz = pick(pr ? pr->scale_z : nullptr, L.s_b);
-    if ((e = t_norm_quant(z, ACT_F32, m, inner, w->down.norm_w, eps, cz, sz, L.sq_b, st, path)) != hipSuccess) return e;
+    if ((e = t_norm_quant(z, act(actt), m, inner, w->down.norm_w, eps, cz, sz, L.sq_b, st, path)) != hipSuccess) return e;
 
     ContractArgs cd{};
     for (int q = 0; q < 3; ++q) { cd.A[q] = cz; cd.s[q] = sz; cd.sumq[q] = L.sq_b; cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
@@ -297,64 +293,6 @@ hipError_t quant_ifg(const mmf_layer_weights *w, const void *x, mmf_dtype actt, 
     ca.m = m; ca.nc = w->d; ca.k = w->d;
     ca.acc_probe = pr ? pr->acc_ifg : nullptr;
     return hipSuccess;
-}
-
-// Decode step with at most 16 rows: four fused kernels, each quantising its
-// own input rows.
-hipError_t decode_fused_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b,
-                             float *h, const LayerWs &L, const mmf_layer_probe *pr, hipStream_t st, std::string *path) {
-    const int d = w->d, inner = w->inner;
-    hipError_t e;
-    float *g = pick(pr ? pr->g : nullptr, L.g);
-    DecodeArgs a{};
-    const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
-    for (int q = 0; q < 3; ++q) { a.c.B[q] = tw[q]->packed; a.c.mu[q] = tw[q]->mu; }
-    a.c.m = b; a.c.nc = d; a.c.k = d;
-    a.c.out0 = h; a.c.out1 = g; a.c.out_type = ACT_F32;
-    a.c.out2 = pr ? pr->f : nullptr;
-    a.c.out3 = pr ? pr->xt : nullptr;
-    a.c.acc_probe = pr ? pr->acc_ifg : nullptr;
-    a.qin = x; a.gain = w->i.norm_w; a.eps = w->eps;
-    a.codes_out = pr ? pr->codes_x[0] : nullptr;
-    a.scale_out = pr ? pr->scale_x[0] : nullptr;
-    if ((e = t_decode(a, EPI_GATES_STEP, actt == MMF_F32 ? QIN_F32 : QIN_BF16, 3, st, path)) != hipSuccess) return e;
-    if (pr && pr->h && (e = hipMemcpyAsync(pr->h, h, (size_t)b * d * sizeof(float), hipMemcpyDeviceToDevice, st)) != hipSuccess)
-        return e;
-
-    float *x1 = pick(pr ? pr->x1 : nullptr, L.x1);
-    a = DecodeArgs{};
-    for (int q = 0; q < 3; ++q) { a.c.B[q] = w->o.packed; a.c.mu[q] = w->o.mu; }
-    a.c.m = b; a.c.nc = d; a.c.k = d;
-    a.c.out0 = x1; a.c.out_type = ACT_F32; a.c.res = x; a.c.res_type = act(actt);
-    a.c.acc_probe = pr ? pr->acc_o : nullptr;
-    a.qin = h; a.g = g; a.gnw = w->g_norm_w; a.gain = w->o.norm_w; a.eps = w->eps;
-    a.codes_out = pr ? pr->codes_u : nullptr;
-    a.scale_out = pr ? pr->scale_u : nullptr;
-    a.u_out = pr ? pr->u : nullptr;
-    if ((e = t_decode(a, EPI_RESID, QIN_GNORM, 1, st, path)) != hipSuccess) return e;
-
-    float *z = pick(pr ? pr->z : nullptr, L.z);
-    a = DecodeArgs{};
-    for (int q = 0; q < 3; ++q) a.c.mu[q] = w->gate.mu;
-    a.c.B[0] = w->gate.packed;
-    a.c.B[1] = a.c.B[2] = w->gate.packed + (size_t)inner * (d / 16);
-    a.c.m = b; a.c.nc = inner; a.c.k = d;
-    a.c.out0 = z; a.c.out_type = ACT_F32;
-    a.c.acc_probe = pr ? pr->acc_gate : nullptr;
-    a.qin = x1; a.gain = w->gate.norm_w; a.eps = w->eps;
-    a.codes_out = pr ? pr->codes_x1 : nullptr;
-    a.scale_out = pr ? pr->scale_x1 : nullptr;
-    if ((e = t_decode(a, EPI_GLU, QIN_F32, 2, st, path)) != hipSuccess) return e;
-
-    a = DecodeArgs{};
-    for (int q = 0; q < 3; ++q) { a.c.B[q] = w->down.packed; a.c.mu[q] = w->down.mu; }
-    a.c.m = b; a.c.nc = d; a.c.k = inner;
-    a.c.out0 = out; a.c.out_type = act(actt); a.c.res = x1; a.c.res_type = ACT_F32;
-    a.c.acc_probe = pr ? pr->acc_down : nullptr;
-    a.qin = z; a.gain = w->down.norm_w; a.eps = w->eps;
-    a.codes_out = pr ? pr->codes_z : nullptr;
-    a.scale_out = pr ? pr->scale_z : nullptr;
-    return t_decode(a, EPI_RESID, QIN_F32, 1, st, path);
 }
 
 }  // namespace
@@ -499,10 +437,11 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
         e = quant_ifg(w, x, actt, m, L, probe, ca, &shared, stream, &path);
         float *f = pick(probe ? probe->f : nullptr, L.f);
         float *xt = pick(probe ? probe->xt : nullptr, L.xt);
-        float *g = pick(probe ? probe->g : nullptr, L.g);
+        void *g = L.g;
         float *h = pick(probe ? probe->h : nullptr, L.h);
         if (e == hipSuccess) {
             ca.out0 = f; ca.out1 = xt; ca.out2 = g; ca.out_type = ACT_F32;
+            ca.aux_type = act(actt); ca.aux_probe = probe ? probe->g : nullptr;
             e = t_contract(ca, EPI_GATES, 3, shared, stream, &path);
         }
         if (e == hipSuccess) e = t_scan(xt, f, h0, h, h_last, b, t, w->d, chunks, L.scan, stream, &path);
@@ -527,22 +466,17 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
         return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
     std::string path;
     hipError_t e = hipSuccess;
-    if (b > 0 && decode_fused_ok(b, w->d) && decode_fused_ok(b, w->inner) && shared_ifg(w) &&
-        decode_fused_supports(w->d, QIN_GNORM)) {
-        Carver c(ws);
-        LayerWs L;
-        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
-        e = decode_fused_step(w, x, out, actt, b, h, L, probe, stream, &path);
-    } else if (b > 0) {
+    if (b > 0) {
         Carver c(ws);
         LayerWs L;
         layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
         ContractArgs ca{};
         bool shared = true;
         e = quant_ifg(w, x, actt, b, L, probe, ca, &shared, stream, &path);
-        float *g = pick(probe ? probe->g : nullptr, L.g);
+        void *g = L.g;
         if (e == hipSuccess) {
             ca.out0 = h; ca.out1 = g; ca.out_type = ACT_F32;
+            ca.aux_type = act(actt); ca.aux_probe = probe ? probe->g : nullptr;
             ca.out2 = probe ? probe->f : nullptr;
             ca.out3 = probe ? probe->xt : nullptr;
             e = t_contract(ca, EPI_GATES_STEP, 3, shared, stream, &path);

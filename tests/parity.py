@@ -96,6 +96,8 @@ def check_layer_stages(L: "oracle.Layer", x: np.ndarray, h0, pr: dict, out_gpu: 
     eps = L.eps
     xf = x.reshape(m, d).astype(np.float32)
     rtol_out = 1e-4 if act == "f32" else 2e-2
+    # g and z are stored in the activation dtype (the probes hold the stored values)
+    rtol_act = rtol_out
     projs = [L.i, L.f, L.g]
     for q in range(1 if shared else 3):
         qq, ss, _ = oracle.quantize(xf, projs[q].gain, eps)
@@ -111,7 +113,7 @@ def check_layer_stages(L: "oracle.Layer", x: np.ndarray, h0, pr: dict, out_gpu: 
     f_ref, xt_ref = oracle.mixer_gates(hat[0], hat[1])
     assert_close(pr["f"], f_ref, 1e-4, "f")
     assert_close(pr["xt"], xt_ref, 1e-4, "xt")
-    assert_close(pr["g"], hat[2], 1e-4, "g")
+    assert_close(pr["g"], hat[2], rtol_act, "g")
     h_ref = oracle.hgrn_scan(pr["xt"].reshape(b, t, d), pr["f"].reshape(b, t, d), h0)
     assert_close(pr["h"], h_ref.reshape(m, d), scan_rtol, "h")
     u_ref = oracle.gnorm_swish(pr["h"], pr["g"], L.g_norm_w, eps)
@@ -131,7 +133,7 @@ def check_layer_stages(L: "oracle.Layer", x: np.ndarray, h0, pr: dict, out_gpu: 
     ab = oracle.dequant(acc_g, pr["scale_x1"], L.gate.mu)
     inner = L.inner
     z_ref = oracle.silu(ab[:, :inner]) * ab[:, inner:]
-    assert_close(pr["z"], z_ref, 1e-4, "z")
+    assert_close(pr["z"], z_ref, rtol_act, "z")
     qq, ss, _ = oracle.quantize(pr["z"], L.down.gain, eps)
     assert_equal(pr["codes_z"], qq, "codes_z")
     assert_equal(pr["scale_z"], ss, "scale_z")

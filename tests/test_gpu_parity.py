@@ -45,6 +45,7 @@ BITLINEAR_CASES = [
     (5, 48, 17, "f32", True),
     (16, 256, 64, "bf16", False),
     (64, 1040, 130, "f32", True),
+    (49, 16, 40, "f32", False),        # four row blocks with a single K word
     (65, 80, 33, "f32", False),
     (200, 1024, 200, "bf16", True),
     (300, 2816, 96, "f32", False),
@@ -207,16 +208,16 @@ def test_layer_c1_end_to_end(gpu):
 
 DECODE_CASES = [
     # b, act, gains, d, inner, expected kernel family
-    (1, "bf16", "shared", 256, 512, "decode_fused"),
-    (5, "f32", None, 272, 1040, "decode_fused"),
-    (16, "bf16", "shared", 256, 512, "decode_fused"),
+    (1, "bf16", "shared", 256, 512, "tgemv"),
+    (5, "f32", None, 272, 1040, "tgemv"),
+    (16, "bf16", "shared", 256, 512, "tgemv"),
     (16, "bf16", "distinct", 256, 512, "tgemv"),
     (17, "f32", "shared", 256, 512, "tgemv"),
     (64, "bf16", "shared", 256, 512, "tgemv"),
     (65, "bf16", "shared", 256, 512, "tgemm"),
-    (3, "bf16", "shared", 256, 4160, "decode_fused"),      # down_proj K > 4096: streamed quantiser rows
-    (16, "bf16", None, 2048, 5632, "decode_fused"),        # the 1.3B decode shape
-    (8, "bf16", None, 2560, 6912, "tgemv"),                # 2.7B width: g_norm row beyond the fused limit
+    (3, "bf16", "shared", 256, 4160, "tgemv"),      # wide down_proj input rows
+    (16, "bf16", None, 2048, 5632, "tgemv"),        # the 1.3B decode shape
+    (8, "bf16", None, 2560, 6912, "tgemv"),         # the 2.7B decode shape
 ]
 
 
