@@ -1,5 +1,5 @@
-// Epilogues of the ternary contraction, shared by the prefill, decode and
-// fused decode kernels: exact int32 sums -> dequantised values -> the fused
+// Epilogues of the ternary contraction, shared by the prefill and decode
+// kernels: exact int32 sums -> dequantised values -> the fused
 // elementwise step of the HGRNBit block (gates + recurrence step, residual,
 // SiLU-gated MLP product).
 #pragma once
@@ -67,30 +67,6 @@ __device__ __forceinline__ void epilogue_vals(const ContractArgs &p, int64_t m, 
     } else if constexpr (EPI == EPI_GLU) {
         store_aux(p, p.out0, o, silu_fast(y[0]) * y[1]);
     }
-}
-
-// The operand an epilogue reads besides the sums, for early loading.
-template <int EPI>
-__device__ __forceinline__ float epilogue_operand(const ContractArgs &p, int64_t m, int c) {
-    const int64_t o = m * (int64_t)p.nc + c;
-    if constexpr (EPI == EPI_RESID) return load_any(p.res, p.res_type, o);
-    else if constexpr (EPI == EPI_GATES_STEP) return static_cast<const float *>(p.out0)[o];
-    else return 0.0f;
-}
-
-// raw[g] = sum c*q of output (m, c) for group g (offset codes). Corrects by
-// sum q, dequantises with 1 / (s * sw) and applies the epilogue.
-template <int EPI, int NG>
-__device__ __forceinline__ void epilogue(const ContractArgs &p, const float (&sw)[3], int64_t m, int c,
-                                         const int32_t (&raw)[NG]) {
-    int32_t v[NG];
-    float dq[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        v[g] = raw[g] - p.sumq[g][m];
-        dq[g] = __builtin_amdgcn_rcpf(p.s[g][m] * sw[g]);
-    }
-    epilogue_vals<EPI, NG>(p, m, c, v, dq);
 }
 
 }  // namespace mmf

@@ -11,11 +11,12 @@
 // sum q a by-product of the activation quantiser.
 //
 // Prefill (m > 64): 128 x (NG * 64 * JN) output tiles (JN = 4, 2, 1 for one,
-// two, three groups), four waves of 64 x (NG * 32 * JN), v_mfma_i32_32x32x32_i8, K staged 128 bytes at a time through
+// two, three groups), four waves of 64 x (NG * 32 * JN), v_mfma_i32_32x32x32_i8,
+// K staged 128 bytes at a time through
 // double-buffered LDS (activation tile XOR-swizzled, packed weights padded to
 // a 48-byte row stride: both conflict-free for 16-lane groups). Tiles are
-// assigned XCD-major so that the workgroups of one XCD share activation rows
-// in their L2.
+// assigned XCD-major, and grouped eight row strips at a time, so that the
+// workgroups of one XCD share activation strips and weight tiles in its L2.
 // Decode (m <= 64): one workgroup per 16 output channels, four waves splitting
 // K, v_mfma_i32_16x16x64_i8 per 16 rows of m, partial sums reduced in LDS.
 //
@@ -36,6 +37,7 @@ namespace mmf {
 constexpr int kBM = 128;      // rows per tile
 constexpr int kBK = 128;      // k (bytes of codes) per LDS stage
 constexpr int kBStride = 48;  // bytes per packed-weight row in LDS (32 used)
+constexpr int kGroupM = 8;    // row strips per group of the tile order
 
 template <int NG, int JN, bool SHARED_A>
 struct TileShape {
@@ -50,6 +52,82 @@ struct TileShape {
     static constexpr int B_LD = (B_CH + 255) / 256;
 };
 
+// Epilogue of one wave's block of the 32x32 MFMA tiles: rows mw + [0, 64) and
+// columns cw + [0, 32 JN) of each of the NG groups (register r of lane l holds
+// row (r/4)*8 + (l/32)*4 + r%4 and column l%32 of its tile). For each batch of
+// 8 registers, every load the epilogue needs (quantiser sums and scales, the
+// residual or the old state) is issued before the batch's first store: the
+// compiler has to assume that a store may alias any later load, so loads mixed
+// in with the stores would each wait for the stores before them. RT is the
+// element type of that operand, fixed at compile time so that a bf16 operand's
+// widening is not tied to its load. Rows past M and columns past nc load from
+// a clamped, valid address and are not stored.
+template <int EPI, int NG, int JN, typename RT>
+__device__ __forceinline__ void wave_epilogue_t(const ContractArgs &p, const i32x16 (&acc)[2][NG][JN], int64_t mw,
+                                                int cw, int lane) {
+    constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
+    const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
+    constexpr int RB = 8;
+    const int lr = lane & 31, lg = lane >> 5;
+    const int64_t M = p.m;
+    float sw[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) sw[g] = weight_sw(p.mu[g]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += RB) {
+            int32_t sq[RB][NG];
+            float dq[RB][NG];
+            float pre[RB][JN];
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+                const int r = r0 + rr;
+                const int64_t m = mw + i * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+                const int64_t mc = m < M ? m : M - 1;
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    sq[rr][g] = p.sumq[g][mc];
+                    dq[rr][g] = __builtin_amdgcn_rcpf(p.s[g][mc] * sw[g]);
+                }
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const int c = cw + j * 32 + lr;
+                    pre[rr][j] = PRE ? load_act(pre_src, mc * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+                const int r = r0 + rr;
+                const int64_t m = mw + i * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+                if (m >= M) continue;
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const int c = cw + j * 32 + lr;
+                    if (c < p.nc) {
+                        int32_t v[NG];
+#pragma unroll
+                        for (int g = 0; g < NG; ++g) v[g] = acc[i][g][j][r] - sq[rr][g];
+                        epilogue_vals<EPI, NG, PRE>(p, m, c, v, dq[rr], pre[rr][j]);
+                    }
+                }
+            }
+        }
+}
+
+template <int EPI, int NG, int JN>
+__device__ __forceinline__ void wave_epilogue(const ContractArgs &p, const i32x16 (&acc)[2][NG][JN], int64_t mw,
+                                              int cw, int lane) {
+    // the residual comes in the activation type; the recurrent state is fp32
+    if constexpr (EPI == EPI_RESID) {
+        if (p.res_type == ACT_BF16) {
+            wave_epilogue_t<EPI, NG, JN, uint16_t>(p, acc, mw, cw, lane);
+            return;
+        }
+    }
+    wave_epilogue_t<EPI, NG, JN, float>(p, acc, mw, cw, lane);
+}
+
 template <int NG, int JN, bool SHARED_A, int EPI>
 __global__ __launch_bounds__(256, 2) void tgemm_kernel(const ContractArgs p, const int tiles_n) {
     using S = TileShape<NG, JN, SHARED_A>;
@@ -61,7 +139,15 @@ __global__ __launch_bounds__(256, 2) void tgemm_kernel(const ContractArgs p, con
     const int xcd = bid & 7, idx = bid >> 3;
     const int per = G >> 3, rem = G & 7;
     const int tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+    // Grouped order: kGroupM row strips at a time, row-fastest, sweeping the
+    // columns. The tiles one XCD has in flight then share a few activation
+    // strips and a few packed-weight tiles, both kept in its L2.
+    const int tiles_m = G / tiles_n;
+    const int group = tile / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gsz = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int in_group = tile - group * kGroupM * tiles_n;
+    const int tm = first_m + in_group % gsz, tn = in_group / gsz;
     const int64_t m0 = (int64_t)tm * kBM;
     const int n0 = tn * S::BNC;
 
@@ -187,34 +273,180 @@ __global__ __launch_bounds__(256, 2) void tgemm_kernel(const ContractArgs p, con
         __syncthreads();
     }
 
-    float sw[NG];
+    wave_epilogue<EPI, NG, JN>(p, acc, m0 + wm * 64, n0 + wn * (32 * JN), lane);
+}
+
+// ----------------------------------------------------------------------------
+// Prefill, K % 128 == 0: three LDS stages filled by 16-byte LDS-DMA loads
+// ----------------------------------------------------------------------------
+// Same tiles, MFMAs and epilogue as tgemm_kernel, but the global -> LDS copy
+// goes straight into LDS (global_load_lds_dwordx4: lane L of an instruction
+// fills LDS bytes [16L, 16L + 16) past the instruction's base), two K steps
+// ahead of the MFMAs, with no staging registers. A lane picks the source of
+// its LDS slot, which is how the activation tile gets its XOR swizzle; rows
+// past M or N are clamped to a valid row (their outputs are never stored).
+// Packed weights use a 32-byte row stride with the two 16-byte halves swapped
+// on every other group of 8 rows (conflict-free reads for 16-lane groups).
+// One bare barrier per K step: each wave first waits (vmcnt, loads retire in
+// order) for its own loads of the step, so after the barrier the whole step
+// is in LDS and every wave has finished with the stage the next loads reuse.
+template <int NG, int JN>
+struct DmaShape {
+    static constexpr int BNC = 64 * JN;
+    static constexpr int BROWS = NG * BNC;
+    static constexpr int A_BYTES = kBM * kBK;                      // 16 KB
+    static constexpr int B_SLOTS = (2 * BROWS + 255) / 256 * 256;  // 16-byte slots, whole waves
+    static constexpr int STAGE = A_BYTES + B_SLOTS * 16;
+    static constexpr int A_INS = A_BYTES / 16 / 256;              // DMA instructions per wave per step
+    static constexpr int B_INS = B_SLOTS / 256;
+    static constexpr int LOADS = A_INS + B_INS;
+};
+constexpr int kStages = 3;
+
+// One 16-byte LDS-DMA load: lane L copies 16 bytes from src to LDS byte
+// lds_base + 16 L (lds_base is wave-uniform). Written in asm so that the
+// compiler's own wait insertion, which cannot tell which LDS bytes the load
+// fills and so waits for it before any LDS read, leaves it alone; the kernel
+// waits for it with an explicit vmcnt. The load has no register result, and
+// M0 and the address registers are read when it issues. One wait state
+// between the M0 write and the load.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void vmcnt_wait(int n) {
+    // s_waitcnt with only the vector-memory counter constrained (expcnt 7, lgkmcnt 15 = no wait)
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+template <int NG, int JN, int EPI>
+__global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p, const int tiles_n) {
+    using S = DmaShape<NG, JN>;
+    // one LDS object per stage, so the compiler can tell the stage being read
+    // from the stages LDS-DMA loads are still filling
+    __shared__ __attribute__((aligned(16))) uint8_t st0[S::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[S::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[S::STAGE];
+
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int per = G >> 3, rem = G & 7;
+    const int tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int tiles_m = G / tiles_n;
+    const int group = tile / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gsz = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int in_group = tile - group * kGroupM * tiles_n;
+    const int tm = first_m + in_group % gsz, tn = in_group / gsz;
+    const int64_t m0 = (int64_t)tm * kBM;
+    const int n0 = tn * S::BNC;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, lg = lane >> 5;
+    const int K = p.k, KW = K >> 4;
+    const int64_t M = p.m;
+    const int ktiles = K / kBK;
+
+    // per-lane sources of its DMA slots (advanced by the K offset each step)
+    const int8_t *asrc[S::A_INS];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) sw[g] = weight_sw(p.mu[g]);
-    // per output row: the row's dequant factors once, then its JN column subtiles
+    for (int i = 0; i < S::A_INS; ++i) {
+        const int slot = (i * 4 + wave) * 64 + lane;
+        const int row = slot >> 3, pc = slot & 7;
+        const int c16 = pc ^ ((row >> 1) & 7);
+        const int64_t gm = m0 + row < M ? m0 + row : M - 1;
+        asrc[i] = p.A[0] + gm * K + 16 * c16;
+    }
+    const uint32_t *bsrc[S::B_INS];
+#pragma unroll
+    for (int i = 0; i < S::B_INS; ++i) {
+        const int slot = (i * 4 + wave) * 64 + lane;
+        int row = slot >> 1;
+        const int half = (slot & 1) ^ ((row >> 3) & 1);
+        if (row >= S::BROWS) row = 0;  // padding slots: any valid source
+        const int gi = row / S::BNC, r = row - gi * S::BNC;
+        const int gn = n0 + r < p.nc ? n0 + r : p.nc - 1;
+        bsrc[i] = p.B[gi] + (int64_t)gn * KW + 4 * half;
+    }
+    auto issue = [&](int kt, uint8_t *base) {
+        // LDS byte offset of the stage (low half of its generic address)
+        const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base + wave * 64 * 16);
+#pragma unroll
+        for (int i = 0; i < S::A_INS; ++i) lds_dma16(asrc[i] + kt * kBK, lds + i * 4 * 64 * 16);
+#pragma unroll
+        for (int i = 0; i < S::B_INS; ++i)
+            lds_dma16(bsrc[i] + kt * (kBK / 16), lds + S::A_BYTES + i * 4 * 64 * 16);
+    };
+
+    i32x16 acc[2][NG][JN];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-            if (m >= M) continue;
-            int32_t sq[NG];
-            float dq[NG];
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                sq[g] = p.sumq[g][m];
-                dq[g] = __builtin_amdgcn_rcpf(p.s[g][m] * sw[g]);
-            }
+            for (int j = 0; j < JN; ++j) acc[i][g][j] = i32x16{};
+
+    auto compute = [&](const uint8_t *sa) {
+        const uint8_t *sb = sa + S::A_BYTES;
+        uint4 bw[NG][JN];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
             for (int j = 0; j < JN; ++j) {
-                const int c = n0 + wn * (32 * JN) + j * 32 + lr;
-                if (c < p.nc) {
-                    int32_t v[NG];
-#pragma unroll
-                    for (int g = 0; g < NG; ++g) v[g] = acc[i][g][j][r] - sq[g];
-                    epilogue_vals<EPI, NG>(p, m, c, v, dq);
-                }
+                const int brow = g * S::BNC + wn * (32 * JN) + j * 32 + lr;
+                bw[g][j] = *reinterpret_cast<const uint4 *>(sb + brow * 32 + ((lg ^ ((brow >> 3) & 1)) << 4));
             }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            i32x4 af[2];
+            const int c = 4 * lg + ks;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = wm * 64 + i * 32 + lr;
+                af[i] = *reinterpret_cast<const i32x4 *>(sa + row * kBK + ((c ^ ((row >> 1) & 7)) << 4));
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    const uint32_t word = ks == 0 ? bw[g][j].x : ks == 1 ? bw[g][j].y : ks == 2 ? bw[g][j].z : bw[g][j].w;
+                    const i32x4 b = decode_word(word);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][g][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], b, acc[i][g][j], 0, 0, 0);
+                }
         }
+    };
+
+    // step kt: wait for its loads, barrier, start the loads of step kt+2 into
+    // the stage step kt-1 used, then compute step kt
+    auto step = [&](int kt, const uint8_t *cur, uint8_t *next2) {
+        vmcnt_wait(kt + 1 < ktiles ? S::LOADS : 0);  // this wave's loads of step kt have landed
+        asm volatile("" ::: "memory");                 // keep LDS accesses on their side of the barrier
+        __builtin_amdgcn_s_barrier();                  // ... and everyone's; next2 is no longer read
+        asm volatile("" ::: "memory");
+        if (kt + 2 < ktiles) issue(kt + 2, next2);
+        compute(cur);
+    };
+    issue(0, st0);
+    if (ktiles > 1) issue(1, st1);
+    for (int kt = 0; kt < ktiles; kt += kStages) {
+        step(kt, st0, st2);
+        if (kt + 1 < ktiles) step(kt + 1, st1, st0);
+        if (kt + 2 < ktiles) step(kt + 2, st2, st1);
+    }
+
+    wave_epilogue<EPI, NG, JN>(p, acc, m0 + wm * 64, n0 + wn * (32 * JN), lane);
 }
 
 // ----------------------------------------------------------------------------
@@ -226,8 +458,9 @@ __global__ __launch_bounds__(256, 2) void tgemm_kernel(const ContractArgs p, con
 // slice and issues every load of the slice -- weights as 16-byte runs,
 // activation codes of its row block as 16-byte chunks -- before its first
 // MFMA, so a GEMV costs about one memory round trip. Wave partial sums are
-// combined with LDS integer atomics (exact, order-free).
-template <int NG, int MB, bool SHARED_A, int EPI, int WPL>
+// combined with LDS integer atomics (exact, order-free). RT is the element
+// type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
+template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT>
 __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const int nslices) {
     constexpr int NA = SHARED_A ? 1 : NG;
     __shared__ int32_t red[MB * NG * 256];
@@ -239,6 +472,24 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
     const int gn = n0 + lc;
     const bool bvec = (KW & 3) == 0;
     for (int i = tid; i < MB * NG * 256; i += blockDim.x) red[i] = 0;
+    // weight scales and the epilogue operands (residual / old state) do not
+    // depend on the contraction: load them before it, unconditionally (clamped
+    // to a valid element; the values of outputs that are not stored go unused)
+    // so that no wait for them comes before the contraction's own loads
+    float mu_v[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) mu_v[g] = *p.mu[g];
+    constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
+    constexpr int EPT = 4;  // epilogue outputs per thread with the smallest block (4 waves, MB = 4)
+    float pre[EPT];
+    const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int idx = tid + e * blockDim.x;
+        const int64_t m = (int64_t)(idx >> 8) * 16 + ((idx >> 4) & 15);
+        const int c = n0 + (idx & 15);
+        pre[e] = PRE ? load_act(pre_src, (m < M ? m : M - 1) * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
+    }
 
     i32x4 acc[MB][NG];
 #pragma unroll
@@ -292,17 +543,23 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
 #pragma unroll
             for (int i = 0; i < 4; ++i) atomicAdd(&red[(mb * NG + g) * 256 + (4 * lg + i) * 16 + lc], acc[mb][g][i]);
     __syncthreads();
-    float sw[3];
+    float sw[NG];
 #pragma unroll
-    for (int g = 0; g < 3; ++g) sw[g] = g < NG ? weight_sw(p.mu[g]) : 1.0f;
-    for (int idx = tid; idx < MB * 256; idx += blockDim.x) {
+    for (int g = 0; g < NG; ++g) sw[g] = __fdiv_rn(1.0f, fmaxf(mu_v[g], 1e-5f));
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int idx = tid + e * blockDim.x;
         const int mb = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
         const int64_t m = mb * 16 + r;
-        if (m < M && n0 + c < p.nc) {
-            int32_t raw[NG];
+        if (idx < MB * 256 && m < M && n0 + c < p.nc) {
+            int32_t v[NG];
+            float dq[NG];
 #pragma unroll
-            for (int g = 0; g < NG; ++g) raw[g] = red[(mb * NG + g) * 256 + r * 16 + c];
-            epilogue<EPI, NG>(p, sw, m, n0 + c, raw);
+            for (int g = 0; g < NG; ++g) {
+                v[g] = red[(mb * NG + g) * 256 + r * 16 + c] - p.sumq[g][m];
+                dq[g] = __builtin_amdgcn_rcpf(p.s[g][m] * sw[g]);
+            }
+            epilogue_vals<EPI, NG, true>(p, m, n0 + c, v, dq, pre[e]);
         }
     }
 }
@@ -329,29 +586,54 @@ static void run_gemm(const ContractArgs &a, hipStream_t st) {
     tgemm_kernel<NG, JN, SH, EPI><<<(unsigned)(tiles_m * tiles_n), 256, 0, st>>>(a, tiles_n);
 }
 
-template <int NG, int MB, bool SH, int EPI, int WPL>
+template <int NG, int MB, bool SH, int EPI, int WPL, typename RT>
 static void run_gemv_mb(const ContractArgs &a, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 4 * WPL - 1) / (4 * WPL);
-    const int waves = nslices < 16 ? nslices : 16;
-    tgemv_kernel<NG, MB, SH, EPI, WPL><<<(unsigned)((a.nc + 15) / 16), waves * 64, 0, st>>>(a, nslices);
+    int waves = nslices < 16 ? nslices : 16;
+    if (waves < MB) waves = MB;  // the epilogue covers MB*256 outputs with at most 4 per thread
+    tgemv_kernel<NG, MB, SH, EPI, WPL, RT><<<(unsigned)((a.nc + 15) / 16), waves * 64, 0, st>>>(a, nslices);
+}
+
+template <int NG, int JN, int EPI>
+static void run_gemm_dma(const ContractArgs &a, hipStream_t st) {
+    using S = DmaShape<NG, JN>;
+    static_assert(S::LOADS == 5 || S::LOADS == 6 || S::LOADS == 7, "vmcnt_wait covers 5..7 loads per step");
+    const int64_t tiles_m = (a.m + kBM - 1) / kBM;
+    const int tiles_n = (a.nc + S::BNC - 1) / S::BNC;
+    tgemm_dma_kernel<NG, JN, EPI><<<(unsigned)(tiles_m * tiles_n), 256, 0, st>>>(a, tiles_n);
+}
+
+template <int NG, bool SH, int EPI, typename RT>
+static void run_gemv_t(const ContractArgs &a, hipStream_t st) {
+    constexpr int NA = SH ? 1 : NG;
+    switch ((int)((a.m + 15) / 16)) {
+        case 1: run_gemv_mb<NG, 1, SH, EPI, (NA <= 2 ? 8 : 4), RT>(a, st); break;
+        case 2: run_gemv_mb<NG, 2, SH, EPI, (NA <= 1 ? 8 : 4), RT>(a, st); break;
+        case 3: run_gemv_mb<NG, 3, SH, EPI, 4, RT>(a, st); break;
+        default: run_gemv_mb<NG, 4, SH, EPI, 4, RT>(a, st); break;
+    }
 }
 
 template <int NG, bool SH, int EPI>
 static void run_gemv(const ContractArgs &a, hipStream_t st) {
-    constexpr int NA = SH ? 1 : NG;
-    switch ((int)((a.m + 15) / 16)) {
-        case 1: run_gemv_mb<NG, 1, SH, EPI, (NA <= 2 ? 8 : 4)>(a, st); break;
-        case 2: run_gemv_mb<NG, 2, SH, EPI, (NA <= 1 ? 8 : 4)>(a, st); break;
-        case 3: run_gemv_mb<NG, 3, SH, EPI, 4>(a, st); break;
-        default: run_gemv_mb<NG, 4, SH, EPI, 4>(a, st); break;
+    // the residual comes in the activation type; the recurrent state is fp32
+    if constexpr (EPI == EPI_RESID) {
+        if (a.res_type == ACT_BF16) {
+            run_gemv_t<NG, SH, EPI, uint16_t>(a, st);
+            return;
+        }
     }
+    run_gemv_t<NG, SH, EPI, float>(a, st);
 }
 
 static bool use_gemv(int64_t m) { return m <= 64; }
+// the LDS-DMA kernel needs whole 128-byte K steps and one activation tensor
+static bool dma_ok(const ContractArgs &a, bool shared_a) { return shared_a && (a.k % kBK) == 0; }
 
-std::string contract_variant(int64_t m, EpiKind epi, bool shared_a) {
-    return std::string(use_gemv(m) ? "tgemv<" : "tgemm<") + epi_name(epi) + (shared_a ? "" : ",split_a") + ">";
+std::string contract_variant(int64_t m, int k, EpiKind epi, bool shared_a) {
+    const char *kind = use_gemv(m) ? "tgemv<" : (shared_a && k % kBK == 0) ? "tgemm_dma<" : "tgemm<";
+    return std::string(kind) + epi_name(epi) + (shared_a ? "" : ",split_a") + ">";
 }
 
 hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a, hipStream_t st,
@@ -370,6 +652,14 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
                 if (shared_a) run_gemv<3, true, EPI_GATES_STEP>(a, st); else run_gemv<3, false, EPI_GATES_STEP>(a, st);
                 break;
         }
+    } else if (dma_ok(a, shared_a)) {
+        switch (epi) {
+            case EPI_LINEAR: run_gemm_dma<1, 4, EPI_LINEAR>(a, st); break;
+            case EPI_RESID: run_gemm_dma<1, 4, EPI_RESID>(a, st); break;
+            case EPI_GLU: run_gemm_dma<2, 2, EPI_GLU>(a, st); break;
+            case EPI_GATES: run_gemm_dma<3, 1, EPI_GATES>(a, st); break;
+            case EPI_GATES_STEP: run_gemm_dma<3, 1, EPI_GATES_STEP>(a, st); break;
+        }
     } else {
         switch (epi) {
             case EPI_LINEAR: run_gemm<1, 4, true, EPI_LINEAR>(a, st); break;
@@ -384,7 +674,7 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
         }
     }
     (void)ng;
-    if (path) *path += contract_variant(a.m, epi, shared_a) + ";";
+    if (path) *path += contract_variant(a.m, a.k, epi, shared_a) + ";";
     return hipGetLastError();
 }
 

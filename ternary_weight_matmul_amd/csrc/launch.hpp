@@ -56,7 +56,7 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
                            hipStream_t stream, std::string *path);
 
 // Variant name of the kernel launch_contract picks, e.g. "tgemm<gates>".
-std::string contract_variant(int64_t m, EpiKind epi, bool shared_a);
+std::string contract_variant(int64_t m, int k, EpiKind epi, bool shared_a);
 
 // HGRN scan. chunks == 1 means the recurrent (sequential) kernel.
 size_t scan_workspace_bytes(int64_t b, int64_t d, int chunks);

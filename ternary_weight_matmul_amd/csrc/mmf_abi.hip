@@ -92,7 +92,7 @@ hipError_t t_gnorm_quant(const float *h, const void *g, ActType gt, int64_t m, i
 
 hipError_t t_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared, hipStream_t st, std::string *path) {
     if (a.m <= 0 || a.nc <= 0) return hipSuccess;
-    return timed(contract_variant(a.m, epi, shared), a.m, ng * a.nc, a.k, st,
+    return timed(contract_variant(a.m, a.k, epi, shared), a.m, ng * a.nc, a.k, st,
                  [&] { return launch_contract(a, epi, ng, shared, st, path); });
 }
 
