@@ -9,10 +9,13 @@ a 24-layer HGRNBit stack (d=2048, MLP inner 5632, random ternarised weights):
 value = layer-tokens/s = B*(T+D)*L / step time (metric "HGRNBit layer tokens/s").
 
 Also printed in the same JSON line:
-  roofline     -- the dominant kernel (largest share of the step's kernel time,
-                  measured with HIP events on the launch stream over the timed
-                  steps) against its roof: int8 MFMA peak for the prefill
-                  contraction, HBM for the decode weight stream;
+  roofline     -- the dominant kernel at its shape (largest share of the step
+                  time) against its roof: int8 MFMA peak for a prefill
+                  contraction, HBM for everything else. Prefill kernels are
+                  timed with HIP events on their stream inside the timed steps;
+                  decode kernels, which run inside a HIP graph there, are timed
+                  the same way on an eager copy of the decode steps queued
+                  behind a prefill;
   cpu_baseline -- the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -45,16 +48,80 @@ def parse():
     return ap.parse_args()
 
 
+ACT_BYTES = 2  # bf16 activations
+
+
+def _kind(kernel: str):
+    base, _, rest = kernel.partition("<")
+    args = rest.rstrip(">").split(",") if rest else []
+    return base, args
+
+
 def algorithmic(kernel: str, m: int, n: int, k: int):
-    """(ops, bytes) one launch must do: ops = 2*m*n*k for a contraction; bytes = packed
-    weights (n*k/4) + int8 codes (m*k) + per-row scale/sum (8m) + outputs (4 bytes per output element)."""
-    if kernel.startswith("tgemm") or kernel.startswith("tgemv"):
-        ops = 2.0 * m * n * k
-        out_elems = {"gates": 3 * (n // 3), "gates_step": 3 * (n // 3), "glu": n // 2}.get(
-            kernel.split("<")[1].split(">")[0].split(",")[0], n)
-        nbytes = n * k / 4.0 + m * k + 8.0 * m + 4.0 * m * out_elems
-        return ops, nbytes
+    """(ops, bytes) one launch must do at the least, from the kernel variant and its shape.
+
+    contraction (m rows, n outputs over all groups, k): ops = 2 m n k; bytes = packed
+      weights n k / 4 + int8 codes m k per activation tensor + scale and code sum 8 m per
+      tensor + the epilogue's own traffic per output channel c of a group:
+        gates: f, x~ (fp32) and g (bf16) written = 10 B; gates_step: h read and written
+        (fp32) and g written (bf16) = 10 B; glu: z (bf16) = 2 B; resid: residual read and
+        sum written, one fp32 and one bf16 = 6 B; linear: 4 B.
+    norm_quant<T> (m rows of k): x read (sizeof T) + codes written (1 B) per element, 8 B per row.
+    gnorm_quant<T>: h (fp32) and g (sizeof T) read + codes written per element, 8 B per row.
+    scan (m = b t, k = d): f and x~ read, h written, 12 B per element.
+    """
+    base, args = _kind(kernel)
+    if base in ("tgemm", "tgemm_dma", "tgemv"):
+        epi = args[0]
+        na = 3 if "split_a" in args else 1
+        ng = {"gates": 3, "gates_step": 3, "glu": 2}.get(epi, 1)
+        per_c = {"gates": 10, "gates_step": 10, "glu": 2, "resid": 4 + ACT_BYTES, "linear": 4}[epi]
+        nbytes = n * k / 4.0 + na * (m * k + 8.0 * m) + m * (n / ng) * per_c
+        return 2.0 * m * n * k, nbytes
+    tb = 4 if args[:1] == ["f32"] else ACT_BYTES
+    if base == "norm_quant":
+        return 0.0, m * k * (tb + 1.0) + 8.0 * m
+    if base == "gnorm_quant":
+        return 0.0, m * k * (4.0 + tb + 1.0) + 8.0 * m
+    if base.startswith("scan"):
+        return 0.0, 12.0 * m * k
     return 0.0, 0.0
+
+
+def source_digest() -> str:
+    """sha256 of the kernel sources, to tell whether stored counter figures still apply."""
+    import hashlib
+    hsh = hashlib.sha256()
+    csrc = os.path.join(ROOT, "ternary_weight_matmul_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                hsh.update(name.encode() + b"\0" + f.read())
+    return hsh.hexdigest()[:16]
+
+
+def stored_traffic(key: str):
+    """HBM bytes per launch of kernel `key` from a counter summary under profiles/ (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-kernel calibration), if one exists for the current sources."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    digest = source_digest()
+    for name in sorted(os.listdir(pdir)):
+        if not (name.startswith("traffic_") and name.endswith(".txt")):
+            continue
+        fields = {}
+        with open(os.path.join(pdir, name)) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    kk, _, vv = line.partition(":")
+                    fields[kk.strip()] = vv.strip()
+        if fields.get("kernel") == key and fields.get("sources") == digest:
+            try:
+                return float(fields["hbm_bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
 
 
 def main():
@@ -130,7 +197,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps; prefill kernels bracketed by HIP events
+    # ---- timed region: K steps; prefill kernels bracketed by HIP events on their stream
     mmf.timing_enable(True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -149,71 +216,87 @@ def main():
     prefill_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     decode_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
 
-    # decode kernels run inside the graph: time one eager instrumented decode step after the timed region
-    mmf.timing_enable(True)
-    xin.copy_(x_decode[0])
-    decode_step()
-    torch.cuda.synchronize()
-    mmf.timing_enable(False)
-    drecs = mmf.timing_collect()
+    # ---- decode kernels: the timed region replays them inside a HIP graph, where no event can
+    # bracket a single kernel. The same decode steps are issued once more eagerly, with the
+    # per-launch events, behind a queued prefill so that the device never waits on the host
+    # between them; their event-measured durations stand for the graph's (the sum is reported
+    # next to the graph's own time per step as a check).
+    DM = min(4, D)
+    drecs = []
+    if DM:
+        prefill()
+        mmf.timing_enable(True)
+        for s_ in range(DM):
+            xin.copy_(x_decode[s_])
+            decode_step()
+        torch.cuda.synchronize()
+        mmf.timing_enable(False)
+        drecs = mmf.timing_collect()
 
     ms_per_step = elapsed * 1000.0 / args.steps
     tokens = B * (T + D)
     value = tokens * L / (ms_per_step / 1000.0)
 
-    # ---- per-kernel summary
-    per = {}
-    for name, m, n, k, ms in recs:
-        e = per.setdefault(name, dict(launches=0, ms=0.0, ops=0.0, bytes=0.0, phase="prefill"))
-        ops, nb = algorithmic(name, m, n, k)
-        e["launches"] += 1
-        e["ms"] += ms
-        e["ops"] += ops
-        e["bytes"] += nb
-    dper = {}
-    for name, m, n, k, ms in drecs:
-        e = dper.setdefault(name, dict(launches=0, ms=0.0, ops=0.0, bytes=0.0, phase="decode"))
-        ops, nb = algorithmic(name, m, n, k)
-        e["launches"] += 1
-        e["ms"] += ms
-        e["ops"] += ops
-        e["bytes"] += nb
-    # decode totals over the timed region: one instrumented step scaled by D steps and K repetitions
-    for e in dper.values():
-        for key in ("launches", "ms", "ops", "bytes"):
-            e[key] *= D * args.steps
+    # ---- per-kernel totals per step, keyed by variant and shape
     kernels = {}
-    for src in (per, dper):
-        for name, e in src.items():
-            key = name if name not in kernels else name + "@" + e["phase"]
-            kernels[key] = e
-    dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["ms"])
-    avg_ms = dom["ms"] / dom["launches"]
-    if dom_name.startswith("tgemm"):
-        achieved = dom["ops"] / dom["launches"] / (avg_ms / 1000.0) / 1e12
+
+    def add(src, phase, scale):
+        for name, m, n, k, ms in src:
+            key = "%s m=%d n=%d k=%d" % (name, m, n, k)
+            e = kernels.setdefault(key, dict(name=name, m=m, n=n, k=k, phase=phase, launches=0.0, ms=0.0))
+            e["launches"] += scale
+            e["ms"] += ms * scale
+
+    add(recs, "prefill", 1.0 / args.steps)
+    if DM:
+        add(drecs, "decode", float(D) / DM)
+    for e in kernels.values():
+        e["avg_ms"] = e["ms"] / e["launches"]
+        e["ops"], e["bytes"] = algorithmic(e["name"], e["m"], e["n"], e["k"])
+    total_kernel_ms = sum(e["ms"] for e in kernels.values())
+    dom_key, dom = max(kernels.items(), key=lambda kv: kv[1]["ms"])
+    avg_s = dom["avg_ms"] / 1000.0
+    if dom["name"].startswith("tgemm"):
+        achieved = dom["ops"] / avg_s / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_MFMA_PEAK_TOPS, unit="TFLOP/s")
     else:
-        achieved = dom["bytes"] / dom["launches"] / (avg_ms / 1000.0) / 1e9
+        achieved = dom["bytes"] / avg_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
-    roof["kernel"] = dom_name
-    roof["avg_launch_us"] = round(avg_ms * 1000.0, 2)
-    roof["share_of_kernel_time"] = round(dom["ms"] / sum(e["ms"] for e in kernels.values()), 3)
+    roof["traffic"] = stored_traffic(dom_key)
+    roof["kernel"] = dom_key
+    roof["phase"] = dom["phase"]
+    roof["avg_launch_us"] = round(dom["avg_ms"] * 1000.0, 2)
+    roof["algorithmic_per_launch"] = dom["ops"] if roof["bound"] == "mfma" else dom["bytes"]
+    roof["share_of_step"] = round(dom["ms"] / ms_per_step, 3)
 
     breakdown = {}
-    for name, e in sorted(kernels.items(), key=lambda kv: -kv[1]["ms"]):
-        avg = e["ms"] / e["launches"]
-        row = dict(launches=int(e["launches"]), avg_us=round(avg * 1000, 2), total_ms=round(e["ms"] / args.steps, 3))
+    for key, e in sorted(kernels.items(), key=lambda kv: -kv[1]["ms"]):
+        row = dict(phase=e["phase"], launches_per_step=round(e["launches"], 1), avg_us=round(e["avg_ms"] * 1000, 2),
+                   ms_per_step=round(e["ms"], 3))
+        t = e["avg_ms"] / 1000.0
         if e["ops"]:
-            row["tops"] = round(e["ops"] / e["launches"] / (avg / 1000) / 1e12, 1)
-            row["gbs"] = round(e["bytes"] / e["launches"] / (avg / 1000) / 1e9, 1)
-        breakdown[name] = row
+            row["int8_tops"] = round(e["ops"] / t / 1e12, 1)
+            row["frac_mfma"] = round(e["ops"] / t / 1e12 / INT8_MFMA_PEAK_TOPS, 4)
+        row["gbs"] = round(e["bytes"] / t / 1e9, 1)
+        row["frac_hbm"] = round(e["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4)
+        breakdown[key] = row
+
+    # the best prefill contraction against the MFMA roof, for reference next to the dominant kernel
+    pre = [e for e in kernels.values() if e["phase"] == "prefill" and e["ops"]]
+    prefill_gemm = None
+    if pre:
+        ops = sum(e["ops"] * e["launches"] for e in pre)
+        ms = sum(e["ms"] for e in pre)
+        prefill_gemm = dict(achieved=round(ops / (ms / 1000) / 1e12, 1), peak=INT8_MFMA_PEAK_TOPS, unit="TFLOP/s",
+                            frac=round(ops / (ms / 1000) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
+                            note="all prefill contractions together, int8 ops over their event-measured time")
 
     cpu = None
     if args.cpu_baseline:
         cpu = cpu_baseline(d, inner, seed)
 
+    dsum = sum(e["ms"] for e in kernels.values() if e["phase"] == "decode")
     line = {
         "metric": "HGRNBit layer tokens/s (prefill + decode), 1.3B shape; % HBM / int8 MFMA peak",
         "value": round(value, 1),
@@ -225,7 +308,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8xternary->int32 contraction; bf16 activations; fp32 state",
+        "dtype": "int8 x ternary -> int32 contraction; bf16 activations; fp32 state",
         "data": "synthetic: seeded x~N(0,1) bf16, latent weights~N(0,0.02) ternarised on device",
         "config": {
             "workload": "hgrnbit-%s-serve: %d layers d=%d inner=%d, prefill B=%d x T=%d, then %d decode steps" % (
@@ -238,9 +321,13 @@ def main():
         "prefill_layer_tokens_per_s": round(B * T * L / (prefill_ms / 1000), 1),
         "decode_layer_tokens_per_s": round(B * D * L / (decode_ms / 1000), 1) if D else None,
         "decode_us_per_token_step": round(decode_ms * 1000 / D, 2) if D else None,
+        "decode_kernel_sum_us_per_token_step": round(dsum * 1000 / D, 2) if D else None,
         "roofline": roof,
+        "prefill_contraction_roofline": prefill_gemm,
         "cpu_baseline": cpu,
         "kernels": breakdown,
+        "kernel_ms_per_step": round(total_kernel_ms, 3),
+        "sources": source_digest(),
         "prep_s": round(prep_s, 1),
     }
     print(json.dumps(line), flush=True)
@@ -248,7 +335,8 @@ def main():
 
 def cpu_baseline(d: int, inner: int, seed: int) -> dict:
     """The oracle (plain C + numpy fp64, OpenMP over independent outputs) on a bounded sample:
-    one layer of the same shape, a 256-token prefill of one sequence plus 4 decode steps at batch 16."""
+    one layer of the same shape, a 1024-token prefill of one sequence plus 16 decode steps at
+    batch 16 continuing from random states."""
     import numpy as np
     import oracle
     from ternary_weight_matmul_amd import synth
@@ -256,18 +344,20 @@ def cpu_baseline(d: int, inner: int, seed: int) -> dict:
     lat = synth.latent_weights(d, inner, synth.layer_seed(seed, 0))
     Lo = oracle.make_layer(lat)
     del lat
-    x = synth.activations((1, 256, d), seed * 10 + 1, "bf16")
-    xs = synth.activations((4, 16, d), seed * 10 + 2, "bf16")
+    T0, S0, B0 = 1024, 16, 16
+    x = synth.activations((1, T0, d), seed * 10 + 1, "bf16")
+    xs = synth.activations((S0, B0, d), seed * 10 + 2, "bf16")
+    h = synth.rng(seed * 10 + 3).standard_normal((B0, d))
     t0 = time.perf_counter()
-    r = oracle.layer_forward(Lo, x)
-    h = np.zeros((16, d))
-    for s in range(4):
-        h = oracle.layer_decode_step(Lo, xs[s], h)["h"]
+    oracle.layer_forward(Lo, x)
+    for s_ in range(S0):
+        h = oracle.layer_decode_step(Lo, xs[s_], h)["h"]
     dt = time.perf_counter() - t0
-    tokens = 256 + 4 * 16
+    tokens = T0 + S0 * B0
     return {"value": round(tokens / dt, 2), "unit": "layer-tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "1 layer at the same shape: prefill of 1x256 tokens + 4 decode steps at batch 16 (%d layer-tokens, %.1f s)" % (tokens, dt)}
+            "sample": "1 layer at the same shape: prefill of 1x%d tokens + %d decode steps at batch %d "
+                      "(%d layer-tokens, %.1f s)" % (T0, S0, B0, tokens, dt)}
 
 
 if __name__ == "__main__":

@@ -472,23 +472,31 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
     const int gn = n0 + lc;
     const bool bvec = (KW & 3) == 0;
     for (int i = tid; i < MB * NG * 256; i += blockDim.x) red[i] = 0;
-    // weight scales and the epilogue operands (residual / old state) do not
-    // depend on the contraction: load them before it, unconditionally (clamped
-    // to a valid element; the values of outputs that are not stored go unused)
-    // so that no wait for them comes before the contraction's own loads
+    // weight scales, the quantiser's per-row scales and sums and the epilogue
+    // operands (residual / old state) do not depend on the contraction: load
+    // them before it, unconditionally (clamped to a valid element; the values
+    // of outputs that are not stored go unused) so that no wait for them comes
+    // before the contraction's own loads
     float mu_v[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) mu_v[g] = *p.mu[g];
     constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
     constexpr int EPT = 4;  // epilogue outputs per thread with the smallest block (4 waves, MB = 4)
-    float pre[EPT];
+    float pre[EPT], sc_e[EPT][NG];
+    int32_t sq_e[EPT][NG];
     const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int idx = tid + e * blockDim.x;
         const int64_t m = (int64_t)(idx >> 8) * 16 + ((idx >> 4) & 15);
+        const int64_t mc = m < M ? m : M - 1;
         const int c = n0 + (idx & 15);
-        pre[e] = PRE ? load_act(pre_src, (m < M ? m : M - 1) * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
+        pre[e] = PRE ? load_act(pre_src, mc * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            sq_e[e][g] = p.sumq[g][mc];
+            sc_e[e][g] = p.s[g][mc];
+        }
     }
 
     i32x4 acc[MB][NG];
@@ -556,8 +564,8 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
             float dq[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                v[g] = red[(mb * NG + g) * 256 + r * 16 + c] - p.sumq[g][m];
-                dq[g] = __builtin_amdgcn_rcpf(p.s[g][m] * sw[g]);
+                v[g] = red[(mb * NG + g) * 256 + r * 16 + c] - sq_e[e][g];
+                dq[g] = __builtin_amdgcn_rcpf(sc_e[e][g] * sw[g]);
             }
             epilogue_vals<EPI, NG, true>(p, m, n0 + c, v, dq, pre[e]);
         }

@@ -63,15 +63,18 @@ hipEvent_t timing_event() {
     return g_events[g_events_used++];
 }
 
+// The events bracket the launch on its stream. Under stream capture they are
+// recorded as external event nodes of the graph, so every replay of the graph
+// re-records them: a collect after a replay reads that replay's durations.
 template <class F>
 hipError_t timed(const std::string &kernel, int64_t m, int n, int k, hipStream_t st, F &&launch) {
     if (!g_timing) return launch();
     hipEvent_t a = timing_event(), b = timing_event();
     if (!a || !b) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(a, st);
+    hipError_t e = hipEventRecordWithFlags(a, st, hipEventRecordExternal);
     if (e != hipSuccess) return e;
     if ((e = launch()) != hipSuccess) return e;
-    if ((e = hipEventRecord(b, st)) != hipSuccess) return e;
+    if ((e = hipEventRecordWithFlags(b, st, hipEventRecordExternal)) != hipSuccess) return e;
     g_recs.push_back(TimingRec{kernel, m, n, k, a, b});
     return hipSuccess;
 }
@@ -79,14 +82,14 @@ hipError_t timed(const std::string &kernel, int64_t m, int n, int k, hipStream_t
 hipError_t t_norm_quant(const void *x, ActType xt, int64_t m, int k, const float *gain, float eps, int8_t *q,
                         float *s, int32_t *sumq, hipStream_t st, std::string *path) {
     if (m <= 0) return hipSuccess;
-    return timed("norm_quant", m, k, k, st,
+    return timed(xt == ACT_F32 ? "norm_quant<f32>" : "norm_quant<bf16>", m, k, k, st,
                  [&] { return launch_norm_quant(x, xt, m, k, gain, eps, q, s, sumq, st, path); });
 }
 
 hipError_t t_gnorm_quant(const float *h, const void *g, ActType gt, int64_t m, int d, const float *gw, const float *og,
                          float eps, int8_t *q, float *s, int32_t *sumq, float *u, hipStream_t st, std::string *path) {
     if (m <= 0) return hipSuccess;
-    return timed("gnorm_quant", m, d, d, st,
+    return timed(gt == ACT_F32 ? "gnorm_quant<f32>" : "gnorm_quant<bf16>", m, d, d, st,
                  [&] { return launch_gnorm_quant(h, g, gt, m, d, gw, og, eps, q, s, sumq, u, st, path); });
 }
 
