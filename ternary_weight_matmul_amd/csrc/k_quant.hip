@@ -18,57 +18,92 @@ namespace mmf {
 // ----------------------------------------------------------------------------
 // norm_quant: q = clamp(rint(((x * r) * gain) * s)), r = rms factor, s = 127/amax
 // ----------------------------------------------------------------------------
+// A 16-byte chunk of a row kept as loaded: 4 fp32 or 8 bf16 elements. The
+// bf16 chunk stays packed in registers (half the registers of fp32) and is
+// widened at each use.
+template <typename T> struct Chunk;
+template <> struct Chunk<float> {
+    using R = float4;
+    static constexpr int E = 4;
+    static __device__ __forceinline__ float get(const R &r, int e) {
+        return e == 0 ? r.x : e == 1 ? r.y : e == 2 ? r.z : r.w;
+    }
+};
+template <> struct Chunk<uint16_t> {
+    using R = uint4;
+    static constexpr int E = 8;
+    static __device__ __forceinline__ float get(const R &r, int e) {
+        const uint32_t w = (e >> 1) == 0 ? r.x : (e >> 1) == 1 ? r.y : (e >> 1) == 2 ? r.z : r.w;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
+// y = (v * r) * gain of element e of chunk c
+template <typename T>
+__device__ __forceinline__ float scaled(const typename Chunk<T>::R &raw, int e, float r, const float *gain, int c) {
+    float y = __fmul_rn(Chunk<T>::get(raw, e), r);
+    if (gain) y = __fmul_rn(y, gain[Chunk<T>::E * c + e]);
+    return y;
+}
+
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void norm_quant_kernel(const T *__restrict__ x, int64_t m, int k,
                                                          const float *__restrict__ gain, float eps,
                                                          int8_t *__restrict__ q, float *__restrict__ s,
                                                          int32_t *__restrict__ sumq) {
+    using C = Chunk<T>;
+    constexpr int E = C::E;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= m) return;
-    const int nch = k >> 2;
-    const T *xr = x + row * (int64_t)k;
-    float v[NV][4];
+    const int nch = k / E;
+    const typename C::R *xr = reinterpret_cast<const typename C::R *>(x + row * (int64_t)k);
+    // every load first: a chunk index past the row end is clamped (its values are
+    // masked below); chunk slots no lane of the wave needs are skipped uniformly
+    typename C::R raw[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        if (kWave * j < nch) raw[j] = xr[min(lane + kWave * j, nch - 1)];
     double ss = 0.0;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int c = lane + kWave * j;
-        float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c < nch) t = load_act4(xr, 4 * (int64_t)c);
-        v[j][0] = t.x; v[j][1] = t.y; v[j][2] = t.z; v[j][3] = t.w;
+    for (int j = 0; j < NV; ++j)
+        if (lane + kWave * j < nch)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss += (double)v[j][e] * (double)v[j][e];
-    }
-    ss = wave_sum(ss);
-    const float r = rms_factor(ss, k, eps);
+            for (int e = 0; e < E; ++e) {
+                const double v = C::get(raw[j], e);
+                ss += v * v;
+            }
+    const float r = rms_factor(wave_sum(ss), k, eps);
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int c = lane + kWave * j;
-        if (c < nch) {
-            float4 gv = gain ? *reinterpret_cast<const float4 *>(gain + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
-            const float ge[4] = {gv.x, gv.y, gv.z, gv.w};
+        if (c < nch)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float y = __fmul_rn(v[j][e], r);
-                if (gain) y = __fmul_rn(y, ge[e]);
-                v[j][e] = y;
-                amax = fmaxf(amax, fabsf(y));
-            }
-        }
+            for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(scaled<T>(raw[j], e, r, gain, c)));
     }
-    amax = wave_max(amax);
-    const float sc = quant_scale(amax);
+    const float sc = quant_scale(wave_max(amax));
     int tot = 0;
-    uint32_t *qr = reinterpret_cast<uint32_t *>(q + row * (int64_t)k);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int c = lane + kWave * j;
         if (c < nch) {
-            const int a0 = quant_code(v[j][0], sc), a1 = quant_code(v[j][1], sc);
-            const int a2 = quant_code(v[j][2], sc), a3 = quant_code(v[j][3], sc);
-            tot += a0 + a1 + a2 + a3;
-            qr[c] = pack_codes4(a0, a1, a2, a3);
+            uint32_t w[E / 4];
+#pragma unroll
+            for (int h = 0; h < E / 4; ++h) {
+                int a[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a[e] = quant_code(scaled<T>(raw[j], 4 * h + e, r, gain, c), sc);
+                    tot += a[e];
+                }
+                w[h] = pack_codes4(a[0], a[1], a[2], a[3]);
+            }
+            int8_t *qc = q + row * (int64_t)k + (int64_t)E * c;
+            if constexpr (E == 8)
+                *reinterpret_cast<uint2 *>(qc) = make_uint2(w[0], w[1]);
+            else
+                *reinterpret_cast<uint32_t *>(qc) = w[0];
         }
     }
     tot = wave_sum_int(tot);
@@ -207,10 +242,11 @@ __global__ __launch_bounds__(256) void norm_quant_row_kernel(const T *__restrict
 
 constexpr int kFewRows = 2048;  // below this many rows a row gets a whole workgroup
 
-constexpr int kMaxCachedChunks = 32;  // 64 lanes * 32 chunks * 4 = 8192 elements per row
+constexpr int kMaxCachedChunks = 32;  // 64 lanes * 32 chunks of 16 bytes per row in registers
 
-static int chunk_bucket(int k) {
-    const int nch = (k / 4 + kWave - 1) / kWave;
+// 16-byte chunks of e elements per lane when a wave owns the row
+static int chunk_bucket(int k, int e = 4) {
+    const int nch = (k / e + kWave - 1) / kWave;
     int b = 1;
     while (b < nch) b *= 2;
     return b;
@@ -239,8 +275,8 @@ static void norm_quant_dispatch(const T *x, int64_t m, int k, const float *gain,
         return;
     }
     const dim3 grid((unsigned)((m + 3) / 4)), block(256);
-    const int nv = chunk_bucket(k);
-    if (nv > kMaxCachedChunks) {
+    const int nv = chunk_bucket(k, Chunk<T>::E);
+    if (k % Chunk<T>::E != 0 || nv > kMaxCachedChunks) {
         norm_quant_long_kernel<T><<<grid, block, 0, st>>>(x, m, k, gain, eps, q, s, sumq);
         if (path) *path += std::string("norm_quant_long<") + tn + ">;";
         return;
@@ -279,19 +315,22 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restric
     const float *hr = h + row * (int64_t)d;
     const TG *gr = g + row * (int64_t)d;
     float u[NV][4], gs[NV][4];
+    // all loads first, from a clamped chunk index (chunks past the row end are
+    // masked below), so that no load waits behind another
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = min(lane + kWave * j, nch - 1);
+        set4(u[j], load_f4(hr, c));
+        set4(gs[j], load_act4(gr, 4 * (int64_t)c));
+    }
     double ss = 0.0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-        const int c = lane + kWave * j;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-        if (c < nch) {
-            a = *reinterpret_cast<const float4 *>(hr + 4 * c);
-            b = load_act4(gr, 4 * (int64_t)c);
-        }
-        u[j][0] = a.x; u[j][1] = a.y; u[j][2] = a.z; u[j][3] = a.w;
-        gs[j][0] = silu_fast(b.x); gs[j][1] = silu_fast(b.y); gs[j][2] = silu_fast(b.z); gs[j][3] = silu_fast(b.w);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss += (double)u[j][e] * (double)u[j][e];
+        for (int e = 0; e < 4; ++e) gs[j][e] = silu_fast(gs[j][e]);
+        if (lane + kWave * j < nch)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += (double)u[j][e] * (double)u[j][e];
     }
     const float rh = rms_factor(wave_sum(ss), d, eps);
     double su = 0.0;
@@ -306,7 +345,7 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restric
             if (gnw) y = y * we[e];
             y = y * gs[j][e];
             u[j][e] = y;
-            su += (double)y * (double)y;
+            if (c < nch) su += (double)y * (double)y;
         }
         if (u_out && c < nch)
             *reinterpret_cast<float4 *>(u_out + row * (int64_t)d + 4 * c) = make_float4(u[j][0], u[j][1], u[j][2], u[j][3]);
