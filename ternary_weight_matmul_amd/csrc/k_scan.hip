@@ -9,11 +9,19 @@
 // 256-byte wave accesses at every step; loads of a block of U steps are issued
 // before the dependent chain of that block runs.
 //  * recurrent: one lane runs the whole sequence of its channel.
-//  * chunked:   t is split into C chunks. Pass 1 reduces each chunk but the last
-//    to its pair (A = prod f, B = the chunk's h started from 0). Pass 2 lane
-//    (b, j, c) folds the pairs of chunks < j into its carry h_in = A*h_in + B
-//    and re-runs chunk j from it. C lanes per channel fill the GPU when b*d is
-//    small; the price is re-reading the first C-1 chunks once more.
+//  * tiled (single pass, chunked): a workgroup of W waves owns 64 channels of
+//    one sequence and walks it in chunks of W*S steps. Wave w reduces its S
+//    steps of the chunk to the pair (A = prod f, B = h started from 0); the W
+//    pairs meet in LDS; each wave folds the pairs before its own into the
+//    chunk's carry, h_in = A*h_in + B, and re-runs its S steps from there. The
+//    loads of the next P chunks are in flight during a chunk's arithmetic and
+//    every element is read once, with streaming (non-temporal) loads and
+//    stores: 12 bytes per (b, t, c). Used when there are enough (sequence,
+//    64-channel) groups to occupy the GPU.
+//  * two-pass chunked: t is split into C chunks. Pass 1 reduces each chunk but
+//    the last to its pair; pass 2 lane (b, j, c) folds the pairs of chunks < j
+//    into its carry and re-runs chunk j from it. C lanes per channel fill the
+//    GPU when b*d is small; the price is re-reading the first C-1 chunks.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -120,6 +128,89 @@ __global__ __launch_bounds__(256) void scan_chunk_apply_kernel(const float *x, c
     if (h_last && j == chunks - 1) h_last[bi * d + c] = state;
 }
 
+// Every element of x, f and h is touched once; with NT the accesses are
+// marked non-temporal (worth it once the three tensors outgrow the 256 MB
+// memory-side cache, where a normal access could still hit).
+template <bool NT>
+__device__ __forceinline__ float ld_stream(const float *p) { return NT ? __builtin_nontemporal_load(p) : *p; }
+template <bool NT>
+__device__ __forceinline__ void st_stream(float *p, float v) {
+    if (NT) __builtin_nontemporal_store(v, p); else *p = v;
+}
+
+template <int W, int S, int P, bool NT>
+__global__ __launch_bounds__(W * 64) void scan_tiled_kernel(const float *x, const float *f, const float *h0,
+                                                            float *h, float *h_last, int64_t t, int64_t d,
+                                                            int64_t groups) {
+    constexpr int CH = W * S;  // steps per chunk; P chunks of loads run ahead of the arithmetic
+    __shared__ float2 pairs[2][W][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t bi = blockIdx.x / groups;
+    const int64_t c = (blockIdx.x % groups) * 64 + lane;
+    const bool live = c < d;
+    const int64_t cl = live ? c : d - 1;  // loads of idle lanes stay in bounds
+    const float *xp = x + bi * t * d + cl;
+    const float *fp = f + bi * t * d + cl;
+    float *hp = h + bi * t * d + c;
+    float carry = (h0 && live) ? h0[bi * d + c] : 0.0f;
+    const int64_t nchunks = (t + CH - 1) / CH;
+    float fa[P + 1][S], xa[P + 1][S];  // [0] = current chunk, [1..P] = chunks in flight
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int64_t ts = min((int64_t)(p * CH + w * S + s), t - 1);
+            fa[p][s] = ld_stream<NT>(fp + ts * d);
+            xa[p][s] = ld_stream<NT>(xp + ts * d);
+        }
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
+        const int64_t t0 = ch * CH + w * S;
+        if (ch + P < nchunks) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int64_t ts = min(t0 + P * CH + s, t - 1);
+                fa[P][s] = ld_stream<NT>(fp + ts * d);
+                xa[P][s] = ld_stream<NT>(xp + ts * d);
+            }
+        }
+        // steps past the end act as the identity (f = 1, x = 0)
+        float a = 1.0f, bb = 0.0f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const bool in = t0 + s < t;
+            fa[0][s] = in ? fa[0][s] : 1.0f;
+            xa[0][s] = in ? xa[0][s] : 0.0f;
+            bb = fa[0][s] * bb + xa[0][s];
+            a = a * fa[0][s];
+        }
+        pairs[ch & 1][w][lane] = make_float2(a, bb);
+        __syncthreads();
+        // fold: the state entering wave w, and the state after the whole chunk
+        float hin = carry, cn = carry;
+#pragma unroll
+        for (int v = 0; v < W; ++v) {
+            if (v == w) hin = cn;
+            const float2 pr = pairs[ch & 1][v][lane];
+            cn = pr.x * cn + pr.y;
+        }
+        float hs = hin;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            hs = fa[0][s] * hs + xa[0][s];
+            if (live && t0 + s < t) st_stream<NT>(hp + (t0 + s) * d, hs);
+        }
+        carry = cn;
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                fa[p][s] = fa[p + 1][s];
+                xa[p][s] = xa[p + 1][s];
+            }
+    }
+    if (h_last && live) h_last[bi * d + c] = carry;
+}
+
 __global__ void copy_state_kernel(const float *h0, float *h_last, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) h_last[i] = h0 ? h0[i] : 0.0f;
@@ -129,10 +220,17 @@ size_t scan_workspace_bytes(int64_t b, int64_t d, int chunks) {
     return chunks > 1 ? (size_t)b * (size_t)(chunks - 1) * (size_t)d * sizeof(float2) : 0;
 }
 
-// Recurrent when b*d lanes already fill the GPU or t is short; otherwise enough
+constexpr int64_t kTiledMinGroups = 128;     // (sequence, 64-channel) groups that occupy the GPU
+constexpr int64_t kTiledManyGroups = 512;    // from here 4-wave workgroups with 4 chunks in flight
+constexpr int64_t kStreamBytes = 256ll << 20;  // x, f and h together beyond the memory-side cache
+
+// Plan: 1 = recurrent, kScanTiled = single-pass tiled, c >= 2 = two-pass with c
+// chunks. Recurrent for explicit requests, t = 1, and (auto) short sequences;
+// tiled when there are enough channel groups; otherwise two passes with enough
 // chunks for ~128k lanes, each chunk at least 64 steps.
 int scan_pick_chunks(int64_t b, int64_t t, int64_t d, int mode) {
     if (mode == 1 || t <= 1) return 1;
+    if (b * ((d + 63) / 64) >= kTiledMinGroups) return (mode == 0 && t < 64) ? 1 : kScanTiled;
     const int64_t lanes = b * d;
     int64_t c = (131072 + lanes - 1) / lanes;
     if (mode == 2 && c < 2) c = 2;
@@ -150,6 +248,21 @@ hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h
     if (t == 0) {
         if (h_last) copy_state_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(h0, h_last, b * d);
         if (path) *path += "scan_empty;";
+        return hipGetLastError();
+    }
+    if (chunks == kScanTiled) {
+        // geometry measured on MI355X: 16-wave workgroups (8 steps each, one chunk
+        // ahead) while (sequence, channel-group) pairs are few; 4-wave
+        // workgroups with 4 chunks ahead once they fill the GPU
+        const int64_t groups = (d + 63) / 64;
+        const unsigned grid = (unsigned)(b * groups);
+        const bool nt = 12 * b * t * d > kStreamBytes;
+        const bool many = b * groups >= kTiledManyGroups;
+        if (many && nt) scan_tiled_kernel<4, 8, 4, true><<<grid, 256, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
+        else if (many) scan_tiled_kernel<4, 8, 4, false><<<grid, 256, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
+        else if (nt) scan_tiled_kernel<16, 8, 1, true><<<grid, 1024, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
+        else scan_tiled_kernel<16, 8, 1, false><<<grid, 1024, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
+        if (path) *path += std::string("scan_tiled<") + (many ? "4w" : "16w") + (nt ? ",nt" : "") + ">;";
         return hipGetLastError();
     }
     if (chunks <= 1) {

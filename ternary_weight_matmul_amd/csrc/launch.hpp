@@ -58,7 +58,9 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
 // Variant name of the kernel launch_contract picks, e.g. "tgemm<gates>".
 std::string contract_variant(int64_t m, int k, EpiKind epi, bool shared_a);
 
-// HGRN scan. chunks == 1 means the recurrent (sequential) kernel.
+// HGRN scan. chunks == 1 means the recurrent (sequential) kernel, kScanTiled
+// the single-pass tiled kernel, chunks >= 2 the two-pass chunked kernels.
+constexpr int kScanTiled = -1;
 size_t scan_workspace_bytes(int64_t b, int64_t d, int chunks);
 int scan_pick_chunks(int64_t b, int64_t t, int64_t d, int mode);
 hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h, float *h_last,

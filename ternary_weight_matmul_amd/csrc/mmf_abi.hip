@@ -101,7 +101,8 @@ hipError_t t_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared, h
 
 hipError_t t_scan(const float *x, const float *f, const float *h0, float *h, float *hl, int64_t b, int64_t t,
                   int64_t d, int chunks, void *ws, hipStream_t st, std::string *path) {
-    return timed(chunks > 1 ? "scan_chunk" : "scan_recurrent", b * t, (int)d, (int)d, st,
+    return timed(chunks == kScanTiled ? "scan_tiled" : chunks > 1 ? "scan_chunk" : "scan_recurrent", b * t, (int)d,
+                 (int)d, st,
                  [&] { return launch_scan(x, f, h0, h, hl, b, t, d, chunks, ws, st, path); });
 }
 

@@ -104,6 +104,11 @@ SCAN_CASES = [
     (2, 300, 96, "chunk", True),
     (1, 4099, 128, "chunk", False),
     (4, 2048, 256, "auto", True),
+    # enough (sequence, 64-channel) groups for the single-pass tiled kernel:
+    (8, 700, 1024, "chunk", True),     # ragged last chunk
+    (16, 300, 520, "auto", False),     # partial channel group
+    (2, 4100, 4096, "chunk", True),    # T >= 4096, streaming accesses
+    (16, 260, 2048, "chunk", True),    # many groups: 4-wave workgroups, ragged last chunk
 ]
 
 
@@ -121,6 +126,8 @@ def test_scan_parity(gpu, b, t, d, mode, with_h0):
     assert_close(host(h_last), ref[:, -1], rtol, "h_last")
     if mode == "recurrent":
         assert "scan_recurrent" in mmf.last_path()
+    elif b * ((d + 63) // 64) >= 128:
+        assert "scan_tiled" in mmf.last_path()
 
 
 def test_scan_in_place_and_empty(gpu):
@@ -137,6 +144,47 @@ def test_scan_in_place_and_empty(gpu):
     h_last = torch.zeros((2, 64), device=gpu)
     mmf.hgrn_scan_fwd(torch.empty((2, 0, 64), device=gpu), torch.empty((2, 0, 64), device=gpu), h0, h_last=h_last)
     assert torch.equal(h_last, h0)
+
+
+def test_scan_tiled_in_place(gpu):
+    mmf = _mmf()
+    x, f = synth.scan_inputs(4, 390, 2048, 405)
+    h0 = synth.activations((4, 2048), 406)
+    ref = oracle.hgrn_scan(x, f, h0)
+    xd = dev(x, gpu)
+    h = mmf.hgrn_scan_fwd(xd, dev(f, gpu), dev(h0, gpu), "chunk", out=xd)
+    assert "scan_tiled" in mmf.last_path()
+    assert h.data_ptr() == xd.data_ptr()
+    assert_close(host(h), ref, 1e-4, "tiled in place")
+
+
+def test_scan_c5_full_size_sampled(gpu):
+    """The long-sequence stress shape: B=16, T=32768, d=2048, f = sigmoid(N(2,1)), chunked,
+    in the configuration the layer uses. Each sequence is generated with its own seed; the
+    oracle runs the whole sequence for 64 sampled channels (4 per sequence)."""
+    import torch
+    mmf = _mmf()
+    b, t, d = 16, 32768, 2048
+    xd = torch.empty((b, t, d), device=gpu)
+    fd = torch.empty((b, t, d), device=gpu)
+    pick = np.stack([synth.rng(5500 + i).choice(d, size=4, replace=False) for i in range(b)])
+    xs, fs = [], []
+    for i in range(b):
+        x, f = synth.scan_inputs(1, t, d, 5 * 1000 + i)
+        xd[i].copy_(torch.from_numpy(x[0]))
+        fd[i].copy_(torch.from_numpy(f[0]))
+        xs.append(x[0][:, pick[i]].copy())
+        fs.append(f[0][:, pick[i]].copy())
+        del x, f
+    h_last = torch.empty((b, d), device=gpu)
+    h = mmf.hgrn_scan_fwd(xd, fd, None, "chunk", h_last=h_last)
+    assert "scan_tiled" in mmf.last_path()
+    idx = torch.from_numpy(pick).to(gpu)
+    got = torch.gather(h, 2, idx[:, None, :].expand(b, t, 4)).cpu().numpy()
+    got_last = torch.gather(h_last, 1, idx).cpu().numpy()
+    ref = oracle.hgrn_scan(np.stack(xs), np.stack(fs))
+    assert_close(got, ref, 1e-3, "h (sampled channels)")
+    assert_close(got_last, ref[:, -1], 1e-3, "h_last (sampled channels)")
 
 
 def test_scan_limits_zero_and_unit_gate(gpu):
