@@ -12,15 +12,10 @@ constexpr int kWave = 64;
 
 // ---- activation element types -------------------------------------------------
 // fp32 and bf16 (stored as raw uint16 bits). bf16 -> fp32 is exact; fp32 -> bf16
-// rounds to nearest even.
+// rounds to nearest even (gfx950's v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float load_act(const float *p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_act(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }

@@ -115,9 +115,120 @@ __device__ __forceinline__ void wave_epilogue_t(const ContractArgs &p, const i32
         }
 }
 
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
+
+// The same epilogue without stage probes and with every element type fixed at
+// compile time (RT residual, OT output of linear/resid, AT the g or z output),
+// addressed as one wave-uniform base plus 32-bit lane offsets. FULL: the wave's
+// block lies inside the output, so no row or column checks. Bit-identical to
+// epilogue_vals: the same operations in the same order.
+template <int EPI, int NG, int JN, typename RT, typename OT, typename AT, bool FULL>
+__device__ __forceinline__ void fast_epilogue(const ContractArgs &p, const i32x16 (&acc)[2][NG][JN], int64_t mw,
+                                              int cw, int lane) {
+    constexpr int RB = 8;
+    const int lr = lane & 31, lg = lane >> 5;
+    const int64_t M = p.m;
+    const int nc = p.nc;
+    const int64_t wbase = mw * nc + cw;          // element (mw, cw), wave-uniform
+    const int lane_rel = lg * 4 * nc + lr;        // lane's offset from it (row lg*4, column lr)
+    float sw[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) sw[g] = weight_sw(p.mu[g]);
+    const RT *res = static_cast<const RT *>(p.res) + wbase;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += RB) {
+            int32_t sq[RB][NG];
+            float dq[RB][NG];
+            float pre[RB][JN];
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+                const int r = r0 + rr;
+                const int rowoff = i * 32 + (r >> 2) * 8 + (r & 3);
+                int64_t m = mw + lg * 4 + rowoff;
+                if (!FULL) m = m < M ? m : M - 1;
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    sq[rr][g] = p.sumq[g][m];
+                    dq[rr][g] = __builtin_amdgcn_rcpf(p.s[g][m] * sw[g]);
+                }
+                if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+                    for (int j = 0; j < JN; ++j) {
+                        int rel = lane_rel + rowoff * nc + j * 32;
+                        if (!FULL) {
+                            const int c = cw + j * 32 + lr;
+                            rel = (int)(m - mw) * nc + (c < nc ? c : nc - 1) - cw;
+                        }
+                        pre[rr][j] = to_f32(res[rel]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+                const int r = r0 + rr;
+                const int rowoff = i * 32 + (r >> 2) * 8 + (r & 3);
+                if (!FULL && mw + lg * 4 + rowoff >= M) continue;
+#pragma unroll
+                for (int j = 0; j < JN; ++j) {
+                    if (!FULL && cw + j * 32 + lr >= nc) continue;
+                    const int rel = lane_rel + rowoff * nc + j * 32;
+                    float y[NG];
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) y[g] = (float)(acc[i][g][j][r] - sq[rr][g]) * dq[rr][g];
+                    if constexpr (EPI == EPI_LINEAR) {
+                        (static_cast<OT *>(p.out0) + wbase)[rel] = from_f32<OT>(y[0]);
+                    } else if constexpr (EPI == EPI_RESID) {
+                        (static_cast<OT *>(p.out0) + wbase)[rel] = from_f32<OT>(pre[rr][j] + y[0]);
+                    } else if constexpr (EPI == EPI_GATES) {
+                        const float f = sigmoid_fast(y[1]);
+                        const float xt = (1.0f - f) * silu_fast(y[0]);
+                        (static_cast<float *>(p.out0) + wbase)[rel] = f;
+                        (static_cast<float *>(p.out1) + wbase)[rel] = xt;
+                        (static_cast<AT *>(p.out2) + wbase)[rel] = from_f32<AT>(y[2]);
+                    } else if constexpr (EPI == EPI_GLU) {
+                        (static_cast<AT *>(p.out0) + wbase)[rel] = from_f32<AT>(silu_fast(y[0]) * y[1]);
+                    }
+                }
+            }
+        }
+}
+
+template <int EPI, int NG, int JN, bool FULL>
+__device__ __forceinline__ void fast_dispatch(const ContractArgs &p, const i32x16 (&acc)[2][NG][JN], int64_t mw,
+                                              int cw, int lane) {
+    const bool ob = p.out_type == ACT_BF16, rb = p.res_type == ACT_BF16, ab = p.aux_type == ACT_BF16;
+    if constexpr (EPI == EPI_GATES || EPI == EPI_GLU) {
+        if (ab) fast_epilogue<EPI, NG, JN, float, float, uint16_t, FULL>(p, acc, mw, cw, lane);
+        else fast_epilogue<EPI, NG, JN, float, float, float, FULL>(p, acc, mw, cw, lane);
+    } else if constexpr (EPI == EPI_RESID) {
+        if (ob && rb) fast_epilogue<EPI, NG, JN, uint16_t, uint16_t, float, FULL>(p, acc, mw, cw, lane);
+        else if (ob) fast_epilogue<EPI, NG, JN, float, uint16_t, float, FULL>(p, acc, mw, cw, lane);
+        else if (rb) fast_epilogue<EPI, NG, JN, uint16_t, float, float, FULL>(p, acc, mw, cw, lane);
+        else fast_epilogue<EPI, NG, JN, float, float, float, FULL>(p, acc, mw, cw, lane);
+    } else if constexpr (EPI == EPI_LINEAR) {
+        if (ob) fast_epilogue<EPI, NG, JN, float, uint16_t, float, FULL>(p, acc, mw, cw, lane);
+        else fast_epilogue<EPI, NG, JN, float, float, float, FULL>(p, acc, mw, cw, lane);
+    }
+}
+
 template <int EPI, int NG, int JN>
 __device__ __forceinline__ void wave_epilogue(const ContractArgs &p, const i32x16 (&acc)[2][NG][JN], int64_t mw,
                                               int cw, int lane) {
+    // fast path: no stage probes (and not the decode step's state update, which
+    // reaches this kernel only for batches above the GEMV path's limit)
+    if (EPI != EPI_GATES_STEP && !p.acc_probe && !p.aux_probe) {
+        if (mw + 64 <= p.m && cw + 32 * JN <= p.nc)
+            fast_dispatch<EPI, NG, JN, true>(p, acc, mw, cw, lane);
+        else
+            fast_dispatch<EPI, NG, JN, false>(p, acc, mw, cw, lane);
+        return;
+    }
     // the residual comes in the activation type; the recurrent state is fp32
     if constexpr (EPI == EPI_RESID) {
         if (p.res_type == ACT_BF16) {

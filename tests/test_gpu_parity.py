@@ -334,6 +334,44 @@ def test_layer_deterministic(gpu):
     assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
 
 
+@pytest.mark.parametrize("d,inner,b,t,act,gains", [
+    (256, 512, 2, 100, "bf16", None),        # ragged tiles
+    (256, 512, 2, 128, "bf16", "shared"),    # whole tiles
+    (128, 352, 3, 70, "f32", "distinct"),    # split activations, fp32
+    (512, 1024, 1, 256, "f32", None),
+])
+def test_layer_probe_does_not_change_results(gpu, d, inner, b, t, act, gains):
+    """Without a probe the contractions take the typed fast epilogue; with one, the
+    generic epilogue that the stage checks cover. Both must give the same bits."""
+    import torch
+    mmf = _mmf()
+    _, P = make_pair(d, inner, 730 + t, gpu, gains)
+    xs = synth.activations((b, t, d), 731 + t, act)
+    x = bf16_tensor(xs, gpu) if act == "bf16" else dev(xs, gpu)
+    h0 = dev(synth.activations((b, d), 732), gpu)
+    out_a, hl_a = mmf.layer_fwd(P, x, h0, want_h_last=True, mode="chunk")
+    probe = mmf.LayerProbe(b * t, d, inner, gpu, shared_ifg=gains != "distinct")
+    out_b, hl_b = mmf.layer_fwd(P, x, h0, want_h_last=True, mode="chunk", probe=probe)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    assert torch.equal(hl_a, hl_b)
+
+
+@pytest.mark.parametrize("m,k,n,dt", [(300, 256, 200, "bf16"), (256, 512, 256, "f32"), (130, 2048, 4096, "bf16")])
+def test_bitlinear_probe_does_not_change_results(gpu, m, k, n, dt):
+    import torch
+    mmf = _mmf()
+    w = synth.rng(741 + m).standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    pl = mmf.ternary_pack(dev(w, gpu))
+    xs = synth.activations((m, k), 742 + m, dt)
+    x = bf16_tensor(xs, gpu) if dt == "bf16" else dev(xs, gpu)
+    y_a = mmf.bitlinear_fwd(x, pl)
+    acc = torch.empty((m, n), dtype=torch.int32, device=gpu)
+    y_b = mmf.bitlinear_fwd(x, pl, acc_out=acc)
+    torch.cuda.synchronize()
+    assert torch.equal(y_a, y_b)
+
+
 def test_layer_empty_sequence(gpu):
     import torch
     mmf = _mmf()
