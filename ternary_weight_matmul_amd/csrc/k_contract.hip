@@ -571,18 +571,17 @@ __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p,
 // MFMA, so a GEMV costs about one memory round trip. Wave partial sums are
 // combined with LDS integer atomics (exact, order-free). RT is the element
 // type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
-template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT>
+template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT, int EPT>
 __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const int nslices) {
     constexpr int NA = SHARED_A ? 1 : NG;
-    __shared__ int32_t red[MB * NG * 256];
+    constexpr int PART = MB * NG * 256;  // one wave's partial sums
+    extern __shared__ int32_t part[];    // [waves][PART]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int lc = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int K = p.k, KW = K >> 4;
     const int64_t M = p.m;
-    const int gn = n0 + lc;
-    const bool bvec = (KW & 3) == 0;
-    for (int i = tid; i < MB * NG * 256; i += blockDim.x) red[i] = 0;
+    const int gn = min(n0 + lc, p.nc - 1);  // columns past nc load a valid row; never stored
     // weight scales, the quantiser's per-row scales and sums and the epilogue
     // operands (residual / old state) do not depend on the contraction: load
     // them before it, unconditionally (clamped to a valid element; the values
@@ -592,7 +591,6 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
 #pragma unroll
     for (int g = 0; g < NG; ++g) mu_v[g] = *p.mu[g];
     constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
-    constexpr int EPT = 4;  // epilogue outputs per thread with the smallest block (4 waves, MB = 4)
     float pre[EPT], sc_e[EPT][NG];
     int32_t sq_e[EPT][NG];
     const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
@@ -616,32 +614,39 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
 #pragma unroll
         for (int g = 0; g < NG; ++g) acc[mb][g] = i32x4{};
 
+    // Every load of a slice is unconditional: words past the row end are
+    // clamped and then zeroed (offset code 0 adds nothing to sum c*q), rows
+    // past m are clamped (their sums are never stored).
+    const bool whole = (KW % (4 * WPL)) == 0;
     for (int sl = wave; sl < nslices; sl += nw) {
         const int w0 = sl * 4 * WPL + lg * WPL;
         uint32_t bw[NG][WPL];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            const uint32_t *src = p.B[g] + (int64_t)gn * KW + w0;
-            if (gn < p.nc && bvec && w0 + WPL <= KW) {
+            const uint32_t *src = p.B[g] + (int64_t)gn * KW;
+            if (whole) {
 #pragma unroll
                 for (int q = 0; q < WPL / 4; ++q) {
-                    const uint4 v = reinterpret_cast<const uint4 *>(src)[q];
+                    const uint4 v = reinterpret_cast<const uint4 *>(src + w0)[q];
                     bw[g][4 * q] = v.x; bw[g][4 * q + 1] = v.y; bw[g][4 * q + 2] = v.z; bw[g][4 * q + 3] = v.w;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < WPL; ++j) bw[g][j] = (gn < p.nc && w0 + j < KW) ? src[j] : 0u;
+                for (int j = 0; j < WPL; ++j) {
+                    const uint32_t v = src[min(w0 + j, KW - 1)];
+                    bw[g][j] = w0 + j < KW ? v : 0u;
+                }
             }
         }
         i32x4 a[MB][NA][WPL];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int64_t row = mb * 16 + lc;
+            const int64_t row = min((int64_t)(mb * 16 + lc), M - 1);
 #pragma unroll
             for (int q = 0; q < NA; ++q) {
-                const i32x4 *src = reinterpret_cast<const i32x4 *>(p.A[q] + row * K) + w0;
+                const i32x4 *src = reinterpret_cast<const i32x4 *>(p.A[q] + row * K);
 #pragma unroll
-                for (int j = 0; j < WPL; ++j) a[mb][q][j] = (row < M && w0 + j < KW) ? src[j] : i32x4{};
+                for (int j = 0; j < WPL; ++j) a[mb][q][j] = src[whole ? w0 + j : min(w0 + j, KW - 1)];
             }
         }
 #pragma unroll
@@ -654,17 +659,19 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
                     acc[mb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][SHARED_A ? 0 : g][j], b, acc[mb][g], 0, 0, 0);
             }
     }
-    __syncthreads();
+    // each wave's partial sums into its own LDS slot; summed below in wave order
+    int32_t *mine = part + wave * PART;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) atomicAdd(&red[(mb * NG + g) * 256 + (4 * lg + i) * 16 + lc], acc[mb][g][i]);
+            for (int i = 0; i < 4; ++i) mine[(mb * NG + g) * 256 + (4 * lg + i) * 16 + lc] = acc[mb][g][i];
     __syncthreads();
     float sw[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) sw[g] = __fdiv_rn(1.0f, fmaxf(mu_v[g], 1e-5f));
+    const int active = nw < nslices ? nw : nslices;  // waves that ran a slice
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int idx = tid + e * blockDim.x;
@@ -675,7 +682,10 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
             float dq[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                v[g] = red[(mb * NG + g) * 256 + r * 16 + c] - sq_e[e][g];
+                const int o = (mb * NG + g) * 256 + r * 16 + c;
+                int32_t sum = 0;
+                for (int w = 0; w < active; ++w) sum += part[w * PART + o];
+                v[g] = sum - sq_e[e][g];
                 dq[g] = __builtin_amdgcn_rcpf(sc_e[e][g] * sw[g]);
             }
             epilogue_vals<EPI, NG, true>(p, m, n0 + c, v, dq, pre[e]);
@@ -709,9 +719,20 @@ template <int NG, int MB, bool SH, int EPI, int WPL, typename RT>
 static void run_gemv_mb(const ContractArgs &a, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 4 * WPL - 1) / (4 * WPL);
-    int waves = nslices < 16 ? nslices : 16;
+    // per-wave partial sums take MB*NG KB of LDS per wave: at most 64 KB in all
+    constexpr int kMaxWaves = 64 / (MB * NG) < 16 ? 64 / (MB * NG) : 16;
+    static_assert(kMaxWaves >= MB, "the epilogue needs a wave per row block");
+    int waves = nslices < kMaxWaves ? nslices : kMaxWaves;
     if (waves < MB) waves = MB;  // the epilogue covers MB*256 outputs with at most 4 per thread
-    tgemv_kernel<NG, MB, SH, EPI, WPL, RT><<<(unsigned)((a.nc + 15) / 16), waves * 64, 0, st>>>(a, nslices);
+    const unsigned grid = (unsigned)((a.nc + 15) / 16);
+    const size_t lds = (size_t)waves * MB * NG * 256 * sizeof(int32_t);
+    const int ept = (MB * 256 + waves * 64 - 1) / (waves * 64);
+    switch (ept) {
+        case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 2: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 3: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 3><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 4><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+    }
 }
 
 template <int NG, int JN, int EPI>
@@ -725,10 +746,10 @@ static void run_gemm_dma(const ContractArgs &a, hipStream_t st) {
 
 template <int NG, bool SH, int EPI, typename RT>
 static void run_gemv_t(const ContractArgs &a, hipStream_t st) {
-    constexpr int NA = SH ? 1 : NG;
+    // 4 words (64 k) per lane per slice: measured fastest at the 1.3B decode shapes
     switch ((int)((a.m + 15) / 16)) {
-        case 1: run_gemv_mb<NG, 1, SH, EPI, (NA <= 2 ? 8 : 4), RT>(a, st); break;
-        case 2: run_gemv_mb<NG, 2, SH, EPI, (NA <= 1 ? 8 : 4), RT>(a, st); break;
+        case 1: run_gemv_mb<NG, 1, SH, EPI, 4, RT>(a, st); break;
+        case 2: run_gemv_mb<NG, 2, SH, EPI, 4, RT>(a, st); break;
         case 3: run_gemv_mb<NG, 3, SH, EPI, 4, RT>(a, st); break;
         default: run_gemv_mb<NG, 4, SH, EPI, 4, RT>(a, st); break;
     }
