@@ -45,7 +45,28 @@ def parse():
     ap.add_argument("--decode", type=int, default=512)
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="launch decode steps eagerly instead of a HIP graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (for scaling HBM counters)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it scales the counters
+    of the library's kernels to bytes."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, device="cuda")
+    b = torch.empty(n, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.copy_(a)
+    e0.record()
+    for _ in range(2):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 2
+    print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": 3, "us_per_launch": round(ms * 1000, 1),
+                      "read_plus_write_GBps": round(8 * n / (ms / 1000) / 1e9, 1)}), flush=True)
 
 
 ACT_BYTES = 2  # bf16 activations
@@ -126,6 +147,9 @@ def stored_traffic(key: str):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)

@@ -214,12 +214,10 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
  * is bracketed by two HIP events recorded on the call's stream, and one
  * record per launch is kept: the kernel variant, its shape and the event
  * pair. This is the only part of the library that allocates (HIP events,
- * host records). Under stream capture the events become external event-record
- * nodes of the graph: each replay re-records them, and a collect after a
- * replay returns that replay's durations.
- *  mmf_timing_enable(1) clears earlier records (a graph captured before then
- *  must not be replayed again while timing is used); mmf_timing_enable(0)
- *  stops recording and keeps the records.
+ * created without the system-scope fence; host records), and it must stay
+ * off while a stream is being captured into a HIP graph.
+ *  mmf_timing_enable(1) clears earlier records; mmf_timing_enable(0) stops
+ *  recording and keeps the records.
  *  mmf_timing_collect synchronises on the recorded events, copies up to
  *  `capacity` records into `out` (which may be NULL when capacity is 0) and
  *  returns the number recorded in *count.

@@ -57,24 +57,24 @@ thread_local size_t g_events_used = 0;
 hipEvent_t timing_event() {
     if (g_events_used == g_events.size()) {
         hipEvent_t e = nullptr;
-        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        // without the system-scope fence an event costs the stream far less, so
+        // the interval between a kernel's two events stays close to the kernel
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
         g_events.push_back(e);
     }
     return g_events[g_events_used++];
 }
 
-// The events bracket the launch on its stream. Under stream capture they are
-// recorded as external event nodes of the graph, so every replay of the graph
-// re-records them: a collect after a replay reads that replay's durations.
+// The events bracket the launch on its stream.
 template <class F>
 hipError_t timed(const std::string &kernel, int64_t m, int n, int k, hipStream_t st, F &&launch) {
     if (!g_timing) return launch();
     hipEvent_t a = timing_event(), b = timing_event();
     if (!a || !b) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecordWithFlags(a, st, hipEventRecordExternal);
+    hipError_t e = hipEventRecord(a, st);
     if (e != hipSuccess) return e;
     if ((e = launch()) != hipSuccess) return e;
-    if ((e = hipEventRecordWithFlags(b, st, hipEventRecordExternal)) != hipSuccess) return e;
+    if ((e = hipEventRecord(b, st)) != hipSuccess) return e;
     g_recs.push_back(TimingRec{kernel, m, n, k, a, b});
     return hipSuccess;
 }
