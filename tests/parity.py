@@ -141,3 +141,73 @@ def check_layer_stages(L: "oracle.Layer", x: np.ndarray, h0, pr: dict, out_gpu: 
     assert_equal(pr["acc_down"], acc_dn, "acc_down")
     out_ref = pr["x1"].astype(np.float64) + oracle.dequant(acc_dn, pr["scale_z"], L.down.mu)
     assert_close(out_gpu.reshape(m, d), out_ref, rtol_out, "out")
+
+
+def probe_rows(probe, rows) -> dict:
+    """The probe's row-indexed stages for the given rows only (host arrays)."""
+    import torch
+    from ternary_weight_matmul_amd.binding import PROBE_FIELDS
+    idx = torch.as_tensor(np.asarray(rows), device=probe.acc_ifg.device)
+    out = {"codes_x": [t.index_select(0, idx).cpu().numpy() for t in probe.codes_x],
+           "scale_x": [t.index_select(0, idx).cpu().numpy() for t in probe.scale_x]}
+    for name in PROBE_FIELDS:
+        out[name] = getattr(probe, name).index_select(0, idx).cpu().numpy()
+    return out
+
+
+def check_layer_sampled(L: "oracle.Layer", x: np.ndarray, h0, probe, out_gpu, act: str, b: int, t: int,
+                        rows, chans, scan_rtol: float):
+    """Stage-fed parity at full size on sampled tokens: every stage of the sampled rows against the
+    oracle applied to the GPU's own stage inputs of those rows; the scan over the whole sequence of
+    the sampled (sequence, channel) pairs, fed with the GPU's gate outputs of those channels."""
+    import torch
+    d = L.d
+    eps = L.eps
+    rows = np.asarray(sorted(rows))
+    pr = probe_rows(probe, rows)
+    xr = x.reshape(b * t, d)[rows].astype(np.float32)
+    rtol_out = 1e-4 if act == "f32" else 2e-2
+    projs = [L.i, L.f, L.g]
+    qq, ss, _ = oracle.quantize(xr, L.i.gain, eps)
+    assert_equal(pr["codes_x"][0], qq, "codes_x")
+    assert_equal(pr["scale_x"][0], ss, "scale_x")
+    acc = pr["acc_ifg"].reshape(len(rows), 3, d)
+    hat = []
+    for q in range(3):
+        ref = oracle.ternary_matmul(pr["codes_x"][0], projs[q].t)
+        assert_equal(acc[:, q], ref, "acc_%s" % "ifg"[q])
+        hat.append(oracle.dequant(ref, pr["scale_x"][0], projs[q].mu))
+    f_ref, xt_ref = oracle.mixer_gates(hat[0], hat[1])
+    assert_close(pr["f"], f_ref, 1e-4, "f")
+    assert_close(pr["xt"], xt_ref, 1e-4, "xt")
+    assert_close(pr["g"], hat[2], rtol_out, "g")
+    # the scan: whole sequences of the sampled channels
+    for (bi, c) in chans:
+        xs = probe.xt.view(b, t, d)[bi, :, c].cpu().numpy().reshape(1, t, 1)
+        fs = probe.f.view(b, t, d)[bi, :, c].cpu().numpy().reshape(1, t, 1)
+        hs = probe.h.view(b, t, d)[bi, :, c].cpu().numpy()
+        h0c = None if h0 is None else np.asarray(h0)[bi, c].reshape(1, 1)
+        assert_close(hs, oracle.hgrn_scan(xs, fs, h0c).reshape(t), scan_rtol, "h[%d,:,%d]" % (bi, c))
+    u_ref = oracle.gnorm_swish(pr["h"], pr["g"], L.g_norm_w, eps)
+    assert_close(pr["u"], u_ref, 1e-4, "u")
+    qq, ss, _ = oracle.quantize(pr["u"], L.o.gain, eps)
+    assert_equal(pr["codes_u"], qq, "codes_u")
+    assert_equal(pr["scale_u"], ss, "scale_u")
+    acc_o = oracle.ternary_matmul(pr["codes_u"], L.o.t)
+    assert_equal(pr["acc_o"], acc_o, "acc_o")
+    assert_close(pr["x1"], xr.astype(np.float64) + oracle.dequant(acc_o, pr["scale_u"], L.o.mu), 1e-4, "x1")
+    qq, ss, _ = oracle.quantize(pr["x1"], L.gate.gain, eps)
+    assert_equal(pr["codes_x1"], qq, "codes_x1")
+    assert_equal(pr["scale_x1"], ss, "scale_x1")
+    acc_g = oracle.ternary_matmul(pr["codes_x1"], L.gate.t)
+    assert_equal(pr["acc_gate"], acc_g, "acc_gate")
+    ab = oracle.dequant(acc_g, pr["scale_x1"], L.gate.mu)
+    assert_close(pr["z"], oracle.silu(ab[:, :L.inner]) * ab[:, L.inner:], rtol_out, "z")
+    qq, ss, _ = oracle.quantize(pr["z"], L.down.gain, eps)
+    assert_equal(pr["codes_z"], qq, "codes_z")
+    assert_equal(pr["scale_z"], ss, "scale_z")
+    acc_dn = oracle.ternary_matmul(pr["codes_z"], L.down.t)
+    assert_equal(pr["acc_down"], acc_dn, "acc_down")
+    out_rows = host(out_gpu.reshape(b * t, d).index_select(0, torch.as_tensor(rows, device=out_gpu.device)))
+    out_ref = pr["x1"].astype(np.float64) + oracle.dequant(acc_dn, pr["scale_z"], L.down.mu)
+    assert_close(out_rows, out_ref, rtol_out, "out")

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 from ternary_weight_matmul_amd import synth
-from parity import assert_close, assert_equal, bf16_tensor, check_layer_stages, dev, host, make_pair, packed_words
+from parity import (assert_close, assert_equal, bf16_tensor, check_layer_sampled, check_layer_stages, dev, host,
+                    make_pair, packed_words)
 
 pytestmark = pytest.mark.gpu
 
@@ -264,7 +265,9 @@ DECODE_CASES = [
     (64, "bf16", "shared", 256, 512, "tgemv"),
     (65, "bf16", "shared", 256, 512, "tgemm"),
     (3, "bf16", "shared", 256, 4160, "tgemv"),      # wide down_proj input rows
-    (16, "bf16", None, 2048, 5632, "tgemv"),        # the 1.3B decode shape
+    (1, "bf16", None, 2048, 5632, "tgemv"),         # the 1.3B decode shape at its three batches
+    (16, "bf16", None, 2048, 5632, "tgemv"),
+    (64, "bf16", None, 2048, 5632, "tgemv"),
     (8, "bf16", None, 2560, 6912, "tgemv"),         # the 2.7B decode shape
 ]
 
@@ -286,6 +289,58 @@ def test_decode_step_stages(gpu, b, act, gains, d, inner, family):
     pr = probe.host()
     check_layer_stages(L, x[:, None, :], h0, pr, host(out), act, shared=shared)
     assert np.array_equal(host(hd), pr["h"])
+
+
+def test_decode_512_steps_then_stages(gpu):
+    """The decode sequence length of the 1.3B decode workload: 512 steps of one layer at batch 16
+    from a carried state h ~ N(0, 1), then the 513th step checked stage by stage."""
+    import torch
+    mmf = _mmf()
+    d, inner, b = 2048, 5632, 16
+    L, P = make_pair(d, inner, 3000, gpu)
+    h = dev(synth.activations((b, d), 3001), gpu)
+    xs = synth.activations((513, b, d), 3002, "bf16")
+    xd = bf16_tensor(xs, gpu)
+    ws = torch.empty(mmf.layer_workspace_size(P, b, 1), dtype=torch.uint8, device=gpu)
+    out = torch.empty((b, d), dtype=torch.bfloat16, device=gpu)
+    for s_ in range(512):
+        mmf.layer_decode_step(P, xd[s_], h, out=out, ws=ws)
+    h_before = host(h)
+    assert np.all(np.isfinite(h_before))
+    probe = mmf.LayerProbe(b, d, inner, gpu)
+    out = mmf.layer_decode_step(P, xd[512], h, probe=probe, ws=ws)
+    torch.cuda.synchronize()
+    check_layer_stages(L, xs[512][:, None, :], h_before, probe.host(), host(out), "bf16")
+
+
+FULL_SIZE_PREFILL = [
+    # shape, batch, tokens, config seed: one layer of each prefill workload at full size, bf16,
+    # in the launch configuration the benchmark uses (scan mode auto)
+    ("370M", 8, 2048, 2),
+    ("1.3B", 16, 2048, 3),
+    ("2.7B", 4, 4096, 4),
+]
+
+
+@pytest.mark.parametrize("shape,b,t,seed", FULL_SIZE_PREFILL)
+def test_layer_full_size_sampled(gpu, shape, b, t, seed):
+    """Every stage of 48 sampled tokens (and the first and last) against the oracle fed with the
+    GPU's stage inputs; the scan over whole sequences for 6 sampled channels."""
+    import torch
+    mmf = _mmf()
+    d, inner, _ = synth.SHAPES[shape]
+    L, P = make_pair(d, inner, synth.layer_seed(seed, 0), gpu)
+    xs = synth.activations((b, t, d), seed * 10 + 1, "bf16")
+    probe = mmf.LayerProbe(b * t, d, inner, gpu)
+    out, _ = mmf.layer_fwd(P, bf16_tensor(xs, gpu), None, want_h_last=True, mode="auto", probe=probe)
+    torch.cuda.synchronize()
+    path = mmf.last_path()
+    assert "tgemm_dma" in path and "scan_tiled" in path, path
+    r = synth.rng(seed * 10 + 7)
+    rows = set(r.choice(b * t, size=48, replace=False).tolist()) | {0, b * t - 1}
+    chans = [(int(r.integers(b)), int(r.integers(d))) for _ in range(6)]
+    check_layer_sampled(L, xs, None, probe, out, "bf16", b, t, rows, chans,
+                        scan_rtol=1e-3 if t >= 4096 else 1e-4)
 
 
 def test_decode_steps_equal_prefill(gpu):
