@@ -90,8 +90,14 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
     norm_quant<T> (m rows of k): x read (sizeof T) + codes written (1 B) per element, 8 B per row.
     gnorm_quant<T>: h (fp32) and g (sizeof T) read + codes written per element, 8 B per row.
     scan (m = b t, k = d): f and x~ read, h written, 12 B per element.
+    decode_step_xcd (m = b, n = d, k = inner; one whole decode step of a block): ops =
+      2 b (4 d^2 + 3 d inner); bytes = all packed weights (4 d^2 + 3 d inner) / 4 + x read
+      and out written (activation dtype) + h read and written (fp32) per row element.
     """
     base, args = _kind(kernel)
+    if base == "decode_step_xcd":
+        wts = 4.0 * n * n + 3.0 * n * k
+        return 2.0 * m * wts, wts / 4.0 + m * n * (2.0 * ACT_BYTES + 8.0)
     if base in ("tgemm", "tgemm_dma", "tgemv"):
         epi = args[0]
         na = 3 if "split_a" in args else 1

@@ -203,10 +203,35 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
  *  x, out : [b][d] in dtype act.  h : [b][d] fp32, read as h_{t-1} and
  *  overwritten with h_t.  Equivalent to mmf_layer_fwd with t = 1, h0 = h.
  *  Errors as mmf_layer_fwd (workspace from mmf_layer_workspace_size(w, b, 1)).
+ *  Two implementations give the same bits: separate kernels per stage, and
+ *  (b <= 16, no probe, equal i/f/g gains, d and inner multiples of 256, d <=
+ *  3072, inner <= 7136) one kernel run by the 32 workgroups of one XCD with
+ *  barriers between the stages (see mmf_set_decode_kernel). Calls of the
+ *  one-XCD kernel share device-wide barrier state: two of them must not run
+ *  at the same time on one device (calls on one stream never do). The first
+ *  call on a device checks the workgroup-to-XCD placement synchronously; a
+ *  call made while the stream is being captured before that check has run
+ *  takes the separate kernels.
  */
 mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype act,
                                  int64_t b, float *h, void *ws, size_t ws_bytes,
                                  const mmf_layer_probe *probe, hipStream_t stream);
+
+/*
+ * mmf_set_decode_kernel -- which implementation mmf_layer_decode_step uses,
+ * process-wide: 0 = the faster implementation for the shape (default; at
+ * present always the separate kernels, which measure faster on MI355X);
+ * 1 = always the separate kernels; 2 = only the one-XCD kernel (UNSUPPORTED
+ * where it does not apply). INVALID_ARG for other values.
+ */
+mmf_status mmf_set_decode_kernel(int mode);
+
+/*
+ * mmf_decode_expired_waits -- how many barrier waits of the one-XCD decode
+ * kernel gave up (each wait is bounded, about a second; a non-zero count means
+ * a result was computed from incomplete data). Synchronous; for diagnostics.
+ */
+mmf_status mmf_decode_expired_waits(uint32_t *count);
 
 /*
  * Measurement support (not part of the computation). While enabled on a

@@ -19,6 +19,7 @@ __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
     "ternary_pack", "bitlinear_fwd", "hgrn_scan_fwd", "layer_fwd", "layer_decode_step",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
+    "set_decode_kernel", "decode_expired_waits", "DECODE_KERNELS",
 ]
 
 # Every entry point declared in include/mmf.h.
@@ -28,6 +29,7 @@ SYMBOLS = [
     "mmf_bitlinear_workspace_size", "mmf_bitlinear_fwd",
     "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd",
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
+    "mmf_set_decode_kernel", "mmf_decode_expired_waits",
     "mmf_timing_enable", "mmf_timing_collect",
 ]
 
@@ -92,6 +94,8 @@ def load():
                                   ctypes.c_int, P, SZ, ctypes.POINTER(CLayerProbe), P]
     lib.mmf_layer_decode_step.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, P, P, SZ,
                                           ctypes.POINTER(CLayerProbe), P]
+    lib.mmf_set_decode_kernel.argtypes = [ctypes.c_int]
+    lib.mmf_decode_expired_waits.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     lib.mmf_timing_enable.argtypes = [ctypes.c_int]
     lib.mmf_timing_collect.argtypes = [ctypes.POINTER(CKernelTiming), I32, ctypes.POINTER(I32)]
     for name in SYMBOLS[2:]:
@@ -106,6 +110,21 @@ def last_error() -> str:
 
 def last_path() -> str:
     return load().mmf_last_path().decode()
+
+
+DECODE_KERNELS = {"auto": 0, "separate": 1, "xcd": 2}
+
+
+def set_decode_kernel(mode: str = "auto"):
+    """Implementation of layer_decode_step, process-wide (mmf_set_decode_kernel)."""
+    _check(load().mmf_set_decode_kernel(DECODE_KERNELS[mode]))
+
+
+def decode_expired_waits() -> int:
+    """Barrier waits of the one-XCD decode kernel that gave up (synchronous diagnostic)."""
+    c = ctypes.c_uint32(0)
+    _check(load().mmf_decode_expired_waits(ctypes.byref(c)))
+    return c.value
 
 
 def timing_enable(on: bool = True):

@@ -12,6 +12,7 @@
 // shuffles, and the int8 codes leave as one 32-bit store per 4 elements.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "row_quant.hpp"
 
 namespace mmf {
 
@@ -153,31 +154,7 @@ __global__ __launch_bounds__(256) void norm_quant_long_kernel(const T *__restric
     }
 }
 
-// Few rows (decode): one 256-thread workgroup per row; the four waves'
-// partial reductions meet in LDS. Each reduction has its own LDS slots, used
-// once, so one barrier per reduction suffices. Every global load (the row and
-// the gains) is issued at the start, unconditionally from a clamped index
-// (lanes past the row end contribute nothing), so the kernel pays one memory
-// round trip before its reductions.
-__device__ __forceinline__ double block_sum(double v, double *sh) {
-    v = wave_sum(v);
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return (sh[0] + sh[1]) + (sh[2] + sh[3]);
-}
-__device__ __forceinline__ float block_max(float v, float *sh) {
-    v = wave_max(v);
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-}
-__device__ __forceinline__ int block_sum_int(int v, int *sh) {
-    v = wave_sum_int(v);
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return (sh[0] + sh[1]) + (sh[2] + sh[3]);
-}
-
+// Few rows (decode): one 256-thread workgroup per row (row_quant.hpp).
 __device__ __forceinline__ float4 load_f4(const float *p, int c) { return *reinterpret_cast<const float4 *>(p + 4 * c); }
 __device__ __forceinline__ void set4(float (&d)[4], float4 v) { d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w; }
 
@@ -186,58 +163,9 @@ __global__ __launch_bounds__(256) void norm_quant_row_kernel(const T *__restrict
                                                              const float *__restrict__ gain, float eps,
                                                              int8_t *__restrict__ q, float *__restrict__ s,
                                                              int32_t *__restrict__ sumq) {
-    __shared__ double shd[4];
-    __shared__ float shf[4];
-    __shared__ int shi[4];
+    __shared__ RowQuantLds sh;
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nch = k >> 2;
-    const T *xr = x + row * (int64_t)k;
-    float v[NV][4], gv[NV][4];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int c = min(tid + 256 * j, nch - 1);
-        set4(v[j], load_act4(xr, 4 * (int64_t)c));
-        set4(gv[j], gain ? load_f4(gain, c) : make_float4(1.f, 1.f, 1.f, 1.f));
-    }
-    double ss = 0.0;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-        if (tid + 256 * j < nch)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ss += (double)v[j][e] * (double)v[j][e];
-    const float r = rms_factor(block_sum(ss, shd), k, eps);
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float y = __fmul_rn(v[j][e], r);
-            if (gain) y = __fmul_rn(y, gv[j][e]);
-            v[j][e] = y;
-        }
-        if (tid + 256 * j < nch)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
-    }
-    const float sc = quant_scale(block_max(amax, shf));
-    int tot = 0;
-    uint32_t *qr = reinterpret_cast<uint32_t *>(q + row * (int64_t)k);
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int c = tid + 256 * j;
-        if (c < nch) {
-            const int a0 = quant_code(v[j][0], sc), a1 = quant_code(v[j][1], sc);
-            const int a2 = quant_code(v[j][2], sc), a3 = quant_code(v[j][3], sc);
-            tot += a0 + a1 + a2 + a3;
-            qr[c] = pack_codes4(a0, a1, a2, a3);
-        }
-    }
-    tot = block_sum_int(tot, shi);
-    if (tid == 0) {
-        s[row] = sc;
-        sumq[row] = tot;
-    }
+    row_quant<T, NV, false>(x + row * (int64_t)k, k, gain, eps, q + row * (int64_t)k, s + row, sumq + row, sh);
 }
 
 constexpr int kFewRows = 2048;  // below this many rows a row gets a whole workgroup
@@ -387,92 +315,18 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restric
     }
 }
 
-// Few rows (decode): one 256-thread workgroup per row, loads issued up front
-// as in norm_quant_row_kernel.
+// Few rows (decode): one 256-thread workgroup per row (row_quant.hpp).
 template <typename TG, int NV>
 __global__ __launch_bounds__(256) void gnorm_quant_row_kernel(const float *__restrict__ h, const TG *__restrict__ g,
                                                               int64_t m, int d, const float *__restrict__ gnw,
                                                               const float *__restrict__ ogain, float eps,
                                                               int8_t *__restrict__ q, float *__restrict__ s,
                                                               int32_t *__restrict__ sumq, float *__restrict__ u_out) {
-    __shared__ double shd[2][4];
-    __shared__ float shf[4];
-    __shared__ int shi[4];
+    __shared__ RowQuantLds sh;
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int nch = d >> 2;
-    const float *hr = h + row * (int64_t)d;
-    const TG *gr = g + row * (int64_t)d;
-    float u[NV][4], gs[NV][4], wn[NV][4], og[NV][4];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int c = min(tid + 256 * j, nch - 1);
-        set4(u[j], load_f4(hr, c));
-        set4(gs[j], load_act4(gr, 4 * (int64_t)c));
-        set4(wn[j], gnw ? load_f4(gnw, c) : make_float4(1.f, 1.f, 1.f, 1.f));
-        set4(og[j], ogain ? load_f4(ogain, c) : make_float4(1.f, 1.f, 1.f, 1.f));
-    }
-    double ss = 0.0;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) gs[j][e] = silu_fast(gs[j][e]);
-        if (tid + 256 * j < nch)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ss += (double)u[j][e] * (double)u[j][e];
-    }
-    const float rh = rms_factor(block_sum(ss, shd[0]), d, eps);
-    double su = 0.0;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int c = tid + 256 * j;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float y = u[j][e] * rh;
-            if (gnw) y = y * wn[j][e];
-            y = y * gs[j][e];
-            u[j][e] = y;
-        }
-        if (c < nch) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) su += (double)u[j][e] * (double)u[j][e];
-            if (u_out)
-                *reinterpret_cast<float4 *>(u_out + row * (int64_t)d + 4 * c) =
-                    make_float4(u[j][0], u[j][1], u[j][2], u[j][3]);
-        }
-    }
-    const float r = rms_factor(block_sum(su, shd[1]), d, eps);
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float y = __fmul_rn(u[j][e], r);
-            if (ogain) y = __fmul_rn(y, og[j][e]);
-            u[j][e] = y;
-        }
-        if (tid + 256 * j < nch)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(u[j][e]));
-    }
-    const float sc = quant_scale(block_max(amax, shf));
-    int tot = 0;
-    uint32_t *qr = reinterpret_cast<uint32_t *>(q + row * (int64_t)d);
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int c = tid + 256 * j;
-        if (c < nch) {
-            const int a0 = quant_code(u[j][0], sc), a1 = quant_code(u[j][1], sc);
-            const int a2 = quant_code(u[j][2], sc), a3 = quant_code(u[j][3], sc);
-            tot += a0 + a1 + a2 + a3;
-            qr[c] = pack_codes4(a0, a1, a2, a3);
-        }
-    }
-    tot = block_sum_int(tot, shi);
-    if (tid == 0) {
-        s[row] = sc;
-        sumq[row] = tot;
-    }
+    row_gnorm_quant<TG, NV, false>(h + row * (int64_t)d, g + row * (int64_t)d, d, gnw, ogain, eps,
+                                   q + row * (int64_t)d, s + row, sumq + row, u_out ? u_out + row * (int64_t)d : nullptr,
+                                   sh);
 }
 
 template <typename TG>

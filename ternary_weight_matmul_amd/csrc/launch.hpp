@@ -51,6 +51,33 @@ struct ContractArgs {
     float *aux_probe;        // optional fp32 copy of g / z as stored (after rounding to aux_type)
 };
 
+// One decode step of a block as a single kernel on one XCD (k_decode.hip).
+struct DecodeStepArgs {
+    const void *x;           // [b][d] activation dtype
+    void *out;               // [b][d] activation dtype
+    float *h;                // [b][d] recurrent state, updated in place
+    const uint32_t *w_ifg[3];
+    const float *mu_ifg[3];
+    const uint32_t *w_o, *w_gate, *w_down;
+    const float *mu_o, *mu_gate, *mu_down;
+    const float *gain_x, *gain_o, *gain_gate, *gain_down, *g_norm_w;
+    int b, d, inner;
+    float eps;
+    ActType act;
+    int8_t *codes;           // [b][max(d, inner)]
+    float *s;                // [b]
+    int32_t *sumq;           // [b]
+    void *g;                 // [b][d] activation dtype
+    float *x1;               // [b][d]
+    void *z;                 // [b][inner] activation dtype
+};
+bool decode_step_supported(int64_t b, int d, int inner);
+// Enqueues the one-XCD decode step when the shape and the device allow it;
+// *launched reports whether it did (otherwise nothing was enqueued).
+hipError_t launch_decode_step(const DecodeStepArgs &a, hipStream_t stream, std::string *path, bool *launched);
+// Barrier waits of the one-XCD decode step that ran out of patience (synchronous).
+hipError_t decode_step_expired_spins(unsigned *count);
+
 // Prefill-shaped contraction (int8 MFMA tiles) and decode-shaped one (m <= 64).
 hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a,
                            hipStream_t stream, std::string *path);

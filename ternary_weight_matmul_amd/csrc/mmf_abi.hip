@@ -13,6 +13,7 @@
 #include <string>
 #include <vector>
 #include <cstring>
+#include <atomic>
 
 #include "mmf.h"
 #include "launch.hpp"
@@ -50,6 +51,7 @@ struct TimingRec {
     hipEvent_t start, stop;
 };
 thread_local bool g_timing = false;
+std::atomic<int> g_decode_mode{0};  // mmf_set_decode_kernel
 thread_local std::vector<TimingRec> g_recs;
 thread_local std::vector<hipEvent_t> g_events;
 thread_local size_t g_events_used = 0;
@@ -456,6 +458,21 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
     return r;
 }
 
+mmf_status mmf_set_decode_kernel(int mode) {
+    if (mode < 0 || mode > 2) return fail(MMF_ERR_INVALID_ARG, "decode kernel mode %d (0 auto, 1 separate, 2 one-XCD)", mode);
+    g_decode_mode.store(mode);
+    g_err.clear();
+    return MMF_OK;
+}
+
+mmf_status mmf_decode_expired_waits(uint32_t *count) {
+    if (!count) return fail(MMF_ERR_INVALID_ARG, "count is NULL");
+    unsigned c = 0;
+    mmf_status st = hip_status(decode_step_expired_spins(&c), "mmf_decode_expired_waits");
+    *count = c;
+    return st;
+}
+
 mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b,
                                  float *h, void *ws, size_t ws_bytes, const mmf_layer_probe *probe,
                                  hipStream_t stream) {
@@ -468,8 +485,40 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
         return fail(MMF_ERR_INVALID_ARG, "x, out and h must be 16-byte aligned");
     if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
         return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    const int mode = g_decode_mode.load();
+    const bool xcd_ok = !probe && shared_ifg(w) && decode_step_supported(b, w->d, w->inner);
+    if (mode == 2 && b > 0 && !xcd_ok)
+        return fail(MMF_ERR_UNSUPPORTED, "one-XCD decode step: needs b <= 16, no probe, equal i/f/g gains, "
+                    "d and inner multiples of 256 within the kernel's limits (b=%lld d=%d inner=%d)",
+                    (long long)b, w->d, w->inner);
     std::string path;
     hipError_t e = hipSuccess;
+    if (b > 0 && mode == 2 && xcd_ok) {
+        Carver c(ws);
+        LayerWs L;
+        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
+        DecodeStepArgs da{};
+        da.x = x; da.out = out; da.h = h;
+        const mmf_ternary_weight *ifg[3] = {&w->i, &w->f, &w->g};
+        for (int q = 0; q < 3; ++q) { da.w_ifg[q] = ifg[q]->packed; da.mu_ifg[q] = ifg[q]->mu; }
+        da.w_o = w->o.packed; da.mu_o = w->o.mu;
+        da.w_gate = w->gate.packed; da.mu_gate = w->gate.mu;
+        da.w_down = w->down.packed; da.mu_down = w->down.mu;
+        da.gain_x = w->i.norm_w; da.gain_o = w->o.norm_w; da.gain_gate = w->gate.norm_w; da.gain_down = w->down.norm_w;
+        da.g_norm_w = w->g_norm_w;
+        da.b = (int)b; da.d = w->d; da.inner = w->inner; da.eps = w->eps; da.act = act(actt);
+        da.codes = L.codes_b; da.s = L.s_b; da.sumq = L.sq_b; da.g = L.g; da.x1 = L.x1; da.z = L.z;
+        bool launched = false;
+        e = timed("decode_step_xcd", b, w->d, w->inner, stream,
+                  [&] { return launch_decode_step(da, stream, &path, &launched); });
+        if (e == hipSuccess && !launched && mode == 2)
+            return fail(MMF_ERR_UNSUPPORTED, "one-XCD decode step: this device cannot run it");
+        if (e != hipSuccess || launched) {
+            mmf_status r = hip_status(e, "mmf_layer_decode_step");
+            if (r == MMF_OK) g_path = path;
+            return r;
+        }
+    }
     if (b > 0) {
         Carver c(ws);
         LayerWs L;

@@ -435,3 +435,111 @@ def test_layer_empty_sequence(gpu):
     out, h_last = mmf.layer_fwd(P, torch.empty((2, 0, 64), device=gpu), h0)
     torch.cuda.synchronize()
     assert out.shape == (2, 0, 64) and torch.equal(h_last, h0)
+
+
+XCD_CASES = [
+    # b, act, gains, d, inner
+    (1, "bf16", None, 256, 512),
+    (5, "f32", "shared", 256, 512),
+    (16, "bf16", "shared", 1024, 2816),
+    (16, "bf16", None, 2048, 5632),
+    (7, "f32", None, 2048, 5632),
+    (16, "bf16", None, 2560, 6912),
+]
+
+
+def _decode_both(P, x, h_init, steps, gpu):
+    """The same decode steps with the separate kernels and with the one-XCD kernel."""
+    import torch
+    mmf = _mmf()
+    res = {}
+    try:
+        for mode in ("separate", "xcd"):
+            mmf.set_decode_kernel(mode)
+            h = h_init.clone()
+            outs = []
+            for s_ in range(steps):
+                outs.append(mmf.layer_decode_step(P, x[s_], h))
+                path = mmf.last_path()
+                assert ("decode_step_xcd" in path) == (mode == "xcd"), (mode, path)
+            torch.cuda.synchronize()
+            res[mode] = (torch.stack(outs), h)
+    finally:
+        mmf.set_decode_kernel("auto")
+    return res
+
+
+@pytest.mark.parametrize("b,act,gains,d,inner", XCD_CASES)
+def test_decode_xcd_kernel_matches_separate(gpu, b, act, gains, d, inner):
+    """One-XCD decode step against the separate kernels (which the stage checks cover): same bits."""
+    import torch
+    mmf = _mmf()
+    _, P = make_pair(d, inner, 900 + b, gpu, gains)
+    steps = 3
+    xs = synth.activations((steps, b, d), 901, act)
+    x = bf16_tensor(xs, gpu) if act == "bf16" else dev(xs, gpu)
+    h = dev(synth.activations((b, d), 902), gpu)
+    r = _decode_both(P, x, h, steps, gpu)
+    assert torch.equal(r["separate"][0], r["xcd"][0])
+    assert torch.equal(r["separate"][1], r["xcd"][1])
+    assert mmf.decode_expired_waits() == 0
+
+
+def test_decode_xcd_kernel_long_chain(gpu):
+    """64 chained steps at the 1.3B shape, batch 16: the state never leaves the bits of the separate path."""
+    import torch
+    mmf = _mmf()
+    d, inner, b, steps = 2048, 5632, 16, 64
+    _, P = make_pair(d, inner, 910, gpu)
+    x = bf16_tensor(synth.activations((steps, b, d), 911, "bf16"), gpu)
+    h = dev(synth.activations((b, d), 912), gpu)
+    r = _decode_both(P, x, h, steps, gpu)
+    assert torch.equal(r["separate"][0], r["xcd"][0])
+    assert torch.equal(r["separate"][1], r["xcd"][1])
+    assert mmf.decode_expired_waits() == 0
+
+
+def test_decode_xcd_kernel_graph_replays(gpu):
+    """A captured one-XCD decode step replayed several times, with eager work between the
+    replays, gives the eager result every time."""
+    import torch
+    mmf = _mmf()
+    d, inner, b = 1024, 2816, 16
+    _, P = make_pair(d, inner, 920, gpu)
+    x = bf16_tensor(synth.activations((b, d), 921, "bf16"), gpu)
+    h0 = dev(synth.activations((b, d), 922), gpu)
+    ws = torch.empty(mmf.layer_workspace_size(P, b, 1), dtype=torch.uint8, device=gpu)
+    out = torch.empty((b, d), dtype=torch.bfloat16, device=gpu)
+    h = h0.clone()
+    mmf.layer_decode_step(P, x, h, out=out, ws=ws)  # eager: also runs the one-time placement check
+    assert "decode_step_xcd" in mmf.last_path()
+    ref_out, ref_h = out.clone(), h.clone()
+    g = torch.cuda.CUDAGraph()
+    h.copy_(h0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        mmf.layer_decode_step(P, x, h, out=out, ws=ws)
+    for _ in range(4):
+        h.copy_(h0)
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(h, ref_h)
+        mmf.layer_fwd(P, x[:, None, :].contiguous(), None)  # unrelated eager work between replays
+    assert mmf.decode_expired_waits() == 0
+
+
+def test_decode_xcd_kernel_unsupported_shapes(gpu):
+    """Forcing the one-XCD kernel where it does not apply is an error, never a silent fallback."""
+    mmf = _mmf()
+    _, P = make_pair(272, 1040, 930, gpu)
+    x = bf16_tensor(synth.activations((4, 272), 931, "bf16"), gpu)
+    h = dev(synth.activations((4, 272), 932), gpu)
+    try:
+        mmf.set_decode_kernel("xcd")
+        with pytest.raises(mmf.MMFError):
+            mmf.layer_decode_step(P, x, h)
+    finally:
+        mmf.set_decode_kernel("auto")
+    mmf.layer_decode_step(P, x, h)
+    assert "decode_step_xcd" not in mmf.last_path()
