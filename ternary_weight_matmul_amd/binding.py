@@ -112,7 +112,7 @@ def last_path() -> str:
     return load().mmf_last_path().decode()
 
 
-DECODE_KERNELS = {"auto": 0, "separate": 1, "xcd": 2}
+DECODE_KERNELS = {"auto": 0, "separate": 1, "xcd": 2, "fused": 3}
 
 
 def set_decode_kernel(mode: str = "auto"):

@@ -273,6 +273,63 @@ hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_
     return t_contract(cd, EPI_RESID, 1, true, st, path);
 }
 
+// Whether the four-kernel decode step applies: every contraction quantises its
+// own input rows (b <= 16, shapes within the fused kernels' limits).
+bool fused_decode_ok(const mmf_layer_weights *w, mmf_dtype actt, int64_t b) {
+    const ActType at = act(actt);
+    return shared_ifg(w) && quant_contract_supported(b, w->d, w->d, EPI_GATES_STEP, QK_ROW, at, at) &&
+           quant_contract_supported(b, w->d, w->d, EPI_RESID, QK_GNORM, ACT_F32, at) &&
+           quant_contract_supported(b, w->inner, w->d, EPI_GLU, QK_ROW, ACT_F32, ACT_F32) &&
+           quant_contract_supported(b, w->d, w->inner, EPI_RESID, QK_ROW, at, at);
+}
+
+// The four-kernel decode step: x -> i/f/g + state update -> g_norm gate + o_proj
+// + residual -> gate_proj + SiLU product -> down_proj + residual, each kernel
+// quantising its own input rows.
+hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b, float *h,
+                        const LayerWs &L, hipStream_t st, std::string *path) {
+    const ActType at = act(actt);
+    const int d = w->d, inner = w->inner;
+    const float eps = w->eps;
+    ContractArgs ci{};
+    const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
+    for (int q = 0; q < 3; ++q) { ci.B[q] = tw[q]->packed; ci.mu[q] = tw[q]->mu; }
+    ci.m = b; ci.nc = d; ci.k = d;
+    ci.out0 = h; ci.out1 = L.g; ci.out_type = ACT_F32; ci.aux_type = at;
+    hipError_t e = timed("tgemv_q<gates_step>", b, 3 * d, d, st, [&] {
+        return launch_quant_contract(ci, EPI_GATES_STEP, QK_ROW, x, at, nullptr, at, w->i.norm_w, nullptr, eps, st, path);
+    });
+    if (e != hipSuccess) return e;
+    ContractArgs co{};
+    for (int q = 0; q < 3; ++q) { co.B[q] = w->o.packed; co.mu[q] = w->o.mu; }
+    co.m = b; co.nc = d; co.k = d;
+    co.out0 = L.x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
+    e = timed("tgemv_q<gnorm_resid>", b, d, d, st, [&] {
+        return launch_quant_contract(co, EPI_RESID, QK_GNORM, h, ACT_F32, L.g, at, w->o.norm_w, w->g_norm_w, eps, st,
+                                     path);
+    });
+    if (e != hipSuccess) return e;
+    ContractArgs cg{};
+    for (int q = 0; q < 3; ++q) cg.mu[q] = w->gate.mu;
+    cg.B[0] = w->gate.packed;
+    cg.B[1] = w->gate.packed + (size_t)inner * (d / 16);
+    cg.B[2] = cg.B[1];
+    cg.m = b; cg.nc = inner; cg.k = d;
+    cg.out0 = L.z; cg.aux_type = at;
+    e = timed("tgemv_q<glu>", b, 2 * inner, d, st, [&] {
+        return launch_quant_contract(cg, EPI_GLU, QK_ROW, L.x1, ACT_F32, nullptr, ACT_F32, w->gate.norm_w, nullptr, eps,
+                                     st, path);
+    });
+    if (e != hipSuccess) return e;
+    ContractArgs cd{};
+    for (int q = 0; q < 3; ++q) { cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
+    cd.m = b; cd.nc = d; cd.k = inner;
+    cd.out0 = out; cd.out_type = at; cd.res = L.x1; cd.res_type = ACT_F32;
+    return timed("tgemv_q<resid>", b, d, inner, st, [&] {
+        return launch_quant_contract(cd, EPI_RESID, QK_ROW, L.z, at, nullptr, at, w->down.norm_w, nullptr, eps, st, path);
+    });
+}
+
 // Quantise x for i/f/g (once when their gains coincide) and fill the contraction's A side.
 hipError_t quant_ifg(const mmf_layer_weights *w, const void *x, mmf_dtype actt, int64_t m, LayerWs &L,
                      const mmf_layer_probe *pr, ContractArgs &ca, bool *shared, hipStream_t st, std::string *path) {
@@ -459,7 +516,8 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
 }
 
 mmf_status mmf_set_decode_kernel(int mode) {
-    if (mode < 0 || mode > 2) return fail(MMF_ERR_INVALID_ARG, "decode kernel mode %d (0 auto, 1 separate, 2 one-XCD)", mode);
+    if (mode < 0 || mode > 3)
+        return fail(MMF_ERR_INVALID_ARG, "decode kernel mode %d (0 auto, 1 separate, 2 one-XCD, 3 fused)", mode);
     g_decode_mode.store(mode);
     g_err.clear();
     return MMF_OK;
@@ -518,6 +576,20 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
             if (r == MMF_OK) g_path = path;
             return r;
         }
+    }
+    const bool fused_ok = b > 0 && !probe && fused_decode_ok(w, actt, b);
+    if (mode == 3 && b > 0 && !fused_ok)
+        return fail(MMF_ERR_UNSUPPORTED, "fused decode step: needs b <= 16, no probe, equal i/f/g gains, d and inner "
+                    "multiples of 256 within the fused kernels' limits (b=%lld d=%d inner=%d)",
+                    (long long)b, w->d, w->inner);
+    if (fused_ok && mode == 3) {
+        Carver c(ws);
+        LayerWs L;
+        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
+        e = fused_decode(w, x, out, actt, b, h, L, stream, &path);
+        mmf_status r = hip_status(e, "mmf_layer_decode_step");
+        if (r == MMF_OK) g_path = path;
+        return r;
     }
     if (b > 0) {
         Carver c(ws);

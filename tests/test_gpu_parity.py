@@ -448,20 +448,24 @@ XCD_CASES = [
 ]
 
 
-def _decode_both(P, x, h_init, steps, gpu):
-    """The same decode steps with the separate kernels and with the one-XCD kernel."""
+DECODE_PATH_MARK = {"separate": "norm_quant_row", "xcd": "decode_step_xcd", "fused": "tgemv_q<"}
+
+
+def _decode_both(P, x, h_init, steps, gpu, modes=("separate", "xcd")):
+    """The same decode steps with each of the given decode implementations."""
     import torch
     mmf = _mmf()
     res = {}
     try:
-        for mode in ("separate", "xcd"):
+        for mode in modes:
             mmf.set_decode_kernel(mode)
             h = h_init.clone()
             outs = []
             for s_ in range(steps):
                 outs.append(mmf.layer_decode_step(P, x[s_], h))
                 path = mmf.last_path()
-                assert ("decode_step_xcd" in path) == (mode == "xcd"), (mode, path)
+                for other, mark in DECODE_PATH_MARK.items():
+                    assert (mark in path) == (other == mode), (mode, path)
             torch.cuda.synchronize()
             res[mode] = (torch.stack(outs), h)
     finally:
@@ -508,11 +512,25 @@ def test_decode_xcd_kernel_graph_replays(gpu):
     _, P = make_pair(d, inner, 920, gpu)
     x = bf16_tensor(synth.activations((b, d), 921, "bf16"), gpu)
     h0 = dev(synth.activations((b, d), 922), gpu)
+    try:
+        mmf.set_decode_kernel("xcd")
+        _graph_replays(P, x, h0, "decode_step_xcd", gpu)
+    finally:
+        mmf.set_decode_kernel("auto")
+    assert mmf.decode_expired_waits() == 0
+
+
+def _graph_replays(P, x, h0, mark, gpu):
+    """Captures one decode step and replays it with eager work between replays; every replay
+    must give the eager result."""
+    import torch
+    mmf = _mmf()
+    b, d = x.shape
     ws = torch.empty(mmf.layer_workspace_size(P, b, 1), dtype=torch.uint8, device=gpu)
-    out = torch.empty((b, d), dtype=torch.bfloat16, device=gpu)
+    out = torch.empty((b, d), dtype=x.dtype, device=gpu)
     h = h0.clone()
-    mmf.layer_decode_step(P, x, h, out=out, ws=ws)  # eager: also runs the one-time placement check
-    assert "decode_step_xcd" in mmf.last_path()
+    mmf.layer_decode_step(P, x, h, out=out, ws=ws)  # eager (the one-XCD kernel's placement check runs here)
+    assert mark in mmf.last_path()
     ref_out, ref_h = out.clone(), h.clone()
     g = torch.cuda.CUDAGraph()
     h.copy_(h0)
@@ -526,7 +544,6 @@ def test_decode_xcd_kernel_graph_replays(gpu):
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out) and torch.equal(h, ref_h)
         mmf.layer_fwd(P, x[:, None, :].contiguous(), None)  # unrelated eager work between replays
-    assert mmf.decode_expired_waits() == 0
 
 
 def test_decode_xcd_kernel_unsupported_shapes(gpu):
@@ -543,3 +560,89 @@ def test_decode_xcd_kernel_unsupported_shapes(gpu):
         mmf.set_decode_kernel("auto")
     mmf.layer_decode_step(P, x, h)
     assert "decode_step_xcd" not in mmf.last_path()
+
+
+FUSED_CASES = [
+    # b, act, gains, d, inner
+    (1, "bf16", None, 256, 512),
+    (5, "f32", "shared", 256, 512),
+    (16, "bf16", "shared", 1024, 2816),
+    (16, "bf16", None, 2048, 5632),
+    (1, "bf16", None, 2048, 5632),
+    (3, "f32", None, 2048, 2816),
+    (9, "bf16", None, 768, 1280),
+    (16, "bf16", None, 2560, 6912),
+    (12, "f32", "shared", 2048, 3072),
+]
+
+
+@pytest.mark.parametrize("b,act,gains,d,inner", FUSED_CASES)
+def test_decode_fused_matches_separate(gpu, b, act, gains, d, inner):
+    """The four-kernel decode step (each contraction quantises its own rows) against the eight
+    separate kernels (which the stage checks cover): same bits, over three chained steps."""
+    import torch
+    _, P = make_pair(d, inner, 940 + b, gpu, gains)
+    steps = 3
+    xs = synth.activations((steps, b, d), 941, act)
+    x = bf16_tensor(xs, gpu) if act == "bf16" else dev(xs, gpu)
+    h = dev(synth.activations((b, d), 942), gpu)
+    r = _decode_both(P, x, h, steps, gpu, modes=("separate", "fused"))
+    assert torch.equal(r["separate"][0], r["fused"][0])
+    assert torch.equal(r["separate"][1], r["fused"][1])
+
+
+def test_decode_fused_long_chain(gpu):
+    """64 chained steps at the 1.3B shape, batch 16: the fused path never leaves the bits of the
+    separate path."""
+    import torch
+    d, inner, b, steps = 2048, 5632, 16, 64
+    _, P = make_pair(d, inner, 950, gpu)
+    x = bf16_tensor(synth.activations((steps, b, d), 951, "bf16"), gpu)
+    h = dev(synth.activations((b, d), 952), gpu)
+    r = _decode_both(P, x, h, steps, gpu, modes=("separate", "fused"))
+    assert torch.equal(r["separate"][0], r["fused"][0])
+    assert torch.equal(r["separate"][1], r["fused"][1])
+
+
+def test_decode_fused_graph_replays(gpu):
+    """A captured fused decode step replayed several times gives the eager result every time."""
+    mmf = _mmf()
+    _, P = make_pair(2048, 5632, 960, gpu)
+    x = bf16_tensor(synth.activations((16, 2048), 961, "bf16"), gpu)
+    h0 = dev(synth.activations((16, 2048), 962), gpu)
+    try:
+        mmf.set_decode_kernel("fused")
+        _graph_replays(P, x, h0, "tgemv_q<", gpu)
+    finally:
+        mmf.set_decode_kernel("auto")
+
+
+def test_decode_fused_unsupported_shapes(gpu):
+    """Forcing the fused kernels where they do not apply (b > 16, fp32 activations with inner >
+    3072, shapes off the 256 grid, distinct i/f/g gains) is an error, never a silent fallback;
+    auto takes the separate kernels there."""
+    mmf = _mmf()
+    cases = [(16, "bf16", 1024, 2816, None, True), (17, "bf16", 1024, 2816, None, False),
+             (4, "f32", 2048, 5632, None, False), (4, "bf16", 272, 1040, None, False),
+             (4, "bf16", 1024, 2816, "distinct", False)]
+    for b, act, d, inner, gains, fused in cases:
+        _, P = make_pair(d, inner, 970 + b, gpu, gains)
+        xs = synth.activations((b, d), 971, act)
+        x = bf16_tensor(xs, gpu) if act == "bf16" else dev(xs, gpu)
+        h = dev(synth.activations((b, d), 972), gpu)
+        mmf.layer_decode_step(P, x, h)
+        assert "tgemv_q<" not in mmf.last_path(), mmf.last_path()
+        if fused:
+            try:
+                mmf.set_decode_kernel("fused")
+                mmf.layer_decode_step(P, x, h)
+                assert "tgemv_q<" in mmf.last_path()
+            finally:
+                mmf.set_decode_kernel("auto")
+        else:
+            try:
+                mmf.set_decode_kernel("fused")
+                with pytest.raises(mmf.MMFError):
+                    mmf.layer_decode_step(P, x, h)
+            finally:
+                mmf.set_decode_kernel("auto")
