@@ -205,9 +205,11 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
  *  Errors as mmf_layer_fwd (workspace from mmf_layer_workspace_size(w, b, 1)).
  *  Three implementations give the same bits: separate kernels per stage
  *  (quantisers and contractions: eight launches); four contraction kernels
- *  that each quantise their own input rows (b <= 16, no probe, equal i/f/g
- *  gains, d and inner multiples of 256; d <= 3072 and inner <= 7168 with bf16
- *  activations, d <= 2048 and inner <= 3072 with fp32 ones); and (b <= 16, no
+ *  whose first b workgroups quantise the input rows and hand them to the
+ *  others within the launch through device-scope stores and a counter (b <=
+ *  16, no probe, equal i/f/g gains, d and inner multiples of 256, d <= 3072,
+ *  inner <= 8192; launches of this kind on one stream are ordered, and each
+ *  stream uses its own counters, 64 streams per process at most); and (b <= 16, no
  *  probe, equal i/f/g gains, d and inner multiples of 256, d <= 3072, inner
  *  <= 7136) one kernel run by the 32 workgroups of one XCD with barriers
  *  between the stages (see mmf_set_decode_kernel). Calls of the
@@ -225,9 +227,10 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
  * mmf_set_decode_kernel -- which implementation mmf_layer_decode_step uses,
  * process-wide: 0 = the fastest implementation measured on MI355X (default;
  * at present the separate kernels for every shape: at the 1.3B shape they
- * take 31 / 37 us per layer at batch 1 / 16, the four fused kernels 35 / 55,
- * whose per-workgroup row quantisers cost more than the launches they save,
- * and the one-XCD kernel 44 / 46, held to one XCD's share of HBM bandwidth);
+ * take 31 / 37 us per layer at batch 1 / 16 in a HIP graph, the four fused
+ * kernels 36 / 47 (a hand-off across XCDs within a launch costs about what a
+ * kernel boundary does), and the one-XCD kernel 45 / 48, held to one XCD's
+ * share of HBM bandwidth);
  * 1 = always the separate kernels; 2 = only the one-XCD kernel; 3 = only the
  * four fused kernels (2 and 3: UNSUPPORTED where they do not apply).
  * INVALID_ARG for other values.

@@ -1,24 +1,29 @@
-// Decode contraction with its input quantiser fused in (gfx950).
+// Decode contraction with its input quantiser in the same launch (gfx950).
 //
 // A decode step of the HGRNBit block ("MatMul-Free LM：把矩陣乘法從語言模型裡拿掉之後，
 // 剩下什麼", section "HGRNBitBlock 的結構") quantises a few rows (one per sequence)
 // before each of its four ternary contractions: x before i/f/g, the g_norm
 // gate output before o_proj, x1 before gate_proj and z before down_proj
 // ("MatMul-Free LLM 深度分析报告", list "可复用的模式与技巧": the RMSNorm and the
-// activation quantiser belong to the same fused step). With b <= 16 rows the
-// quantiser is tiny next to a kernel boundary (about 2 us in a HIP graph on
-// MI355X), so each contraction kernel here quantises its b input rows itself:
-// every workgroup redundantly, one wave per row, into LDS. A decode step is
-// then four kernels instead of eight, and the codes never go through memory.
+// activation quantiser belong to the same fused step). As separate kernels a
+// quantiser and its contraction pay a kernel boundary (about 2 us in a HIP
+// graph on MI355X) and the contraction's weight loads start only after it.
 //
-// Workgroup: 16 waves, CB blocks of 16 output channels. A unit of work is one
-// (block, 256-k slice) pair; wave w takes units w and w + 16 and issues all
-// its weight loads (16 bytes per lane per group and unit) first, then the
-// epilogue operand, the gains and its input row, so that one memory round
-// trip covers them all. The row quantisers (row_quant.hpp) reproduce the
-// reduction order of the separate quantiser kernels, so both decode paths give
-// the same bits. Partial sums of a block meet in LDS by integer atomic adds
-// (exact, order-free).
+// Here one launch does both. Workgroups 0..b-1 each quantise one row (the
+// 256-thread quantisers of row_quant.hpp, so the bits equal those of the
+// separate quantiser kernels) and publish it: codes, scale and code sum go out
+// with device-scope stores, which write through to memory, and a device-scope
+// counter counts the rows. The other workgroups, one per 16 output channels,
+// issue their weight and epilogue-operand loads at once, wait (bounded) until
+// the counter reaches b, then read the codes with device-scope loads (which do
+// not return an older cached copy; the XCDs' L2 caches are not coherent with
+// each other) and finish as the decode GEMV does. Workgroups are dispatched in
+// index order, so the quantising ones run before anyone waits for them.
+//
+// The counter pair (rows published, workgroups finished) is library state on
+// the device: the last workgroup to finish returns both to zero, so the next
+// launch starts from zero. Calls on one stream therefore never interfere;
+// each stream gets its own pair (kHSlots streams per device at most).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "epilogue.hpp"
@@ -26,12 +31,18 @@
 
 #include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 namespace mmf {
 
-constexpr int kQWaves = 16;
-constexpr int kQThreads = kQWaves * 64;
-constexpr int kQUnits = 2;  // units per wave at most
+constexpr int kHSlots = 64;               // counter pairs: one per stream
+constexpr long kHSpinLimit = 1L << 20;    // about a second of polling
+constexpr unsigned kBufferRsrcWord3 = 0x00020000u;  // raw buffer descriptor, gfx9 data format
+constexpr int kSc1 = 16;                  // buffer-load cache policy: device scope
+
+// slot s: rows published at [64 s], workgroups finished at [64 s + 32];
+// waits that gave up at [64 kHSlots]
+__device__ unsigned g_handoff[64 * kHSlots + 64];
 
 struct QuantContractArgs {
     ContractArgs c;      // contraction: B, mu, m (= b rows), nc, k, outputs, residual
@@ -40,134 +51,137 @@ struct QuantContractArgs {
     const float *gain;   // quantiser gain (RMSNorm weight) or null
     const float *gnw;    // QK_GNORM: g_norm weight or null
     float eps;
+    int8_t *codes;       // handoff: codes [b][k], scale [b], code sum [b]
+    float *s;
+    int32_t *sumq;
+    int slot;
+    int nslices;         // 256-k slices of a row
 };
 
-static size_t q_lds_bytes(int k, int ng, int cb, int qk) {
-    return (size_t)16 * (k + 16) + (size_t)cb * ng * 1024 + (size_t)(qk == QK_GNORM ? 2 : 1) * k * 4 + 128;
+__device__ __forceinline__ unsigned ld_dev(const unsigned *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NG, int EPI, int QK, typename XT, typename GT, typename RT, int NC, int CB>
-__global__ __launch_bounds__(kQThreads) void tgemv_q_kernel(const QuantContractArgs a) {
+template <int NG, int EPI, int QK, typename XT, typename GT, typename RT, int NVQ, int SPW>
+__global__ __launch_bounds__(1024) void tgemv_q_kernel(const QuantContractArgs a) {
     const ContractArgs &p = a.c;
-    extern __shared__ __attribute__((aligned(16))) char dyn[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lc = lane & 15, lg = lane >> 4;
-    const int K = p.k, KW = K >> 4, nsl = K >> 8;
-    const int b = (int)p.m;
-    const int stride = K + 16;
-    const int nunits = CB * nsl;
-    const int n0 = blockIdx.x * (16 * CB);
-    int8_t *codes = reinterpret_cast<int8_t *>(dyn);
-    int32_t *accl = reinterpret_cast<int32_t *>(dyn + 16 * stride);
-    float *gl = reinterpret_cast<float *>(dyn + 16 * stride + CB * NG * 1024);
-    float *gl2 = gl + K;  // QK_GNORM: o_proj gain after the g_norm weight
-    float *sl = gl + (QK == QK_GNORM ? 2 * K : K);
-    int32_t *sql = reinterpret_cast<int32_t *>(sl + 16);
+    extern __shared__ int32_t part[];  // [waves][NG][256]
+    __shared__ RowQuantLds sh;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int b = (int)p.m, K = p.k, KW = K >> 4;
+    unsigned *done = g_handoff + 64 * a.slot, *fin = done + 32;
 
-    // 1. weights of this wave's units
-    uint4 wv[kQUnits][NG];
-#pragma unroll
-    for (int i = 0; i < kQUnits; ++i) {
-        const int u = wave + kQWaves * i;
-        if (u < nunits) {
-            const int cb = u / nsl, s16 = (u - cb * nsl) * 16;
-            const int ch = min(n0 + cb * 16 + lc, p.nc - 1);  // channels past nc load a valid row, never stored
-#pragma unroll
-            for (int g = 0; g < NG; ++g)
-                wv[i][g] = *reinterpret_cast<const uint4 *>(p.B[g] + (int64_t)ch * KW + s16 + 4 * lg);
-        }
-    }
-    float sw[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) sw[g] = weight_sw(p.mu[g]);
-
-    // 2. the epilogue operand of this thread's output (residual or old state)
-    constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
-    const int ecb = tid >> 8, er = (tid >> 4) & 15, ec = tid & 15;
-    const int ech = n0 + ecb * 16 + ec;
-    float pre = 0.0f;
-    if (PRE && tid < CB * 256) {
-        const RT *src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
-        pre = load_act(src, (int64_t)min(er, b - 1) * p.nc + min(ech, p.nc - 1));
-    }
-
-    // 3. gains into LDS
-    const int nch = K >> 2;
-    if constexpr (QK == QK_GNORM) {
-        for (int c = tid; c < nch; c += kQThreads) {
-            if (a.gnw) reinterpret_cast<float4 *>(gl)[c] = reinterpret_cast<const float4 *>(a.gnw)[c];
-            if (a.gain) reinterpret_cast<float4 *>(gl2)[c] = reinterpret_cast<const float4 *>(a.gain)[c];
-        }
-    } else {
-        if (a.gain)
-            for (int c = tid; c < nch; c += kQThreads)
-                reinterpret_cast<float4 *>(gl)[c] = reinterpret_cast<const float4 *>(a.gain)[c];
-    }
-
-    // 4. this wave's input row (wave r quantises row r)
-    const bool qwave = wave < b;
-    typename RawRow<XT>::type raw[NC];
-    typename RawRow<GT>::type graw[QK == QK_GNORM ? NC : 1];
-    if (qwave) {
-        wave_row_load<XT, NC, false>(static_cast<const XT *>(a.x) + (int64_t)wave * K, K, raw);
-        if constexpr (QK == QK_GNORM)
-            wave_row_load<GT, NC, false>(static_cast<const GT *>(a.g) + (int64_t)wave * K, K, graw);
-    }
-    for (int i = tid; i < CB * NG * 256; i += kQThreads) accl[i] = 0;
-    __syncthreads();
-
-    // 5. quantise into LDS
-    if (qwave) {
+    if ((int)blockIdx.x < b) {
+        // ---- quantiser workgroup: row r, published with device-scope stores
+        const int r = blockIdx.x;
         if constexpr (QK == QK_GNORM) {
             static_assert(std::is_same<XT, float>::value, "g_norm reads the fp32 state");
-            wave_row_gnorm_quant<GT, NC>(raw, graw, K, a.gnw ? gl : nullptr, a.gain ? gl2 : nullptr, a.eps,
-                                         codes + wave * stride, sl + wave, sql + wave);
+            row_gnorm_quant<GT, NVQ, false, true>(static_cast<const float *>(a.x) + (int64_t)r * K,
+                                                  static_cast<const GT *>(a.g) + (int64_t)r * K, K, a.gnw, a.gain,
+                                                  a.eps, a.codes + (int64_t)r * K, a.s + r, a.sumq + r, nullptr, sh);
         } else {
-            wave_row_quant<XT, NC>(raw, K, a.gain ? gl : nullptr, a.eps, codes + wave * stride, sl + wave,
-                                   sql + wave);
+            row_quant<XT, NVQ, false, true>(static_cast<const XT *>(a.x) + (int64_t)r * K, K, a.gain, a.eps,
+                                            a.codes + (int64_t)r * K, a.s + r, a.sumq + r, sh);
         }
-    }
-    __syncthreads();
-
-    // 6. contraction of this wave's units; rows past b read row b - 1 (never stored)
-    const int8_t *arow = codes + min(lc, b - 1) * stride;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        // ---- contraction workgroup: 16 output channels
+        const int lc = lane & 15, lg = lane >> 4;
+        const int n0 = ((int)blockIdx.x - b) * 16;
+        const int gn = min(n0 + lc, p.nc - 1);  // columns past nc load a valid row; never stored
+        // weights of this wave's slices (straight-line: slices past the row load the last one, unused)
+        uint4 bw[SPW][NG];
 #pragma unroll
-    for (int i = 0; i < kQUnits; ++i) {
-        const int u = wave + kQWaves * i;
-        if (u < nunits) {
-            const int cb = u / nsl, s16 = (u - cb * nsl) * 16;
-            i32x4 acc[NG];
-#pragma unroll
-            for (int g = 0; g < NG; ++g) acc[g] = i32x4{};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const i32x4 af = *reinterpret_cast<const i32x4 *>(arow + 16 * (s16 + 4 * lg + j));
-#pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const uint32_t word = j == 0 ? wv[i][g].x : j == 1 ? wv[i][g].y : j == 2 ? wv[i][g].z : wv[i][g].w;
-                    acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, decode_word(word), acc[g], 0, 0, 0);
-                }
-            }
+        for (int j = 0; j < SPW; ++j) {
+            const int sl = min(wave + nw * j, a.nslices - 1);
 #pragma unroll
             for (int g = 0; g < NG; ++g)
+                bw[j][g] = *reinterpret_cast<const uint4 *>(p.B[g] + (int64_t)gn * KW + sl * 16 + lg * 4);
+        }
+        float sw[NG];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) atomicAdd(accl + (cb * NG + g) * 256 + (4 * lg + e) * 16 + lc, acc[g][e]);
+        for (int g = 0; g < NG; ++g) sw[g] = weight_sw(p.mu[g]);
+        // the epilogue operand of this thread's output (row er, channel n0 + ec)
+        constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
+        const int er = tid >> 4, ec = tid & 15;
+        float pre = 0.0f;
+        if (PRE && tid < 256) {
+            const RT *src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
+            pre = load_act(src, (int64_t)min(er, b - 1) * p.nc + min(n0 + ec, p.nc - 1));
+        }
+        // wait for the b rows
+        if (tid == 0) {
+            long spins = 0;
+            while (ld_dev(done) < (unsigned)b) {
+                __builtin_amdgcn_s_sleep(1);
+                if (++spins > kHSpinLimit) {
+                    __hip_atomic_fetch_add(g_handoff + 64 * kHSlots, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        // codes of row lc (rows past b read row b - 1, never stored), device scope
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(a.codes, 0, b * K, kBufferRsrcWord3);
+        const int arow = min(lc, b - 1) * K;
+        i32x4 af[SPW][4];
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const int sl = min(wave + nw * j, a.nslices - 1);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                af[j][q] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rsrc, arow + 16 * (sl * 16 + lg * 4 + q), 0, kSc1));
+        }
+        float srow = 0.0f;
+        int32_t sqrow = 0;
+        if (tid < 256 && er < b) {
+            srow = __uint_as_float(ld_dev(reinterpret_cast<const unsigned *>(a.s) + er));
+            sqrow = (int32_t)ld_dev(reinterpret_cast<const unsigned *>(a.sumq) + er);
+        }
+        i32x4 acc[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[g] = i32x4{};
+#pragma unroll
+        for (int j = 0; j < SPW; ++j)
+            if (wave + nw * j < a.nslices)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) {
+                        const uint32_t word = q == 0 ? bw[j][g].x : q == 1 ? bw[j][g].y : q == 2 ? bw[j][g].z : bw[j][g].w;
+                        acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[j][q], decode_word(word), acc[g], 0, 0, 0);
+                    }
+        int32_t *mine = part + wave * NG * 256;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mine[g * 256 + (4 * lg + i) * 16 + lc] = acc[g][i];
+        __syncthreads();
+        if (tid < 256 && er < b && n0 + ec < p.nc) {
+            int32_t v[NG];
+            float dq[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                int32_t sum = 0;
+                for (int w = 0; w < nw; ++w) sum += part[(w * NG + g) * 256 + er * 16 + ec];
+                v[g] = sum - sqrow;
+                dq[g] = __builtin_amdgcn_rcpf(srow * sw[g]);
+            }
+            epilogue_vals<EPI, NG, true>(p, er, n0 + ec, v, dq, pre);
         }
     }
+    // the last workgroup to finish returns the counters to zero for the next launch
     __syncthreads();
-
-    // 7. epilogue: one thread per output (row er, channel ech)
-    if (tid < CB * 256 && er < b && ech < p.nc) {
-        int32_t v[NG];
-        float dq[NG];
-        const float srow = sl[er];
-        const int32_t sqrow = sql[er];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            v[g] = accl[(ecb * NG + g) * 256 + er * 16 + ec] - sqrow;
-            dq[g] = __builtin_amdgcn_rcpf(srow * sw[g]);
+    if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == gridDim.x - 1) {
+            __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(fin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        epilogue_vals<EPI, NG, true>(p, er, ech, v, dq, pre);
     }
 }
 
@@ -183,96 +197,108 @@ static const char *q_epi_name(int epi) {
     return "?";
 }
 
-// chunk rounds per lane the row registers must hold, for the element types
-static int q_pick_nc(int k, int qk, ActType xt, ActType gt) {
-    const int need = k >> 8;
-    int opts[3] = {8, 12, 28};
-    int nopt = 3;
-    if (qk == QK_GNORM) nopt = gt == ACT_F32 ? 1 : 2;  // fp32 h plus g rows
-    else if (xt == ACT_F32) nopt = 2;
+// 256-thread chunks per row the quantiser registers must hold
+static int q_pick_nv(int k, int qk) {
+    const int need = (k + 1023) / 1024;
+    const int opts[3] = {2, 3, 7};
+    const int nopt = qk == QK_GNORM ? 2 : 3;
     for (int i = 0; i < nopt; ++i)
         if (need <= opts[i]) return opts[i];
     return 0;
 }
 
-static int q_pick_cb(int k) { return (k >> 8) >= 16 ? 1 : 2; }
+static int q_waves(int nslices) { return nslices < 4 ? 4 : nslices > 16 ? 16 : nslices; }
 
 bool quant_contract_supported(int64_t b, int nc, int k, EpiKind epi, int qk, ActType xt, ActType gt) {
+    (void)xt;
+    (void)gt;
     if (b < 1 || b > 16 || nc < 1 || k < 256 || k % 256) return false;
     if (epi != EPI_GATES_STEP && epi != EPI_RESID && epi != EPI_GLU) return false;
-    if (q_pick_nc(k, qk, xt, gt) == 0) return false;
-    const int cb = q_pick_cb(k);
-    if (cb * (k >> 8) > kQUnits * kQWaves) return false;
-    const int ng = epi == EPI_GATES_STEP ? 3 : epi == EPI_GLU ? 2 : 1;
-    return q_lds_bytes(k, ng, cb, qk) <= (size_t)160 * 1024;
+    if (q_pick_nv(k, qk) == 0) return false;
+    if ((qk == QK_GNORM || epi != EPI_RESID) && k > 3072) return false;  // one slice per wave for K = d
+    return (k >> 8) <= 32;
 }
 
-template <int NG, int EPI, int QK, typename XT, typename GT, typename RT, int NC, int CB>
+// The counter pair of a stream (kHSlots per process; -1 once they are taken).
+static int handoff_slot(hipStream_t st) {
+    static std::mutex mu;
+    static std::unordered_map<hipStream_t, int> slots;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = slots.find(st);
+    if (it != slots.end()) return it->second;
+    if ((int)slots.size() >= kHSlots) return -1;
+    const int s = (int)slots.size();
+    slots.emplace(st, s);
+    return s;
+}
+
+template <int NG, int EPI, int QK, typename XT, typename GT, typename RT, int NVQ, int SPW>
 static hipError_t run_q(const QuantContractArgs &a, hipStream_t st) {
-    const void *fn = reinterpret_cast<const void *>(&tgemv_q_kernel<NG, EPI, QK, XT, GT, RT, NC, CB>);
-    static std::once_flag once;
-    static hipError_t attr = hipSuccess;
-    std::call_once(once, [&] { attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024); });
-    if (attr != hipSuccess) return attr;
-    const size_t lds = q_lds_bytes(a.c.k, NG, CB, QK);
-    const unsigned grid = (unsigned)((a.c.nc + 16 * CB - 1) / (16 * CB));
-    tgemv_q_kernel<NG, EPI, QK, XT, GT, RT, NC, CB><<<grid, kQThreads, lds, st>>>(a);
+    const int nw = q_waves(a.nslices);
+    const size_t lds = (size_t)nw * NG * 256 * sizeof(int32_t);
+    const unsigned grid = (unsigned)(a.c.m + (a.c.nc + 15) / 16);
+    tgemv_q_kernel<NG, EPI, QK, XT, GT, RT, NVQ, SPW><<<grid, nw * 64, lds, st>>>(a);
     return hipGetLastError();
 }
 
-template <int NG, int EPI, int QK, typename XT, typename GT, typename RT, int NC>
-static hipError_t run_q_cb(const QuantContractArgs &a, int cb, hipStream_t st) {
-    return cb == 1 ? run_q<NG, EPI, QK, XT, GT, RT, NC, 1>(a, st) : run_q<NG, EPI, QK, XT, GT, RT, NC, 2>(a, st);
-}
-
 template <int NG, int EPI, int QK, typename XT, typename GT, typename RT>
-static hipError_t run_q_nc(const QuantContractArgs &a, int nc, int cb, hipStream_t st) {
-    if constexpr (QK == QK_GNORM && std::is_same<GT, float>::value) {
-        return run_q_cb<NG, EPI, QK, XT, GT, RT, 8>(a, cb, st);
-    } else if constexpr (QK == QK_ROW && std::is_same<XT, float>::value) {
-        return nc == 8 ? run_q_cb<NG, EPI, QK, XT, GT, RT, 8>(a, cb, st) : run_q_cb<NG, EPI, QK, XT, GT, RT, 12>(a, cb, st);
-    } else if constexpr (QK == QK_GNORM) {
-        return nc == 8 ? run_q_cb<NG, EPI, QK, XT, GT, RT, 8>(a, cb, st) : run_q_cb<NG, EPI, QK, XT, GT, RT, 12>(a, cb, st);
+static hipError_t run_q_nv(const QuantContractArgs &a, int nv, int spw, hipStream_t st) {
+    if constexpr (QK == QK_GNORM || EPI != EPI_RESID) {
+        // K = d: at most 3072, one slice per wave
+        if (spw != 1 || nv == 7) return hipErrorInvalidValue;
+        return nv == 2 ? run_q<NG, EPI, QK, XT, GT, RT, 2, 1>(a, st) : run_q<NG, EPI, QK, XT, GT, RT, 3, 1>(a, st);
     } else {
-        switch (nc) {
-            case 8: return run_q_cb<NG, EPI, QK, XT, GT, RT, 8>(a, cb, st);
-            case 12: return run_q_cb<NG, EPI, QK, XT, GT, RT, 12>(a, cb, st);
-            default: return run_q_cb<NG, EPI, QK, XT, GT, RT, 28>(a, cb, st);
+        switch (nv * 2 + spw) {
+            case 2 * 2 + 1: return run_q<NG, EPI, QK, XT, GT, RT, 2, 1>(a, st);
+            case 3 * 2 + 1: return run_q<NG, EPI, QK, XT, GT, RT, 3, 1>(a, st);
+            case 7 * 2 + 1: return run_q<NG, EPI, QK, XT, GT, RT, 7, 1>(a, st);
+            case 7 * 2 + 2: return run_q<NG, EPI, QK, XT, GT, RT, 7, 2>(a, st);
         }
+        return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_quant_contract(const ContractArgs &c, EpiKind epi, int qk, const void *x, ActType xt,
                                  const void *g, ActType gt, const float *gain, const float *gnw, float eps,
-                                 hipStream_t st, std::string *path) {
+                                 int8_t *codes, float *s, int32_t *sumq, hipStream_t st, std::string *path) {
     if (!quant_contract_supported(c.m, c.nc, c.k, epi, qk, xt, gt)) return hipErrorInvalidValue;
     QuantContractArgs a{};
     a.c = c;
     a.x = x; a.g = g; a.gain = gain; a.gnw = gnw; a.eps = eps;
-    const int nc = q_pick_nc(c.k, qk, xt, gt), cb = q_pick_cb(c.k);
+    a.codes = codes; a.s = s; a.sumq = sumq;
+    a.nslices = c.k >> 8;
+    a.slot = handoff_slot(st);
+    if (a.slot < 0) return hipErrorInvalidValue;
+    const int nv = q_pick_nv(c.k, qk);
+    const int spw = a.nslices > 16 ? 2 : 1;
     if (path) *path += std::string("tgemv_q<") + (qk == QK_GNORM ? "gnorm_resid" : q_epi_name(epi)) + ">;";
     const bool xf = xt == ACT_F32, gf = gt == ACT_F32;
     switch (epi) {
         case EPI_GATES_STEP:  // quantised x, state in place
             if (qk != QK_ROW) return hipErrorInvalidValue;
-            return xf ? run_q_nc<3, EPI_GATES_STEP, QK_ROW, float, float, float>(a, nc, cb, st)
-                      : run_q_nc<3, EPI_GATES_STEP, QK_ROW, uint16_t, uint16_t, float>(a, nc, cb, st);
+            return xf ? run_q_nv<3, EPI_GATES_STEP, QK_ROW, float, float, float>(a, nv, spw, st)
+                      : run_q_nv<3, EPI_GATES_STEP, QK_ROW, uint16_t, uint16_t, float>(a, nv, spw, st);
         case EPI_GLU:  // quantised x1 (fp32)
             if (qk != QK_ROW || !xf) return hipErrorInvalidValue;
-            return run_q_nc<2, EPI_GLU, QK_ROW, float, float, float>(a, nc, cb, st);
+            return run_q_nv<2, EPI_GLU, QK_ROW, float, float, float>(a, nv, spw, st);
         case EPI_RESID:
             if (qk == QK_GNORM) {  // g_norm gate of (h, g) + o_proj, residual x in g's type
                 if (!xf || c.res_type != gt) return hipErrorInvalidValue;
-                return gf ? run_q_nc<1, EPI_RESID, QK_GNORM, float, float, float>(a, nc, cb, st)
-                          : run_q_nc<1, EPI_RESID, QK_GNORM, float, uint16_t, uint16_t>(a, nc, cb, st);
+                return gf ? run_q_nv<1, EPI_RESID, QK_GNORM, float, float, float>(a, nv, spw, st)
+                          : run_q_nv<1, EPI_RESID, QK_GNORM, float, uint16_t, uint16_t>(a, nv, spw, st);
             }
             // quantised z + down_proj, residual x1 (fp32)
             if (c.res_type != ACT_F32) return hipErrorInvalidValue;
-            return xf ? run_q_nc<1, EPI_RESID, QK_ROW, float, float, float>(a, nc, cb, st)
-                      : run_q_nc<1, EPI_RESID, QK_ROW, uint16_t, uint16_t, float>(a, nc, cb, st);
+            return xf ? run_q_nv<1, EPI_RESID, QK_ROW, float, float, float>(a, nv, spw, st)
+                      : run_q_nv<1, EPI_RESID, QK_ROW, uint16_t, uint16_t, float>(a, nv, spw, st);
         default:
             return hipErrorInvalidValue;
     }
+}
+
+hipError_t quant_contract_expired_waits(unsigned *count) {
+    return hipMemcpyFromSymbol(count, HIP_SYMBOL(g_handoff), sizeof(unsigned), 64 * kHSlots * sizeof(unsigned),
+                               hipMemcpyDeviceToHost);
 }
 
 }  // namespace mmf

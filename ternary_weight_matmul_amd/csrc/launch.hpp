@@ -78,15 +78,18 @@ hipError_t launch_decode_step(const DecodeStepArgs &a, hipStream_t stream, std::
 // Barrier waits of the one-XCD decode step that ran out of patience (synchronous).
 hipError_t decode_step_expired_spins(unsigned *count);
 
-// Decode contraction that quantises its own b <= 16 input rows (k_gemv_q.hip):
-// QK_ROW: RMSNorm + absmax int8 of x [b][k] (type xt) with gain;
-// QK_GNORM: g_norm gate of h (fp32) and g (type gt) with g_norm weight gnw,
-// then the quantiser with gain. c's A / s / sumq are not used.
+// Decode contraction with the quantiser of its b <= 16 input rows in the same
+// launch (k_gemv_q.hip): QK_ROW: RMSNorm + absmax int8 of x [b][k] (type xt)
+// with gain; QK_GNORM: g_norm gate of h (fp32) and g (type gt) with g_norm
+// weight gnw, then the quantiser with gain. The rows' codes, scales and sums
+// pass through codes [b][k], s [b], sumq [b]; c's A / s / sumq are not used.
 enum QuantKind { QK_ROW = 0, QK_GNORM = 1 };
 bool quant_contract_supported(int64_t b, int nc, int k, EpiKind epi, int qk, ActType xt, ActType gt);
 hipError_t launch_quant_contract(const ContractArgs &c, EpiKind epi, int qk, const void *x, ActType xt,
                                  const void *g, ActType gt, const float *gain, const float *gnw, float eps,
-                                 hipStream_t stream, std::string *path);
+                                 int8_t *codes, float *s, int32_t *sumq, hipStream_t stream, std::string *path);
+// Waits of those launches that gave up (synchronous).
+hipError_t quant_contract_expired_waits(unsigned *count);
 
 // Prefill-shaped contraction (int8 MFMA tiles) and decode-shaped one (m <= 64).
 hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a,

@@ -297,7 +297,8 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
     ci.m = b; ci.nc = d; ci.k = d;
     ci.out0 = h; ci.out1 = L.g; ci.out_type = ACT_F32; ci.aux_type = at;
     hipError_t e = timed("tgemv_q<gates_step>", b, 3 * d, d, st, [&] {
-        return launch_quant_contract(ci, EPI_GATES_STEP, QK_ROW, x, at, nullptr, at, w->i.norm_w, nullptr, eps, st, path);
+        return launch_quant_contract(ci, EPI_GATES_STEP, QK_ROW, x, at, nullptr, at, w->i.norm_w, nullptr, eps, L.codes_b,
+                                     L.s_b, L.sq_b, st, path);
     });
     if (e != hipSuccess) return e;
     ContractArgs co{};
@@ -305,8 +306,8 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
     co.m = b; co.nc = d; co.k = d;
     co.out0 = L.x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
     e = timed("tgemv_q<gnorm_resid>", b, d, d, st, [&] {
-        return launch_quant_contract(co, EPI_RESID, QK_GNORM, h, ACT_F32, L.g, at, w->o.norm_w, w->g_norm_w, eps, st,
-                                     path);
+        return launch_quant_contract(co, EPI_RESID, QK_GNORM, h, ACT_F32, L.g, at, w->o.norm_w, w->g_norm_w, eps,
+                                     L.codes_b, L.s_b, L.sq_b, st, path);
     });
     if (e != hipSuccess) return e;
     ContractArgs cg{};
@@ -318,7 +319,7 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
     cg.out0 = L.z; cg.aux_type = at;
     e = timed("tgemv_q<glu>", b, 2 * inner, d, st, [&] {
         return launch_quant_contract(cg, EPI_GLU, QK_ROW, L.x1, ACT_F32, nullptr, ACT_F32, w->gate.norm_w, nullptr, eps,
-                                     st, path);
+                                     L.codes_b, L.s_b, L.sq_b, st, path);
     });
     if (e != hipSuccess) return e;
     ContractArgs cd{};
@@ -326,7 +327,8 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
     cd.m = b; cd.nc = d; cd.k = inner;
     cd.out0 = out; cd.out_type = at; cd.res = L.x1; cd.res_type = ACT_F32;
     return timed("tgemv_q<resid>", b, d, inner, st, [&] {
-        return launch_quant_contract(cd, EPI_RESID, QK_ROW, L.z, at, nullptr, at, w->down.norm_w, nullptr, eps, st, path);
+        return launch_quant_contract(cd, EPI_RESID, QK_ROW, L.z, at, nullptr, at, w->down.norm_w, nullptr, eps, L.codes_b,
+                                     L.s_b, L.sq_b, st, path);
     });
 }
 
@@ -525,9 +527,10 @@ mmf_status mmf_set_decode_kernel(int mode) {
 
 mmf_status mmf_decode_expired_waits(uint32_t *count) {
     if (!count) return fail(MMF_ERR_INVALID_ARG, "count is NULL");
-    unsigned c = 0;
+    unsigned c = 0, c2 = 0;
     mmf_status st = hip_status(decode_step_expired_spins(&c), "mmf_decode_expired_waits");
-    *count = c;
+    if (st == MMF_OK) st = hip_status(quant_contract_expired_waits(&c2), "mmf_decode_expired_waits");
+    *count = c + c2;
     return st;
 }
 

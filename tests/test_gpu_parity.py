@@ -570,6 +570,7 @@ FUSED_CASES = [
     (16, "bf16", None, 2048, 5632),
     (1, "bf16", None, 2048, 5632),
     (3, "f32", None, 2048, 2816),
+    (7, "f32", None, 2048, 5632),
     (9, "bf16", None, 768, 1280),
     (16, "bf16", None, 2560, 6912),
     (12, "f32", "shared", 2048, 3072),
@@ -618,13 +619,12 @@ def test_decode_fused_graph_replays(gpu):
 
 
 def test_decode_fused_unsupported_shapes(gpu):
-    """Forcing the fused kernels where they do not apply (b > 16, fp32 activations with inner >
-    3072, shapes off the 256 grid, distinct i/f/g gains) is an error, never a silent fallback;
-    auto takes the separate kernels there."""
+    """Forcing the fused kernels where they do not apply (b > 16, d > 3072, shapes off the 256
+    grid, distinct i/f/g gains) is an error, never a silent fallback."""
     mmf = _mmf()
     cases = [(16, "bf16", 1024, 2816, None, True), (17, "bf16", 1024, 2816, None, False),
-             (4, "f32", 2048, 5632, None, False), (4, "bf16", 272, 1040, None, False),
-             (4, "bf16", 1024, 2816, "distinct", False)]
+             (4, "f32", 2048, 5632, None, True), (4, "bf16", 3328, 256, None, False),
+             (4, "bf16", 272, 1040, None, False), (4, "bf16", 1024, 2816, "distinct", False)]
     for b, act, d, inner, gains, fused in cases:
         _, P = make_pair(d, inner, 970 + b, gpu, gains)
         xs = synth.activations((b, d), 971, act)
