@@ -115,25 +115,47 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
     return 0.0, 0.0
 
 
-def source_digest() -> str:
-    """sha256 of the kernel sources, to tell whether stored counter figures still apply."""
+# the source files each kernel family is built from
+_COMMON = ["device_common.hpp", "launch.hpp"]
+KERNEL_SOURCES = {
+    "tgemv": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
+    "tgemm": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
+    "tgemm_dma": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
+    "tgemv_q": ["k_gemv_q.hip", "row_quant.hpp", "epilogue.hpp"] + _COMMON,
+    "decode_step_xcd": ["k_decode.hip", "row_quant.hpp", "epilogue.hpp"] + _COMMON,
+    "norm_quant": ["k_quant.hip", "row_quant.hpp"] + _COMMON,
+    "gnorm_quant": ["k_quant.hip", "row_quant.hpp"] + _COMMON,
+    "scan": ["k_scan.hip"] + _COMMON,
+}
+
+
+def kernel_files(kernel: str):
+    base = _kind(kernel.split(" ")[0])[0]
+    return KERNEL_SOURCES.get("scan" if base.startswith("scan") else base)
+
+
+def source_digest(files=None) -> str:
+    """sha256 of kernel sources (the given files of csrc/, else all of them), to tell whether
+    stored counter figures still apply to the code that runs."""
     import hashlib
     hsh = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_matmul_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                hsh.update(name.encode() + b"\0" + f.read())
+    names = sorted(files) if files else sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp")))
+    for name in names:
+        with open(os.path.join(csrc, name), "rb") as f:
+            hsh.update(name.encode() + b"\0" + f.read())
     return hsh.hexdigest()[:16]
 
 
 def stored_traffic(key: str):
     """HBM bytes per launch of kernel `key` from a counter summary under profiles/ (FETCH_SIZE +
-    WRITE_SIZE, scaled by the copy-kernel calibration), if one exists for the current sources."""
+    WRITE_SIZE, scaled by the copy-kernel calibration), if one exists for the current sources of
+    that kernel (the digest of the files it is built from)."""
     pdir = os.path.join(ROOT, "profiles")
-    if not os.path.isdir(pdir):
+    files = kernel_files(key)
+    if not os.path.isdir(pdir) or not files:
         return None
-    digest = source_digest()
+    digest = source_digest(files)
     for name in sorted(os.listdir(pdir)):
         if not (name.startswith("traffic_") and name.endswith(".txt")):
             continue
