@@ -116,13 +116,17 @@ __device__ __forceinline__ void row_quant(const T *xr, int k, const float *gain,
     const int tid = threadIdx.x;
     const int nch = k >> 2;
     float v[NV][4], gv[NV][4];
+    // straight-line loads under one wave-uniform branch (slots past the row end
+    // read the last chunk and go unused): a branch per slot would make the
+    // compiler wait for each load before the next
+    if (tid < 256) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        if (tid < 256 && 256 * j < nch) {
+        for (int j = 0; j < NV; ++j) {
             const int c = min(tid + 256 * j, nch - 1);
             rq_set4(v[j], row_ld4<NT>(xr + 4 * (int64_t)c));
             rq_set4(gv[j], gain ? *reinterpret_cast<const float4 *>(gain + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f));
         }
+    }
     double ss = 0.0;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
@@ -152,15 +156,16 @@ __device__ __forceinline__ void row_gnorm_quant(const float *hr, const TG *gr, i
     const int tid = threadIdx.x;
     const int nch = d >> 2;
     float u[NV][4], gs[NV][4], wn[NV][4], og[NV][4];
+    if (tid < 256) {  // straight-line loads, as in row_quant
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
-        if (tid < 256 && 256 * j < nch) {
+        for (int j = 0; j < NV; ++j) {
             const int c = min(tid + 256 * j, nch - 1);
             rq_set4(u[j], row_ld4<NT>(hr + 4 * (int64_t)c));
             rq_set4(gs[j], row_ld4<NT>(gr + 4 * (int64_t)c));
             rq_set4(wn[j], gnw ? *reinterpret_cast<const float4 *>(gnw + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f));
             rq_set4(og[j], ogain ? *reinterpret_cast<const float4 *>(ogain + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f));
         }
+    }
     double ss = 0.0;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
