@@ -227,9 +227,9 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
  * mmf_set_decode_kernel -- which implementation mmf_layer_decode_step uses,
  * process-wide: 0 = the fastest implementation measured on MI355X (default;
  * at present the separate kernels for every shape: at the 1.3B shape they
- * take 31 / 37 us per layer at batch 1 / 16 in a HIP graph, the four fused
- * kernels 36 / 47 (a hand-off across XCDs within a launch costs about what a
- * kernel boundary does), and the one-XCD kernel 45 / 48, held to one XCD's
+ * take 29 / 35 us per layer at batch 1 / 16 in a HIP graph, the four fused
+ * kernels 34 / 46 (a hand-off across XCDs within a launch costs about what a
+ * kernel boundary does), and the one-XCD kernel 45 / 46, held to one XCD's
  * share of HBM bandwidth);
  * 1 = always the separate kernels; 2 = only the one-XCD kernel; 3 = only the
  * four fused kernels (2 and 3: UNSUPPORTED where they do not apply).
@@ -238,9 +238,11 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
 mmf_status mmf_set_decode_kernel(int mode);
 
 /*
- * mmf_decode_expired_waits -- how many barrier waits of the one-XCD decode
- * kernel gave up (each wait is bounded, about a second; a non-zero count means
- * a result was computed from incomplete data). Synchronous; for diagnostics.
+ * mmf_decode_expired_waits -- how many waits of the one-XCD decode kernel
+ * (barriers) and of the fused decode kernels (rows handed over) gave up since
+ * the library loaded, on the current device (each wait is bounded, about a
+ * second; a non-zero count means a result was computed from incomplete data).
+ * Synchronous; for diagnostics.
  */
 mmf_status mmf_decode_expired_waits(uint32_t *count);
 
