@@ -269,6 +269,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(const DecodeSt
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+// XCD of each workgroup of a probe launch (the placement check below)
+constexpr int kXccMapGroups = 2048;
+__device__ unsigned g_xccmap[kXccMapGroups];
+
 __global__ void xcc_map_kernel(unsigned *out) {
     if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
 }
@@ -294,30 +298,25 @@ static bool xcd_layout_ok(hipStream_t st, std::string *why) {
     }
     (void)hipGetLastError();
     bool ok = false;
+    std::string note;
     unsigned *buf = nullptr;
-    const int n = 2048;
-    std::string note = "no-check";
-    if (hipMalloc(&buf, n * sizeof(unsigned)) == hipSuccess) {
-        xcc_map_kernel<<<n, 64, 0, st>>>(buf);
-        unsigned host[n];
-        const hipError_t e1 = hipMemcpyAsync(host, buf, sizeof host, hipMemcpyDeviceToHost, st);
-        const hipError_t e2 = e1 == hipSuccess ? hipStreamSynchronize(st) : e1;
-        if (e2 == hipSuccess) {
-            ok = true;
+    hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&buf), HIP_SYMBOL(g_xccmap));
+    if (e == hipSuccess) {
+        xcc_map_kernel<<<kXccMapGroups, 64, 0, st>>>(buf);
+        unsigned host[kXccMapGroups];
+        e = hipMemcpyAsync(host, buf, sizeof host, hipMemcpyDeviceToHost, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e == hipSuccess) {
             int bad = -1;
-            for (int i = 0; i < n; ++i)
+            for (int i = 0; i < kXccMapGroups; ++i)
                 if (host[i] != (host[0] + i) % 8 && bad < 0) bad = i;
             ok = bad < 0;
             note = "xcc";
             for (int i = 0; i < 8; ++i) note += char('0' + (host[i] & 15));
             if (bad >= 0) note += ",first-mismatch@" + std::to_string(bad);
-        } else {
-            note = std::string("copy:") + hipGetErrorName(e2);
         }
-        (void)hipFree(buf);
-    } else {
-        note = "malloc";
     }
+    if (e != hipSuccess) note = std::string("check:") + hipGetErrorName(e);
     seen[dev] = note;
     *why = note;
     state[dev] = ok ? 1 : 2;
