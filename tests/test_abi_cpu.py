@@ -146,3 +146,20 @@ def test_workspace_grows_with_tokens(lib):
     sz2 = ctypes.c_size_t(0)
     assert lib.mmf_layer_workspace_size(ctypes.byref(L2), 2, 256, ctypes.byref(sz2)) == OK
     assert sz2.value > sizes[2]
+
+
+def test_decode_kernel_modes(lib):
+    """mmf_set_decode_kernel accepts auto / separate / one-XCD / fused and rejects the rest
+    without touching the GPU."""
+    try:
+        for mode in (0, 1, 2, 3):
+            assert lib.mmf_set_decode_kernel(mode) == OK
+        for mode in (-1, 4, 99):
+            assert lib.mmf_set_decode_kernel(mode) == INVALID
+            assert b"decode kernel mode" in lib.mmf_last_error()
+    finally:
+        lib.mmf_set_decode_kernel(0)
+    for name, mode in B.DECODE_KERNELS.items():
+        B.set_decode_kernel(name)
+    B.set_decode_kernel("auto")
+    assert lib.mmf_decode_expired_waits(None) == INVALID
