@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch decode steps eagerly instead of a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (for scaling HBM counters)")
+    ap.add_argument("--vendor-int8-gemm", action="store_true",
+                    help="only time the vendor library's dense int8 GEMM (torch._int_mm) at the prefill "
+                         "contraction shapes, as a reference for the int8 MFMA fraction")
     return ap.parse_args()
 
 
@@ -67,6 +70,33 @@ def calibrate_copy():
     ms = e0.elapsed_time(e1) / 2
     print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": 3, "us_per_launch": round(ms * 1000, 1),
                       "read_plus_write_GBps": round(8 * n / (ms / 1000) / 1e9, 1)}), flush=True)
+
+
+def vendor_int8_gemm(shape: str, batch: int, prompt: int):
+    """Dense int8 x int8 -> int32 products of the vendor library at the prefill shapes (weights as
+    plain int8, no epilogue): what the same matrix cores reach without this library's kernels."""
+    import torch
+    from ternary_weight_matmul_amd import synth
+    d, inner, _ = synth.SHAPES[shape]
+    M = batch * prompt
+    out = []
+    for name, N, K in [("i/f/g", 3 * d, d), ("o_proj", d, d), ("gate_proj", 2 * inner, d), ("down_proj", d, inner)]:
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+        b = torch.randint(-1, 2, (K, N), dtype=torch.int8, device="cuda")
+        for _ in range(3):
+            torch._int_mm(a, b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch._int_mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 100.0
+        tops = 2.0 * M * N * K / (us / 1e6) / 1e12
+        out.append({"contraction": name, "m": M, "n": N, "k": K, "us": round(us, 1), "int8_tops": round(tops, 1),
+                    "frac_mfma": round(tops / INT8_MFMA_PEAK_TOPS, 4)})
+        del a, b
+    print(json.dumps({"vendor_int8_gemm": out, "shape": shape}), flush=True)
 
 
 ACT_BYTES = 2  # bf16 activations
@@ -177,6 +207,9 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.vendor_int8_gemm:
+        vendor_int8_gemm(args.shape, args.batch, args.prompt)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
