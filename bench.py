@@ -49,7 +49,7 @@ def parse():
                     help="only run a plain 1 GiB device-to-device copy three times (for scaling HBM counters)")
     ap.add_argument("--vendor-int8-gemm", action="store_true",
                     help="only time the vendor library's dense int8 GEMM (torch._int_mm) at the prefill "
-                         "contraction shapes, as a reference for the int8 MFMA fraction")
+                         "contraction shapes and its dense bf16 product at the decode shapes, as references")
     return ap.parse_args()
 
 
@@ -96,7 +96,32 @@ def vendor_int8_gemm(shape: str, batch: int, prompt: int):
         out.append({"contraction": name, "m": M, "n": N, "k": K, "us": round(us, 1), "int8_tops": round(tops, 1),
                     "frac_mfma": round(tops / INT8_MFMA_PEAK_TOPS, 4)})
         del a, b
-    print(json.dumps({"vendor_int8_gemm": out, "shape": shape}), flush=True)
+    # decode-shaped products (batch rows x dense bf16 weights): the same contractions as one
+    # token step at this batch, with 16-bit instead of 2-bit weights
+    dec = []
+    for name, N, K in [("i/f/g", 3 * d, d), ("o_proj", d, d), ("gate_proj", 2 * inner, d), ("down_proj", d, inner)]:
+        x = torch.randn(batch, K, device="cuda").to(torch.bfloat16)
+        w = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+        y = torch.nn.functional.linear(x, w)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()  # replayed, so that host launch cost does not count
+        with torch.cuda.graph(g):
+            for _ in range(20):
+                y = torch.nn.functional.linear(x, w)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / 100
+        nbytes = 2.0 * (N * K + batch * K + batch * N)
+        dec.append({"contraction": name, "m": batch, "n": N, "k": K, "us": round(us, 2),
+                    "gbs": round(nbytes / (us / 1e6) / 1e9, 1), "frac_hbm": round(nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4)})
+        del x, w, y, g
+    print(json.dumps({"vendor_int8_gemm": out, "vendor_bf16_decode_linear": dec, "shape": shape}), flush=True)
 
 
 ACT_BYTES = 2  # bf16 activations
