@@ -571,7 +571,7 @@ __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p,
 // MFMA, so a GEMV costs about one memory round trip. Wave partial sums are
 // combined with LDS integer atomics (exact, order-free). RT is the element
 // type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
-template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT, int EPT>
+template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT, int EPT, int SPW>
 __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const int nslices) {
     constexpr int NA = SHARED_A ? 1 : NG;
     constexpr int PART = MB * NG * 256;  // one wave's partial sums
@@ -618,13 +618,12 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
     // clamped and then zeroed (offset code 0 adds nothing to sum c*q), rows
     // past m are clamped (their sums are never stored).
     const bool whole = (KW % (4 * WPL)) == 0;
-    for (int sl = wave; sl < nslices; sl += nw) {
+    auto load_slice = [&](int sl, uint32_t (&bw)[NG][WPL], i32x4 (&a)[MB][NA][WPL], bool is_whole) {
         const int w0 = sl * 4 * WPL + lg * WPL;
-        uint32_t bw[NG][WPL];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const uint32_t *src = p.B[g] + (int64_t)gn * KW;
-            if (whole) {
+            if (is_whole) {
 #pragma unroll
                 for (int q = 0; q < WPL / 4; ++q) {
                     const uint4 v = reinterpret_cast<const uint4 *>(src + w0)[q];
@@ -638,7 +637,6 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
                 }
             }
         }
-        i32x4 a[MB][NA][WPL];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int64_t row = min((int64_t)(mb * 16 + lc), M - 1);
@@ -646,9 +644,11 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
             for (int q = 0; q < NA; ++q) {
                 const i32x4 *src = reinterpret_cast<const i32x4 *>(p.A[q] + row * K);
 #pragma unroll
-                for (int j = 0; j < WPL; ++j) a[mb][q][j] = src[whole ? w0 + j : min(w0 + j, KW - 1)];
+                for (int j = 0; j < WPL; ++j) a[mb][q][j] = src[is_whole ? w0 + j : min(w0 + j, KW - 1)];
             }
         }
+    };
+    auto mma_slice = [&](const uint32_t (&bw)[NG][WPL], const i32x4 (&a)[MB][NA][WPL]) {
 #pragma unroll
         for (int j = 0; j < WPL; ++j)
 #pragma unroll
@@ -658,6 +658,24 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][SHARED_A ? 0 : g][j], b, acc[mb][g], 0, 0, 0);
             }
+    };
+    if constexpr (SPW == 2) {
+        // two slices per wave at most (whole rows): both slices' loads are issued
+        // before the first MFMA, so the wave pays one memory round trip, not two;
+        // a wave without a second slice loads the last one again and skips it
+        uint32_t bw0[NG][WPL], bw1[NG][WPL];
+        i32x4 a0[MB][NA][WPL], a1[MB][NA][WPL];
+        load_slice(wave, bw0, a0, true);
+        load_slice(min(wave + nw, nslices - 1), bw1, a1, true);
+        mma_slice(bw0, a0);
+        if (wave + nw < nslices) mma_slice(bw1, a1);
+    } else {
+        for (int sl = wave; sl < nslices; sl += nw) {
+            uint32_t bw[NG][WPL];
+            i32x4 a[MB][NA][WPL];
+            load_slice(sl, bw, a, whole);
+            mma_slice(bw, a);
+        }
     }
     // each wave's partial sums into its own LDS slot; summed below in wave order
     int32_t *mine = part + wave * PART;
@@ -727,11 +745,22 @@ static void run_gemv_mb(const ContractArgs &a, hipStream_t st) {
     const unsigned grid = (unsigned)((a.nc + 15) / 16);
     const size_t lds = (size_t)waves * MB * NG * 256 * sizeof(int32_t);
     const int ept = (MB * 256 + waves * 64 - 1) / (waves * 64);
+    // up to two whole slices per wave: both loaded before the MFMAs (one round trip)
+    const bool two = MB <= 2 && nslices > waves && nslices <= 2 * waves && kw % (4 * WPL) == 0;
+    if constexpr (MB <= 2) {
+        if (two) {
+            switch (ept) {
+                case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1, 2><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+                default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2, 2><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+            }
+            return;
+        }
+    }
     switch (ept) {
-        case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        case 2: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        case 3: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 3><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 4><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 2: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 3: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 3, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 4, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
     }
 }
 
