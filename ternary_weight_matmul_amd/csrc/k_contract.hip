@@ -571,22 +571,25 @@ __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p,
 // MFMA, so a GEMV costs about one memory round trip. Wave partial sums are
 // combined with LDS integer atomics (exact, order-free). RT is the element
 // type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
-template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT, int EPT, int SPW>
+template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT, int EPT, int SPW, int CB>
 __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const int nslices) {
     constexpr int NA = SHARED_A ? 1 : NG;
-    constexpr int PART = MB * NG * 256;  // one wave's partial sums
-    extern __shared__ int32_t part[];    // [waves][PART]
+    constexpr int PART = MB * CB * NG * 256;  // one wave's partial sums
+    extern __shared__ int32_t part[];         // [waves][PART]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int lc = lane & 15, lg = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * CB;
     const int K = p.k, KW = K >> 4;
     const int64_t M = p.m;
-    const int gn = min(n0 + lc, p.nc - 1);  // columns past nc load a valid row; never stored
+    int gn[CB];  // columns past nc load a valid row; never stored
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) gn[cb] = min(n0 + cb * 16 + lc, p.nc - 1);
     // weight scales, the quantiser's per-row scales and sums and the epilogue
     // operands (residual / old state) do not depend on the contraction: load
     // them before it, unconditionally (clamped to a valid element; the values
     // of outputs that are not stored go unused) so that no wait for them comes
-    // before the contraction's own loads
+    // before the contraction's own loads. Output idx of the workgroup: row block
+    // idx / (256 CB), channel block (idx / 256) % CB, row (idx / 16) % 16, channel idx % 16.
     float mu_v[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) mu_v[g] = *p.mu[g];
@@ -597,9 +600,9 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int idx = tid + e * blockDim.x;
-        const int64_t m = (int64_t)(idx >> 8) * 16 + ((idx >> 4) & 15);
+        const int64_t m = (int64_t)(idx / (256 * CB)) * 16 + ((idx >> 4) & 15);
         const int64_t mc = m < M ? m : M - 1;
-        const int c = n0 + (idx & 15);
+        const int c = n0 + ((idx >> 8) % CB) * 16 + (idx & 15);
         pre[e] = PRE ? load_act(pre_src, mc * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -608,35 +611,41 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
         }
     }
 
-    i32x4 acc[MB][NG];
+    i32x4 acc[MB][CB][NG];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) acc[mb][g] = i32x4{};
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[mb][cb][g] = i32x4{};
 
     // Every load of a slice is unconditional: words past the row end are
     // clamped and then zeroed (offset code 0 adds nothing to sum c*q), rows
-    // past m are clamped (their sums are never stored).
+    // past m are clamped (their sums are never stored). An activation fragment
+    // serves the CB channel blocks and NG groups of the workgroup.
     const bool whole = (KW % (4 * WPL)) == 0;
-    auto load_slice = [&](int sl, uint32_t (&bw)[NG][WPL], i32x4 (&a)[MB][NA][WPL], bool is_whole) {
+    auto load_slice = [&](int sl, uint32_t (&bw)[CB][NG][WPL], i32x4 (&a)[MB][NA][WPL], bool is_whole) {
         const int w0 = sl * 4 * WPL + lg * WPL;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const uint32_t *src = p.B[g] + (int64_t)gn * KW;
-            if (is_whole) {
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int q = 0; q < WPL / 4; ++q) {
-                    const uint4 v = reinterpret_cast<const uint4 *>(src + w0)[q];
-                    bw[g][4 * q] = v.x; bw[g][4 * q + 1] = v.y; bw[g][4 * q + 2] = v.z; bw[g][4 * q + 3] = v.w;
-                }
-            } else {
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t *src = p.B[g] + (int64_t)gn[cb] * KW;
+                if (is_whole) {
 #pragma unroll
-                for (int j = 0; j < WPL; ++j) {
-                    const uint32_t v = src[min(w0 + j, KW - 1)];
-                    bw[g][j] = w0 + j < KW ? v : 0u;
+                    for (int q = 0; q < WPL / 4; ++q) {
+                        const uint4 v = reinterpret_cast<const uint4 *>(src + w0)[q];
+                        bw[cb][g][4 * q] = v.x; bw[cb][g][4 * q + 1] = v.y;
+                        bw[cb][g][4 * q + 2] = v.z; bw[cb][g][4 * q + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < WPL; ++j) {
+                        const uint32_t v = src[min(w0 + j, KW - 1)];
+                        bw[cb][g][j] = w0 + j < KW ? v : 0u;
+                    }
                 }
             }
-        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int64_t row = min((int64_t)(mb * 16 + lc), M - 1);
@@ -648,22 +657,25 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
             }
         }
     };
-    auto mma_slice = [&](const uint32_t (&bw)[NG][WPL], const i32x4 (&a)[MB][NA][WPL]) {
+    auto mma_slice = [&](const uint32_t (&bw)[CB][NG][WPL], const i32x4 (&a)[MB][NA][WPL]) {
 #pragma unroll
         for (int j = 0; j < WPL; ++j)
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const i32x4 b = decode_word(bw[g][j]);
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[mb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][SHARED_A ? 0 : g][j], b, acc[mb][g], 0, 0, 0);
-            }
+                for (int g = 0; g < NG; ++g) {
+                    const i32x4 b = decode_word(bw[cb][g][j]);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb][cb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][SHARED_A ? 0 : g][j], b,
+                                                                               acc[mb][cb][g], 0, 0, 0);
+                }
     };
     if constexpr (SPW == 2) {
         // two slices per wave at most (whole rows): both slices' loads are issued
         // before the first MFMA, so the wave pays one memory round trip, not two;
         // a wave without a second slice loads the last one again and skips it
-        uint32_t bw0[NG][WPL], bw1[NG][WPL];
+        uint32_t bw0[CB][NG][WPL], bw1[CB][NG][WPL];
         i32x4 a0[MB][NA][WPL], a1[MB][NA][WPL];
         load_slice(wave, bw0, a0, true);
         load_slice(min(wave + nw, nslices - 1), bw1, a1, true);
@@ -671,7 +683,7 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
         if (wave + nw < nslices) mma_slice(bw1, a1);
     } else {
         for (int sl = wave; sl < nslices; sl += nw) {
-            uint32_t bw[NG][WPL];
+            uint32_t bw[CB][NG][WPL];
             i32x4 a[MB][NA][WPL];
             load_slice(sl, bw, a, whole);
             mma_slice(bw, a);
@@ -682,9 +694,12 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mine[(mb * NG + g) * 256 + (4 * lg + i) * 16 + lc] = acc[mb][g][i];
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    mine[((mb * CB + cb) * NG + g) * 256 + (4 * lg + i) * 16 + lc] = acc[mb][cb][g][i];
     __syncthreads();
     float sw[NG];
 #pragma unroll
@@ -693,20 +708,21 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int idx = tid + e * blockDim.x;
-        const int mb = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+        const int mb = idx / (256 * CB), cb = (idx >> 8) % CB, r = (idx >> 4) & 15, c = idx & 15;
         const int64_t m = mb * 16 + r;
-        if (idx < MB * 256 && m < M && n0 + c < p.nc) {
+        const int ch = n0 + cb * 16 + c;
+        if (idx < MB * CB * 256 && m < M && ch < p.nc) {
             int32_t v[NG];
             float dq[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const int o = (mb * NG + g) * 256 + r * 16 + c;
+                const int o = ((mb * CB + cb) * NG + g) * 256 + r * 16 + c;
                 int32_t sum = 0;
                 for (int w = 0; w < active; ++w) sum += part[w * PART + o];
                 v[g] = sum - sq_e[e][g];
                 dq[g] = __builtin_amdgcn_rcpf(sc_e[e][g] * sw[g]);
             }
-            epilogue_vals<EPI, NG, true>(p, m, n0 + c, v, dq, pre[e]);
+            epilogue_vals<EPI, NG, true>(p, m, ch, v, dq, pre[e]);
         }
     }
 }
@@ -733,34 +749,34 @@ static void run_gemm(const ContractArgs &a, hipStream_t st) {
     tgemm_kernel<NG, JN, SH, EPI><<<(unsigned)(tiles_m * tiles_n), 256, 0, st>>>(a, tiles_n);
 }
 
-template <int NG, int MB, bool SH, int EPI, int WPL, typename RT>
+template <int NG, int MB, bool SH, int EPI, int WPL, typename RT, int CB>
 static void run_gemv_mb(const ContractArgs &a, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 4 * WPL - 1) / (4 * WPL);
-    // per-wave partial sums take MB*NG KB of LDS per wave: at most 64 KB in all
-    constexpr int kMaxWaves = 64 / (MB * NG) < 16 ? 64 / (MB * NG) : 16;
-    static_assert(kMaxWaves >= MB, "the epilogue needs a wave per row block");
+    // per-wave partial sums take MB*CB*NG KB of LDS per wave: at most 64 KB in all
+    constexpr int kMaxWaves = 64 / (MB * CB * NG) < 16 ? 64 / (MB * CB * NG) : 16;
+    static_assert(kMaxWaves >= MB * CB, "the epilogue needs a wave per row and channel block");
     int waves = nslices < kMaxWaves ? nslices : kMaxWaves;
-    if (waves < MB) waves = MB;  // the epilogue covers MB*256 outputs with at most 4 per thread
-    const unsigned grid = (unsigned)((a.nc + 15) / 16);
-    const size_t lds = (size_t)waves * MB * NG * 256 * sizeof(int32_t);
-    const int ept = (MB * 256 + waves * 64 - 1) / (waves * 64);
+    if (waves < MB * CB) waves = MB * CB;  // the epilogue covers MB*CB*256 outputs with at most 4 per thread
+    const unsigned grid = (unsigned)((a.nc + 16 * CB - 1) / (16 * CB));
+    const size_t lds = (size_t)waves * MB * CB * NG * 256 * sizeof(int32_t);
+    const int ept = (MB * CB * 256 + waves * 64 - 1) / (waves * 64);
     // up to two whole slices per wave: both loaded before the MFMAs (one round trip)
-    const bool two = MB <= 2 && nslices > waves && nslices <= 2 * waves && kw % (4 * WPL) == 0;
-    if constexpr (MB <= 2) {
+    const bool two = MB * CB <= 2 && nslices > waves && nslices <= 2 * waves && kw % (4 * WPL) == 0;
+    if constexpr (MB * CB <= 2) {
         if (two) {
             switch (ept) {
-                case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1, 2><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-                default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2, 2><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+                case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1, 2, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+                default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2, 2, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
             }
             return;
         }
     }
     switch (ept) {
-        case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        case 2: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        case 3: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 3, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 4, 1><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 2: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 3: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 3, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 4, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
     }
 }
 
@@ -773,14 +789,40 @@ static void run_gemm_dma(const ContractArgs &a, hipStream_t st) {
     tgemm_dma_kernel<NG, JN, EPI><<<(unsigned)(tiles_m * tiles_n), 256, 0, st>>>(a, tiles_n);
 }
 
+// Channel blocks per workgroup for one row block: the most (1, 2 or 4, with
+// ng * cb <= 4) that still leaves kGemvMinGroups workgroups; fewer, wider
+// workgroups read the codes less often but leave the latency-bound small
+// shapes with too few CUs pulling weights (measured on MI355X: 2048 outputs
+// keep 16-channel workgroups, 5632 x 2 take two blocks, 11264 x 1 four).
+constexpr int kGemvMinGroups = 160;
+static int gemv_channel_blocks(int nc, int ng) {
+    int cb = 1;
+    for (int c = 2; c <= 4; c *= 2)
+        if (ng * c <= 4 && (nc + 16 * c - 1) / (16 * c) >= kGemvMinGroups) cb = c;
+    return cb;
+}
+
 template <int NG, bool SH, int EPI, typename RT>
 static void run_gemv_t(const ContractArgs &a, hipStream_t st) {
     // 4 words (64 k) per lane per slice: measured fastest at the 1.3B decode shapes
+    // one row block (b <= 16): CB channel blocks per workgroup share each
+    // activation fragment (the codes of all rows are read once per workgroup,
+    // 4x the bytes of a 16-channel block of weights)
     switch ((int)((a.m + 15) / 16)) {
-        case 1: run_gemv_mb<NG, 1, SH, EPI, 4, RT>(a, st); break;
-        case 2: run_gemv_mb<NG, 2, SH, EPI, 4, RT>(a, st); break;
-        case 3: run_gemv_mb<NG, 3, SH, EPI, 4, RT>(a, st); break;
-        default: run_gemv_mb<NG, 4, SH, EPI, 4, RT>(a, st); break;
+        case 1:
+            switch (gemv_channel_blocks(a.nc, NG)) {
+                case 4:
+                    if constexpr (NG == 1) { run_gemv_mb<NG, 1, SH, EPI, 4, RT, 4>(a, st); break; }
+                    [[fallthrough]];
+                case 2:
+                    if constexpr (NG <= 2) { run_gemv_mb<NG, 1, SH, EPI, 4, RT, 2>(a, st); break; }
+                    [[fallthrough]];
+                default: run_gemv_mb<NG, 1, SH, EPI, 4, RT, 1>(a, st); break;
+            }
+            break;
+        case 2: run_gemv_mb<NG, 2, SH, EPI, 4, RT, 1>(a, st); break;
+        case 3: run_gemv_mb<NG, 3, SH, EPI, 4, RT, 1>(a, st); break;
+        default: run_gemv_mb<NG, 4, SH, EPI, 4, RT, 1>(a, st); break;
     }
 }
 
