@@ -571,8 +571,15 @@ __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p,
 // MFMA, so a GEMV costs about one memory round trip. Wave partial sums are
 // combined with LDS integer atomics (exact, order-free). RT is the element
 // type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
+// Workgroup size limit of a GEMV variant: the ones with two or more row blocks
+// or per-group activation codes and several groups hold more registers than a
+// 1024-thread workgroup leaves a wave (128), so they run 512 threads (256).
+template <int NG, int MB, bool SHARED_A>
+constexpr int gemv_max_threads() { return NG >= 2 && (MB >= 2 || !SHARED_A) ? 512 : 1024; }
+
 template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT, int EPT, int SPW, int CB>
-__global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const int nslices) {
+__global__ __launch_bounds__((gemv_max_threads<NG, MB, SHARED_A>())) void tgemv_kernel(const ContractArgs p,
+                                                                                    const int nslices) {
     constexpr int NA = SHARED_A ? 1 : NG;
     constexpr int PART = MB * CB * NG * 256;  // one wave's partial sums
     extern __shared__ int32_t part[];         // [waves][PART]
@@ -681,12 +688,38 @@ __global__ __launch_bounds__(1024) void tgemv_kernel(const ContractArgs p, const
         load_slice(min(wave + nw, nslices - 1), bw1, a1, true);
         mma_slice(bw0, a0);
         if (wave + nw < nslices) mma_slice(bw1, a1);
-    } else {
-        for (int sl = wave; sl < nslices; sl += nw) {
+    } else if (nslices <= nw) {
+        if (wave < nslices) {  // one slice per wave
+            uint32_t bw[CB][NG][WPL];
+            i32x4 a[MB][NA][WPL];
+            load_slice(wave, bw, a, whole);
+            mma_slice(bw, a);
+        }
+    } else if constexpr (MB > 2 || EPT > 2) {
+        for (int sl = wave; sl < nslices; sl += nw) {  // no registers for a second set
             uint32_t bw[CB][NG][WPL];
             i32x4 a[MB][NA][WPL];
             load_slice(sl, bw, a, whole);
             mma_slice(bw, a);
+        }
+    } else if (wave < nslices) {
+        // more slices: two register sets, the next slice's loads in flight
+        // during the current one's MFMAs (the last loads repeat the final
+        // slice and go unused)
+        uint32_t bw0[CB][NG][WPL], bw1[CB][NG][WPL];
+        i32x4 a0[MB][NA][WPL], a1[MB][NA][WPL];
+        const int last = nslices - 1;
+        int sl = wave;
+        load_slice(sl, bw0, a0, whole);
+        while (true) {
+            load_slice(min(sl + nw, last), bw1, a1, whole);
+            mma_slice(bw0, a0);
+            sl += nw;
+            if (sl >= nslices) break;
+            load_slice(min(sl + nw, last), bw0, a0, whole);
+            mma_slice(bw1, a1);
+            sl += nw;
+            if (sl >= nslices) break;
         }
     }
     // each wave's partial sums into its own LDS slot; summed below in wave order
@@ -754,7 +787,8 @@ static void run_gemv_mb(const ContractArgs &a, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 4 * WPL - 1) / (4 * WPL);
     // per-wave partial sums take MB*CB*NG KB of LDS per wave: at most 64 KB in all
-    constexpr int kMaxWaves = 64 / (MB * CB * NG) < 16 ? 64 / (MB * CB * NG) : 16;
+    constexpr int kThreadWaves = gemv_max_threads<NG, MB, SH>() / 64;
+    constexpr int kMaxWaves = 64 / (MB * CB * NG) < kThreadWaves ? 64 / (MB * CB * NG) : kThreadWaves;
     static_assert(kMaxWaves >= MB * CB, "the epilogue needs a wave per row and channel block");
     int waves = nslices < kMaxWaves ? nslices : kMaxWaves;
     if (waves < MB * CB) waves = MB * CB;  // the epilogue covers MB*CB*256 outputs with at most 4 per thread
@@ -795,8 +829,9 @@ static void run_gemm_dma(const ContractArgs &a, hipStream_t st) {
 // shapes with too few CUs pulling weights (measured on MI355X: 2048 outputs
 // keep 16-channel workgroups, 5632 x 2 take two blocks, 11264 x 1 four).
 constexpr int kGemvMinGroups = 160;
-static int gemv_channel_blocks(int nc, int ng) {
+static int gemv_channel_blocks(int nc, int ng, int k) {
     int cb = 1;
+    if (k < 1024) return cb;  // fewer than 4 slices: too few waves for the wider epilogue
     for (int c = 2; c <= 4; c *= 2)
         if (ng * c <= 4 && (nc + 16 * c - 1) / (16 * c) >= kGemvMinGroups) cb = c;
     return cb;
@@ -810,7 +845,7 @@ static void run_gemv_t(const ContractArgs &a, hipStream_t st) {
     // 4x the bytes of a 16-channel block of weights)
     switch ((int)((a.m + 15) / 16)) {
         case 1:
-            switch (gemv_channel_blocks(a.nc, NG)) {
+            switch (gemv_channel_blocks(a.nc, NG, a.k)) {
                 case 4:
                     if constexpr (NG == 1) { run_gemv_mb<NG, 1, SH, EPI, 4, RT, 4>(a, st); break; }
                     [[fallthrough]];
