@@ -227,7 +227,7 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
  * mmf_set_decode_kernel -- which implementation mmf_layer_decode_step uses,
  * process-wide: 0 = the fastest implementation measured on MI355X (default;
  * at present the separate kernels for every shape: at the 1.3B shape they
- * take 29 / 35 us per layer at batch 1 / 16 in a HIP graph, the four fused
+ * take 29 / 34 us per layer at batch 1 / 16 in a HIP graph, the four fused
  * kernels 34 / 46 (a hand-off across XCDs within a launch costs about what a
  * kernel boundary does), and the one-XCD kernel 45 / 46, held to one XCD's
  * share of HBM bandwidth);
