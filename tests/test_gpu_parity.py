@@ -51,6 +51,14 @@ BITLINEAR_CASES = [
     (200, 1024, 200, "bf16", True),
     (300, 2816, 96, "f32", False),
     (513, 2048, 1111, "bf16", False),
+    # decode GEMV paths: two slices per wave (21 slices over 16 waves), two and four
+    # channel blocks per workgroup (ragged last block), the double-buffered slice loop
+    # (64 slices) and a K that is no whole number of slices (33 slices, last one partial)
+    (3, 5376, 300, "bf16", True),
+    (16, 2048, 5136, "f32", False),
+    (8, 2048, 10250, "bf16", False),
+    (16, 16384, 64, "bf16", False),
+    (2, 8208, 100, "f32", True),
 ]
 
 
