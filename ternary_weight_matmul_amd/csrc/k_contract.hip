@@ -563,14 +563,18 @@ __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p,
 // ----------------------------------------------------------------------------
 // Decode: m <= 64 rows, latency-bound weight streaming
 // ----------------------------------------------------------------------------
-// One workgroup per 16 output channels (x NG groups). K is cut into slices of
-// 4*WPL words; one wave per slice (up to 16 waves; further slices loop). A lane
-// (column lc, word group lg) owns WPL consecutive words of its column in the
-// slice and issues every load of the slice -- weights as 16-byte runs,
-// activation codes of its row block as 16-byte chunks -- before its first
-// MFMA, so a GEMV costs about one memory round trip. Wave partial sums are
-// combined with LDS integer atomics (exact, order-free). RT is the element
-// type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
+// One workgroup per CB blocks of 16 output channels (x NG groups). K is cut
+// into slices of 4*WPL words, dealt to up to 16 waves. A lane (column lc,
+// word group lg) owns WPL consecutive words of its column in a slice and
+// issues every load of the slice -- weights as 16-byte runs, activation codes
+// of its row block as 16-byte chunks -- before its first MFMA: with up to two
+// slices per wave (SPW = 2) both slices' loads go first, so a GEMV costs about
+// one memory round trip; with more, two register sets alternate. The codes
+// of a slice are 4x the bytes of one 16-channel block of weights, so the CB
+// blocks share each activation fragment. Each wave's partial sums go to its
+// own LDS slot and are summed in wave order (exact integers). RT is the
+// element type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
+//
 // Workgroup size limit of a GEMV variant: the ones with two or more row blocks
 // or per-group activation codes and several groups hold more registers than a
 // 1024-thread workgroup leaves a wave (128), so they run 512 threads (256).
