@@ -189,16 +189,24 @@ def kernel_files(kernel: str):
     return KERNEL_SOURCES.get("scan" if base.startswith("scan") else base)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed (what the compiler sees)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(files=None) -> str:
-    """sha256 of kernel sources (the given files of csrc/, else all of them), to tell whether
-    stored counter figures still apply to the code that runs."""
+    """sha256 of kernel sources (the given files of csrc/, else all of them), comments and
+    layout left out, to tell whether stored counter figures still apply to the code that runs."""
     import hashlib
     hsh = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_matmul_amd", "csrc")
     names = sorted(files) if files else sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp")))
     for name in names:
-        with open(os.path.join(csrc, name), "rb") as f:
-            hsh.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            hsh.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return hsh.hexdigest()[:16]
 
 

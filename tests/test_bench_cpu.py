@@ -89,3 +89,10 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_digest_ignores_comments_and_layout():
+    a = "int f(int x) { // doubles x\n  return 2 * x; /* plain */ }\n"
+    b = "int f(int x) {\n    return 2 * x;\n}  // edited note\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(a.replace("2 * x", "3 * x"))
