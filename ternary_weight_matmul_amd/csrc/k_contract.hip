@@ -575,15 +575,19 @@ __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p,
 // own LDS slot and are summed in wave order (exact integers). RT is the
 // element type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
 //
-// Workgroup size limit of a GEMV variant: the ones with two or more row blocks
-// or per-group activation codes and several groups hold more registers than a
-// 1024-thread workgroup leaves a wave (128), so they run 512 threads (256).
-template <int NG, int MB, bool SHARED_A>
-constexpr int gemv_max_threads() { return NG >= 2 && (MB >= 2 || !SHARED_A) ? 512 : 1024; }
+// Workgroup size limit of a GEMV variant: the ones with per-group activation
+// codes and several groups hold more registers than a 1024-thread workgroup
+// leaves a wave (128), so they run 512 threads (256).
+template <int NG, bool SHARED_A>
+constexpr int gemv_max_threads() { return NG >= 2 && !SHARED_A ? 512 : 1024; }
 
-template <int NG, int MB, bool SHARED_A, int EPI, int WPL, typename RT, int EPT, int SPW, int CB>
-__global__ __launch_bounds__((gemv_max_threads<NG, MB, SHARED_A>())) void tgemv_kernel(const ContractArgs p,
-                                                                                    const int nslices) {
+template <int NG, bool SHARED_A, int EPI, int WPL, typename RT, int EPT, int SPW, int CB>
+__global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kernel(const ContractArgs p,
+                                                                                const int nslices) {
+    // one block of 16 rows per workgroup (grid.y covers the row blocks): with
+    // more rows per workgroup each one reads all their codes and fewer
+    // workgroups pull weights (measured 1.5x slower at 64 rows)
+    constexpr int MB = 1;
     constexpr int NA = SHARED_A ? 1 : NG;
     constexpr int PART = MB * CB * NG * 256;  // one wave's partial sums
     extern __shared__ int32_t part[];         // [waves][PART]
@@ -592,6 +596,7 @@ __global__ __launch_bounds__((gemv_max_threads<NG, MB, SHARED_A>())) void tgemv_
     const int n0 = blockIdx.x * 16 * CB;
     const int K = p.k, KW = K >> 4;
     const int64_t M = p.m;
+    const int64_t row0 = (int64_t)blockIdx.y * 16 * MB;  // first row of this workgroup's row blocks
     int gn[CB];  // columns past nc load a valid row; never stored
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) gn[cb] = min(n0 + cb * 16 + lc, p.nc - 1);
@@ -611,7 +616,7 @@ __global__ __launch_bounds__((gemv_max_threads<NG, MB, SHARED_A>())) void tgemv_
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const int idx = tid + e * blockDim.x;
-        const int64_t m = (int64_t)(idx / (256 * CB)) * 16 + ((idx >> 4) & 15);
+        const int64_t m = row0 + (int64_t)(idx / (256 * CB)) * 16 + ((idx >> 4) & 15);
         const int64_t mc = m < M ? m : M - 1;
         const int c = n0 + ((idx >> 8) % CB) * 16 + (idx & 15);
         pre[e] = PRE ? load_act(pre_src, mc * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
@@ -659,7 +664,7 @@ __global__ __launch_bounds__((gemv_max_threads<NG, MB, SHARED_A>())) void tgemv_
             }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int64_t row = min((int64_t)(mb * 16 + lc), M - 1);
+            const int64_t row = min(row0 + mb * 16 + lc, M - 1);
 #pragma unroll
             for (int q = 0; q < NA; ++q) {
                 const i32x4 *src = reinterpret_cast<const i32x4 *>(p.A[q] + row * K);
@@ -746,7 +751,7 @@ __global__ __launch_bounds__((gemv_max_threads<NG, MB, SHARED_A>())) void tgemv_
     for (int e = 0; e < EPT; ++e) {
         const int idx = tid + e * blockDim.x;
         const int mb = idx / (256 * CB), cb = (idx >> 8) % CB, r = (idx >> 4) & 15, c = idx & 15;
-        const int64_t m = mb * 16 + r;
+        const int64_t m = row0 + mb * 16 + r;
         const int ch = n0 + cb * 16 + c;
         if (idx < MB * CB * 256 && m < M && ch < p.nc) {
             int32_t v[NG];
@@ -786,17 +791,19 @@ static void run_gemm(const ContractArgs &a, hipStream_t st) {
     tgemm_kernel<NG, JN, SH, EPI><<<(unsigned)(tiles_m * tiles_n), 256, 0, st>>>(a, tiles_n);
 }
 
-template <int NG, int MB, bool SH, int EPI, int WPL, typename RT, int CB>
-static void run_gemv_mb(const ContractArgs &a, hipStream_t st) {
+template <int NG, bool SH, int EPI, int WPL, typename RT, int CB>
+static void run_gemv_cb(const ContractArgs &a, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 4 * WPL - 1) / (4 * WPL);
+    constexpr int MB = 1;  // row blocks per workgroup
     // per-wave partial sums take MB*CB*NG KB of LDS per wave: at most 64 KB in all
-    constexpr int kThreadWaves = gemv_max_threads<NG, MB, SH>() / 64;
+    constexpr int kThreadWaves = gemv_max_threads<NG, SH>() / 64;
     constexpr int kMaxWaves = 64 / (MB * CB * NG) < kThreadWaves ? 64 / (MB * CB * NG) : kThreadWaves;
     static_assert(kMaxWaves >= MB * CB, "the epilogue needs a wave per row and channel block");
     int waves = nslices < kMaxWaves ? nslices : kMaxWaves;
     if (waves < MB * CB) waves = MB * CB;  // the epilogue covers MB*CB*256 outputs with at most 4 per thread
-    const unsigned grid = (unsigned)((a.nc + 16 * CB - 1) / (16 * CB));
+    // x: channel blocks; y: groups of MB row blocks (rows past m are clamped, never stored)
+    const dim3 grid((unsigned)((a.nc + 16 * CB - 1) / (16 * CB)), (unsigned)((a.m + 16 * MB - 1) / (16 * MB)));
     const size_t lds = (size_t)waves * MB * CB * NG * 256 * sizeof(int32_t);
     const int ept = (MB * CB * 256 + waves * 64 - 1) / (waves * 64);
     // up to two whole slices per wave: both loaded before the MFMAs (one round trip)
@@ -804,17 +811,17 @@ static void run_gemv_mb(const ContractArgs &a, hipStream_t st) {
     if constexpr (MB * CB <= 2) {
         if (two) {
             switch (ept) {
-                case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1, 2, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-                default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2, 2, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+                case 1: tgemv_kernel<NG, SH, EPI, WPL, RT, 1, 2, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+                default: tgemv_kernel<NG, SH, EPI, WPL, RT, 2, 2, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
             }
             return;
         }
     }
     switch (ept) {
-        case 1: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 1, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        case 2: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 2, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        case 3: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 3, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        default: tgemv_kernel<NG, MB, SH, EPI, WPL, RT, 4, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 1: tgemv_kernel<NG, SH, EPI, WPL, RT, 1, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 2: tgemv_kernel<NG, SH, EPI, WPL, RT, 2, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 3: tgemv_kernel<NG, SH, EPI, WPL, RT, 3, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        default: tgemv_kernel<NG, SH, EPI, WPL, RT, 4, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
     }
 }
 
@@ -833,35 +840,28 @@ static void run_gemm_dma(const ContractArgs &a, hipStream_t st) {
 // shapes with too few CUs pulling weights (measured on MI355X: 2048 outputs
 // keep 16-channel workgroups, 5632 x 2 take two blocks, 11264 x 1 four).
 constexpr int kGemvMinGroups = 160;
-static int gemv_channel_blocks(int nc, int ng, int k) {
+static int gemv_channel_blocks(int nc, int ng, int k, int row_blocks) {
     int cb = 1;
     if (k < 1024) return cb;  // fewer than 4 slices: too few waves for the wider epilogue
     for (int c = 2; c <= 4; c *= 2)
-        if (ng * c <= 4 && (nc + 16 * c - 1) / (16 * c) >= kGemvMinGroups) cb = c;
+        if (ng * c <= 4 && (nc + 16 * c - 1) / (16 * c) * row_blocks >= kGemvMinGroups) cb = c;
     return cb;
 }
 
 template <int NG, bool SH, int EPI, typename RT>
 static void run_gemv_t(const ContractArgs &a, hipStream_t st) {
     // 4 words (64 k) per lane per slice: measured fastest at the 1.3B decode shapes
-    // one row block (b <= 16): CB channel blocks per workgroup share each
-    // activation fragment (the codes of all rows are read once per workgroup,
+    // one workgroup per 16-row block and CB channel blocks: the channel blocks
+    // share each activation fragment (a workgroup reads its rows' codes once,
     // 4x the bytes of a 16-channel block of weights)
-    switch ((int)((a.m + 15) / 16)) {
-        case 1:
-            switch (gemv_channel_blocks(a.nc, NG, a.k)) {
-                case 4:
-                    if constexpr (NG == 1) { run_gemv_mb<NG, 1, SH, EPI, 4, RT, 4>(a, st); break; }
-                    [[fallthrough]];
-                case 2:
-                    if constexpr (NG <= 2) { run_gemv_mb<NG, 1, SH, EPI, 4, RT, 2>(a, st); break; }
-                    [[fallthrough]];
-                default: run_gemv_mb<NG, 1, SH, EPI, 4, RT, 1>(a, st); break;
-            }
-            break;
-        case 2: run_gemv_mb<NG, 2, SH, EPI, 4, RT, 1>(a, st); break;
-        case 3: run_gemv_mb<NG, 3, SH, EPI, 4, RT, 1>(a, st); break;
-        default: run_gemv_mb<NG, 4, SH, EPI, 4, RT, 1>(a, st); break;
+    switch (gemv_channel_blocks(a.nc, NG, a.k, (int)((a.m + 15) / 16))) {
+        case 4:
+            if constexpr (NG == 1) { run_gemv_cb<NG, SH, EPI, 4, RT, 4>(a, st); break; }
+            [[fallthrough]];
+        case 2:
+            if constexpr (NG <= 2) { run_gemv_cb<NG, SH, EPI, 4, RT, 2>(a, st); break; }
+            [[fallthrough]];
+        default: run_gemv_cb<NG, SH, EPI, 4, RT, 1>(a, st); break;
     }
 }
 
