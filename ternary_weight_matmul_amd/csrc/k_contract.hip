@@ -8,7 +8,8 @@
 // in registers with one shift and one mask per 4 values: a word decodes
 // straight into the 16-byte int8 operand of one MFMA lane. The int8 MFMA
 // computes sum c*q; sum t*q = sum c*q - sum q is exact (|acc| < 2^24), with
-// sum q a by-product of the activation quantiser.
+// sum q a by-product of the activation quantiser (prefill) or of one more MFMA
+// against an all-ones operand (decode).
 //
 // Prefill (m > 64): 128 x (NG * 64 * JN) output tiles (JN = 4, 2, 1 for one,
 // two, three groups), four waves of 64 x (NG * 32 * JN), v_mfma_i32_32x32x32_i8,
@@ -17,8 +18,9 @@
 // a 48-byte row stride: both conflict-free for 16-lane groups). Tiles are
 // assigned XCD-major, and grouped eight row strips at a time, so that the
 // workgroups of one XCD share activation strips and weight tiles in its L2.
-// Decode (m <= 64): one workgroup per 16 output channels, four waves splitting
-// K, v_mfma_i32_16x16x64_i8 per 16 rows of m, partial sums reduced in LDS.
+// Decode (m <= 64): one workgroup per 16-row block and 16 to 64 output
+// channels, up to 16 waves splitting K, v_mfma_i32_16x16x64_i8, partial sums
+// reduced in LDS.
 //
 // NG groups of output channels share an output tile so that the epilogue sees
 // the matching channels of several projections in one lane: i/f/g for the
@@ -571,8 +573,11 @@ __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p,
 // slices per wave (SPW = 2) both slices' loads go first, so a GEMV costs about
 // one memory round trip; with more, two register sets alternate. The codes
 // of a slice are 4x the bytes of one 16-channel block of weights, so the CB
-// blocks share each activation fragment. Each wave's partial sums go to its
-// own LDS slot and are summed in wave order (exact integers). RT is the
+// blocks share each activation fragment. The sum of the codes of a row comes
+// from one more MFMA per word against an all-ones operand (sum q in the same
+// lane layout as sum c*q), so each wave stores sum (c - 1) q = sum t*q of its
+// slices and the quantiser need not form sum q. Each wave's partial sums go to
+// its own LDS slot and are summed in wave order (exact integers). RT is the
 // element type of the residual (EPI_RESID) or state (EPI_GATES_STEP) operand.
 //
 // Workgroup size limit of a GEMV variant: the ones with per-group activation
@@ -581,9 +586,14 @@ __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p,
 template <int NG, bool SHARED_A>
 constexpr int gemv_max_threads() { return NG >= 2 && !SHARED_A ? 512 : 1024; }
 
+// Three or four outputs per thread mean fewer than 2 CB waves (at most 448
+// threads): such launches get the registers of a 512-thread workgroup.
+template <int NG, bool SHARED_A, int EPT>
+constexpr int gemv_bound() { return EPT >= 3 ? 512 : gemv_max_threads<NG, SHARED_A>(); }
+
 template <int NG, bool SHARED_A, int EPI, int WPL, typename RT, int EPT, int SPW, int CB>
-__global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kernel(const ContractArgs p,
-                                                                                const int nslices) {
+__global__ __launch_bounds__((gemv_bound<NG, SHARED_A, EPT>())) void tgemv_kernel(const ContractArgs p,
+                                                                               const int nslices) {
     // one block of 16 rows per workgroup (grid.y covers the row blocks): with
     // more rows per workgroup each one reads all their codes and fewer
     // workgroups pull weights (measured 1.5x slower at 64 rows)
@@ -600,8 +610,8 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
     int gn[CB];  // columns past nc load a valid row; never stored
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) gn[cb] = min(n0 + cb * 16 + lc, p.nc - 1);
-    // weight scales, the quantiser's per-row scales and sums and the epilogue
-    // operands (residual / old state) do not depend on the contraction: load
+    // weight scales, the quantiser's per-row scales and the epilogue operands
+    // (residual / old state) do not depend on the contraction: load
     // them before it, unconditionally (clamped to a valid element; the values
     // of outputs that are not stored go unused) so that no wait for them comes
     // before the contraction's own loads. Output idx of the workgroup: row block
@@ -611,7 +621,6 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
     for (int g = 0; g < NG; ++g) mu_v[g] = *p.mu[g];
     constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
     float pre[EPT], sc_e[EPT][NG];
-    int32_t sq_e[EPT][NG];
     const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -621,23 +630,24 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
         const int c = n0 + ((idx >> 8) % CB) * 16 + (idx & 15);
         pre[e] = PRE ? load_act(pre_src, mc * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            sq_e[e][g] = p.sumq[g][mc];
-            sc_e[e][g] = p.s[g][mc];
-        }
+        for (int g = 0; g < NG; ++g) sc_e[e][g] = p.s[g][mc];
     }
 
-    i32x4 acc[MB][CB][NG];
+    i32x4 acc[MB][CB][NG], accq[MB][NA];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int g = 0; g < NG; ++g) acc[mb][cb][g] = i32x4{};
+#pragma unroll
+        for (int q = 0; q < NA; ++q) accq[mb][q] = i32x4{};
+    }
 
     // Every load of a slice is unconditional: words past the row end are
-    // clamped and then zeroed (offset code 0 adds nothing to sum c*q), rows
-    // past m are clamped (their sums are never stored). An activation fragment
+    // clamped and their weights zeroed (offset code 0 adds nothing to sum c*q;
+    // the all-ones operand is zeroed for them too), rows past m are clamped
+    // (their sums are never stored). An activation fragment
     // serves the CB channel blocks and NG groups of the workgroup.
     const bool whole = (KW % (4 * WPL)) == 0;
     auto load_slice = [&](int sl, uint32_t (&bw)[CB][NG][WPL], i32x4 (&a)[MB][NA][WPL], bool is_whole) {
@@ -673,9 +683,11 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
             }
         }
     };
-    auto mma_slice = [&](const uint32_t (&bw)[CB][NG][WPL], const i32x4 (&a)[MB][NA][WPL]) {
+    auto mma_slice = [&](const uint32_t (&bw)[CB][NG][WPL], const i32x4 (&a)[MB][NA][WPL], int sl) {
 #pragma unroll
-        for (int j = 0; j < WPL; ++j)
+        for (int j = 0; j < WPL; ++j) {
+            const int32_t o = sl * 4 * WPL + lg * WPL + j < KW ? 0x01010101 : 0;
+            const i32x4 ones = {o, o, o, o};
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -686,6 +698,12 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
                         acc[mb][cb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][SHARED_A ? 0 : g][j], b,
                                                                                acc[mb][cb][g], 0, 0, 0);
                 }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int q = 0; q < NA; ++q)
+                    accq[mb][q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][q][j], ones, accq[mb][q], 0, 0, 0);
+        }
     };
     if constexpr (SPW == 2) {
         // two slices per wave at most (whole rows): both slices' loads are issued
@@ -695,21 +713,23 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
         i32x4 a0[MB][NA][WPL], a1[MB][NA][WPL];
         load_slice(wave, bw0, a0, true);
         load_slice(min(wave + nw, nslices - 1), bw1, a1, true);
-        mma_slice(bw0, a0);
-        if (wave + nw < nslices) mma_slice(bw1, a1);
+        mma_slice(bw0, a0, wave);
+        if (wave + nw < nslices) mma_slice(bw1, a1, wave + nw);
     } else if (nslices <= nw) {
         if (wave < nslices) {  // one slice per wave
             uint32_t bw[CB][NG][WPL];
             i32x4 a[MB][NA][WPL];
             load_slice(wave, bw, a, whole);
-            mma_slice(bw, a);
+            mma_slice(bw, a, wave);
         }
-    } else if constexpr (MB > 2 || EPT > 2) {
-        for (int sl = wave; sl < nslices; sl += nw) {  // no registers for a second set
+    } else if constexpr (MB > 2 || EPT > 2 || (EPT == 2 && CB * NG >= 4)) {
+        // no registers for a second set (with two outputs per thread and four
+        // channel blocks a launch has fewer than 16 slices: one per wave, above)
+        for (int sl = wave; sl < nslices; sl += nw) {
             uint32_t bw[CB][NG][WPL];
             i32x4 a[MB][NA][WPL];
             load_slice(sl, bw, a, whole);
-            mma_slice(bw, a);
+            mma_slice(bw, a, sl);
         }
     } else if (wave < nslices) {
         // more slices: two register sets, the next slice's loads in flight
@@ -722,16 +742,16 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
         load_slice(sl, bw0, a0, whole);
         while (true) {
             load_slice(min(sl + nw, last), bw1, a1, whole);
-            mma_slice(bw0, a0);
+            mma_slice(bw0, a0, sl);
             sl += nw;
             if (sl >= nslices) break;
             load_slice(min(sl + nw, last), bw0, a0, whole);
-            mma_slice(bw1, a1);
+            mma_slice(bw1, a1, sl);
             sl += nw;
             if (sl >= nslices) break;
         }
     }
-    // each wave's partial sums into its own LDS slot; summed below in wave order
+    // each wave's partial sums of t*q into its own LDS slot; summed below in wave order
     int32_t *mine = part + wave * PART;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -741,7 +761,8 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
             for (int g = 0; g < NG; ++g)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    mine[((mb * CB + cb) * NG + g) * 256 + (4 * lg + i) * 16 + lc] = acc[mb][cb][g][i];
+                    mine[((mb * CB + cb) * NG + g) * 256 + (4 * lg + i) * 16 + lc] =
+                        acc[mb][cb][g][i] - accq[mb][SHARED_A ? 0 : g][i];
     __syncthreads();
     float sw[NG];
 #pragma unroll
@@ -761,7 +782,7 @@ __global__ __launch_bounds__((gemv_max_threads<NG, SHARED_A>())) void tgemv_kern
                 const int o = ((mb * CB + cb) * NG + g) * 256 + r * 16 + c;
                 int32_t sum = 0;
                 for (int w = 0; w < active; ++w) sum += part[w * PART + o];
-                v[g] = sum - sq_e[e][g];
+                v[g] = sum;
                 dq[g] = __builtin_amdgcn_rcpf(sc_e[e][g] * sw[g]);
             }
             epilogue_vals<EPI, NG, true>(p, m, ch, v, dq, pre[e]);
@@ -878,6 +899,7 @@ static void run_gemv(const ContractArgs &a, hipStream_t st) {
 }
 
 static bool use_gemv(int64_t m) { return m <= 64; }
+bool contract_sums_codes(int64_t m) { return use_gemv(m); }
 // the LDS-DMA kernel needs whole 128-byte K steps and one activation tensor
 static bool dma_ok(const ContractArgs &a, bool shared_a) { return shared_a && (a.k % kBK) == 0; }
 

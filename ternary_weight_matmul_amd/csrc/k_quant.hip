@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const T *__restrict__ x
     tot = wave_sum_int(tot);
     if (lane == 0) {
         s[row] = sc;
-        sumq[row] = tot;
+        if (sumq) sumq[row] = tot;
     }
 }
 
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void norm_quant_long_kernel(const T *__restric
     tot = wave_sum_int(tot);
     if (lane == 0) {
         s[row] = sc;
-        sumq[row] = tot;
+        if (sumq) sumq[row] = tot;
     }
 }
 
@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void norm_quant_row_kernel(const T *__restrict
                                                              int32_t *__restrict__ sumq) {
     __shared__ RowQuantLds sh;
     const int64_t row = blockIdx.x;
-    row_quant<T, NV, false>(x + row * (int64_t)k, k, gain, eps, q + row * (int64_t)k, s + row, sumq + row, sh);
+    row_quant<T, NV, false>(x + row * (int64_t)k, k, gain, eps, q + row * (int64_t)k, s + row,
+                            sumq ? sumq + row : nullptr, sh);
 }
 
 constexpr int kFewRows = 2048;  // below this many rows a row gets a whole workgroup
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(256) void gnorm_quant_kernel(const float *__restric
     tot = wave_sum_int(tot);
     if (lane == 0) {
         s[row] = sc;
-        sumq[row] = tot;
+        if (sumq) sumq[row] = tot;
     }
 }
 
@@ -325,7 +326,8 @@ __global__ __launch_bounds__(256) void gnorm_quant_row_kernel(const float *__res
     __shared__ RowQuantLds sh;
     const int64_t row = blockIdx.x;
     row_gnorm_quant<TG, NV, false>(h + row * (int64_t)d, g + row * (int64_t)d, d, gnw, ogain, eps,
-                                   q + row * (int64_t)d, s + row, sumq + row, u_out ? u_out + row * (int64_t)d : nullptr,
+                                   q + row * (int64_t)d, s + row, sumq ? sumq + row : nullptr,
+                                   u_out ? u_out + row * (int64_t)d : nullptr,
                                    sh);
 }
 

@@ -37,7 +37,7 @@ struct ContractArgs {
     // per group (i/f/g, or the two halves of gate_proj, or one tensor)
     const int8_t *A[3];      // codes [m][k]
     const float *s[3];       // activation scale per row
-    const int32_t *sumq[3];  // sum of codes per row
+    const int32_t *sumq[3];  // sum of codes per row (read by the prefill kernels only)
     const uint32_t *B[3];    // packed rows [nc][k/16]
     const float *mu[3];      // device scalar per group
     int64_t m;
@@ -94,6 +94,10 @@ hipError_t quant_contract_expired_waits(unsigned *count);
 // Prefill-shaped contraction (int8 MFMA tiles) and decode-shaped one (m <= 64).
 hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a,
                            hipStream_t stream, std::string *path);
+
+// Whether the contraction over m rows forms each row's sum of codes itself
+// (the decode GEMV does); otherwise it reads the quantiser's sumq.
+bool contract_sums_codes(int64_t m);
 
 // Variant name of the kernel launch_contract picks, e.g. "tgemm<gates>".
 std::string contract_variant(int64_t m, int k, EpiKind epi, bool shared_a);

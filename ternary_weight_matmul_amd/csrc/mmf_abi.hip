@@ -81,9 +81,12 @@ hipError_t timed(const std::string &kernel, int64_t m, int n, int k, hipStream_t
     return hipSuccess;
 }
 
+// The quantisers feed a contraction over the same m rows; when that
+// contraction sums the codes itself, the quantiser does not.
 hipError_t t_norm_quant(const void *x, ActType xt, int64_t m, int k, const float *gain, float eps, int8_t *q,
                         float *s, int32_t *sumq, hipStream_t st, std::string *path) {
     if (m <= 0) return hipSuccess;
+    if (contract_sums_codes(m)) sumq = nullptr;
     return timed(xt == ACT_F32 ? "norm_quant<f32>" : "norm_quant<bf16>", m, k, k, st,
                  [&] { return launch_norm_quant(x, xt, m, k, gain, eps, q, s, sumq, st, path); });
 }
@@ -91,6 +94,7 @@ hipError_t t_norm_quant(const void *x, ActType xt, int64_t m, int k, const float
 hipError_t t_gnorm_quant(const float *h, const void *g, ActType gt, int64_t m, int d, const float *gw, const float *og,
                          float eps, int8_t *q, float *s, int32_t *sumq, float *u, hipStream_t st, std::string *path) {
     if (m <= 0) return hipSuccess;
+    if (contract_sums_codes(m)) sumq = nullptr;
     return timed(gt == ACT_F32 ? "gnorm_quant<f32>" : "gnorm_quant<bf16>", m, d, d, st,
                  [&] { return launch_gnorm_quant(h, g, gt, m, d, gw, og, eps, q, s, sumq, u, st, path); });
 }

@@ -12,6 +12,12 @@
 // depend on the caller: the separate decode kernels and the persistent decode
 // step produce the same bits. NT: the row was written by another workgroup of
 // the same launch and is read with non-temporal loads.
+//
+// Without a gain, y = x * r is monotone in |x| (r > 0, round-to-nearest is
+// monotone and symmetric), so max |y| = (max |x|) * r exactly: the sum of
+// squares and max |x| are reduced in the same round. With sumq == nullptr the
+// sum of the codes is not formed (the decode GEMV computes it from the codes
+// itself), which saves the last round.
 #pragma once
 #include "device_common.hpp"
 
@@ -62,6 +68,19 @@ __device__ __forceinline__ float rq_max(float v, float *sh) {
     __syncthreads();
     return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
 }
+// Sum and max in one round (two LDS arrays, one barrier).
+__device__ __forceinline__ void rq_sum_max(double &v, float &mx, double *shd, float *shf) {
+    v = wave_sum(v);
+    mx = wave_max(mx);
+    const int t = threadIdx.x;
+    if (t < 256 && (t & 63) == 0) {
+        shd[t >> 6] = v;
+        shf[t >> 6] = mx;
+    }
+    __syncthreads();
+    v = (shd[0] + shd[1]) + (shd[2] + shd[3]);
+    mx = fmaxf(fmaxf(shf[0], shf[1]), fmaxf(shf[2], shf[3]));
+}
 __device__ __forceinline__ int rq_sum_int(int v, int *sh) {
     v = wave_sum_int(v);
     const int t = threadIdx.x;
@@ -84,12 +103,13 @@ __device__ __forceinline__ void rq_store(uint32_t *p, uint32_t v) {
     else *p = v;
 }
 
-// Codes of the 4-element chunks owned by the thread, the scale s and sum q.
+// Codes of the 4-element chunks owned by the thread, the scale s (from the
+// row's max |y|, already reduced) and, when sumq != nullptr, the sum of codes.
 template <int NV, bool SC1 = false>
-__device__ __forceinline__ void rq_emit(const float (&v)[NV][4], float amax, int nch, int8_t *qr, float *s, int32_t *sumq,
-                                        RowQuantLds &sh) {
+__device__ __forceinline__ void rq_emit(const float (&v)[NV][4], float row_amax, int nch, int8_t *qr, float *s,
+                                        int32_t *sumq, RowQuantLds &sh) {
     const int tid = threadIdx.x;
-    const float sc = quant_scale(rq_max(amax, sh.f));
+    const float sc = quant_scale(row_amax);
     int tot = 0;
     uint32_t *qw = reinterpret_cast<uint32_t *>(qr);
 #pragma unroll
@@ -102,10 +122,10 @@ __device__ __forceinline__ void rq_emit(const float (&v)[NV][4], float amax, int
             rq_store<SC1>(qw + c, pack_codes4(a0, a1, a2, a3));
         }
     }
-    tot = rq_sum_int(tot, sh.i);
+    if (sumq) tot = rq_sum_int(tot, sh.i);
     if (tid == 0) {
         rq_store<SC1>(reinterpret_cast<uint32_t *>(s), __float_as_uint(sc));
-        rq_store<SC1>(reinterpret_cast<uint32_t *>(sumq), (uint32_t)tot);
+        if (sumq) rq_store<SC1>(reinterpret_cast<uint32_t *>(sumq), (uint32_t)tot);
     }
 }
 
@@ -128,23 +148,37 @@ __device__ __forceinline__ void row_quant(const T *xr, int k, const float *gain,
         }
     }
     double ss = 0.0;
+    float xmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; ++j)
         if (tid < 256 && tid + 256 * j < nch)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ss += (double)v[j][e] * (double)v[j][e];
-    const float r = rms_factor(rq_sum(ss, sh.d[0]), k, eps);
-    float amax = 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                ss += (double)v[j][e] * (double)v[j][e];
+                xmax = fmaxf(xmax, fabsf(v[j][e]));
+            }
+    float r, amax;
+    if (!gain) {
+        rq_sum_max(ss, xmax, sh.d[0], sh.f);
+        r = rms_factor(ss, k, eps);
+        amax = __fmul_rn(xmax, r);
+    } else {
+        r = rms_factor(rq_sum(ss, sh.d[0]), k, eps);
+        amax = 0.0f;
+    }
 #pragma unroll
     for (int j = 0; j < NV; ++j)
         if (tid < 256 && tid + 256 * j < nch)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float y = __fmul_rn(v[j][e], r);
-                if (gain) y = __fmul_rn(y, gv[j][e]);
+                if (gain) {
+                    y = __fmul_rn(y, gv[j][e]);
+                    amax = fmaxf(amax, fabsf(y));
+                }
                 v[j][e] = y;
-                amax = fmaxf(amax, fabsf(y));
             }
+    if (gain) amax = rq_max(amax, sh.f);
     rq_emit<NV, SC1>(v, amax, nch, qr, s, sumq, sh);
 }
 
@@ -178,6 +212,7 @@ __device__ __forceinline__ void row_gnorm_quant(const float *hr, const TG *gr, i
         }
     const float rh = rms_factor(rq_sum(ss, sh.d[0]), d, eps);
     double su = 0.0;
+    float umax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int c = tid + 256 * j;
@@ -189,22 +224,33 @@ __device__ __forceinline__ void row_gnorm_quant(const float *hr, const TG *gr, i
                 y = y * gs[j][e];
                 u[j][e] = y;
                 su += (double)y * (double)y;
+                umax = fmaxf(umax, fabsf(y));
             }
             if (u_out) *reinterpret_cast<float4 *>(u_out + 4 * c) = make_float4(u[j][0], u[j][1], u[j][2], u[j][3]);
         }
     }
-    const float r = rms_factor(rq_sum(su, sh.d[1]), d, eps);
-    float amax = 0.0f;
+    float r, amax;
+    if (!ogain) {
+        rq_sum_max(su, umax, sh.d[1], sh.f);
+        r = rms_factor(su, d, eps);
+        amax = __fmul_rn(umax, r);
+    } else {
+        r = rms_factor(rq_sum(su, sh.d[1]), d, eps);
+        amax = 0.0f;
+    }
 #pragma unroll
     for (int j = 0; j < NV; ++j)
         if (tid < 256 && tid + 256 * j < nch)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float y = __fmul_rn(u[j][e], r);
-                if (ogain) y = __fmul_rn(y, og[j][e]);
+                if (ogain) {
+                    y = __fmul_rn(y, og[j][e]);
+                    amax = fmaxf(amax, fabsf(y));
+                }
                 u[j][e] = y;
-                amax = fmaxf(amax, fabsf(y));
             }
+    if (ogain) amax = rq_max(amax, sh.f);
     rq_emit<NV, SC1>(u, amax, nch, qr, s, sumq, sh);
 }
 
