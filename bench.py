@@ -145,6 +145,7 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
     norm_quant<T> (m rows of k): x read (sizeof T) + codes written (1 B) per element, 8 B per row.
     gnorm_quant<T>: h (fp32) and g (sizeof T) read + codes written per element, 8 B per row.
     scan (m = b t, k = d): f and x~ read, h written, 12 B per element.
+    scan_bwd (m = b t, k = d): dh, f and h read, dx and df written, 20 B per element.
     decode_step_xcd (m = b, n = d, k = inner; one whole decode step of a block): ops =
       2 b (4 d^2 + 3 d inner); bytes = all packed weights (4 d^2 + 3 d inner) / 4 + x read
       and out written (activation dtype) + h read and written (fp32) per row element.
@@ -165,6 +166,8 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
         return 0.0, m * k * (tb + 1.0) + 8.0 * m
     if base == "gnorm_quant":
         return 0.0, m * k * (4.0 + tb + 1.0) + 8.0 * m
+    if base.startswith("scan_bwd"):
+        return 0.0, 20.0 * m * k
     if base.startswith("scan"):
         return 0.0, 12.0 * m * k
     return 0.0, 0.0
@@ -410,6 +413,16 @@ def main():
                             frac=round(ops / (ms / 1000) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
                             note="all prefill contractions together, int8 ops over their event-measured time")
 
+    # ---- outside the timed region: the scan's derivative at the prefill's scan shape, and the
+    # decode step at the other batch sizes of the 1.3B decode workload (graph-replayed)
+    scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev) if T > 0 else None
+    by_batch = {str(B): round(decode_ms * 1000 / D / L, 2)} if D else {}
+    if D and graph is not None:
+        for bb in (1, 64):
+            if bb != B:
+                by_batch[str(bb)] = round(decode_us_per_layer(mmf, torch, layers, bb, d, dev, seed), 2)
+    by_batch = dict(sorted(by_batch.items(), key=lambda kv: int(kv[0])))
+
     cpu = None
     if args.cpu_baseline:
         cpu = cpu_baseline(d, inner, seed)
@@ -442,6 +455,8 @@ def main():
         "decode_kernel_sum_us_per_token_step": round(dsum * 1000 / D, 2) if D else None,
         "roofline": roof,
         "prefill_contraction_roofline": prefill_gemm,
+        "decode_us_per_layer_by_batch": by_batch,
+        "scan_bwd": scan_bwd,
         "cpu_baseline": cpu,
         "kernels": breakdown,
         "kernel_ms_per_step": round(total_kernel_ms, 3),
@@ -449,6 +464,64 @@ def main():
         "prep_s": round(prep_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_scan_bwd(mmf, torch, b: int, t: int, d: int, dev, launches: int = 10) -> dict:
+    """The derivative of the recurrence (mmf_hgrn_scan_bwd, chunked) on seeded f, h, dh of the
+    prefill's scan shape, timed per launch with HIP events on its stream."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(37)
+    f = torch.sigmoid(torch.randn((b, t, d), device=dev, generator=gen) + 2.0)
+    h = torch.randn((b, t, d), device=dev, generator=gen)
+    dh = torch.randn((b, t, d), device=dev, generator=gen)
+    dx, df = torch.empty_like(f), torch.empty_like(f)
+    mmf.hgrn_scan_bwd(f, h, dh, None, None, "chunk", dx=dx, df=df)
+    torch.cuda.synchronize()
+    mmf.timing_enable(True)
+    for _ in range(launches):
+        mmf.hgrn_scan_bwd(f, h, dh, None, None, "chunk", dx=dx, df=df)
+    torch.cuda.synchronize()
+    mmf.timing_enable(False)
+    recs = mmf.timing_collect()
+    name = recs[0][0]
+    avg_s = sum(r[4] for r in recs) / len(recs) / 1000.0
+    _, nbytes = algorithmic(name, b * t, d, d)
+    gbs = nbytes / avg_s / 1e9
+    del f, h, dh, dx, df
+    return dict(kernel="%s m=%d n=%d k=%d" % (name, b * t, d, d), shape="b=%d t=%d d=%d" % (b, t, d),
+                avg_launch_us=round(avg_s * 1e6, 2), algorithmic_per_launch=nbytes, achieved=round(gbs, 1),
+                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
+def decode_us_per_layer(mmf, torch, layers, b: int, d: int, dev, seed: int, steps: int = 32) -> float:
+    """One decode step of every layer at batch b, captured in a HIP graph and replayed `steps`
+    times from a seeded state; microseconds per layer."""
+    L = len(layers)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 100 + b)
+    hs = torch.randn((L, b, d), device=dev, generator=gen)
+    xin = torch.randn((b, d), device=dev, generator=gen).to(torch.bfloat16)
+    outs = [torch.empty_like(xin) for _ in range(2)]
+    ws = torch.empty(mmf.layer_workspace_size(layers[0], b, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        y = xin
+        for l in range(L):
+            y = mmf.layer_decode_step(layers[l], y, hs[l], out=outs[l % 2], ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e6 / steps / L
 
 
 def cpu_baseline(d: int, inner: int, seed: int) -> dict:

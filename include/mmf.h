@@ -177,6 +177,26 @@ mmf_status mmf_hgrn_scan_fwd(const float *x, const float *f, const float *h0, fl
                              void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * mmf_hgrn_scan_bwd -- derivative of mmf_hgrn_scan_fwd's recurrence, fp32
+ * (the recurrence of [R1] table "创新之处", differentiated; [R1] list
+ * "可复用的模式与技巧" names training through the quantisers with a
+ * straight-through estimator, which leaves this step exact). For a loss with
+ * dL/dh = dh [b][t][d] and dL/dh_last = dh_last [b][d] (or NULL: zeros):
+ *   D_t   = dh_t + f_{t+1} D_{t+1}     (f_T taken as 1, D_T = dh_last)
+ *   dx_t  = D_t;   df_t = D_t * h_{t-1};   dh0 = f_0 * D_0   (h_{-1} = h0 or 0)
+ *  f, h (the forward's output), dh, dx, df : [b][t][d] fp32; h0, dh_last, dh0 :
+ *  [b][d] fp32 or NULL (dh0 NULL: not computed). dx may equal dh (in place);
+ *  no other output may alias an input. RECURRENT runs each channel from
+ *  t-1 down to 0; CHUNK (and AUTO from t = 64) walks the sequence in chunks
+ *  from the end, composing chunk carries as (prod f, partial) pairs (same value
+ *  up to rounding). No workspace. t may be 0 (dh0 = dh_last).
+ *  Errors: INVALID_ARG.
+ */
+mmf_status mmf_hgrn_scan_bwd(const float *f, const float *h, const float *h0, const float *dh,
+                             const float *dh_last, float *dx, float *df, float *dh0, int64_t b,
+                             int64_t t, int64_t d, mmf_scan_mode mode, hipStream_t stream);
+
+/*
  * mmf_layer_fwd -- one HGRNBit block over b sequences of t tokens ([R3]):
  *   i^, f^, g^ = BitLinear_{i,f,g}(x)
  *   f  = sigmoid(f^);  x~ = (1 - f) * SiLU(i^)

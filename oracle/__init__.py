@@ -27,6 +27,10 @@ two halves of gate_proj. Further readings (the 1e-5 floors, round half to
 even, g_norm's eps, the residual wiring, which half of gate_proj is gated)
 are listed in the project's design notes.
 
+Beyond the forward pass: ``hgrn_scan_bwd``, the derivative of the recurrence
+(reverse time), for training through the quantisers with a straight-through
+estimator ([R1] list "可复用的模式与技巧"), which leaves this step exact.
+
 Precision: every step is binary64 except the two quantisers, which decide
 integers and therefore run in the kernel's precision (binary32 operations,
 binary64 sum of squares); their input vector is rounded to binary32 first.
@@ -62,8 +66,9 @@ def _load():
     lib.oracle_unpack.argtypes = [P, I64, I64, P]
     lib.oracle_ternary_matmul.argtypes = [P, P, I64, I64, I64, P]
     lib.oracle_hgrn_scan.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.oracle_hgrn_scan_bwd.argtypes = [P, P, P, P, P, I64, I64, I64, P, P, P]
     for fn in (lib.oracle_quant_rows, lib.oracle_ternarize, lib.oracle_pack, lib.oracle_unpack,
-               lib.oracle_ternary_matmul, lib.oracle_hgrn_scan, lib.oracle_num_threads):
+               lib.oracle_ternary_matmul, lib.oracle_hgrn_scan, lib.oracle_hgrn_scan_bwd, lib.oracle_num_threads):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -205,6 +210,29 @@ def hgrn_scan(x: np.ndarray, f: np.ndarray, h0: Optional[np.ndarray] = None) -> 
     if _load().oracle_hgrn_scan(_ptr(x), _ptr(f), _ptr(h0a), b, t, d, _ptr(h)) != 0:
         raise ValueError("oracle_hgrn_scan failed")
     return h
+
+
+def hgrn_scan_bwd(f: np.ndarray, h: np.ndarray, dh: np.ndarray, h0: Optional[np.ndarray] = None,
+                  dh_last: Optional[np.ndarray] = None):
+    """Derivative of ``hgrn_scan`` for a loss with dL/dh = dh and dL/dh_last = dh_last, binary64,
+    sequential from the last step: D_t = dh_t + f_{t+1} D_{t+1} (D_{T-1} = dh_{T-1} + dh_last);
+    returns dx = D, df = D * h_{t-1} (h_{-1} = h0 or 0) and dh0 = f_0 D_0 (the recurrence of [R1]
+    table "创新之处", differentiated)."""
+    f = np.ascontiguousarray(np.asarray(f, dtype=np.float64))
+    h = np.ascontiguousarray(np.asarray(h, dtype=np.float64))
+    dh = np.ascontiguousarray(np.asarray(dh, dtype=np.float64))
+    if f.shape != h.shape or f.shape != dh.shape or f.ndim != 3:
+        raise ValueError("f, h and dh must all be [b, t, d]")
+    b, t, d = f.shape
+    h0a = None if h0 is None else np.ascontiguousarray(np.asarray(h0, dtype=np.float64).reshape(b, d))
+    gla = None if dh_last is None else np.ascontiguousarray(np.asarray(dh_last, dtype=np.float64).reshape(b, d))
+    dx = np.empty_like(f)
+    df = np.empty_like(f)
+    dh0 = np.empty((b, d), dtype=np.float64)
+    if _load().oracle_hgrn_scan_bwd(_ptr(f), _ptr(h), _ptr(h0a), _ptr(dh), _ptr(gla), b, t, d, _ptr(dx), _ptr(df),
+                                    _ptr(dh0)) != 0:
+        raise ValueError("oracle_hgrn_scan_bwd failed")
+    return dx, df, dh0
 
 
 def gnorm_swish(h, g, weight=None, eps: float = 1e-8):

@@ -199,6 +199,39 @@ int oracle_hgrn_scan(const double *x, const double *f, const double *h0, int64_t
     return 0;
 }
 
+/*
+ * Derivative of the recurrence above, binary64. A loss L sees h through
+ * dL/dh[b][t][c] = dh and dL/dh_last[b][c] = dh_last (NULL: 0). With D_t the
+ * whole derivative of L with respect to h_t (directly, and through h_{t+1},
+ * which holds f_{t+1} * h_t):
+ *   D_{T-1} = dh_{T-1} + dh_last,   D_t = dh_t + f_{t+1} * D_{t+1}
+ *   dx_t = D_t,   df_t = D_t * h_{t-1},   dh0 = f_0 * D_0      (h_{-1} = h0 or 0)
+ * taken for t = T-1 down to 0. dh0 may be NULL; with t = 0, dh0 = dh_last.
+ */
+int oracle_hgrn_scan_bwd(const double *f, const double *h, const double *h0, const double *dh,
+                         const double *dh_last, int64_t b, int64_t t, int64_t d, double *dx, double *df,
+                         double *dh0)
+{
+    if (b < 0 || t < 0 || d <= 0) return -1;
+    if (t > 0 && (!f || !h || !dh || !dx || !df)) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bi = 0; bi < b; ++bi) {
+        for (int64_t c = 0; c < d; ++c) {
+            double total = dh_last ? dh_last[bi * d + c] : 0.0;  /* D_{t+1} times nothing yet */
+            for (int64_t s = t - 1; s >= 0; --s) {
+                int64_t idx = (bi * t + s) * d + c;
+                double f_next = (s + 1 < t) ? f[idx + d] : 1.0;
+                double h_prev = (s > 0) ? h[idx - d] : (h0 ? h0[bi * d + c] : 0.0);
+                total = dh[idx] + f_next * total;
+                dx[idx] = total;
+                df[idx] = total * h_prev;
+            }
+            if (dh0) dh0[bi * d + c] = (t > 0) ? f[(bi * t) * d + c] * total : total;
+        }
+    }
+    return 0;
+}
+
 /* Number of OpenMP threads the parallel loops above use (1 without OpenMP). */
 int oracle_num_threads(void)
 {

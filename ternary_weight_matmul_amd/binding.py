@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmmf.so")
 
 __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
-    "ternary_pack", "bitlinear_fwd", "hgrn_scan_fwd", "layer_fwd", "layer_decode_step",
+    "ternary_pack", "bitlinear_fwd", "hgrn_scan_fwd", "hgrn_scan_bwd", "layer_fwd", "layer_decode_step",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
     "set_decode_kernel", "decode_expired_waits", "DECODE_KERNELS",
 ]
@@ -27,7 +27,7 @@ SYMBOLS = [
     "mmf_last_error", "mmf_last_path",
     "mmf_ternary_pack_workspace_size", "mmf_ternary_pack",
     "mmf_bitlinear_workspace_size", "mmf_bitlinear_fwd",
-    "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd",
+    "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd", "mmf_hgrn_scan_bwd",
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
     "mmf_set_decode_kernel", "mmf_decode_expired_waits",
     "mmf_timing_enable", "mmf_timing_collect",
@@ -89,6 +89,7 @@ def load():
                                       ctypes.c_int, P, P, P, P, SZ, P]
     lib.mmf_hgrn_scan_workspace_size.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.mmf_hgrn_scan_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P, SZ, P]
+    lib.mmf_hgrn_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
     lib.mmf_layer_workspace_size.argtypes = [ctypes.POINTER(CLayerWeights), I64, I64, ctypes.POINTER(SZ)]
     lib.mmf_layer_fwd.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, I64, P, P,
                                   ctypes.c_int, P, SZ, ctypes.POINTER(CLayerProbe), P]
@@ -244,6 +245,25 @@ def hgrn_scan_fwd(x, f, h0=None, mode: str = "auto", out=None, h_last=None, ws=N
     _check(lib.mmf_hgrn_scan_fwd(_ptr(x), _ptr(f), _ptr(h0), _ptr(h), _ptr(h_last), b, t, d, SCAN_MODES[mode],
                                  _ptr(wsb), wsb.numel(), _stream()))
     return h
+
+
+def hgrn_scan_bwd(f, h, dh, h0=None, dh_last=None, mode: str = "auto", dx=None, df=None, want_dh0=False):
+    """Derivative of the recurrence (mmf_hgrn_scan_bwd): f, h (the forward's output) and dh = dL/dh,
+    all [b, t, d] fp32; returns (dx, df, dh0 or None)."""
+    torch = _torch()
+    lib = load()
+    if f.shape != h.shape or f.shape != dh.shape or f.dim() != 3:
+        raise ValueError("f, h and dh must all be [b, t, d]")
+    for t_ in (f, h, dh):
+        if t_.dtype != torch.float32 or not t_.is_contiguous():
+            raise TypeError("f, h and dh must be contiguous float32")
+    b, t, d = f.shape
+    dx = dx if dx is not None else torch.empty_like(f)
+    df = df if df is not None else torch.empty_like(f)
+    dh0 = torch.empty((b, d), dtype=torch.float32, device=f.device) if want_dh0 else None
+    _check(lib.mmf_hgrn_scan_bwd(_ptr(f), _ptr(h), _ptr(h0), _ptr(dh), _ptr(dh_last), _ptr(dx), _ptr(df),
+                                 _ptr(dh0), b, t, d, SCAN_MODES[mode], _stream()))
+    return dx, df, dh0
 
 
 @dataclass

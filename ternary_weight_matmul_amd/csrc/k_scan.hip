@@ -211,6 +211,150 @@ __global__ __launch_bounds__(W * 64) void scan_tiled_kernel(const float *x, cons
     if (h_last && live) h_last[bi * d + c] = carry;
 }
 
+// ----------------------------------------------------------------------------
+// Backward of the recurrence (reverse time)
+// ----------------------------------------------------------------------------
+// With d_t the whole derivative of the loss with respect to h_t (through h_t
+// itself and through every later step):
+//   d_t = dh_t + f_{t+1} d_{t+1},   d_{T-1} = dh_{T-1} + dh_last
+//   dx_t = d_t,   df_t = d_t h_{t-1},   dh0 = f_0 d_0      (h_{-1} = h0 or 0)
+// which is the forward recurrence run from t = T-1 down, with f shifted by one
+// step (f_T taken as 1) and the carry starting at dh_last; chunk carries
+// compose as the same (prod f, partial) pairs. 20 bytes per (b, t, c): read
+// dh, f and h, write dx and df. dx may be dh (every element is read before it
+// is written, by the same lane).
+__global__ __launch_bounds__(256) void scan_bwd_recurrent_kernel(const float *f, const float *h, const float *h0,
+                                                                 const float *dh, const float *dh_last, float *dx,
+                                                                 float *df, float *dh0, int64_t b, int64_t t,
+                                                                 int64_t d) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= b * d) return;
+    const int64_t bi = gid / d, c = gid % d;
+    const int64_t base = bi * t * d + c;
+    const float *fp = f + base, *hp = h + base, *gp = dh + base;
+    float *xo = dx + base, *fo = df + base;
+    const float hinit = h0 ? h0[gid] : 0.0f;
+    float carry = dh_last ? dh_last[gid] : 0.0f;
+    float fnext = 1.0f;  // f_{s+1} of the step s being taken
+    int64_t s = t - 1;
+    for (; s + 1 >= kScanU; s -= kScanU) {  // steps s, s-1, ..., s-U+1
+        float ga[kScanU], fa[kScanU], ha[kScanU];
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int64_t ts = s - u;
+            ga[u] = gp[ts * d];
+            fa[u] = fp[ts * d];
+            const float hv = hp[(ts > 0 ? ts - 1 : 0) * d];
+            ha[u] = ts > 0 ? hv : hinit;
+        }
+#pragma unroll
+        for (int u = 0; u < kScanU; ++u) {
+            const int64_t ts = s - u;
+            carry = fnext * carry + ga[u];
+            xo[ts * d] = carry;
+            fo[ts * d] = carry * ha[u];
+            fnext = fa[u];
+        }
+    }
+    for (; s >= 0; --s) {
+        const float g = gp[s * d], fv = fp[s * d];
+        const float hm = s > 0 ? hp[(s - 1) * d] : hinit;
+        carry = fnext * carry + g;
+        xo[s * d] = carry;
+        fo[s * d] = carry * hm;
+        fnext = fv;
+    }
+    if (dh0) dh0[gid] = fnext * carry;
+}
+
+// Tiled backward: the forward tiled kernel's scheme walked from the last chunk
+// to the first. Wave w of a chunk owns its steps w*S .. w*S+S-1 and takes them
+// from the last; the carry enters the chunk's last wave first, so wave w folds
+// the pairs of the waves after it.
+template <int W, int S, int P, bool NT>
+__global__ __launch_bounds__(W * 64) void scan_bwd_tiled_kernel(const float *f, const float *h, const float *h0,
+                                                                const float *dh, const float *dh_last, float *dx,
+                                                                float *df, float *dh0, int64_t t, int64_t d,
+                                                                int64_t groups) {
+    constexpr int CH = W * S;
+    __shared__ float2 pairs[2][W][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t bi = blockIdx.x / groups;
+    const int64_t c = (blockIdx.x % groups) * 64 + lane;
+    const bool live = c < d;
+    const int64_t cl = live ? c : d - 1;  // loads of idle lanes stay in bounds
+    const float *fp = f + bi * t * d + cl;
+    const float *hp = h + bi * t * d + cl;
+    const float *gp = dh + bi * t * d + cl;
+    float *xo = dx + bi * t * d + c;
+    float *fo = df + bi * t * d + c;
+    const float hinit = (h0 && live) ? h0[bi * d + c] : 0.0f;
+    float carry = (dh_last && live) ? dh_last[bi * d + c] : 0.0f;
+    const int64_t nchunks = (t + CH - 1) / CH;
+    // per step ts of a slot: dh_ts, f_{ts+1} and h_{ts-1} (indices clamped;
+    // the values that fall outside [0, t) are replaced where they are used)
+    float ga[P + 1][S], fa[P + 1][S], ha[P + 1][S];
+    auto load = [&](int slot, int64_t ck) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int64_t ts = ck * CH + w * S + s;
+            const int64_t tg = min(ts, t - 1), tf = min(ts + 1, t - 1);
+            const int64_t th = ts > 0 ? min(ts - 1, t - 1) : 0;
+            ga[slot][s] = ld_stream<NT>(gp + tg * d);
+            fa[slot][s] = ld_stream<NT>(fp + tf * d);
+            ha[slot][s] = ld_stream<NT>(hp + th * d);
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < P; ++p) load(p, nchunks - 1 - p >= 0 ? nchunks - 1 - p : 0);
+    for (int64_t k = 0; k < nchunks; ++k) {
+        const int64_t ck = nchunks - 1 - k;
+        const int64_t t0 = ck * CH + w * S;
+        if (k + P < nchunks) load(P, ck - P);
+        // this wave's steps, last first: steps past the end act as the identity
+        float a = 1.0f, bb = 0.0f;
+#pragma unroll
+        for (int s = S - 1; s >= 0; --s) {
+            const int64_t ts = t0 + s;
+            fa[0][s] = ts + 1 < t ? fa[0][s] : 1.0f;
+            ga[0][s] = ts < t ? ga[0][s] : 0.0f;
+            ha[0][s] = ts > 0 ? ha[0][s] : hinit;
+            bb = fa[0][s] * bb + ga[0][s];
+            a = a * fa[0][s];
+        }
+        pairs[k & 1][w][lane] = make_float2(a, bb);
+        __syncthreads();
+        // fold from the chunk's last wave: the carry entering wave w, and after the chunk
+        float hin = carry, cn = carry;
+#pragma unroll
+        for (int v = W - 1; v >= 0; --v) {
+            if (v == w) hin = cn;
+            const float2 pr = pairs[k & 1][v][lane];
+            cn = pr.x * cn + pr.y;
+        }
+        float gs = hin;
+#pragma unroll
+        for (int s = S - 1; s >= 0; --s) {
+            const int64_t ts = t0 + s;
+            gs = fa[0][s] * gs + ga[0][s];
+            if (live && ts < t) {
+                st_stream<NT>(xo + ts * d, gs);
+                st_stream<NT>(fo + ts * d, gs * ha[0][s]);
+            }
+        }
+        carry = cn;
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                ga[p][s] = ga[p + 1][s];
+                fa[p][s] = fa[p + 1][s];
+                ha[p][s] = ha[p + 1][s];
+            }
+    }
+    if (dh0 && live && w == 0) dh0[bi * d + c] = fp[0] * carry;
+}
+
 __global__ void copy_state_kernel(const float *h0, float *h_last, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) h_last[i] = h0 ? h0[i] : 0.0f;
@@ -240,6 +384,43 @@ int scan_pick_chunks(int64_t b, int64_t t, int64_t d, int mode) {
     if (c < 1) c = 1;
     if (mode == 2 && c < 2 && t >= 2) c = 2;
     return (int)c;
+}
+
+int scan_bwd_pick(int64_t t, int mode) {
+    if (mode == 1 || t <= 1 || (mode == 0 && t < 64)) return 1;
+    return kScanTiled;
+}
+
+hipError_t launch_scan_bwd(const float *f, const float *h, const float *h0, const float *dh, const float *dh_last,
+                           float *dx, float *df, float *dh0, int64_t b, int64_t t, int64_t d, int plan,
+                           hipStream_t stream, std::string *path) {
+    if (b <= 0) return hipSuccess;
+    if (t == 0) {
+        // h_last is h0: its derivative passes straight through
+        if (dh0) copy_state_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(dh_last, dh0, b * d);
+        if (path) *path += "scan_bwd_empty;";
+        return hipGetLastError();
+    }
+    if (plan == kScanTiled) {
+        const int64_t groups = (d + 63) / 64;
+        const unsigned grid = (unsigned)(b * groups);
+        const bool nt = 20 * b * t * d > kStreamBytes;
+        const bool many = b * groups >= kTiledManyGroups;
+        if (many && nt)
+            scan_bwd_tiled_kernel<4, 8, 3, true><<<grid, 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+        else if (many)
+            scan_bwd_tiled_kernel<4, 8, 3, false><<<grid, 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+        else if (nt)
+            scan_bwd_tiled_kernel<16, 8, 1, true><<<grid, 1024, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+        else
+            scan_bwd_tiled_kernel<16, 8, 1, false><<<grid, 1024, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+        if (path) *path += std::string("scan_bwd_tiled<") + (many ? "4w" : "16w") + (nt ? ",nt" : "") + ">;";
+        return hipGetLastError();
+    }
+    scan_bwd_recurrent_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df,
+                                                                                   dh0, b, t, d);
+    if (path) *path += "scan_bwd_recurrent;";
+    return hipGetLastError();
 }
 
 hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h, float *h_last, int64_t b,

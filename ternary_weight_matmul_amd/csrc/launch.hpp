@@ -111,4 +111,11 @@ hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h
                        int64_t b, int64_t t, int64_t d, int chunks, void *ws, hipStream_t stream,
                        std::string *path);
 
+// Backward of the HGRN scan: 1 = recurrent, kScanTiled = single-pass tiled
+// (reverse time). dh0 and dh_last optional; h0 NULL means zeros.
+int scan_bwd_pick(int64_t t, int mode);
+hipError_t launch_scan_bwd(const float *f, const float *h, const float *h0, const float *dh, const float *dh_last,
+                           float *dx, float *df, float *dh0, int64_t b, int64_t t, int64_t d, int plan,
+                           hipStream_t stream, std::string *path);
+
 }  // namespace mmf

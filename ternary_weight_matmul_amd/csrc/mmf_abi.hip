@@ -466,6 +466,30 @@ mmf_status mmf_hgrn_scan_fwd(const float *x, const float *f, const float *h0, fl
     return r;
 }
 
+mmf_status mmf_hgrn_scan_bwd(const float *f, const float *h, const float *h0, const float *dh, const float *dh_last,
+                             float *dx, float *df, float *dh0, int64_t b, int64_t t, int64_t d, mmf_scan_mode mode,
+                             hipStream_t stream) {
+    if (b < 0 || t < 0 || d <= 0) return fail(MMF_ERR_INVALID_ARG, "b, t >= 0 and d > 0 required");
+    if (mode != MMF_SCAN_AUTO && mode != MMF_SCAN_RECURRENT && mode != MMF_SCAN_CHUNK)
+        return fail(MMF_ERR_INVALID_ARG, "bad scan mode %d", (int)mode);
+    if (b > 0 && t > 0 && (!f || !h || !dh || !dx || !df))
+        return fail(MMF_ERR_INVALID_ARG, "f, h, dh, dx and df must be non-NULL");
+    const void *ins[] = {f, h, h0, dh, dh_last};
+    const void *outs[] = {df, dh0};
+    for (const void *o : outs)
+        for (const void *i : ins)
+            if (o && o == i) return fail(MMF_ERR_INVALID_ARG, "df and dh0 may not alias an input");
+    if (dx && (dx == f || dx == h || dx == h0 || dx == dh_last || dx == df || dx == dh0))
+        return fail(MMF_ERR_INVALID_ARG, "dx may alias dh only");
+    std::string path;
+    const int plan = scan_bwd_pick(t, (int)mode);
+    hipError_t e = timed(plan == kScanTiled ? "scan_bwd_tiled" : "scan_bwd_recurrent", b * t, (int)d, (int)d, stream,
+                         [&] { return launch_scan_bwd(f, h, h0, dh, dh_last, dx, df, dh0, b, t, d, plan, stream, &path); });
+    mmf_status r = hip_status(e, "mmf_hgrn_scan_bwd");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
 mmf_status mmf_layer_workspace_size(const mmf_layer_weights *w, int64_t b, int64_t t, size_t *bytes) {
     if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
     mmf_status st = check_layer(w);

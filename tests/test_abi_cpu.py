@@ -109,6 +109,21 @@ def test_scan_validation(lib):
     assert lib.mmf_hgrn_scan_fwd(FAKE, FAKE, None, FAKE, None, 1, 4096, 64, 2, None, 0, None) == WORKSPACE
 
 
+def test_scan_bwd_validation(lib):
+    f, h, dh, dx, df, h0, gl, dh0 = (FAKE + 256 * i for i in range(8))
+    call = lib.mmf_hgrn_scan_bwd
+    assert call(None, h, h0, dh, gl, dx, df, dh0, 1, 4, 64, 1, None) == INVALID  # f missing
+    assert call(f, h, h0, dh, gl, None, df, dh0, 1, 4, 64, 1, None) == INVALID   # dx missing
+    assert call(f, h, h0, dh, gl, dx, df, dh0, 1, 4, 0, 1, None) == INVALID      # d = 0
+    assert call(f, h, h0, dh, gl, dx, df, dh0, 1, 4, 64, 7, None) == INVALID     # mode
+    assert call(f, h, h0, dh, gl, dx, h, dh0, 1, 4, 64, 1, None) == INVALID      # df aliases h
+    assert call(f, h, h0, dh, gl, dx, df, gl, 1, 4, 64, 1, None) == INVALID      # dh0 aliases dh_last
+    assert call(f, h, h0, dh, gl, f, df, dh0, 1, 4, 64, 1, None) == INVALID      # dx aliases f
+    assert "alias" in _err(lib)
+    # no sequences: valid, nothing launched
+    assert call(None, None, None, None, None, None, None, None, 0, 4, 64, 0, None) == OK
+
+
 def test_layer_validation(lib):
     L = _layer()
     sz = ctypes.c_size_t(0)

@@ -38,6 +38,9 @@ def test_split_activation_codes_counted_per_group():
 
 def test_elementwise_kernels():
     assert bench.algorithmic("scan_tiled", 100, 7, 64) == (0.0, 12.0 * 100 * 64)
+    # the derivative: dh, f, h read and dx, df written
+    assert bench.algorithmic("scan_bwd_tiled", 100, 64, 64) == (0.0, 20.0 * 100 * 64)
+    assert bench.kernel_files("scan_bwd_recurrent m=1 n=2 k=2") == bench.kernel_files("scan_tiled")
     assert bench.algorithmic("norm_quant<f32>", 10, 0, 256) == (0.0, 10 * 256 * 5 + 80)
     assert bench.algorithmic("norm_quant<bf16>", 10, 0, 256) == (0.0, 10 * 256 * 3 + 80)
     assert bench.algorithmic("gnorm_quant<bf16>", 10, 0, 256) == (0.0, 10 * 256 * 7 + 80)

@@ -206,6 +206,119 @@ def test_scan_limits_zero_and_unit_gate(gpu):
     assert_close(h, np.cumsum(x.astype(np.float64), axis=1), 1e-5, "cumsum")
 
 
+SCAN_BWD_CASES = [
+    # b, t, d, mode, with_h0, with_last
+    (1, 1, 64, "recurrent", True, True),
+    (2, 7, 48, "recurrent", False, True),
+    (3, 300, 96, "recurrent", True, False),
+    (4, 63, 256, "auto", True, True),        # auto below 64 steps: recurrent
+    (2, 300, 96, "chunk", True, True),       # few groups: 16-wave workgroups
+    (1, 4099, 128, "chunk", True, True),     # T >= 4096
+    (8, 700, 1024, "chunk", True, True),     # ragged last chunk
+    (16, 300, 520, "auto", False, True),     # partial channel group
+    (2, 4100, 4096, "chunk", True, False),   # streaming accesses
+    (16, 260, 2048, "chunk", True, True),    # many groups: 4-wave workgroups, ragged last chunk
+]
+
+
+def _scan_bwd_inputs(b, t, d, seed, with_h0, with_last):
+    """f and the forward's h (the oracle's, rounded to binary32), an upstream dh, and optional
+    h0 and dh_last, all seeded."""
+    x, f = synth.scan_inputs(b, t, d, seed)
+    h0 = synth.activations((b, d), seed + 1) if with_h0 else None
+    h = oracle.hgrn_scan(x, f, h0).astype(np.float32)
+    dh = synth.activations((b, t, d), seed + 2)
+    gl = synth.activations((b, d), seed + 3) if with_last else None
+    return f, h, dh, h0, gl
+
+
+@pytest.mark.parametrize("b,t,d,mode,with_h0,with_last", SCAN_BWD_CASES)
+def test_scan_bwd_parity(gpu, b, t, d, mode, with_h0, with_last):
+    mmf = _mmf()
+    f, h, dh, h0, gl = _scan_bwd_inputs(b, t, d, 700 + t + d, with_h0, with_last)
+    dx, df, dh0 = mmf.hgrn_scan_bwd(dev(f, gpu), dev(h, gpu), dev(dh, gpu), dev(h0, gpu) if with_h0 else None,
+                                    dev(gl, gpu) if with_last else None, mode, want_dh0=True)
+    rdx, rdf, rdh0 = oracle.hgrn_scan_bwd(f, h, dh, h0, gl)
+    rtol = 1e-3 if (mode != "recurrent" and t >= 4096) else 1e-4
+    assert_close(host(dx), rdx, rtol, "dx")
+    assert_close(host(df), rdf, rtol, "df")
+    assert_close(host(dh0), rdh0, rtol, "dh0")
+    path = mmf.last_path()
+    if mode == "recurrent" or (mode == "auto" and t < 64):
+        assert "scan_bwd_recurrent" in path, path
+    else:
+        assert "scan_bwd_tiled" in path, path
+
+
+def test_scan_bwd_in_place_empty_and_limits(gpu):
+    import torch
+    mmf = _mmf()
+    f, h, dh, h0, gl = _scan_bwd_inputs(4, 390, 2048, 704, True, True)
+    rdx, rdf, rdh0 = oracle.hgrn_scan_bwd(f, h, dh, h0, gl)
+    for mode in ("recurrent", "chunk"):
+        dhd = dev(dh, gpu)
+        dx, df, dh0 = mmf.hgrn_scan_bwd(dev(f, gpu), dev(h, gpu), dhd, dev(h0, gpu), dev(gl, gpu), mode, dx=dhd,
+                                        want_dh0=True)
+        assert dx.data_ptr() == dhd.data_ptr()
+        assert_close(host(dx), rdx, 1e-4, "in-place dx " + mode)
+        assert_close(host(df), rdf, 1e-4, "in-place df " + mode)
+        assert_close(host(dh0), rdh0, 1e-4, "in-place dh0 " + mode)
+    # no steps: h_last is h0, so dh0 = dh_last
+    e = torch.empty((2, 0, 64), device=gpu)
+    gl2 = dev(synth.activations((2, 64), 706), gpu)
+    _, _, dh0 = mmf.hgrn_scan_bwd(e, e, e, None, gl2, want_dh0=True)
+    assert torch.equal(dh0, gl2)
+    # f = 0: nothing reaches back, dx = dh (+ dh_last on the last step), dh0 = 0
+    zero = np.zeros((2, 257, 64), dtype=np.float32)
+    dh3 = synth.activations((2, 257, 64), 707)
+    h3 = synth.activations((2, 257, 64), 708)
+    gl3 = synth.activations((2, 64), 709)
+    for mode in ("recurrent", "chunk"):
+        dx, _, dh0 = mmf.hgrn_scan_bwd(dev(zero, gpu), dev(h3, gpu), dev(dh3, gpu), None, dev(gl3, gpu), mode,
+                                       want_dh0=True)
+        want = dh3.copy()
+        want[:, -1] += gl3
+        assert np.array_equal(host(dx), want), mode
+        assert not host(dh0).any(), mode
+
+
+def test_scan_bwd_c5_full_size_sampled(gpu):
+    """The backward at the long-sequence stress shape (B=16, T=32768, d=2048, f = sigmoid(N(2,1))),
+    chunked: h from the forward kernel, dh ~ N(0, 1); the oracle runs whole sequences for 64
+    sampled channels (4 per sequence) from the same f, h and dh."""
+    import torch
+    mmf = _mmf()
+    b, t, d = 16, 32768, 2048
+    fd = torch.empty((b, t, d), device=gpu)
+    hd = torch.empty((b, t, d), device=gpu)
+    dhd = torch.empty((b, t, d), device=gpu)
+    pick = np.stack([synth.rng(7500 + i).choice(d, size=4, replace=False) for i in range(b)])
+    fs, dhs = [], []
+    for i in range(b):
+        x, f = synth.scan_inputs(1, t, d, 7 * 1000 + i)
+        hd[i].copy_(torch.from_numpy(x[0]))  # x for now; the forward overwrites it with h
+        fd[i].copy_(torch.from_numpy(f[0]))
+        fs.append(f[0][:, pick[i]].copy())
+        del x, f
+        g = synth.activations((t, d), 7 * 1000 + 500 + i)
+        dhd[i].copy_(torch.from_numpy(g))
+        dhs.append(g[:, pick[i]].copy())
+        del g
+    mmf.hgrn_scan_fwd(hd, fd, None, "chunk", out=hd)
+    dx, df, dh0 = mmf.hgrn_scan_bwd(fd, hd, dhd, None, None, "chunk", want_dh0=True)
+    assert "scan_bwd_tiled" in mmf.last_path()
+    idx = torch.from_numpy(pick).to(gpu)
+    sel = idx[:, None, :].expand(b, t, 4)
+    hs = torch.gather(hd, 2, sel).cpu().numpy()
+    got_dx = torch.gather(dx, 2, sel).cpu().numpy()
+    got_df = torch.gather(df, 2, sel).cpu().numpy()
+    got_dh0 = torch.gather(dh0, 1, idx).cpu().numpy()
+    rdx, rdf, rdh0 = oracle.hgrn_scan_bwd(np.stack(fs), hs, np.stack(dhs))
+    assert_close(got_dx, rdx, 1e-3, "dx (sampled channels)")
+    assert_close(got_df, rdf, 1e-3, "df (sampled channels)")
+    assert_close(got_dh0, rdh0, 1e-3, "dh0 (sampled channels)")
+
+
 LAYER_CASES = [
     # d, inner, b, t, act, gains, mode
     (64, 96, 1, 1, "f32", None, "recurrent"),

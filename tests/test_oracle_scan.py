@@ -71,3 +71,82 @@ def test_split_sequence_carries_state():
     h1 = oracle.hgrn_scan(x[:, :9], f[:, :9])
     h2 = oracle.hgrn_scan(x[:, 9:], f[:, 9:], h1[:, -1])
     assert np.array_equal(np.concatenate([h1, h2], axis=1), h)
+
+
+# ---- derivative of the recurrence (reverse time) ------------------------------------------------
+def _loss(xs, fs, h0, dh, gl):
+    """L = sum_t dh_t h_t + gl h_{T-1}, with h from the exact closed form above."""
+    h = _closed_form(xs, fs, h0)
+    return sum(Fraction(a) * b for a, b in zip(dh, h)) + Fraction(gl) * h[-1]
+
+
+def test_scan_bwd_is_the_exact_derivative():
+    """L is affine in every single x_s, f_s and h_0 (the closed form is multilinear), so
+    L(v + 1) - L(v) is the exact partial derivative. With dyadic inputs of a few bits the
+    oracle's binary64 arithmetic is exact and must equal it."""
+    g = synth.rng(31)
+    for T in range(1, 7):
+        xs = (g.integers(-16, 17, size=T) / 16.0).tolist()
+        fs = (g.integers(0, 9, size=T) / 8.0).tolist()
+        dh = (g.integers(-8, 9, size=T) / 8.0).tolist()
+        h0 = g.integers(-4, 5) / 4.0
+        gl = g.integers(-4, 5) / 4.0
+        h = oracle.hgrn_scan(np.array(xs).reshape(1, T, 1), np.array(fs).reshape(1, T, 1), np.array([[h0]]))
+        dx, df, dh0 = oracle.hgrn_scan_bwd(np.array(fs).reshape(1, T, 1), h, np.array(dh).reshape(1, T, 1),
+                                           np.array([[h0]]), np.array([[gl]]))
+        base = _loss(xs, fs, h0, dh, gl)
+        for s in range(T):
+            up = list(xs)
+            up[s] += 1
+            assert Fraction(dx[0, s, 0]) == _loss(up, fs, h0, dh, gl) - base, (T, s, "x")
+            up = list(fs)
+            up[s] += 1
+            assert Fraction(df[0, s, 0]) == _loss(xs, up, h0, dh, gl) - base, (T, s, "f")
+        assert Fraction(dh0[0, 0]) == _loss(xs, fs, h0 + 1, dh, gl) - base, (T, "h0")
+
+
+def test_scan_bwd_adjoint_identity():
+    """For fixed f the map (x, h0) -> h is linear, so <dh, h> + <dh_last, h_last> = <dx, x> + <dh0, h0>."""
+    g = synth.rng(32)
+    x = g.standard_normal((3, 40, 5))
+    f = g.uniform(0, 1, (3, 40, 5))
+    h0 = g.standard_normal((3, 5))
+    dh = g.standard_normal((3, 40, 5))
+    gl = g.standard_normal((3, 5))
+    h = oracle.hgrn_scan(x, f, h0)
+    dx, df, dh0 = oracle.hgrn_scan_bwd(f, h, dh, h0, gl)
+    lhs = np.sum(dh * h) + np.sum(gl * h[:, -1])
+    rhs = np.sum(dx * x) + np.sum(dh0 * h0)
+    assert abs(lhs - rhs) <= 1e-12 * (np.sum(np.abs(dh * h)) + np.sum(np.abs(gl * h[:, -1])))
+
+
+def test_scan_bwd_limits():
+    """f = 0: no step reaches back, dx = dh (dh_last joins the last step), dh0 = 0. f = 1: dx is
+    the reverse cumulative sum of dh plus dh_last, and dh0 = dx_0."""
+    g = synth.rng(33)
+    x = g.integers(-64, 64, size=(2, 7, 3)) / 8.0
+    h0 = g.integers(-8, 8, size=(2, 3)) / 4.0
+    dh = g.integers(-64, 64, size=(2, 7, 3)) / 8.0
+    gl = g.integers(-8, 8, size=(2, 3)) / 4.0
+    zero = np.zeros_like(x)
+    h = oracle.hgrn_scan(x, zero, h0)
+    dx, df, dh0 = oracle.hgrn_scan_bwd(zero, h, dh, h0, gl)
+    want = dh.copy()
+    want[:, -1] += gl
+    assert np.array_equal(dx, want)
+    h_prev = np.concatenate([h0[:, None, :], h[:, :-1]], axis=1)
+    assert np.array_equal(df, want * h_prev)
+    assert np.array_equal(dh0, np.zeros_like(h0))
+    one = np.ones_like(x)
+    h = oracle.hgrn_scan(x, one, h0)
+    dx, df, dh0 = oracle.hgrn_scan_bwd(one, h, dh, h0, gl)
+    want = np.flip(np.cumsum(np.flip(dh, axis=1), axis=1), axis=1) + gl[:, None, :]
+    assert np.array_equal(dx, want)
+    assert np.array_equal(dh0, want[:, 0])
+
+
+def test_scan_bwd_empty_sequence_passes_dh_last():
+    gl = np.arange(6.0).reshape(2, 3)
+    e = np.zeros((2, 0, 3))
+    dx, df, dh0 = oracle.hgrn_scan_bwd(e, e, e, np.ones((2, 3)), gl)
+    assert dx.shape == (2, 0, 3) and np.array_equal(dh0, gl)
