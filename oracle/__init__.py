@@ -27,9 +27,10 @@ two halves of gate_proj. Further readings (the 1e-5 floors, round half to
 even, g_norm's eps, the residual wiring, which half of gate_proj is gated)
 are listed in the project's design notes.
 
-Beyond the forward pass: ``hgrn_scan_bwd``, the derivative of the recurrence
-(reverse time), for training through the quantisers with a straight-through
-estimator ([R1] list "可复用的模式与技巧"), which leaves this step exact.
+Beyond the forward pass, for training through the quantisers with a
+straight-through estimator ([R1] list "可复用的模式与技巧"): ``hgrn_scan_bwd``,
+the derivative of the recurrence (reverse time), and ``bitlinear_bwd``, the
+derivative of FusedBitLinear with both quantisers passed straight through.
 
 Precision: every step is binary64 except the two quantisers, which decide
 integers and therefore run in the kernel's precision (binary32 operations,
@@ -190,6 +191,36 @@ def bitlinear(x: np.ndarray, t: np.ndarray, mu, gain=None, eps: float = 1e-8):
     q, s, sq = quantize(x, gain, eps)
     acc = ternary_matmul(q, t)
     return dict(y=dequant(acc, s, mu), q=q, s=s, sumq=sq, acc=acc)
+
+
+def bitlinear_bwd(x: np.ndarray, t: np.ndarray, mu, dy: np.ndarray, gain=None, eps: float = 1e-8):
+    """Derivative of ``bitlinear`` with straight-through quantisers, binary64.
+
+    [R1] list "可复用的模式与技巧": ``weight_quant`` quantises in the forward pass and lets
+    the gradient through unchanged in the backward pass (straight-through estimator); the
+    same reading is taken for the activation quantiser. With u = RMSNorm(x) * gain, the
+    dequantised operands u^ = q / s and W^ = t / sw of the forward product y = u^ W^T:
+        du = dy W^                     (the activation quantiser passes du to u)
+        dW = dy^T u^                   (weight_quant passes dW^ to the latent W)
+        r = (mean(x^2) + eps)^(-1/2),  c = sum_k x_k gain_k du_k
+        dx_k = r gain_k du_k - (r^3 / K) x_k c,   dgain_k = sum_rows du_k x_k r
+    Returns (dx [m,k], dW [n,k], dgain [k]).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    dy64 = np.asarray(dy, dtype=np.float64)
+    k = x64.shape[-1]
+    q, s, _ = quantize(x, gain, eps)
+    sw = np.float64(weight_scale(mu))
+    w_hat = np.asarray(t, dtype=np.float64) / sw
+    u_hat = q.astype(np.float64) / s.astype(np.float64)[:, None]
+    du = dy64 @ w_hat
+    dw = dy64.T @ u_hat
+    g = np.ones(k) if gain is None else np.asarray(gain, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=1) + np.float64(np.float32(eps)))
+    c = np.sum(x64 * g * du, axis=1)
+    dx = r[:, None] * g * du - (r ** 3 / k)[:, None] * x64 * c[:, None]
+    dgain = np.sum(du * x64 * r[:, None], axis=0)
+    return dx, dw, dgain
 
 
 def mixer_gates(i_hat, f_hat):
