@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
 def parse():
@@ -416,6 +417,7 @@ def main():
     # ---- outside the timed region: the scan's derivative at the prefill's scan shape, and the
     # decode step at the other batch sizes of the 1.3B decode workload (graph-replayed)
     scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev) if T > 0 else None
+    bitlinear_bwd = measure_bitlinear_bwd(mmf, torch, layers[0].o, B * T, dev) if T > 0 else None
     by_batch = {str(B): round(decode_ms * 1000 / D / L, 2)} if D else {}
     if D and graph is not None:
         for bb in (1, 64):
@@ -457,6 +459,7 @@ def main():
         "prefill_contraction_roofline": prefill_gemm,
         "decode_us_per_layer_by_batch": by_batch,
         "scan_bwd": scan_bwd,
+        "bitlinear_bwd": bitlinear_bwd,
         "cpu_baseline": cpu,
         "kernels": breakdown,
         "kernel_ms_per_step": round(total_kernel_ms, 3),
@@ -491,6 +494,37 @@ def measure_scan_bwd(mmf, torch, b: int, t: int, d: int, dev, launches: int = 10
     return dict(kernel="%s m=%d n=%d k=%d" % (name, b * t, d, d), shape="b=%d t=%d d=%d" % (b, t, d),
                 avg_launch_us=round(avg_s * 1e6, 2), algorithmic_per_launch=nbytes, achieved=round(gbs, 1),
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
+def measure_bitlinear_bwd(mmf, torch, lin, m: int, dev, launches: int = 5) -> dict:
+    """The straight-through derivative of one FusedBitLinear (mmf_bitlinear_bwd: dx, dW and
+    dgain, bf16 x and dy) at m rows, per kernel with HIP events: the two bf16 products against
+    the dense bf16 MFMA peak, the rest against HBM."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(41)
+    x = torch.randn((m, lin.k), device=dev, generator=gen).to(torch.bfloat16)
+    dy = torch.randn((m, lin.n), device=dev, generator=gen).to(torch.bfloat16)
+    mmf.bitlinear_bwd(x, lin, dy, want_dgain=True)
+    torch.cuda.synchronize()
+    mmf.timing_enable(True)
+    for _ in range(launches):
+        mmf.bitlinear_bwd(x, lin, dy, want_dgain=True)
+    torch.cuda.synchronize()
+    mmf.timing_enable(False)
+    per = {}
+    for name, mm, nn, kk, ms in mmf.timing_collect():
+        e = per.setdefault(name, dict(m=mm, n=nn, k=kk, ms=0.0))
+        e["ms"] += ms / launches
+    total_ms = sum(e["ms"] for e in per.values())
+    gemm_ms = sum(e["ms"] for k_, e in per.items() if k_.startswith("gemm_bf16"))
+    flops = sum(2.0 * e["m"] * e["n"] * e["k"] for k_, e in per.items() if k_.startswith("gemm_bf16"))
+    kernels = {k_: round(e["ms"] * 1000, 1) for k_, e in sorted(per.items(), key=lambda kv: -kv[1]["ms"])}
+    del x, dy
+    tf = flops / (gemm_ms / 1000) / 1e12
+    return dict(shape="m=%d n=%d k=%d" % (m, lin.n, lin.k), us_per_call=round(total_ms * 1000, 1),
+                kernels_us=kernels, gemm_achieved=round(tf, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                gemm_frac=round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                note="products through rocBLAS (bf16, fp32 accumulation); the rest hand-written")
 
 
 def decode_us_per_layer(mmf, torch, layers, b: int, d: int, dev, seed: int, steps: int = 32) -> float:

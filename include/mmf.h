@@ -162,6 +162,30 @@ mmf_status mmf_bitlinear_fwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
                              int32_t *acc_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * mmf_bitlinear_bwd -- derivative of mmf_bitlinear_fwd with straight-through
+ * quantisers ([R1] list "可复用的模式与技巧": weight_quant rounds in the forward
+ * pass and lets the gradient through unchanged in the backward pass; the
+ * activation quantiser is read the same way). With u = RMSNorm(x) * gain and
+ * the forward's dequantised operands u^ = q / s, W^ = t / sw:
+ *   du = dy W^;   dw = dy^T u^   (the latent weight's gradient)
+ *   dx_k = r gain_k du_k - (r^3 / k) x_k sum_j x_j gain_j du_j,  r = (mean(x^2) + eps)^(-1/2)
+ *   dgain_k = sum over rows of du_k x_k r
+ *  x : [m][k] in dtype xt (the forward's input); dy : [m][n] in dtype dyt;
+ *  dx : [m][k] in dtype dxt or NULL; dw : [n][k] fp32 or NULL; dgain : [k] fp32
+ *  or NULL (also without a gain: the derivative at gain = 1). The codes are
+ *  recomputed from x with the forward's quantiser. The two products are bf16
+ *  GEMMs with fp32 accumulation (rocBLAS): t and q are exact in bf16, an fp32 dy
+ *  and q / s are rounded to bf16. Outputs do not alias inputs. m may be 0
+ *  (dw and dgain are zero). Errors: INVALID_ARG, UNSUPPORTED (n % 8, k > 8192),
+ *  WORKSPACE, HIP (also a rocBLAS failure, named in mmf_last_error).
+ */
+mmf_status mmf_bitlinear_bwd_workspace_size(int64_t m, const mmf_ternary_weight *w, mmf_dtype dyt,
+                                            size_t *bytes);
+mmf_status mmf_bitlinear_bwd(const void *x, mmf_dtype xt, int64_t m, const mmf_ternary_weight *w,
+                             float eps, const void *dy, mmf_dtype dyt, void *dx, mmf_dtype dxt,
+                             float *dw, float *dgain, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * mmf_hgrn_scan_fwd -- the HGRN recurrence ([R1] table "创新之处"), fp32:
  *   h[b][t][c] = f[b][t][c] * h[b][t-1][c] + x[b][t][c],   h[b][-1][c] = h0[b][c]
  *  x, f, h : [b][t][d] fp32; h0 : [b][d] or NULL (zeros); h_last : [b][d] or NULL.

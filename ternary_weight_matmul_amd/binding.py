@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmmf.so")
 
 __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
-    "ternary_pack", "bitlinear_fwd", "hgrn_scan_fwd", "hgrn_scan_bwd", "layer_fwd", "layer_decode_step",
+    "ternary_pack", "bitlinear_fwd", "bitlinear_bwd", "hgrn_scan_fwd", "hgrn_scan_bwd", "layer_fwd",
+    "layer_decode_step",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
     "set_decode_kernel", "decode_expired_waits", "DECODE_KERNELS",
 ]
@@ -27,6 +28,7 @@ SYMBOLS = [
     "mmf_last_error", "mmf_last_path",
     "mmf_ternary_pack_workspace_size", "mmf_ternary_pack",
     "mmf_bitlinear_workspace_size", "mmf_bitlinear_fwd",
+    "mmf_bitlinear_bwd_workspace_size", "mmf_bitlinear_bwd",
     "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd", "mmf_hgrn_scan_bwd",
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
     "mmf_set_decode_kernel", "mmf_decode_expired_waits",
@@ -87,6 +89,10 @@ def load():
     lib.mmf_bitlinear_workspace_size.argtypes = [I64, I32, ctypes.POINTER(SZ)]
     lib.mmf_bitlinear_fwd.argtypes = [P, ctypes.c_int, I64, ctypes.POINTER(CTernaryWeight), F32, P,
                                       ctypes.c_int, P, P, P, P, SZ, P]
+    lib.mmf_bitlinear_bwd_workspace_size.argtypes = [I64, ctypes.POINTER(CTernaryWeight), ctypes.c_int,
+                                                     ctypes.POINTER(SZ)]
+    lib.mmf_bitlinear_bwd.argtypes = [P, ctypes.c_int, I64, ctypes.POINTER(CTernaryWeight), F32, P, ctypes.c_int,
+                                      P, ctypes.c_int, P, P, P, SZ, P]
     lib.mmf_hgrn_scan_workspace_size.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.mmf_hgrn_scan_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P, SZ, P]
     lib.mmf_hgrn_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
@@ -226,6 +232,32 @@ def bitlinear_fwd(x, w: PackedLinear, eps: float = 1e-8, out_dtype=None, codes_o
                                  _dtype_code(out_dtype), _ptr(codes_out), _ptr(scale_out), _ptr(acc_out),
                                  _ptr(ws), ws.numel(), _stream()))
     return y
+
+
+def bitlinear_bwd(x, w: PackedLinear, dy, eps: float = 1e-8, want_dx=True, want_dw=True, want_dgain=False,
+                  dx_dtype=None, ws=None):
+    """Derivative of FusedBitLinear with straight-through quantisers (mmf_bitlinear_bwd):
+    x [m, k] (the forward's input), dy [m, n]; returns (dx [m, k] or None, dw [n, k] fp32 or None,
+    dgain [k] fp32 or None)."""
+    torch = _torch()
+    lib = load()
+    if not x.is_contiguous() or not dy.is_contiguous():
+        raise ValueError("x and dy must be contiguous")
+    k = x.shape[-1]
+    m = x.numel() // k if k else 0
+    if dy.shape[-1] != w.n or dy.numel() != m * w.n:
+        raise ValueError("dy must be [m, n]")
+    dx = torch.empty(x.shape, dtype=dx_dtype or x.dtype, device=x.device) if want_dx else None
+    dw = torch.empty((w.n, k), dtype=torch.float32, device=x.device) if want_dw else None
+    dgain = torch.empty((k,), dtype=torch.float32, device=x.device) if want_dgain else None
+    cw = w.c()
+    need = SZ(0)
+    _check(lib.mmf_bitlinear_bwd_workspace_size(m, ctypes.byref(cw), _dtype_code(dy.dtype), ctypes.byref(need)))
+    ws = _workspace(need.value, x.device, ws)
+    _check(lib.mmf_bitlinear_bwd(_ptr(x), _dtype_code(x.dtype), m, ctypes.byref(cw), F32(eps), _ptr(dy),
+                                 _dtype_code(dy.dtype), _ptr(dx), _dtype_code(dx.dtype if dx is not None else x.dtype),
+                                 _ptr(dw), _ptr(dgain), _ptr(ws), ws.numel(), _stream()))
+    return dx, dw, dgain
 
 
 def hgrn_scan_fwd(x, f, h0=None, mode: str = "auto", out=None, h_last=None, ws=None):

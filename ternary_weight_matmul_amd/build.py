@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmmf.so")
-SOURCES = ["k_quant.hip", "k_scan.hip", "k_contract.hip", "k_gemv_q.hip", "k_decode.hip", "mmf_abi.hip"]
+SOURCES = ["k_quant.hip", "k_scan.hip", "k_contract.hip", "k_gemv_q.hip", "k_decode.hip", "k_bwd.hip", "mmf_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -45,7 +45,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
+    # rocBLAS: the bf16 products of the backward pass (plain dense GEMMs)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-lrocblas", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -1,0 +1,323 @@
+// Derivative of FusedBitLinear with straight-through quantisers (gfx950).
+//
+// "MatMul-Free LLM 深度分析报告", list "可复用的模式与技巧": the ternary weight
+// quantiser rounds in the forward pass and passes the gradient through unchanged
+// in the backward pass (straight-through estimator); the activation quantiser is
+// read the same way. The forward product is y = u^ W^T with the dequantised
+// operands u^ = q / s (codes of the RMSNorm'd row) and W^ = t / sw, so
+//   du = dy W^,   dW = dy^T u^,
+// and the RMSNorm u = x r gain, r = (mean(x^2) + eps)^(-1/2), gives
+//   dx_k = r gain_k du_k - (r^3 / K) x_k sum_j x_j gain_j du_j,
+//   dgain_k = sum over rows of du_k x_k r.
+//
+// The two products are plain dense contractions once the operands are
+// expanded: t is exact in bf16 ({-1, 0, +1}), the codes q are exact in bf16, so
+// they run as bf16 GEMMs with fp32 accumulation in the vendor library
+// (rocBLAS); the factor 1 / sw is applied afterwards in fp32. What is not a
+// plain product -- the expansion of the 2-bit words, the scaled codes, the
+// RMSNorm derivative and the gain's column sums -- is the kernels below.
+#include <rocblas/rocblas.h>
+
+#include <mutex>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace mmf {
+
+// bf16 bit patterns of t = c - 1 for the offset codes c = 0, 1, 2
+__device__ __forceinline__ uint32_t ternary_bf16(uint32_t c) { return c == 0 ? 0xBF80u : (c == 2 ? 0x3F80u : 0u); }
+
+// packed [n][k/16] -> bf16 t [n][k]. Word w of a row holds k = 16 w + 4 j + b in
+// bits 8 b + 2 j (b, j = 0..3); one thread expands one word into two 16-byte stores.
+__global__ __launch_bounds__(256) void expand_ternary_kernel(const uint32_t *__restrict__ packed, int64_t words,
+                                                             uint16_t *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= words) return;
+    const uint32_t w = packed[i];
+    uint32_t v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int k0 = 2 * p, k1 = 2 * p + 1;  // k within the word: j = k / 4, b = k % 4
+        const uint32_t c0 = (w >> (8 * (k0 & 3) + 2 * (k0 >> 2))) & 3u;
+        const uint32_t c1 = (w >> (8 * (k1 & 3) + 2 * (k1 >> 2))) & 3u;
+        v[p] = ternary_bf16(c0) | (ternary_bf16(c1) << 16);
+    }
+    uint4 *o = reinterpret_cast<uint4 *>(out + 16 * i);
+    o[0] = make_uint4(v[0], v[1], v[2], v[3]);
+    o[1] = make_uint4(v[4], v[5], v[6], v[7]);
+}
+
+// u^ = q / s (correctly rounded, then to bf16) for codes [m][k]; 8 codes per thread
+__global__ __launch_bounds__(256) void scaled_codes_kernel(const int8_t *__restrict__ q, const float *__restrict__ s,
+                                                           int64_t m, int k, uint16_t *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 8 codes
+    const int64_t per_row = k / 8;
+    if (i >= m * per_row) return;
+    const int64_t row = i / per_row;
+    const float sr = s[row];
+    const uint2 raw = reinterpret_cast<const uint2 *>(q)[i];
+    uint32_t v[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t word = p < 2 ? raw.x : raw.y;
+        const int sh = 16 * (p & 1);
+        const float a = (float)(int8_t)((word >> sh) & 0xff), b = (float)(int8_t)((word >> (sh + 8)) & 0xff);
+        v[p] = (uint32_t)f32_to_bf16(__fdiv_rn(a, sr)) | ((uint32_t)f32_to_bf16(__fdiv_rn(b, sr)) << 16);
+    }
+    reinterpret_cast<uint4 *>(out)[i] = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// fp32 -> bf16 (round to nearest even), 4 per thread
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ x, int64_t n4, uint16_t *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 v = reinterpret_cast<const float4 *>(x)[i];
+    reinterpret_cast<uint2 *>(out)[i] =
+        make_uint2((uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                   (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16));
+}
+
+// The RMSNorm derivative for `rows` consecutive rows per workgroup (256
+// threads; thread t owns the 4-element chunks t, t + 256, ... of a row):
+// du = du_raw / sw, then per row the sums x.x (binary64) and x.(gain du) meet in
+// LDS in one round, and dx = r gain du - (r^3 / K) x c. The gain's derivative is
+// summed over the workgroup's rows in registers and written as one partial row.
+template <typename TX, typename TD, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const TX *__restrict__ x, const float *__restrict__ du_raw,
+                                                          const float *__restrict__ gain, const float *__restrict__ mu,
+                                                          float eps, int64_t m, int k, int rows, TD *__restrict__ dx,
+                                                          float *__restrict__ gpart) {
+    __shared__ double red[2][2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nch = k >> 2;
+    const float sw = __fdiv_rn(1.0f, fmaxf(*mu, 1e-5f));
+    float gv[NV][4], gacc[NV][4];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = min(tid + 256 * j, nch - 1);
+        const float4 g = gain ? *reinterpret_cast<const float4 *>(gain + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
+        gv[j][0] = g.x; gv[j][1] = g.y; gv[j][2] = g.z; gv[j][3] = g.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gacc[j][e] = 0.0f;
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * rows;
+    const int64_t r1 = r0 + rows < m ? r0 + rows : m;
+    for (int64_t row = r0; row < r1; ++row) {
+        const int buf = (int)(row & 1);
+        float xv[NV][4], dv[NV][4];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {  // straight-line loads; slots past the row end repeat the last chunk
+            const int c = min(tid + 256 * j, nch - 1);
+            const float4 a = load_act4(x + row * k, 4 * c);
+            const float4 d = *reinterpret_cast<const float4 *>(du_raw + row * k + 4 * c);
+            xv[j][0] = a.x; xv[j][1] = a.y; xv[j][2] = a.z; xv[j][3] = a.w;
+            dv[j][0] = d.x; dv[j][1] = d.y; dv[j][2] = d.z; dv[j][3] = d.w;
+        }
+        double ss = 0.0, cs = 0.0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            if (tid + 256 * j < nch)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dv[j][e] = __fdiv_rn(dv[j][e], sw);
+                    ss += (double)xv[j][e] * (double)xv[j][e];
+                    cs += (double)xv[j][e] * (double)(gv[j][e] * dv[j][e]);
+                }
+        ss = wave_sum(ss);
+        cs = wave_sum(cs);
+        if (lane == 0) {
+            red[buf][0][wv] = ss;
+            red[buf][1][wv] = cs;
+        }
+        __syncthreads();
+        ss = (red[buf][0][0] + red[buf][0][1]) + (red[buf][0][2] + red[buf][0][3]);
+        cs = (red[buf][1][0] + red[buf][1][1]) + (red[buf][1][2] + red[buf][1][3]);
+        const float r = rms_factor(ss, k, eps);
+        const float coef = (r * r * r) / (float)k;
+        const float c = (float)cs;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int ch = tid + 256 * j;
+            if (ch < nch) {
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[e] = r * gv[j][e] * dv[j][e] - coef * xv[j][e] * c;
+                    gacc[j][e] += dv[j][e] * xv[j][e] * r;
+                }
+                if (dx) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) store_act(dx, row * k + 4 * ch + e, o[e]);
+                }
+            }
+        }
+    }
+    if (gpart) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int ch = tid + 256 * j;
+            if (ch < nch)
+                *reinterpret_cast<float4 *>(gpart + (int64_t)blockIdx.x * k + 4 * ch) =
+                    make_float4(gacc[j][0], gacc[j][1], gacc[j][2], gacc[j][3]);
+        }
+    }
+}
+
+// dgain[k] = sum of the partial rows, in two fixed-order levels: workgroup
+// (x, y) sums the partial rows of split y for 64 columns (four row groups of 64
+// threads meet in LDS) into part2[y]; then each column sums part2 over y.
+constexpr int kGainSplits = 64;
+__global__ __launch_bounds__(256) void gain_reduce_kernel(const float *__restrict__ part, int nblk, int k,
+                                                          float *__restrict__ part2) {
+    __shared__ float red[4][64];
+    const int lane = threadIdx.x & 63, rg = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
+    const int per = (nblk + gridDim.y - 1) / gridDim.y;
+    const int b0 = blockIdx.y * per, b1 = min(b0 + per, nblk);
+    float acc = 0.0f;
+    if (c < k)
+        for (int b = b0 + rg; b < b1; b += 4) acc += part[(int64_t)b * k + c];
+    red[rg][lane] = acc;
+    __syncthreads();
+    if (rg == 0 && c < k) part2[(int64_t)blockIdx.y * k + c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+}
+
+__global__ __launch_bounds__(256) void gain_final_kernel(const float *__restrict__ part2, int splits, int k,
+                                                         float *__restrict__ dgain) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= k) return;
+    float acc = 0.0f;
+    for (int y = 0; y < splits; ++y) acc += part2[(int64_t)y * k + c];
+    dgain[c] = acc;
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+int rmsnorm_bwd_rows(int64_t m) {
+    const int64_t target = 2048;  // workgroups
+    int64_t r = (m + target - 1) / target;
+    return (int)(r < 1 ? 1 : r);
+}
+
+static int nv_bucket(int k) {
+    const int n = (k / 4 + 255) / 256;
+    int b = 1;
+    while (b < n) b *= 2;
+    return b;
+}
+
+bool rmsnorm_bwd_supported(int k) { return k % 8 == 0 && nv_bucket(k) <= 8; }
+
+hipError_t launch_expand_ternary(const uint32_t *packed, int n, int k, uint16_t *out, hipStream_t st) {
+    const int64_t words = (int64_t)n * (k / 16);
+    if (words == 0) return hipSuccess;
+    expand_ternary_kernel<<<(unsigned)((words + 255) / 256), 256, 0, st>>>(packed, words, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_scaled_codes(const int8_t *q, const float *s, int64_t m, int k, uint16_t *out, hipStream_t st) {
+    const int64_t n8 = m * (k / 8);
+    if (n8 == 0) return hipSuccess;
+    scaled_codes_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(q, s, m, k, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *out, hipStream_t st) {
+    const int64_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    to_bf16_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(x, n4, out);
+    return hipGetLastError();
+}
+
+template <typename TX, typename TD>
+static void rms_bwd_t(const TX *x, const float *du_raw, const float *gain, const float *mu, float eps, int64_t m, int k,
+                      TD *dx, float *gpart, hipStream_t st) {
+    const int rows = rmsnorm_bwd_rows(m);
+    const unsigned grid = (unsigned)((m + rows - 1) / rows);
+    switch (nv_bucket(k)) {
+#define MMF_RB(NV) case NV: rmsnorm_bwd_kernel<TX, TD, NV><<<grid, 256, 0, st>>>(x, du_raw, gain, mu, eps, m, k, rows, dx, gpart); break;
+        MMF_RB(1) MMF_RB(2) MMF_RB(4) MMF_RB(8)
+#undef MMF_RB
+    }
+}
+
+hipError_t launch_rmsnorm_bwd(const void *x, ActType xt, const float *du_raw, const float *gain, const float *mu,
+                              float eps, int64_t m, int k, void *dx, ActType dxt, float *gpart, hipStream_t st) {
+    if (m <= 0) return hipSuccess;
+    if (xt == ACT_F32) {
+        if (dxt == ACT_F32) rms_bwd_t(static_cast<const float *>(x), du_raw, gain, mu, eps, m, k, static_cast<float *>(dx), gpart, st);
+        else rms_bwd_t(static_cast<const float *>(x), du_raw, gain, mu, eps, m, k, static_cast<uint16_t *>(dx), gpart, st);
+    } else {
+        if (dxt == ACT_F32) rms_bwd_t(static_cast<const uint16_t *>(x), du_raw, gain, mu, eps, m, k, static_cast<float *>(dx), gpart, st);
+        else rms_bwd_t(static_cast<const uint16_t *>(x), du_raw, gain, mu, eps, m, k, static_cast<uint16_t *>(dx), gpart, st);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t st) {
+    if (n > 0) zero_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+    return hipGetLastError();
+}
+
+int gain_reduce_splits(int nblk) { return nblk < kGainSplits ? (nblk > 0 ? nblk : 1) : kGainSplits; }
+
+hipError_t launch_gain_reduce(const float *gpart, int nblk, int k, float *part2, float *dgain, hipStream_t st) {
+    const int splits = gain_reduce_splits(nblk);
+    gain_reduce_kernel<<<dim3((unsigned)((k + 63) / 64), (unsigned)splits), 256, 0, st>>>(gpart, nblk, k, part2);
+    gain_final_kernel<<<(unsigned)((k + 255) / 256), 256, 0, st>>>(part2, splits, k, dgain);
+    return hipGetLastError();
+}
+
+// One rocBLAS handle per device, made on first use.
+static rocblas_handle blas_handle(std::string *err) {
+    static std::mutex mu;
+    static rocblas_handle handles[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        *err = "no current device";
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!handles[dev]) {
+        rocblas_handle h = nullptr;
+        const rocblas_status s = rocblas_create_handle(&h);
+        if (s != rocblas_status_success) {
+            *err = std::string("rocblas_create_handle: ") + rocblas_status_to_string(s);
+            return nullptr;
+        }
+        handles[dev] = h;
+    }
+    return handles[dev];
+}
+
+// Row-major C[rows][cols] (fp32) = A B with bf16 operands, fp32 accumulation:
+// A is [rows][inner] (trans_a: stored as [inner][rows]), B is [inner][cols].
+// rocBLAS is column-major, so it computes C^T = B^T A^T.
+hipError_t gemm_bf16_f32(const uint16_t *a, bool trans_a, const uint16_t *b, int64_t rows, int64_t cols, int64_t inner,
+                         float *c, hipStream_t st, std::string *err) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    rocblas_handle h = blas_handle(err);
+    if (!h) return hipErrorUnknown;
+    rocblas_status s = rocblas_set_stream(h, st);
+    const float one = 1.0f, zero = 0.0f;
+    if (s == rocblas_status_success)
+        s = rocblas_gemm_ex(h, rocblas_operation_none, trans_a ? rocblas_operation_transpose : rocblas_operation_none,
+                            (rocblas_int)cols, (rocblas_int)rows, (rocblas_int)inner, &one, b, rocblas_datatype_bf16_r,
+                            (rocblas_int)cols, a, rocblas_datatype_bf16_r, (rocblas_int)(trans_a ? rows : inner), &zero,
+                            c, rocblas_datatype_f32_r, (rocblas_int)cols, c, rocblas_datatype_f32_r, (rocblas_int)cols,
+                            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    if (s != rocblas_status_success) {
+        *err = std::string("rocblas_gemm_ex: ") + rocblas_status_to_string(s);
+        return hipErrorUnknown;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mmf

@@ -118,4 +118,23 @@ hipError_t launch_scan_bwd(const float *f, const float *h, const float *h0, cons
                            float *dx, float *df, float *dh0, int64_t b, int64_t t, int64_t d, int plan,
                            hipStream_t stream, std::string *path);
 
+// Derivative of FusedBitLinear (k_bwd.hip): bf16 expansion of the ternary
+// words (t in {-1, 0, +1}, [n][k]), bf16 scaled codes q / s ([m][k]), fp32 ->
+// bf16, the RMSNorm derivative (du = du_raw / sw; optional dx, per-workgroup
+// partial sums of the gain's derivative) and their reduction, and a bf16 GEMM
+// with fp32 output through rocBLAS (row-major C[rows][cols] = A B, A given as
+// [rows][inner] or, with trans_a, as [inner][rows]).
+hipError_t launch_expand_ternary(const uint32_t *packed, int n, int k, uint16_t *out, hipStream_t st);
+hipError_t launch_scaled_codes(const int8_t *q, const float *s, int64_t m, int k, uint16_t *out, hipStream_t st);
+hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *out, hipStream_t st);
+int rmsnorm_bwd_rows(int64_t m);
+bool rmsnorm_bwd_supported(int k);
+hipError_t launch_rmsnorm_bwd(const void *x, ActType xt, const float *du_raw, const float *gain, const float *mu,
+                              float eps, int64_t m, int k, void *dx, ActType dxt, float *gpart, hipStream_t st);
+int gain_reduce_splits(int nblk);  // rows of the second level's workspace ([splits][k] fp32)
+hipError_t launch_gain_reduce(const float *gpart, int nblk, int k, float *part2, float *dgain, hipStream_t st);
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t st);  // a fill kernel (capturable)
+hipError_t gemm_bf16_f32(const uint16_t *a, bool trans_a, const uint16_t *b, int64_t rows, int64_t cols, int64_t inner,
+                         float *c, hipStream_t st, std::string *err);
+
 }  // namespace mmf

@@ -9,6 +9,7 @@
 // "什麼情況下這個工具是錯的選擇", names a silent fallback to a slow path as a
 // failure mode.
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 #include <vector>
@@ -437,6 +438,105 @@ mmf_status mmf_bitlinear_fwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
         e = t_contract(a, EPI_LINEAR, 1, true, stream, &path);
     }
     mmf_status r = hip_status(e, "mmf_bitlinear_fwd");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+// ------------------------------------------------------------ bitlinear bwd --
+struct BitlinearBwdWs {
+    int8_t *q;
+    float *s;
+    uint16_t *t16, *dy16, *u16;
+    float *du, *gpart, *gpart2;
+};
+
+size_t bitlinear_bwd_plan(Carver &c, int64_t m, int n, int k, mmf_dtype dyt, BitlinearBwdWs *o) {
+    BitlinearBwdWs w;
+    w.q = c.take<int8_t>((size_t)m * k);
+    w.s = c.take<float>((size_t)m);
+    w.t16 = c.take<uint16_t>((size_t)n * k);
+    w.dy16 = dyt == MMF_F32 ? c.take<uint16_t>((size_t)m * n) : nullptr;
+    w.u16 = c.take<uint16_t>((size_t)m * k);
+    w.du = c.take<float>((size_t)m * k);
+    const int64_t nblk = m > 0 ? (m + rmsnorm_bwd_rows(m) - 1) / rmsnorm_bwd_rows(m) : 0;
+    w.gpart = c.take<float>((size_t)nblk * k);
+    w.gpart2 = c.take<float>((size_t)gain_reduce_splits((int)nblk) * k);
+    if (o) *o = w;
+    return c.off;
+}
+
+mmf_status mmf_bitlinear_bwd_workspace_size(int64_t m, const mmf_ternary_weight *w, mmf_dtype dyt, size_t *bytes) {
+    if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
+    mmf_status st = check_weight(w, "weight");
+    if (st != MMF_OK) return st;
+    if (m < 0) return fail(MMF_ERR_INVALID_ARG, "m=%lld < 0", (long long)m);
+    if (!valid_dtype(dyt)) return fail(MMF_ERR_INVALID_ARG, "bad dtype");
+    Carver c(nullptr);
+    *bytes = bitlinear_bwd_plan(c, m, w->n, w->k, dyt, nullptr);
+    return MMF_OK;
+}
+
+mmf_status mmf_bitlinear_bwd(const void *x, mmf_dtype xt, int64_t m, const mmf_ternary_weight *w, float eps,
+                             const void *dy, mmf_dtype dyt, void *dx, mmf_dtype dxt, float *dw, float *dgain,
+                             void *ws, size_t ws_bytes, hipStream_t stream) {
+    size_t need = 0;
+    mmf_status st = mmf_bitlinear_bwd_workspace_size(m, w, dyt, &need);
+    if (st != MMF_OK) return st;
+    if (!valid_dtype(xt) || !valid_dtype(dxt)) return fail(MMF_ERR_INVALID_ARG, "bad dtype");
+    if (!(eps >= 0.0f)) return fail(MMF_ERR_INVALID_ARG, "eps must be >= 0");
+    const int n = w->n, k = w->k;
+    if (n % 8) return fail(MMF_ERR_UNSUPPORTED, "n=%d is not a multiple of 8", n);
+    if (!rmsnorm_bwd_supported(k)) return fail(MMF_ERR_UNSUPPORTED, "k=%d exceeds %d", k, kMaxNormRow);
+    if ((int64_t)n > INT32_MAX || m > INT32_MAX) return fail(MMF_ERR_UNSUPPORTED, "m or n beyond 32-bit GEMM sizes");
+    if (m > 0 && (!x || !dy)) return fail(MMF_ERR_INVALID_ARG, "x and dy must be non-NULL");
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw) || !aligned16(dgain))
+        return fail(MMF_ERR_INVALID_ARG, "x, dy, dx, dw and dgain must be 16-byte aligned");
+    if (m > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    if (m == 0) {
+        // no rows: dW and dgain are sums over nothing
+        hipError_t e = hipSuccess;
+        if (dw) e = launch_zero_f32(dw, (int64_t)n * k, stream);
+        if (e == hipSuccess && dgain) e = launch_zero_f32(dgain, k, stream);
+        mmf_status r = hip_status(e, "mmf_bitlinear_bwd");
+        if (r == MMF_OK) g_path = "empty";
+        return r;
+    }
+    Carver c(ws);
+    BitlinearBwdWs B;
+    bitlinear_bwd_plan(c, m, n, k, dyt, &B);
+    std::string path, err;
+    hipError_t e = t_norm_quant(x, act(xt), m, k, w->norm_w, eps, B.q, B.s, nullptr, stream, &path);
+    const uint16_t *dy16 = dyt == MMF_F32 ? B.dy16 : static_cast<const uint16_t *>(dy);
+    if (e == hipSuccess && dyt == MMF_F32)
+        e = timed("to_bf16", m, n, n, stream,
+                  [&] { return launch_to_bf16(static_cast<const float *>(dy), m * n, B.dy16, stream); });
+    if (e == hipSuccess && (dx || dgain)) {
+        e = timed("expand_ternary", n, k, k, stream, [&] { return launch_expand_ternary(w->packed, n, k, B.t16, stream); });
+        if (e == hipSuccess)  // du (before 1 / sw) = dy t
+            e = timed("gemm_bf16<du>", m, k, n, stream,
+                      [&] { return gemm_bf16_f32(dy16, false, B.t16, m, k, n, B.du, stream, &err); });
+        if (e == hipSuccess)
+            e = timed("rmsnorm_bwd", m, k, k, stream, [&] {
+                return launch_rmsnorm_bwd(x, act(xt), B.du, w->norm_w, w->mu, eps, m, k, dx, act(dxt),
+                                          dgain ? B.gpart : nullptr, stream);
+            });
+        if (e == hipSuccess && dgain) {
+            const int rows = rmsnorm_bwd_rows(m);
+            const int nblk = (int)((m + rows - 1) / rows);
+            e = timed("gain_reduce", nblk, k, k, stream, [&] { return launch_gain_reduce(B.gpart, nblk, k, B.gpart2, dgain, stream); });
+        }
+        path += "expand_ternary;gemm_bf16<du>;rmsnorm_bwd;" + std::string(dgain ? "gain_reduce;" : "");
+    }
+    if (e == hipSuccess && dw) {
+        e = timed("scaled_codes", m, k, k, stream, [&] { return launch_scaled_codes(B.q, B.s, m, k, B.u16, stream); });
+        if (e == hipSuccess)  // dW = dy^T (q / s)
+            e = timed("gemm_bf16<dw>", n, k, m, stream,
+                      [&] { return gemm_bf16_f32(dy16, true, B.u16, n, k, m, dw, stream, &err); });
+        path += "scaled_codes;gemm_bf16<dw>;";
+    }
+    if (e != hipSuccess && !err.empty()) return fail(MMF_ERR_HIP, "mmf_bitlinear_bwd: %s", err.c_str());
+    mmf_status r = hip_status(e, "mmf_bitlinear_bwd");
     if (r == MMF_OK) g_path = path;
     return r;
 }

@@ -109,6 +109,26 @@ def test_scan_validation(lib):
     assert lib.mmf_hgrn_scan_fwd(FAKE, FAKE, None, FAKE, None, 1, 4096, 64, 2, None, 0, None) == WORKSPACE
 
 
+def test_bitlinear_bwd_validation(lib):
+    sz = ctypes.c_size_t(0)
+    w = _weight(64, 128)
+    assert lib.mmf_bitlinear_bwd_workspace_size(32, ctypes.byref(w), 0, ctypes.byref(sz)) == OK
+    f32_need = sz.value
+    assert lib.mmf_bitlinear_bwd_workspace_size(32, ctypes.byref(w), 1, ctypes.byref(sz)) == OK
+    assert f32_need > sz.value > 0  # an fp32 dy needs a bf16 copy
+    assert lib.mmf_bitlinear_bwd_workspace_size(-1, ctypes.byref(w), 1, ctypes.byref(sz)) == INVALID
+    x, dy, dx, dw, dg, ws = (FAKE + 65536 * i for i in range(6))
+    call = lib.mmf_bitlinear_bwd
+    big = 1 << 30
+    assert call(None, 1, 32, ctypes.byref(w), 1e-8, dy, 1, dx, 1, dw, dg, ws, big, None) == INVALID
+    assert call(x, 1, 32, ctypes.byref(w), -1.0, dy, 1, dx, 1, dw, dg, ws, big, None) == INVALID
+    assert call(x, 1, 32, ctypes.byref(w), 1e-8, dy, 1, dx, 1, dw, dg, ws, 16, None) == WORKSPACE
+    odd = _weight(60, 128)
+    assert call(x, 1, 32, ctypes.byref(odd), 1e-8, dy, 1, dx, 1, dw, dg, ws, big, None) == UNSUPPORTED
+    wide = _weight(64, 8192 + 16)
+    assert call(x, 1, 32, ctypes.byref(wide), 1e-8, dy, 1, dx, 1, dw, dg, ws, big, None) == UNSUPPORTED
+
+
 def test_scan_bwd_validation(lib):
     f, h, dh, dx, df, h0, gl, dh0 = (FAKE + 256 * i for i in range(8))
     call = lib.mmf_hgrn_scan_bwd

@@ -206,6 +206,66 @@ def test_scan_limits_zero_and_unit_gate(gpu):
     assert_close(h, np.cumsum(x.astype(np.float64), axis=1), 1e-5, "cumsum")
 
 
+BITLINEAR_BWD_CASES = [
+    # m, k, n, x dtype, dy dtype, with gain
+    (3, 64, 32, "f32", "f32", False),
+    (17, 256, 96, "bf16", "bf16", True),
+    (64, 1024, 200, "f32", "bf16", True),
+    (300, 512, 1024, "bf16", "bf16", False),
+    (1000, 2048, 2048, "bf16", "f32", True),   # the 1.3B width
+    (129, 5632, 2048, "bf16", "bf16", False),  # down_proj's shape, ragged row count
+]
+
+
+@pytest.mark.parametrize("m,k,n,xt,dyt,with_gain", BITLINEAR_BWD_CASES)
+def test_bitlinear_bwd_parity(gpu, m, k, n, xt, dyt, with_gain):
+    """dx, dW and dgain against the oracle's straight-through derivative. With a bf16 dy the
+    first product is exact up to fp32 summation order (rtol 1e-4); an fp32 dy and the scaled
+    codes of dW are rounded to bf16 on the way into the products (the bf16 bar, rtol 2e-2)."""
+    import torch
+    mmf = _mmf()
+    x = synth.activations((m, k), 800 + m, xt)
+    w = synth.rng(801 + k).standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    dy = synth.activations((m, n), 802 + n, dyt)
+    gain = (1.0 + 0.1 * synth.rng(803).standard_normal(k)).astype(np.float32) if with_gain else None
+    t, mu = oracle.ternarize(w)
+    rdx, rdw, rdg = oracle.bitlinear_bwd(x, t, mu, dy, gain)
+    pl = mmf.ternary_pack(dev(w, gpu), norm_w=dev(gain, gpu) if with_gain else None)
+    xd = bf16_tensor(x, gpu) if xt == "bf16" else dev(x, gpu)
+    dyd = bf16_tensor(dy, gpu) if dyt == "bf16" else dev(dy, gpu)
+    dx, dw, dg = mmf.bitlinear_bwd(xd, pl, dyd, want_dgain=True, dx_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tight = 1e-4 if dyt == "bf16" else 2e-2
+    assert_close(host(dx), rdx, tight, "dx")
+    assert_close(host(dg), rdg, tight, "dgain")
+    assert_close(host(dw), rdw, 2e-2, "dw")
+    assert "gemm_bf16<du>" in mmf.last_path() and "gemm_bf16<dw>" in mmf.last_path()
+
+
+def test_bitlinear_bwd_outputs_optional_and_empty(gpu):
+    import torch
+    mmf = _mmf()
+    m, k, n = 40, 256, 64
+    x = synth.activations((m, k), 810, "bf16")
+    w = synth.rng(811).standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    dy = synth.activations((m, n), 812, "bf16")
+    t, mu = oracle.ternarize(w)
+    rdx, rdw, _ = oracle.bitlinear_bwd(x, t, mu, dy)
+    pl = mmf.ternary_pack(dev(w, gpu))
+    xd, dyd = bf16_tensor(x, gpu), bf16_tensor(dy, gpu)
+    dx, dw, dg = mmf.bitlinear_bwd(xd, pl, dyd, want_dw=False)
+    assert dw is None and dg is None and dx.dtype == torch.bfloat16
+    assert "gemm_bf16<dw>" not in mmf.last_path()
+    assert_close(host(dx), rdx, 2e-2, "dx (bf16)")
+    dx, dw, _ = mmf.bitlinear_bwd(xd, pl, dyd, want_dx=False)
+    assert dx is None and "gemm_bf16<du>" not in mmf.last_path()
+    assert_close(host(dw), rdw, 2e-2, "dw alone")
+    # no rows: dW and dgain are empty sums
+    _, dw, dg = mmf.bitlinear_bwd(torch.empty((0, k), device=gpu), pl, torch.empty((0, n), device=gpu),
+                                  want_dgain=True)
+    assert not host(dw).any() and not host(dg).any()
+
+
 SCAN_BWD_CASES = [
     # b, t, d, mode, with_h0, with_last
     (1, 1, 64, "recurrent", True, True),
