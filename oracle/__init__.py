@@ -30,7 +30,9 @@ are listed in the project's design notes.
 Beyond the forward pass, for training through the quantisers with a
 straight-through estimator ([R1] list "可复用的模式与技巧"): ``hgrn_scan_bwd``,
 the derivative of the recurrence (reverse time), and ``bitlinear_bwd``, the
-derivative of FusedBitLinear with both quantisers passed straight through.
+derivative of FusedBitLinear with both quantisers passed straight through;
+and for the token-to-token loop of generation, ``embed`` and ``greedy_head``
+(a FusedBitLinear head whose largest exact sum picks the next token).
 
 Precision: every step is binary64 except the two quantisers, which decide
 integers and therefore run in the kernel's precision (binary32 operations,
@@ -221,6 +223,40 @@ def bitlinear_bwd(x: np.ndarray, t: np.ndarray, mu, dy: np.ndarray, gain=None, e
     dx = r[:, None] * g * du - (r ** 3 / k)[:, None] * x64 * c[:, None]
     dgain = np.sum(du * x64 * r[:, None], axis=0)
     return dx, dw, dgain
+
+
+def embed(ids: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Rows of an embedding table for token ids; an id outside [0, vocab) gives a zero row
+    (the token-to-token loop of generation; [R3] section "安裝與初始化：三行指令與一個 config
+    物件": the default config has 32000 tokens, width 2048, 24 layers, and a generation example)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    table = np.asarray(table)
+    out = np.zeros((ids.size, table.shape[1]), dtype=table.dtype)
+    ok = (ids >= 0) & (ids < table.shape[0])
+    out[ok] = table[ids[ok]]
+    return out
+
+
+def first_argmax(acc: np.ndarray) -> np.ndarray:
+    """Per row, the smallest index holding the row's largest value (a plain scan)."""
+    acc = np.asarray(acc)
+    out = np.empty(acc.shape[0], dtype=np.int32)
+    for r in range(acc.shape[0]):
+        best, arg = acc[r, 0], 0
+        for j in range(1, acc.shape[1]):
+            if acc[r, j] > best:
+                best, arg = acc[r, j], j
+        out[r] = arg
+    return out
+
+
+def greedy_head(x: np.ndarray, t: np.ndarray, mu, gain=None, eps: float = 1e-8) -> dict:
+    """Greedy next token from a FusedBitLinear head: the head's logits are acc * dq with one
+    dq > 0 per row, so the largest logit is the largest exact int32 sum acc; ties go to the
+    smallest token id. Returns the head's bitlinear result plus ``tokens`` [m] int32."""
+    r = bitlinear(x, t, mu, gain, eps)
+    r["tokens"] = first_argmax(r["acc"])
+    return r
 
 
 def mixer_gates(i_hat, f_hat):
