@@ -424,6 +424,7 @@ def main():
             if bb != B:
                 by_batch[str(bb)] = round(decode_us_per_layer(mmf, torch, layers, bb, d, dev, seed), 2)
     by_batch = dict(sorted(by_batch.items(), key=lambda kv: int(kv[0])))
+    generate = [measure_generate(mmf, torch, layers, bb, d, dev, seed) for bb in (1, B)] if D else None
 
     cpu = None
     if args.cpu_baseline:
@@ -460,6 +461,7 @@ def main():
         "decode_us_per_layer_by_batch": by_batch,
         "scan_bwd": scan_bwd,
         "bitlinear_bwd": bitlinear_bwd,
+        "generate": generate,
         "cpu_baseline": cpu,
         "kernels": breakdown,
         "kernel_ms_per_step": round(total_kernel_ms, 3),
@@ -525,6 +527,56 @@ def measure_bitlinear_bwd(mmf, torch, lin, m: int, dev, launches: int = 5) -> di
                 kernels_us=kernels, gemm_achieved=round(tf, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                 gemm_frac=round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                 note="products through rocBLAS (bf16, fp32 accumulation); the rest hand-written")
+
+
+def measure_generate(mmf, torch, layers, b: int, d: int, dev, seed: int, vocab: int = 32000,
+                     steps: int = 64) -> dict:
+    """The token-to-token loop at batch b: embedding rows of a seeded bf16 table -> one decode
+    step of every block -> greedy FusedBitLinear head over `vocab` tokens, whose tokens feed the
+    next step on the device; one loop step captured in a HIP graph and replayed `steps` times."""
+    L = len(layers)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 7919 + b)
+    table = torch.randn((vocab, d), device=dev, generator=gen).to(torch.bfloat16)
+    w_head = torch.randn((vocab, d), device=dev, generator=gen) * 0.02
+    head = mmf.ternary_pack(w_head)
+    del w_head
+    ids = torch.randint(0, vocab, (b,), device=dev, dtype=torch.int32, generator=gen)
+    hs = torch.randn((L, b, d), device=dev, generator=gen)
+    x = torch.empty((b, d), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty_like(x) for _ in range(2)]
+    ws = torch.empty(mmf.layer_workspace_size(layers[0], b, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        mmf.embed(ids, table, out=x)
+        y = x
+        for l in range(L):
+            y = mmf.layer_decode_step(layers[l], y, hs[l], out=outs[l % 2], ws=ws)
+        mmf.greedy_head(y, head, tokens=ids)
+
+    step()
+    torch.cuda.synchronize()
+    mmf.timing_enable(True)
+    y = outs[(L - 1) % 2]
+    for _ in range(4):
+        mmf.greedy_head(y, head, tokens=ids)
+    torch.cuda.synchronize()
+    mmf.timing_enable(False)
+    head_us = sum(r[4] for r in mmf.timing_collect()) * 1000.0 / 4
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    return dict(batch=b, vocab=vocab, layers=L, us_per_token_step=round(us, 1),
+                tokens_per_s=round(b / (us / 1e6), 1), head_us_eager=round(head_us, 1),
+                note="embed + %d decode blocks + greedy ternary head per step, HIP graph, tokens stay on the device" % L)
 
 
 def decode_us_per_layer(mmf, torch, layers, b: int, d: int, dev, seed: int, steps: int = 32) -> float:

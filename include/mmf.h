@@ -186,6 +186,32 @@ mmf_status mmf_bitlinear_bwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
                              float *dw, float *dgain, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * mmf_embed -- embedding rows for token ids, the entry of the token-to-token
+ * loop of generation ([R3] section "安裝與初始化：三行指令與一個 config 物件":
+ * a 32000-token vocabulary, a generation example):
+ *   out[i][:] = table[ids[i]][:]      (a zero row when ids[i] is outside [0, vocab))
+ *  ids : [count] int32 (device); table : [vocab][d] in dtype tt; out : [count][d]
+ *  in dtype tt. A row must be a whole number of 16 bytes. count may be 0.
+ *  Errors: INVALID_ARG, UNSUPPORTED.
+ */
+mmf_status mmf_embed(const int32_t *ids, int64_t count, const void *table, mmf_dtype tt, int64_t vocab,
+                     int32_t d, void *out, hipStream_t stream);
+
+/*
+ * mmf_greedy_head -- the next token of each row from a FusedBitLinear head
+ * (read as ternary, like every projection of the model): the head's logits are
+ * acc_n / (s * sw) with one positive factor per row, so the greedy token is the
+ * smallest n holding the largest exact int32 sum acc_n.
+ *  x : [b][k] in dtype xt (the last block's output); head : [vocab][k] packed,
+ *  vocab % 4 == 0; tokens : [b] int32; logits : [b][vocab] fp32 or NULL.
+ *  b may be 0. Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE.
+ */
+mmf_status mmf_greedy_head_workspace_size(int64_t b, const mmf_ternary_weight *head, size_t *bytes);
+mmf_status mmf_greedy_head(const void *x, mmf_dtype xt, int64_t b, const mmf_ternary_weight *head,
+                           float eps, int32_t *tokens, float *logits, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
  * mmf_hgrn_scan_fwd -- the HGRN recurrence ([R1] table "创新之处"), fp32:
  *   h[b][t][c] = f[b][t][c] * h[b][t-1][c] + x[b][t][c],   h[b][-1][c] = h0[b][c]
  *  x, f, h : [b][t][d] fp32; h0 : [b][d] or NULL (zeros); h_last : [b][d] or NULL.

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmmf.so")
 
 __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
-    "ternary_pack", "bitlinear_fwd", "bitlinear_bwd", "hgrn_scan_fwd", "hgrn_scan_bwd", "layer_fwd",
+    "ternary_pack", "bitlinear_fwd", "bitlinear_bwd", "embed", "greedy_head", "hgrn_scan_fwd", "hgrn_scan_bwd",
+    "layer_fwd",
     "layer_decode_step",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
     "set_decode_kernel", "decode_expired_waits", "DECODE_KERNELS",
@@ -29,6 +30,7 @@ SYMBOLS = [
     "mmf_ternary_pack_workspace_size", "mmf_ternary_pack",
     "mmf_bitlinear_workspace_size", "mmf_bitlinear_fwd",
     "mmf_bitlinear_bwd_workspace_size", "mmf_bitlinear_bwd",
+    "mmf_embed", "mmf_greedy_head_workspace_size", "mmf_greedy_head",
     "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd", "mmf_hgrn_scan_bwd",
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
     "mmf_set_decode_kernel", "mmf_decode_expired_waits",
@@ -93,6 +95,9 @@ def load():
                                                      ctypes.POINTER(SZ)]
     lib.mmf_bitlinear_bwd.argtypes = [P, ctypes.c_int, I64, ctypes.POINTER(CTernaryWeight), F32, P, ctypes.c_int,
                                       P, ctypes.c_int, P, P, P, SZ, P]
+    lib.mmf_embed.argtypes = [P, I64, P, ctypes.c_int, I64, I32, P, P]
+    lib.mmf_greedy_head_workspace_size.argtypes = [I64, ctypes.POINTER(CTernaryWeight), ctypes.POINTER(SZ)]
+    lib.mmf_greedy_head.argtypes = [P, ctypes.c_int, I64, ctypes.POINTER(CTernaryWeight), F32, P, P, P, SZ, P]
     lib.mmf_hgrn_scan_workspace_size.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.mmf_hgrn_scan_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P, SZ, P]
     lib.mmf_hgrn_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
@@ -258,6 +263,38 @@ def bitlinear_bwd(x, w: PackedLinear, dy, eps: float = 1e-8, want_dx=True, want_
                                  _dtype_code(dy.dtype), _ptr(dx), _dtype_code(dx.dtype if dx is not None else x.dtype),
                                  _ptr(dw), _ptr(dgain), _ptr(ws), ws.numel(), _stream()))
     return dx, dw, dgain
+
+
+def embed(ids, table, out=None):
+    """Rows of an embedding table [vocab, d] (fp32 or bf16) for int32 token ids (mmf_embed);
+    ids outside [0, vocab) give zero rows."""
+    torch = _torch()
+    lib = load()
+    if ids.dtype != torch.int32 or not ids.is_contiguous() or not table.is_contiguous() or table.dim() != 2:
+        raise TypeError("ids must be contiguous int32 and table a contiguous [vocab, d] tensor")
+    vocab, d = table.shape
+    out = out if out is not None else torch.empty((ids.numel(), d), dtype=table.dtype, device=table.device)
+    _check(lib.mmf_embed(_ptr(ids), ids.numel(), _ptr(table), _dtype_code(table.dtype), vocab, d, _ptr(out),
+                         _stream()))
+    return out
+
+
+def greedy_head(x, head: PackedLinear, eps: float = 1e-8, tokens=None, logits=None, ws=None):
+    """Next token of each row of x [b, k] from a FusedBitLinear head (mmf_greedy_head): the smallest
+    id of the largest exact sum. Returns tokens [b] int32 (logits [b, vocab] fp32 filled if given)."""
+    torch = _torch()
+    lib = load()
+    if not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous [b, k] tensor")
+    b = x.shape[0]
+    tokens = tokens if tokens is not None else torch.empty((b,), dtype=torch.int32, device=x.device)
+    cw = head.c()
+    need = SZ(0)
+    _check(lib.mmf_greedy_head_workspace_size(b, ctypes.byref(cw), ctypes.byref(need)))
+    ws = _workspace(need.value, x.device, ws)
+    _check(lib.mmf_greedy_head(_ptr(x), _dtype_code(x.dtype), b, ctypes.byref(cw), F32(eps), _ptr(tokens),
+                               _ptr(logits), _ptr(ws), ws.numel(), _stream()))
+    return tokens
 
 
 def hgrn_scan_fwd(x, f, h0=None, mode: str = "auto", out=None, h_last=None, ws=None):

@@ -137,4 +137,11 @@ hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t st);  // a fill kern
 hipError_t gemm_bf16_f32(const uint16_t *a, bool trans_a, const uint16_t *b, int64_t rows, int64_t cols, int64_t inner,
                          float *c, hipStream_t st, std::string *err);
 
+// Generation (k_generate.hip): embedding rows (16-byte pieces of a row of
+// row_bytes; zero rows for ids outside [0, vocab)), and per row of an int32
+// matrix [m][n] (n % 4 == 0) the smallest index of its largest value.
+hipError_t launch_embed(const int32_t *ids, int64_t count, const void *table, int64_t vocab, int64_t row_bytes,
+                        void *out, hipStream_t st);
+hipError_t launch_argmax_rows(const int32_t *acc, int64_t m, int64_t n, int32_t *tokens, hipStream_t st);
+
 }  // namespace mmf

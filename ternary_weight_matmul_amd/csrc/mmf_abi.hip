@@ -541,6 +541,92 @@ mmf_status mmf_bitlinear_bwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
     return r;
 }
 
+// --------------------------------------------------------------- generation --
+mmf_status mmf_embed(const int32_t *ids, int64_t count, const void *table, mmf_dtype tt, int64_t vocab, int32_t d,
+                     void *out, hipStream_t stream) {
+    if (!valid_dtype(tt)) return fail(MMF_ERR_INVALID_ARG, "bad dtype");
+    if (count < 0 || vocab <= 0 || d <= 0) return fail(MMF_ERR_INVALID_ARG, "count >= 0, vocab > 0 and d > 0 required");
+    const int64_t row_bytes = (int64_t)d * (tt == MMF_F32 ? 4 : 2);
+    if (row_bytes % 16) return fail(MMF_ERR_UNSUPPORTED, "a row of %d elements is not a whole number of 16 bytes", d);
+    if (count > 0 && (!ids || !table || !out)) return fail(MMF_ERR_INVALID_ARG, "ids, table and out must be non-NULL");
+    if (!aligned16(table) || !aligned16(out)) return fail(MMF_ERR_INVALID_ARG, "table and out must be 16-byte aligned");
+    if (count > INT32_MAX) return fail(MMF_ERR_UNSUPPORTED, "count beyond 2^31 rows");
+    std::string path = "embed;";
+    hipError_t e = timed("embed", count, d, d, stream,
+                         [&] { return launch_embed(ids, count, table, vocab, row_bytes, out, stream); });
+    mmf_status r = hip_status(e, "mmf_embed");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+struct GreedyWs {
+    int8_t *codes;
+    float *s;
+    int32_t *sumq, *acc;
+    float *logits;
+};
+
+size_t greedy_plan(Carver &c, int64_t b, int n, int k, GreedyWs *o) {
+    GreedyWs w;
+    w.codes = c.take<int8_t>((size_t)b * k);
+    w.s = c.take<float>((size_t)b);
+    w.sumq = c.take<int32_t>((size_t)b);
+    w.acc = c.take<int32_t>((size_t)b * n);
+    w.logits = c.take<float>((size_t)b * n);
+    if (o) *o = w;
+    return c.off;
+}
+
+mmf_status mmf_greedy_head_workspace_size(int64_t b, const mmf_ternary_weight *head, size_t *bytes) {
+    if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
+    mmf_status st = check_weight(head, "head");
+    if (st != MMF_OK) return st;
+    if (b < 0) return fail(MMF_ERR_INVALID_ARG, "b=%lld < 0", (long long)b);
+    Carver c(nullptr);
+    *bytes = greedy_plan(c, b, head->n, head->k, nullptr);
+    return MMF_OK;
+}
+
+mmf_status mmf_greedy_head(const void *x, mmf_dtype xt, int64_t b, const mmf_ternary_weight *head, float eps,
+                           int32_t *tokens, float *logits, void *ws, size_t ws_bytes, hipStream_t stream) {
+    size_t need = 0;
+    mmf_status st = mmf_greedy_head_workspace_size(b, head, &need);
+    if (st != MMF_OK) return st;
+    if (!valid_dtype(xt)) return fail(MMF_ERR_INVALID_ARG, "bad dtype");
+    if (!(eps >= 0.0f)) return fail(MMF_ERR_INVALID_ARG, "eps must be >= 0");
+    if (head->n % 4) return fail(MMF_ERR_UNSUPPORTED, "vocabulary %d is not a multiple of 4", head->n);
+    if (b > 0 && (!x || !tokens)) return fail(MMF_ERR_INVALID_ARG, "x and tokens must be non-NULL");
+    if (!aligned16(x) || !aligned16(logits)) return fail(MMF_ERR_INVALID_ARG, "x and logits must be 16-byte aligned");
+    if (b > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    if (b == 0) {
+        g_path = "empty";
+        g_err.clear();
+        return MMF_OK;
+    }
+    Carver c(ws);
+    GreedyWs G;
+    greedy_plan(c, b, head->n, head->k, &G);
+    std::string path;
+    // the head: FusedBitLinear with its exact int32 sums kept
+    hipError_t e = t_norm_quant(x, act(xt), b, head->k, head->norm_w, eps, G.codes, G.s, G.sumq, stream, &path);
+    if (e == hipSuccess) {
+        ContractArgs a{};
+        for (int q = 0; q < 3; ++q) { a.A[q] = G.codes; a.s[q] = G.s; a.sumq[q] = G.sumq; a.B[q] = head->packed; a.mu[q] = head->mu; }
+        a.m = b; a.nc = head->n; a.k = head->k;
+        a.out0 = logits ? logits : G.logits; a.out_type = ACT_F32;
+        a.acc_probe = G.acc;
+        e = t_contract(a, EPI_LINEAR, 1, true, stream, &path);
+    }
+    if (e == hipSuccess)
+        e = timed("argmax_rows", b, head->n, head->n, stream,
+                  [&] { return launch_argmax_rows(G.acc, b, head->n, tokens, stream); });
+    path += "argmax_rows;";
+    mmf_status r = hip_status(e, "mmf_greedy_head");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
 mmf_status mmf_hgrn_scan_workspace_size(int64_t b, int64_t t, int64_t d, mmf_scan_mode mode, size_t *bytes) {
     if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
     if (b < 0 || t < 0 || d <= 0) return fail(MMF_ERR_INVALID_ARG, "b, t >= 0 and d > 0 required");

@@ -129,6 +129,22 @@ def test_bitlinear_bwd_validation(lib):
     assert call(x, 1, 32, ctypes.byref(wide), 1e-8, dy, 1, dx, 1, dw, dg, ws, big, None) == UNSUPPORTED
 
 
+def test_generation_validation(lib):
+    ids, table, out, x, tok, ws = (FAKE + 65536 * i for i in range(6))
+    assert lib.mmf_embed(ids, 4, table, 1, 1000, 0, out, None) == INVALID          # d = 0
+    assert lib.mmf_embed(ids, 4, table, 1, 1000, 4, out, None) == UNSUPPORTED      # 8-byte rows
+    assert lib.mmf_embed(None, 4, table, 1, 1000, 64, out, None) == INVALID
+    assert lib.mmf_embed(None, 0, None, 1, 1000, 64, None, None) == OK             # nothing to do
+    sz = ctypes.c_size_t(0)
+    head = _weight(1000, 256)
+    assert lib.mmf_greedy_head_workspace_size(8, ctypes.byref(head), ctypes.byref(sz)) == OK and sz.value > 0
+    odd = _weight(1002, 256)
+    big = 1 << 30
+    assert lib.mmf_greedy_head(x, 1, 8, ctypes.byref(odd), 1e-8, tok, None, ws, big, None) == UNSUPPORTED
+    assert lib.mmf_greedy_head(x, 1, 8, ctypes.byref(head), 1e-8, None, None, ws, big, None) == INVALID
+    assert lib.mmf_greedy_head(x, 1, 8, ctypes.byref(head), 1e-8, tok, None, ws, 16, None) == WORKSPACE
+
+
 def test_scan_bwd_validation(lib):
     f, h, dh, dx, df, h0, gl, dh0 = (FAKE + 256 * i for i in range(8))
     call = lib.mmf_hgrn_scan_bwd

@@ -266,6 +266,90 @@ def test_bitlinear_bwd_outputs_optional_and_empty(gpu):
     assert not host(dw).any() and not host(dg).any()
 
 
+def test_embed_rows(gpu):
+    import torch
+    mmf = _mmf()
+    for dtype in ("f32", "bf16"):
+        table = synth.activations((1000, 272), 820, dtype)
+        ids = np.array([5, 0, 999, -1, 1000, 5, 123], dtype=np.int32)
+        td = bf16_tensor(table, gpu) if dtype == "bf16" else dev(table, gpu)
+        out = mmf.embed(dev(ids, gpu), td)
+        assert_equal(host(out), oracle.embed(ids, table), "embed " + dtype)
+    assert mmf.embed(torch.empty((0,), dtype=torch.int32, device=gpu), td).shape == (0, 272)
+
+
+GREEDY_CASES = [
+    # b, k, vocab, x dtype, with gain
+    (1, 2048, 32000, "bf16", False),   # the 1.3B head: width 2048, 32000 tokens
+    (16, 2048, 32000, "bf16", True),
+    (5, 256, 1000, "f32", False),
+    (70, 512, 4096, "bf16", False),    # above the GEMV limit: tiled contraction
+]
+
+
+@pytest.mark.parametrize("b,k,vocab,xt,with_gain", GREEDY_CASES)
+def test_greedy_head_parity(gpu, b, k, vocab, xt, with_gain):
+    """Tokens bit-exact (the first largest exact sum); logits within the fp32 tolerance."""
+    import torch
+    mmf = _mmf()
+    x = synth.activations((b, k), 830 + b, xt)
+    w = synth.rng(831 + vocab).standard_normal((vocab, k), dtype=np.float32) * np.float32(0.02)
+    gain = (1.0 + 0.1 * synth.rng(832).standard_normal(k)).astype(np.float32) if with_gain else None
+    t, mu = oracle.ternarize(w)
+    ref = oracle.greedy_head(x, t, mu, gain)
+    pl = mmf.ternary_pack(dev(w, gpu), norm_w=dev(gain, gpu) if with_gain else None)
+    xd = bf16_tensor(x, gpu) if xt == "bf16" else dev(x, gpu)
+    logits = torch.empty((b, vocab), device=gpu)
+    tokens = mmf.greedy_head(xd, pl, logits=logits)
+    assert_equal(host(tokens), ref["tokens"], "tokens")
+    assert_close(host(logits), ref["y"], 1e-4, "logits")
+    assert "argmax_rows" in mmf.last_path()
+
+
+def test_greedy_head_ties_go_to_the_smallest_token(gpu):
+    mmf = _mmf()
+    k, vocab = 256, 1000
+    w = synth.rng(840).standard_normal((vocab, k), dtype=np.float32) * np.float32(0.02)
+    x = synth.activations((3, k), 841)
+    x[1] = 0.0  # a zero row: every sum is 0
+    w_same = np.repeat(w[:1], vocab, axis=0)  # identical rows: every sum equal
+    for wt, want in ((w, None), (w_same, 0)):
+        t, mu = oracle.ternarize(wt)
+        ref = oracle.greedy_head(x, t, mu)["tokens"]
+        got = host(mmf.greedy_head(dev(x, gpu), mmf.ternary_pack(dev(wt, gpu))))
+        assert_equal(got, ref, "tokens")
+        assert got[1] == 0
+        if want is not None:
+            assert np.all(got == want)
+
+
+def test_generate_loop_stage_by_stage(gpu):
+    """The token-to-token loop of a two-block model: embed -> decode steps -> greedy head. At
+    every step the embedding is checked bit for bit and the head's tokens are checked bit for bit
+    against the oracle fed with the GPU's last block output; the tokens feed the next step."""
+    import torch
+    mmf = _mmf()
+    d, inner, vocab, b, L = 256, 512, 1000, 3, 2
+    table = synth.activations((vocab, d), 850, "bf16")
+    pairs = [make_pair(d, inner, 851 + l, gpu) for l in range(L)]
+    w_head = synth.rng(853).standard_normal((vocab, d), dtype=np.float32) * np.float32(0.02)
+    t_head, mu_head = oracle.ternarize(w_head)
+    head = mmf.ternary_pack(dev(w_head, gpu))
+    hs = [dev(synth.activations((b, d), 854 + l), gpu) for l in range(L)]
+    td = bf16_tensor(table, gpu)
+    ids = dev(np.array([1, 500, 999], dtype=np.int32), gpu)
+    for step in range(4):
+        x = mmf.embed(ids, td)
+        assert_equal(host(x), oracle.embed(host(ids), table), "embed step %d" % step)
+        y = x
+        for l in range(L):
+            y = mmf.layer_decode_step(pairs[l][1], y, hs[l])
+        nxt = mmf.greedy_head(y, head)
+        ref = oracle.greedy_head(host(y), t_head, mu_head)["tokens"]
+        assert_equal(host(nxt), ref, "tokens step %d" % step)
+        ids = nxt
+
+
 SCAN_BWD_CASES = [
     # b, t, d, mode, with_h0, with_last
     (1, 1, 64, "recurrent", True, True),
