@@ -811,6 +811,56 @@ def _graph_replays(P, x, h0, mark, gpu):
         mmf.layer_fwd(P, x[:, None, :].contiguous(), None)  # unrelated eager work between replays
 
 
+@pytest.mark.parametrize("b", [16, 64])
+def test_decode_separate_graph_replays(gpu, b):
+    """The default decode step (the path the benchmark replays) at the 1.3B shape: captured once,
+    replayed several times with eager work between, every replay equals the eager result."""
+    _, P = make_pair(2048, 5632, 940 + b, gpu)
+    x = bf16_tensor(synth.activations((b, 2048), 941, "bf16"), gpu)
+    h0 = dev(synth.activations((b, 2048), 942), gpu)
+    _graph_replays(P, x, h0, "tgemv<", gpu)
+
+
+def test_generate_step_graph_replays(gpu):
+    """One token-to-token step (embed, two blocks, greedy head) captured and replayed from the
+    same ids and states: every replay gives the eager tokens and states."""
+    import torch
+    mmf = _mmf()
+    d, inner, vocab, b, L = 256, 512, 1000, 4, 2
+    table = bf16_tensor(synth.activations((vocab, d), 950, "bf16"), gpu)
+    Ps = [make_pair(d, inner, 951 + l, gpu)[1] for l in range(L)]
+    head = mmf.ternary_pack(dev(synth.rng(953).standard_normal((vocab, d), dtype=np.float32) * np.float32(0.02), gpu))
+    ids0 = dev(np.array([3, 77, 500, 999], dtype=np.int32), gpu)
+    h0 = [dev(synth.activations((b, d), 954 + l), gpu) for l in range(L)]
+    ids, hs = ids0.clone(), [h.clone() for h in h0]
+    x = torch.empty((b, d), dtype=torch.bfloat16, device=gpu)
+    outs = [torch.empty_like(x) for _ in range(2)]
+    ws = torch.empty(mmf.layer_workspace_size(Ps[0], b, 1), dtype=torch.uint8, device=gpu)
+
+    def step():
+        mmf.embed(ids, table, out=x)
+        y = x
+        for l in range(L):
+            y = mmf.layer_decode_step(Ps[l], y, hs[l], out=outs[l % 2], ws=ws)
+        mmf.greedy_head(y, head, tokens=ids)
+
+    step()
+    torch.cuda.synchronize()
+    ref_ids, ref_hs = ids.clone(), [h.clone() for h in hs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        ids.copy_(ids0)
+        for h, h_init in zip(hs, h0):
+            h.copy_(h_init)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ref_ids)
+        assert all(torch.equal(h, r) for h, r in zip(hs, ref_hs))
+        mmf.bitlinear_fwd(x, head)  # unrelated eager work between replays
+
+
 def test_decode_xcd_kernel_unsupported_shapes(gpu):
     """Forcing the one-XCD kernel where it does not apply is an error, never a silent fallback."""
     mmf = _mmf()
