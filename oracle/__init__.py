@@ -391,6 +391,73 @@ def layer_decode_step(L: Layer, x: np.ndarray, h: np.ndarray) -> dict:
     return dict(out=r["out"][:, 0, :], h=r["h_last"], stages=r)
 
 
+def dsilu(z):
+    """d SiLU(z) / dz = sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    z = np.asarray(z, dtype=np.float64)
+    sg = sigmoid(z)
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def layer_backward(L: Layer, x: np.ndarray, dout: np.ndarray, h0: Optional[np.ndarray] = None,
+                   dh_last: Optional[np.ndarray] = None) -> dict:
+    """Derivative of ``layer_forward`` with straight-through quantisers, binary64, for a loss
+    with dL/dout = dout and dL/dh_last = dh_last. Every FusedBitLinear goes through
+    ``bitlinear_bwd``; the rest is the chain rule through the block, last step first:
+    MLP (SiLU product), o_proj, g_norm (RMSNorm of h times weight times SiLU(g)), the
+    recurrence (``hgrn_scan_bwd``), the gates f = sigmoid(f^), x~ = (1 - f) SiLU(i^), and the
+    i/f/g projections, whose input derivatives add to the residual path's. Returns dx, dh0,
+    the latent weights' derivatives ``dw``, the gains' ``dgain`` (derivative at 1 where a
+    projection has no gain), ``dg_norm_w`` and the intermediate derivatives."""
+    x = np.asarray(x, dtype=np.float64)
+    b, t, d = x.shape
+    m, inner, eps = b * t, L.inner, L.eps
+    r = layer_forward(L, x, h0)
+    dO = np.asarray(dout, dtype=np.float64).reshape(m, d)
+    # MLP: out = x1 + down(z), z = SiLU(a) * b with [a | b] = gate(x1)
+    x1 = r["x1"].reshape(m, d)
+    z = r["z"].reshape(m, inner)
+    dz, dw_down, dg_down = bitlinear_bwd(z, L.down.t, L.down.mu, dO, L.down.gain, eps)
+    ab = L.gate(x1, eps)["y"]
+    a, bb = ab[:, :inner], ab[:, inner:]
+    da = dz * bb * dsilu(a)
+    db = dz * silu(a)
+    dx1_gate, dw_gate, dg_gate = bitlinear_bwd(x1, L.gate.t, L.gate.mu, np.concatenate([da, db], axis=1),
+                                               L.gate.gain, eps)
+    dx1 = dO + dx1_gate
+    # o_proj: x1 = x + o(u)
+    u = r["u"].reshape(m, d)
+    du, dw_o, dg_o = bitlinear_bwd(u, L.o.t, L.o.mu, dx1, L.o.gain, eps)
+    # g_norm: u = (h r_h) * w * SiLU(g^)
+    h = r["h"].reshape(m, d)
+    gh = r["g_hat"].reshape(m, d)
+    rh = 1.0 / np.sqrt(np.mean(h * h, axis=1) + np.float64(np.float32(eps)))
+    nrm = h * rh[:, None]
+    w = np.ones(d) if L.g_norm_w is None else np.asarray(L.g_norm_w, dtype=np.float64)
+    sg = silu(gh)
+    dn = du * w * sg
+    dg_norm_w = np.sum(du * nrm * sg, axis=0)
+    dg_hat = du * nrm * w * dsilu(gh)
+    c = np.sum(h * dn, axis=1)
+    dh = rh[:, None] * dn - (rh ** 3 / d)[:, None] * h * c[:, None]
+    # the recurrence, then the gates
+    dxt, df, dh0 = hgrn_scan_bwd(r["f"], r["h"], dh.reshape(b, t, d), h0, dh_last)
+    f, ih = r["f"].reshape(m, d), r["i_hat"].reshape(m, d)
+    dxt, df = dxt.reshape(m, d), df.reshape(m, d)
+    df_hat = (df - dxt * silu(ih)) * f * (1.0 - f)
+    di_hat = dxt * (1.0 - f) * dsilu(ih)
+    # i/f/g projections of x, plus the residual path
+    X = x.reshape(m, d)
+    dx_i, dw_i, dg_i = bitlinear_bwd(X, L.i.t, L.i.mu, di_hat, L.i.gain, eps)
+    dx_f, dw_f, dg_f = bitlinear_bwd(X, L.f.t, L.f.mu, df_hat, L.f.gain, eps)
+    dx_g, dw_g, dg_g = bitlinear_bwd(X, L.g.t, L.g.mu, dg_hat, L.g.gain, eps)
+    dx = dx1 + dx_i + dx_f + dx_g
+    return dict(dx=dx.reshape(b, t, d), dh0=dh0,
+                dw=dict(i=dw_i, f=dw_f, g=dw_g, o=dw_o, gate=dw_gate, down=dw_down),
+                dgain=dict(i=dg_i, f=dg_f, g=dg_g, o=dg_o, gate=dg_gate, down=dg_down),
+                dg_norm_w=dg_norm_w, dz=dz, da=da, db=db, dx1=dx1, du=du, dh=dh, dxt=dxt, df=df,
+                di_hat=di_hat, df_hat=df_hat, dg_hat=dg_hat)
+
+
 def make_layer(latent: dict, gains: Optional[dict] = None, eps: float = 1e-8) -> Layer:
     """Ternarise a dict of latent fp32 weights {i,f,g,o,gate,down} (+ optional gains)."""
     gains = gains or {}
