@@ -418,6 +418,7 @@ def main():
     # decode step at the other batch sizes of the 1.3B decode workload (graph-replayed)
     scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev) if T > 0 else None
     bitlinear_bwd = measure_bitlinear_bwd(mmf, torch, layers[0].o, B * T, dev) if T > 0 else None
+    layer_bwd = measure_layer_bwd(mmf, torch, layers[0], B, T, d, dev) if T > 0 else None
     by_batch = {str(B): round(decode_ms * 1000 / D / L, 2)} if D else {}
     if D and graph is not None:
         for bb in (1, 64):
@@ -461,6 +462,7 @@ def main():
         "decode_us_per_layer_by_batch": by_batch,
         "scan_bwd": scan_bwd,
         "bitlinear_bwd": bitlinear_bwd,
+        "layer_bwd": layer_bwd,
         "generate": generate,
         "cpu_baseline": cpu,
         "kernels": breakdown,
@@ -527,6 +529,28 @@ def measure_bitlinear_bwd(mmf, torch, lin, m: int, dev, launches: int = 5) -> di
                 kernels_us=kernels, gemm_achieved=round(tf, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                 gemm_frac=round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                 note="products through rocBLAS (bf16, fp32 accumulation); the rest hand-written")
+
+
+def measure_layer_bwd(mmf, torch, layer, b: int, t: int, d: int, dev, launches: int = 2) -> dict:
+    """The block's derivative (mmf_layer_bwd: the forward recomputed, then every derivative, all
+    weight and gain derivatives) on seeded bf16 x and dout of b x t tokens, timed with events."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(43)
+    x = torch.randn((b, t, d), device=dev, generator=gen).to(torch.bfloat16)
+    dout = torch.randn((b, t, d), device=dev, generator=gen).to(torch.bfloat16)
+    res = mmf.layer_bwd(layer, x, dout, want_gains=True)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(launches):
+        res = mmf.layer_bwd(layer, x, dout, want_gains=True)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / launches
+    del x, dout, res
+    return dict(shape="b=%d t=%d d=%d" % (b, t, d), ms_per_call=round(ms, 2),
+                tokens_per_s=round(b * t / (ms / 1000), 1),
+                note="forward recomputed inside; products of the derivative through rocBLAS (bf16)")
 
 
 def measure_generate(mmf, torch, layers, b: int, d: int, dev, seed: int, vocab: int = 32000,

@@ -212,6 +212,35 @@ mmf_status mmf_greedy_head(const void *x, mmf_dtype xt, int64_t b, const mmf_ter
                            hipStream_t stream);
 
 /*
+ * mmf_layer_bwd -- derivative of mmf_layer_fwd with straight-through quantisers
+ * (as mmf_bitlinear_bwd) for a loss with dL/dout = dout and dL/dh_last =
+ * dh_last (or NULL: 0). The forward is run again from x and h0, keeping the
+ * pre-activations; then, last step first: down_proj, the SiLU product, gate_proj
+ * plus the residual, o_proj, g_norm (RMSNorm of h times weight times SiLU(g)),
+ * the recurrence (mmf_hgrn_scan_bwd), the gates f = sigmoid(f^),
+ * x~ = (1 - f) SiLU(i^), and i/f/g, whose input derivatives add to the
+ * residual's.
+ *  x, dout : [b][t][d] in dtype act; h0, dh_last : [b][d] fp32 or NULL.
+ *  grads : dx [b][t][d] fp32 (required); dh0 [b][d]; dw[q] [n][k] and dgain[q]
+ *  [k] for q = i, f, g, o, gate, down; dg_norm_w [d] -- each fp32 or NULL.
+ *  mode picks the scan kernels of the forward's recompute and of the
+ *  derivative. Errors: INVALID_ARG, UNSUPPORTED (d, inner beyond 8192 or not
+ *  multiples of 8), WORKSPACE, HIP.
+ */
+typedef struct {
+    float *dx;
+    float *dh0;
+    float *dw[6];
+    float *dgain[6];
+    float *dg_norm_w;
+} mmf_layer_grads;
+
+mmf_status mmf_layer_bwd_workspace_size(const mmf_layer_weights *w, int64_t b, int64_t t, size_t *bytes);
+mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *dout, mmf_dtype act,
+                         int64_t b, int64_t t, const float *h0, const float *dh_last, mmf_scan_mode mode,
+                         const mmf_layer_grads *grads, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * mmf_hgrn_scan_fwd -- the HGRN recurrence ([R1] table "创新之处"), fp32:
  *   h[b][t][c] = f[b][t][c] * h[b][t-1][c] + x[b][t][c],   h[b][-1][c] = h0[b][c]
  *  x, f, h : [b][t][d] fp32; h0 : [b][d] or NULL (zeros); h_last : [b][d] or NULL.

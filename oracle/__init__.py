@@ -399,7 +399,7 @@ def dsilu(z):
 
 
 def layer_backward(L: Layer, x: np.ndarray, dout: np.ndarray, h0: Optional[np.ndarray] = None,
-                   dh_last: Optional[np.ndarray] = None) -> dict:
+                   dh_last: Optional[np.ndarray] = None, stages: Optional[dict] = None) -> dict:
     """Derivative of ``layer_forward`` with straight-through quantisers, binary64, for a loss
     with dL/dout = dout and dL/dh_last = dh_last. Every FusedBitLinear goes through
     ``bitlinear_bwd``; the rest is the chain rule through the block, last step first:
@@ -407,17 +407,26 @@ def layer_backward(L: Layer, x: np.ndarray, dout: np.ndarray, h0: Optional[np.nd
     recurrence (``hgrn_scan_bwd``), the gates f = sigmoid(f^), x~ = (1 - f) SiLU(i^), and the
     i/f/g projections, whose input derivatives add to the residual path's. Returns dx, dh0,
     the latent weights' derivatives ``dw``, the gains' ``dgain`` (derivative at 1 where a
-    projection has no gain), ``dg_norm_w`` and the intermediate derivatives."""
+    projection has no gain), ``dg_norm_w`` and the intermediate derivatives.
+
+    ``stages`` (optional) supplies the forward values the chain is evaluated at -- i_hat, f, g
+    (as g_norm saw it), h, u, x1, ab (= [a | b]) and z, each [b*t, ...] -- in place of the
+    oracle's own forward, so that a derivative can be checked at another implementation's
+    forward values (its quantisers then see the same inputs)."""
     x = np.asarray(x, dtype=np.float64)
     b, t, d = x.shape
     m, inner, eps = b * t, L.inner, L.eps
-    r = layer_forward(L, x, h0)
+    if stages is None:
+        r = layer_forward(L, x, h0)
+        st = dict(i_hat=r["i_hat"], f=r["f"], g=r["g_hat"], h=r["h"], u=r["u"], x1=r["x1"], z=r["z"])
+        st["ab"] = L.gate(np.asarray(r["x1"]).reshape(m, d), eps)["y"]
+    else:
+        st = stages
+    st = {k: np.asarray(v, dtype=np.float64).reshape(m, -1) for k, v in st.items()}
     dO = np.asarray(dout, dtype=np.float64).reshape(m, d)
     # MLP: out = x1 + down(z), z = SiLU(a) * b with [a | b] = gate(x1)
-    x1 = r["x1"].reshape(m, d)
-    z = r["z"].reshape(m, inner)
+    x1, z, ab = st["x1"], st["z"], st["ab"]
     dz, dw_down, dg_down = bitlinear_bwd(z, L.down.t, L.down.mu, dO, L.down.gain, eps)
-    ab = L.gate(x1, eps)["y"]
     a, bb = ab[:, :inner], ab[:, inner:]
     da = dz * bb * dsilu(a)
     db = dz * silu(a)
@@ -425,11 +434,11 @@ def layer_backward(L: Layer, x: np.ndarray, dout: np.ndarray, h0: Optional[np.nd
                                                L.gate.gain, eps)
     dx1 = dO + dx1_gate
     # o_proj: x1 = x + o(u)
-    u = r["u"].reshape(m, d)
+    u = st["u"]
     du, dw_o, dg_o = bitlinear_bwd(u, L.o.t, L.o.mu, dx1, L.o.gain, eps)
     # g_norm: u = (h r_h) * w * SiLU(g^)
-    h = r["h"].reshape(m, d)
-    gh = r["g_hat"].reshape(m, d)
+    h = st["h"]
+    gh = st["g"]
     rh = 1.0 / np.sqrt(np.mean(h * h, axis=1) + np.float64(np.float32(eps)))
     nrm = h * rh[:, None]
     w = np.ones(d) if L.g_norm_w is None else np.asarray(L.g_norm_w, dtype=np.float64)
@@ -440,8 +449,8 @@ def layer_backward(L: Layer, x: np.ndarray, dout: np.ndarray, h0: Optional[np.nd
     c = np.sum(h * dn, axis=1)
     dh = rh[:, None] * dn - (rh ** 3 / d)[:, None] * h * c[:, None]
     # the recurrence, then the gates
-    dxt, df, dh0 = hgrn_scan_bwd(r["f"], r["h"], dh.reshape(b, t, d), h0, dh_last)
-    f, ih = r["f"].reshape(m, d), r["i_hat"].reshape(m, d)
+    f, ih = st["f"], st["i_hat"]
+    dxt, df, dh0 = hgrn_scan_bwd(f.reshape(b, t, d), h.reshape(b, t, d), dh.reshape(b, t, d), h0, dh_last)
     dxt, df = dxt.reshape(m, d), df.reshape(m, d)
     df_hat = (df - dxt * silu(ih)) * f * (1.0 - f)
     di_hat = dxt * (1.0 - f) * dsilu(ih)

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmmf.so")
 __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
     "ternary_pack", "bitlinear_fwd", "bitlinear_bwd", "embed", "greedy_head", "hgrn_scan_fwd", "hgrn_scan_bwd",
-    "layer_fwd",
+    "layer_fwd", "layer_bwd",
     "layer_decode_step",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
     "set_decode_kernel", "decode_expired_waits", "DECODE_KERNELS",
@@ -33,6 +33,7 @@ SYMBOLS = [
     "mmf_embed", "mmf_greedy_head_workspace_size", "mmf_greedy_head",
     "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd", "mmf_hgrn_scan_bwd",
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
+    "mmf_layer_bwd_workspace_size", "mmf_layer_bwd",
     "mmf_set_decode_kernel", "mmf_decode_expired_waits",
     "mmf_timing_enable", "mmf_timing_collect",
 ]
@@ -67,6 +68,10 @@ PROBE_FIELDS = ["acc_ifg", "f", "xt", "g", "h", "u", "codes_u", "scale_u", "acc_
 
 class CKernelTiming(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_char * 40), ("m", I64), ("n", I32), ("k", I32), ("ms", F32)]
+
+
+class CLayerGrads(ctypes.Structure):
+    _fields_ = [("dx", P), ("dh0", P), ("dw", P * 6), ("dgain", P * 6), ("dg_norm_w", P)]
 
 
 class CLayerProbe(ctypes.Structure):
@@ -106,6 +111,9 @@ def load():
                                   ctypes.c_int, P, SZ, ctypes.POINTER(CLayerProbe), P]
     lib.mmf_layer_decode_step.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, P, P, SZ,
                                           ctypes.POINTER(CLayerProbe), P]
+    lib.mmf_layer_bwd_workspace_size.argtypes = [ctypes.POINTER(CLayerWeights), I64, I64, ctypes.POINTER(SZ)]
+    lib.mmf_layer_bwd.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, I64, P, P, ctypes.c_int,
+                                  ctypes.POINTER(CLayerGrads), P, SZ, P]
     lib.mmf_set_decode_kernel.argtypes = [ctypes.c_int]
     lib.mmf_decode_expired_waits.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     lib.mmf_timing_enable.argtypes = [ctypes.c_int]
@@ -431,6 +439,44 @@ def layer_fwd(params: LayerParams, x, h0=None, want_h_last: bool = True, mode: s
                              _ptr(h_last), SCAN_MODES[mode], _ptr(wsb), wsb.numel(),
                              ctypes.byref(cp) if cp is not None else None, _stream()))
     return out, h_last
+
+
+LAYER_WEIGHTS = ("i", "f", "g", "o", "gate", "down")
+
+
+def layer_bwd(params: LayerParams, x, dout, h0=None, dh_last=None, mode: str = "auto", want_dh0: bool = True,
+              want_weights: bool = True, want_gains: bool = False, ws=None) -> dict:
+    """Derivative of one block (mmf_layer_bwd, straight-through quantisers): x, dout [b, t, d];
+    returns a dict with dx [b, t, d] fp32, dh0 [b, d], dw {name: [n, k]}, dgain {name: [k]} and
+    dg_norm_w [d] (fp32; the parts not asked for are None)."""
+    torch = _torch()
+    lib = load()
+    if x.dim() != 3 or not x.is_contiguous() or not dout.is_contiguous() or dout.shape != x.shape:
+        raise ValueError("x and dout must be contiguous [b, t, d] tensors")
+    b, t, d = x.shape
+    dev = x.device
+    lins = [getattr(params, n) for n in LAYER_WEIGHTS]
+    res = dict(dx=torch.empty((b, t, d), dtype=torch.float32, device=dev),
+               dh0=torch.empty((b, d), dtype=torch.float32, device=dev) if want_dh0 else None,
+               dw={n: torch.empty((l.n, l.k), dtype=torch.float32, device=dev) for n, l in zip(LAYER_WEIGHTS, lins)}
+               if want_weights else None,
+               dgain={n: torch.empty((l.k,), dtype=torch.float32, device=dev) for n, l in zip(LAYER_WEIGHTS, lins)}
+               if want_gains else None,
+               dg_norm_w=torch.empty((d,), dtype=torch.float32, device=dev) if want_gains else None)
+    cg = CLayerGrads()
+    cg.dx = _ptr(res["dx"])
+    cg.dh0 = _ptr(res["dh0"])
+    for q, n in enumerate(LAYER_WEIGHTS):
+        cg.dw[q] = _ptr(res["dw"][n]) if res["dw"] else None
+        cg.dgain[q] = _ptr(res["dgain"][n]) if res["dgain"] else None
+    cg.dg_norm_w = _ptr(res["dg_norm_w"])
+    cw = params.c()
+    need = SZ(0)
+    _check(lib.mmf_layer_bwd_workspace_size(ctypes.byref(cw), b, t, ctypes.byref(need)))
+    wsb = _workspace(need.value, dev, ws)
+    _check(lib.mmf_layer_bwd(ctypes.byref(cw), _ptr(x), _ptr(dout), _dtype_code(x.dtype), b, t, _ptr(h0),
+                             _ptr(dh_last), SCAN_MODES[mode], ctypes.byref(cg), _ptr(wsb), wsb.numel(), _stream()))
+    return res
 
 
 def layer_decode_step(params: LayerParams, x, h, probe: Optional[LayerProbe] = None, out=None, ws=None):

@@ -192,6 +192,175 @@ __global__ __launch_bounds__(256) void gain_final_kernel(const float *__restrict
     dgain[c] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// The block's elementwise pieces (forward values kept for the derivative, and
+// their derivatives); n4 = elements / 4, four per thread.
+// ---------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ T act_from(float v);
+template <> __device__ __forceinline__ float act_from<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t act_from<uint16_t>(float v) { return f32_to_bf16(v); }
+
+// f = sigmoid(f^), x~ = (1 - f) SiLU(i^), g stored in the activation type: the
+// same operations as the fused gate epilogue of the forward contraction
+template <typename AT>
+__global__ __launch_bounds__(256) void gates_keep_kernel(const float *__restrict__ ih, const float *__restrict__ fh,
+                                                         const float *__restrict__ gh, int64_t n4, float *__restrict__ f,
+                                                         float *__restrict__ xt, AT *__restrict__ g) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const float4 a = reinterpret_cast<const float4 *>(ih)[i], b = reinterpret_cast<const float4 *>(fh)[i];
+    const float4 c = reinterpret_cast<const float4 *>(gh)[i];
+    const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w}, cv[4] = {c.x, c.y, c.z, c.w};
+    float fo[4], xo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        fo[e] = sigmoid_fast(bv[e]);
+        xo[e] = (1.0f - fo[e]) * silu_fast(av[e]);
+        g[4 * i + e] = act_from<AT>(cv[e]);
+    }
+    reinterpret_cast<float4 *>(f)[i] = make_float4(fo[0], fo[1], fo[2], fo[3]);
+    reinterpret_cast<float4 *>(xt)[i] = make_float4(xo[0], xo[1], xo[2], xo[3]);
+}
+
+// z = SiLU(a) * b for [a | b] rows of 2 inner, z stored in the activation type
+// (the forward's GLU epilogue)
+template <typename AT>
+__global__ __launch_bounds__(256) void glu_keep_kernel(const float *__restrict__ ab, int64_t m, int inner,
+                                                       AT *__restrict__ z) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m * inner) return;
+    const int64_t row = i / inner, c = i - row * inner;
+    const float a = ab[row * 2 * inner + c], b = ab[row * 2 * inner + inner + c];
+    z[i] = act_from<AT>(silu_fast(a) * b);
+}
+
+__device__ __forceinline__ float dsilu_f(float z) {
+    const float sg = sigmoid_fast(z);
+    return sg * (1.0f + z * (1.0f - sg));
+}
+
+// da = dz b SiLU'(a), db = dz SiLU(a)
+__global__ __launch_bounds__(256) void glu_bwd_kernel(const float *__restrict__ dz, const float *__restrict__ ab,
+                                                      int64_t m, int inner, float *__restrict__ dab) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m * inner) return;
+    const int64_t row = i / inner, c = i - row * inner;
+    const float a = ab[row * 2 * inner + c], b = ab[row * 2 * inner + inner + c], g = dz[i];
+    dab[row * 2 * inner + c] = g * b * dsilu_f(a);
+    dab[row * 2 * inner + inner + c] = g * silu_fast(a);
+}
+
+// gate derivatives in place: dxt <- di^ = dxt (1 - f) SiLU'(i^), df <- df^ = (df - dxt SiLU(i^)) f (1 - f)
+__global__ __launch_bounds__(256) void gates_bwd_kernel(float *__restrict__ dxt, float *__restrict__ df,
+                                                        const float *__restrict__ ih, const float *__restrict__ f,
+                                                        int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float x = dxt[i], fv = f[i], iv = ih[i];
+    df[i] = (df[i] - x * silu_fast(iv)) * fv * (1.0f - fv);
+    dxt[i] = x * (1.0f - fv) * dsilu_f(iv);
+}
+
+// out = a (type TA) + b + c + d (fp32; c, d may be null), in that order
+template <typename TA>
+__global__ __launch_bounds__(256) void sum_kernel(const TA *__restrict__ a, const float *__restrict__ b,
+                                                  const float *__restrict__ c, const float *__restrict__ d, int64_t n,
+                                                  float *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v = load_act(a, i) + b[i];
+    if (c) v += c[i];
+    if (d) v += d[i];
+    out[i] = v;
+}
+
+// g_norm's derivative per row, u = (h r) w SiLU(g), r = (mean(h^2) + eps)^(-1/2):
+// dn = du w SiLU(g); dg = du (h r) w SiLU'(g); dh = r dn - (r^3 / d) h (h . dn);
+// the weight's derivative du (h r) SiLU(g) summed over the workgroup's rows.
+// Same row scheme as rmsnorm_bwd_kernel.
+template <typename TG, int NV>
+__global__ __launch_bounds__(256) void gnorm_bwd_kernel(const float *__restrict__ h, const TG *__restrict__ g,
+                                                        const float *__restrict__ du, const float *__restrict__ w,
+                                                        float eps, int64_t m, int d, int rows, float *__restrict__ dh,
+                                                        float *__restrict__ dg, float *__restrict__ wpart) {
+    __shared__ double red[2][2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nch = d >> 2;
+    float wvv[NV][4], wacc[NV][4];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = min(tid + 256 * j, nch - 1);
+        const float4 q = w ? *reinterpret_cast<const float4 *>(w + 4 * c) : make_float4(1.f, 1.f, 1.f, 1.f);
+        wvv[j][0] = q.x; wvv[j][1] = q.y; wvv[j][2] = q.z; wvv[j][3] = q.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wacc[j][e] = 0.0f;
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * rows;
+    const int64_t r1 = r0 + rows < m ? r0 + rows : m;
+    for (int64_t row = r0; row < r1; ++row) {
+        const int buf = (int)(row & 1);
+        float hv[NV][4], gv[NV][4], uv[NV][4], dn[NV][4];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int c = min(tid + 256 * j, nch - 1);
+            const float4 a = *reinterpret_cast<const float4 *>(h + row * d + 4 * c);
+            const float4 b = load_act4(g + row * d, 4 * c);
+            const float4 e = *reinterpret_cast<const float4 *>(du + row * d + 4 * c);
+            hv[j][0] = a.x; hv[j][1] = a.y; hv[j][2] = a.z; hv[j][3] = a.w;
+            gv[j][0] = b.x; gv[j][1] = b.y; gv[j][2] = b.z; gv[j][3] = b.w;
+            uv[j][0] = e.x; uv[j][1] = e.y; uv[j][2] = e.z; uv[j][3] = e.w;
+        }
+        double ss = 0.0, cs = 0.0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dn[j][e] = uv[j][e] * wvv[j][e] * silu_fast(gv[j][e]);
+                if (tid + 256 * j < nch) {
+                    ss += (double)hv[j][e] * (double)hv[j][e];
+                    cs += (double)hv[j][e] * (double)dn[j][e];
+                }
+            }
+        ss = wave_sum(ss);
+        cs = wave_sum(cs);
+        if (lane == 0) {
+            red[buf][0][wv] = ss;
+            red[buf][1][wv] = cs;
+        }
+        __syncthreads();
+        ss = (red[buf][0][0] + red[buf][0][1]) + (red[buf][0][2] + red[buf][0][3]);
+        cs = (red[buf][1][0] + red[buf][1][1]) + (red[buf][1][2] + red[buf][1][3]);
+        const float r = rms_factor(ss, d, eps);
+        const float coef = (r * r * r) / (float)d;
+        const float c = (float)cs;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int ch = tid + 256 * j;
+            if (ch < nch) {
+                float oh[4], og[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float nv = hv[j][e] * r;
+                    oh[e] = r * dn[j][e] - coef * hv[j][e] * c;
+                    og[e] = uv[j][e] * nv * wvv[j][e] * dsilu_f(gv[j][e]);
+                    wacc[j][e] += uv[j][e] * nv * silu_fast(gv[j][e]);
+                }
+                *reinterpret_cast<float4 *>(dh + row * d + 4 * ch) = make_float4(oh[0], oh[1], oh[2], oh[3]);
+                *reinterpret_cast<float4 *>(dg + row * d + 4 * ch) = make_float4(og[0], og[1], og[2], og[3]);
+            }
+        }
+    }
+    if (wpart) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int ch = tid + 256 * j;
+            if (ch < nch)
+                *reinterpret_cast<float4 *>(wpart + (int64_t)blockIdx.x * d + 4 * ch) =
+                    make_float4(wacc[j][0], wacc[j][1], wacc[j][2], wacc[j][3]);
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void zero_f32_kernel(float *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0.0f;
@@ -258,6 +427,61 @@ hipError_t launch_rmsnorm_bwd(const void *x, ActType xt, const float *du_raw, co
         if (dxt == ACT_F32) rms_bwd_t(static_cast<const uint16_t *>(x), du_raw, gain, mu, eps, m, k, static_cast<float *>(dx), gpart, st);
         else rms_bwd_t(static_cast<const uint16_t *>(x), du_raw, gain, mu, eps, m, k, static_cast<uint16_t *>(dx), gpart, st);
     }
+    return hipGetLastError();
+}
+
+static unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+hipError_t launch_gates_keep(const float *ih, const float *fh, const float *gh, int64_t n, float *f, float *xt, void *g,
+                             ActType gt, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    if (gt == ACT_F32) gates_keep_kernel<float><<<blocks(n / 4), 256, 0, st>>>(ih, fh, gh, n / 4, f, xt, static_cast<float *>(g));
+    else gates_keep_kernel<uint16_t><<<blocks(n / 4), 256, 0, st>>>(ih, fh, gh, n / 4, f, xt, static_cast<uint16_t *>(g));
+    return hipGetLastError();
+}
+
+hipError_t launch_glu_keep(const float *ab, int64_t m, int inner, void *z, ActType zt, hipStream_t st) {
+    if (m <= 0) return hipSuccess;
+    if (zt == ACT_F32) glu_keep_kernel<float><<<blocks(m * inner), 256, 0, st>>>(ab, m, inner, static_cast<float *>(z));
+    else glu_keep_kernel<uint16_t><<<blocks(m * inner), 256, 0, st>>>(ab, m, inner, static_cast<uint16_t *>(z));
+    return hipGetLastError();
+}
+
+hipError_t launch_glu_bwd(const float *dz, const float *ab, int64_t m, int inner, float *dab, hipStream_t st) {
+    if (m > 0) glu_bwd_kernel<<<blocks(m * inner), 256, 0, st>>>(dz, ab, m, inner, dab);
+    return hipGetLastError();
+}
+
+hipError_t launch_gates_bwd(float *dxt, float *df, const float *ih, const float *f, int64_t n, hipStream_t st) {
+    if (n > 0) gates_bwd_kernel<<<blocks(n), 256, 0, st>>>(dxt, df, ih, f, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum(const void *a, ActType at, const float *b, const float *c, const float *d, int64_t n, float *out,
+                      hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    if (at == ACT_F32) sum_kernel<float><<<blocks(n), 256, 0, st>>>(static_cast<const float *>(a), b, c, d, n, out);
+    else sum_kernel<uint16_t><<<blocks(n), 256, 0, st>>>(static_cast<const uint16_t *>(a), b, c, d, n, out);
+    return hipGetLastError();
+}
+
+template <typename TG>
+static void gnorm_bwd_t(const float *h, const TG *g, const float *du, const float *w, float eps, int64_t m, int d,
+                        float *dh, float *dg, float *wpart, hipStream_t st) {
+    const int rows = rmsnorm_bwd_rows(m);
+    const unsigned grid = (unsigned)((m + rows - 1) / rows);
+    switch (nv_bucket(d)) {
+#define MMF_GB(NV) case NV: gnorm_bwd_kernel<TG, NV><<<grid, 256, 0, st>>>(h, g, du, w, eps, m, d, rows, dh, dg, wpart); break;
+        MMF_GB(1) MMF_GB(2) MMF_GB(4) MMF_GB(8)
+#undef MMF_GB
+    }
+}
+
+hipError_t launch_gnorm_bwd(const float *h, const void *g, ActType gt, const float *du, const float *w, float eps,
+                            int64_t m, int d, float *dh, float *dg, float *wpart, hipStream_t st) {
+    if (m <= 0) return hipSuccess;
+    if (gt == ACT_F32) gnorm_bwd_t(h, static_cast<const float *>(g), du, w, eps, m, d, dh, dg, wpart, st);
+    else gnorm_bwd_t(h, static_cast<const uint16_t *>(g), du, w, eps, m, d, dh, dg, wpart, st);
     return hipGetLastError();
 }
 

@@ -134,6 +134,20 @@ hipError_t launch_rmsnorm_bwd(const void *x, ActType xt, const float *du_raw, co
 int gain_reduce_splits(int nblk);  // rows of the second level's workspace ([splits][k] fp32)
 hipError_t launch_gain_reduce(const float *gpart, int nblk, int k, float *part2, float *dgain, hipStream_t st);
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t st);  // a fill kernel (capturable)
+// The block derivative's elementwise pieces (k_bwd.hip): the forward's gate and
+// GLU values kept for the derivative (same operations as the fused
+// epilogues; g, z in the activation type), the GLU and gate derivatives, an
+// elementwise sum, and g_norm's row-wise derivative with per-workgroup partial
+// sums of its weight's derivative (rows per workgroup: rmsnorm_bwd_rows).
+hipError_t launch_gates_keep(const float *ih, const float *fh, const float *gh, int64_t n, float *f, float *xt, void *g,
+                             ActType gt, hipStream_t st);
+hipError_t launch_glu_keep(const float *ab, int64_t m, int inner, void *z, ActType zt, hipStream_t st);
+hipError_t launch_glu_bwd(const float *dz, const float *ab, int64_t m, int inner, float *dab, hipStream_t st);
+hipError_t launch_gates_bwd(float *dxt, float *df, const float *ih, const float *f, int64_t n, hipStream_t st);
+hipError_t launch_sum(const void *a, ActType at, const float *b, const float *c, const float *d, int64_t n, float *out,
+                      hipStream_t st);
+hipError_t launch_gnorm_bwd(const float *h, const void *g, ActType gt, const float *du, const float *w, float eps,
+                            int64_t m, int d, float *dh, float *dg, float *wpart, hipStream_t st);
 hipError_t gemm_bf16_f32(const uint16_t *a, bool trans_a, const uint16_t *b, int64_t rows, int64_t cols, int64_t inner,
                          float *c, hipStream_t st, std::string *err);
 

@@ -465,6 +465,46 @@ size_t bitlinear_bwd_plan(Carver &c, int64_t m, int n, int k, mmf_dtype dyt, Bit
     return c.off;
 }
 
+// One FusedBitLinear derivative (m > 0) on a carved workspace sized for at
+// least (m, n, k) with an fp32 dy: codes from the forward's quantiser, bf16
+// products through rocBLAS, the RMSNorm derivative and the gain's sums.
+hipError_t bitlinear_bwd_run(const void *x, ActType xt, int64_t m, const mmf_ternary_weight *w, float eps,
+                             const void *dy, ActType dyt, void *dx, ActType dxt, float *dw, float *dgain,
+                             const BitlinearBwdWs &B, hipStream_t stream, std::string *path, std::string *err) {
+    const int n = w->n, k = w->k;
+    hipError_t e = t_norm_quant(x, xt, m, k, w->norm_w, eps, B.q, B.s, nullptr, stream, path);
+    const uint16_t *dy16 = dyt == ACT_F32 ? B.dy16 : static_cast<const uint16_t *>(dy);
+    if (e == hipSuccess && dyt == ACT_F32)
+        e = timed("to_bf16", m, n, n, stream,
+                  [&] { return launch_to_bf16(static_cast<const float *>(dy), m * n, B.dy16, stream); });
+    if (e == hipSuccess && (dx || dgain)) {
+        e = timed("expand_ternary", n, k, k, stream, [&] { return launch_expand_ternary(w->packed, n, k, B.t16, stream); });
+        if (e == hipSuccess)  // du (before 1 / sw) = dy t
+            e = timed("gemm_bf16<du>", m, k, n, stream,
+                      [&] { return gemm_bf16_f32(dy16, false, B.t16, m, k, n, B.du, stream, err); });
+        if (e == hipSuccess)
+            e = timed("rmsnorm_bwd", m, k, k, stream, [&] {
+                return launch_rmsnorm_bwd(x, xt, B.du, w->norm_w, w->mu, eps, m, k, dx, dxt, dgain ? B.gpart : nullptr,
+                                          stream);
+            });
+        if (e == hipSuccess && dgain) {
+            const int rows = rmsnorm_bwd_rows(m);
+            const int nblk = (int)((m + rows - 1) / rows);
+            e = timed("gain_reduce", nblk, k, k, stream,
+                      [&] { return launch_gain_reduce(B.gpart, nblk, k, B.gpart2, dgain, stream); });
+        }
+        *path += "expand_ternary;gemm_bf16<du>;rmsnorm_bwd;" + std::string(dgain ? "gain_reduce;" : "");
+    }
+    if (e == hipSuccess && dw) {
+        e = timed("scaled_codes", m, k, k, stream, [&] { return launch_scaled_codes(B.q, B.s, m, k, B.u16, stream); });
+        if (e == hipSuccess)  // dW = dy^T (q / s)
+            e = timed("gemm_bf16<dw>", n, k, m, stream,
+                      [&] { return gemm_bf16_f32(dy16, true, B.u16, n, k, m, dw, stream, err); });
+        *path += "scaled_codes;gemm_bf16<dw>;";
+    }
+    return e;
+}
+
 mmf_status mmf_bitlinear_bwd_workspace_size(int64_t m, const mmf_ternary_weight *w, mmf_dtype dyt, size_t *bytes) {
     if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
     mmf_status st = check_weight(w, "weight");
@@ -506,35 +546,7 @@ mmf_status mmf_bitlinear_bwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
     BitlinearBwdWs B;
     bitlinear_bwd_plan(c, m, n, k, dyt, &B);
     std::string path, err;
-    hipError_t e = t_norm_quant(x, act(xt), m, k, w->norm_w, eps, B.q, B.s, nullptr, stream, &path);
-    const uint16_t *dy16 = dyt == MMF_F32 ? B.dy16 : static_cast<const uint16_t *>(dy);
-    if (e == hipSuccess && dyt == MMF_F32)
-        e = timed("to_bf16", m, n, n, stream,
-                  [&] { return launch_to_bf16(static_cast<const float *>(dy), m * n, B.dy16, stream); });
-    if (e == hipSuccess && (dx || dgain)) {
-        e = timed("expand_ternary", n, k, k, stream, [&] { return launch_expand_ternary(w->packed, n, k, B.t16, stream); });
-        if (e == hipSuccess)  // du (before 1 / sw) = dy t
-            e = timed("gemm_bf16<du>", m, k, n, stream,
-                      [&] { return gemm_bf16_f32(dy16, false, B.t16, m, k, n, B.du, stream, &err); });
-        if (e == hipSuccess)
-            e = timed("rmsnorm_bwd", m, k, k, stream, [&] {
-                return launch_rmsnorm_bwd(x, act(xt), B.du, w->norm_w, w->mu, eps, m, k, dx, act(dxt),
-                                          dgain ? B.gpart : nullptr, stream);
-            });
-        if (e == hipSuccess && dgain) {
-            const int rows = rmsnorm_bwd_rows(m);
-            const int nblk = (int)((m + rows - 1) / rows);
-            e = timed("gain_reduce", nblk, k, k, stream, [&] { return launch_gain_reduce(B.gpart, nblk, k, B.gpart2, dgain, stream); });
-        }
-        path += "expand_ternary;gemm_bf16<du>;rmsnorm_bwd;" + std::string(dgain ? "gain_reduce;" : "");
-    }
-    if (e == hipSuccess && dw) {
-        e = timed("scaled_codes", m, k, k, stream, [&] { return launch_scaled_codes(B.q, B.s, m, k, B.u16, stream); });
-        if (e == hipSuccess)  // dW = dy^T (q / s)
-            e = timed("gemm_bf16<dw>", n, k, m, stream,
-                      [&] { return gemm_bf16_f32(dy16, true, B.u16, n, k, m, dw, stream, &err); });
-        path += "scaled_codes;gemm_bf16<dw>;";
-    }
+    hipError_t e = bitlinear_bwd_run(x, act(xt), m, w, eps, dy, act(dyt), dx, act(dxt), dw, dgain, B, stream, &path, &err);
     if (e != hipSuccess && !err.empty()) return fail(MMF_ERR_HIP, "mmf_bitlinear_bwd: %s", err.c_str());
     mmf_status r = hip_status(e, "mmf_bitlinear_bwd");
     if (r == MMF_OK) g_path = path;
@@ -828,6 +840,174 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
         if (e == hipSuccess) e = block_tail(w, x, out, actt, b, L, h, g, probe, stream, &path);
     }
     mmf_status r = hip_status(e, "mmf_layer_decode_step");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+// --------------------------------------------------------- block derivative --
+struct LayerBwdWs {
+    int8_t *codes_x[3];
+    float *s_x[3];
+    int32_t *sq_x[3];
+    float *ih, *fh, *gh, *f, *xt, *h, *u, *x1, *ab;
+    void *g, *z;  // activation dtype (fp32-sized)
+    int8_t *codes_b;
+    float *s_b;
+    int32_t *sq_b;
+    float *dz, *dab, *dx1g, *dx1, *du, *dh, *dg, *df, *dxi, *dxf, *dxg, *wpart, *wpart2;
+    void *scan;
+    BitlinearBwdWs blin;
+};
+
+size_t layer_bwd_plan(Carver &c, const mmf_layer_weights *w, int64_t b, int64_t t, int chunks, LayerBwdWs *o) {
+    const int64_t m = b * t;
+    const size_t d = (size_t)w->d, inner = (size_t)w->inner, md = (size_t)m * d;
+    LayerBwdWs L{};
+    for (int q = 0; q < 3; ++q) {
+        L.codes_x[q] = c.take<int8_t>(md);
+        L.s_x[q] = c.take<float>(m);
+        L.sq_x[q] = c.take<int32_t>(m);
+    }
+    float **f32s[] = {&L.ih, &L.fh, &L.gh, &L.f, &L.xt, &L.h, &L.u, &L.x1, &L.dx1g, &L.dx1, &L.du, &L.dh, &L.dg,
+                      &L.df, &L.dxi, &L.dxf, &L.dxg};
+    for (float **p : f32s) *p = c.take<float>(md);
+    L.g = c.take<float>(md);
+    L.ab = c.take<float>((size_t)m * 2 * inner);
+    L.dab = c.take<float>((size_t)m * 2 * inner);
+    L.z = c.take<float>((size_t)m * inner);
+    L.dz = c.take<float>((size_t)m * inner);
+    L.codes_b = c.take<int8_t>((size_t)m * (d > inner ? d : inner));
+    L.s_b = c.take<float>(m);
+    L.sq_b = c.take<int32_t>(m);
+    const int64_t rows = m > 0 ? rmsnorm_bwd_rows(m) : 1;
+    const int64_t nblk = (m + rows - 1) / rows;
+    L.wpart = c.take<float>((size_t)nblk * d);
+    L.wpart2 = c.take<float>((size_t)gain_reduce_splits((int)nblk) * d);
+    L.scan = c.take<char>(scan_workspace_bytes(b, w->d, chunks));
+    const int nmax = 2 * w->inner > w->d ? 2 * w->inner : w->d;
+    const int kmax = w->inner > w->d ? w->inner : w->d;
+    bitlinear_bwd_plan(c, m, nmax, kmax, MMF_F32, &L.blin);
+    if (o) *o = L;
+    return c.off;
+}
+
+mmf_status mmf_layer_bwd_workspace_size(const mmf_layer_weights *w, int64_t b, int64_t t, size_t *bytes) {
+    if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
+    mmf_status st = check_layer(w);
+    if (st != MMF_OK) return st;
+    if (b < 0 || t < 0) return fail(MMF_ERR_INVALID_ARG, "b, t must be >= 0");
+    Carver c(nullptr);
+    *bytes = layer_bwd_plan(c, w, b, t, scan_pick_chunks(b, t, w->d, MMF_SCAN_CHUNK), nullptr);
+    return MMF_OK;
+}
+
+mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *dout, mmf_dtype actt, int64_t b,
+                         int64_t t, const float *h0, const float *dh_last, mmf_scan_mode mode,
+                         const mmf_layer_grads *gr, void *ws, size_t ws_bytes, hipStream_t stream) {
+    size_t need = 0;
+    mmf_status st = mmf_layer_bwd_workspace_size(w, b, t, &need);
+    if (st != MMF_OK) return st;
+    if (!valid_dtype(actt)) return fail(MMF_ERR_INVALID_ARG, "bad activation dtype");
+    if (mode != MMF_SCAN_AUTO && mode != MMF_SCAN_RECURRENT && mode != MMF_SCAN_CHUNK)
+        return fail(MMF_ERR_INVALID_ARG, "bad scan mode %d", (int)mode);
+    if (!gr) return fail(MMF_ERR_INVALID_ARG, "grads is NULL");
+    const int64_t m = b * t;
+    const int d = w->d, inner = w->inner;
+    if (m > 0 && (!x || !dout || !gr->dx)) return fail(MMF_ERR_INVALID_ARG, "x, dout and grads->dx must be non-NULL");
+    if (!rmsnorm_bwd_supported(d) || !rmsnorm_bwd_supported(inner) || (2 * inner) % 8 || d % 8)
+        return fail(MMF_ERR_UNSUPPORTED, "d=%d, inner=%d outside the derivative kernels' limits", d, inner);
+    if (m > INT32_MAX) return fail(MMF_ERR_UNSUPPORTED, "b*t beyond 32-bit GEMM sizes");
+    if (!aligned16(x) || !aligned16(dout) || !aligned16(gr->dx) || !aligned16(h0) || !aligned16(dh_last))
+        return fail(MMF_ERR_INVALID_ARG, "x, dout, dx, h0 and dh_last must be 16-byte aligned");
+    if (m > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    const mmf_ternary_weight *tw[6] = {&w->i, &w->f, &w->g, &w->o, &w->gate, &w->down};
+    std::string path, err;
+    hipError_t e = hipSuccess;
+    if (m == 0) {
+        // no tokens: h_last is h0, and every weight and gain sees nothing
+        if (gr->dh0 && b > 0) e = launch_scan_bwd(nullptr, nullptr, nullptr, nullptr, dh_last, nullptr, nullptr, gr->dh0,
+                                                  b, 0, d, 1, stream, &path);
+        for (int q = 0; q < 6 && e == hipSuccess; ++q) {
+            if (gr->dw[q]) e = launch_zero_f32(gr->dw[q], (int64_t)tw[q]->n * tw[q]->k, stream);
+            if (e == hipSuccess && gr->dgain[q]) e = launch_zero_f32(gr->dgain[q], tw[q]->k, stream);
+        }
+        if (e == hipSuccess && gr->dg_norm_w) e = launch_zero_f32(gr->dg_norm_w, d, stream);
+        mmf_status r = hip_status(e, "mmf_layer_bwd");
+        if (r == MMF_OK) g_path = "empty";
+        return r;
+    }
+    const ActType at = act(actt);
+    const float eps = w->eps;
+    const int chunks = scan_pick_chunks(b, t, d, (int)mode);
+    Carver c(ws);
+    LayerBwdWs L;
+    layer_bwd_plan(c, w, b, t, scan_pick_chunks(b, t, d, MMF_SCAN_CHUNK), &L);
+    const int64_t md = m * d;
+    // ---- the forward again, keeping what the derivative needs
+    const bool shared = shared_ifg(w);
+    float *pre[3] = {L.ih, L.fh, L.gh};
+    for (int q = 0; q < 3 && e == hipSuccess; ++q) {
+        const int src = shared ? 0 : q;
+        if (src == q) e = t_norm_quant(x, at, m, d, tw[q]->norm_w, eps, L.codes_x[q], L.s_x[q], L.sq_x[q], stream, &path);
+        if (e != hipSuccess) break;
+        ContractArgs ca{};
+        for (int j = 0; j < 3; ++j) { ca.A[j] = L.codes_x[src]; ca.s[j] = L.s_x[src]; ca.sumq[j] = L.sq_x[src]; ca.B[j] = tw[q]->packed; ca.mu[j] = tw[q]->mu; }
+        ca.m = m; ca.nc = d; ca.k = d;
+        ca.out0 = pre[q]; ca.out_type = ACT_F32;
+        e = t_contract(ca, EPI_LINEAR, 1, true, stream, &path);
+    }
+    if (e == hipSuccess) e = launch_gates_keep(L.ih, L.fh, L.gh, md, L.f, L.xt, L.g, at, stream);
+    if (e == hipSuccess) e = t_scan(L.xt, L.f, h0, L.h, nullptr, b, t, d, chunks, L.scan, stream, &path);
+    if (e == hipSuccess)
+        e = t_gnorm_quant(L.h, L.g, at, m, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, L.u, stream, &path);
+    if (e == hipSuccess) {
+        ContractArgs co{};
+        for (int j = 0; j < 3; ++j) { co.A[j] = L.codes_b; co.s[j] = L.s_b; co.sumq[j] = L.sq_b; co.B[j] = w->o.packed; co.mu[j] = w->o.mu; }
+        co.m = m; co.nc = d; co.k = d;
+        co.out0 = L.x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
+        e = t_contract(co, EPI_RESID, 1, true, stream, &path);
+    }
+    if (e == hipSuccess) e = t_norm_quant(L.x1, ACT_F32, m, d, w->gate.norm_w, eps, L.codes_b, L.s_b, L.sq_b, stream, &path);
+    if (e == hipSuccess) {
+        ContractArgs cg{};
+        for (int j = 0; j < 3; ++j) { cg.A[j] = L.codes_b; cg.s[j] = L.s_b; cg.sumq[j] = L.sq_b; cg.B[j] = w->gate.packed; cg.mu[j] = w->gate.mu; }
+        cg.m = m; cg.nc = 2 * inner; cg.k = d;
+        cg.out0 = L.ab; cg.out_type = ACT_F32;
+        e = t_contract(cg, EPI_LINEAR, 1, true, stream, &path);
+    }
+    if (e == hipSuccess) e = launch_glu_keep(L.ab, m, inner, L.z, at, stream);
+    // ---- derivatives, last step first
+    if (e == hipSuccess)  // down_proj: dz
+        e = bitlinear_bwd_run(L.z, at, m, &w->down, eps, dout, at, L.dz, ACT_F32, gr->dw[5], gr->dgain[5], L.blin,
+                              stream, &path, &err);
+    if (e == hipSuccess) e = launch_glu_bwd(L.dz, L.ab, m, inner, L.dab, stream);
+    if (e == hipSuccess)  // gate_proj: into x1
+        e = bitlinear_bwd_run(L.x1, ACT_F32, m, &w->gate, eps, L.dab, ACT_F32, L.dx1g, ACT_F32, gr->dw[4], gr->dgain[4],
+                              L.blin, stream, &path, &err);
+    if (e == hipSuccess) e = launch_sum(dout, at, L.dx1g, nullptr, nullptr, md, L.dx1, stream);  // + the residual
+    if (e == hipSuccess)  // o_proj: du
+        e = bitlinear_bwd_run(L.u, ACT_F32, m, &w->o, eps, L.dx1, ACT_F32, L.du, ACT_F32, gr->dw[3], gr->dgain[3], L.blin,
+                              stream, &path, &err);
+    if (e == hipSuccess)  // g_norm: dh, dg^ and the weight's partial sums
+        e = launch_gnorm_bwd(L.h, L.g, at, L.du, w->g_norm_w, eps, m, d, L.dh, L.dg, gr->dg_norm_w ? L.wpart : nullptr,
+                             stream);
+    if (e == hipSuccess && gr->dg_norm_w) {
+        const int rows = rmsnorm_bwd_rows(m);
+        e = launch_gain_reduce(L.wpart, (int)((m + rows - 1) / rows), d, L.wpart2, gr->dg_norm_w, stream);
+    }
+    if (e == hipSuccess)  // the recurrence: dx~ (over dh), df, dh0
+        e = launch_scan_bwd(L.f, L.h, h0, L.dh, dh_last, L.dh, L.df, gr->dh0, b, t, d, scan_bwd_pick(t, (int)mode),
+                            stream, &path);
+    if (e == hipSuccess) e = launch_gates_bwd(L.dh, L.df, L.ih, L.f, md, stream);  // -> di^, df^
+    const float *dpre[3] = {L.dh, L.df, L.dg};
+    float *dxq[3] = {L.dxi, L.dxf, L.dxg};
+    for (int q = 0; q < 3 && e == hipSuccess; ++q)
+        e = bitlinear_bwd_run(x, at, m, tw[q], eps, dpre[q], ACT_F32, dxq[q], ACT_F32, gr->dw[q], gr->dgain[q], L.blin,
+                              stream, &path, &err);
+    if (e == hipSuccess) e = launch_sum(L.dx1, ACT_F32, L.dxi, L.dxf, L.dxg, md, gr->dx, stream);
+    if (e != hipSuccess && !err.empty()) return fail(MMF_ERR_HIP, "mmf_layer_bwd: %s", err.c_str());
+    mmf_status r = hip_status(e, "mmf_layer_bwd");
     if (r == MMF_OK) g_path = path;
     return r;
 }

@@ -350,6 +350,59 @@ def test_generate_loop_stage_by_stage(gpu):
         ids = nxt
 
 
+LAYER_BWD_CASES = [
+    # d, inner, b, t, act, gains, mode
+    (256, 512, 2, 33, "f32", None, "recurrent"),
+    (256, 512, 2, 70, "bf16", "distinct", "chunk"),
+    (128, 352, 1, 300, "bf16", "shared", "auto"),
+]
+
+
+@pytest.mark.parametrize("d,inner,b,t,act,gains,mode", LAYER_BWD_CASES)
+def test_layer_bwd_parity(gpu, d, inner, b, t, act, gains, mode):
+    """Every derivative of the block (straight-through quantisers) against the oracle's chain,
+    evaluated at the GPU forward's own stage values (a probed forward call runs the kernels the
+    derivative's recompute runs), so that both sides' quantisers see the same inputs. The
+    products run in bf16 (rocBLAS): the bf16 bar applies (rtol 2e-2)."""
+    mmf = _mmf()
+    L, P = make_pair(d, inner, 860 + t, gpu, gains)
+    x = synth.activations((b, t, d), 861, act)
+    dout = synth.activations((b, t, d), 862, act)
+    h0 = synth.activations((b, d), 863)
+    dhl = synth.activations((b, d), 864)
+    xd = bf16_tensor(x, gpu) if act == "bf16" else dev(x, gpu)
+    m = b * t
+    probe = mmf.LayerProbe(m, d, inner, gpu, shared_ifg=gains != "distinct")
+    mmf.layer_fwd(P, xd, dev(h0, gpu), mode=mode, probe=probe)
+    pr = probe.host()
+    i_hat = oracle.dequant(pr["acc_ifg"].reshape(m, 3, d)[:, 0], pr["scale_x"][0], L.i.mu)
+    ab = oracle.dequant(pr["acc_gate"], pr["scale_x1"], L.gate.mu)
+    stages = dict(i_hat=i_hat, f=pr["f"], g=pr["g"], h=pr["h"], u=pr["u"], x1=pr["x1"], ab=ab, z=pr["z"])
+    ref = oracle.layer_backward(L, x, dout, h0, dhl, stages=stages)
+    dod = bf16_tensor(dout, gpu) if act == "bf16" else dev(dout, gpu)
+    got = mmf.layer_bwd(P, xd, dod, dev(h0, gpu), dev(dhl, gpu), mode, want_gains=True)
+    tol = 2e-2
+    assert_close(host(got["dx"]), ref["dx"], tol, "dx")
+    assert_close(host(got["dh0"]), ref["dh0"], tol, "dh0")
+    assert_close(host(got["dg_norm_w"]), ref["dg_norm_w"], tol, "dg_norm_w")
+    for k in ("i", "f", "g", "o", "gate", "down"):
+        assert_close(host(got["dw"][k]), ref["dw"][k], tol, "dw " + k)
+        assert_close(host(got["dgain"][k]), ref["dgain"][k], tol, "dgain " + k)
+    path = mmf.last_path()
+    assert "gemm_bf16<dw>" in path and ("scan_bwd_recurrent" if mode == "recurrent" else "scan_bwd") in path
+
+
+def test_layer_bwd_empty_sequence(gpu):
+    import torch
+    mmf = _mmf()
+    _, P = make_pair(64, 96, 870, gpu)
+    dhl = dev(synth.activations((2, 64), 871), gpu)
+    e = torch.empty((2, 0, 64), device=gpu)
+    got = mmf.layer_bwd(P, e, e, None, dhl, want_gains=True)
+    assert torch.equal(got["dh0"], dhl)
+    assert not host(got["dw"]["gate"]).any() and not host(got["dg_norm_w"]).any()
+
+
 SCAN_BWD_CASES = [
     # b, t, d, mode, with_h0, with_last
     (1, 1, 64, "recurrent", True, True),
