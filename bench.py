@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--decode", type=int, default=512)
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="launch decode steps eagerly instead of a HIP graph")
+    ap.add_argument("--extras", type=int, default=1,
+                    help="0 skips the figures measured outside the timed steps (other batches, B=8 prefill, "
+                         "derivatives, generation)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (for scaling HBM counters)")
     ap.add_argument("--vendor-int8-gemm", action="store_true",
@@ -416,16 +419,18 @@ def main():
 
     # ---- outside the timed region: the scan's derivative at the prefill's scan shape, and the
     # decode step at the other batch sizes of the 1.3B decode workload (graph-replayed)
-    scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev) if T > 0 else None
-    bitlinear_bwd = measure_bitlinear_bwd(mmf, torch, layers[0].o, B * T, dev) if T > 0 else None
-    layer_bwd = measure_layer_bwd(mmf, torch, layers[0], B, T, d, dev) if T > 0 else None
+    ex = args.extras != 0
+    scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev) if ex and T > 0 else None
+    bitlinear_bwd = measure_bitlinear_bwd(mmf, torch, layers[0].o, B * T, dev) if ex and T > 0 else None
+    layer_bwd = measure_layer_bwd(mmf, torch, layers[0], B, T, d, dev) if ex and T > 0 else None
     by_batch = {str(B): round(decode_ms * 1000 / D / L, 2)} if D else {}
-    if D and graph is not None:
+    if ex and D and graph is not None:
         for bb in (1, 64):
             if bb != B:
                 by_batch[str(bb)] = round(decode_us_per_layer(mmf, torch, layers, bb, d, dev, seed), 2)
     by_batch = dict(sorted(by_batch.items(), key=lambda kv: int(kv[0])))
-    generate = [measure_generate(mmf, torch, layers, bb, d, dev, seed) for bb in (1, B)] if D else None
+    prefill_b8 = measure_prefill(mmf, torch, layers, 8, T, d, dev, seed) if ex and T > 0 and B != 8 else None
+    generate = [measure_generate(mmf, torch, layers, bb, d, dev, seed) for bb in (1, B)] if ex and D else None
 
     cpu = None
     if args.cpu_baseline:
@@ -451,6 +456,7 @@ def main():
             "layers": L, "d": d, "inner": inner, "batch": B, "prompt_tokens": T, "decode_steps": D,
             "decode_launch": "hip-graph" if graph is not None else "eager",
         },
+        "stack_tokens_per_s": round(tokens / (ms_per_step / 1000.0), 1),
         "prefill_ms": round(prefill_ms, 3),
         "decode_ms": round(decode_ms, 3),
         "prefill_layer_tokens_per_s": round(B * T * L / (prefill_ms / 1000), 1),
@@ -460,6 +466,7 @@ def main():
         "roofline": roof,
         "prefill_contraction_roofline": prefill_gemm,
         "decode_us_per_layer_by_batch": by_batch,
+        "prefill_b8": prefill_b8,
         "scan_bwd": scan_bwd,
         "bitlinear_bwd": bitlinear_bwd,
         "layer_bwd": layer_bwd,
@@ -471,6 +478,36 @@ def main():
         "prep_s": round(prep_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_prefill(mmf, torch, layers, b: int, t: int, d: int, dev, seed: int, reps: int = 3) -> dict:
+    """The whole-stack prefill alone at batch b (the 1.3B prefill read at b = 8, t = 2048), seeded
+    bf16 input, timed with events over `reps` runs after one warm-up."""
+    from ternary_weight_matmul_amd import synth
+    L = len(layers)
+    x = torch.from_numpy(synth.activations((b, t, d), seed * 10 + 5, "bf16")).to(dev).to(torch.bfloat16)
+    bufs = [torch.empty_like(x) for _ in range(2)]
+    hs = torch.empty((L, b, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(mmf.layer_workspace_size(layers[0], b, t), dtype=torch.uint8, device=dev)
+
+    def run():
+        cur = x
+        for l in range(L):
+            mmf.layer_fwd(layers[l], cur, None, out=bufs[l % 2], h_last=hs[l], ws=ws)
+            cur = bufs[l % 2]
+
+    run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del x, bufs, hs, ws
+    return dict(batch=b, prompt_tokens=t, ms=round(ms, 3), layer_tokens_per_s=round(b * t * L / (ms / 1000), 1),
+                stack_tokens_per_s=round(b * t / (ms / 1000), 1))
 
 
 def measure_scan_bwd(mmf, torch, b: int, t: int, d: int, dev, launches: int = 10) -> dict:

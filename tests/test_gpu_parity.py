@@ -542,6 +542,25 @@ def test_layer_stages(gpu, d, inner, b, t, act, gains, mode):
     assert_close(host(h_last), pr["h"].reshape(b, t, d)[:, -1], 0, "h_last")
 
 
+def test_stack_of_blocks_stage_fed(gpu):
+    """A stack of three blocks of the 370M width, bf16, each block's output feeding the next (the
+    stack the benchmark runs): every block is checked stage by stage against the oracle fed with
+    the GPU's input to that block, and its output is the next block's input bit for bit."""
+    import torch
+    mmf = _mmf()
+    d, inner, b, t = 1024, 2816, 2, 96
+    pairs = [make_pair(d, inner, synth.layer_seed(2, l), gpu) for l in range(3)]
+    cur = bf16_tensor(synth.activations((b, t, d), 21, "bf16"), gpu)
+    for l, (L, P) in enumerate(pairs):
+        probe = mmf.LayerProbe(b * t, d, inner, gpu)
+        x_in = host(cur)
+        out, _ = mmf.layer_fwd(P, cur, None, want_h_last=True, mode="chunk", probe=probe)
+        torch.cuda.synchronize()
+        check_layer_stages(L, x_in, None, probe.host(), host(out), "bf16")
+        cur = out
+    assert cur.dtype == torch.bfloat16
+
+
 def test_layer_c1_end_to_end(gpu):
     """370M-width layer, fp32, batch 1, T=128, recurrent scan: stage-fed and free-running against the oracle."""
     import torch
