@@ -252,7 +252,7 @@ def main():
         vendor_int8_gemm(args.shape, args.batch, args.prompt)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
