@@ -365,7 +365,7 @@ size_t scan_workspace_bytes(int64_t b, int64_t d, int chunks) {
 }
 
 constexpr int64_t kTiledMinGroups = 128;     // (sequence, 64-channel) groups that occupy the GPU
-constexpr int64_t kTiledManyGroups = 512;    // from here 4-wave workgroups with 4 chunks in flight
+constexpr int64_t kTiledManyGroups = 512;    // from here 4-wave workgroups (more chunks in flight)
 constexpr int64_t kStreamBytes = 256ll << 20;  // x, f and h together beyond the memory-side cache
 
 // Plan: 1 = recurrent, kScanTiled = single-pass tiled, c >= 2 = two-pass with c
@@ -406,10 +406,13 @@ hipError_t launch_scan_bwd(const float *f, const float *h, const float *h0, cons
         const unsigned grid = (unsigned)(b * groups);
         const bool nt = 20 * b * t * d > kStreamBytes;
         const bool many = b * groups >= kTiledManyGroups;
+        // measured on MI355X: 4-wave workgroups of 4 steps per wave with 6 chunks
+        // ahead once the groups fill the GPU (71 % of 8 TB/s at 16 x 2048 x 2048,
+        // 63 % with 8 steps and 3 ahead)
         if (many && nt)
-            scan_bwd_tiled_kernel<4, 8, 3, true><<<grid, 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+            scan_bwd_tiled_kernel<4, 4, 6, true><<<grid, 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
         else if (many)
-            scan_bwd_tiled_kernel<4, 8, 3, false><<<grid, 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+            scan_bwd_tiled_kernel<4, 4, 6, false><<<grid, 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
         else if (nt)
             scan_bwd_tiled_kernel<16, 8, 1, true><<<grid, 1024, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
         else
@@ -434,13 +437,14 @@ hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h
     if (chunks == kScanTiled) {
         // geometry measured on MI355X: 16-wave workgroups (8 steps each, one chunk
         // ahead) while (sequence, channel-group) pairs are few; 4-wave
-        // workgroups with 4 chunks ahead once they fill the GPU
+        // workgroups with 2 chunks ahead once they fill the GPU (72 % of 8 TB/s
+        // at 16 x 2048 x 2048 against 69 % with 4 ahead)
         const int64_t groups = (d + 63) / 64;
         const unsigned grid = (unsigned)(b * groups);
         const bool nt = 12 * b * t * d > kStreamBytes;
         const bool many = b * groups >= kTiledManyGroups;
-        if (many && nt) scan_tiled_kernel<4, 8, 4, true><<<grid, 256, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
-        else if (many) scan_tiled_kernel<4, 8, 4, false><<<grid, 256, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
+        if (many && nt) scan_tiled_kernel<4, 8, 2, true><<<grid, 256, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
+        else if (many) scan_tiled_kernel<4, 8, 2, false><<<grid, 256, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
         else if (nt) scan_tiled_kernel<16, 8, 1, true><<<grid, 1024, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
         else scan_tiled_kernel<16, 8, 1, false><<<grid, 1024, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
         if (path) *path += std::string("scan_tiled<") + (many ? "4w" : "16w") + (nt ? ",nt" : "") + ">;";
