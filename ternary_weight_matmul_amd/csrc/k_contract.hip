@@ -791,6 +791,164 @@ __global__ __launch_bounds__((gemv_bound<NG, SHARED_A, EPT>())) void tgemv_kerne
 }
 
 // ----------------------------------------------------------------------------
+// Decode at one row: the contraction quantises its own input row
+// ----------------------------------------------------------------------------
+// With a single row, quantising it costs each workgroup a few VALU operations
+// per thread, less than the launch of a separate quantiser. Every thread loads
+// its 4-element chunks of the raw row first, then the weights of its wave's
+// slices (SPW per wave), so the weights are in flight while the row is reduced:
+// sum x^2 (binary64) and max |x| meet in LDS in one round (no gain: max |x r| =
+// (max |x|) r exactly), the codes go to LDS, and each wave reads its
+// activation fragments from there (all 16 fragment rows read the one row).
+// The MFMAs, the all-ones sum of codes and the epilogue are those of the GEMV;
+// only row 0 is stored. Same codes and scale as the separate quantiser (its
+// operations, binary64 sum in another order).
+template <int NG, int EPI, typename XT, typename RT, int CB, int SPW>
+__global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, const XT *__restrict__ x, float eps,
+                                                         const int nslices) {
+    constexpr int WPL = 4, MAXCH = 4;
+    constexpr int PART = CB * NG * 16;  // row 0 of each wave's partial sums
+    extern __shared__ int32_t part[];   // [waves][PART], then the row's codes
+    __shared__ double red_d[16];
+    __shared__ float red_f[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int lc = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * 16 * CB;
+    const int K = p.k, KW = K >> 4, nch = K >> 2, T = blockDim.x;
+    uint32_t *codes = reinterpret_cast<uint32_t *>(part + nw * PART);
+    // 1. the row (straight-line, clamped chunk indices)
+    float xv[MAXCH][4];
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j) {
+        const float4 v = load_act4(x, 4 * (int64_t)min(tid + j * T, nch - 1));
+        xv[j][0] = v.x; xv[j][1] = v.y; xv[j][2] = v.z; xv[j][3] = v.w;
+    }
+    // 2. the weights of the wave's slices (a wave without a second slice loads the last again)
+    int gn[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) gn[cb] = min(n0 + cb * 16 + lc, p.nc - 1);
+    const bool whole = (KW % (4 * WPL)) == 0;
+    uint32_t bw[SPW][CB][NG][WPL];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        const int sl = min(wave + sp * nw, nslices - 1);
+        const int w0 = sl * 4 * WPL + lg * WPL;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t *src = p.B[g] + (int64_t)gn[cb] * KW;
+                if (whole) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(src + w0);
+                    bw[sp][cb][g][0] = v.x; bw[sp][cb][g][1] = v.y; bw[sp][cb][g][2] = v.z; bw[sp][cb][g][3] = v.w;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < WPL; ++j) {
+                        const uint32_t v = src[min(w0 + j, KW - 1)];
+                        bw[sp][cb][g][j] = w0 + j < KW ? v : 0u;
+                    }
+                }
+            }
+    }
+    // epilogue operands of row 0 (threads < 16 CB)
+    float mu_v[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) mu_v[g] = *p.mu[g];
+    constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
+    const int ec = n0 + (tid >> 4) * 16 + (tid & 15);
+    float pre = 0.0f;
+    if constexpr (PRE) {
+        const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
+        pre = load_act(pre_src, (int64_t)(ec < p.nc ? ec : p.nc - 1));
+    }
+    // 3. sum x^2 and max |x| in one round
+    double ss = 0.0;
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j)
+        if (tid + j * T < nch)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ss += (double)xv[j][e] * (double)xv[j][e];
+                mx = fmaxf(mx, fabsf(xv[j][e]));
+            }
+    ss = wave_sum(ss);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        red_d[wave] = ss;
+        red_f[wave] = mx;
+    }
+    __syncthreads();
+    ss = 0.0;
+    mx = 0.0f;
+    for (int w = 0; w < nw; ++w) {
+        ss += red_d[w];
+        mx = fmaxf(mx, red_f[w]);
+    }
+    const float r = rms_factor(ss, K, eps);
+    const float sc = quant_scale(__fmul_rn(mx, r));
+    // 4. the codes to LDS
+#pragma unroll
+    for (int j = 0; j < MAXCH; ++j) {
+        const int c = tid + j * T;
+        if (c < nch)
+            codes[c] = pack_codes4(quant_code(__fmul_rn(xv[j][0], r), sc), quant_code(__fmul_rn(xv[j][1], r), sc),
+                                   quant_code(__fmul_rn(xv[j][2], r), sc), quant_code(__fmul_rn(xv[j][3], r), sc));
+    }
+    __syncthreads();
+    // 5. the contraction
+    i32x4 acc[CB][NG], accq = i32x4{};
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[cb][g] = i32x4{};
+    const i32x4 *cw = reinterpret_cast<const i32x4 *>(codes);
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        const int sl = wave + sp * nw;
+        if (sl < nslices) {
+#pragma unroll
+            for (int j = 0; j < WPL; ++j) {
+                const int w = sl * 4 * WPL + lg * WPL + j;
+                const i32x4 a = cw[min(w, KW - 1)];
+                const int32_t o = w < KW ? 0x01010101 : 0;
+                const i32x4 ones = {o, o, o, o};
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        acc[cb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, decode_word(bw[sp][cb][g][j]), acc[cb][g],
+                                                                           0, 0, 0);
+                accq = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, ones, accq, 0, 0, 0);
+            }
+        }
+    }
+    // row 0 of the result lives in register 0 of lanes 0..15
+    if (lg == 0) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) part[wave * PART + (cb * NG + g) * 16 + lc] = acc[cb][g][0] - accq[0];
+    }
+    __syncthreads();
+    // 6. the epilogue of row 0: 16 CB outputs
+    const int active = nw < nslices ? nw : nslices;
+    if (tid < 16 * CB && ec < p.nc) {
+        const int cb = tid >> 4, c = tid & 15;
+        int32_t v[NG];
+        float dq[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            int32_t sum = 0;
+            for (int w = 0; w < active; ++w) sum += part[w * PART + (cb * NG + g) * 16 + c];
+            v[g] = sum;
+            dq[g] = __builtin_amdgcn_rcpf(sc * __fdiv_rn(1.0f, fmaxf(mu_v[g], 1e-5f)));
+        }
+        epilogue_vals<EPI, NG, true>(p, 0, ec, v, dq, pre);
+    }
+}
+
+// ----------------------------------------------------------------------------
 // Host dispatch
 // ----------------------------------------------------------------------------
 static const char *epi_name(EpiKind e) {
@@ -896,6 +1054,64 @@ static void run_gemv(const ContractArgs &a, hipStream_t st) {
         }
     }
     run_gemv_t<NG, SH, EPI, float>(a, st);
+}
+
+template <int NG, int EPI, typename XT, typename RT, int CB>
+static void run_row_cb(const ContractArgs &a, const void *x, float eps, hipStream_t st) {
+    const int kw = a.k >> 4;
+    const int nslices = (kw + 15) / 16;
+    int waves = nslices < 16 ? nslices : 16;
+    const dim3 grid((unsigned)((a.nc + 16 * CB - 1) / (16 * CB)));
+    const size_t lds = (size_t)waves * CB * NG * 16 * sizeof(int32_t) + (size_t)a.k;
+    const XT *xp = static_cast<const XT *>(x);
+    if (nslices <= waves) tgemv_row_kernel<NG, EPI, XT, RT, CB, 1><<<grid, waves * 64, lds, st>>>(a, xp, eps, nslices);
+    else tgemv_row_kernel<NG, EPI, XT, RT, CB, 2><<<grid, waves * 64, lds, st>>>(a, xp, eps, nslices);
+}
+
+template <int NG, int EPI, typename XT, typename RT>
+static void run_row(const ContractArgs &a, const void *x, float eps, hipStream_t st) {
+    switch (gemv_channel_blocks(a.nc, NG, a.k, 1)) {
+        case 4:
+            if constexpr (NG == 1) { run_row_cb<NG, EPI, XT, RT, 4>(a, x, eps, st); break; }
+            [[fallthrough]];
+        case 2:
+            if constexpr (NG <= 2) { run_row_cb<NG, EPI, XT, RT, 2>(a, x, eps, st); break; }
+            [[fallthrough]];
+        default: run_row_cb<NG, EPI, XT, RT, 1>(a, x, eps, st); break;
+    }
+}
+
+bool contract_row_supported(int64_t m, int k, EpiKind epi) {
+    return m == 1 && k % 16 == 0 && k <= 8192 &&
+           (epi == EPI_GATES_STEP || epi == EPI_GLU || epi == EPI_RESID || epi == EPI_LINEAR);
+}
+
+hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x, ActType xt, float eps,
+                               hipStream_t st, std::string *path) {
+    const bool xb = xt == ACT_BF16, rb = a.res_type == ACT_BF16;
+    switch (epi) {
+        case EPI_GATES_STEP:
+            if (xb) run_row<3, EPI_GATES_STEP, uint16_t, float>(a, x, eps, st);
+            else run_row<3, EPI_GATES_STEP, float, float>(a, x, eps, st);
+            break;
+        case EPI_GLU:
+            if (xb) run_row<2, EPI_GLU, uint16_t, float>(a, x, eps, st);
+            else run_row<2, EPI_GLU, float, float>(a, x, eps, st);
+            break;
+        case EPI_RESID:
+            if (xb && rb) run_row<1, EPI_RESID, uint16_t, uint16_t>(a, x, eps, st);
+            else if (xb) run_row<1, EPI_RESID, uint16_t, float>(a, x, eps, st);
+            else if (rb) run_row<1, EPI_RESID, float, uint16_t>(a, x, eps, st);
+            else run_row<1, EPI_RESID, float, float>(a, x, eps, st);
+            break;
+        case EPI_LINEAR:
+            if (xb) run_row<1, EPI_LINEAR, uint16_t, float>(a, x, eps, st);
+            else run_row<1, EPI_LINEAR, float, float>(a, x, eps, st);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    if (path) *path += std::string("tgemv_row<") + epi_name(epi) + ">;";
+    return hipGetLastError();
 }
 
 static bool use_gemv(int64_t m) { return m <= 64; }

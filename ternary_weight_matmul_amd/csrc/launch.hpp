@@ -95,6 +95,12 @@ hipError_t quant_contract_expired_waits(unsigned *count);
 hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a,
                            hipStream_t stream, std::string *path);
 
+// Decode at one row without a gain: the contraction quantises its input row x
+// (type xt) itself in every workgroup (k <= 8192); a.A, a.s, a.sumq unused.
+bool contract_row_supported(int64_t m, int k, EpiKind epi);
+hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x, ActType xt, float eps,
+                               hipStream_t st, std::string *path);
+
 // Whether the contraction over m rows forms each row's sum of codes itself
 // (the decode GEMV does); otherwise it reads the quantiser's sumq.
 bool contract_sums_codes(int64_t m);

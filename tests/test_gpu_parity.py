@@ -933,6 +933,65 @@ def test_generate_step_graph_replays(gpu):
         mmf.bitlinear_fwd(x, head)  # unrelated eager work between replays
 
 
+ROW_CASES = [
+    # d, inner, act: one row, no gains -> the contractions quantise their own input row
+    (256, 512, "bf16"),
+    (272, 1040, "f32"),     # slices past the row end
+    (2048, 5632, "bf16"),   # the 1.3B decode shape
+    (2560, 6912, "f32"),    # the 2.7B width, two slices per wave in down_proj
+]
+
+
+@pytest.mark.parametrize("d,inner,act", ROW_CASES)
+def test_decode_row_path_matches_separate(gpu, d, inner, act):
+    """At one row the default decode step lets i/f/g, gate_proj and down_proj quantise their own
+    input row; over a chain of steps it must give the separate kernels' outputs and states bit
+    for bit."""
+    import torch
+    mmf = _mmf()
+    _, P = make_pair(d, inner, 970 + d, gpu)
+    xs = [synth.activations((1, d), 971 + s_, act) for s_ in range(4)]
+    h0 = synth.activations((1, d), 975)
+    res = {}
+    for mode in ("auto", "separate"):
+        mmf.set_decode_kernel(mode)
+        try:
+            h = dev(h0, gpu)
+            outs = []
+            for xv in xs:
+                xd = bf16_tensor(xv, gpu) if act == "bf16" else dev(xv, gpu)
+                outs.append(host(mmf.layer_decode_step(P, xd, h)))
+                if mode == "auto":
+                    steps = mmf.last_path().split(";")
+                    assert "tgemv_row<resid>" in steps and not any(k.startswith("norm_quant_row") for k in steps)
+            torch.cuda.synchronize()
+            res[mode] = (outs, host(h))
+        finally:
+            mmf.set_decode_kernel("auto")
+    for a_, b_ in zip(res["auto"][0], res["separate"][0]):
+        assert_equal(a_, b_, "out")
+    assert_equal(res["auto"][1], res["separate"][1], "h")
+
+
+def test_decode_row_path_needs_one_row_and_no_gains(gpu):
+    mmf = _mmf()
+    _, P = make_pair(256, 512, 980, gpu, "shared")  # gains: the separate quantisers run
+    x = bf16_tensor(synth.activations((1, 256), 981, "bf16"), gpu)
+    mmf.layer_decode_step(P, x, dev(synth.activations((1, 256), 982), gpu))
+    assert "tgemv_row" not in mmf.last_path()
+    _, P2 = make_pair(256, 512, 983, gpu)
+    x2 = bf16_tensor(synth.activations((2, 256), 984, "bf16"), gpu)
+    mmf.layer_decode_step(P2, x2, dev(synth.activations((2, 256), 985), gpu))
+    assert "tgemv_row" not in mmf.last_path()
+
+
+def test_decode_row_path_graph_replays(gpu):
+    _, P = make_pair(2048, 5632, 990, gpu)
+    x = bf16_tensor(synth.activations((1, 2048), 991, "bf16"), gpu)
+    h0 = dev(synth.activations((1, 2048), 992), gpu)
+    _graph_replays(P, x, h0, "tgemv_row<", gpu)
+
+
 def test_decode_xcd_kernel_unsupported_shapes(gpu):
     """Forcing the one-XCD kernel where it does not apply is an error, never a silent fallback."""
     mmf = _mmf()
