@@ -302,8 +302,12 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
  *  x, out : [b][d] in dtype act.  h : [b][d] fp32, read as h_{t-1} and
  *  overwritten with h_t.  Equivalent to mmf_layer_fwd with t = 1, h0 = h.
  *  Errors as mmf_layer_fwd (workspace from mmf_layer_workspace_size(w, b, 1)).
- *  Three implementations give the same bits: separate kernels per stage
- *  (quantisers and contractions: eight launches); four contraction kernels
+ *  Four implementations give the same bits: separate kernels per stage
+ *  (quantisers and contractions: eight launches); contractions that quantise
+ *  their own input rows in every workgroup, where a row fits (b <= 16, no
+ *  probe, no gains on i/f/g, gate_proj and down_proj; one row up to 8192
+ *  wide, 2 to 16 rows up to 2048; the other stages keep their quantisers:
+ *  five launches at one row, six at the 1.3B shape and 16 rows); four contraction kernels
  *  whose first b workgroups quantise the input rows and hand them to the
  *  others within the launch through device-scope stores and a counter (b <=
  *  16, no probe, equal i/f/g gains, d and inner multiples of 256, d <= 3072,
@@ -324,12 +328,13 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
 
 /*
  * mmf_set_decode_kernel -- which implementation mmf_layer_decode_step uses,
- * process-wide: 0 = the fastest implementation measured on MI355X (default;
- * at present the separate kernels for every shape: at the 1.3B shape they
- * take 29 / 34 us per layer at batch 1 / 16 in a HIP graph, the four fused
- * kernels 34 / 46 (a hand-off across XCDs within a launch costs about what a
- * kernel boundary does), and the one-XCD kernel 45 / 46, held to one XCD's
- * share of HBM bandwidth);
+ * process-wide: 0 = the fastest implementation measured on MI355X (default:
+ * the self-quantising contractions where they apply, else the separate
+ * kernels; at the 1.3B shape in a HIP graph they take 23 / 33 us per layer
+ * at batch 1 / 16, the separate kernels 29 / 33, the four fused kernels
+ * 34 / 46 (a hand-off across XCDs within a launch costs about what a kernel
+ * boundary does), and the one-XCD kernel 45 / 46, held to one XCD's share
+ * of HBM bandwidth);
  * 1 = always the separate kernels; 2 = only the one-XCD kernel; 3 = only the
  * four fused kernels (2 and 3: UNSUPPORTED where they do not apply).
  * INVALID_ARG for other values.

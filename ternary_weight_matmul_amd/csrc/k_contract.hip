@@ -31,6 +31,8 @@
 #include "launch.hpp"
 #include "epilogue.hpp"
 
+#include <mutex>
+
 namespace mmf {
 
 // ----------------------------------------------------------------------------
@@ -1056,16 +1058,200 @@ static void run_gemv(const ContractArgs &a, hipStream_t st) {
     run_gemv_t<NG, SH, EPI, float>(a, st);
 }
 
+// Decode at a few rows: the same, with a wave per input row (RPW rows per wave
+// at most): the row's sums are wave reductions, its codes go to LDS at a
+// padded row stride (K + 16 bytes: the 16 fragment rows fall in different
+// banks) with its scale, and the epilogue is the GEMV's over the 16-row block.
+template <int NG, int EPI, typename XT, typename RT, int CB, int SPW, int CPL, int RPW>
+__global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, const XT *__restrict__ x, float eps,
+                                                          const int nslices) {
+    constexpr int WPL = 4;
+    constexpr int PART = CB * NG * 256;
+    extern __shared__ int32_t part[];  // [waves][PART], then codes [16][K + 16], then scales [16]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int lc = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * 16 * CB;
+    const int K = p.k, KW = K >> 4, nch = K >> 2, stride = K + 16;
+    const int M = (int)p.m;
+    int8_t *codes = reinterpret_cast<int8_t *>(part + nw * PART);
+    float *srow = reinterpret_cast<float *>(codes + 16 * stride);
+    // 1. this wave's rows (straight-line, clamped)
+    float xv[RPW][CPL][4];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int rr = min(wave + i * nw, M - 1);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const float4 v = load_act4(x + (int64_t)rr * K, 4 * (int64_t)min(lane + 64 * j, nch - 1));
+            xv[i][j][0] = v.x; xv[i][j][1] = v.y; xv[i][j][2] = v.z; xv[i][j][3] = v.w;
+        }
+    }
+    // 2. the weights of the wave's slices
+    int gn[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) gn[cb] = min(n0 + cb * 16 + lc, p.nc - 1);
+    const bool whole = (KW % (4 * WPL)) == 0;
+    uint32_t bw[SPW][CB][NG][WPL];
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        const int sl = min(wave + sp * nw, nslices - 1);
+        const int w0 = sl * 4 * WPL + lg * WPL;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t *src = p.B[g] + (int64_t)gn[cb] * KW;
+                if (whole) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(src + w0);
+                    bw[sp][cb][g][0] = v.x; bw[sp][cb][g][1] = v.y; bw[sp][cb][g][2] = v.z; bw[sp][cb][g][3] = v.w;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < WPL; ++j) {
+                        const uint32_t v = src[min(w0 + j, KW - 1)];
+                        bw[sp][cb][g][j] = w0 + j < KW ? v : 0u;
+                    }
+                }
+            }
+    }
+    // epilogue operands (output idx: row (idx / 16) % 16, channel block idx / 256, channel idx % 16)
+    constexpr int EPT = 4;
+    constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_GATES_STEP;
+    float pre[EPT];
+    const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int idx = tid + e * (int)blockDim.x;
+        const int m = min((idx >> 4) & 15, M - 1);
+        const int c = n0 + ((idx >> 8) % CB) * 16 + (idx & 15);
+        pre[e] = PRE ? load_act(pre_src, (int64_t)m * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
+    }
+    float mu_v[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) mu_v[g] = *p.mu[g];
+    // 3. each row: sum x^2 and max |x| (wave reductions), scale, codes to LDS
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = wave + i * nw;
+        if (r < M) {
+            double ss = 0.0;
+            float mx = 0.0f;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j)
+                if (lane + 64 * j < nch)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ss += (double)xv[i][j][e] * (double)xv[i][j][e];
+                        mx = fmaxf(mx, fabsf(xv[i][j][e]));
+                    }
+            ss = wave_sum(ss);
+            mx = wave_max(mx);
+            const float rr = rms_factor(ss, K, eps);
+            const float sc = quant_scale(__fmul_rn(mx, rr));
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int c = lane + 64 * j;
+                if (c < nch)
+                    *reinterpret_cast<uint32_t *>(codes + r * stride + 4 * c) =
+                        pack_codes4(quant_code(__fmul_rn(xv[i][j][0], rr), sc), quant_code(__fmul_rn(xv[i][j][1], rr), sc),
+                                    quant_code(__fmul_rn(xv[i][j][2], rr), sc), quant_code(__fmul_rn(xv[i][j][3], rr), sc));
+            }
+            if (lane == 0) srow[r] = sc;
+        }
+    }
+    __syncthreads();
+    // 4. the contraction (fragment row lc reads input row min(lc, M - 1))
+    i32x4 acc[CB][NG], accq = i32x4{};
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[cb][g] = i32x4{};
+    const int8_t *arow = codes + min(lc, M - 1) * stride;
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+        const int sl = wave + sp * nw;
+        if (sl < nslices) {
+#pragma unroll
+            for (int j = 0; j < WPL; ++j) {
+                const int w = sl * 4 * WPL + lg * WPL + j;
+                const i32x4 a = *reinterpret_cast<const i32x4 *>(arow + 16 * min(w, KW - 1));
+                const int32_t o = w < KW ? 0x01010101 : 0;
+                const i32x4 ones = {o, o, o, o};
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        acc[cb][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, decode_word(bw[sp][cb][g][j]), acc[cb][g],
+                                                                           0, 0, 0);
+                accq = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, ones, accq, 0, 0, 0);
+            }
+        }
+    }
+    int32_t *mine = part + wave * PART;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mine[(cb * NG + g) * 256 + (4 * lg + i) * 16 + lc] = acc[cb][g][i] - accq[i];
+    __syncthreads();
+    // 5. the epilogue of the 16-row block
+    float sw[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) sw[g] = __fdiv_rn(1.0f, fmaxf(mu_v[g], 1e-5f));
+    const int active = nw < nslices ? nw : nslices;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int idx = tid + e * (int)blockDim.x;
+        const int cb = (idx >> 8) % CB, r = (idx >> 4) & 15, c = idx & 15;
+        const int ch = n0 + cb * 16 + c;
+        if (idx < CB * 256 && r < M && ch < p.nc) {
+            int32_t v[NG];
+            float dq[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                int32_t sum = 0;
+                for (int w = 0; w < active; ++w) sum += part[w * PART + (cb * NG + g) * 256 + r * 16 + c];
+                v[g] = sum;
+                dq[g] = __builtin_amdgcn_rcpf(srow[r] * sw[g]);
+            }
+            epilogue_vals<EPI, NG, true>(p, r, ch, v, dq, pre[e]);
+        }
+    }
+}
+
+// The multi-row kernels take more dynamic LDS than the default 64 KB: each
+// kernel's limit is raised once, before its first launch.
+template <auto KERNEL, typename XT>
+static void launch_rows(const ContractArgs &a, const XT *x, float eps, int nslices, dim3 grid, int waves, size_t lds,
+                        hipStream_t st) {
+    static std::once_flag once;
+    std::call_once(once, [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(KERNEL), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  160 * 1024);
+    });
+    KERNEL<<<grid, waves * 64, lds, st>>>(a, x, eps, nslices);
+}
+
 template <int NG, int EPI, typename XT, typename RT, int CB>
 static void run_row_cb(const ContractArgs &a, const void *x, float eps, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 15) / 16;
-    int waves = nslices < 16 ? nslices : 16;
     const dim3 grid((unsigned)((a.nc + 16 * CB - 1) / (16 * CB)));
-    const size_t lds = (size_t)waves * CB * NG * 16 * sizeof(int32_t) + (size_t)a.k;
     const XT *xp = static_cast<const XT *>(x);
-    if (nslices <= waves) tgemv_row_kernel<NG, EPI, XT, RT, CB, 1><<<grid, waves * 64, lds, st>>>(a, xp, eps, nslices);
-    else tgemv_row_kernel<NG, EPI, XT, RT, CB, 2><<<grid, waves * 64, lds, st>>>(a, xp, eps, nslices);
+    if (a.m == 1) {
+        const int waves = nslices < 16 ? nslices : 16;
+        const size_t lds = (size_t)waves * CB * NG * 16 * sizeof(int32_t) + (size_t)a.k;
+        if (nslices <= waves) tgemv_row_kernel<NG, EPI, XT, RT, CB, 1><<<grid, waves * 64, lds, st>>>(a, xp, eps, nslices);
+        else tgemv_row_kernel<NG, EPI, XT, RT, CB, 2><<<grid, waves * 64, lds, st>>>(a, xp, eps, nslices);
+        return;
+    }
+    // 2 to 8 rows of at most 2048: a wave per row (8 chunks of 4 per lane)
+    const int m = (int)a.m;
+    int waves = nslices < 16 ? nslices : 16;
+    if (waves < m) waves = m;
+    const size_t lds = (size_t)waves * CB * NG * 256 * sizeof(int32_t) + (size_t)16 * (a.k + 16) + 16 * sizeof(float);
+    if (nslices > waves) launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 2, 8, 1>>(a, xp, eps, nslices, grid, waves, lds, st);
+    else launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 1, 8, 1>>(a, xp, eps, nslices, grid, waves, lds, st);
 }
 
 template <int NG, int EPI, typename XT, typename RT>
@@ -1081,9 +1267,14 @@ static void run_row(const ContractArgs &a, const void *x, float eps, hipStream_t
     }
 }
 
+// One row up to k = 8192; 2 to 16 rows up to k = 2048, one wave per row (a
+// wider row leaves the multi-row kernel too few registers, and its codes in
+// LDS would limit the workgroups per CU).
 bool contract_row_supported(int64_t m, int k, EpiKind epi) {
-    return m == 1 && k % 16 == 0 && k <= 8192 &&
-           (epi == EPI_GATES_STEP || epi == EPI_GLU || epi == EPI_RESID || epi == EPI_LINEAR);
+    const bool kind = epi == EPI_GATES_STEP || epi == EPI_GLU || epi == EPI_RESID || epi == EPI_LINEAR;
+    if (!kind || k % 16 || m < 1) return false;
+    if (m == 1) return k <= 8192;
+    return m <= 16 && k <= 2048;
 }
 
 hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x, ActType xt, float eps,

@@ -337,27 +337,39 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
     });
 }
 
-// The decode step at one row without gains: the i/f/g, gate_proj and down_proj
-// contractions quantise their own input row (launch_contract_row), so only
-// g_norm keeps a separate quantiser: five kernels instead of eight.
-hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, float *h,
+// The decode step at up to 16 rows without gains: a contraction quantises its
+// own input rows (launch_contract_row) where that costs each workgroup less
+// than a quantiser launch (contract_row_supported); otherwise the separate
+// quantiser runs first. g_norm keeps its own quantiser. At one row: five
+// kernels instead of eight; at 16 rows of 2048 with an inner width of 5632,
+// six (down_proj's rows are too wide).
+
+hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b, float *h,
                            const LayerWs &L, hipStream_t st, std::string *path) {
     const ActType at = act(actt);
     const int d = w->d, inner = w->inner;
     const float eps = w->eps;
+    auto fused = [&](int k, EpiKind epi) { return contract_row_supported(b, k, epi); };
+    hipError_t e;
     ContractArgs ca{};
     const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
     for (int q = 0; q < 3; ++q) { ca.B[q] = tw[q]->packed; ca.mu[q] = tw[q]->mu; }
-    ca.m = 1; ca.nc = d; ca.k = d;
+    ca.m = b; ca.nc = d; ca.k = d;
     ca.out0 = h; ca.out1 = L.g; ca.out_type = ACT_F32; ca.aux_type = at;
-    hipError_t e = timed("tgemv_row<gates_step>", 1, 3 * d, d, st,
-                         [&] { return launch_contract_row(ca, EPI_GATES_STEP, x, at, eps, st, path); });
+    if (fused(d, EPI_GATES_STEP)) {
+        e = timed("tgemv_row<gates_step>", b, 3 * d, d, st,
+                  [&] { return launch_contract_row(ca, EPI_GATES_STEP, x, at, eps, st, path); });
+    } else {
+        e = t_norm_quant(x, at, b, d, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
+        for (int q = 0; q < 3; ++q) { ca.A[q] = L.codes_b; ca.s[q] = L.s_b; ca.sumq[q] = L.sq_b; }
+        if (e == hipSuccess) e = t_contract(ca, EPI_GATES_STEP, 3, true, st, path);
+    }
     if (e != hipSuccess) return e;
-    e = t_gnorm_quant(h, L.g, at, 1, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, nullptr, st, path);
+    e = t_gnorm_quant(h, L.g, at, b, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, nullptr, st, path);
     if (e != hipSuccess) return e;
     ContractArgs co{};
     for (int q = 0; q < 3; ++q) { co.A[q] = L.codes_b; co.s[q] = L.s_b; co.sumq[q] = L.sq_b; co.B[q] = w->o.packed; co.mu[q] = w->o.mu; }
-    co.m = 1; co.nc = d; co.k = d;
+    co.m = b; co.nc = d; co.k = d;
     co.out0 = L.x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
     if ((e = t_contract(co, EPI_RESID, 1, true, st, path)) != hipSuccess) return e;
     ContractArgs cg{};
@@ -365,17 +377,28 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
     cg.B[0] = w->gate.packed;
     cg.B[1] = w->gate.packed + (size_t)inner * (d / 16);
     cg.B[2] = cg.B[1];
-    cg.m = 1; cg.nc = inner; cg.k = d;
+    cg.m = b; cg.nc = inner; cg.k = d;
     cg.out0 = L.z; cg.aux_type = at;
-    e = timed("tgemv_row<glu>", 1, 2 * inner, d, st,
-              [&] { return launch_contract_row(cg, EPI_GLU, L.x1, ACT_F32, eps, st, path); });
+    if (fused(d, EPI_GLU)) {
+        e = timed("tgemv_row<glu>", b, 2 * inner, d, st,
+                  [&] { return launch_contract_row(cg, EPI_GLU, L.x1, ACT_F32, eps, st, path); });
+    } else {
+        e = t_norm_quant(L.x1, ACT_F32, b, d, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
+        for (int q = 0; q < 3; ++q) { cg.A[q] = L.codes_b; cg.s[q] = L.s_b; cg.sumq[q] = L.sq_b; }
+        if (e == hipSuccess) e = t_contract(cg, EPI_GLU, 2, true, st, path);
+    }
     if (e != hipSuccess) return e;
     ContractArgs cd{};
     for (int q = 0; q < 3; ++q) { cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
-    cd.m = 1; cd.nc = d; cd.k = inner;
+    cd.m = b; cd.nc = d; cd.k = inner;
     cd.out0 = out; cd.out_type = at; cd.res = L.x1; cd.res_type = ACT_F32;
-    return timed("tgemv_row<resid>", 1, d, inner, st,
-                 [&] { return launch_contract_row(cd, EPI_RESID, L.z, at, eps, st, path); });
+    if (fused(inner, EPI_RESID))
+        return timed("tgemv_row<resid>", b, d, inner, st,
+                     [&] { return launch_contract_row(cd, EPI_RESID, L.z, at, eps, st, path); });
+    e = t_norm_quant(L.z, at, b, inner, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
+    for (int q = 0; q < 3; ++q) { cd.A[q] = L.codes_b; cd.s[q] = L.s_b; cd.sumq[q] = L.sq_b; }
+    if (e == hipSuccess) e = t_contract(cd, EPI_RESID, 1, true, st, path);
+    return e;
 }
 
 // Quantise x for i/f/g (once when their gains coincide) and fill the contraction's A side.
@@ -861,13 +884,13 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
         if (r == MMF_OK) g_path = path;
         return r;
     }
-    const bool row_ok = b == 1 && !probe && shared_ifg(w) && !w->i.norm_w && !w->gate.norm_w && !w->down.norm_w &&
-                        contract_row_supported(1, w->d, EPI_GATES_STEP) && contract_row_supported(1, w->inner, EPI_RESID);
+    const bool row_ok = b >= 1 && b <= 16 && !probe && shared_ifg(w) && !w->i.norm_w && !w->gate.norm_w &&
+                        !w->down.norm_w;
     if (row_ok && mode == 0) {
         Carver c(ws);
         LayerWs L;
         layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
-        e = decode_row_step(w, x, out, actt, h, L, stream, &path);
+        e = decode_row_step(w, x, out, actt, b, h, L, stream, &path);
         mmf_status r = hip_status(e, "mmf_layer_decode_step");
         if (r == MMF_OK) g_path = path;
         return r;

@@ -934,24 +934,28 @@ def test_generate_step_graph_replays(gpu):
 
 
 ROW_CASES = [
-    # d, inner, act: one row, no gains -> the contractions quantise their own input row
-    (256, 512, "bf16"),
-    (272, 1040, "f32"),     # slices past the row end
-    (2048, 5632, "bf16"),   # the 1.3B decode shape
-    (2560, 6912, "f32"),    # the 2.7B width, two slices per wave in down_proj
+    # b, d, inner, act: no gains -> contractions quantise their own input rows where cheap
+    (1, 256, 512, "bf16"),
+    (1, 272, 1040, "f32"),     # slices past the row end
+    (1, 2048, 5632, "bf16"),   # the 1.3B decode shape
+    (1, 2560, 6912, "f32"),    # the 2.7B width, two slices per wave in down_proj
+    (2, 2048, 5632, "bf16"),   # a wave per row
+    (5, 272, 1040, "f32"),
+    (16, 2048, 5632, "bf16"),  # the 1.3B decode batch: i/f/g and gate_proj fused, down_proj not
+    (8, 2560, 6912, "bf16"),   # rows wider than 2048: the separate quantisers
 ]
 
 
-@pytest.mark.parametrize("d,inner,act", ROW_CASES)
-def test_decode_row_path_matches_separate(gpu, d, inner, act):
-    """At one row the default decode step lets i/f/g, gate_proj and down_proj quantise their own
-    input row; over a chain of steps it must give the separate kernels' outputs and states bit
-    for bit."""
+@pytest.mark.parametrize("b,d,inner,act", ROW_CASES)
+def test_decode_row_path_matches_separate(gpu, b, d, inner, act):
+    """The default decode step lets i/f/g, gate_proj and down_proj quantise their own input rows
+    where that is cheaper than a quantiser launch (one row; up to 16 rows of at most 2048); over
+    a chain of steps it must give the separate kernels' outputs and states bit for bit."""
     import torch
     mmf = _mmf()
     _, P = make_pair(d, inner, 970 + d, gpu)
-    xs = [synth.activations((1, d), 971 + s_, act) for s_ in range(4)]
-    h0 = synth.activations((1, d), 975)
+    xs = [synth.activations((b, d), 971 + s_, act) for s_ in range(4)]
+    h0 = synth.activations((b, d), 975)
     res = {}
     for mode in ("auto", "separate"):
         mmf.set_decode_kernel(mode)
@@ -963,7 +967,11 @@ def test_decode_row_path_matches_separate(gpu, d, inner, act):
                 outs.append(host(mmf.layer_decode_step(P, xd, h)))
                 if mode == "auto":
                     steps = mmf.last_path().split(";")
-                    assert "tgemv_row<resid>" in steps and not any(k.startswith("norm_quant_row") for k in steps)
+                    fused = [k for k in steps if k.startswith("tgemv_row<")]
+                    widest = 8192 if b == 1 else 2048  # widest input row a contraction quantises itself
+                    want = [e for e, k in (("gates_step", d), ("glu", d), ("resid", inner)) if k <= widest]
+                    assert fused == ["tgemv_row<%s>" % e for e in want], steps
+                    assert sum(k.startswith("norm_quant") for k in steps) == 3 - len(want), steps
             torch.cuda.synchronize()
             res[mode] = (outs, host(h))
         finally:
@@ -973,22 +981,23 @@ def test_decode_row_path_matches_separate(gpu, d, inner, act):
     assert_equal(res["auto"][1], res["separate"][1], "h")
 
 
-def test_decode_row_path_needs_one_row_and_no_gains(gpu):
+def test_decode_row_path_needs_few_rows_and_no_gains(gpu):
     mmf = _mmf()
     _, P = make_pair(256, 512, 980, gpu, "shared")  # gains: the separate quantisers run
     x = bf16_tensor(synth.activations((1, 256), 981, "bf16"), gpu)
     mmf.layer_decode_step(P, x, dev(synth.activations((1, 256), 982), gpu))
     assert "tgemv_row" not in mmf.last_path()
     _, P2 = make_pair(256, 512, 983, gpu)
-    x2 = bf16_tensor(synth.activations((2, 256), 984, "bf16"), gpu)
-    mmf.layer_decode_step(P2, x2, dev(synth.activations((2, 256), 985), gpu))
+    x2 = bf16_tensor(synth.activations((17, 256), 984, "bf16"), gpu)  # more than one row block
+    mmf.layer_decode_step(P2, x2, dev(synth.activations((17, 256), 985), gpu))
     assert "tgemv_row" not in mmf.last_path()
 
 
-def test_decode_row_path_graph_replays(gpu):
+@pytest.mark.parametrize("b", [1, 16])
+def test_decode_row_path_graph_replays(gpu, b):
     _, P = make_pair(2048, 5632, 990, gpu)
-    x = bf16_tensor(synth.activations((1, 2048), 991, "bf16"), gpu)
-    h0 = dev(synth.activations((1, 2048), 992), gpu)
+    x = bf16_tensor(synth.activations((b, 2048), 991, "bf16"), gpu)
+    h0 = dev(synth.activations((b, 2048), 992), gpu)
     _graph_replays(P, x, h0, "tgemv_row<", gpu)
 
 
