@@ -146,6 +146,8 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
         gates: f, x~ (fp32) and g (bf16) written = 10 B; gates_step: h read and written
         (fp32) and g written (bf16) = 10 B; glu: z (bf16) = 2 B; resid: residual read and
         sum written, one fp32 and one bf16 = 6 B; linear: 4 B.
+    tgemv_row<epi,T> (a contraction that quantises its own input rows): as a contraction, with
+      the rows read once in type T (m k sizeof T) in place of the codes, scale and code sum.
     norm_quant<T> (m rows of k): x read (sizeof T) + codes written (1 B) per element, 8 B per row.
     gnorm_quant<T>: h (fp32) and g (sizeof T) read + codes written per element, 8 B per row.
     scan (m = b t, k = d): f and x~ read, h written, 12 B per element.
@@ -158,12 +160,16 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
     if base == "decode_step_xcd":
         wts = 4.0 * n * n + 3.0 * n * k
         return 2.0 * m * wts, wts / 4.0 + m * n * (2.0 * ACT_BYTES + 8.0)
-    if base in ("tgemm", "tgemm_dma", "tgemv"):
+    if base in ("tgemm", "tgemm_dma", "tgemv", "tgemv_row"):
         epi = args[0]
         na = 3 if "split_a" in args else 1
         ng = {"gates": 3, "gates_step": 3, "glu": 2}.get(epi, 1)
         per_c = {"gates": 10, "gates_step": 10, "glu": 2, "resid": 4 + ACT_BYTES, "linear": 4}[epi]
-        nbytes = n * k / 4.0 + na * (m * k + 8.0 * m) + m * (n / ng) * per_c
+        if base == "tgemv_row":
+            rows = m * k * (4.0 if args[1:] == ["f32"] else ACT_BYTES)
+        else:
+            rows = na * (m * k + 8.0 * m)
+        nbytes = n * k / 4.0 + rows + m * (n / ng) * per_c
         return 2.0 * m * n * k, nbytes
     tb = 4 if args[:1] == ["f32"] else ACT_BYTES
     if base == "norm_quant":
@@ -181,6 +187,7 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
 _COMMON = ["device_common.hpp", "launch.hpp"]
 KERNEL_SOURCES = {
     "tgemv": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
+    "tgemv_row": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
     "tgemm": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
     "tgemm_dma": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
     "tgemv_q": ["k_gemv_q.hip", "row_quant.hpp", "epilogue.hpp"] + _COMMON,

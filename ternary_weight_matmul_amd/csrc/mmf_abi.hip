@@ -344,6 +344,11 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
 // kernels instead of eight; at 16 rows of 2048 with an inner width of 5632,
 // six (down_proj's rows are too wide).
 
+// Timing name of a self-quantising contraction: its epilogue and the type of the rows it reads.
+std::string row_name(const char *epi, ActType xt) {
+    return std::string("tgemv_row<") + epi + (xt == ACT_F32 ? ",f32>" : ",bf16>");
+}
+
 hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b, float *h,
                            const LayerWs &L, hipStream_t st, std::string *path) {
     const ActType at = act(actt);
@@ -357,7 +362,7 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
     ca.m = b; ca.nc = d; ca.k = d;
     ca.out0 = h; ca.out1 = L.g; ca.out_type = ACT_F32; ca.aux_type = at;
     if (fused(d, EPI_GATES_STEP)) {
-        e = timed("tgemv_row<gates_step>", b, 3 * d, d, st,
+        e = timed(row_name("gates_step", at), b, 3 * d, d, st,
                   [&] { return launch_contract_row(ca, EPI_GATES_STEP, x, at, eps, st, path); });
     } else {
         e = t_norm_quant(x, at, b, d, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
@@ -380,7 +385,7 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
     cg.m = b; cg.nc = inner; cg.k = d;
     cg.out0 = L.z; cg.aux_type = at;
     if (fused(d, EPI_GLU)) {
-        e = timed("tgemv_row<glu>", b, 2 * inner, d, st,
+        e = timed(row_name("glu", ACT_F32), b, 2 * inner, d, st,
                   [&] { return launch_contract_row(cg, EPI_GLU, L.x1, ACT_F32, eps, st, path); });
     } else {
         e = t_norm_quant(L.x1, ACT_F32, b, d, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
@@ -393,7 +398,7 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
     cd.m = b; cd.nc = d; cd.k = inner;
     cd.out0 = out; cd.out_type = at; cd.res = L.x1; cd.res_type = ACT_F32;
     if (fused(inner, EPI_RESID))
-        return timed("tgemv_row<resid>", b, d, inner, st,
+        return timed(row_name("resid", at), b, d, inner, st,
                      [&] { return launch_contract_row(cd, EPI_RESID, L.z, at, eps, st, path); });
     e = t_norm_quant(L.z, at, b, inner, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
     for (int q = 0; q < 3; ++q) { cd.A[q] = L.codes_b; cd.s[q] = L.s_b; cd.sumq[q] = L.sq_b; }

@@ -30,6 +30,15 @@ def test_gate_groups_share_their_epilogue_bytes():
     assert glu == 2 * 5632 * 2048 / 4 + 1024 * 2048 + 8 * 1024 + 1024 * 5632 * 2
 
 
+def test_self_quantising_contractions_read_rows_not_codes():
+    # gate_proj + up_proj at the 1.3B shape, 16 fp32 rows; i/f/g from 16 bf16 rows
+    _, glu = bench.algorithmic("tgemv_row<glu,f32>", 16, 2 * 5632, 2048)
+    assert glu == 2 * 5632 * 2048 / 4 + 16 * 2048 * 4 + 16 * 5632 * 2
+    _, gates = bench.algorithmic("tgemv_row<gates_step,bf16>", 16, 3 * 2048, 2048)
+    assert gates == 3 * 2048 * 2048 / 4 + 16 * 2048 * 2 + 16 * 2048 * 10
+    assert bench.kernel_files("tgemv_row<resid,bf16> m=1 n=2 k=3") == bench.kernel_files("tgemv<resid>")
+
+
 def test_split_activation_codes_counted_per_group():
     _, shared = bench.algorithmic("tgemm<gates>", 256, 3 * 512, 512)
     _, split = bench.algorithmic("tgemm<gates,split_a>", 256, 3 * 512, 512)
@@ -55,7 +64,7 @@ def test_decode_step_kernel_counts_every_weight_once():
 
 
 def test_every_kernel_name_maps_to_its_sources():
-    names = ["tgemv<resid>", "tgemm<gates,split_a>", "tgemm_dma<glu>", "tgemv_q<gnorm_resid>", "decode_step_xcd",
+    names = ["tgemv<resid>", "tgemv_row<glu,f32>", "tgemm<gates,split_a>", "tgemm_dma<glu>", "tgemv_q<gnorm_resid>", "decode_step_xcd",
              "norm_quant<f32>", "gnorm_quant<bf16>", "scan_tiled", "scan_chunk", "scan_recurrent"]
     csrc = os.path.join(ROOT, "ternary_weight_matmul_amd", "csrc")
     for n in names:
