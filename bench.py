@@ -147,7 +147,8 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
         (fp32) and g written (bf16) = 10 B; glu: z (bf16) = 2 B; resid: residual read and
         sum written, one fp32 and one bf16 = 6 B; linear: 4 B.
     tgemv_row<epi,T> (a contraction that quantises its own input rows): as a contraction, with
-      the rows read once in type T (m k sizeof T) in place of the codes, scale and code sum.
+      the rows read once in type T (m k sizeof T) in place of the codes, scale and code sum;
+      tgemv_row<resid,gnorm,T>: h (fp32) and g (T) per element and g_norm's gain (fp32) per k.
     norm_quant<T> (m rows of k): x read (sizeof T) + codes written (1 B) per element, 8 B per row.
     gnorm_quant<T>: h (fp32) and g (sizeof T) read + codes written per element, 8 B per row.
     scan (m = b t, k = d): f and x~ read, h written, 12 B per element.
@@ -166,7 +167,9 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
         ng = {"gates": 3, "gates_step": 3, "glu": 2}.get(epi, 1)
         per_c = {"gates": 10, "gates_step": 10, "glu": 2, "resid": 4 + ACT_BYTES, "linear": 4}[epi]
         if base == "tgemv_row":
-            rows = m * k * (4.0 if args[1:] == ["f32"] else ACT_BYTES)
+            tb = 4.0 if args[-1] == "f32" else ACT_BYTES
+            # the gated g_norm reads h (fp32), g and g_norm's gain instead of x
+            rows = m * k * (4.0 + tb) + 4.0 * k if "gnorm" in args else m * k * tb
         else:
             rows = na * (m * k + 8.0 * m)
         nbytes = n * k / 4.0 + rows + m * (n / ng) * per_c

@@ -306,8 +306,9 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
  *  (quantisers and contractions: eight launches); contractions that quantise
  *  their own input rows in every workgroup, where a row fits (b <= 16, no
  *  probe, no gains on i/f/g, gate_proj and down_proj; one row up to 8192
- *  wide, 2 to 16 rows up to 2048; the other stages keep their quantisers:
- *  five launches at one row, six at the 1.3B shape and 16 rows); four contraction kernels
+ *  wide, 2 to 16 rows up to 2048; at one row o_proj also forms the gated
+ *  g_norm of h and g unless o_proj has a gain; the other stages keep their
+ *  quantisers: four launches at one row, six at the 1.3B shape and 16 rows); four contraction kernels
  *  whose first b workgroups quantise the input rows and hand them to the
  *  others within the launch through device-scope stores and a counter (b <=
  *  16, no probe, equal i/f/g gains, d and inner multiples of 256, d <= 3072,
@@ -330,7 +331,7 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
  * mmf_set_decode_kernel -- which implementation mmf_layer_decode_step uses,
  * process-wide: 0 = the fastest implementation measured on MI355X (default:
  * the self-quantising contractions where they apply, else the separate
- * kernels; at the 1.3B shape in a HIP graph they take 23 / 33 us per layer
+ * kernels; at the 1.3B shape in a HIP graph they take 21 / 33 us per layer
  * at batch 1 / 16, the separate kernels 29 / 33, the four fused kernels
  * 34 / 46 (a hand-off across XCDs within a launch costs about what a kernel
  * boundary does), and the one-XCD kernel 45 / 46, held to one XCD's share

@@ -795,6 +795,31 @@ __global__ __launch_bounds__((gemv_bound<NG, SHARED_A, EPT>())) void tgemv_kerne
 // ----------------------------------------------------------------------------
 // Decode at one row: the contraction quantises its own input row
 // ----------------------------------------------------------------------------
+// A 4-element chunk at element c4 of the input row that starts at element
+// row_off: x, or h with g and the
+// g_norm gain (1 where there is none: multiplying by 1 is exact).
+template <bool GN, typename XT>
+__device__ __forceinline__ void load_row_chunk(const RowSrc &src, int64_t row_off, int64_t c4, float (&x)[4],
+                                               float (&g)[4], float (&w)[4]) {
+    if constexpr (GN) {
+        const float4 h = load_act4(static_cast<const float *>(src.x) + row_off, c4);
+        const float4 gg = load_act4(static_cast<const XT *>(src.g) + row_off, c4);
+        const float4 ww = src.gnw ? *reinterpret_cast<const float4 *>(src.gnw + c4) : make_float4(1.f, 1.f, 1.f, 1.f);
+        x[0] = h.x; x[1] = h.y; x[2] = h.z; x[3] = h.w;
+        g[0] = gg.x; g[1] = gg.y; g[2] = gg.z; g[3] = gg.w;
+        w[0] = ww.x; w[1] = ww.y; w[2] = ww.z; w[3] = ww.w;
+    } else {
+        const float4 v = load_act4(static_cast<const XT *>(src.x) + row_off, c4);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    }
+}
+
+// y = ((h r_h) w) silu(g), rounded after each product as the g_norm quantiser does.
+__device__ __forceinline__ void gated_norm4(float (&x)[4], const float (&g)[4], const float (&w)[4], float rh) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __fmul_rn(__fmul_rn(__fmul_rn(x[e], rh), w[e]), silu_fast(g[e]));
+}
+
 // With a single row, quantising it costs each workgroup a few VALU operations
 // per thread, less than the launch of a separate quantiser. Every thread loads
 // its 4-element chunks of the raw row first, then the weights of its wave's
@@ -804,14 +829,18 @@ __global__ __launch_bounds__((gemv_bound<NG, SHARED_A, EPT>())) void tgemv_kerne
 // activation fragments from there (all 16 fragment rows read the one row).
 // The MFMAs, the all-ones sum of codes and the epilogue are those of the GEMV;
 // only row 0 is stored. Same codes and scale as the separate quantiser (its
-// operations, binary64 sum in another order).
-template <int NG, int EPI, typename XT, typename RT, int CB, int SPW>
-__global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, const XT *__restrict__ x, float eps,
+// operations, binary64 sum in another order). With GN the row is the gated
+// g_norm of (h, g): a first round forms sum h^2 and r_h, then
+// y = ((h r_h) w) silu(g) is quantised as x is, in the g_norm quantiser's
+// order of roundings.
+template <int NG, int EPI, typename XT, typename RT, int CB, int SPW, bool GN>
+__global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, const RowSrc src, float eps,
                                                          const int nslices) {
     constexpr int WPL = 4, MAXCH = 4;
     constexpr int PART = CB * NG * 16;  // row 0 of each wave's partial sums
     extern __shared__ int32_t part[];   // [waves][PART], then the row's codes
     __shared__ double red_d[16];
+    __shared__ double red_h[16];
     __shared__ float red_f[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int lc = lane & 15, lg = lane >> 4;
@@ -820,11 +849,10 @@ __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, c
     uint32_t *codes = reinterpret_cast<uint32_t *>(part + nw * PART);
     // 1. the row (straight-line, clamped chunk indices)
     float xv[MAXCH][4];
+    [[maybe_unused]] float gv[GN ? MAXCH : 1][4], wv[GN ? MAXCH : 1][4];
 #pragma unroll
-    for (int j = 0; j < MAXCH; ++j) {
-        const float4 v = load_act4(x, 4 * (int64_t)min(tid + j * T, nch - 1));
-        xv[j][0] = v.x; xv[j][1] = v.y; xv[j][2] = v.z; xv[j][3] = v.w;
-    }
+    for (int j = 0; j < MAXCH; ++j)
+        load_row_chunk<GN, XT>(src, 0, 4 * (int64_t)min(tid + j * T, nch - 1), xv[j], gv[GN ? j : 0], wv[GN ? j : 0]);
     // 2. the weights of the wave's slices (a wave without a second slice loads the last again)
     int gn[CB];
 #pragma unroll
@@ -862,6 +890,22 @@ __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, c
     if constexpr (PRE) {
         const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
         pre = load_act(pre_src, (int64_t)(ec < p.nc ? ec : p.nc - 1));
+    }
+    if constexpr (GN) {  // the gated g_norm: sum h^2, then y in place of x
+        double sh = 0.0;
+#pragma unroll
+        for (int j = 0; j < MAXCH; ++j)
+            if (tid + j * T < nch)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sh += (double)xv[j][e] * (double)xv[j][e];
+        sh = wave_sum(sh);
+        if (lane == 0) red_h[wave] = sh;
+        __syncthreads();
+        sh = 0.0;
+        for (int w = 0; w < nw; ++w) sh += red_h[w];
+        const float rh = rms_factor(sh, K, eps);
+#pragma unroll
+        for (int j = 0; j < MAXCH; ++j) gated_norm4(xv[j], gv[j], wv[j], rh);
     }
     // 3. sum x^2 and max |x| in one round
     double ss = 0.0;
@@ -1063,7 +1107,7 @@ static void run_gemv(const ContractArgs &a, hipStream_t st) {
 // padded row stride (K + 16 bytes: the 16 fragment rows fall in different
 // banks) with its scale, and the epilogue is the GEMV's over the 16-row block.
 template <int NG, int EPI, typename XT, typename RT, int CB, int SPW, int CPL, int RPW>
-__global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, const XT *__restrict__ x, float eps,
+__global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, const RowSrc src, float eps,
                                                           const int nslices) {
     constexpr int WPL = 4;
     constexpr int PART = CB * NG * 256;
@@ -1076,15 +1120,14 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
     int8_t *codes = reinterpret_cast<int8_t *>(part + nw * PART);
     float *srow = reinterpret_cast<float *>(codes + 16 * stride);
     // 1. this wave's rows (straight-line, clamped)
-    float xv[RPW][CPL][4];
+    float xv[RPW][CPL][4], unused[4];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int rr = min(wave + i * nw, M - 1);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const float4 v = load_act4(x + (int64_t)rr * K, 4 * (int64_t)min(lane + 64 * j, nch - 1));
-            xv[i][j][0] = v.x; xv[i][j][1] = v.y; xv[i][j][2] = v.z; xv[i][j][3] = v.w;
-        }
+        for (int j = 0; j < CPL; ++j)
+            load_row_chunk<false, XT>(src, (int64_t)rr * K, 4 * (int64_t)min(lane + 64 * j, nch - 1), xv[i][j],
+                                      unused, unused);
     }
     // 2. the weights of the wave's slices
     int gn[CB];
@@ -1221,49 +1264,56 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
 
 // The multi-row kernels take more dynamic LDS than the default 64 KB: each
 // kernel's limit is raised once, before its first launch.
-template <auto KERNEL, typename XT>
-static void launch_rows(const ContractArgs &a, const XT *x, float eps, int nslices, dim3 grid, int waves, size_t lds,
-                        hipStream_t st) {
+template <auto KERNEL>
+static void launch_rows(const ContractArgs &a, const RowSrc &src, float eps, int nslices, dim3 grid, int waves,
+                        size_t lds, hipStream_t st) {
     static std::once_flag once;
     std::call_once(once, [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(KERNEL), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   160 * 1024);
     });
-    KERNEL<<<grid, waves * 64, lds, st>>>(a, x, eps, nslices);
+    KERNEL<<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
 }
 
-template <int NG, int EPI, typename XT, typename RT, int CB>
-static void run_row_cb(const ContractArgs &a, const void *x, float eps, hipStream_t st) {
+template <int NG, int EPI, typename XT, typename RT, int CB, bool GN>
+static void run_row_cb(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 15) / 16;
     const dim3 grid((unsigned)((a.nc + 16 * CB - 1) / (16 * CB)));
-    const XT *xp = static_cast<const XT *>(x);
     if (a.m == 1) {
         const int waves = nslices < 16 ? nslices : 16;
         const size_t lds = (size_t)waves * CB * NG * 16 * sizeof(int32_t) + (size_t)a.k;
-        if (nslices <= waves) tgemv_row_kernel<NG, EPI, XT, RT, CB, 1><<<grid, waves * 64, lds, st>>>(a, xp, eps, nslices);
-        else tgemv_row_kernel<NG, EPI, XT, RT, CB, 2><<<grid, waves * 64, lds, st>>>(a, xp, eps, nslices);
+        if (nslices <= waves)
+            tgemv_row_kernel<NG, EPI, XT, RT, CB, 1, GN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
+        else
+            tgemv_row_kernel<NG, EPI, XT, RT, CB, 2, GN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
         return;
     }
-    // 2 to 8 rows of at most 2048: a wave per row (8 chunks of 4 per lane)
-    const int m = (int)a.m;
-    int waves = nslices < 16 ? nslices : 16;
-    if (waves < m) waves = m;
-    const size_t lds = (size_t)waves * CB * NG * 256 * sizeof(int32_t) + (size_t)16 * (a.k + 16) + 16 * sizeof(float);
-    if (nslices > waves) launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 2, 8, 1>>(a, xp, eps, nslices, grid, waves, lds, st);
-    else launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 1, 8, 1>>(a, xp, eps, nslices, grid, waves, lds, st);
+    // 2 to 16 rows of at most 2048: a wave per row (8 chunks of 4 per lane);
+    // the gated g_norm runs at one row only
+    if constexpr (!GN) {
+        const int m = (int)a.m;
+        int waves = nslices < 16 ? nslices : 16;
+        if (waves < m) waves = m;
+        const size_t lds =
+            (size_t)waves * CB * NG * 256 * sizeof(int32_t) + (size_t)16 * (a.k + 16) + 16 * sizeof(float);
+        if (nslices > waves)
+            launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 2, 8, 1>>(a, src, eps, nslices, grid, waves, lds, st);
+        else
+            launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 1, 8, 1>>(a, src, eps, nslices, grid, waves, lds, st);
+    }
 }
 
-template <int NG, int EPI, typename XT, typename RT>
-static void run_row(const ContractArgs &a, const void *x, float eps, hipStream_t st) {
+template <int NG, int EPI, typename XT, typename RT, bool GN = false>
+static void run_row(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
     switch (gemv_channel_blocks(a.nc, NG, a.k, 1)) {
         case 4:
-            if constexpr (NG == 1) { run_row_cb<NG, EPI, XT, RT, 4>(a, x, eps, st); break; }
+            if constexpr (NG == 1) { run_row_cb<NG, EPI, XT, RT, 4, GN>(a, src, eps, st); break; }
             [[fallthrough]];
         case 2:
-            if constexpr (NG <= 2) { run_row_cb<NG, EPI, XT, RT, 2>(a, x, eps, st); break; }
+            if constexpr (NG <= 2) { run_row_cb<NG, EPI, XT, RT, 2, GN>(a, src, eps, st); break; }
             [[fallthrough]];
-        default: run_row_cb<NG, EPI, XT, RT, 1>(a, x, eps, st); break;
+        default: run_row_cb<NG, EPI, XT, RT, 1, GN>(a, src, eps, st); break;
     }
 }
 
@@ -1277,9 +1327,15 @@ bool contract_row_supported(int64_t m, int k, EpiKind epi) {
     return m <= 16 && k <= 2048;
 }
 
-hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x, ActType xt, float eps,
+// The gated g_norm in o_proj: one row up to k = 8192 (at several rows, each
+// workgroup reading h and g of every row and a second reduction per row cost
+// more than the g_norm quantiser's launch: measured slower at 8 and 16 rows).
+bool contract_row_gnorm_supported(int64_t m, int k) { return m == 1 && k % 16 == 0 && k <= 8192; }
+
+hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *xp, ActType xt, float eps,
                                hipStream_t st, std::string *path) {
     const bool xb = xt == ACT_BF16, rb = a.res_type == ACT_BF16;
+    const RowSrc x{xp, nullptr, nullptr};
     switch (epi) {
         case EPI_GATES_STEP:
             if (xb) run_row<3, EPI_GATES_STEP, uint16_t, float>(a, x, eps, st);
@@ -1302,6 +1358,19 @@ hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x
         default: return hipErrorInvalidValue;
     }
     if (path) *path += std::string("tgemv_row<") + epi_name(epi) + ">;";
+    return hipGetLastError();
+}
+
+hipError_t launch_contract_row_gnorm(const ContractArgs &a, const float *h, const void *g, ActType gt,
+                                     const float *gnw, float eps, hipStream_t st, std::string *path) {
+    if (!contract_row_gnorm_supported(a.m, a.k)) return hipErrorInvalidValue;
+    const RowSrc src{h, g, gnw};
+    const bool gb = gt == ACT_BF16, rb = a.res_type == ACT_BF16;
+    if (gb && rb) run_row<1, EPI_RESID, uint16_t, uint16_t, true>(a, src, eps, st);
+    else if (gb) run_row<1, EPI_RESID, uint16_t, float, true>(a, src, eps, st);
+    else if (rb) run_row<1, EPI_RESID, float, uint16_t, true>(a, src, eps, st);
+    else run_row<1, EPI_RESID, float, float, true>(a, src, eps, st);
+    if (path) *path += "tgemv_row<resid,gnorm>;";
     return hipGetLastError();
 }
 

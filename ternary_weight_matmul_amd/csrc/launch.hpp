@@ -51,6 +51,15 @@ struct ContractArgs {
     float *aux_probe;        // optional fp32 copy of g / z as stored (after rounding to aux_type)
 };
 
+// The input rows of a contraction that quantises them itself: x [m][k] in the
+// activation type, or (gated g_norm) y = ((h r_h) w) silu(g) formed from h
+// [m][k] fp32, g [m][k] in the activation type and the optional gain w [k].
+struct RowSrc {
+    const void *x;       // x, or h
+    const void *g;       // g (gated g_norm only)
+    const float *gnw;    // g_norm's gain or NULL (gated g_norm only)
+};
+
 // One decode step of a block as a single kernel on one XCD (k_decode.hip).
 struct DecodeStepArgs {
     const void *x;           // [b][d] activation dtype
@@ -100,6 +109,10 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
 bool contract_row_supported(int64_t m, int k, EpiKind epi);
 hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x, ActType xt, float eps,
                                hipStream_t st, std::string *path);
+// o_proj over the gated g_norm of (h, g), quantised in each workgroup (EPI_RESID only).
+bool contract_row_gnorm_supported(int64_t m, int k);
+hipError_t launch_contract_row_gnorm(const ContractArgs &a, const float *h, const void *g, ActType gt,
+                                     const float *gnw, float eps, hipStream_t st, std::string *path);
 
 // Whether the contraction over m rows forms each row's sum of codes itself
 // (the decode GEMV does); otherwise it reads the quantiser's sumq.

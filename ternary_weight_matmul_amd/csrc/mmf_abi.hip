@@ -340,9 +340,10 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
 // The decode step at up to 16 rows without gains: a contraction quantises its
 // own input rows (launch_contract_row) where that costs each workgroup less
 // than a quantiser launch (contract_row_supported); otherwise the separate
-// quantiser runs first. g_norm keeps its own quantiser. At one row: five
-// kernels instead of eight; at 16 rows of 2048 with an inner width of 5632,
-// six (down_proj's rows are too wide).
+// quantiser runs first. At one row o_proj also forms the gated g_norm of
+// (h, g) itself unless it has a gain: four kernels instead of eight; at 16
+// rows of 2048 with an inner width of 5632, six (g_norm keeps its quantiser,
+// and down_proj's rows are too wide).
 
 // Timing name of a self-quantising contraction: its epilogue and the type of the rows it reads.
 std::string row_name(const char *epi, ActType xt) {
@@ -370,13 +371,20 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
         if (e == hipSuccess) e = t_contract(ca, EPI_GATES_STEP, 3, true, st, path);
     }
     if (e != hipSuccess) return e;
-    e = t_gnorm_quant(h, L.g, at, b, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, nullptr, st, path);
-    if (e != hipSuccess) return e;
     ContractArgs co{};
-    for (int q = 0; q < 3; ++q) { co.A[q] = L.codes_b; co.s[q] = L.s_b; co.sumq[q] = L.sq_b; co.B[q] = w->o.packed; co.mu[q] = w->o.mu; }
+    for (int q = 0; q < 3; ++q) { co.B[q] = w->o.packed; co.mu[q] = w->o.mu; }
     co.m = b; co.nc = d; co.k = d;
     co.out0 = L.x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
-    if ((e = t_contract(co, EPI_RESID, 1, true, st, path)) != hipSuccess) return e;
+    if (!w->o.norm_w && contract_row_gnorm_supported(b, d)) {
+        e = timed(row_name("resid,gnorm", at), b, d, d, st,
+                  [&] { return launch_contract_row_gnorm(co, h, L.g, at, w->g_norm_w, eps, st, path); });
+    } else {
+        e = t_gnorm_quant(h, L.g, at, b, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, nullptr, st,
+                          path);
+        for (int q = 0; q < 3; ++q) { co.A[q] = L.codes_b; co.s[q] = L.s_b; co.sumq[q] = L.sq_b; }
+        if (e == hipSuccess) e = t_contract(co, EPI_RESID, 1, true, st, path);
+    }
+    if (e != hipSuccess) return e;
     ContractArgs cg{};
     for (int q = 0; q < 3; ++q) cg.mu[q] = w->gate.mu;
     cg.B[0] = w->gate.packed;

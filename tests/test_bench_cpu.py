@@ -37,6 +37,9 @@ def test_self_quantising_contractions_read_rows_not_codes():
     _, gates = bench.algorithmic("tgemv_row<gates_step,bf16>", 16, 3 * 2048, 2048)
     assert gates == 3 * 2048 * 2048 / 4 + 16 * 2048 * 2 + 16 * 2048 * 10
     assert bench.kernel_files("tgemv_row<resid,bf16> m=1 n=2 k=3") == bench.kernel_files("tgemv<resid>")
+    # o_proj over the gated g_norm of one row: h, g and the gain read, residual and sum per output
+    _, o = bench.algorithmic("tgemv_row<resid,gnorm,bf16>", 1, 2048, 2048)
+    assert o == 2048 * 2048 / 4 + 2048 * (4 + 2) + 4 * 2048 + 2048 * (4 + 2)
 
 
 def test_split_activation_codes_counted_per_group():

@@ -934,26 +934,30 @@ def test_generate_step_graph_replays(gpu):
 
 
 ROW_CASES = [
-    # b, d, inner, act: no gains -> contractions quantise their own input rows where cheap
-    (1, 256, 512, "bf16"),
-    (1, 272, 1040, "f32"),     # slices past the row end
-    (1, 2048, 5632, "bf16"),   # the 1.3B decode shape
-    (1, 2560, 6912, "f32"),    # the 2.7B width, two slices per wave in down_proj
-    (2, 2048, 5632, "bf16"),   # a wave per row
-    (5, 272, 1040, "f32"),
-    (16, 2048, 5632, "bf16"),  # the 1.3B decode batch: i/f/g and gate_proj fused, down_proj not
-    (8, 2560, 6912, "bf16"),   # rows wider than 2048: the separate quantisers
+    # b, d, inner, act, gains: without gains on i/f/g, gate_proj and down_proj the contractions
+    # quantise their own input rows where cheap; o_proj forms the gated g_norm itself unless it
+    # has a gain
+    (1, 256, 512, "bf16", None),
+    (1, 272, 1040, "f32", ("g_norm",)),  # slices past the row end; g_norm's gain
+    (1, 2048, 5632, "bf16", None),       # the 1.3B decode shape
+    (1, 2560, 6912, "f32", None),        # the 2.7B width, two slices per wave in down_proj
+    (2, 2048, 5632, "bf16", ("g_norm",)),  # a wave per row
+    (5, 272, 1040, "f32", ("o",)),       # o_proj's gain: the g_norm quantiser runs
+    (16, 2048, 5632, "bf16", None),      # the 1.3B decode batch: down_proj's rows too wide
+    (16, 1024, 2816, "f32", ("g_norm", "o")),
+    (8, 2560, 6912, "bf16", None),       # rows wider than 2048: the separate quantisers
 ]
 
 
-@pytest.mark.parametrize("b,d,inner,act", ROW_CASES)
-def test_decode_row_path_matches_separate(gpu, b, d, inner, act):
+@pytest.mark.parametrize("b,d,inner,act,gains", ROW_CASES)
+def test_decode_row_path_matches_separate(gpu, b, d, inner, act, gains):
     """The default decode step lets i/f/g, gate_proj and down_proj quantise their own input rows
-    where that is cheaper than a quantiser launch (one row; up to 16 rows of at most 2048); over
-    a chain of steps it must give the separate kernels' outputs and states bit for bit."""
+    where that is cheaper than a quantiser launch (one row; up to 16 rows of at most 2048), and
+    o_proj form and quantise the gated g_norm of one row; over a chain of steps it must give the
+    separate kernels' outputs and states bit for bit."""
     import torch
     mmf = _mmf()
-    _, P = make_pair(d, inner, 970 + d, gpu)
+    _, P = make_pair(d, inner, 970 + d, gpu, gains)
     xs = [synth.activations((b, d), 971 + s_, act) for s_ in range(4)]
     h0 = synth.activations((b, d), 975)
     res = {}
@@ -969,9 +973,12 @@ def test_decode_row_path_matches_separate(gpu, b, d, inner, act):
                     steps = mmf.last_path().split(";")
                     fused = [k for k in steps if k.startswith("tgemv_row<")]
                     widest = 8192 if b == 1 else 2048  # widest input row a contraction quantises itself
-                    want = [e for e, k in (("gates_step", d), ("glu", d), ("resid", inner)) if k <= widest]
+                    o_gain = gains is not None and "o" in gains
+                    want = [e for e, k in (("gates_step", d), ("resid,gnorm", d if b == 1 and not o_gain else 1 << 30), ("glu", d),
+                                           ("resid", inner)) if k <= widest]
                     assert fused == ["tgemv_row<%s>" % e for e in want], steps
-                    assert sum(k.startswith("norm_quant") for k in steps) == 3 - len(want), steps
+                    quant = [k for k in steps if "norm_quant" in k]
+                    assert len(quant) == 4 - len(want), steps
             torch.cuda.synchronize()
             res[mode] = (outs, host(h))
         finally:
