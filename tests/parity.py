@@ -63,6 +63,24 @@ def packed_words(pl) -> np.ndarray:
     return host(pl.packed).view(np.uint32)
 
 
+def decode_reference(L: "oracle.Layer", x: np.ndarray, h0: np.ndarray, act: str) -> dict:
+    """The oracle's decode step composed from its own stage functions, with g and z rounded to
+    the activation type where the GPU stores them (bf16 activations keep g and z in bf16, the
+    state and x1 in fp32): the free-running reference for a bf16 decode step."""
+    def rd(v):  # the value as stored
+        return np.asarray(synth.bf16_round(v.astype(np.float32)), np.float64) if act == "bf16" else v
+    eps = L.eps
+    x = np.asarray(x, np.float64)
+    ri, rf, rg = L.i(x, eps), L.f(x, eps), L.g(x, eps)
+    f, xt = oracle.mixer_gates(ri["y"], rf["y"])
+    h = oracle.hgrn_scan(xt[:, None, :], f[:, None, :], h0)[:, 0, :]
+    g = rd(rg["y"])
+    x1 = x + L.o(oracle.gnorm_swish(h, g, L.g_norm_w, eps), eps)["y"]
+    ya = L.gate(x1, eps)["y"]
+    z = rd(oracle.silu(ya[:, :L.inner]) * ya[:, L.inner:])
+    return dict(h=h, out=x1 + L.down(z, eps)["y"])
+
+
 def make_pair(d, inner, seed, device, gains=None, eps=1e-8):
     """The same latent weights packed by the oracle (host) and by the GPU (mmf_ternary_pack)."""
     import ternary_weight_matmul_amd as mmf

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 from ternary_weight_matmul_amd import synth
-from parity import (assert_close, assert_equal, bf16_tensor, check_layer_sampled, check_layer_stages, dev, host,
+from parity import (assert_close, assert_equal, bf16_tensor, check_layer_sampled, check_layer_stages, decode_reference,
+                    dev, host,
                     make_pair, packed_words)
 
 pytestmark = pytest.mark.gpu
@@ -986,6 +987,38 @@ def test_decode_row_path_matches_separate(gpu, b, d, inner, act, gains):
     for a_, b_ in zip(res["auto"][0], res["separate"][0]):
         assert_equal(a_, b_, "out")
     assert_equal(res["auto"][1], res["separate"][1], "h")
+
+
+@pytest.mark.parametrize("b,act,gains", [(1, "f32", None), (1, "bf16", ("g_norm",)), (16, "f32", None),
+                                          (16, "bf16", None)])
+def test_decode_default_path_end_to_end(gpu, b, act, gains):
+    """The default decode step at the 1.3B shape (the contractions that quantise their own rows)
+    against the free-running oracle, with g and z rounded to the activation type where the GPU
+    stores them: the state within fp32 rounding (it depends only on the first quantiser, whose
+    input is the same on both sides); the output within the activation type's tolerance and, as
+    a code flip in a later quantiser moves a row by a few quantisation steps at most, normwise
+    within 1e-3."""
+    import torch
+    mmf = _mmf()
+    d, inner = 2048, 5632
+    L, P = make_pair(d, inner, 1900 + b, gpu, gains)
+    x = synth.activations((b, d), 1901, act)
+    h0 = synth.activations((b, d), 1902)
+    h = dev(h0, gpu)
+    out = mmf.layer_decode_step(P, bf16_tensor(x, gpu) if act == "bf16" else dev(x, gpu), h)
+    torch.cuda.synchronize()
+    assert "tgemv_row<" in mmf.last_path(), mmf.last_path()
+    ref = decode_reference(L, x, h0, act)
+    if act == "f32":  # nothing is stored below fp32: the plain oracle step is the same reference
+        plain = oracle.layer_decode_step(L, x, h0)
+        assert np.array_equal(plain["out"], ref["out"]) and np.array_equal(plain["h"], ref["h"])
+    assert_close(host(h), ref["h"], 1e-4, "h")
+    outg = host(out).astype(np.float64)
+    if act == "bf16":
+        assert_close(outg, ref["out"], 2e-2, "out")
+    # fp32: a few code flips at most; bf16: also the output's own rounding (about 1.1e-3 normwise)
+    rel = np.linalg.norm(outg - ref["out"]) / np.linalg.norm(ref["out"])
+    assert rel < (1e-3 if act == "f32" else 4e-3), rel
 
 
 def test_decode_row_path_needs_few_rows_and_no_gains(gpu):
