@@ -243,8 +243,14 @@ __device__ __forceinline__ void wave_epilogue(const ContractArgs &p, const i32x1
     wave_epilogue_t<EPI, NG, JN, float>(p, acc, mw, cw, lane);
 }
 
+// Two workgroups per CU, except with one activation tile per group and three
+// groups (i/f/g with distinct gains), whose registers allow one.
+template <int NG, bool SHARED_A>
+constexpr int tgemm_min_blocks() { return !SHARED_A && NG == 3 ? 1 : 2; }
+
 template <int NG, int JN, bool SHARED_A, int EPI>
-__global__ __launch_bounds__(256, 2) void tgemm_kernel(const ContractArgs p, const int tiles_n) {
+__global__ __launch_bounds__(256, (tgemm_min_blocks<NG, SHARED_A>())) void tgemm_kernel(const ContractArgs p,
+                                                                                        const int tiles_n) {
     using S = TileShape<NG, JN, SHARED_A>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * S::STAGE];
 
