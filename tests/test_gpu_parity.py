@@ -947,6 +947,9 @@ ROW_CASES = [
     (16, 2048, 5632, "bf16", None),      # the 1.3B decode batch: down_proj's rows too wide
     (16, 1024, 2816, "f32", ("g_norm", "o")),
     (8, 2560, 6912, "bf16", None),       # rows wider than 2048: the separate quantisers
+    (1, 16, 32, "bf16", ("g_norm",)),    # one packed word per row
+    (3, 16, 48, "f32", None),
+    (16, 48, 16, "bf16", None),          # 16 rows of three words; down_proj over one word
 ]
 
 
