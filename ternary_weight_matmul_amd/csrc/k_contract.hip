@@ -802,8 +802,8 @@ __global__ __launch_bounds__((gemv_bound<NG, SHARED_A, EPT>())) void tgemv_kerne
 // Decode at one row: the contraction quantises its own input row
 // ----------------------------------------------------------------------------
 // A 4-element chunk at element c4 of the input row that starts at element
-// row_off: x, or h with g and the
-// g_norm gain (1 where there is none: multiplying by 1 is exact).
+// row_off: x, or h with g and the g_norm gain (1 where there is none:
+// multiplying by 1 is exact).
 template <bool GN, typename XT>
 __device__ __forceinline__ void load_row_chunk(const RowSrc &src, int64_t row_off, int64_t c4, float (&x)[4],
                                                float (&g)[4], float (&w)[4]) {
