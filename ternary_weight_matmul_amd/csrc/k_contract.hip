@@ -31,6 +31,7 @@
 #include "launch.hpp"
 #include "epilogue.hpp"
 
+#include <atomic>
 #include <mutex>
 
 namespace mmf {
@@ -1268,21 +1269,36 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
     }
 }
 
-// The multi-row kernels take more dynamic LDS than the default 64 KB: each
-// kernel's limit is raised once, before its first launch.
+// The multi-row kernels take more dynamic LDS than the default 64 KB. The
+// limit belongs to the kernel on each device: it is raised on a device before
+// the kernel's first launch there, and a failure is returned, not launched.
 template <auto KERNEL>
-static void launch_rows(const ContractArgs &a, const RowSrc &src, float eps, int nslices, dim3 grid, int waves,
-                        size_t lds, hipStream_t st) {
-    static std::once_flag once;
-    std::call_once(once, [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(KERNEL), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  160 * 1024);
-    });
+static hipError_t raise_lds_limit() {
+    constexpr int kDevices = 64;  // devices past this raise it on every launch
+    static std::atomic<bool> done[kDevices];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < kDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+    std::lock_guard<std::mutex> lock(mu);
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(KERNEL), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024);
+    if (e == hipSuccess && dev < kDevices) done[dev].store(true, std::memory_order_release);
+    return e;
+}
+
+template <auto KERNEL>
+static hipError_t launch_rows(const ContractArgs &a, const RowSrc &src, float eps, int nslices, dim3 grid, int waves,
+                              size_t lds, hipStream_t st) {
+    const hipError_t e = raise_lds_limit<KERNEL>();
+    if (e != hipSuccess) return e;
     KERNEL<<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
+    return hipSuccess;
 }
 
 template <int NG, int EPI, typename XT, typename RT, int CB, bool GN>
-static void run_row_cb(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
+static hipError_t run_row_cb(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 15) / 16;
     const dim3 grid((unsigned)((a.nc + 16 * CB - 1) / (16 * CB)));
@@ -1293,7 +1309,7 @@ static void run_row_cb(const ContractArgs &a, const RowSrc &src, float eps, hipS
             tgemv_row_kernel<NG, EPI, XT, RT, CB, 1, GN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
         else
             tgemv_row_kernel<NG, EPI, XT, RT, CB, 2, GN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
-        return;
+        return hipSuccess;
     }
     // 2 to 16 rows of at most 2048: a wave per row (8 chunks of 4 per lane);
     // the gated g_norm runs at one row only
@@ -1304,22 +1320,23 @@ static void run_row_cb(const ContractArgs &a, const RowSrc &src, float eps, hipS
         const size_t lds =
             (size_t)waves * CB * NG * 256 * sizeof(int32_t) + (size_t)16 * (a.k + 16) + 16 * sizeof(float);
         if (nslices > waves)
-            launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 2, 8, 1>>(a, src, eps, nslices, grid, waves, lds, st);
-        else
-            launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 1, 8, 1>>(a, src, eps, nslices, grid, waves, lds, st);
+            return launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 2, 8, 1>>(a, src, eps, nslices, grid, waves, lds,
+                                                                                st);
+        return launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 1, 8, 1>>(a, src, eps, nslices, grid, waves, lds, st);
     }
+    return hipErrorInvalidValue;  // the gated g_norm takes one row only
 }
 
 template <int NG, int EPI, typename XT, typename RT, bool GN = false>
-static void run_row(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
+static hipError_t run_row(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
     switch (gemv_channel_blocks(a.nc, NG, a.k, 1)) {
         case 4:
-            if constexpr (NG == 1) { run_row_cb<NG, EPI, XT, RT, 4, GN>(a, src, eps, st); break; }
+            if constexpr (NG == 1) return run_row_cb<NG, EPI, XT, RT, 4, GN>(a, src, eps, st);
             [[fallthrough]];
         case 2:
-            if constexpr (NG <= 2) { run_row_cb<NG, EPI, XT, RT, 2, GN>(a, src, eps, st); break; }
+            if constexpr (NG <= 2) return run_row_cb<NG, EPI, XT, RT, 2, GN>(a, src, eps, st);
             [[fallthrough]];
-        default: run_row_cb<NG, EPI, XT, RT, 1, GN>(a, src, eps, st); break;
+        default: return run_row_cb<NG, EPI, XT, RT, 1, GN>(a, src, eps, st);
     }
 }
 
@@ -1342,27 +1359,29 @@ hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x
                                hipStream_t st, std::string *path) {
     const bool xb = xt == ACT_BF16, rb = a.res_type == ACT_BF16;
     const RowSrc x{xp, nullptr, nullptr};
+    hipError_t e = hipSuccess;
     switch (epi) {
         case EPI_GATES_STEP:
-            if (xb) run_row<3, EPI_GATES_STEP, uint16_t, float>(a, x, eps, st);
-            else run_row<3, EPI_GATES_STEP, float, float>(a, x, eps, st);
+            if (xb) e = run_row<3, EPI_GATES_STEP, uint16_t, float>(a, x, eps, st);
+            else e = run_row<3, EPI_GATES_STEP, float, float>(a, x, eps, st);
             break;
         case EPI_GLU:
-            if (xb) run_row<2, EPI_GLU, uint16_t, float>(a, x, eps, st);
-            else run_row<2, EPI_GLU, float, float>(a, x, eps, st);
+            if (xb) e = run_row<2, EPI_GLU, uint16_t, float>(a, x, eps, st);
+            else e = run_row<2, EPI_GLU, float, float>(a, x, eps, st);
             break;
         case EPI_RESID:
-            if (xb && rb) run_row<1, EPI_RESID, uint16_t, uint16_t>(a, x, eps, st);
-            else if (xb) run_row<1, EPI_RESID, uint16_t, float>(a, x, eps, st);
-            else if (rb) run_row<1, EPI_RESID, float, uint16_t>(a, x, eps, st);
-            else run_row<1, EPI_RESID, float, float>(a, x, eps, st);
+            if (xb && rb) e = run_row<1, EPI_RESID, uint16_t, uint16_t>(a, x, eps, st);
+            else if (xb) e = run_row<1, EPI_RESID, uint16_t, float>(a, x, eps, st);
+            else if (rb) e = run_row<1, EPI_RESID, float, uint16_t>(a, x, eps, st);
+            else e = run_row<1, EPI_RESID, float, float>(a, x, eps, st);
             break;
         case EPI_LINEAR:
-            if (xb) run_row<1, EPI_LINEAR, uint16_t, float>(a, x, eps, st);
-            else run_row<1, EPI_LINEAR, float, float>(a, x, eps, st);
+            if (xb) e = run_row<1, EPI_LINEAR, uint16_t, float>(a, x, eps, st);
+            else e = run_row<1, EPI_LINEAR, float, float>(a, x, eps, st);
             break;
         default: return hipErrorInvalidValue;
     }
+    if (e != hipSuccess) return e;
     if (path) *path += std::string("tgemv_row<") + epi_name(epi) + ">;";
     return hipGetLastError();
 }
@@ -1372,10 +1391,12 @@ hipError_t launch_contract_row_gnorm(const ContractArgs &a, const float *h, cons
     if (!contract_row_gnorm_supported(a.m, a.k)) return hipErrorInvalidValue;
     const RowSrc src{h, g, gnw};
     const bool gb = gt == ACT_BF16, rb = a.res_type == ACT_BF16;
-    if (gb && rb) run_row<1, EPI_RESID, uint16_t, uint16_t, true>(a, src, eps, st);
-    else if (gb) run_row<1, EPI_RESID, uint16_t, float, true>(a, src, eps, st);
-    else if (rb) run_row<1, EPI_RESID, float, uint16_t, true>(a, src, eps, st);
-    else run_row<1, EPI_RESID, float, float, true>(a, src, eps, st);
+    hipError_t e;
+    if (gb && rb) e = run_row<1, EPI_RESID, uint16_t, uint16_t, true>(a, src, eps, st);
+    else if (gb) e = run_row<1, EPI_RESID, uint16_t, float, true>(a, src, eps, st);
+    else if (rb) e = run_row<1, EPI_RESID, float, uint16_t, true>(a, src, eps, st);
+    else e = run_row<1, EPI_RESID, float, float, true>(a, src, eps, st);
+    if (e != hipSuccess) return e;
     if (path) *path += "tgemv_row<resid,gnorm>;";
     return hipGetLastError();
 }
