@@ -802,13 +802,26 @@ __global__ __launch_bounds__((gemv_bound<NG, SHARED_A, EPT>())) void tgemv_kerne
 // ----------------------------------------------------------------------------
 // Decode at one row: the contraction quantises its own input row
 // ----------------------------------------------------------------------------
+// What a self-quantising contraction reads as its input rows.
+enum RowIn : int {
+    ROW_X = 0,           // x as it is (no gain)
+    ROW_GNORM = 1,       // the gated g_norm of (h, g) (one row)
+    ROW_GAIN = 2,        // x with its FusedBitLinear gain (one row)
+    ROW_GNORM_GAIN = 3,  // the gated g_norm, then o_proj's gain (one row)
+};
+
 // A 4-element chunk at element c4 of the input row that starts at element
-// row_off: x, or h with g and the g_norm gain (1 where there is none:
-// multiplying by 1 is exact).
-template <bool GN, typename XT>
+// row_off: x (and its FusedBitLinear gain into o); or h with g and the g_norm
+// gain (1 where there is none: multiplying by 1 is exact), and o_proj's gain
+// into o.
+template <int IN, typename XT>
 __device__ __forceinline__ void load_row_chunk(const RowSrc &src, int64_t row_off, int64_t c4, float (&x)[4],
-                                               float (&g)[4], float (&w)[4]) {
-    if constexpr (GN) {
+                                               float (&g)[4], float (&w)[4], float (&o)[4]) {
+    if constexpr (IN == ROW_GAIN || IN == ROW_GNORM_GAIN) {
+        const float4 v = *reinterpret_cast<const float4 *>(src.gain + c4);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    if constexpr (IN == ROW_GNORM || IN == ROW_GNORM_GAIN) {
         const float4 h = load_act4(static_cast<const float *>(src.x) + row_off, c4);
         const float4 gg = load_act4(static_cast<const XT *>(src.g) + row_off, c4);
         const float4 ww = src.gnw ? *reinterpret_cast<const float4 *>(src.gnw + c4) : make_float4(1.f, 1.f, 1.f, 1.f);
@@ -836,11 +849,14 @@ __device__ __forceinline__ void gated_norm4(float (&x)[4], const float (&g)[4], 
 // activation fragments from there (all 16 fragment rows read the one row).
 // The MFMAs, the all-ones sum of codes and the epilogue are those of the GEMV;
 // only row 0 is stored. Same codes and scale as the separate quantiser (its
-// operations, binary64 sum in another order). With GN the row is the gated
-// g_norm of (h, g): a first round forms sum h^2 and r_h, then
+// operations, binary64 sum in another order). IN = ROW_GNORM: the row is the
+// gated g_norm of (h, g): a first round forms sum h^2 and r_h, then
 // y = ((h r_h) w) silu(g) is quantised as x is, in the g_norm quantiser's
-// order of roundings.
-template <int NG, int EPI, typename XT, typename RT, int CB, int SPW, bool GN>
+// order of roundings. IN = ROW_GAIN: a first round forms sum x^2 and r, then
+// y = (x r) w, and the last round takes max |y| alone (the gain breaks
+// max |y| = (max |x|) r), as the quantiser does with a gain.
+// IN = ROW_GNORM_GAIN: both, in that order (three rounds).
+template <int NG, int EPI, typename XT, typename RT, int CB, int SPW, int IN>
 __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, const RowSrc src, float eps,
                                                          const int nslices) {
     constexpr int WPL = 4, MAXCH = 4;
@@ -856,10 +872,12 @@ __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, c
     uint32_t *codes = reinterpret_cast<uint32_t *>(part + nw * PART);
     // 1. the row (straight-line, clamped chunk indices)
     float xv[MAXCH][4];
-    [[maybe_unused]] float gv[GN ? MAXCH : 1][4], wv[GN ? MAXCH : 1][4];
+    constexpr bool GN = IN == ROW_GNORM || IN == ROW_GNORM_GAIN, GAIN = IN == ROW_GAIN || IN == ROW_GNORM_GAIN;
+    [[maybe_unused]] float gv[GN ? MAXCH : 1][4], wv[GN ? MAXCH : 1][4], ov[GAIN ? MAXCH : 1][4];
 #pragma unroll
     for (int j = 0; j < MAXCH; ++j)
-        load_row_chunk<GN, XT>(src, 0, 4 * (int64_t)min(tid + j * T, nch - 1), xv[j], gv[GN ? j : 0], wv[GN ? j : 0]);
+        load_row_chunk<IN, XT>(src, 0, 4 * (int64_t)min(tid + j * T, nch - 1), xv[j], gv[GN ? j : 0],
+                               wv[GN ? j : 0], ov[GAIN ? j : 0]);
     // 2. the weights of the wave's slices (a wave without a second slice loads the last again)
     int gn[CB];
 #pragma unroll
@@ -898,7 +916,10 @@ __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, c
         const RT *pre_src = static_cast<const RT *>(EPI == EPI_RESID ? p.res : p.out0);
         pre = load_act(pre_src, (int64_t)(ec < p.nc ? ec : p.nc - 1));
     }
-    if constexpr (GN) {  // the gated g_norm: sum h^2, then y in place of x
+    // rounds before the last: sum h^2 for the gated g_norm (red_h), sum x^2
+    // before a gain (red_d); each round has its own slots, so no wave can
+    // overwrite a slot another wave is still reading
+    auto block_rms = [&](double *slots) {
         double sh = 0.0;
 #pragma unroll
         for (int j = 0; j < MAXCH; ++j)
@@ -906,15 +927,25 @@ __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, c
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sh += (double)xv[j][e] * (double)xv[j][e];
         sh = wave_sum(sh);
-        if (lane == 0) red_h[wave] = sh;
+        if (lane == 0) slots[wave] = sh;
         __syncthreads();
         sh = 0.0;
-        for (int w = 0; w < nw; ++w) sh += red_h[w];
-        const float rh = rms_factor(sh, K, eps);
+        for (int w = 0; w < nw; ++w) sh += slots[w];
+        return rms_factor(sh, K, eps);
+    };
+    if constexpr (GN) {
+        const float rh = block_rms(red_h);
 #pragma unroll
         for (int j = 0; j < MAXCH; ++j) gated_norm4(xv[j], gv[j], wv[j], rh);
     }
-    // 3. sum x^2 and max |x| in one round
+    if constexpr (GAIN) {
+        const float r1 = block_rms(red_d);
+#pragma unroll
+        for (int j = 0; j < MAXCH; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[j][e] = __fmul_rn(__fmul_rn(xv[j][e], r1), ov[j][e]);
+    }
+    // 3. sum x^2 and max |x| in one round (max |y| alone with a gain)
     double ss = 0.0;
     float mx = 0.0f;
 #pragma unroll
@@ -922,31 +953,31 @@ __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, c
         if (tid + j * T < nch)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ss += (double)xv[j][e] * (double)xv[j][e];
+                if constexpr (!GAIN) ss += (double)xv[j][e] * (double)xv[j][e];
                 mx = fmaxf(mx, fabsf(xv[j][e]));
             }
-    ss = wave_sum(ss);
+    if constexpr (!GAIN) ss = wave_sum(ss);
     mx = wave_max(mx);
     if (lane == 0) {
-        red_d[wave] = ss;
+        if constexpr (!GAIN) red_d[wave] = ss;
         red_f[wave] = mx;
     }
     __syncthreads();
     ss = 0.0;
     mx = 0.0f;
     for (int w = 0; w < nw; ++w) {
-        ss += red_d[w];
+        if constexpr (!GAIN) ss += red_d[w];
         mx = fmaxf(mx, red_f[w]);
     }
-    const float r = rms_factor(ss, K, eps);
-    const float sc = quant_scale(__fmul_rn(mx, r));
+    // with a gain the row is already y = (x r) w: its codes take no further factor
+    const float r = GAIN ? 1.0f : rms_factor(ss, K, eps);
+    const float sc = quant_scale(GAIN ? mx : __fmul_rn(mx, r));
+    auto qv = [&](float v) { return quant_code(GAIN ? v : __fmul_rn(v, r), sc); };
     // 4. the codes to LDS
 #pragma unroll
     for (int j = 0; j < MAXCH; ++j) {
         const int c = tid + j * T;
-        if (c < nch)
-            codes[c] = pack_codes4(quant_code(__fmul_rn(xv[j][0], r), sc), quant_code(__fmul_rn(xv[j][1], r), sc),
-                                   quant_code(__fmul_rn(xv[j][2], r), sc), quant_code(__fmul_rn(xv[j][3], r), sc));
+        if (c < nch) codes[c] = pack_codes4(qv(xv[j][0]), qv(xv[j][1]), qv(xv[j][2]), qv(xv[j][3]));
     }
     __syncthreads();
     // 5. the contraction
@@ -1113,6 +1144,8 @@ static void run_gemv(const ContractArgs &a, hipStream_t st) {
 // at most): the row's sums are wave reductions, its codes go to LDS at a
 // padded row stride (K + 16 bytes: the 16 fragment rows fall in different
 // banks) with its scale, and the epilogue is the GEMV's over the 16-row block.
+// Rows without a gain only (with one, a second reduction per row and the
+// gain's registers were measured to spill).
 template <int NG, int EPI, typename XT, typename RT, int CB, int SPW, int CPL, int RPW>
 __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, const RowSrc src, float eps,
                                                           const int nslices) {
@@ -1133,8 +1166,8 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
         const int rr = min(wave + i * nw, M - 1);
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
-            load_row_chunk<false, XT>(src, (int64_t)rr * K, 4 * (int64_t)min(lane + 64 * j, nch - 1), xv[i][j],
-                                      unused, unused);
+            load_row_chunk<ROW_X, XT>(src, (int64_t)rr * K, 4 * (int64_t)min(lane + 64 * j, nch - 1), xv[i][j],
+                                      unused, unused, unused);
     }
     // 2. the weights of the wave's slices
     int gn[CB];
@@ -1197,13 +1230,13 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
             mx = wave_max(mx);
             const float rr = rms_factor(ss, K, eps);
             const float sc = quant_scale(__fmul_rn(mx, rr));
+            auto qv = [&](float v) { return quant_code(__fmul_rn(v, rr), sc); };
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = lane + 64 * j;
                 if (c < nch)
                     *reinterpret_cast<uint32_t *>(codes + r * stride + 4 * c) =
-                        pack_codes4(quant_code(__fmul_rn(xv[i][j][0], rr), sc), quant_code(__fmul_rn(xv[i][j][1], rr), sc),
-                                    quant_code(__fmul_rn(xv[i][j][2], rr), sc), quant_code(__fmul_rn(xv[i][j][3], rr), sc));
+                        pack_codes4(qv(xv[i][j][0]), qv(xv[i][j][1]), qv(xv[i][j][2]), qv(xv[i][j][3]));
             }
             if (lane == 0) srow[r] = sc;
         }
@@ -1297,7 +1330,7 @@ static hipError_t launch_rows(const ContractArgs &a, const RowSrc &src, float ep
     return hipSuccess;
 }
 
-template <int NG, int EPI, typename XT, typename RT, int CB, bool GN>
+template <int NG, int EPI, typename XT, typename RT, int CB, int IN>
 static hipError_t run_row_cb(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 15) / 16;
@@ -1306,14 +1339,14 @@ static hipError_t run_row_cb(const ContractArgs &a, const RowSrc &src, float eps
         const int waves = nslices < 16 ? nslices : 16;
         const size_t lds = (size_t)waves * CB * NG * 16 * sizeof(int32_t) + (size_t)a.k;
         if (nslices <= waves)
-            tgemv_row_kernel<NG, EPI, XT, RT, CB, 1, GN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
+            tgemv_row_kernel<NG, EPI, XT, RT, CB, 1, IN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
         else
-            tgemv_row_kernel<NG, EPI, XT, RT, CB, 2, GN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
+            tgemv_row_kernel<NG, EPI, XT, RT, CB, 2, IN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
         return hipSuccess;
     }
-    // 2 to 16 rows of at most 2048: a wave per row (8 chunks of 4 per lane);
-    // the gated g_norm runs at one row only
-    if constexpr (!GN) {
+    // 2 to 16 rows of at most 2048, without a gain: a wave per row (8 chunks of
+    // 4 per lane); the gated g_norm and gains run at one row only
+    if constexpr (IN == ROW_X) {
         const int m = (int)a.m;
         int waves = nslices < 16 ? nslices : 16;
         if (waves < m) waves = m;
@@ -1324,41 +1357,54 @@ static hipError_t run_row_cb(const ContractArgs &a, const RowSrc &src, float eps
                                                                                 st);
         return launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 1, 8, 1>>(a, src, eps, nslices, grid, waves, lds, st);
     }
-    return hipErrorInvalidValue;  // the gated g_norm takes one row only
+    return hipErrorInvalidValue;  // the gated g_norm and gains take one row only
 }
 
-template <int NG, int EPI, typename XT, typename RT, bool GN = false>
-static hipError_t run_row(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
+template <int NG, int EPI, typename XT, typename RT, int IN>
+static hipError_t run_row_in(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
+    // four channel blocks take 10240 outputs or more; the gated g_norm's rows (at most 8192
+    // wide, o_proj square) never reach them, and its registers would not fit them
+    constexpr bool CB4 = NG == 1 && IN != ROW_GNORM && IN != ROW_GNORM_GAIN;
     switch (gemv_channel_blocks(a.nc, NG, a.k, 1)) {
         case 4:
-            if constexpr (NG == 1) return run_row_cb<NG, EPI, XT, RT, 4, GN>(a, src, eps, st);
+            if constexpr (CB4) return run_row_cb<NG, EPI, XT, RT, 4, IN>(a, src, eps, st);
             [[fallthrough]];
         case 2:
-            if constexpr (NG <= 2) return run_row_cb<NG, EPI, XT, RT, 2, GN>(a, src, eps, st);
+            if constexpr (NG <= 2) return run_row_cb<NG, EPI, XT, RT, 2, IN>(a, src, eps, st);
             [[fallthrough]];
-        default: return run_row_cb<NG, EPI, XT, RT, 1, GN>(a, src, eps, st);
+        default: return run_row_cb<NG, EPI, XT, RT, 1, IN>(a, src, eps, st);
     }
 }
 
-// One row up to k = 8192; 2 to 16 rows up to k = 2048, one wave per row (a
-// wider row leaves the multi-row kernel too few registers, and its codes in
-// LDS would limit the workgroups per CU).
-bool contract_row_supported(int64_t m, int k, EpiKind epi) {
+// x with or without its gain
+template <int NG, int EPI, typename XT, typename RT>
+static hipError_t run_row(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
+    return src.gain ? run_row_in<NG, EPI, XT, RT, ROW_GAIN>(a, src, eps, st)
+                    : run_row_in<NG, EPI, XT, RT, ROW_X>(a, src, eps, st);
+}
+
+// One row up to k = 8192, with or without a gain; 2 to 16 rows up to k =
+// 2048 without a gain, one wave per row (a wider row leaves the multi-row
+// kernel too few registers, and its codes in LDS would limit the workgroups
+// per CU).
+bool contract_row_supported(int64_t m, int k, EpiKind epi, bool gain) {
     const bool kind = epi == EPI_GATES_STEP || epi == EPI_GLU || epi == EPI_RESID || epi == EPI_LINEAR;
     if (!kind || k % 16 || m < 1) return false;
     if (m == 1) return k <= 8192;
-    return m <= 16 && k <= 2048;
+    return m <= 16 && k <= 2048 && !gain;
 }
 
-// The gated g_norm in o_proj: one row up to k = 8192 (at several rows, each
+// The gated g_norm in o_proj (with or without o_proj's own gain): one row up
+// to k = 8192 (at several rows, each
 // workgroup reading h and g of every row and a second reduction per row cost
 // more than the g_norm quantiser's launch: measured slower at 8 and 16 rows).
 bool contract_row_gnorm_supported(int64_t m, int k) { return m == 1 && k % 16 == 0 && k <= 8192; }
 
-hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *xp, ActType xt, float eps,
-                               hipStream_t st, std::string *path) {
+hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *xp, ActType xt, const float *gain,
+                               float eps, hipStream_t st, std::string *path) {
+    if (!contract_row_supported(a.m, a.k, epi, gain != nullptr)) return hipErrorInvalidValue;
     const bool xb = xt == ACT_BF16, rb = a.res_type == ACT_BF16;
-    const RowSrc x{xp, nullptr, nullptr};
+    const RowSrc x{xp, nullptr, nullptr, gain};
     hipError_t e = hipSuccess;
     switch (epi) {
         case EPI_GATES_STEP:
@@ -1386,16 +1432,23 @@ hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x
     return hipGetLastError();
 }
 
+template <int IN>
+static hipError_t run_row_gnorm(const ContractArgs &a, const RowSrc &src, bool gb, float eps, hipStream_t st) {
+    const bool rb = a.res_type == ACT_BF16;
+    if (gb && rb) return run_row_in<1, EPI_RESID, uint16_t, uint16_t, IN>(a, src, eps, st);
+    if (gb) return run_row_in<1, EPI_RESID, uint16_t, float, IN>(a, src, eps, st);
+    if (rb) return run_row_in<1, EPI_RESID, float, uint16_t, IN>(a, src, eps, st);
+    return run_row_in<1, EPI_RESID, float, float, IN>(a, src, eps, st);
+}
+
 hipError_t launch_contract_row_gnorm(const ContractArgs &a, const float *h, const void *g, ActType gt,
-                                     const float *gnw, float eps, hipStream_t st, std::string *path) {
+                                     const float *gnw, const float *ogain, float eps, hipStream_t st,
+                                     std::string *path) {
     if (!contract_row_gnorm_supported(a.m, a.k)) return hipErrorInvalidValue;
-    const RowSrc src{h, g, gnw};
-    const bool gb = gt == ACT_BF16, rb = a.res_type == ACT_BF16;
-    hipError_t e;
-    if (gb && rb) e = run_row<1, EPI_RESID, uint16_t, uint16_t, true>(a, src, eps, st);
-    else if (gb) e = run_row<1, EPI_RESID, uint16_t, float, true>(a, src, eps, st);
-    else if (rb) e = run_row<1, EPI_RESID, float, uint16_t, true>(a, src, eps, st);
-    else e = run_row<1, EPI_RESID, float, float, true>(a, src, eps, st);
+    const RowSrc src{h, g, gnw, ogain};
+    const bool gb = gt == ACT_BF16;
+    const hipError_t e = ogain ? run_row_gnorm<ROW_GNORM_GAIN>(a, src, gb, eps, st)
+                               : run_row_gnorm<ROW_GNORM>(a, src, gb, eps, st);
     if (e != hipSuccess) return e;
     if (path) *path += "tgemv_row<resid,gnorm>;";
     return hipGetLastError();

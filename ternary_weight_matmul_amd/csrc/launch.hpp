@@ -58,6 +58,7 @@ struct RowSrc {
     const void *x;       // x, or h
     const void *g;       // g (gated g_norm only)
     const float *gnw;    // g_norm's gain or NULL (gated g_norm only)
+    const float *gain;   // the FusedBitLinear gain of x, or o_proj's after the gated g_norm; or NULL
 };
 
 // One decode step of a block as a single kernel on one XCD (k_decode.hip).
@@ -106,13 +107,14 @@ hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shar
 
 // Decode at one row without a gain: the contraction quantises its input row x
 // (type xt) itself in every workgroup (k <= 8192); a.A, a.s, a.sumq unused.
-bool contract_row_supported(int64_t m, int k, EpiKind epi);
-hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x, ActType xt, float eps,
-                               hipStream_t st, std::string *path);
+bool contract_row_supported(int64_t m, int k, EpiKind epi, bool gain);
+hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x, ActType xt, const float *gain,
+                               float eps, hipStream_t st, std::string *path);
 // o_proj over the gated g_norm of (h, g), quantised in each workgroup (EPI_RESID only).
 bool contract_row_gnorm_supported(int64_t m, int k);
 hipError_t launch_contract_row_gnorm(const ContractArgs &a, const float *h, const void *g, ActType gt,
-                                     const float *gnw, float eps, hipStream_t st, std::string *path);
+                                     const float *gnw, const float *ogain, float eps, hipStream_t st,
+                                     std::string *path);
 
 // Whether the contraction over m rows forms each row's sum of codes itself
 // (the decode GEMV does); otherwise it reads the quantiser's sumq.

@@ -337,13 +337,15 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
     });
 }
 
-// The decode step at up to 16 rows without gains: a contraction quantises its
-// own input rows (launch_contract_row) where that costs each workgroup less
-// than a quantiser launch (contract_row_supported); otherwise the separate
-// quantiser runs first. At one row o_proj also forms the gated g_norm of
-// (h, g) itself unless it has a gain: four kernels instead of eight; at 16
-// rows of 2048 with an inner width of 5632, six (g_norm keeps its quantiser,
-// and down_proj's rows are too wide).
+// The decode step at up to 16 rows (i/f/g sharing one gain or none): a
+// contraction quantises its own input rows (launch_contract_row) where that
+// costs each workgroup less than a quantiser launch (contract_row_supported:
+// one row with or without a gain, several rows without); otherwise the
+// separate quantiser runs first, with the stage's gain. At one row o_proj
+// also forms the gated g_norm of (h, g) itself (then applies its own gain, if
+// any): four kernels instead of eight; at 16 rows of 2048 with an inner width
+// of 5632, six (g_norm keeps its quantiser, and down_proj's rows are too
+// wide).
 
 // Timing name of a self-quantising contraction: its epilogue and the type of the rows it reads.
 std::string row_name(const char *epi, ActType xt) {
@@ -355,18 +357,19 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
     const ActType at = act(actt);
     const int d = w->d, inner = w->inner;
     const float eps = w->eps;
-    auto fused = [&](int k, EpiKind epi) { return contract_row_supported(b, k, epi); };
+    auto fused = [&](int k, EpiKind epi, const float *gain) { return contract_row_supported(b, k, epi, gain); };
+    const float *gx = w->i.norm_w;  // i/f/g share one gain (or none): one quantisation of x serves all three
     hipError_t e;
     ContractArgs ca{};
     const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
     for (int q = 0; q < 3; ++q) { ca.B[q] = tw[q]->packed; ca.mu[q] = tw[q]->mu; }
     ca.m = b; ca.nc = d; ca.k = d;
     ca.out0 = h; ca.out1 = L.g; ca.out_type = ACT_F32; ca.aux_type = at;
-    if (fused(d, EPI_GATES_STEP)) {
+    if (fused(d, EPI_GATES_STEP, gx)) {
         e = timed(row_name("gates_step", at), b, 3 * d, d, st,
-                  [&] { return launch_contract_row(ca, EPI_GATES_STEP, x, at, eps, st, path); });
+                  [&] { return launch_contract_row(ca, EPI_GATES_STEP, x, at, gx, eps, st, path); });
     } else {
-        e = t_norm_quant(x, at, b, d, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
+        e = t_norm_quant(x, at, b, d, gx, eps, L.codes_b, L.s_b, L.sq_b, st, path);
         for (int q = 0; q < 3; ++q) { ca.A[q] = L.codes_b; ca.s[q] = L.s_b; ca.sumq[q] = L.sq_b; }
         if (e == hipSuccess) e = t_contract(ca, EPI_GATES_STEP, 3, true, st, path);
     }
@@ -375,9 +378,9 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
     for (int q = 0; q < 3; ++q) { co.B[q] = w->o.packed; co.mu[q] = w->o.mu; }
     co.m = b; co.nc = d; co.k = d;
     co.out0 = L.x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
-    if (!w->o.norm_w && contract_row_gnorm_supported(b, d)) {
+    if (contract_row_gnorm_supported(b, d)) {
         e = timed(row_name("resid,gnorm", at), b, d, d, st,
-                  [&] { return launch_contract_row_gnorm(co, h, L.g, at, w->g_norm_w, eps, st, path); });
+                  [&] { return launch_contract_row_gnorm(co, h, L.g, at, w->g_norm_w, w->o.norm_w, eps, st, path); });
     } else {
         e = t_gnorm_quant(h, L.g, at, b, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, nullptr, st,
                           path);
@@ -392,11 +395,11 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
     cg.B[2] = cg.B[1];
     cg.m = b; cg.nc = inner; cg.k = d;
     cg.out0 = L.z; cg.aux_type = at;
-    if (fused(d, EPI_GLU)) {
+    if (fused(d, EPI_GLU, w->gate.norm_w)) {
         e = timed(row_name("glu", ACT_F32), b, 2 * inner, d, st,
-                  [&] { return launch_contract_row(cg, EPI_GLU, L.x1, ACT_F32, eps, st, path); });
+                  [&] { return launch_contract_row(cg, EPI_GLU, L.x1, ACT_F32, w->gate.norm_w, eps, st, path); });
     } else {
-        e = t_norm_quant(L.x1, ACT_F32, b, d, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
+        e = t_norm_quant(L.x1, ACT_F32, b, d, w->gate.norm_w, eps, L.codes_b, L.s_b, L.sq_b, st, path);
         for (int q = 0; q < 3; ++q) { cg.A[q] = L.codes_b; cg.s[q] = L.s_b; cg.sumq[q] = L.sq_b; }
         if (e == hipSuccess) e = t_contract(cg, EPI_GLU, 2, true, st, path);
     }
@@ -405,10 +408,10 @@ hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out,
     for (int q = 0; q < 3; ++q) { cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
     cd.m = b; cd.nc = d; cd.k = inner;
     cd.out0 = out; cd.out_type = at; cd.res = L.x1; cd.res_type = ACT_F32;
-    if (fused(inner, EPI_RESID))
+    if (fused(inner, EPI_RESID, w->down.norm_w))
         return timed(row_name("resid", at), b, d, inner, st,
-                     [&] { return launch_contract_row(cd, EPI_RESID, L.z, at, eps, st, path); });
-    e = t_norm_quant(L.z, at, b, inner, nullptr, eps, L.codes_b, L.s_b, L.sq_b, st, path);
+                     [&] { return launch_contract_row(cd, EPI_RESID, L.z, at, w->down.norm_w, eps, st, path); });
+    e = t_norm_quant(L.z, at, b, inner, w->down.norm_w, eps, L.codes_b, L.s_b, L.sq_b, st, path);
     for (int q = 0; q < 3; ++q) { cd.A[q] = L.codes_b; cd.s[q] = L.s_b; cd.sumq[q] = L.sq_b; }
     if (e == hipSuccess) e = t_contract(cd, EPI_RESID, 1, true, st, path);
     return e;
@@ -897,8 +900,7 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
         if (r == MMF_OK) g_path = path;
         return r;
     }
-    const bool row_ok = b >= 1 && b <= 16 && !probe && shared_ifg(w) && !w->i.norm_w && !w->gate.norm_w &&
-                        !w->down.norm_w;
+    const bool row_ok = b >= 1 && b <= 16 && !probe && shared_ifg(w);
     if (row_ok && mode == 0) {
         Carver c(ws);
         LayerWs L;
