@@ -305,11 +305,11 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
  *  Four implementations give the same bits: separate kernels per stage
  *  (quantisers and contractions: eight launches); contractions that quantise
  *  their own input rows in every workgroup, where a row fits (b <= 16, no
- *  probe, i/f/g sharing one gain or none; one row up to 8192 wide, with or
- *  without its gain, where o_proj also forms the gated g_norm of h and g;
- *  2 to 16 rows up to 2048 wide for stages without a gain; the other stages
- *  keep their quantisers: four launches at one row, six at the 1.3B shape
- *  and 16 rows without gains); four contraction kernels
+ *  probe, i/f/g sharing one gain or none; one row up to 8192 wide, where
+ *  o_proj also forms the gated g_norm of h and g; 2 to 16 rows up to 2048
+ *  wide, 12 for a stage with a gain; the other stages keep their
+ *  quantisers: four launches at one row, six at the 1.3B shape and 16 rows
+ *  without gains); four contraction kernels
  *  whose first b workgroups quantise the input rows and hand them to the
  *  others within the launch through device-scope stores and a counter (b <=
  *  16, no probe, equal i/f/g gains, d and inner multiples of 256, d <= 3072,

@@ -1144,9 +1144,8 @@ static void run_gemv(const ContractArgs &a, hipStream_t st) {
 // at most): the row's sums are wave reductions, its codes go to LDS at a
 // padded row stride (K + 16 bytes: the 16 fragment rows fall in different
 // banks) with its scale, and the epilogue is the GEMV's over the 16-row block.
-// Rows without a gain only (with one, a second reduction per row and the
-// gain's registers were measured to spill).
-template <int NG, int EPI, typename XT, typename RT, int CB, int SPW, int CPL, int RPW>
+// IN = ROW_GAIN: each row with its gain (sum x^2, then max |(x r) w| alone).
+template <int NG, int EPI, typename XT, typename RT, int CB, int SPW, int CPL, int RPW, int IN>
 __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, const RowSrc src, float eps,
                                                           const int nslices) {
     constexpr int WPL = 4;
@@ -1160,14 +1159,17 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
     int8_t *codes = reinterpret_cast<int8_t *>(part + nw * PART);
     float *srow = reinterpret_cast<float *>(codes + 16 * stride);
     // 1. this wave's rows (straight-line, clamped)
+    static_assert(IN == ROW_X || IN == ROW_GAIN, "several rows: x, with or without its gain");
+    constexpr bool GAIN = IN == ROW_GAIN;
     float xv[RPW][CPL][4], unused[4];
+    [[maybe_unused]] float ov[GAIN ? CPL : 1][4];  // the gain (the same for every row)
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int rr = min(wave + i * nw, M - 1);
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
-            load_row_chunk<ROW_X, XT>(src, (int64_t)rr * K, 4 * (int64_t)min(lane + 64 * j, nch - 1), xv[i][j],
-                                      unused, unused, unused);
+            load_row_chunk<IN, XT>(src, (int64_t)rr * K, 4 * (int64_t)min(lane + 64 * j, nch - 1), xv[i][j], unused,
+                                   unused, GAIN ? ov[j] : unused);
     }
     // 2. the weights of the wave's slices
     int gn[CB];
@@ -1227,10 +1229,20 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
                         mx = fmaxf(mx, fabsf(xv[i][j][e]));
                     }
             ss = wave_sum(ss);
-            mx = wave_max(mx);
             const float rr = rms_factor(ss, K, eps);
-            const float sc = quant_scale(__fmul_rn(mx, rr));
-            auto qv = [&](float v) { return quant_code(__fmul_rn(v, rr), sc); };
+            if constexpr (GAIN) {  // y = (x r) w: its max |y| alone decides the scale
+                mx = 0.0f;
+#pragma unroll
+                for (int j = 0; j < CPL; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xv[i][j][e] = __fmul_rn(__fmul_rn(xv[i][j][e], rr), ov[j][e]);
+                        if (lane + 64 * j < nch) mx = fmaxf(mx, fabsf(xv[i][j][e]));
+                    }
+            }
+            mx = wave_max(mx);
+            const float sc = quant_scale(GAIN ? mx : __fmul_rn(mx, rr));
+            auto qv = [&](float v) { return quant_code(GAIN ? v : __fmul_rn(v, rr), sc); };
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = lane + 64 * j;
@@ -1344,27 +1356,27 @@ static hipError_t run_row_cb(const ContractArgs &a, const RowSrc &src, float eps
             tgemv_row_kernel<NG, EPI, XT, RT, CB, 2, IN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
         return hipSuccess;
     }
-    // 2 to 16 rows of at most 2048, without a gain: a wave per row (8 chunks of
-    // 4 per lane); the gated g_norm and gains run at one row only
-    if constexpr (IN == ROW_X) {
+    // 2 to 16 rows of at most 2048, with or without a gain: a wave per row (8
+    // chunks of 4 per lane); the gated g_norm runs at one row only
+    if constexpr (IN == ROW_X || IN == ROW_GAIN) {
         const int m = (int)a.m;
         int waves = nslices < 16 ? nslices : 16;
         if (waves < m) waves = m;
         const size_t lds =
             (size_t)waves * CB * NG * 256 * sizeof(int32_t) + (size_t)16 * (a.k + 16) + 16 * sizeof(float);
-        if (nslices > waves)
-            return launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 2, 8, 1>>(a, src, eps, nslices, grid, waves, lds,
+        // rows of at most 2048 make at most 8 slices: one per wave
+        if (nslices > waves || a.k > 64 * 4 * 8) return hipErrorInvalidValue;
+        return launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 1, 8, 1, IN>>(a, src, eps, nslices, grid, waves, lds,
                                                                                 st);
-        return launch_rows<tgemv_rows_kernel<NG, EPI, XT, RT, CB, 1, 8, 1>>(a, src, eps, nslices, grid, waves, lds, st);
     }
-    return hipErrorInvalidValue;  // the gated g_norm and gains take one row only
+    return hipErrorInvalidValue;  // the gated g_norm takes one row only
 }
 
 template <int NG, int EPI, typename XT, typename RT, int IN>
 static hipError_t run_row_in(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
-    // four channel blocks take 10240 outputs or more; the gated g_norm's rows (at most 8192
-    // wide, o_proj square) never reach them, and its registers would not fit them
-    constexpr bool CB4 = NG == 1 && IN != ROW_GNORM && IN != ROW_GNORM_GAIN;
+    // four channel blocks take 10240 outputs or more: not with the gated g_norm (o_proj square,
+    // at most 8192 wide) or with a gain, whose registers would not fit them
+    constexpr bool CB4 = NG == 1 && IN == ROW_X;
     switch (gemv_channel_blocks(a.nc, NG, a.k, 1)) {
         case 4:
             if constexpr (CB4) return run_row_cb<NG, EPI, XT, RT, 4, IN>(a, src, eps, st);
@@ -1383,15 +1395,16 @@ static hipError_t run_row(const ContractArgs &a, const RowSrc &src, float eps, h
                     : run_row_in<NG, EPI, XT, RT, ROW_X>(a, src, eps, st);
 }
 
-// One row up to k = 8192, with or without a gain; 2 to 16 rows up to k =
-// 2048 without a gain, one wave per row (a wider row leaves the multi-row
+// One row up to k = 8192; 2 to 16 rows up to k = 2048, one wave per row
+// (12 with a gain: its second reduction per row made 16 rows slower than the
+// separate quantiser, measured 35.4 against 34.5 us per 1.3B layer) (a wider row leaves the multi-row
 // kernel too few registers, and its codes in LDS would limit the workgroups
 // per CU).
 bool contract_row_supported(int64_t m, int k, EpiKind epi, bool gain) {
     const bool kind = epi == EPI_GATES_STEP || epi == EPI_GLU || epi == EPI_RESID || epi == EPI_LINEAR;
     if (!kind || k % 16 || m < 1) return false;
     if (m == 1) return k <= 8192;
-    return m <= 16 && k <= 2048 && !gain;
+    return k <= 2048 && m <= (gain ? 12 : 16);
 }
 
 // The gated g_norm in o_proj (with or without o_proj's own gain): one row up

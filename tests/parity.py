@@ -92,9 +92,11 @@ def make_pair(d, inner, seed, device, gains=None, eps=1e-8):
               "g_norm": g["g_norm"]}
     elif gains == "distinct":
         gn = synth.norm_gains(d, inner, seed + 1)
-    elif isinstance(gains, tuple):  # only the named gains
+    elif isinstance(gains, tuple):  # only the named gains; an "i" gain is shared by f and g
         g = synth.norm_gains(d, inner, seed + 1)
         gn = {k: g[k] for k in gains}
+        if "i" in gn:
+            gn["f"] = gn["g"] = gn["i"]
     L = oracle.make_layer(lat, gn, eps)
     dgains = None
     if gn is not None:

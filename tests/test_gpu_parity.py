@@ -951,7 +951,9 @@ ROW_CASES = [
     (1, 2048, 5632, "bf16", "shared"),   # gains: each one-row contraction applies its own
     (1, 272, 1040, "f32", ("gate",)),
     (1, 272, 1040, "f32", ("o", "g_norm")),  # o_proj's gain after the gated g_norm
-    (4, 256, 512, "bf16", ("down",)),    # several rows: only the stages without a gain
+    (4, 256, 512, "bf16", ("down",)),    # several rows with a gain
+    (16, 2048, 5632, "bf16", "shared"),  # more than 12 rows with gains: the separate quantisers
+    (12, 2048, 2048, "f32", ("i", "gate", "down")),
     (3, 16, 48, "f32", None),
     (16, 48, 16, "bf16", None),          # 16 rows of three words; down_proj over one word
 ]
@@ -981,14 +983,14 @@ def test_decode_row_path_matches_separate(gpu, b, d, inner, act, gains):
                     steps = mmf.last_path().split(";")
                     fused = [k for k in steps if k.startswith("tgemv_row<")]
                     widest = 8192 if b == 1 else 2048  # widest input row a contraction quantises itself
-
+                    # a stage is fused where its row fits, with or without its gain; o_proj forms the
+                    # gated g_norm (then applies its own gain) at one row
                     def gain(name):
                         return gains == "shared" or (isinstance(gains, tuple) and name in gains)
-                    # a stage is fused where its row fits and, at several rows, where it has no gain;
-                    # o_proj forms the gated g_norm (then applies its own gain) at one row
+                    # more than 12 rows with a gain keep the separate quantiser
                     stages = (("gates_step", d, gain("i")), ("resid,gnorm", d if b == 1 else 1 << 30, False),
                               ("glu", d, gain("gate")), ("resid", inner, gain("down")))
-                    want = [e for e, k, g in stages if k <= widest and (b == 1 or not g)]
+                    want = [e for e, k, g in stages if k <= widest and not (g and b > 12)]
                     assert fused == ["tgemv_row<%s>" % e for e in want], steps
                     quant = [k for k in steps if "norm_quant" in k]
                     assert len(quant) == 4 - len(want), steps
@@ -1002,7 +1004,8 @@ def test_decode_row_path_matches_separate(gpu, b, d, inner, act, gains):
 
 
 @pytest.mark.parametrize("b,act,gains", [(1, "f32", None), (1, "bf16", ("g_norm",)), (16, "f32", None),
-                                          (16, "bf16", None), (1, "f32", "shared"), (1, "bf16", "shared")])
+                                          (16, "bf16", None), (1, "f32", "shared"), (1, "bf16", "shared"),
+                                          (12, "bf16", "shared")])
 def test_decode_default_path_end_to_end(gpu, b, act, gains):
     """The default decode step at the 1.3B shape (the contractions that quantise their own rows)
     against the free-running oracle, with g and z rounded to the activation type where the GPU
@@ -1033,15 +1036,11 @@ def test_decode_default_path_end_to_end(gpu, b, act, gains):
     assert rel < (1e-3 if act == "f32" else 4e-3), rel
 
 
-def test_decode_row_path_needs_few_rows_and_shared_gains(gpu):
+def test_decode_row_path_needs_few_rows_and_one_ifg_gain(gpu):
     mmf = _mmf()
     _, P = make_pair(256, 512, 980, gpu, "distinct")  # i/f/g gains differ: three quantisations of x
     x = bf16_tensor(synth.activations((1, 256), 981, "bf16"), gpu)
     mmf.layer_decode_step(P, x, dev(synth.activations((1, 256), 982), gpu))
-    assert "tgemv_row" not in mmf.last_path()
-    _, P1 = make_pair(256, 512, 986, gpu, "shared")  # several rows with gains: the separate quantisers
-    x1 = bf16_tensor(synth.activations((2, 256), 987, "bf16"), gpu)
-    mmf.layer_decode_step(P1, x1, dev(synth.activations((2, 256), 988), gpu))
     assert "tgemv_row" not in mmf.last_path()
     _, P2 = make_pair(256, 512, 983, gpu)
     x2 = bf16_tensor(synth.activations((17, 256), 984, "bf16"), gpu)  # more than one row block
