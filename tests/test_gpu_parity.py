@@ -951,6 +951,7 @@ ROW_CASES = [
     (1, 2048, 5632, "bf16", "shared"),   # gains: each one-row contraction applies its own
     (1, 272, 1040, "f32", ("gate",)),
     (1, 272, 1040, "f32", ("o", "g_norm")),  # o_proj's gain after the gated g_norm
+    (1, 4608, 256, "f32", ("o", "g_norm")),  # ... with two slices per wave in o_proj
     (4, 256, 512, "bf16", ("down",)),    # several rows with a gain
     (16, 2048, 5632, "bf16", "shared"),  # more than 12 rows with gains: the separate quantisers
     (12, 2048, 2048, "f32", ("i", "gate", "down")),
