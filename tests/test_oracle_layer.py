@@ -59,6 +59,33 @@ def test_identity_weight_block_closed_form():
     np.testing.assert_allclose(r["out"], out, rtol=1e-12, atol=1e-14)
 
 
+def test_identity_weight_block_with_g_norm_gain():
+    """The same closed form with a g_norm gain w: u = (h / rms(h)) * w * SiLU(g), the gain on the
+    normalised state (not on g, not after o_proj's own normalisation)."""
+    d, c, eps = 32, 0.25, 1e-8
+    eye = (np.eye(d) * c).astype(np.float32)
+    zero = np.zeros((d, d), np.float32)
+    lat = {"i": eye, "f": zero, "g": eye, "o": eye, "gate": np.concatenate([eye, -eye]), "down": eye}
+    w = (1.0 + 0.5 * np.sin(np.arange(d))).astype(np.float32)
+    L = oracle.make_layer(lat, {"g_norm": w}, eps=eps)
+    x = synth.activations((1, 5, d), 41)
+    r = oracle.layer_forward(L, x)
+
+    def deq(v):
+        q, s, _ = oracle.quantize(v, None, eps)
+        return q.astype(np.float64) / s.astype(np.float64)[..., None] * (c / d)
+
+    ihat = deq(x)
+    xt = 0.5 * ihat / (1 + np.exp(-ihat))
+    h = np.zeros_like(xt)
+    for t in range(5):
+        h[:, t] = xt[:, t] + (0.5 * h[:, t - 1] if t else 0.0)
+    rms = np.sqrt(np.mean(h ** 2, axis=-1, keepdims=True) + np.float64(np.float32(eps)))
+    u = h / rms * w.astype(np.float64) * (ihat / (1 + np.exp(-ihat)))
+    np.testing.assert_allclose(r["u"], u, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(r["x1"], x + deq(u), rtol=1e-12, atol=1e-14)
+
+
 def test_batch_rows_independent():
     L = _layer(48, 64, 33, gains=True)
     x = synth.activations((3, 4, 48), 34)
