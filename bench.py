@@ -5,18 +5,25 @@ One step is one serving pass over one batch of seeded synthetic input through
 a 24-layer HGRNBit stack (d=2048, MLP inner 5632, random ternarised weights):
   1. prefill: B sequences of T prompt tokens through every layer (chunked scan);
   2. decode: D tokens per sequence, one layer step at a time, each continuing
-     from the state the prefill left in that layer.
+     from the state the prefill left in that layer (a HIP graph per token step).
 value = layer-tokens/s = B*(T+D)*L / step time (metric "HGRNBit layer tokens/s").
 
 Also printed in the same JSON line:
   roofline     -- the dominant kernel at its shape (largest share of the step
                   time) against its roof: int8 MFMA peak for a prefill
-                  contraction, HBM for everything else. Prefill kernels are
-                  timed with HIP events on their stream inside the timed steps;
-                  decode kernels, which run inside a HIP graph there, are timed
-                  the same way on an eager copy of the decode steps queued
-                  behind a prefill;
-  cpu_baseline -- the CPU oracle on a bounded sample of the same workload.
+                  contraction, HBM for everything else. Kernels are timed by
+                  HIP events recorded around each launch on its stream:
+                  prefill kernels inside the timed steps; decode kernels, which
+                  run inside a HIP graph there, on an eager copy of the decode
+                  steps queued behind a prefill. Where profiles/ holds a
+                  rocprofv3 kernel trace of the same sources, that kernel's
+                  trace average is printed beside the event figure;
+  cpu_baseline -- the CPU oracle on a bounded sample of the same workload;
+  configs      -- with --extras (default): every other config of the workload
+                  (370M layer fp32; 370M and 2.7B stack prefills; the 1.3B
+                  decode step at batch 1, 16, 64; the long-sequence scan), each
+                  with its own roofline, next to a measured HBM ceiling.
+--only LEG runs one config leg alone, for profiling it.
 """
 from __future__ import annotations
 
@@ -47,8 +54,10 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle leg")
     ap.add_argument("--no-graph", action="store_true", help="launch decode steps eagerly instead of a HIP graph")
     ap.add_argument("--extras", type=int, default=1,
-                    help="0 skips the figures measured outside the timed steps (other batches, B=8 prefill, "
-                         "derivatives, generation)")
+                    help="0 skips the figures measured outside the timed steps (the other configs, the "
+                         "measured HBM ceiling, derivatives, generation)")
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "prefill_b8", "ceiling"],
+                    help="run one config leg alone and print its JSON (for profiling a config)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (for scaling HBM counters)")
     ap.add_argument("--vendor-int8-gemm", action="store_true",
@@ -143,9 +152,9 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
     contraction (m rows, n outputs over all groups, k): ops = 2 m n k; bytes = packed
       weights n k / 4 + int8 codes m k per activation tensor + scale and code sum 8 m per
       tensor + the epilogue's own traffic per output channel c of a group:
-        gates: f, x~ (fp32) and g (bf16) written = 10 B; gates_step: h read and written
-        (fp32) and g written (bf16) = 10 B; glu: z (bf16) = 2 B; resid: residual read and
-        sum written, one fp32 and one bf16 = 6 B; linear: 4 B.
+        gates: f, x~ and g written (fp32) = 12 B; gates_step: h read and written and g
+        written (fp32) = 12 B; glu: z (fp32) = 4 B; resid: residual read and sum written, one
+        fp32 and one bf16 = 6 B; linear: 4 B.
     tgemv_row<epi,T> (a contraction that quantises its own input rows): as a contraction, with
       the rows read once in type T (m k sizeof T) in place of the codes, scale and code sum;
       tgemv_row<resid,gnorm,T>: h (fp32) and g (T) per element and g_norm's gain (fp32) per k.
@@ -153,19 +162,13 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
     gnorm_quant<T>: h (fp32) and g (sizeof T) read + codes written per element, 8 B per row.
     scan (m = b t, k = d): f and x~ read, h written, 12 B per element.
     scan_bwd (m = b t, k = d): dh, f and h read, dx and df written, 20 B per element.
-    decode_step_xcd (m = b, n = d, k = inner; one whole decode step of a block): ops =
-      2 b (4 d^2 + 3 d inner); bytes = all packed weights (4 d^2 + 3 d inner) / 4 + x read
-      and out written (activation dtype) + h read and written (fp32) per row element.
     """
     base, args = _kind(kernel)
-    if base == "decode_step_xcd":
-        wts = 4.0 * n * n + 3.0 * n * k
-        return 2.0 * m * wts, wts / 4.0 + m * n * (2.0 * ACT_BYTES + 8.0)
     if base in ("tgemm", "tgemm_dma", "tgemv", "tgemv_row"):
         epi = args[0]
         na = 3 if "split_a" in args else 1
         ng = {"gates": 3, "gates_step": 3, "glu": 2}.get(epi, 1)
-        per_c = {"gates": 10, "gates_step": 10, "glu": 2, "resid": 4 + ACT_BYTES, "linear": 4}[epi]
+        per_c = {"gates": 12, "gates_step": 12, "glu": 4, "resid": 4 + ACT_BYTES, "linear": 4}[epi]
         if base == "tgemv_row":
             tb = 4.0 if args[-1] == "f32" else ACT_BYTES
             # the gated g_norm reads h (fp32), g and g_norm's gain instead of x
@@ -193,8 +196,6 @@ KERNEL_SOURCES = {
     "tgemv_row": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
     "tgemm": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
     "tgemm_dma": ["k_contract.hip", "epilogue.hpp"] + _COMMON,
-    "tgemv_q": ["k_gemv_q.hip", "row_quant.hpp", "epilogue.hpp"] + _COMMON,
-    "decode_step_xcd": ["k_decode.hip", "row_quant.hpp", "epilogue.hpp"] + _COMMON,
     "norm_quant": ["k_quant.hip", "row_quant.hpp"] + _COMMON,
     "gnorm_quant": ["k_quant.hip", "row_quant.hpp"] + _COMMON,
     "scan": ["k_scan.hip"] + _COMMON,
@@ -253,6 +254,359 @@ def stored_traffic(key: str):
     return None
 
 
+class KernelTable:
+    """Per-kernel totals from the library's timing records (events bound to each dispatch),
+    keyed by variant and shape, with each launch's algorithmic ops and bytes."""
+
+    def __init__(self):
+        self.k = {}
+
+    def add(self, recs, phase: str, scale: float):
+        for name, m, n, k, ms in recs:
+            key = "%s m=%d n=%d k=%d" % (name, m, n, k)
+            e = self.k.setdefault(key, dict(name=name, m=m, n=n, k=k, phase=phase, launches=0.0, ms=0.0))
+            e["launches"] += scale
+            e["ms"] += ms * scale
+        for e in self.k.values():
+            e["avg_ms"] = e["ms"] / e["launches"]
+            e["ops"], e["bytes"] = algorithmic(e["name"], e["m"], e["n"], e["k"])
+        return self
+
+    def total_ms(self, phase=None):
+        return sum(e["ms"] for e in self.k.values() if phase is None or e["phase"] == phase)
+
+    def dominant(self):
+        return max(self.k.items(), key=lambda kv: kv[1]["ms"])
+
+    def roofline(self, step_ms: float, key=None) -> dict:
+        """The dominant kernel (or `key`) against its roof: the int8 MFMA peak for a prefill-shaped
+        contraction, HBM for everything else; achieved = algorithmic work per launch / average
+        launch duration."""
+        key, e = (key, self.k[key]) if key else self.dominant()
+        avg_s = e["avg_ms"] / 1000.0
+        if e["name"].startswith("tgemm"):
+            roof = dict(bound="mfma", achieved=round(e["ops"] / avg_s / 1e12, 2), peak=INT8_MFMA_PEAK_TOPS,
+                        unit="TFLOP/s")
+        else:
+            roof = dict(bound="hbm", achieved=round(e["bytes"] / avg_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        roof["traffic"] = stored_traffic(key)
+        roof["kernel"] = key
+        roof["phase"] = e["phase"]
+        roof["avg_launch_us"] = round(e["avg_ms"] * 1000.0, 2)
+        roof["launches_per_step"] = round(e["launches"], 1)
+        roof["algorithmic_per_launch"] = e["ops"] if roof["bound"] == "mfma" else e["bytes"]
+        roof["share_of_step"] = round(e["ms"] / step_ms, 3)
+        tr = stored_trace_us(key)
+        if tr:  # the same kernel's average in a committed rocprofv3 trace of these sources
+            us, fname = tr
+            work = roof["algorithmic_per_launch"]
+            roof["trace_avg_launch_us"] = us
+            roof["trace_frac"] = round(work / (us / 1e6) / (1e12 if roof["bound"] == "mfma" else 1e9) / roof["peak"], 4)
+            roof["trace_file"] = "profiles/" + fname
+        return roof
+
+    def contractions(self, phase: str = "prefill"):
+        """All prefill-shaped contractions together against the int8 MFMA peak."""
+        pre = [e for e in self.k.values() if e["phase"] == phase and e["name"].startswith("tgemm")]
+        if not pre:
+            return None
+        ops = sum(e["ops"] * e["launches"] for e in pre)
+        ms = sum(e["ms"] for e in pre)
+        tops = ops / (ms / 1000) / 1e12
+        return dict(achieved=round(tops, 1), peak=INT8_MFMA_PEAK_TOPS, unit="TFLOP/s",
+                    frac=round(tops / INT8_MFMA_PEAK_TOPS, 4),
+                    per_kernel={e["name"]: round(e["ops"] / (e["avg_ms"] / 1000) / 1e12 / INT8_MFMA_PEAK_TOPS, 4)
+                                for e in pre})
+
+    def breakdown(self, top: int = 0) -> dict:
+        out = {}
+        rows = sorted(self.k.items(), key=lambda kv: -kv[1]["ms"])
+        for key, e in rows[:top] if top else rows:
+            t = e["avg_ms"] / 1000.0
+            row = dict(phase=e["phase"], launches_per_step=round(e["launches"], 1), avg_us=round(e["avg_ms"] * 1000, 2),
+                       ms_per_step=round(e["ms"], 3))
+            if e["ops"]:
+                row["int8_tops"] = round(e["ops"] / t / 1e12, 1)
+                row["frac_mfma"] = round(e["ops"] / t / 1e12 / INT8_MFMA_PEAK_TOPS, 4)
+            row["gbs"] = round(e["bytes"] / t / 1e9, 1)
+            row["frac_hbm"] = round(e["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4)
+            out[key] = row
+        return out
+
+
+def timed_records(mmf, fn, reps: int = 1):
+    """Runs fn() reps times with the library's per-launch timing on; returns the records."""
+    import torch
+    torch.cuda.synchronize()
+    mmf.timing_enable(True)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    mmf.timing_enable(False)
+    return mmf.timing_collect()
+
+
+def device_layers(mmf, torch, d: int, inner: int, L: int, seed: int, dev):
+    """L blocks of random ternarised weights: latent weights ~ N(0, 0.02) drawn on the device
+    (torch's generator seeded per layer with c*1000 + l), packed by mmf_ternary_pack."""
+    shapes = {"i": (d, d), "f": (d, d), "g": (d, d), "o": (d, d), "gate": (2 * inner, d), "down": (d, inner)}
+    layers = []
+    gen = torch.Generator(device=dev)
+    for l in range(L):
+        gen.manual_seed(seed * 1000 + l)
+        lat = {k: torch.randn(s_, device=dev, generator=gen) * 0.02 for k, s_ in shapes.items()}
+        layers.append(mmf.LayerParams.pack(lat))
+        del lat
+    torch.cuda.synchronize()
+    return layers
+
+
+def event_ms(torch, fn, reps: int, warmup: int = 1):
+    """Mean milliseconds of fn() over reps runs (events on the current stream), after warmup runs."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def hbm_ceilings(mmf, torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> dict:
+    """Measured HBM roof: mmf_hbm_ceiling's streaming read and streaming copy of nbytes."""
+    src = torch.ones(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(8192, dtype=torch.uint8, device=dev)
+    mmf.hbm_ceiling(src, sink, "read")
+    mmf.hbm_ceiling(src, dst, "copy")
+    recs = timed_records(mmf, lambda: (mmf.hbm_ceiling(src, sink, "read"), mmf.hbm_ceiling(src, dst, "copy")), reps)
+    rd = sum(r[4] for r in recs if r[0] == "stream_read") / reps
+    cp = sum(r[4] for r in recs if r[0] == "stream_copy") / reps
+    del src, dst, sink
+    return dict(bytes=nbytes, read_GBs=round(nbytes / rd / 1e6, 1), copy_GBs=round(2 * nbytes / cp / 1e6, 1),
+                read_frac=round(nbytes / rd / 1e6 / HBM_PEAK_GBS, 4), copy_frac=round(2 * nbytes / cp / 1e6 / HBM_PEAK_GBS, 4),
+                note="hand-written streaming read (cached 16-byte loads) and copy (non-temporal), 2048 x 256 threads")
+
+
+def with_ceiling(roof: dict, ceil: dict) -> dict:
+    """The HBM-bound roof also read against the measured streaming roof."""
+    if ceil and roof.get("bound") == "hbm":
+        roof["frac_of_measured_read"] = round(roof["achieved"] / ceil["read_GBs"], 4)
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / ceil["copy_GBs"], 4)
+    return roof
+
+
+def leg_prefill(mmf, torch, dev, shape: str, b: int, t: int, seed: int, reps: int, ceil=None) -> dict:
+    """A whole-stack prefill of one config: L layers of `shape`, b x t bf16 tokens (x ~ N(0, 1)
+    drawn on the device), scan mode auto; value = layer-tokens/s."""
+    from ternary_weight_matmul_amd import synth
+    d, inner, L = synth.SHAPES[shape]
+    layers = device_layers(mmf, torch, d, inner, L, seed, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 10 + 1)
+    x = torch.randn((b, t, d), device=dev, generator=gen).to(torch.bfloat16)
+    bufs = [torch.empty_like(x) for _ in range(2)]
+    hs = torch.empty((L, b, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(mmf.layer_workspace_size(layers[0], b, t), dtype=torch.uint8, device=dev)
+
+    def run():
+        cur = x
+        for l in range(L):
+            mmf.layer_fwd(layers[l], cur, None, out=bufs[l % 2], h_last=hs[l], ws=ws)
+            cur = bufs[l % 2]
+
+    ms = event_ms(torch, run, reps)
+    kt = KernelTable().add(timed_records(mmf, run), "prefill", 1.0)
+    del x, bufs, hs, ws, layers
+    return dict(workload="%s stack prefill: %d layers d=%d inner=%d, bf16, B=%d x T=%d" % (shape, L, d, inner, b, t),
+                value=round(b * t * L / (ms / 1000), 1), unit="layer-tokens/s", ms=round(ms, 3),
+                stack_tokens_per_s=round(b * t / (ms / 1000), 1),
+                roofline=with_ceiling(kt.roofline(ms), ceil), contraction_roofline=kt.contractions(),
+                kernels=kt.breakdown(8))
+
+
+def leg_c1(mmf, torch, dev, reps: int = 100, cpu: bool = True) -> dict:
+    """One 370M-width layer, fp32, batch 1 x 128 tokens, recurrent scan (the small config the
+    oracle finishes in seconds): median of `reps` event-timed calls; the oracle timed on the same
+    seeded host input and weights."""
+    import numpy as np
+    from ternary_weight_matmul_amd import synth
+    d, inner, _ = synth.SHAPES["370M"]
+    lat = synth.latent_weights(d, inner, synth.layer_seed(1, 0))
+    P = mmf.LayerParams.pack({k: torch.from_numpy(v).to(dev) for k, v in lat.items()})
+    xs = synth.activations((1, 128, d), 1)
+    x = torch.from_numpy(xs).to(dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(mmf.layer_workspace_size(P, 1, 128), dtype=torch.uint8, device=dev)
+
+    def run():
+        mmf.layer_fwd(P, x, None, out=out, ws=ws, mode="recurrent")
+
+    for _ in range(5):
+        run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    kt = KernelTable().add(timed_records(mmf, run, 20), "prefill", 1.0 / 20)
+    res = dict(workload="370M layer, fp32, B=1 x T=128, recurrent scan", value=round(128 / (ms / 1000), 1),
+               unit="layer-tokens/s", ms_median=round(ms, 4), roofline=kt.roofline(ms), kernels=kt.breakdown(6),
+               note="latency-bound: the whole layer is a few microseconds per kernel")
+    if cpu:
+        import oracle
+        Lo = oracle.make_layer(lat)
+        t0 = time.perf_counter()
+        oracle.layer_forward(Lo, xs)
+        dt = time.perf_counter() - t0
+        res["cpu_oracle"] = dict(value=round(128 / dt, 2), unit="layer-tokens/s", cores=oracle.num_threads(),
+                                 cpu=cpu_model(), sample="the whole config: 1 layer, 128 tokens (%.2f s)" % dt)
+    return res
+
+
+def leg_decode(mmf, torch, dev, batches=(1, 16, 64), steps: int = 32, ceil=None) -> dict:
+    """The 1.3B decode step (24 layers, bf16 x, fp32 carried state h ~ N(0,1)) at each batch:
+    one step of every layer captured in a HIP graph and replayed; per-kernel durations from an
+    eager copy of 4 steps (events bound to each dispatch)."""
+    from ternary_weight_matmul_amd import synth
+    d, inner, L = synth.SHAPES["1.3B"]
+    layers = device_layers(mmf, torch, d, inner, L, 3, dev)
+    res = {}
+    for b in batches:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(300 + b)
+        hs = torch.randn((L, b, d), device=dev, generator=gen)
+        xin = torch.randn((b, d), device=dev, generator=gen).to(torch.bfloat16)
+        outs = [torch.empty_like(xin) for _ in range(2)]
+        ws = torch.empty(mmf.layer_workspace_size(layers[0], b, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            y = xin
+            for l in range(L):
+                y = mmf.layer_decode_step(layers[l], y, hs[l], out=outs[l % 2], ws=ws)
+
+        step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        us = event_ms(torch, g.replay, steps, warmup=3) * 1000.0
+        kt = KernelTable().add(timed_records(mmf, step, 4), "decode", 0.25)
+        res[str(b)] = dict(us_per_layer=round(us / L, 2), us_per_token_step=round(us, 2),
+                           layer_tokens_per_s=round(b * L / (us / 1e6), 1),
+                           launches_per_layer=round(sum(e["launches"] for e in kt.k.values()) / L, 1),
+                           roofline=with_ceiling(kt.roofline(us / 1000.0), ceil), kernels=kt.breakdown(4))
+        del hs, xin, outs, ws, g
+    del layers
+    return dict(workload="1.3B decode step: 24 layers d=2048 inner=5632, bf16 x, fp32 state, HIP graph", by_batch=res)
+
+
+def leg_c5(mmf, torch, dev, reps: int = 10, ceil=None, cpu: bool = True) -> dict:
+    """The long-sequence scan stress at 1.3B width: x~ ~ N(0,1) and f = sigmoid(N(2,1)) fp32,
+    16 x 32768 x 2048 (4 GiB each), chunked scan, h out of place; value = tokens/s (b*t per
+    second). The oracle runs the sequential scan on a sample (one sequence, 256 channels)."""
+    b, t, d = 16, 32768, 2048
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    x = torch.randn((b, t, d), device=dev, generator=gen)
+    f = torch.sigmoid(torch.randn((b, t, d), device=dev, generator=gen) + 2.0)
+    h = torch.empty_like(x)
+
+    def run():
+        mmf.hgrn_scan_fwd(x, f, None, "chunk", out=h)
+
+    ms = event_ms(torch, run, reps)
+    kt = KernelTable().add(timed_records(mmf, run, reps), "scan", 1.0 / reps)
+    res = dict(workload="HGRN scan stress: d=2048, B=16 x T=32768, fp32, chunked", value=round(b * t / (ms / 1000), 1),
+               unit="tokens/s", ms=round(ms, 3), roofline=with_ceiling(kt.roofline(ms), ceil), kernels=kt.breakdown())
+    if cpu:
+        import numpy as np
+        import oracle
+        xs = x[0, :, :256].double().cpu().numpy()[None]
+        fs = f[0, :, :256].double().cpu().numpy()[None]
+        t0 = time.perf_counter()
+        oracle.hgrn_scan(xs, fs)
+        dt = time.perf_counter() - t0
+        res["cpu_oracle"] = dict(value=round(t * 256 / d / dt, 1), unit="tokens/s (full-width equivalent)",
+                                 cores=oracle.num_threads(), cpu=cpu_model(),
+                                 sample="sequential scan of one sequence x 256 of 2048 channels (%.2f s), "
+                                        "scaled to the full width" % dt)
+        del xs, fs
+    del x, f, h
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def run_only(args):
+    """One leg alone (for profiling a config under rocprofv3): prints its JSON."""
+    import torch
+    import ternary_weight_matmul_amd as mmf
+    mmf.load()
+    dev = torch.device("cuda", 0)
+    cpu = args.cpu_baseline != 0
+    if args.only == "c1":
+        res = leg_c1(mmf, torch, dev, cpu=cpu)
+    elif args.only == "c2":
+        res = leg_prefill(mmf, torch, dev, "370M", 8, 2048, 2, 5)
+    elif args.only == "c4":
+        res = leg_prefill(mmf, torch, dev, "2.7B", 4, 4096, 4, 3)
+    elif args.only == "prefill_b8":
+        res = leg_prefill(mmf, torch, dev, "1.3B", 8, 2048, 3, 3)
+    elif args.only == "c3":
+        res = leg_decode(mmf, torch, dev)
+    elif args.only == "c5":
+        res = leg_c5(mmf, torch, dev, cpu=cpu)
+    else:
+        res = hbm_ceilings(mmf, torch, dev)
+    print(json.dumps({"leg": args.only, **res}), flush=True)
+
+
+def stored_trace_us(key: str):
+    """(average duration in us, file) of kernel `key` from a rocprofv3 kernel-trace summary under
+    profiles/ (lines "bench_kernel: <key>", "trace_avg_us: <us>", "sources: <digest>"), if one
+    exists for the current sources of that kernel."""
+    pdir = os.path.join(ROOT, "profiles")
+    files = kernel_files(key)
+    if not os.path.isdir(pdir) or not files:
+        return None
+    digest = source_digest(files)
+    for name in sorted(os.listdir(pdir)):
+        if not name.startswith("kernel_stats_"):
+            continue
+        cur = {}
+        with open(os.path.join(pdir, name)) as f:
+            for line in f:
+                kk, _, vv = line.partition(":")
+                kk = kk.strip()
+                if kk == "bench_kernel":
+                    cur = {"bench_kernel": vv.strip()}
+                elif kk in ("trace_avg_us", "sources") and cur:
+                    cur[kk] = vv.strip()
+                    if cur.get("bench_kernel") == key and cur.get("sources") == digest and "trace_avg_us" in cur:
+                        return float(cur["trace_avg_us"]), name
+    return None
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -264,6 +618,9 @@ def main():
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.only:
+        run_only(args)
+        return
     import numpy as np
     import torch
     import ternary_weight_matmul_amd as mmf
@@ -277,13 +634,11 @@ def main():
 
     # ---- untimed preparation: weights ternarised + packed on the device, inputs resident in HBM
     t0 = time.time()
-    layers = []
-    for l in range(L):
-        lat = synth.latent_weights(d, inner, synth.layer_seed(seed, l))
-        layers.append(mmf.LayerParams.pack({k: torch.from_numpy(v).to(dev) for k, v in lat.items()}))
-        del lat
-    x_prefill = torch.from_numpy(synth.activations((B, T, d), seed * 10 + 1, "bf16")).to(dev).to(torch.bfloat16)
-    x_decode = torch.from_numpy(synth.activations((max(D, 1), B, d), seed * 10 + 2, "bf16")).to(dev).to(torch.bfloat16)
+    layers = device_layers(mmf, torch, d, inner, L, seed, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 10 + 1)
+    x_prefill = torch.randn((B, T, d), device=dev, generator=gen).to(torch.bfloat16)
+    x_decode = torch.randn((max(D, 1), B, d), device=dev, generator=gen).to(torch.bfloat16)
     bufs = [torch.empty_like(x_prefill) for _ in range(2)]
     hs = torch.zeros((L, B, d), dtype=torch.float32, device=dev)
     ws_p = torch.empty(mmf.layer_workspace_size(layers[0], B, T), dtype=torch.uint8, device=dev)
@@ -324,15 +679,12 @@ def main():
             else:
                 decode_step()
 
-    def step():
+    for _ in range(args.warmup):
         prefill()
         decode()
-
-    for _ in range(args.warmup):
-        step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps; prefill kernels bracketed by HIP events on their stream
+    # ---- timed region: K steps; prefill kernels timed per dispatch on their stream
     mmf.timing_enable(True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -352,10 +704,9 @@ def main():
     decode_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
 
     # ---- decode kernels: the timed region replays them inside a HIP graph, where no event can
-    # bracket a single kernel. The same decode steps are issued once more eagerly, with the
-    # per-launch events, behind a queued prefill so that the device never waits on the host
-    # between them; their event-measured durations stand for the graph's (the sum is reported
-    # next to the graph's own time per step as a check).
+    # be bound to one kernel. The same decode steps are issued once more eagerly behind a queued
+    # prefill (so the device never waits on the host between them), each kernel timed by events
+    # bound to its own dispatch: its start and end, as a kernel trace records them.
     DM = min(4, D)
     drecs = []
     if DM:
@@ -372,81 +723,41 @@ def main():
     tokens = B * (T + D)
     value = tokens * L / (ms_per_step / 1000.0)
 
-    # ---- per-kernel totals per step, keyed by variant and shape
-    kernels = {}
-
-    def add(src, phase, scale):
-        for name, m, n, k, ms in src:
-            key = "%s m=%d n=%d k=%d" % (name, m, n, k)
-            e = kernels.setdefault(key, dict(name=name, m=m, n=n, k=k, phase=phase, launches=0.0, ms=0.0))
-            e["launches"] += scale
-            e["ms"] += ms * scale
-
-    add(recs, "prefill", 1.0 / args.steps)
+    kt = KernelTable()
+    kt.add(recs, "prefill", 1.0 / args.steps)
     if DM:
-        add(drecs, "decode", float(D) / DM)
-    for e in kernels.values():
-        e["avg_ms"] = e["ms"] / e["launches"]
-        e["ops"], e["bytes"] = algorithmic(e["name"], e["m"], e["n"], e["k"])
-    total_kernel_ms = sum(e["ms"] for e in kernels.values())
-    dom_key, dom = max(kernels.items(), key=lambda kv: kv[1]["ms"])
-    avg_s = dom["avg_ms"] / 1000.0
-    if dom["name"].startswith("tgemm"):
-        achieved = dom["ops"] / avg_s / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_MFMA_PEAK_TOPS, unit="TFLOP/s")
-    else:
-        achieved = dom["bytes"] / avg_s / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s")
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = stored_traffic(dom_key)
-    roof["kernel"] = dom_key
-    roof["phase"] = dom["phase"]
-    roof["avg_launch_us"] = round(dom["avg_ms"] * 1000.0, 2)
-    roof["algorithmic_per_launch"] = dom["ops"] if roof["bound"] == "mfma" else dom["bytes"]
-    roof["share_of_step"] = round(dom["ms"] / ms_per_step, 3)
-
-    breakdown = {}
-    for key, e in sorted(kernels.items(), key=lambda kv: -kv[1]["ms"]):
-        row = dict(phase=e["phase"], launches_per_step=round(e["launches"], 1), avg_us=round(e["avg_ms"] * 1000, 2),
-                   ms_per_step=round(e["ms"], 3))
-        t = e["avg_ms"] / 1000.0
-        if e["ops"]:
-            row["int8_tops"] = round(e["ops"] / t / 1e12, 1)
-            row["frac_mfma"] = round(e["ops"] / t / 1e12 / INT8_MFMA_PEAK_TOPS, 4)
-        row["gbs"] = round(e["bytes"] / t / 1e9, 1)
-        row["frac_hbm"] = round(e["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4)
-        breakdown[key] = row
-
-    # the best prefill contraction against the MFMA roof, for reference next to the dominant kernel
-    pre = [e for e in kernels.values() if e["phase"] == "prefill" and e["ops"]]
-    prefill_gemm = None
-    if pre:
-        ops = sum(e["ops"] * e["launches"] for e in pre)
-        ms = sum(e["ms"] for e in pre)
-        prefill_gemm = dict(achieved=round(ops / (ms / 1000) / 1e12, 1), peak=INT8_MFMA_PEAK_TOPS, unit="TFLOP/s",
-                            frac=round(ops / (ms / 1000) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
-                            note="all prefill contractions together, int8 ops over their event-measured time")
-
-    # ---- outside the timed region: the scan's derivative at the prefill's scan shape, and the
-    # decode step at the other batch sizes of the 1.3B decode workload (graph-replayed)
+        kt.add(drecs, "decode", float(D) / DM)
     ex = args.extras != 0
-    scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev) if ex and T > 0 else None
-    bitlinear_bwd = measure_bitlinear_bwd(mmf, torch, layers[0].o, B * T, dev) if ex and T > 0 else None
-    layer_bwd = measure_layer_bwd(mmf, torch, layers[0], B, T, d, dev) if ex and T > 0 else None
-    by_batch = {str(B): round(decode_ms * 1000 / D / L, 2)} if D else {}
-    if ex and D and graph is not None:
-        for bb in (1, 64):
-            if bb != B:
-                by_batch[str(bb)] = round(decode_us_per_layer(mmf, torch, layers, bb, d, dev, seed), 2)
-    by_batch = dict(sorted(by_batch.items(), key=lambda kv: int(kv[0])))
-    prefill_b8 = measure_prefill(mmf, torch, layers, 8, T, d, dev, seed) if ex and T > 0 and B != 8 else None
-    generate = [measure_generate(mmf, torch, layers, bb, d, dev, seed) for bb in (1, B)] if ex and D else None
+    ceil = hbm_ceilings(mmf, torch, dev) if ex else None
+    roof = with_ceiling(kt.roofline(ms_per_step), ceil)
+
+    # ---- outside the timed region: every other config of the workload, the derivatives and
+    # generation, each with its own roofline
+    configs = None
+    scan_bwd = bitlinear_bwd = layer_bwd = generate = None
+    if ex:
+        del bufs, ws_p
+        torch.cuda.empty_cache()
+        configs = {}
+        configs["c1"] = leg_c1(mmf, torch, dev, cpu=args.cpu_baseline != 0)
+        configs["c2"] = leg_prefill(mmf, torch, dev, "370M", 8, 2048, 2, 5, ceil)
+        configs["c3"] = leg_decode(mmf, torch, dev, ceil=ceil)
+        configs["c4"] = leg_prefill(mmf, torch, dev, "2.7B", 4, 4096, 4, 3, ceil)
+        configs["prefill_1p3b_b8"] = leg_prefill(mmf, torch, dev, "1.3B", 8, 2048, 3, 3, ceil)
+        torch.cuda.empty_cache()
+        configs["c5"] = leg_c5(mmf, torch, dev, ceil=ceil, cpu=args.cpu_baseline != 0)
+        torch.cuda.empty_cache()
+        if T > 0:
+            scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev)
+            bitlinear_bwd = measure_bitlinear_bwd(mmf, torch, layers[0].o, B * T, dev)
+            layer_bwd = measure_layer_bwd(mmf, torch, layers[0], B, T, d, dev)
+        if D:
+            generate = [measure_generate(mmf, torch, layers, bb, d, dev, seed) for bb in (1, B)]
 
     cpu = None
     if args.cpu_baseline:
         cpu = cpu_baseline(d, inner, seed)
 
-    dsum = sum(e["ms"] for e in kernels.values() if e["phase"] == "decode")
     line = {
         "metric": "HGRNBit layer tokens/s (prefill + decode), 1.3B shape; % HBM / int8 MFMA peak",
         "value": round(value, 1),
@@ -459,65 +770,37 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 x ternary -> int32 contraction; bf16 activations; fp32 state",
-        "data": "synthetic: seeded x~N(0,1) bf16, latent weights~N(0,0.02) ternarised on device",
+        "data": "synthetic: x ~ N(0,1) bf16 and latent weights ~ N(0,0.02) drawn on the device (seeded), "
+                "ternarised and packed on the device",
         "config": {
             "workload": "hgrnbit-%s-serve: %d layers d=%d inner=%d, prefill B=%d x T=%d, then %d decode steps" % (
                 args.shape, L, d, inner, B, T, D),
             "layers": L, "d": d, "inner": inner, "batch": B, "prompt_tokens": T, "decode_steps": D,
             "decode_launch": "hip-graph" if graph is not None else "eager",
         },
+        "roofline": roof,
+        "cpu_baseline": cpu,
         "stack_tokens_per_s": round(tokens / (ms_per_step / 1000.0), 1),
         "prefill_ms": round(prefill_ms, 3),
         "decode_ms": round(decode_ms, 3),
         "prefill_layer_tokens_per_s": round(B * T * L / (prefill_ms / 1000), 1),
         "decode_layer_tokens_per_s": round(B * D * L / (decode_ms / 1000), 1) if D else None,
         "decode_us_per_token_step": round(decode_ms * 1000 / D, 2) if D else None,
-        "decode_kernel_sum_us_per_token_step": round(dsum * 1000 / D, 2) if D else None,
-        "roofline": roof,
-        "prefill_contraction_roofline": prefill_gemm,
-        "decode_us_per_layer_by_batch": by_batch,
-        "prefill_b8": prefill_b8,
+        "decode_us_per_layer": round(decode_ms * 1000 / D / L, 2) if D else None,
+        "decode_kernel_sum_us_per_token_step": round(kt.total_ms("decode") * 1000 / D, 2) if D else None,
+        "prefill_contraction_roofline": kt.contractions(),
+        "hbm_ceiling": ceil,
+        "configs": configs,
         "scan_bwd": scan_bwd,
         "bitlinear_bwd": bitlinear_bwd,
         "layer_bwd": layer_bwd,
         "generate": generate,
-        "cpu_baseline": cpu,
-        "kernels": breakdown,
-        "kernel_ms_per_step": round(total_kernel_ms, 3),
+        "kernels": kt.breakdown(),
+        "kernel_ms_per_step": round(kt.total_ms(), 3),
         "sources": source_digest(),
         "prep_s": round(prep_s, 1),
     }
     print(json.dumps(line), flush=True)
-
-
-def measure_prefill(mmf, torch, layers, b: int, t: int, d: int, dev, seed: int, reps: int = 3) -> dict:
-    """The whole-stack prefill alone at batch b (the 1.3B prefill read at b = 8, t = 2048), seeded
-    bf16 input, timed with events over `reps` runs after one warm-up."""
-    from ternary_weight_matmul_amd import synth
-    L = len(layers)
-    x = torch.from_numpy(synth.activations((b, t, d), seed * 10 + 5, "bf16")).to(dev).to(torch.bfloat16)
-    bufs = [torch.empty_like(x) for _ in range(2)]
-    hs = torch.empty((L, b, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(mmf.layer_workspace_size(layers[0], b, t), dtype=torch.uint8, device=dev)
-
-    def run():
-        cur = x
-        for l in range(L):
-            mmf.layer_fwd(layers[l], cur, None, out=bufs[l % 2], h_last=hs[l], ws=ws)
-            cur = bufs[l % 2]
-
-    run()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
-    for _ in range(reps):
-        run()
-    ev[1].record()
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / reps
-    del x, bufs, hs, ws
-    return dict(batch=b, prompt_tokens=t, ms=round(ms, 3), layer_tokens_per_s=round(b * t * L / (ms / 1000), 1),
-                stack_tokens_per_s=round(b * t / (ms / 1000), 1))
 
 
 def measure_scan_bwd(mmf, torch, b: int, t: int, d: int, dev, launches: int = 10) -> dict:
@@ -650,37 +933,6 @@ def measure_generate(mmf, torch, layers, b: int, d: int, dev, seed: int, vocab: 
                 note="embed + %d decode blocks + greedy ternary head per step, HIP graph, tokens stay on the device" % L)
 
 
-def decode_us_per_layer(mmf, torch, layers, b: int, d: int, dev, seed: int, steps: int = 32) -> float:
-    """One decode step of every layer at batch b, captured in a HIP graph and replayed `steps`
-    times from a seeded state; microseconds per layer."""
-    L = len(layers)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(seed * 100 + b)
-    hs = torch.randn((L, b, d), device=dev, generator=gen)
-    xin = torch.randn((b, d), device=dev, generator=gen).to(torch.bfloat16)
-    outs = [torch.empty_like(xin) for _ in range(2)]
-    ws = torch.empty(mmf.layer_workspace_size(layers[0], b, 1), dtype=torch.uint8, device=dev)
-
-    def step():
-        y = xin
-        for l in range(L):
-            y = mmf.layer_decode_step(layers[l], y, hs[l], out=outs[l % 2], ws=ws)
-
-    step()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        g.replay()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e6 / steps / L
-
-
 def cpu_baseline(d: int, inner: int, seed: int) -> dict:
     """The oracle (plain C + numpy fp64, OpenMP over independent outputs) on a bounded sample:
     one layer of the same shape, a 1024-token prefill of one sequence plus 16 decode steps at
@@ -703,7 +955,7 @@ def cpu_baseline(d: int, inner: int, seed: int) -> dict:
     dt = time.perf_counter() - t0
     tokens = T0 + S0 * B0
     return {"value": round(tokens / dt, 2), "unit": "layer-tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": "1 layer at the same shape: prefill of 1x%d tokens + %d decode steps at batch %d "
                       "(%d layer-tokens, %.1f s)" % (T0, S0, B0, tokens, dt)}
 

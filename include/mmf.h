@@ -285,7 +285,8 @@ mmf_status mmf_hgrn_scan_bwd(const float *f, const float *h, const float *h0, co
  *   [a | b] = BitLinear_gate(x1);  z = SiLU(a) * b
  *   out = x1 + BitLinear_down(z)
  *  x, out : [b][t][d] in dtype act (fp32 or bf16); everything inside is fp32
- *  (quantised codes int8, contractions exact int32).
+ *  (quantised codes int8, contractions exact int32), including the stored
+ *  g_proj output and the MLP product z.
  *  h0 : [b][d] fp32 or NULL; h_last : [b][d] fp32 output or NULL.
  *  probe : NULL or stage outputs (above).
  *  Errors: INVALID_ARG (shapes inconsistent with d/inner, null weights),
@@ -302,27 +303,16 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
  *  x, out : [b][d] in dtype act.  h : [b][d] fp32, read as h_{t-1} and
  *  overwritten with h_t.  Equivalent to mmf_layer_fwd with t = 1, h0 = h.
  *  Errors as mmf_layer_fwd (workspace from mmf_layer_workspace_size(w, b, 1)).
- *  Four implementations give the same bits: separate kernels per stage
- *  (quantisers and contractions: eight launches); contractions that quantise
- *  their own input rows in every workgroup, where a row fits (b <= 16, no
- *  probe, i/f/g sharing one gain or none; one row up to 8192 wide, where
- *  o_proj also forms the gated g_norm of h and g; 2 to 16 rows up to 2048
- *  wide, 12 for a stage with a gain; the other stages keep their
- *  quantisers: four launches at one row, six at the 1.3B shape and 16 rows
- *  without gains); four contraction kernels
- *  whose first b workgroups quantise the input rows and hand them to the
- *  others within the launch through device-scope stores and a counter (b <=
- *  16, no probe, equal i/f/g gains, d and inner multiples of 256, d <= 3072,
- *  inner <= 8192; launches of this kind on one stream are ordered, and each
- *  stream uses its own counters, 64 streams per process at most); and (b <= 16, no
- *  probe, equal i/f/g gains, d and inner multiples of 256, d <= 3072, inner
- *  <= 7136) one kernel run by the 32 workgroups of one XCD with barriers
- *  between the stages (see mmf_set_decode_kernel). Calls of the
- *  one-XCD kernel share device-wide barrier state: two of them must not run
- *  at the same time on one device (calls on one stream never do). The first
- *  call on a device checks the workgroup-to-XCD placement synchronously; a
- *  call made while the stream is being captured before that check has run
- *  takes the separate kernels.
+ *  Two implementations give the same bits: separate kernels per stage
+ *  (quantisers and contractions: eight launches), and contractions that
+ *  quantise their own input rows in every workgroup where a row fits (b <= 16,
+ *  i/f/g sharing one gain or none; one row up to 8192 wide, where o_proj also
+ *  forms the gated g_norm of h and g; 2 to 16 rows up to 2048 wide, 12 for a
+ *  stage with a gain; the other stages keep their quantisers: four launches
+ *  at one row, six at the 1.3B shape and 16 rows without gains). A probe does
+ *  not change which kernels run: the self-quantising contractions write the
+ *  codes and scales of their input rows (and the gated g_norm its row) from
+ *  their first workgroup.
  */
 mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype act,
                                  int64_t b, float *h, void *ws, size_t ws_bytes,
@@ -330,27 +320,13 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
 
 /*
  * mmf_set_decode_kernel -- which implementation mmf_layer_decode_step uses,
- * process-wide: 0 = the fastest implementation measured on MI355X (default:
- * the self-quantising contractions where they apply, else the separate
- * kernels; at the 1.3B shape in a HIP graph they take 21 / 33 us per layer
- * at batch 1 / 16, the separate kernels 29 / 33, the four fused kernels
- * 34 / 46 (a hand-off across XCDs within a launch costs about what a kernel
- * boundary does), and the one-XCD kernel 45 / 46, held to one XCD's share
- * of HBM bandwidth);
- * 1 = always the separate kernels; 2 = only the one-XCD kernel; 3 = only the
- * four fused kernels (2 and 3: UNSUPPORTED where they do not apply).
+ * process-wide: 0 = the fastest measured on MI355X (default: the
+ * self-quantising contractions where they apply, else the separate kernels;
+ * at the 1.3B shape in a HIP graph 21 / 33 us per layer at batch 1 / 16,
+ * against 29 / 33 for the separate kernels); 1 = always the separate kernels.
  * INVALID_ARG for other values.
  */
 mmf_status mmf_set_decode_kernel(int mode);
-
-/*
- * mmf_decode_expired_waits -- how many waits of the one-XCD decode kernel
- * (barriers) and of the fused decode kernels (rows handed over) gave up since
- * the library loaded, on the current device (each wait is bounded, about a
- * second; a non-zero count means a result was computed from incomplete data).
- * Synchronous; for diagnostics.
- */
-mmf_status mmf_decode_expired_waits(uint32_t *count);
 
 /*
  * Measurement support (not part of the computation). While enabled on a
@@ -379,6 +355,21 @@ typedef struct {
 
 mmf_status mmf_timing_enable(int on);
 mmf_status mmf_timing_collect(mmf_kernel_timing *out, int32_t capacity, int32_t *count);
+
+/*
+ * mmf_hbm_ceiling -- measured HBM roof (measurement support): streams `bytes`
+ * of device memory in the access pattern of the library's bandwidth-bound
+ * kernels (16-byte loads by consecutive lanes, four in flight per lane,
+ * 2048 workgroups of 256 threads).
+ *  mode 0 : read src only (the packed-weight stream of a GEMV); dst receives
+ *           one uint32 per workgroup (at least MMF_HBM_CEILING_SINK_BYTES).
+ *  mode 1 : copy src to dst (a read stream and a write stream, as the scan).
+ *  bytes % 16 == 0; src and dst 16-byte aligned and not overlapping.
+ *  Timed like every other launch while mmf_timing_enable is on ("stream_read",
+ *  "stream_copy"). Errors: INVALID_ARG.
+ */
+#define MMF_HBM_CEILING_SINK_BYTES 8192
+mmf_status mmf_hbm_ceiling(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

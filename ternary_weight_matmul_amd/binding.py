@@ -21,7 +21,7 @@ __all__ = [
     "layer_fwd", "layer_bwd",
     "layer_decode_step",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
-    "set_decode_kernel", "decode_expired_waits", "DECODE_KERNELS",
+    "set_decode_kernel", "DECODE_KERNELS", "hbm_ceiling",
 ]
 
 # Every entry point declared in include/mmf.h.
@@ -34,8 +34,8 @@ SYMBOLS = [
     "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd", "mmf_hgrn_scan_bwd",
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
     "mmf_layer_bwd_workspace_size", "mmf_layer_bwd",
-    "mmf_set_decode_kernel", "mmf_decode_expired_waits",
-    "mmf_timing_enable", "mmf_timing_collect",
+    "mmf_set_decode_kernel",
+    "mmf_timing_enable", "mmf_timing_collect", "mmf_hbm_ceiling",
 ]
 
 SCAN_MODES = {"auto": 0, "recurrent": 1, "chunk": 2}
@@ -115,9 +115,9 @@ def load():
     lib.mmf_layer_bwd.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, I64, P, P, ctypes.c_int,
                                   ctypes.POINTER(CLayerGrads), P, SZ, P]
     lib.mmf_set_decode_kernel.argtypes = [ctypes.c_int]
-    lib.mmf_decode_expired_waits.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     lib.mmf_timing_enable.argtypes = [ctypes.c_int]
     lib.mmf_timing_collect.argtypes = [ctypes.POINTER(CKernelTiming), I32, ctypes.POINTER(I32)]
+    lib.mmf_hbm_ceiling.argtypes = [ctypes.c_int, P, P, I64, P]
     for name in SYMBOLS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -132,19 +132,12 @@ def last_path() -> str:
     return load().mmf_last_path().decode()
 
 
-DECODE_KERNELS = {"auto": 0, "separate": 1, "xcd": 2, "fused": 3}
+DECODE_KERNELS = {"auto": 0, "separate": 1}
 
 
 def set_decode_kernel(mode: str = "auto"):
     """Implementation of layer_decode_step, process-wide (mmf_set_decode_kernel)."""
     _check(load().mmf_set_decode_kernel(DECODE_KERNELS[mode]))
-
-
-def decode_expired_waits() -> int:
-    """Barrier waits of the one-XCD decode kernel that gave up (synchronous diagnostic)."""
-    c = ctypes.c_uint32(0)
-    _check(load().mmf_decode_expired_waits(ctypes.byref(c)))
-    return c.value
 
 
 def timing_enable(on: bool = True):
@@ -160,6 +153,13 @@ def timing_collect() -> list:
     recs = (CKernelTiming * max(count.value, 1))()
     _check(lib.mmf_timing_collect(recs, count.value, ctypes.byref(count)))
     return [(r.kernel.decode(), r.m, r.n, r.k, r.ms) for r in recs[:count.value]]
+
+
+def hbm_ceiling(src, dst, mode: str = "read"):
+    """Measured HBM roof (mmf_hbm_ceiling): stream src (read) or copy it into dst (copy).
+    For "read", dst is a sink of at least 8192 bytes."""
+    n = src.numel() * src.element_size()
+    _check(load().mmf_hbm_ceiling(0 if mode == "read" else 1, _ptr(src), _ptr(dst), n, _stream()))
 
 
 def _check(status: int):
@@ -496,3 +496,4 @@ def layer_decode_step(params: LayerParams, x, h, probe: Optional[LayerProbe] = N
                                      _ptr(wsb), wsb.numel(), ctypes.byref(cp) if cp is not None else None,
                                      _stream()))
     return out
+

@@ -387,21 +387,21 @@ bool rmsnorm_bwd_supported(int k) { return k % 8 == 0 && nv_bucket(k) <= 8; }
 hipError_t launch_expand_ternary(const uint32_t *packed, int n, int k, uint16_t *out, hipStream_t st) {
     const int64_t words = (int64_t)n * (k / 16);
     if (words == 0) return hipSuccess;
-    expand_ternary_kernel<<<(unsigned)((words + 255) / 256), 256, 0, st>>>(packed, words, out);
+    launch_k(expand_ternary_kernel, (unsigned)((words + 255) / 256), 256, 0, st, packed, words, out);
     return hipGetLastError();
 }
 
 hipError_t launch_scaled_codes(const int8_t *q, const float *s, int64_t m, int k, uint16_t *out, hipStream_t st) {
     const int64_t n8 = m * (k / 8);
     if (n8 == 0) return hipSuccess;
-    scaled_codes_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(q, s, m, k, out);
+    launch_k(scaled_codes_kernel, (unsigned)((n8 + 255) / 256), 256, 0, st, q, s, m, k, out);
     return hipGetLastError();
 }
 
 hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *out, hipStream_t st) {
     const int64_t n4 = n / 4;
     if (n4 == 0) return hipSuccess;
-    to_bf16_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(x, n4, out);
+    launch_k(to_bf16_kernel, (unsigned)((n4 + 255) / 256), 256, 0, st, x, n4, out);
     return hipGetLastError();
 }
 
@@ -411,7 +411,7 @@ static void rms_bwd_t(const TX *x, const float *du_raw, const float *gain, const
     const int rows = rmsnorm_bwd_rows(m);
     const unsigned grid = (unsigned)((m + rows - 1) / rows);
     switch (nv_bucket(k)) {
-#define MMF_RB(NV) case NV: rmsnorm_bwd_kernel<TX, TD, NV><<<grid, 256, 0, st>>>(x, du_raw, gain, mu, eps, m, k, rows, dx, gpart); break;
+#define MMF_RB(NV) case NV: launch_k(rmsnorm_bwd_kernel<TX, TD, NV>, grid, 256, 0, st, x, du_raw, gain, mu, eps, m, k, rows, dx, gpart); break;
         MMF_RB(1) MMF_RB(2) MMF_RB(4) MMF_RB(8)
 #undef MMF_RB
     }
@@ -435,33 +435,33 @@ static unsigned blocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 hipError_t launch_gates_keep(const float *ih, const float *fh, const float *gh, int64_t n, float *f, float *xt, void *g,
                              ActType gt, hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    if (gt == ACT_F32) gates_keep_kernel<float><<<blocks(n / 4), 256, 0, st>>>(ih, fh, gh, n / 4, f, xt, static_cast<float *>(g));
-    else gates_keep_kernel<uint16_t><<<blocks(n / 4), 256, 0, st>>>(ih, fh, gh, n / 4, f, xt, static_cast<uint16_t *>(g));
+    if (gt == ACT_F32) launch_k(gates_keep_kernel<float>, blocks(n / 4), 256, 0, st, ih, fh, gh, n / 4, f, xt, static_cast<float *>(g));
+    else launch_k(gates_keep_kernel<uint16_t>, blocks(n / 4), 256, 0, st, ih, fh, gh, n / 4, f, xt, static_cast<uint16_t *>(g));
     return hipGetLastError();
 }
 
 hipError_t launch_glu_keep(const float *ab, int64_t m, int inner, void *z, ActType zt, hipStream_t st) {
     if (m <= 0) return hipSuccess;
-    if (zt == ACT_F32) glu_keep_kernel<float><<<blocks(m * inner), 256, 0, st>>>(ab, m, inner, static_cast<float *>(z));
-    else glu_keep_kernel<uint16_t><<<blocks(m * inner), 256, 0, st>>>(ab, m, inner, static_cast<uint16_t *>(z));
+    if (zt == ACT_F32) launch_k(glu_keep_kernel<float>, blocks(m * inner), 256, 0, st, ab, m, inner, static_cast<float *>(z));
+    else launch_k(glu_keep_kernel<uint16_t>, blocks(m * inner), 256, 0, st, ab, m, inner, static_cast<uint16_t *>(z));
     return hipGetLastError();
 }
 
 hipError_t launch_glu_bwd(const float *dz, const float *ab, int64_t m, int inner, float *dab, hipStream_t st) {
-    if (m > 0) glu_bwd_kernel<<<blocks(m * inner), 256, 0, st>>>(dz, ab, m, inner, dab);
+    if (m > 0) launch_k(glu_bwd_kernel, blocks(m * inner), 256, 0, st, dz, ab, m, inner, dab);
     return hipGetLastError();
 }
 
 hipError_t launch_gates_bwd(float *dxt, float *df, const float *ih, const float *f, int64_t n, hipStream_t st) {
-    if (n > 0) gates_bwd_kernel<<<blocks(n), 256, 0, st>>>(dxt, df, ih, f, n);
+    if (n > 0) launch_k(gates_bwd_kernel, blocks(n), 256, 0, st, dxt, df, ih, f, n);
     return hipGetLastError();
 }
 
 hipError_t launch_sum(const void *a, ActType at, const float *b, const float *c, const float *d, int64_t n, float *out,
                       hipStream_t st) {
     if (n <= 0) return hipSuccess;
-    if (at == ACT_F32) sum_kernel<float><<<blocks(n), 256, 0, st>>>(static_cast<const float *>(a), b, c, d, n, out);
-    else sum_kernel<uint16_t><<<blocks(n), 256, 0, st>>>(static_cast<const uint16_t *>(a), b, c, d, n, out);
+    if (at == ACT_F32) launch_k(sum_kernel<float>, blocks(n), 256, 0, st, static_cast<const float *>(a), b, c, d, n, out);
+    else launch_k(sum_kernel<uint16_t>, blocks(n), 256, 0, st, static_cast<const uint16_t *>(a), b, c, d, n, out);
     return hipGetLastError();
 }
 
@@ -471,7 +471,7 @@ static void gnorm_bwd_t(const float *h, const TG *g, const float *du, const floa
     const int rows = rmsnorm_bwd_rows(m);
     const unsigned grid = (unsigned)((m + rows - 1) / rows);
     switch (nv_bucket(d)) {
-#define MMF_GB(NV) case NV: gnorm_bwd_kernel<TG, NV><<<grid, 256, 0, st>>>(h, g, du, w, eps, m, d, rows, dh, dg, wpart); break;
+#define MMF_GB(NV) case NV: launch_k(gnorm_bwd_kernel<TG, NV>, grid, 256, 0, st, h, g, du, w, eps, m, d, rows, dh, dg, wpart); break;
         MMF_GB(1) MMF_GB(2) MMF_GB(4) MMF_GB(8)
 #undef MMF_GB
     }
@@ -486,7 +486,7 @@ hipError_t launch_gnorm_bwd(const float *h, const void *g, ActType gt, const flo
 }
 
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t st) {
-    if (n > 0) zero_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+    if (n > 0) launch_k(zero_f32_kernel, (unsigned)((n + 255) / 256), 256, 0, st, p, n);
     return hipGetLastError();
 }
 
@@ -494,8 +494,8 @@ int gain_reduce_splits(int nblk) { return nblk < kGainSplits ? (nblk > 0 ? nblk 
 
 hipError_t launch_gain_reduce(const float *gpart, int nblk, int k, float *part2, float *dgain, hipStream_t st) {
     const int splits = gain_reduce_splits(nblk);
-    gain_reduce_kernel<<<dim3((unsigned)((k + 63) / 64), (unsigned)splits), 256, 0, st>>>(gpart, nblk, k, part2);
-    gain_final_kernel<<<(unsigned)((k + 255) / 256), 256, 0, st>>>(part2, splits, k, dgain);
+    launch_k(gain_reduce_kernel, dim3((unsigned)((k + 63) / 64), (unsigned)splits), 256, 0, st, gpart, nblk, k, part2);
+    launch_k(gain_final_kernel, (unsigned)((k + 255) / 256), 256, 0, st, part2, splits, k, dgain);
     return hipGetLastError();
 }
 

@@ -933,10 +933,18 @@ __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, c
         for (int w = 0; w < nw; ++w) sh += slots[w];
         return rms_factor(sh, K, eps);
     };
+    const bool probe0 = blockIdx.x == 0;  // workgroup 0 writes the optional stage outputs
     if constexpr (GN) {
         const float rh = block_rms(red_h);
 #pragma unroll
         for (int j = 0; j < MAXCH; ++j) gated_norm4(xv[j], gv[j], wv[j], rh);
+        if (probe0 && src.u_out) {
+#pragma unroll
+            for (int j = 0; j < MAXCH; ++j) {
+                const int c = tid + j * T;
+                if (c < nch) *reinterpret_cast<float4 *>(src.u_out + 4 * c) = make_float4(xv[j][0], xv[j][1], xv[j][2], xv[j][3]);
+            }
+        }
     }
     if constexpr (GAIN) {
         const float r1 = block_rms(red_d);
@@ -973,12 +981,18 @@ __global__ __launch_bounds__(1024) void tgemv_row_kernel(const ContractArgs p, c
     const float r = GAIN ? 1.0f : rms_factor(ss, K, eps);
     const float sc = quant_scale(GAIN ? mx : __fmul_rn(mx, r));
     auto qv = [&](float v) { return quant_code(GAIN ? v : __fmul_rn(v, r), sc); };
-    // 4. the codes to LDS
+    // 4. the codes to LDS (and, from workgroup 0, to the optional outputs)
+    uint32_t *codes_g = probe0 ? reinterpret_cast<uint32_t *>(src.codes_out) : nullptr;
 #pragma unroll
     for (int j = 0; j < MAXCH; ++j) {
         const int c = tid + j * T;
-        if (c < nch) codes[c] = pack_codes4(qv(xv[j][0]), qv(xv[j][1]), qv(xv[j][2]), qv(xv[j][3]));
+        if (c < nch) {
+            const uint32_t v = pack_codes4(qv(xv[j][0]), qv(xv[j][1]), qv(xv[j][2]), qv(xv[j][3]));
+            codes[c] = v;
+            if (codes_g) codes_g[c] = v;
+        }
     }
+    if (probe0 && src.scale_out && tid == 0) *src.scale_out = sc;
     __syncthreads();
     // 5. the contraction
     i32x4 acc[CB][NG], accq = i32x4{};
@@ -1051,7 +1065,7 @@ static void run_gemm(const ContractArgs &a, hipStream_t st) {
     using S = TileShape<NG, JN, SH>;
     const int64_t tiles_m = (a.m + kBM - 1) / kBM;
     const int tiles_n = (a.nc + S::BNC - 1) / S::BNC;
-    tgemm_kernel<NG, JN, SH, EPI><<<(unsigned)(tiles_m * tiles_n), 256, 0, st>>>(a, tiles_n);
+    launch_k(tgemm_kernel<NG, JN, SH, EPI>, (unsigned)(tiles_m * tiles_n), 256, 0, st, a, tiles_n);
 }
 
 template <int NG, bool SH, int EPI, int WPL, typename RT, int CB>
@@ -1074,17 +1088,17 @@ static void run_gemv_cb(const ContractArgs &a, hipStream_t st) {
     if constexpr (MB * CB <= 2) {
         if (two) {
             switch (ept) {
-                case 1: tgemv_kernel<NG, SH, EPI, WPL, RT, 1, 2, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-                default: tgemv_kernel<NG, SH, EPI, WPL, RT, 2, 2, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+                case 1: launch_k(tgemv_kernel<NG, SH, EPI, WPL, RT, 1, 2, CB>, grid, waves * 64, lds, st, a, nslices); break;
+                default: launch_k(tgemv_kernel<NG, SH, EPI, WPL, RT, 2, 2, CB>, grid, waves * 64, lds, st, a, nslices); break;
             }
             return;
         }
     }
     switch (ept) {
-        case 1: tgemv_kernel<NG, SH, EPI, WPL, RT, 1, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        case 2: tgemv_kernel<NG, SH, EPI, WPL, RT, 2, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        case 3: tgemv_kernel<NG, SH, EPI, WPL, RT, 3, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
-        default: tgemv_kernel<NG, SH, EPI, WPL, RT, 4, 1, CB><<<grid, waves * 64, lds, st>>>(a, nslices); break;
+        case 1: launch_k(tgemv_kernel<NG, SH, EPI, WPL, RT, 1, 1, CB>, grid, waves * 64, lds, st, a, nslices); break;
+        case 2: launch_k(tgemv_kernel<NG, SH, EPI, WPL, RT, 2, 1, CB>, grid, waves * 64, lds, st, a, nslices); break;
+        case 3: launch_k(tgemv_kernel<NG, SH, EPI, WPL, RT, 3, 1, CB>, grid, waves * 64, lds, st, a, nslices); break;
+        default: launch_k(tgemv_kernel<NG, SH, EPI, WPL, RT, 4, 1, CB>, grid, waves * 64, lds, st, a, nslices); break;
     }
 }
 
@@ -1094,7 +1108,7 @@ static void run_gemm_dma(const ContractArgs &a, hipStream_t st) {
     static_assert(S::LOADS == 5 || S::LOADS == 6 || S::LOADS == 7, "vmcnt_wait covers 5..7 loads per step");
     const int64_t tiles_m = (a.m + kBM - 1) / kBM;
     const int tiles_n = (a.nc + S::BNC - 1) / S::BNC;
-    tgemm_dma_kernel<NG, JN, EPI><<<(unsigned)(tiles_m * tiles_n), 256, 0, st>>>(a, tiles_n);
+    launch_k(tgemm_dma_kernel<NG, JN, EPI>, (unsigned)(tiles_m * tiles_n), 256, 0, st, a, tiles_n);
 }
 
 // Channel blocks per workgroup for one row block: the most (1, 2 or 4, with
@@ -1243,14 +1257,21 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
             mx = wave_max(mx);
             const float sc = quant_scale(GAIN ? mx : __fmul_rn(mx, rr));
             auto qv = [&](float v) { return quant_code(GAIN ? v : __fmul_rn(v, rr), sc); };
+            uint32_t *codes_g = blockIdx.x == 0 && src.codes_out
+                                    ? reinterpret_cast<uint32_t *>(src.codes_out + (int64_t)r * K) : nullptr;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = lane + 64 * j;
-                if (c < nch)
-                    *reinterpret_cast<uint32_t *>(codes + r * stride + 4 * c) =
-                        pack_codes4(qv(xv[i][j][0]), qv(xv[i][j][1]), qv(xv[i][j][2]), qv(xv[i][j][3]));
+                if (c < nch) {
+                    const uint32_t v = pack_codes4(qv(xv[i][j][0]), qv(xv[i][j][1]), qv(xv[i][j][2]), qv(xv[i][j][3]));
+                    *reinterpret_cast<uint32_t *>(codes + r * stride + 4 * c) = v;
+                    if (codes_g) codes_g[c] = v;
+                }
             }
-            if (lane == 0) srow[r] = sc;
+            if (lane == 0) {
+                srow[r] = sc;
+                if (blockIdx.x == 0 && src.scale_out) src.scale_out[r] = sc;
+            }
         }
     }
     __syncthreads();
@@ -1338,7 +1359,7 @@ static hipError_t launch_rows(const ContractArgs &a, const RowSrc &src, float ep
                               size_t lds, hipStream_t st) {
     const hipError_t e = raise_lds_limit<KERNEL>();
     if (e != hipSuccess) return e;
-    KERNEL<<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
+    launch_k(KERNEL, grid, waves * 64, lds, st, a, src, eps, nslices);
     return hipSuccess;
 }
 
@@ -1351,9 +1372,9 @@ static hipError_t run_row_cb(const ContractArgs &a, const RowSrc &src, float eps
         const int waves = nslices < 16 ? nslices : 16;
         const size_t lds = (size_t)waves * CB * NG * 16 * sizeof(int32_t) + (size_t)a.k;
         if (nslices <= waves)
-            tgemv_row_kernel<NG, EPI, XT, RT, CB, 1, IN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
+            launch_k(tgemv_row_kernel<NG, EPI, XT, RT, CB, 1, IN>, grid, waves * 64, lds, st, a, src, eps, nslices);
         else
-            tgemv_row_kernel<NG, EPI, XT, RT, CB, 2, IN><<<grid, waves * 64, lds, st>>>(a, src, eps, nslices);
+            launch_k(tgemv_row_kernel<NG, EPI, XT, RT, CB, 2, IN>, grid, waves * 64, lds, st, a, src, eps, nslices);
         return hipSuccess;
     }
     // 2 to 16 rows of at most 2048, with or without a gain: a wave per row (8
@@ -1414,10 +1435,10 @@ bool contract_row_supported(int64_t m, int k, EpiKind epi, bool gain) {
 bool contract_row_gnorm_supported(int64_t m, int k) { return m == 1 && k % 16 == 0 && k <= 8192; }
 
 hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *xp, ActType xt, const float *gain,
-                               float eps, hipStream_t st, std::string *path) {
+                               float eps, int8_t *codes_out, float *scale_out, hipStream_t st, std::string *path) {
     if (!contract_row_supported(a.m, a.k, epi, gain != nullptr)) return hipErrorInvalidValue;
     const bool xb = xt == ACT_BF16, rb = a.res_type == ACT_BF16;
-    const RowSrc x{xp, nullptr, nullptr, gain};
+    const RowSrc x{xp, nullptr, nullptr, gain, codes_out, scale_out, nullptr};
     hipError_t e = hipSuccess;
     switch (epi) {
         case EPI_GATES_STEP:
@@ -1455,10 +1476,10 @@ static hipError_t run_row_gnorm(const ContractArgs &a, const RowSrc &src, bool g
 }
 
 hipError_t launch_contract_row_gnorm(const ContractArgs &a, const float *h, const void *g, ActType gt,
-                                     const float *gnw, const float *ogain, float eps, hipStream_t st,
-                                     std::string *path) {
+                                     const float *gnw, const float *ogain, float eps, int8_t *codes_out,
+                                     float *scale_out, float *u_out, hipStream_t st, std::string *path) {
     if (!contract_row_gnorm_supported(a.m, a.k)) return hipErrorInvalidValue;
-    const RowSrc src{h, g, gnw, ogain};
+    const RowSrc src{h, g, gnw, ogain, codes_out, scale_out, u_out};
     const bool gb = gt == ACT_BF16;
     const hipError_t e = ogain ? run_row_gnorm<ROW_GNORM_GAIN>(a, src, gb, eps, st)
                                : run_row_gnorm<ROW_GNORM>(a, src, gb, eps, st);

@@ -68,13 +68,13 @@ hipError_t launch_embed(const int32_t *ids, int64_t count, const void *table, in
     if (count <= 0) return hipSuccess;
     const int64_t pieces = row_bytes / 16;
     const dim3 grid((unsigned)count, (unsigned)((pieces + 255) / 256));
-    embed_kernel<<<grid, 256, 0, st>>>(ids, static_cast<const uint4 *>(table), vocab, pieces, static_cast<uint4 *>(out));
+    launch_k(embed_kernel, grid, 256, 0, st, ids, static_cast<const uint4 *>(table), vocab, pieces, static_cast<uint4 *>(out));
     return hipGetLastError();
 }
 
 hipError_t launch_argmax_rows(const int32_t *acc, int64_t m, int64_t n, int32_t *tokens, hipStream_t st) {
     if (m <= 0) return hipSuccess;
-    argmax_rows_kernel<<<(unsigned)m, 256, 0, st>>>(acc, n, tokens);
+    launch_k(argmax_rows_kernel, (unsigned)m, 256, 0, st, acc, n, tokens);
     return hipGetLastError();
 }
 

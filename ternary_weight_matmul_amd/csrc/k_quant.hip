@@ -196,7 +196,7 @@ static void norm_quant_dispatch(const T *x, int64_t m, int k, const float *gain,
     const int nvb = block_bucket(k);
     if (m < kFewRows && nvb <= 8) {
         switch (nvb) {
-#define MMF_NQB(NV) case NV: norm_quant_row_kernel<T, NV><<<(unsigned)m, 256, 0, st>>>(x, m, k, gain, eps, q, s, sumq); break;
+#define MMF_NQB(NV) case NV: launch_k(norm_quant_row_kernel<T, NV>, (unsigned)m, 256, 0, st, x, m, k, gain, eps, q, s, sumq); break;
             MMF_NQB(1) MMF_NQB(2) MMF_NQB(4) MMF_NQB(8)
 #undef MMF_NQB
         }
@@ -206,12 +206,12 @@ static void norm_quant_dispatch(const T *x, int64_t m, int k, const float *gain,
     const dim3 grid((unsigned)((m + 3) / 4)), block(256);
     const int nv = chunk_bucket(k, Chunk<T>::E);
     if (k % Chunk<T>::E != 0 || nv > kMaxCachedChunks) {
-        norm_quant_long_kernel<T><<<grid, block, 0, st>>>(x, m, k, gain, eps, q, s, sumq);
+        launch_k(norm_quant_long_kernel<T>, grid, block, 0, st, x, m, k, gain, eps, q, s, sumq);
         if (path) *path += std::string("norm_quant_long<") + tn + ">;";
         return;
     }
     switch (nv) {
-#define MMF_NQ(NV) case NV: norm_quant_kernel<T, NV><<<grid, block, 0, st>>>(x, m, k, gain, eps, q, s, sumq); break;
+#define MMF_NQ(NV) case NV: launch_k(norm_quant_kernel<T, NV>, grid, block, 0, st, x, m, k, gain, eps, q, s, sumq); break;
         MMF_NQ(1) MMF_NQ(2) MMF_NQ(4) MMF_NQ(8) MMF_NQ(16) MMF_NQ(32)
 #undef MMF_NQ
     }
@@ -338,7 +338,7 @@ static hipError_t gnorm_dispatch(const float *h, const TG *g, int64_t m, int d, 
     const int nvb = block_bucket(d);
     if (m < kFewRows && nvb <= 8) {
         switch (nvb) {
-#define MMF_GQB(NV) case NV: gnorm_quant_row_kernel<TG, NV><<<(unsigned)m, 256, 0, stream>>>(h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
+#define MMF_GQB(NV) case NV: launch_k(gnorm_quant_row_kernel<TG, NV>, (unsigned)m, 256, 0, stream, h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
             MMF_GQB(1) MMF_GQB(2) MMF_GQB(4) MMF_GQB(8)
 #undef MMF_GQB
         }
@@ -348,7 +348,7 @@ static hipError_t gnorm_dispatch(const float *h, const TG *g, int64_t m, int d, 
     const dim3 grid((unsigned)((m + 3) / 4)), block(256);
     const int nv = chunk_bucket(d);
     switch (nv) {
-#define MMF_GQ(NV) case NV: gnorm_quant_kernel<TG, NV><<<grid, block, 0, stream>>>(h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
+#define MMF_GQ(NV) case NV: launch_k(gnorm_quant_kernel<TG, NV>, grid, block, 0, stream, h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
         MMF_GQ(1) MMF_GQ(2) MMF_GQ(4) MMF_GQ(8) MMF_GQ(16) MMF_GQ(32)
 #undef MMF_GQ
         default: return hipErrorInvalidValue;  // d > 8192 is rejected by the ABI layer
@@ -435,9 +435,9 @@ hipError_t launch_pack(const float *w, int n, int k, uint32_t *packed, float *mu
     per = (per + 255) / 256 * 256;
     const int nparts = (int)((count + per - 1) / per);
     double *partial = static_cast<double *>(ws);
-    abs_sum_partial_kernel<<<nparts, 256, 0, stream>>>(w, count, per, partial);
+    launch_k(abs_sum_partial_kernel, nparts, 256, 0, stream, w, count, per, partial);
     const int64_t words = (int64_t)n * (k >> 4);
-    pack_kernel<<<(unsigned)((words + 255) / 256), 256, 0, stream>>>(w, n, k, partial, nparts, packed, mu);
+    launch_k(pack_kernel, (unsigned)((words + 255) / 256), 256, 0, stream, w, n, k, partial, nparts, packed, mu);
     if (path) *path += "abs_sum_partial;pack;";
     return hipGetLastError();
 }

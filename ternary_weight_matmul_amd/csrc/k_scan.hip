@@ -397,7 +397,7 @@ hipError_t launch_scan_bwd(const float *f, const float *h, const float *h0, cons
     if (b <= 0) return hipSuccess;
     if (t == 0) {
         // h_last is h0: its derivative passes straight through
-        if (dh0) copy_state_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(dh_last, dh0, b * d);
+        if (dh0) launch_k(copy_state_kernel, (unsigned)((b * d + 255) / 256), 256, 0, stream, dh_last, dh0, b * d);
         if (path) *path += "scan_bwd_empty;";
         return hipGetLastError();
     }
@@ -410,17 +410,17 @@ hipError_t launch_scan_bwd(const float *f, const float *h, const float *h0, cons
         // ahead once the groups fill the GPU (71 % of 8 TB/s at 16 x 2048 x 2048,
         // 63 % with 8 steps and 3 ahead)
         if (many && nt)
-            scan_bwd_tiled_kernel<4, 4, 6, true><<<grid, 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+            launch_k(scan_bwd_tiled_kernel<4, 4, 6, true>, grid, 256, 0, stream, f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
         else if (many)
-            scan_bwd_tiled_kernel<4, 4, 6, false><<<grid, 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+            launch_k(scan_bwd_tiled_kernel<4, 4, 6, false>, grid, 256, 0, stream, f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
         else if (nt)
-            scan_bwd_tiled_kernel<16, 8, 1, true><<<grid, 1024, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+            launch_k(scan_bwd_tiled_kernel<16, 8, 1, true>, grid, 1024, 0, stream, f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
         else
-            scan_bwd_tiled_kernel<16, 8, 1, false><<<grid, 1024, 0, stream>>>(f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
+            launch_k(scan_bwd_tiled_kernel<16, 8, 1, false>, grid, 1024, 0, stream, f, h, h0, dh, dh_last, dx, df, dh0, t, d, groups);
         if (path) *path += std::string("scan_bwd_tiled<") + (many ? "4w" : "16w") + (nt ? ",nt" : "") + ">;";
         return hipGetLastError();
     }
-    scan_bwd_recurrent_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(f, h, h0, dh, dh_last, dx, df,
+    launch_k(scan_bwd_recurrent_kernel, (unsigned)((b * d + 255) / 256), 256, 0, stream, f, h, h0, dh, dh_last, dx, df,
                                                                                    dh0, b, t, d);
     if (path) *path += "scan_bwd_recurrent;";
     return hipGetLastError();
@@ -430,7 +430,7 @@ hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h
                        int64_t t, int64_t d, int chunks, void *ws, hipStream_t stream, std::string *path) {
     if (b <= 0) return hipSuccess;
     if (t == 0) {
-        if (h_last) copy_state_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(h0, h_last, b * d);
+        if (h_last) launch_k(copy_state_kernel, (unsigned)((b * d + 255) / 256), 256, 0, stream, h0, h_last, b * d);
         if (path) *path += "scan_empty;";
         return hipGetLastError();
     }
@@ -443,15 +443,15 @@ hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h
         const unsigned grid = (unsigned)(b * groups);
         const bool nt = 12 * b * t * d > kStreamBytes;
         const bool many = b * groups >= kTiledManyGroups;
-        if (many && nt) scan_tiled_kernel<4, 8, 2, true><<<grid, 256, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
-        else if (many) scan_tiled_kernel<4, 8, 2, false><<<grid, 256, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
-        else if (nt) scan_tiled_kernel<16, 8, 1, true><<<grid, 1024, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
-        else scan_tiled_kernel<16, 8, 1, false><<<grid, 1024, 0, stream>>>(x, f, h0, h, h_last, t, d, groups);
+        if (many && nt) launch_k(scan_tiled_kernel<4, 8, 2, true>, grid, 256, 0, stream, x, f, h0, h, h_last, t, d, groups);
+        else if (many) launch_k(scan_tiled_kernel<4, 8, 2, false>, grid, 256, 0, stream, x, f, h0, h, h_last, t, d, groups);
+        else if (nt) launch_k(scan_tiled_kernel<16, 8, 1, true>, grid, 1024, 0, stream, x, f, h0, h, h_last, t, d, groups);
+        else launch_k(scan_tiled_kernel<16, 8, 1, false>, grid, 1024, 0, stream, x, f, h0, h, h_last, t, d, groups);
         if (path) *path += std::string("scan_tiled<") + (many ? "4w" : "16w") + (nt ? ",nt" : "") + ">;";
         return hipGetLastError();
     }
     if (chunks <= 1) {
-        scan_recurrent_kernel<<<(unsigned)((b * d + 255) / 256), 256, 0, stream>>>(x, f, h0, h, h_last, b, t, d);
+        launch_k(scan_recurrent_kernel, (unsigned)((b * d + 255) / 256), 256, 0, stream, x, f, h0, h, h_last, b, t, d);
         if (path) *path += "scan_recurrent;";
         return hipGetLastError();
     }
@@ -460,10 +460,10 @@ hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h
     float2 *agg = static_cast<float2 *>(ws);
     if (c_eff > 1) {
         const int64_t n1 = b * (int64_t)(c_eff - 1) * d;
-        scan_chunk_reduce_kernel<<<(unsigned)((n1 + 255) / 256), 256, 0, stream>>>(x, f, b, t, d, c_eff, clen, agg);
+        launch_k(scan_chunk_reduce_kernel, (unsigned)((n1 + 255) / 256), 256, 0, stream, x, f, b, t, d, c_eff, clen, agg);
     }
     const int64_t n2 = b * (int64_t)c_eff * d;
-    scan_chunk_apply_kernel<<<(unsigned)((n2 + 255) / 256), 256, 0, stream>>>(x, f, h0, h, h_last, b, t, d, c_eff,
+    launch_k(scan_chunk_apply_kernel, (unsigned)((n2 + 255) / 256), 256, 0, stream, x, f, h0, h, h_last, b, t, d, c_eff,
                                                                               clen, agg);
     if (path) *path += "scan_chunk(" + std::to_string(c_eff) + "x" + std::to_string(clen) + ");";
     return hipGetLastError();

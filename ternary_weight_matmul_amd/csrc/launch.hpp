@@ -10,6 +10,12 @@ namespace mmf {
 
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
 
+// Every kernel of the library is launched through here (one launch point).
+template <typename... KP, typename... A>
+inline void launch_k(void (*kernel)(KP...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A... args) {
+    kernel<<<grid, block, lds, st>>>(args...);
+}
+
 // Row RMSNorm + absmax int8 quantiser over m rows of k elements.
 hipError_t launch_norm_quant(const void *x, ActType xt, int64_t m, int k, const float *gain, float eps,
                              int8_t *q, float *s, int32_t *sumq, hipStream_t stream, std::string *path);
@@ -54,67 +60,35 @@ struct ContractArgs {
 // The input rows of a contraction that quantises them itself: x [m][k] in the
 // activation type, or (gated g_norm) y = ((h r_h) w) silu(g) formed from h
 // [m][k] fp32, g [m][k] in the activation type and the optional gain w [k].
+// Optional stage outputs, written by workgroup 0 only: the rows' int8 codes
+// [m][k] and scales [m], and (gated g_norm) the gated row u [k] before
+// o_proj's own gain.
 struct RowSrc {
     const void *x;       // x, or h
     const void *g;       // g (gated g_norm only)
     const float *gnw;    // g_norm's gain or NULL (gated g_norm only)
     const float *gain;   // the FusedBitLinear gain of x, or o_proj's after the gated g_norm; or NULL
+    int8_t *codes_out;   // or NULL
+    float *scale_out;    // or NULL
+    float *u_out;        // or NULL
 };
-
-// One decode step of a block as a single kernel on one XCD (k_decode.hip).
-struct DecodeStepArgs {
-    const void *x;           // [b][d] activation dtype
-    void *out;               // [b][d] activation dtype
-    float *h;                // [b][d] recurrent state, updated in place
-    const uint32_t *w_ifg[3];
-    const float *mu_ifg[3];
-    const uint32_t *w_o, *w_gate, *w_down;
-    const float *mu_o, *mu_gate, *mu_down;
-    const float *gain_x, *gain_o, *gain_gate, *gain_down, *g_norm_w;
-    int b, d, inner;
-    float eps;
-    ActType act;
-    int8_t *codes;           // [b][max(d, inner)]
-    float *s;                // [b]
-    int32_t *sumq;           // [b]
-    void *g;                 // [b][d] activation dtype
-    float *x1;               // [b][d]
-    void *z;                 // [b][inner] activation dtype
-};
-bool decode_step_supported(int64_t b, int d, int inner);
-// Enqueues the one-XCD decode step when the shape and the device allow it;
-// *launched reports whether it did (otherwise nothing was enqueued).
-hipError_t launch_decode_step(const DecodeStepArgs &a, hipStream_t stream, std::string *path, bool *launched);
-// Barrier waits of the one-XCD decode step that ran out of patience (synchronous).
-hipError_t decode_step_expired_spins(unsigned *count);
-
-// Decode contraction with the quantiser of its b <= 16 input rows in the same
-// launch (k_gemv_q.hip): QK_ROW: RMSNorm + absmax int8 of x [b][k] (type xt)
-// with gain; QK_GNORM: g_norm gate of h (fp32) and g (type gt) with g_norm
-// weight gnw, then the quantiser with gain. The rows' codes, scales and sums
-// pass through codes [b][k], s [b], sumq [b]; c's A / s / sumq are not used.
-enum QuantKind { QK_ROW = 0, QK_GNORM = 1 };
-bool quant_contract_supported(int64_t b, int nc, int k, EpiKind epi, int qk, ActType xt, ActType gt);
-hipError_t launch_quant_contract(const ContractArgs &c, EpiKind epi, int qk, const void *x, ActType xt,
-                                 const void *g, ActType gt, const float *gain, const float *gnw, float eps,
-                                 int8_t *codes, float *s, int32_t *sumq, hipStream_t stream, std::string *path);
-// Waits of those launches that gave up (synchronous).
-hipError_t quant_contract_expired_waits(unsigned *count);
 
 // Prefill-shaped contraction (int8 MFMA tiles) and decode-shaped one (m <= 64).
 hipError_t launch_contract(const ContractArgs &a, EpiKind epi, int ng, bool shared_a,
                            hipStream_t stream, std::string *path);
 
-// Decode at one row without a gain: the contraction quantises its input row x
-// (type xt) itself in every workgroup (k <= 8192); a.A, a.s, a.sumq unused.
+// Decode at up to 16 rows: the contraction quantises its input rows x (type
+// xt) itself in every workgroup; a.A, a.s, a.sumq unused. codes_out [m][k] and
+// scale_out [m] (each optional) receive the rows' codes and scales.
 bool contract_row_supported(int64_t m, int k, EpiKind epi, bool gain);
 hipError_t launch_contract_row(const ContractArgs &a, EpiKind epi, const void *x, ActType xt, const float *gain,
-                               float eps, hipStream_t st, std::string *path);
-// o_proj over the gated g_norm of (h, g), quantised in each workgroup (EPI_RESID only).
+                               float eps, int8_t *codes_out, float *scale_out, hipStream_t st, std::string *path);
+// o_proj over the gated g_norm of (h, g), quantised in each workgroup (EPI_RESID
+// only); optional outputs: the codes, the scale and the gated row u.
 bool contract_row_gnorm_supported(int64_t m, int k);
 hipError_t launch_contract_row_gnorm(const ContractArgs &a, const float *h, const void *g, ActType gt,
-                                     const float *gnw, const float *ogain, float eps, hipStream_t st,
-                                     std::string *path);
+                                     const float *gnw, const float *ogain, float eps, int8_t *codes_out,
+                                     float *scale_out, float *u_out, hipStream_t st, std::string *path);
 
 // Whether the contraction over m rows forms each row's sum of codes itself
 // (the decode GEMV does); otherwise it reads the quantiser's sumq.
@@ -171,6 +145,13 @@ hipError_t launch_gnorm_bwd(const float *h, const void *g, ActType gt, const flo
                             int64_t m, int d, float *dh, float *dg, float *wpart, hipStream_t st);
 hipError_t gemm_bf16_f32(const uint16_t *a, bool trans_a, const uint16_t *b, int64_t rows, int64_t cols, int64_t inner,
                          float *c, hipStream_t st, std::string *err);
+
+// Measured HBM ceilings (k_ceiling.hip): a streaming read of `bytes` (a
+// multiple of 16; one word per workgroup to sink, ceiling_blocks() words) and
+// a streaming copy.
+int ceiling_blocks();
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t st);
+hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t st);
 
 // Generation (k_generate.hip): embedding rows (16-byte pieces of a row of
 // row_bytes; zero rows for ids outside [0, vocab)), and per row of an int32

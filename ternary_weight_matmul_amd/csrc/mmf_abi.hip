@@ -68,7 +68,8 @@ hipEvent_t timing_event() {
     return g_events[g_events_used++];
 }
 
-// The events bracket the launch on its stream.
+// The events bracket the launch on its stream: an interval runs from the point
+// the stream reaches the first record to the point it reaches the second.
 template <class F>
 hipError_t timed(const std::string &kernel, int64_t m, int n, int k, hipStream_t st, F &&launch) {
     if (!g_timing) return launch();
@@ -167,7 +168,7 @@ struct LayerWs {
     float *s_x[3];
     int32_t *sq_x[3];
     float *f, *xt, *h, *x1;
-    void *g, *z;  // stored in the activation dtype (room for fp32)
+    float *g, *z;  // fp32, whatever the activation dtype
     int8_t *codes_b;
     float *s_b;
     int32_t *sq_b;
@@ -195,7 +196,7 @@ size_t layer_plan(Carver &c, const mmf_layer_weights *w, int64_t b, int64_t t, i
     }
     L.f = c.take<float>(m * d);
     L.xt = c.take<float>(m * d);
-    L.g = c.take<float>(m * d);  // fp32-sized; holds activation-dtype values
+    L.g = c.take<float>(m * d);
     L.h = c.take<float>(m * d);
     L.x1 = c.take<float>(m * d);
     L.z = c.take<float>(m * inner);
@@ -239,8 +240,8 @@ hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_
     hipError_t e;
     int8_t *cu = pick(pr ? pr->codes_u : nullptr, L.codes_b);
     float *su = pick(pr ? pr->scale_u : nullptr, L.s_b);
-    e = t_gnorm_quant(h, g, act(actt), m, d, w->g_norm_w, w->o.norm_w, eps, cu, su, L.sq_b, pr ? pr->u : nullptr, st,
-                      path);
+    e = t_gnorm_quant(h, static_cast<const float *>(g), ACT_F32, m, d, w->g_norm_w, w->o.norm_w, eps, cu, su, L.sq_b,
+                      pr ? pr->u : nullptr, st, path);
     if (e != hipSuccess) return e;
 
     float *x1 = pick(pr ? pr->x1 : nullptr, L.x1);
@@ -262,13 +263,13 @@ hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_
     cg.B[1] = w->gate.packed + (size_t)inner * (d / 16);
     cg.B[2] = cg.B[1];
     cg.m = m; cg.nc = inner; cg.k = d;
-    cg.out0 = z; cg.aux_type = act(actt); cg.aux_probe = pr ? pr->z : nullptr;
+    cg.out0 = z; cg.aux_type = ACT_F32; cg.aux_probe = pr ? pr->z : nullptr;
     cg.acc_probe = pr ? pr->acc_gate : nullptr;
     if ((e = t_contract(cg, EPI_GLU, 2, true, st, path)) != hipSuccess) return e;
 
     int8_t *cz = pick(pr ? pr->codes_z : nullptr, L.codes_b);
     float *sz = pick(pr ? pr->scale_z : nullptr, L.s_b);
-    if ((e = t_norm_quant(z, act(actt), m, inner, w->down.norm_w, eps, cz, sz, L.sq_b, st, path)) != hipSuccess) return e;
+    if ((e = t_norm_quant(z, ACT_F32, m, inner, w->down.norm_w, eps, cz, sz, L.sq_b, st, path)) != hipSuccess) return e;
 
     ContractArgs cd{};
     for (int q = 0; q < 3; ++q) { cd.A[q] = cz; cd.s[q] = sz; cd.sumq[q] = L.sq_b; cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
@@ -276,65 +277,6 @@ hipError_t block_tail(const mmf_layer_weights *w, const void *x, void *out, mmf_
     cd.out0 = out; cd.out_type = act(actt); cd.res = x1; cd.res_type = ACT_F32;
     cd.acc_probe = pr ? pr->acc_down : nullptr;
     return t_contract(cd, EPI_RESID, 1, true, st, path);
-}
-
-// Whether the four-kernel decode step applies: every contraction quantises its
-// own input rows (b <= 16, shapes within the fused kernels' limits).
-bool fused_decode_ok(const mmf_layer_weights *w, mmf_dtype actt, int64_t b) {
-    const ActType at = act(actt);
-    return shared_ifg(w) && quant_contract_supported(b, w->d, w->d, EPI_GATES_STEP, QK_ROW, at, at) &&
-           quant_contract_supported(b, w->d, w->d, EPI_RESID, QK_GNORM, ACT_F32, at) &&
-           quant_contract_supported(b, w->inner, w->d, EPI_GLU, QK_ROW, ACT_F32, ACT_F32) &&
-           quant_contract_supported(b, w->d, w->inner, EPI_RESID, QK_ROW, at, at);
-}
-
-// The four-kernel decode step: x -> i/f/g + state update -> g_norm gate + o_proj
-// + residual -> gate_proj + SiLU product -> down_proj + residual, each kernel
-// quantising its own input rows.
-hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b, float *h,
-                        const LayerWs &L, hipStream_t st, std::string *path) {
-    const ActType at = act(actt);
-    const int d = w->d, inner = w->inner;
-    const float eps = w->eps;
-    ContractArgs ci{};
-    const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
-    for (int q = 0; q < 3; ++q) { ci.B[q] = tw[q]->packed; ci.mu[q] = tw[q]->mu; }
-    ci.m = b; ci.nc = d; ci.k = d;
-    ci.out0 = h; ci.out1 = L.g; ci.out_type = ACT_F32; ci.aux_type = at;
-    hipError_t e = timed("tgemv_q<gates_step>", b, 3 * d, d, st, [&] {
-        return launch_quant_contract(ci, EPI_GATES_STEP, QK_ROW, x, at, nullptr, at, w->i.norm_w, nullptr, eps, L.codes_b,
-                                     L.s_b, L.sq_b, st, path);
-    });
-    if (e != hipSuccess) return e;
-    ContractArgs co{};
-    for (int q = 0; q < 3; ++q) { co.B[q] = w->o.packed; co.mu[q] = w->o.mu; }
-    co.m = b; co.nc = d; co.k = d;
-    co.out0 = L.x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
-    e = timed("tgemv_q<gnorm_resid>", b, d, d, st, [&] {
-        return launch_quant_contract(co, EPI_RESID, QK_GNORM, h, ACT_F32, L.g, at, w->o.norm_w, w->g_norm_w, eps,
-                                     L.codes_b, L.s_b, L.sq_b, st, path);
-    });
-    if (e != hipSuccess) return e;
-    ContractArgs cg{};
-    for (int q = 0; q < 3; ++q) cg.mu[q] = w->gate.mu;
-    cg.B[0] = w->gate.packed;
-    cg.B[1] = w->gate.packed + (size_t)inner * (d / 16);
-    cg.B[2] = cg.B[1];
-    cg.m = b; cg.nc = inner; cg.k = d;
-    cg.out0 = L.z; cg.aux_type = at;
-    e = timed("tgemv_q<glu>", b, 2 * inner, d, st, [&] {
-        return launch_quant_contract(cg, EPI_GLU, QK_ROW, L.x1, ACT_F32, nullptr, ACT_F32, w->gate.norm_w, nullptr, eps,
-                                     L.codes_b, L.s_b, L.sq_b, st, path);
-    });
-    if (e != hipSuccess) return e;
-    ContractArgs cd{};
-    for (int q = 0; q < 3; ++q) { cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
-    cd.m = b; cd.nc = d; cd.k = inner;
-    cd.out0 = out; cd.out_type = at; cd.res = L.x1; cd.res_type = ACT_F32;
-    return timed("tgemv_q<resid>", b, d, inner, st, [&] {
-        return launch_quant_contract(cd, EPI_RESID, QK_ROW, L.z, at, nullptr, at, w->down.norm_w, nullptr, eps, L.codes_b,
-                                     L.s_b, L.sq_b, st, path);
-    });
 }
 
 // The decode step at up to 16 rows (i/f/g sharing one gain or none): a
@@ -345,7 +287,8 @@ hipError_t fused_decode(const mmf_layer_weights *w, const void *x, void *out, mm
 // also forms the gated g_norm of (h, g) itself (then applies its own gain, if
 // any): four kernels instead of eight; at 16 rows of 2048 with an inner width
 // of 5632, six (g_norm keeps its quantiser, and down_proj's rows are too
-// wide).
+// wide). A probe receives every stage from the same kernels: codes and scales
+// of a self-quantising contraction come from its workgroup 0.
 
 // Timing name of a self-quantising contraction: its epilogue and the type of the rows it reads.
 std::string row_name(const char *epi, ActType xt) {
@@ -353,66 +296,94 @@ std::string row_name(const char *epi, ActType xt) {
 }
 
 hipError_t decode_row_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b, float *h,
-                           const LayerWs &L, hipStream_t st, std::string *path) {
+                           const LayerWs &L, const mmf_layer_probe *pr, hipStream_t st, std::string *path) {
     const ActType at = act(actt);
     const int d = w->d, inner = w->inner;
     const float eps = w->eps;
     auto fused = [&](int k, EpiKind epi, const float *gain) { return contract_row_supported(b, k, epi, gain); };
     const float *gx = w->i.norm_w;  // i/f/g share one gain (or none): one quantisation of x serves all three
     hipError_t e;
+    // mixer: i/f/g + gates + the state update; g kept in fp32
+    int8_t *cx = pick(pr ? pr->codes_x[0] : nullptr, L.codes_b);
+    float *sx = pick(pr ? pr->scale_x[0] : nullptr, L.s_b);
     ContractArgs ca{};
     const mmf_ternary_weight *tw[3] = {&w->i, &w->f, &w->g};
     for (int q = 0; q < 3; ++q) { ca.B[q] = tw[q]->packed; ca.mu[q] = tw[q]->mu; }
     ca.m = b; ca.nc = d; ca.k = d;
-    ca.out0 = h; ca.out1 = L.g; ca.out_type = ACT_F32; ca.aux_type = at;
+    ca.out0 = h; ca.out1 = L.g; ca.out_type = ACT_F32; ca.aux_type = ACT_F32;
+    if (pr) { ca.acc_probe = pr->acc_ifg; ca.aux_probe = pr->g; ca.out2 = pr->f; ca.out3 = pr->xt; }
     if (fused(d, EPI_GATES_STEP, gx)) {
-        e = timed(row_name("gates_step", at), b, 3 * d, d, st,
-                  [&] { return launch_contract_row(ca, EPI_GATES_STEP, x, at, gx, eps, st, path); });
+        e = timed(row_name("gates_step", at), b, 3 * d, d, st, [&] {
+            return launch_contract_row(ca, EPI_GATES_STEP, x, at, gx, eps, pr ? pr->codes_x[0] : nullptr,
+                                       pr ? pr->scale_x[0] : nullptr, st, path);
+        });
     } else {
-        e = t_norm_quant(x, at, b, d, gx, eps, L.codes_b, L.s_b, L.sq_b, st, path);
-        for (int q = 0; q < 3; ++q) { ca.A[q] = L.codes_b; ca.s[q] = L.s_b; ca.sumq[q] = L.sq_b; }
+        e = t_norm_quant(x, at, b, d, gx, eps, cx, sx, L.sq_b, st, path);
+        for (int q = 0; q < 3; ++q) { ca.A[q] = cx; ca.s[q] = sx; ca.sumq[q] = L.sq_b; }
         if (e == hipSuccess) e = t_contract(ca, EPI_GATES_STEP, 3, true, st, path);
     }
+    if (e == hipSuccess && pr && pr->h)
+        e = hipMemcpyAsync(pr->h, h, (size_t)b * d * sizeof(float), hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return e;
+    // g_norm + o_proj + residual
+    float *x1 = pick(pr ? pr->x1 : nullptr, L.x1);
     ContractArgs co{};
     for (int q = 0; q < 3; ++q) { co.B[q] = w->o.packed; co.mu[q] = w->o.mu; }
     co.m = b; co.nc = d; co.k = d;
-    co.out0 = L.x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
+    co.out0 = x1; co.out_type = ACT_F32; co.res = x; co.res_type = at;
+    co.acc_probe = pr ? pr->acc_o : nullptr;
     if (contract_row_gnorm_supported(b, d)) {
-        e = timed(row_name("resid,gnorm", at), b, d, d, st,
-                  [&] { return launch_contract_row_gnorm(co, h, L.g, at, w->g_norm_w, w->o.norm_w, eps, st, path); });
+        e = timed(row_name("resid,gnorm", ACT_F32), b, d, d, st, [&] {
+            return launch_contract_row_gnorm(co, h, L.g, ACT_F32, w->g_norm_w, w->o.norm_w, eps,
+                                             pr ? pr->codes_u : nullptr, pr ? pr->scale_u : nullptr,
+                                             pr ? pr->u : nullptr, st, path);
+        });
     } else {
-        e = t_gnorm_quant(h, L.g, at, b, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, nullptr, st,
-                          path);
-        for (int q = 0; q < 3; ++q) { co.A[q] = L.codes_b; co.s[q] = L.s_b; co.sumq[q] = L.sq_b; }
+        int8_t *cu = pick(pr ? pr->codes_u : nullptr, L.codes_b);
+        float *su = pick(pr ? pr->scale_u : nullptr, L.s_b);
+        e = t_gnorm_quant(h, L.g, ACT_F32, b, d, w->g_norm_w, w->o.norm_w, eps, cu, su, L.sq_b, pr ? pr->u : nullptr,
+                          st, path);
+        for (int q = 0; q < 3; ++q) { co.A[q] = cu; co.s[q] = su; co.sumq[q] = L.sq_b; }
         if (e == hipSuccess) e = t_contract(co, EPI_RESID, 1, true, st, path);
     }
     if (e != hipSuccess) return e;
+    // gate_proj + SiLU product; z kept in fp32
     ContractArgs cg{};
     for (int q = 0; q < 3; ++q) cg.mu[q] = w->gate.mu;
     cg.B[0] = w->gate.packed;
     cg.B[1] = w->gate.packed + (size_t)inner * (d / 16);
     cg.B[2] = cg.B[1];
     cg.m = b; cg.nc = inner; cg.k = d;
-    cg.out0 = L.z; cg.aux_type = at;
+    cg.out0 = L.z; cg.aux_type = ACT_F32;
+    if (pr) { cg.acc_probe = pr->acc_gate; cg.aux_probe = pr->z; }
     if (fused(d, EPI_GLU, w->gate.norm_w)) {
-        e = timed(row_name("glu", ACT_F32), b, 2 * inner, d, st,
-                  [&] { return launch_contract_row(cg, EPI_GLU, L.x1, ACT_F32, w->gate.norm_w, eps, st, path); });
+        e = timed(row_name("glu", ACT_F32), b, 2 * inner, d, st, [&] {
+            return launch_contract_row(cg, EPI_GLU, x1, ACT_F32, w->gate.norm_w, eps, pr ? pr->codes_x1 : nullptr,
+                                       pr ? pr->scale_x1 : nullptr, st, path);
+        });
     } else {
-        e = t_norm_quant(L.x1, ACT_F32, b, d, w->gate.norm_w, eps, L.codes_b, L.s_b, L.sq_b, st, path);
-        for (int q = 0; q < 3; ++q) { cg.A[q] = L.codes_b; cg.s[q] = L.s_b; cg.sumq[q] = L.sq_b; }
+        int8_t *c1 = pick(pr ? pr->codes_x1 : nullptr, L.codes_b);
+        float *s1 = pick(pr ? pr->scale_x1 : nullptr, L.s_b);
+        e = t_norm_quant(x1, ACT_F32, b, d, w->gate.norm_w, eps, c1, s1, L.sq_b, st, path);
+        for (int q = 0; q < 3; ++q) { cg.A[q] = c1; cg.s[q] = s1; cg.sumq[q] = L.sq_b; }
         if (e == hipSuccess) e = t_contract(cg, EPI_GLU, 2, true, st, path);
     }
     if (e != hipSuccess) return e;
+    // down_proj + residual
     ContractArgs cd{};
     for (int q = 0; q < 3; ++q) { cd.B[q] = w->down.packed; cd.mu[q] = w->down.mu; }
     cd.m = b; cd.nc = d; cd.k = inner;
-    cd.out0 = out; cd.out_type = at; cd.res = L.x1; cd.res_type = ACT_F32;
+    cd.out0 = out; cd.out_type = at; cd.res = x1; cd.res_type = ACT_F32;
+    cd.acc_probe = pr ? pr->acc_down : nullptr;
     if (fused(inner, EPI_RESID, w->down.norm_w))
-        return timed(row_name("resid", at), b, d, inner, st,
-                     [&] { return launch_contract_row(cd, EPI_RESID, L.z, at, w->down.norm_w, eps, st, path); });
-    e = t_norm_quant(L.z, at, b, inner, w->down.norm_w, eps, L.codes_b, L.s_b, L.sq_b, st, path);
-    for (int q = 0; q < 3; ++q) { cd.A[q] = L.codes_b; cd.s[q] = L.s_b; cd.sumq[q] = L.sq_b; }
+        return timed(row_name("resid", ACT_F32), b, d, inner, st, [&] {
+            return launch_contract_row(cd, EPI_RESID, L.z, ACT_F32, w->down.norm_w, eps, pr ? pr->codes_z : nullptr,
+                                       pr ? pr->scale_z : nullptr, st, path);
+        });
+    int8_t *cz = pick(pr ? pr->codes_z : nullptr, L.codes_b);
+    float *sz = pick(pr ? pr->scale_z : nullptr, L.s_b);
+    e = t_norm_quant(L.z, ACT_F32, b, inner, w->down.norm_w, eps, cz, sz, L.sq_b, st, path);
+    for (int q = 0; q < 3; ++q) { cd.A[q] = cz; cd.s[q] = sz; cd.sumq[q] = L.sq_b; }
     if (e == hipSuccess) e = t_contract(cd, EPI_RESID, 1, true, st, path);
     return e;
 }
@@ -443,6 +414,46 @@ hipError_t quant_ifg(const mmf_layer_weights *w, const void *x, mmf_dtype actt, 
     ca.m = m; ca.nc = w->d; ca.k = w->d;
     ca.acc_probe = pr ? pr->acc_ifg : nullptr;
     return hipSuccess;
+}
+
+// The decode step on a validated workspace of at least mmf_layer_workspace_size(w, b, 1) bytes.
+mmf_status decode_step_run(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b, float *h,
+                           void *ws, const mmf_layer_probe *probe, hipStream_t stream) {
+    const int mode = g_decode_mode.load();
+    std::string path;
+    hipError_t e = hipSuccess;
+    const bool row_ok = b >= 1 && b <= 16 && shared_ifg(w);
+    if (row_ok && mode == 0) {
+        Carver c(ws);
+        LayerWs L;
+        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
+        e = decode_row_step(w, x, out, actt, b, h, L, probe, stream, &path);
+        mmf_status r = hip_status(e, "mmf_layer_decode_step");
+        if (r == MMF_OK) g_path = path;
+        return r;
+    }
+    if (b > 0) {
+        Carver c(ws);
+        LayerWs L;
+        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
+        ContractArgs ca{};
+        bool shared = true;
+        e = quant_ifg(w, x, actt, b, L, probe, ca, &shared, stream, &path);
+        void *g = L.g;
+        if (e == hipSuccess) {
+            ca.out0 = h; ca.out1 = g; ca.out_type = ACT_F32;
+            ca.aux_type = ACT_F32; ca.aux_probe = probe ? probe->g : nullptr;
+            ca.out2 = probe ? probe->f : nullptr;
+            ca.out3 = probe ? probe->xt : nullptr;
+            e = t_contract(ca, EPI_GATES_STEP, 3, shared, stream, &path);
+        }
+        if (e == hipSuccess && probe && probe->h)
+            e = hipMemcpyAsync(probe->h, h, (size_t)b * w->d * sizeof(float), hipMemcpyDeviceToDevice, stream);
+        if (e == hipSuccess) e = block_tail(w, x, out, actt, b, L, h, g, probe, stream, &path);
+    }
+    mmf_status r = hip_status(e, "mmf_layer_decode_step");
+    if (r == MMF_OK) g_path = path;
+    return r;
 }
 
 }  // namespace
@@ -812,7 +823,7 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
         float *h = pick(probe ? probe->h : nullptr, L.h);
         if (e == hipSuccess) {
             ca.out0 = f; ca.out1 = xt; ca.out2 = g; ca.out_type = ACT_F32;
-            ca.aux_type = act(actt); ca.aux_probe = probe ? probe->g : nullptr;
+            ca.aux_type = ACT_F32; ca.aux_probe = probe ? probe->g : nullptr;
             e = t_contract(ca, EPI_GATES, 3, shared, stream, &path);
         }
         if (e == hipSuccess) e = t_scan(xt, f, h0, h, h_last, b, t, w->d, chunks, L.scan, stream, &path);
@@ -824,20 +835,10 @@ mmf_status mmf_layer_fwd(const mmf_layer_weights *w, const void *x, void *out, m
 }
 
 mmf_status mmf_set_decode_kernel(int mode) {
-    if (mode < 0 || mode > 3)
-        return fail(MMF_ERR_INVALID_ARG, "decode kernel mode %d (0 auto, 1 separate, 2 one-XCD, 3 fused)", mode);
+    if (mode < 0 || mode > 1) return fail(MMF_ERR_INVALID_ARG, "decode kernel mode %d (0 auto, 1 separate)", mode);
     g_decode_mode.store(mode);
     g_err.clear();
     return MMF_OK;
-}
-
-mmf_status mmf_decode_expired_waits(uint32_t *count) {
-    if (!count) return fail(MMF_ERR_INVALID_ARG, "count is NULL");
-    unsigned c = 0, c2 = 0;
-    mmf_status st = hip_status(decode_step_expired_spins(&c), "mmf_decode_expired_waits");
-    if (st == MMF_OK) st = hip_status(quant_contract_expired_waits(&c2), "mmf_decode_expired_waits");
-    *count = c + c2;
-    return st;
 }
 
 mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt, int64_t b,
@@ -852,86 +853,7 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
         return fail(MMF_ERR_INVALID_ARG, "x, out and h must be 16-byte aligned");
     if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
         return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
-    const int mode = g_decode_mode.load();
-    const bool xcd_ok = !probe && shared_ifg(w) && decode_step_supported(b, w->d, w->inner);
-    if (mode == 2 && b > 0 && !xcd_ok)
-        return fail(MMF_ERR_UNSUPPORTED, "one-XCD decode step: needs b <= 16, no probe, equal i/f/g gains, "
-                    "d and inner multiples of 256 within the kernel's limits (b=%lld d=%d inner=%d)",
-                    (long long)b, w->d, w->inner);
-    std::string path;
-    hipError_t e = hipSuccess;
-    if (b > 0 && mode == 2 && xcd_ok) {
-        Carver c(ws);
-        LayerWs L;
-        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
-        DecodeStepArgs da{};
-        da.x = x; da.out = out; da.h = h;
-        const mmf_ternary_weight *ifg[3] = {&w->i, &w->f, &w->g};
-        for (int q = 0; q < 3; ++q) { da.w_ifg[q] = ifg[q]->packed; da.mu_ifg[q] = ifg[q]->mu; }
-        da.w_o = w->o.packed; da.mu_o = w->o.mu;
-        da.w_gate = w->gate.packed; da.mu_gate = w->gate.mu;
-        da.w_down = w->down.packed; da.mu_down = w->down.mu;
-        da.gain_x = w->i.norm_w; da.gain_o = w->o.norm_w; da.gain_gate = w->gate.norm_w; da.gain_down = w->down.norm_w;
-        da.g_norm_w = w->g_norm_w;
-        da.b = (int)b; da.d = w->d; da.inner = w->inner; da.eps = w->eps; da.act = act(actt);
-        da.codes = L.codes_b; da.s = L.s_b; da.sumq = L.sq_b; da.g = L.g; da.x1 = L.x1; da.z = L.z;
-        bool launched = false;
-        e = timed("decode_step_xcd", b, w->d, w->inner, stream,
-                  [&] { return launch_decode_step(da, stream, &path, &launched); });
-        if (e == hipSuccess && !launched && mode == 2)
-            return fail(MMF_ERR_UNSUPPORTED, "one-XCD decode step: this device cannot run it");
-        if (e != hipSuccess || launched) {
-            mmf_status r = hip_status(e, "mmf_layer_decode_step");
-            if (r == MMF_OK) g_path = path;
-            return r;
-        }
-    }
-    const bool fused_ok = b > 0 && !probe && fused_decode_ok(w, actt, b);
-    if (mode == 3 && b > 0 && !fused_ok)
-        return fail(MMF_ERR_UNSUPPORTED, "fused decode step: needs b <= 16, no probe, equal i/f/g gains, d and inner "
-                    "multiples of 256 within the fused kernels' limits (b=%lld d=%d inner=%d)",
-                    (long long)b, w->d, w->inner);
-    if (fused_ok && mode == 3) {
-        Carver c(ws);
-        LayerWs L;
-        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
-        e = fused_decode(w, x, out, actt, b, h, L, stream, &path);
-        mmf_status r = hip_status(e, "mmf_layer_decode_step");
-        if (r == MMF_OK) g_path = path;
-        return r;
-    }
-    const bool row_ok = b >= 1 && b <= 16 && !probe && shared_ifg(w);
-    if (row_ok && mode == 0) {
-        Carver c(ws);
-        LayerWs L;
-        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
-        e = decode_row_step(w, x, out, actt, b, h, L, stream, &path);
-        mmf_status r = hip_status(e, "mmf_layer_decode_step");
-        if (r == MMF_OK) g_path = path;
-        return r;
-    }
-    if (b > 0) {
-        Carver c(ws);
-        LayerWs L;
-        layer_plan(c, w, b, 1, scan_pick_chunks(b, 1, w->d, MMF_SCAN_CHUNK), &L);
-        ContractArgs ca{};
-        bool shared = true;
-        e = quant_ifg(w, x, actt, b, L, probe, ca, &shared, stream, &path);
-        void *g = L.g;
-        if (e == hipSuccess) {
-            ca.out0 = h; ca.out1 = g; ca.out_type = ACT_F32;
-            ca.aux_type = act(actt); ca.aux_probe = probe ? probe->g : nullptr;
-            ca.out2 = probe ? probe->f : nullptr;
-            ca.out3 = probe ? probe->xt : nullptr;
-            e = t_contract(ca, EPI_GATES_STEP, 3, shared, stream, &path);
-        }
-        if (e == hipSuccess && probe && probe->h)
-            e = hipMemcpyAsync(probe->h, h, (size_t)b * w->d * sizeof(float), hipMemcpyDeviceToDevice, stream);
-        if (e == hipSuccess) e = block_tail(w, x, out, actt, b, L, h, g, probe, stream, &path);
-    }
-    mmf_status r = hip_status(e, "mmf_layer_decode_step");
-    if (r == MMF_OK) g_path = path;
-    return r;
+    return decode_step_run(w, x, out, actt, b, h, ws, probe, stream);
 }
 
 // --------------------------------------------------------- block derivative --
@@ -940,7 +862,7 @@ struct LayerBwdWs {
     float *s_x[3];
     int32_t *sq_x[3];
     float *ih, *fh, *gh, *f, *xt, *h, *u, *x1, *ab;
-    void *g, *z;  // activation dtype (fp32-sized)
+    float *g, *z;  // fp32
     int8_t *codes_b;
     float *s_b;
     int32_t *sq_b;
@@ -1047,10 +969,11 @@ mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *
         ca.out0 = pre[q]; ca.out_type = ACT_F32;
         e = t_contract(ca, EPI_LINEAR, 1, true, stream, &path);
     }
-    if (e == hipSuccess) e = launch_gates_keep(L.ih, L.fh, L.gh, md, L.f, L.xt, L.g, at, stream);
+    if (e == hipSuccess) e = launch_gates_keep(L.ih, L.fh, L.gh, md, L.f, L.xt, L.g, ACT_F32, stream);
     if (e == hipSuccess) e = t_scan(L.xt, L.f, h0, L.h, nullptr, b, t, d, chunks, L.scan, stream, &path);
     if (e == hipSuccess)
-        e = t_gnorm_quant(L.h, L.g, at, m, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, L.u, stream, &path);
+        e = t_gnorm_quant(L.h, L.g, ACT_F32, m, d, w->g_norm_w, w->o.norm_w, eps, L.codes_b, L.s_b, L.sq_b, L.u, stream,
+                          &path);
     if (e == hipSuccess) {
         ContractArgs co{};
         for (int j = 0; j < 3; ++j) { co.A[j] = L.codes_b; co.s[j] = L.s_b; co.sumq[j] = L.sq_b; co.B[j] = w->o.packed; co.mu[j] = w->o.mu; }
@@ -1066,11 +989,11 @@ mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *
         cg.out0 = L.ab; cg.out_type = ACT_F32;
         e = t_contract(cg, EPI_LINEAR, 1, true, stream, &path);
     }
-    if (e == hipSuccess) e = launch_glu_keep(L.ab, m, inner, L.z, at, stream);
+    if (e == hipSuccess) e = launch_glu_keep(L.ab, m, inner, L.z, ACT_F32, stream);
     // ---- derivatives, last step first
     if (e == hipSuccess)  // down_proj: dz
-        e = bitlinear_bwd_run(L.z, at, m, &w->down, eps, dout, at, L.dz, ACT_F32, gr->dw[5], gr->dgain[5], L.blin,
-                              stream, &path, &err);
+        e = bitlinear_bwd_run(L.z, ACT_F32, m, &w->down, eps, dout, at, L.dz, ACT_F32, gr->dw[5], gr->dgain[5],
+                              L.blin, stream, &path, &err);
     if (e == hipSuccess) e = launch_glu_bwd(L.dz, L.ab, m, inner, L.dab, stream);
     if (e == hipSuccess)  // gate_proj: into x1
         e = bitlinear_bwd_run(L.x1, ACT_F32, m, &w->gate, eps, L.dab, ACT_F32, L.dx1g, ACT_F32, gr->dw[4], gr->dgain[4],
@@ -1080,8 +1003,8 @@ mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *
         e = bitlinear_bwd_run(L.u, ACT_F32, m, &w->o, eps, L.dx1, ACT_F32, L.du, ACT_F32, gr->dw[3], gr->dgain[3], L.blin,
                               stream, &path, &err);
     if (e == hipSuccess)  // g_norm: dh, dg^ and the weight's partial sums
-        e = launch_gnorm_bwd(L.h, L.g, at, L.du, w->g_norm_w, eps, m, d, L.dh, L.dg, gr->dg_norm_w ? L.wpart : nullptr,
-                             stream);
+        e = launch_gnorm_bwd(L.h, L.g, ACT_F32, L.du, w->g_norm_w, eps, m, d, L.dh, L.dg,
+                             gr->dg_norm_w ? L.wpart : nullptr, stream);
     if (e == hipSuccess && gr->dg_norm_w) {
         const int rows = rmsnorm_bwd_rows(m);
         e = launch_gain_reduce(L.wpart, (int)((m + rows - 1) / rows), d, L.wpart2, gr->dg_norm_w, stream);
@@ -1098,6 +1021,27 @@ mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *
     if (e == hipSuccess) e = launch_sum(L.dx1, ACT_F32, L.dxi, L.dxf, L.dxg, md, gr->dx, stream);
     if (e != hipSuccess && !err.empty()) return fail(MMF_ERR_HIP, "mmf_layer_bwd: %s", err.c_str());
     mmf_status r = hip_status(e, "mmf_layer_bwd");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+mmf_status mmf_hbm_ceiling(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream) {
+    if (mode != 0 && mode != 1) return fail(MMF_ERR_INVALID_ARG, "mode %d (0 read, 1 copy)", mode);
+    if (bytes <= 0 || bytes % 16) return fail(MMF_ERR_INVALID_ARG, "bytes=%lld must be a positive multiple of 16",
+                                             (long long)bytes);
+    if (!src || !dst || !aligned16(src) || !aligned16(dst))
+        return fail(MMF_ERR_INVALID_ARG, "src and dst must be non-NULL and 16-byte aligned");
+    if (ceiling_blocks() * 4 > MMF_HBM_CEILING_SINK_BYTES) return fail(MMF_ERR_INVALID_ARG, "sink too small");
+    const char *s = static_cast<const char *>(src);
+    const char *d = static_cast<const char *>(dst);
+    const int64_t dlen = mode == 0 ? MMF_HBM_CEILING_SINK_BYTES : bytes;
+    if (s < d + dlen && d < s + bytes) return fail(MMF_ERR_INVALID_ARG, "src and dst overlap");
+    std::string path = mode == 0 ? "stream_read;" : "stream_copy;";
+    const hipError_t e = timed(mode == 0 ? "stream_read" : "stream_copy", bytes, 0, 0, stream, [&] {
+        return mode == 0 ? launch_stream_read(src, bytes, static_cast<uint32_t *>(dst), stream)
+                         : launch_stream_copy(src, dst, bytes, stream);
+    });
+    mmf_status r = hip_status(e, "mmf_hbm_ceiling");
     if (r == MMF_OK) g_path = path;
     return r;
 }

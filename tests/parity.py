@@ -63,22 +63,29 @@ def packed_words(pl) -> np.ndarray:
     return host(pl.packed).view(np.uint32)
 
 
-def decode_reference(L: "oracle.Layer", x: np.ndarray, h0: np.ndarray, act: str) -> dict:
-    """The oracle's decode step composed from its own stage functions, with g and z rounded to
-    the activation type where the GPU stores them (bf16 activations keep g and z in bf16, the
-    state and x1 in fp32): the free-running reference for a bf16 decode step."""
-    def rd(v):  # the value as stored
-        return np.asarray(synth.bf16_round(v.astype(np.float32)), np.float64) if act == "bf16" else v
-    eps = L.eps
-    x = np.asarray(x, np.float64)
-    ri, rf, rg = L.i(x, eps), L.f(x, eps), L.g(x, eps)
-    f, xt = oracle.mixer_gates(ri["y"], rf["y"])
-    h = oracle.hgrn_scan(xt[:, None, :], f[:, None, :], h0)[:, 0, :]
-    g = rd(rg["y"])
-    x1 = x + L.o(oracle.gnorm_swish(h, g, L.g_norm_w, eps), eps)["y"]
-    ya = L.gate(x1, eps)["y"]
-    z = rd(oracle.silu(ya[:, :L.inner]) * ya[:, L.inner:])
-    return dict(h=h, out=x1 + L.down(z, eps)["y"])
+def check_free_running(pr: dict, ref: dict, out_gpu: np.ndarray, act: str, what: str = "out"):
+    """The GPU layer against the oracle run free (not fed with the GPU's stages). The first
+    quantiser sees the same input on both sides, so its codes must be equal; a later quantiser's
+    input differs by rounding only, so a code may flip by one where y*s lies within rounding of a
+    half-integer (rare). Rows with no flipped code must match within the activation type's
+    tolerance; a row with flips moves by a few quantisation steps at most (normwise bound)."""
+    m = out_gpu.shape[0]
+    assert_equal(pr["codes_x"][0], ref["q_i"].reshape(pr["codes_x"][0].shape), "codes_x (free-running)")
+    flipped = np.zeros(m, bool)
+    for key, rk in (("codes_u", "q_u"), ("codes_x1", "q_x1"), ("codes_z", "q_z")):
+        r = ref[rk].reshape(pr[key].shape)
+        diff = pr[key] != r
+        assert np.all(np.abs(pr[key].astype(int) - r.astype(int))[diff] == 1), key
+        assert diff.mean() < 1e-3, (key, diff.mean())
+        flipped |= diff.any(axis=1)
+    refo = ref["out"].reshape(m, -1)
+    clean = ~flipped
+    outg = np.asarray(out_gpu, np.float64)
+    assert_close(outg[clean], refo[clean], 1e-4 if act == "f32" else 2e-2, what + " on rows without a code flip")
+    rel = np.linalg.norm(outg - refo) / np.linalg.norm(refo)
+    # bf16 output: its own rounding adds about 1.1e-3 normwise
+    assert rel < (1e-3 if act == "f32" else 4e-3), (what, rel)
+    return int(flipped.sum())
 
 
 def make_pair(d, inner, seed, device, gains=None, eps=1e-8):
@@ -119,8 +126,6 @@ def check_layer_stages(L: "oracle.Layer", x: np.ndarray, h0, pr: dict, out_gpu: 
     eps = L.eps
     xf = x.reshape(m, d).astype(np.float32)
     rtol_out = 1e-4 if act == "f32" else 2e-2
-    # g and z are stored in the activation dtype (the probes hold the stored values)
-    rtol_act = rtol_out
     projs = [L.i, L.f, L.g]
     for q in range(1 if shared else 3):
         qq, ss, _ = oracle.quantize(xf, projs[q].gain, eps)
@@ -136,7 +141,7 @@ def check_layer_stages(L: "oracle.Layer", x: np.ndarray, h0, pr: dict, out_gpu: 
     f_ref, xt_ref = oracle.mixer_gates(hat[0], hat[1])
     assert_close(pr["f"], f_ref, 1e-4, "f")
     assert_close(pr["xt"], xt_ref, 1e-4, "xt")
-    assert_close(pr["g"], hat[2], rtol_act, "g")
+    assert_close(pr["g"], hat[2], 1e-4, "g")
     h_ref = oracle.hgrn_scan(pr["xt"].reshape(b, t, d), pr["f"].reshape(b, t, d), h0)
     assert_close(pr["h"], h_ref.reshape(m, d), scan_rtol, "h")
     u_ref = oracle.gnorm_swish(pr["h"], pr["g"], L.g_norm_w, eps)
@@ -156,7 +161,7 @@ def check_layer_stages(L: "oracle.Layer", x: np.ndarray, h0, pr: dict, out_gpu: 
     ab = oracle.dequant(acc_g, pr["scale_x1"], L.gate.mu)
     inner = L.inner
     z_ref = oracle.silu(ab[:, :inner]) * ab[:, inner:]
-    assert_close(pr["z"], z_ref, rtol_act, "z")
+    assert_close(pr["z"], z_ref, 1e-4, "z")
     qq, ss, _ = oracle.quantize(pr["z"], L.down.gain, eps)
     assert_equal(pr["codes_z"], qq, "codes_z")
     assert_equal(pr["scale_z"], ss, "scale_z")
@@ -203,7 +208,7 @@ def check_layer_sampled(L: "oracle.Layer", x: np.ndarray, h0, probe, out_gpu, ac
     f_ref, xt_ref = oracle.mixer_gates(hat[0], hat[1])
     assert_close(pr["f"], f_ref, 1e-4, "f")
     assert_close(pr["xt"], xt_ref, 1e-4, "xt")
-    assert_close(pr["g"], hat[2], rtol_out, "g")
+    assert_close(pr["g"], hat[2], 1e-4, "g")
     # the scan: whole sequences of the sampled channels
     for (bi, c) in chans:
         xs = probe.xt.view(b, t, d)[bi, :, c].cpu().numpy().reshape(1, t, 1)
@@ -225,7 +230,7 @@ def check_layer_sampled(L: "oracle.Layer", x: np.ndarray, h0, probe, out_gpu, ac
     acc_g = oracle.ternary_matmul(pr["codes_x1"], L.gate.t)
     assert_equal(pr["acc_gate"], acc_g, "acc_gate")
     ab = oracle.dequant(acc_g, pr["scale_x1"], L.gate.mu)
-    assert_close(pr["z"], oracle.silu(ab[:, :L.inner]) * ab[:, L.inner:], rtol_out, "z")
+    assert_close(pr["z"], oracle.silu(ab[:, :L.inner]) * ab[:, L.inner:], 1e-4, "z")
     qq, ss, _ = oracle.quantize(pr["z"], L.down.gain, eps)
     assert_equal(pr["codes_z"], qq, "codes_z")
     assert_equal(pr["scale_z"], ss, "scale_z")

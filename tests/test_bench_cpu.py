@@ -25,21 +25,21 @@ def test_decode_gemv_bytes_match_the_documented_figure():
 def test_gate_groups_share_their_epilogue_bytes():
     # n counts all groups' outputs; the epilogue bytes are per channel of one group
     _, gates = bench.algorithmic("tgemv<gates_step>", 16, 3 * 2048, 2048)
-    assert gates == 3 * 2048 * 2048 / 4 + 16 * 2048 + 8 * 16 + 16 * 2048 * 10
+    assert gates == 3 * 2048 * 2048 / 4 + 16 * 2048 + 8 * 16 + 16 * 2048 * 12
     _, glu = bench.algorithmic("tgemm_dma<glu>", 1024, 2 * 5632, 2048)
-    assert glu == 2 * 5632 * 2048 / 4 + 1024 * 2048 + 8 * 1024 + 1024 * 5632 * 2
+    assert glu == 2 * 5632 * 2048 / 4 + 1024 * 2048 + 8 * 1024 + 1024 * 5632 * 4
 
 
 def test_self_quantising_contractions_read_rows_not_codes():
     # gate_proj + up_proj at the 1.3B shape, 16 fp32 rows; i/f/g from 16 bf16 rows
     _, glu = bench.algorithmic("tgemv_row<glu,f32>", 16, 2 * 5632, 2048)
-    assert glu == 2 * 5632 * 2048 / 4 + 16 * 2048 * 4 + 16 * 5632 * 2
+    assert glu == 2 * 5632 * 2048 / 4 + 16 * 2048 * 4 + 16 * 5632 * 4
     _, gates = bench.algorithmic("tgemv_row<gates_step,bf16>", 16, 3 * 2048, 2048)
-    assert gates == 3 * 2048 * 2048 / 4 + 16 * 2048 * 2 + 16 * 2048 * 10
+    assert gates == 3 * 2048 * 2048 / 4 + 16 * 2048 * 2 + 16 * 2048 * 12
     assert bench.kernel_files("tgemv_row<resid,bf16> m=1 n=2 k=3") == bench.kernel_files("tgemv<resid>")
     # o_proj over the gated g_norm of one row: h, g and the gain read, residual and sum per output
-    _, o = bench.algorithmic("tgemv_row<resid,gnorm,bf16>", 1, 2048, 2048)
-    assert o == 2048 * 2048 / 4 + 2048 * (4 + 2) + 4 * 2048 + 2048 * (4 + 2)
+    _, o = bench.algorithmic("tgemv_row<resid,gnorm,f32>", 1, 2048, 2048)
+    assert o == 2048 * 2048 / 4 + 2048 * (4 + 4) + 4 * 2048 + 2048 * (4 + 2)
 
 
 def test_split_activation_codes_counted_per_group():
@@ -58,16 +58,8 @@ def test_elementwise_kernels():
     assert bench.algorithmic("gnorm_quant<bf16>", 10, 0, 256) == (0.0, 10 * 256 * 7 + 80)
 
 
-def test_decode_step_kernel_counts_every_weight_once():
-    d, inner, b = 2048, 5632, 16
-    ops, nbytes = bench.algorithmic("decode_step_xcd", b, d, inner)
-    weights = 4 * d * d + 3 * d * inner
-    assert ops == 2.0 * b * weights
-    assert nbytes == weights / 4 + b * d * (2 * 2 + 8)
-
-
 def test_every_kernel_name_maps_to_its_sources():
-    names = ["tgemv<resid>", "tgemv_row<glu,f32>", "tgemm<gates,split_a>", "tgemm_dma<glu>", "tgemv_q<gnorm_resid>", "decode_step_xcd",
+    names = ["tgemv<resid>", "tgemv_row<glu,f32>", "tgemm<gates,split_a>", "tgemm_dma<glu>",
              "norm_quant<f32>", "gnorm_quant<bf16>", "scan_tiled", "scan_chunk", "scan_recurrent"]
     csrc = os.path.join(ROOT, "ternary_weight_matmul_amd", "csrc")
     for n in names:

@@ -9,9 +9,8 @@ import pytest
 
 import oracle
 from ternary_weight_matmul_amd import synth
-from parity import (assert_close, assert_equal, bf16_tensor, check_layer_sampled, check_layer_stages, decode_reference,
-                    dev, host,
-                    make_pair, packed_words)
+from parity import (assert_close, assert_equal, bf16_tensor, check_free_running, check_layer_sampled,
+                    check_layer_stages, dev, host, make_pair, packed_words)
 
 pytestmark = pytest.mark.gpu
 
@@ -577,20 +576,7 @@ def test_layer_c1_end_to_end(gpu):
     check_layer_stages(L, x, None, pr, outg, "f32")
     # free-running oracle: the input codes are identical; later quantisers see inputs that differ
     # by rounding only, so a code may flip where y*s lies within rounding of a half-integer
-    ref = oracle.layer_forward(L, x)
-    assert_equal(pr["codes_x"][0], ref["q_i"].reshape(128, d), "codes_x (free-running)")
-    flipped = np.zeros(128, bool)
-    for key, rk in (("codes_u", "q_u"), ("codes_x1", "q_x1"), ("codes_z", "q_z")):
-        diff = pr[key] != ref[rk].reshape(pr[key].shape)
-        assert np.all(np.abs(pr[key].astype(int) - ref[rk].reshape(pr[key].shape).astype(int))[diff] == 1), key
-        assert diff.mean() < 1e-3, (key, diff.mean())
-        flipped |= diff.any(axis=1)
-    refo = ref["out"].reshape(128, d)
-    clean = ~flipped
-    assert_close(outg[clean], refo[clean], 1e-4, "out on rows without a code flip")
-    # a row with flips differs by a few quantisation steps at most
-    rel = np.linalg.norm(outg - refo) / np.linalg.norm(refo)
-    assert rel < 1e-3, rel
+    check_free_running(pr, oracle.layer_forward(L, x), outg, "f32")
 
 
 DECODE_CASES = [
@@ -621,11 +607,41 @@ def test_decode_step_stages(gpu, b, act, gains, d, inner, family):
     shared = gains != "distinct"
     probe = mmf.LayerProbe(b, d, inner, gpu, shared_ifg=shared)
     xd = bf16_tensor(x, gpu) if act == "bf16" else dev(x, gpu)
+    h_plain = hd.clone()
+    out_plain = mmf.layer_decode_step(P, xd, h_plain)
+    path_plain = mmf.last_path()
     out = mmf.layer_decode_step(P, xd, hd, probe=probe)
     torch.cuda.synchronize()
     assert family in mmf.last_path(), mmf.last_path()
+    # a probe changes neither the kernels the default path launches nor their bits
+    assert mmf.last_path() == path_plain, (mmf.last_path(), path_plain)
+    assert torch.equal(out, out_plain) and torch.equal(hd, h_plain)
     pr = probe.host()
     check_layer_stages(L, x[:, None, :], h0, pr, host(out), act, shared=shared)
+    assert np.array_equal(host(hd), pr["h"])
+
+
+@pytest.mark.parametrize("b,act,gains,d,inner", [(1, "bf16", None, 2048, 5632), (16, "bf16", None, 2048, 5632),
+                                                  (5, "f32", "shared", 272, 1040), (1, "f32", ("o", "g_norm"), 272, 1040)])
+def test_decode_step_stages_separate(gpu, b, act, gains, d, inner):
+    """The separate-kernel decode step (mmf_set_decode_kernel 1) stage by stage."""
+    import torch
+    mmf = _mmf()
+    L, P = make_pair(d, inner, 650 + b, gpu, gains)
+    x = synth.activations((b, d), 651, act)
+    h0 = synth.activations((b, d), 652)
+    hd = dev(h0, gpu)
+    probe = mmf.LayerProbe(b, d, inner, gpu)
+    xd = bf16_tensor(x, gpu) if act == "bf16" else dev(x, gpu)
+    try:
+        mmf.set_decode_kernel("separate")
+        out = mmf.layer_decode_step(P, xd, hd, probe=probe)
+        torch.cuda.synchronize()
+        assert "tgemv_row" not in mmf.last_path() and "norm_quant_row" in mmf.last_path(), mmf.last_path()
+    finally:
+        mmf.set_decode_kernel("auto")
+    pr = probe.host()
+    check_layer_stages(L, x[:, None, :], h0, pr, host(out), act)
     assert np.array_equal(host(hd), pr["h"])
 
 
@@ -662,20 +678,31 @@ FULL_SIZE_PREFILL = [
 
 @pytest.mark.parametrize("shape,b,t,seed", FULL_SIZE_PREFILL)
 def test_layer_full_size_sampled(gpu, shape, b, t, seed):
-    """Every stage of 48 sampled tokens (and the first and last) against the oracle fed with the
-    GPU's stage inputs; the scan over whole sequences for 6 sampled channels."""
+    """One layer at full size in the benchmark's launch configuration (no probe: the typed fast
+    epilogues), then again with a probe (the generic epilogues the stage checks read): both give
+    the same bits. Every stage of one sampled token per 128-row tile of the contractions (and
+    the first and last token) is checked against the oracle fed with the GPU's stage inputs, and
+    the scan over whole sequences for 6 sampled channels."""
     import torch
     mmf = _mmf()
     d, inner, _ = synth.SHAPES[shape]
     L, P = make_pair(d, inner, synth.layer_seed(seed, 0), gpu)
     xs = synth.activations((b, t, d), seed * 10 + 1, "bf16")
+    xd = bf16_tensor(xs, gpu)
+    out_plain, hl_plain = mmf.layer_fwd(P, xd, None, want_h_last=True, mode="auto")
+    torch.cuda.synchronize()
+    path_plain = mmf.last_path()
     probe = mmf.LayerProbe(b * t, d, inner, gpu)
-    out, _ = mmf.layer_fwd(P, bf16_tensor(xs, gpu), None, want_h_last=True, mode="auto", probe=probe)
+    out, hl = mmf.layer_fwd(P, xd, None, want_h_last=True, mode="auto", probe=probe)
     torch.cuda.synchronize()
     path = mmf.last_path()
+    assert path == path_plain, (path, path_plain)
     assert "tgemm_dma" in path and "scan_tiled" in path, path
+    assert torch.equal(out_plain, out) and torch.equal(hl_plain, hl)
+    del out_plain, hl_plain
+    m = b * t
     r = synth.rng(seed * 10 + 7)
-    rows = set(r.choice(b * t, size=48, replace=False).tolist()) | {0, b * t - 1}
+    rows = {int(r.integers(s0, min(s0 + 128, m))) for s0 in range(0, m, 128)} | {0, m - 1}
     chans = [(int(r.integers(b)), int(r.integers(d))) for _ in range(6)]
     check_layer_sampled(L, xs, None, probe, out, "bf16", b, t, rows, chans,
                         scan_rtol=1e-3 if t >= 4096 else 1e-4)
@@ -775,89 +802,6 @@ def test_layer_empty_sequence(gpu):
     assert out.shape == (2, 0, 64) and torch.equal(h_last, h0)
 
 
-XCD_CASES = [
-    # b, act, gains, d, inner
-    (1, "bf16", None, 256, 512),
-    (5, "f32", "shared", 256, 512),
-    (16, "bf16", "shared", 1024, 2816),
-    (16, "bf16", None, 2048, 5632),
-    (7, "f32", None, 2048, 5632),
-    (16, "bf16", None, 2560, 6912),
-]
-
-
-DECODE_PATH_MARK = {"separate": "norm_quant_row", "xcd": "decode_step_xcd", "fused": "tgemv_q<"}
-
-
-def _decode_both(P, x, h_init, steps, gpu, modes=("separate", "xcd")):
-    """The same decode steps with each of the given decode implementations."""
-    import torch
-    mmf = _mmf()
-    res = {}
-    try:
-        for mode in modes:
-            mmf.set_decode_kernel(mode)
-            h = h_init.clone()
-            outs = []
-            for s_ in range(steps):
-                outs.append(mmf.layer_decode_step(P, x[s_], h))
-                path = mmf.last_path()
-                for other, mark in DECODE_PATH_MARK.items():
-                    assert (mark in path) == (other == mode), (mode, path)
-            torch.cuda.synchronize()
-            res[mode] = (torch.stack(outs), h)
-    finally:
-        mmf.set_decode_kernel("auto")
-    return res
-
-
-@pytest.mark.parametrize("b,act,gains,d,inner", XCD_CASES)
-def test_decode_xcd_kernel_matches_separate(gpu, b, act, gains, d, inner):
-    """One-XCD decode step against the separate kernels (which the stage checks cover): same bits."""
-    import torch
-    mmf = _mmf()
-    _, P = make_pair(d, inner, 900 + b, gpu, gains)
-    steps = 3
-    xs = synth.activations((steps, b, d), 901, act)
-    x = bf16_tensor(xs, gpu) if act == "bf16" else dev(xs, gpu)
-    h = dev(synth.activations((b, d), 902), gpu)
-    r = _decode_both(P, x, h, steps, gpu)
-    assert torch.equal(r["separate"][0], r["xcd"][0])
-    assert torch.equal(r["separate"][1], r["xcd"][1])
-    assert mmf.decode_expired_waits() == 0
-
-
-def test_decode_xcd_kernel_long_chain(gpu):
-    """64 chained steps at the 1.3B shape, batch 16: the state never leaves the bits of the separate path."""
-    import torch
-    mmf = _mmf()
-    d, inner, b, steps = 2048, 5632, 16, 64
-    _, P = make_pair(d, inner, 910, gpu)
-    x = bf16_tensor(synth.activations((steps, b, d), 911, "bf16"), gpu)
-    h = dev(synth.activations((b, d), 912), gpu)
-    r = _decode_both(P, x, h, steps, gpu)
-    assert torch.equal(r["separate"][0], r["xcd"][0])
-    assert torch.equal(r["separate"][1], r["xcd"][1])
-    assert mmf.decode_expired_waits() == 0
-
-
-def test_decode_xcd_kernel_graph_replays(gpu):
-    """A captured one-XCD decode step replayed several times, with eager work between the
-    replays, gives the eager result every time."""
-    import torch
-    mmf = _mmf()
-    d, inner, b = 1024, 2816, 16
-    _, P = make_pair(d, inner, 920, gpu)
-    x = bf16_tensor(synth.activations((b, d), 921, "bf16"), gpu)
-    h0 = dev(synth.activations((b, d), 922), gpu)
-    try:
-        mmf.set_decode_kernel("xcd")
-        _graph_replays(P, x, h0, "decode_step_xcd", gpu)
-    finally:
-        mmf.set_decode_kernel("auto")
-    assert mmf.decode_expired_waits() == 0
-
-
 def _graph_replays(P, x, h0, mark, gpu):
     """Captures one decode step and replays it with eager work between replays; every replay
     must give the eager result."""
@@ -867,7 +811,7 @@ def _graph_replays(P, x, h0, mark, gpu):
     ws = torch.empty(mmf.layer_workspace_size(P, b, 1), dtype=torch.uint8, device=gpu)
     out = torch.empty((b, d), dtype=x.dtype, device=gpu)
     h = h0.clone()
-    mmf.layer_decode_step(P, x, h, out=out, ws=ws)  # eager (the one-XCD kernel's placement check runs here)
+    mmf.layer_decode_step(P, x, h, out=out, ws=ws)  # eager
     assert mark in mmf.last_path()
     ref_out, ref_h = out.clone(), h.clone()
     g = torch.cuda.CUDAGraph()
@@ -1005,36 +949,37 @@ def test_decode_row_path_matches_separate(gpu, b, d, inner, act, gains):
 
 
 @pytest.mark.parametrize("b,act,gains", [(1, "f32", None), (1, "bf16", ("g_norm",)), (16, "f32", None),
-                                          (16, "bf16", None), (1, "f32", "shared"), (1, "bf16", "shared"),
-                                          (12, "bf16", "shared")])
+                                          (16, "bf16", None), (64, "bf16", None), (64, "f32", None),
+                                          (1, "f32", "shared"), (1, "bf16", "shared"), (12, "bf16", "shared")])
 def test_decode_default_path_end_to_end(gpu, b, act, gains):
-    """The default decode step at the 1.3B shape (the contractions that quantise their own rows)
-    against the free-running oracle, with g and z rounded to the activation type where the GPU
-    stores them: the state within fp32 rounding (it depends only on the first quantiser, whose
-    input is the same on both sides); the output within the activation type's tolerance and, as
-    a code flip in a later quantiser moves a row by a few quantisation steps at most, normwise
-    within 1e-3."""
+    """The default decode step at the 1.3B shape (at b <= 16 the contractions that quantise their
+    own rows) against the unmodified oracle run free: the state within fp32 rounding (it depends
+    only on the first quantiser, whose input is the same on both sides); the output elementwise
+    within the activation type's tolerance on every row without a code flip, normwise on all.
+    The probe that names the flipped rows does not change the kernels or their bits: the same
+    step without it gives the same output and state."""
     import torch
     mmf = _mmf()
     d, inner = 2048, 5632
     L, P = make_pair(d, inner, 1900 + b, gpu, gains)
     x = synth.activations((b, d), 1901, act)
     h0 = synth.activations((b, d), 1902)
+    xd = bf16_tensor(x, gpu) if act == "bf16" else dev(x, gpu)
     h = dev(h0, gpu)
-    out = mmf.layer_decode_step(P, bf16_tensor(x, gpu) if act == "bf16" else dev(x, gpu), h)
+    out = mmf.layer_decode_step(P, xd, h)
+    path_plain = mmf.last_path()
+    hp = dev(h0, gpu)
+    probe = mmf.LayerProbe(b, d, inner, gpu)
+    outp = mmf.layer_decode_step(P, xd, hp, probe=probe)
     torch.cuda.synchronize()
-    assert "tgemv_row<" in mmf.last_path(), mmf.last_path()
-    ref = decode_reference(L, x, h0, act)
-    if act == "f32":  # nothing is stored below fp32: the plain oracle step is the same reference
-        plain = oracle.layer_decode_step(L, x, h0)
-        assert np.array_equal(plain["out"], ref["out"]) and np.array_equal(plain["h"], ref["h"])
+    assert mmf.last_path() == path_plain, (mmf.last_path(), path_plain)
+    assert ("tgemv_row<" in path_plain) == (b <= 16), path_plain
+    assert torch.equal(out, outp) and torch.equal(h, hp)
+    pr = probe.host()
+    check_layer_stages(L, x[:, None, :], h0, pr, host(out), act)
+    ref = oracle.layer_decode_step(L, x, h0)
     assert_close(host(h), ref["h"], 1e-4, "h")
-    outg = host(out).astype(np.float64)
-    if act == "bf16":
-        assert_close(outg, ref["out"], 2e-2, "out")
-    # fp32: a few code flips at most; bf16: also the output's own rounding (about 1.1e-3 normwise)
-    rel = np.linalg.norm(outg - ref["out"]) / np.linalg.norm(ref["out"])
-    assert rel < (1e-3 if act == "f32" else 4e-3), rel
+    check_free_running(pr, ref["stages"], host(out), act)
 
 
 def test_decode_row_path_needs_few_rows_and_one_ifg_gain(gpu):
@@ -1057,103 +1002,61 @@ def test_decode_row_path_graph_replays(gpu, b):
     _graph_replays(P, x, h0, "tgemv_row<", gpu)
 
 
-def test_decode_xcd_kernel_unsupported_shapes(gpu):
-    """Forcing the one-XCD kernel where it does not apply is an error, never a silent fallback."""
-    mmf = _mmf()
-    _, P = make_pair(272, 1040, 930, gpu)
-    x = bf16_tensor(synth.activations((4, 272), 931, "bf16"), gpu)
-    h = dev(synth.activations((4, 272), 932), gpu)
-    try:
-        mmf.set_decode_kernel("xcd")
-        with pytest.raises(mmf.MMFError):
-            mmf.layer_decode_step(P, x, h)
-    finally:
-        mmf.set_decode_kernel("auto")
-    mmf.layer_decode_step(P, x, h)
-    assert "decode_step_xcd" not in mmf.last_path()
-
-
-FUSED_CASES = [
-    # b, act, gains, d, inner
-    (1, "bf16", None, 256, 512),
-    (5, "f32", "shared", 256, 512),
-    (16, "bf16", "shared", 1024, 2816),
-    (16, "bf16", None, 2048, 5632),
-    (1, "bf16", None, 2048, 5632),
-    (3, "f32", None, 2048, 2816),
-    (7, "f32", None, 2048, 5632),
-    (9, "bf16", None, 768, 1280),
-    (16, "bf16", None, 2560, 6912),
-    (12, "f32", "shared", 2048, 3072),
-]
-
-
-@pytest.mark.parametrize("b,act,gains,d,inner", FUSED_CASES)
-def test_decode_fused_matches_separate(gpu, b, act, gains, d, inner):
-    """The four-kernel decode step (each contraction quantises its own rows) against the eight
-    separate kernels (which the stage checks cover): same bits, over three chained steps."""
+@pytest.mark.timeout(900)
+def test_stack_1p3b_decode_step_24_layers_stage_fed(gpu):
+    """One decode step of the whole 24-layer 1.3B stack at batch 16 on the default path (the
+    graph the benchmark replays, here eager with a probe per layer): every layer is checked
+    stage by stage against the oracle fed with the GPU's input to that layer and its carried
+    state, and is checked free-running against the unmodified oracle step; its output is the
+    next layer's input."""
     import torch
-    _, P = make_pair(d, inner, 940 + b, gpu, gains)
-    steps = 3
-    xs = synth.activations((steps, b, d), 941, act)
-    x = bf16_tensor(xs, gpu) if act == "bf16" else dev(xs, gpu)
-    h = dev(synth.activations((b, d), 942), gpu)
-    r = _decode_both(P, x, h, steps, gpu, modes=("separate", "fused"))
-    assert torch.equal(r["separate"][0], r["fused"][0])
-    assert torch.equal(r["separate"][1], r["fused"][1])
+    mmf = _mmf()
+    d, inner, L_, b = 2048, 5632, 24, 16
+    cur_np = synth.activations((b, d), 3 * 10 + 2, "bf16")
+    cur = bf16_tensor(cur_np, gpu)
+    ws = None
+    flips = 0
+    for l in range(L_):
+        L, P = make_pair(d, inner, synth.layer_seed(3, l), gpu)
+        if ws is None:
+            ws = torch.empty(mmf.layer_workspace_size(P, b, 1), dtype=torch.uint8, device=gpu)
+        h0 = synth.activations((b, d), 3 * 100 + l)
+        h = dev(h0, gpu)
+        probe = mmf.LayerProbe(b, d, inner, gpu)
+        x_in = host(cur)
+        out = mmf.layer_decode_step(P, cur, h, probe=probe, ws=ws)
+        torch.cuda.synchronize()
+        assert "tgemv_row<" in mmf.last_path(), (l, mmf.last_path())
+        pr = probe.host()
+        check_layer_stages(L, x_in[:, None, :], h0, pr, host(out), "bf16")
+        assert np.array_equal(host(h), pr["h"])
+        flips += check_free_running(pr, oracle.layer_decode_step(L, x_in, h0)["stages"], host(out), "bf16",
+                                    "out of layer %d" % l)
+        cur = out
+        del L, P
+    # a flip needs a quantiser input within rounding of a half-integer decision point: a small
+    # share of the rows, never most of them
+    assert flips < L_ * b // 2, flips
 
 
-def test_decode_fused_long_chain(gpu):
-    """64 chained steps at the 1.3B shape, batch 16: the fused path never leaves the bits of the
-    separate path."""
+@pytest.mark.timeout(900)
+def test_stack_370m_prefill_24_layers_stage_fed(gpu):
+    """The 24-layer 370M-width prefill stack (bf16, chunked scan, the kernels the benchmark's
+    370M leg runs) at a reduced length: every block checked stage by stage against the oracle
+    fed with the GPU's input to that block; each output is the next block's input."""
     import torch
-    d, inner, b, steps = 2048, 5632, 16, 64
-    _, P = make_pair(d, inner, 950, gpu)
-    x = bf16_tensor(synth.activations((steps, b, d), 951, "bf16"), gpu)
-    h = dev(synth.activations((b, d), 952), gpu)
-    r = _decode_both(P, x, h, steps, gpu, modes=("separate", "fused"))
-    assert torch.equal(r["separate"][0], r["fused"][0])
-    assert torch.equal(r["separate"][1], r["fused"][1])
-
-
-def test_decode_fused_graph_replays(gpu):
-    """A captured fused decode step replayed several times gives the eager result every time."""
     mmf = _mmf()
-    _, P = make_pair(2048, 5632, 960, gpu)
-    x = bf16_tensor(synth.activations((16, 2048), 961, "bf16"), gpu)
-    h0 = dev(synth.activations((16, 2048), 962), gpu)
-    try:
-        mmf.set_decode_kernel("fused")
-        _graph_replays(P, x, h0, "tgemv_q<", gpu)
-    finally:
-        mmf.set_decode_kernel("auto")
-
-
-def test_decode_fused_unsupported_shapes(gpu):
-    """Forcing the fused kernels where they do not apply (b > 16, d > 3072, shapes off the 256
-    grid, distinct i/f/g gains) is an error, never a silent fallback."""
-    mmf = _mmf()
-    cases = [(16, "bf16", 1024, 2816, None, True), (17, "bf16", 1024, 2816, None, False),
-             (4, "f32", 2048, 5632, None, True), (4, "bf16", 3328, 256, None, False),
-             (4, "bf16", 272, 1040, None, False), (4, "bf16", 1024, 2816, "distinct", False)]
-    for b, act, d, inner, gains, fused in cases:
-        _, P = make_pair(d, inner, 970 + b, gpu, gains)
-        xs = synth.activations((b, d), 971, act)
-        x = bf16_tensor(xs, gpu) if act == "bf16" else dev(xs, gpu)
-        h = dev(synth.activations((b, d), 972), gpu)
-        mmf.layer_decode_step(P, x, h)
-        assert "tgemv_q<" not in mmf.last_path(), mmf.last_path()
-        if fused:
-            try:
-                mmf.set_decode_kernel("fused")
-                mmf.layer_decode_step(P, x, h)
-                assert "tgemv_q<" in mmf.last_path()
-            finally:
-                mmf.set_decode_kernel("auto")
-        else:
-            try:
-                mmf.set_decode_kernel("fused")
-                with pytest.raises(mmf.MMFError):
-                    mmf.layer_decode_step(P, x, h)
-            finally:
-                mmf.set_decode_kernel("auto")
+    d, inner, L_ = synth.SHAPES["370M"]
+    b, t = 2, 160
+    cur = bf16_tensor(synth.activations((b, t, d), 2 * 10 + 1, "bf16"), gpu)
+    for l in range(L_):
+        L, P = make_pair(d, inner, synth.layer_seed(2, l), gpu)
+        probe = mmf.LayerProbe(b * t, d, inner, gpu)
+        x_in = host(cur)
+        out, _ = mmf.layer_fwd(P, cur, None, want_h_last=True, mode="chunk", probe=probe)
+        torch.cuda.synchronize()
+        assert "tgemm" in mmf.last_path(), mmf.last_path()
+        check_layer_stages(L, x_in, None, probe.host(), host(out), "bf16")
+        cur = out
+        del L, P
+    assert np.all(np.isfinite(host(cur)))
