@@ -319,6 +319,27 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
                                  const mmf_layer_probe *probe, hipStream_t stream);
 
 /*
+ * mmf_layer_decode_step_noalloc -- mmf_layer_decode_step for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and the same bits, with
+ * the workspace taken from an 8 MiB array the library holds in device memory,
+ * one per GPU, until the process ends. The call allocates nothing and calls no
+ * allocating routine. The first call on a device looks up that device's array
+ * (hipGetSymbolAddress) and should not be made while the stream is being
+ * captured; later calls may be.
+ *  Arguments as mmf_layer_decode_step, without ws / ws_bytes.
+ *  Errors as mmf_layer_decode_step; WORKSPACE when mmf_layer_workspace_size(w,
+ *  b, 1) exceeds 8 MiB (about b = 64 at d = 4096, inner = 11008; b = 128 at the
+ *  1.3B shape).
+ *  Every call on a GPU shares that GPU's array and leaves its last contents
+ *  there (nothing in it needs to start at zero: every stage writes its part
+ *  before reading it): calls that overlap on one GPU (on different streams, or
+ *  from several threads without ordering) race and may return wrong results.
+ */
+mmf_status mmf_layer_decode_step_noalloc(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype act,
+                                         int64_t b, float *h, const mmf_layer_probe *probe, hipStream_t stream);
+
+/*
  * mmf_set_decode_kernel -- which implementation mmf_layer_decode_step uses,
  * process-wide: 0 = the fastest measured on MI355X (default: the
  * self-quantising contractions where they apply, else the separate kernels;

@@ -19,7 +19,7 @@ __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
     "ternary_pack", "bitlinear_fwd", "bitlinear_bwd", "embed", "greedy_head", "hgrn_scan_fwd", "hgrn_scan_bwd",
     "layer_fwd", "layer_bwd",
-    "layer_decode_step",
+    "layer_decode_step", "layer_decode_step_noalloc",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
     "set_decode_kernel", "DECODE_KERNELS", "hbm_ceiling",
 ]
@@ -32,7 +32,7 @@ SYMBOLS = [
     "mmf_bitlinear_bwd_workspace_size", "mmf_bitlinear_bwd",
     "mmf_embed", "mmf_greedy_head_workspace_size", "mmf_greedy_head",
     "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd", "mmf_hgrn_scan_bwd",
-    "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step",
+    "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step", "mmf_layer_decode_step_noalloc",
     "mmf_layer_bwd_workspace_size", "mmf_layer_bwd",
     "mmf_set_decode_kernel",
     "mmf_timing_enable", "mmf_timing_collect", "mmf_hbm_ceiling",
@@ -111,6 +111,8 @@ def load():
                                   ctypes.c_int, P, SZ, ctypes.POINTER(CLayerProbe), P]
     lib.mmf_layer_decode_step.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, P, P, SZ,
                                           ctypes.POINTER(CLayerProbe), P]
+    lib.mmf_layer_decode_step_noalloc.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, P,
+                                                  ctypes.POINTER(CLayerProbe), P]
     lib.mmf_layer_bwd_workspace_size.argtypes = [ctypes.POINTER(CLayerWeights), I64, I64, ctypes.POINTER(SZ)]
     lib.mmf_layer_bwd.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, I64, P, P, ctypes.c_int,
                                   ctypes.POINTER(CLayerGrads), P, SZ, P]
@@ -497,3 +499,18 @@ def layer_decode_step(params: LayerParams, x, h, probe: Optional[LayerProbe] = N
                                      _stream()))
     return out
 
+
+def layer_decode_step_noalloc(params: LayerParams, x, h, out, probe: Optional[LayerProbe] = None):
+    """layer_decode_step with the library's own per-device scratch (mmf_layer_decode_step_noalloc):
+    no workspace argument, nothing allocated by the call; `out` [b, d] must be given."""
+    torch = _torch()
+    if x.dim() != 2 or not x.is_contiguous() or not h.is_contiguous() or h.dtype != torch.float32:
+        raise ValueError("x must be contiguous [b, d]; h contiguous float32 [b, d]")
+    if out is None or out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like x")
+    b = x.shape[0]
+    cw = params.c()
+    cp = probe.c() if probe is not None else None
+    _check(load().mmf_layer_decode_step_noalloc(ctypes.byref(cw), _ptr(x), _ptr(out), _dtype_code(x.dtype), b,
+                                                _ptr(h), ctypes.byref(cp) if cp is not None else None, _stream()))
+    return out

@@ -15,6 +15,7 @@
 #include <vector>
 #include <cstring>
 #include <atomic>
+#include <mutex>
 
 #include "mmf.h"
 #include "launch.hpp"
@@ -456,6 +457,41 @@ mmf_status decode_step_run(const mmf_layer_weights *w, const void *x, void *out,
     return r;
 }
 
+// ------------------------------------------------- decode without allocation --
+// The workspace of mmf_layer_decode_step_noalloc: one array per device, held
+// until the process ends. Host code never uses the array's name as an address
+// (on the host it is only a stand-in for the symbol): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoallocScratchBytes = size_t(8) << 20;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// This device's copy of the scratch array, looked up on the first call on the device.
+mmf_status scratch_for_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MMF_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MMF_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MMF_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MMF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -853,6 +889,23 @@ mmf_status mmf_layer_decode_step(const mmf_layer_weights *w, const void *x, void
         return fail(MMF_ERR_INVALID_ARG, "x, out and h must be 16-byte aligned");
     if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
         return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    return decode_step_run(w, x, out, actt, b, h, ws, probe, stream);
+}
+
+mmf_status mmf_layer_decode_step_noalloc(const mmf_layer_weights *w, const void *x, void *out, mmf_dtype actt,
+                                         int64_t b, float *h, const mmf_layer_probe *probe, hipStream_t stream) {
+    size_t need = 0;
+    mmf_status st = mmf_layer_workspace_size(w, b, 1, &need);
+    if (st != MMF_OK) return st;
+    if (!valid_dtype(actt)) return fail(MMF_ERR_INVALID_ARG, "bad activation dtype");
+    if (b > 0 && (!x || !out || !h)) return fail(MMF_ERR_INVALID_ARG, "x, out and h must be non-NULL");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(h))
+        return fail(MMF_ERR_INVALID_ARG, "x, out and h must be 16-byte aligned");
+    if (need > kNoallocScratchBytes)
+        return fail(MMF_ERR_WORKSPACE, "decode step needs %zu bytes of scratch, beyond the %zu the library holds "
+                    "(use mmf_layer_decode_step with a workspace)", need, kNoallocScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != MMF_OK) return st;
     return decode_step_run(w, x, out, actt, b, h, ws, probe, stream);
 }
 
