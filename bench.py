@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--extras", type=int, default=1,
                     help="0 skips the figures measured outside the timed steps (the other configs, the "
                          "measured HBM ceiling, derivatives, generation)")
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "prefill_b8", "ceiling"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "prefill_b8", "ceiling", "bwd"],
                     help="run one config leg alone and print its JSON (for profiling a config)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (for scaling HBM counters)")
@@ -576,6 +576,14 @@ def run_only(args):
         res = leg_decode(mmf, torch, dev)
     elif args.only == "c5":
         res = leg_c5(mmf, torch, dev, cpu=cpu)
+    elif args.only == "bwd":
+        from ternary_weight_matmul_amd import synth
+        d, inner, _ = synth.SHAPES["1.3B"]
+        layer = device_layers(mmf, torch, d, inner, 1, 3, dev)[0]
+        res = dict(scan_bwd=measure_scan_bwd(mmf, torch, 16, 2048, d, dev),
+                   bitlinear_bwd=measure_bitlinear_bwd(mmf, torch, layer.o, 16 * 2048, dev),
+                   bitlinear_bwd_gate=measure_bitlinear_bwd(mmf, torch, layer.gate, 16 * 2048, dev),
+                   layer_bwd=measure_layer_bwd(mmf, torch, layer, 16, 2048, d, dev))
     else:
         res = hbm_ceilings(mmf, torch, dev)
     print(json.dumps({"leg": args.only, **res}), flush=True)
@@ -858,7 +866,7 @@ def measure_bitlinear_bwd(mmf, torch, lin, m: int, dev, launches: int = 5) -> di
     return dict(shape="m=%d n=%d k=%d" % (m, lin.n, lin.k), us_per_call=round(total_ms * 1000, 1),
                 kernels_us=kernels, gemm_achieved=round(tf, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                 gemm_frac=round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                note="products through rocBLAS (bf16, fp32 accumulation); the rest hand-written")
+                note="hand-written bf16 products (fp32 accumulation), operand layouts and RMSNorm derivative")
 
 
 def measure_layer_bwd(mmf, torch, layer, b: int, t: int, d: int, dev, launches: int = 2) -> dict:
@@ -880,7 +888,7 @@ def measure_layer_bwd(mmf, torch, layer, b: int, t: int, d: int, dev, launches: 
     del x, dout, res
     return dict(shape="b=%d t=%d d=%d" % (b, t, d), ms_per_call=round(ms, 2),
                 tokens_per_s=round(b * t / (ms / 1000), 1),
-                note="forward recomputed inside; products of the derivative through rocBLAS (bf16)")
+                note="forward recomputed inside; hand-written bf16 products of the derivative")
 
 
 def measure_generate(mmf, torch, layers, b: int, d: int, dev, seed: int, vocab: int = 32000,

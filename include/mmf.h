@@ -173,11 +173,11 @@ mmf_status mmf_bitlinear_fwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
  *  x : [m][k] in dtype xt (the forward's input); dy : [m][n] in dtype dyt;
  *  dx : [m][k] in dtype dxt or NULL; dw : [n][k] fp32 or NULL; dgain : [k] fp32
  *  or NULL (also without a gain: the derivative at gain = 1). The codes are
- *  recomputed from x with the forward's quantiser. The two products are bf16
- *  GEMMs with fp32 accumulation (rocBLAS): t and q are exact in bf16, an fp32 dy
- *  and q / s are rounded to bf16. Outputs do not alias inputs. m may be 0
- *  (dw and dgain are zero). Errors: INVALID_ARG, UNSUPPORTED (n % 8, k > 8192),
- *  WORKSPACE, HIP (also a rocBLAS failure, named in mmf_last_error).
+ *  recomputed from x with the forward's quantiser. The two products are
+ *  hand-written bf16 GEMMs with fp32 accumulation: t and q are exact in bf16;
+ *  for du an fp32 dy is rounded to bf16, for dw each dy / s is (one rounding of
+ *  the product). Outputs do not alias inputs. m may be 0 (dw and dgain are
+ *  zero). Errors: INVALID_ARG, UNSUPPORTED (n % 8, k > 8192), WORKSPACE, HIP.
  */
 mmf_status mmf_bitlinear_bwd_workspace_size(int64_t m, const mmf_ternary_weight *w, mmf_dtype dyt,
                                             size_t *bytes);

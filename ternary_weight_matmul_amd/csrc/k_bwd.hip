@@ -10,63 +10,13 @@
 //   dx_k = r gain_k du_k - (r^3 / K) x_k sum_j x_j gain_j du_j,
 //   dgain_k = sum over rows of du_k x_k r.
 //
-// The two products are plain dense contractions once the operands are
-// expanded: t is exact in bf16 ({-1, 0, +1}), the codes q are exact in bf16, so
-// they run as bf16 GEMMs with fp32 accumulation in the vendor library
-// (rocBLAS); the factor 1 / sw is applied afterwards in fp32. What is not a
-// plain product -- the expansion of the 2-bit words, the scaled codes, the
-// RMSNorm derivative and the gain's column sums -- is the kernels below.
-#include <rocblas/rocblas.h>
-
-#include <mutex>
-
+// The two products run as hand-written bf16 GEMMs (k_gemm_bf16.hip); what is
+// not a product -- fp32 -> bf16, the RMSNorm derivative and the gain's column
+// sums -- is the kernels below.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace mmf {
-
-// bf16 bit patterns of t = c - 1 for the offset codes c = 0, 1, 2
-__device__ __forceinline__ uint32_t ternary_bf16(uint32_t c) { return c == 0 ? 0xBF80u : (c == 2 ? 0x3F80u : 0u); }
-
-// packed [n][k/16] -> bf16 t [n][k]. Word w of a row holds k = 16 w + 4 j + b in
-// bits 8 b + 2 j (b, j = 0..3); one thread expands one word into two 16-byte stores.
-__global__ __launch_bounds__(256) void expand_ternary_kernel(const uint32_t *__restrict__ packed, int64_t words,
-                                                             uint16_t *__restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= words) return;
-    const uint32_t w = packed[i];
-    uint32_t v[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int k0 = 2 * p, k1 = 2 * p + 1;  // k within the word: j = k / 4, b = k % 4
-        const uint32_t c0 = (w >> (8 * (k0 & 3) + 2 * (k0 >> 2))) & 3u;
-        const uint32_t c1 = (w >> (8 * (k1 & 3) + 2 * (k1 >> 2))) & 3u;
-        v[p] = ternary_bf16(c0) | (ternary_bf16(c1) << 16);
-    }
-    uint4 *o = reinterpret_cast<uint4 *>(out + 16 * i);
-    o[0] = make_uint4(v[0], v[1], v[2], v[3]);
-    o[1] = make_uint4(v[4], v[5], v[6], v[7]);
-}
-
-// u^ = q / s (correctly rounded, then to bf16) for codes [m][k]; 8 codes per thread
-__global__ __launch_bounds__(256) void scaled_codes_kernel(const int8_t *__restrict__ q, const float *__restrict__ s,
-                                                           int64_t m, int k, uint16_t *__restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 8 codes
-    const int64_t per_row = k / 8;
-    if (i >= m * per_row) return;
-    const int64_t row = i / per_row;
-    const float sr = s[row];
-    const uint2 raw = reinterpret_cast<const uint2 *>(q)[i];
-    uint32_t v[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t word = p < 2 ? raw.x : raw.y;
-        const int sh = 16 * (p & 1);
-        const float a = (float)(int8_t)((word >> sh) & 0xff), b = (float)(int8_t)((word >> (sh + 8)) & 0xff);
-        v[p] = (uint32_t)f32_to_bf16(__fdiv_rn(a, sr)) | ((uint32_t)f32_to_bf16(__fdiv_rn(b, sr)) << 16);
-    }
-    reinterpret_cast<uint4 *>(out)[i] = make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 // fp32 -> bf16 (round to nearest even), 4 per thread
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ x, int64_t n4, uint16_t *__restrict__ out) {
@@ -384,20 +334,6 @@ static int nv_bucket(int k) {
 
 bool rmsnorm_bwd_supported(int k) { return k % 8 == 0 && nv_bucket(k) <= 8; }
 
-hipError_t launch_expand_ternary(const uint32_t *packed, int n, int k, uint16_t *out, hipStream_t st) {
-    const int64_t words = (int64_t)n * (k / 16);
-    if (words == 0) return hipSuccess;
-    launch_k(expand_ternary_kernel, (unsigned)((words + 255) / 256), 256, 0, st, packed, words, out);
-    return hipGetLastError();
-}
-
-hipError_t launch_scaled_codes(const int8_t *q, const float *s, int64_t m, int k, uint16_t *out, hipStream_t st) {
-    const int64_t n8 = m * (k / 8);
-    if (n8 == 0) return hipSuccess;
-    launch_k(scaled_codes_kernel, (unsigned)((n8 + 255) / 256), 256, 0, st, q, s, m, k, out);
-    return hipGetLastError();
-}
-
 hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *out, hipStream_t st) {
     const int64_t n4 = n / 4;
     if (n4 == 0) return hipSuccess;
@@ -496,51 +432,6 @@ hipError_t launch_gain_reduce(const float *gpart, int nblk, int k, float *part2,
     const int splits = gain_reduce_splits(nblk);
     launch_k(gain_reduce_kernel, dim3((unsigned)((k + 63) / 64), (unsigned)splits), 256, 0, st, gpart, nblk, k, part2);
     launch_k(gain_final_kernel, (unsigned)((k + 255) / 256), 256, 0, st, part2, splits, k, dgain);
-    return hipGetLastError();
-}
-
-// One rocBLAS handle per device, made on first use.
-static rocblas_handle blas_handle(std::string *err) {
-    static std::mutex mu;
-    static rocblas_handle handles[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-        *err = "no current device";
-        return nullptr;
-    }
-    std::lock_guard<std::mutex> lock(mu);
-    if (!handles[dev]) {
-        rocblas_handle h = nullptr;
-        const rocblas_status s = rocblas_create_handle(&h);
-        if (s != rocblas_status_success) {
-            *err = std::string("rocblas_create_handle: ") + rocblas_status_to_string(s);
-            return nullptr;
-        }
-        handles[dev] = h;
-    }
-    return handles[dev];
-}
-
-// Row-major C[rows][cols] (fp32) = A B with bf16 operands, fp32 accumulation:
-// A is [rows][inner] (trans_a: stored as [inner][rows]), B is [inner][cols].
-// rocBLAS is column-major, so it computes C^T = B^T A^T.
-hipError_t gemm_bf16_f32(const uint16_t *a, bool trans_a, const uint16_t *b, int64_t rows, int64_t cols, int64_t inner,
-                         float *c, hipStream_t st, std::string *err) {
-    if (rows == 0 || cols == 0) return hipSuccess;
-    rocblas_handle h = blas_handle(err);
-    if (!h) return hipErrorUnknown;
-    rocblas_status s = rocblas_set_stream(h, st);
-    const float one = 1.0f, zero = 0.0f;
-    if (s == rocblas_status_success)
-        s = rocblas_gemm_ex(h, rocblas_operation_none, trans_a ? rocblas_operation_transpose : rocblas_operation_none,
-                            (rocblas_int)cols, (rocblas_int)rows, (rocblas_int)inner, &one, b, rocblas_datatype_bf16_r,
-                            (rocblas_int)cols, a, rocblas_datatype_bf16_r, (rocblas_int)(trans_a ? rows : inner), &zero,
-                            c, rocblas_datatype_f32_r, (rocblas_int)cols, c, rocblas_datatype_f32_r, (rocblas_int)cols,
-                            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    if (s != rocblas_status_success) {
-        *err = std::string("rocblas_gemm_ex: ") + rocblas_status_to_string(s);
-        return hipErrorUnknown;
-    }
     return hipGetLastError();
 }
 

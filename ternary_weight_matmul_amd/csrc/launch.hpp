@@ -113,14 +113,24 @@ hipError_t launch_scan_bwd(const float *f, const float *h, const float *h0, cons
                            float *dx, float *df, float *dh0, int64_t b, int64_t t, int64_t d, int plan,
                            hipStream_t stream, std::string *path);
 
-// Derivative of FusedBitLinear (k_bwd.hip): bf16 expansion of the ternary
-// words (t in {-1, 0, +1}, [n][k]), bf16 scaled codes q / s ([m][k]), fp32 ->
-// bf16, the RMSNorm derivative (du = du_raw / sw; optional dx, per-workgroup
-// partial sums of the gain's derivative) and their reduction, and a bf16 GEMM
-// with fp32 output through rocBLAS (row-major C[rows][cols] = A B, A given as
-// [rows][inner] or, with trans_a, as [inner][rows]).
-hipError_t launch_expand_ternary(const uint32_t *packed, int n, int k, uint16_t *out, hipStream_t st);
-hipError_t launch_scaled_codes(const int8_t *q, const float *s, int64_t m, int k, uint16_t *out, hipStream_t st);
+// Derivative of FusedBitLinear: its two products as hand-written bf16 GEMMs
+// (k_gemm_bf16.hip): C[m][n] (fp32, row stride ldc) = A[m][k] B[n][k]^T with bf16
+// operands whose rows are k-contiguous (strides lda, ldb elements; k % 8 == 0, rows
+// 16-byte aligned); the operand layouts: t^T [k][ldn] bf16 from the packed words
+// (columns n..ldn-1 zero), and out [cols][ldm] bf16 = the transpose of src
+// [rows][cols] (src_kind 0: fp32 scaled by 1 / s per row, 1: bf16 scaled, 2:
+// int8 codes as they are; columns rows..ldm-1 zero; ldm % 8 == 0).
+// With part non-NULL a product of few tiles may be split along k: part must hold
+// gemm_bf16_splits(m, n, k) * m * ldc floats (the per-split partial blocks).
+int gemm_bf16_splits(int m, int n, int k);
+hipError_t launch_gemm_bf16_nt(const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb, int m, int n, int k,
+                               float *c, int64_t ldc, float *part, hipStream_t st);
+hipError_t launch_expand_ternary_t(const uint32_t *packed, int n, int k, uint16_t *out, int ldn, hipStream_t st);
+hipError_t launch_transpose_bf16(const void *src, int src_kind, const float *s, int64_t rows, int cols, uint16_t *out,
+                                 int64_t ldm, hipStream_t st);
+// The rest of the derivative (k_bwd.hip): fp32 -> bf16, the RMSNorm derivative
+// (du = du_raw / sw; optional dx, per-workgroup partial sums of the gain's
+// derivative) and their reduction.
 hipError_t launch_to_bf16(const float *x, int64_t n, uint16_t *out, hipStream_t st);
 int rmsnorm_bwd_rows(int64_t m);
 bool rmsnorm_bwd_supported(int k);
@@ -143,8 +153,6 @@ hipError_t launch_sum(const void *a, ActType at, const float *b, const float *c,
                       hipStream_t st);
 hipError_t launch_gnorm_bwd(const float *h, const void *g, ActType gt, const float *du, const float *w, float eps,
                             int64_t m, int d, float *dh, float *dg, float *wpart, hipStream_t st);
-hipError_t gemm_bf16_f32(const uint16_t *a, bool trans_a, const uint16_t *b, int64_t rows, int64_t cols, int64_t inner,
-                         float *c, hipStream_t st, std::string *err);
 
 // Measured HBM ceilings (k_ceiling.hip): a streaming read of `bytes` (a
 // multiple of 16; one word per workgroup to sink, ceiling_blocks() words) and

@@ -573,42 +573,61 @@ mmf_status mmf_bitlinear_fwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
 struct BitlinearBwdWs {
     int8_t *q;
     float *s;
-    uint16_t *t16, *dy16, *u16;
-    float *du, *gpart, *gpart2;
+    uint16_t *tT, *dy16, *dyT, *qT;
+    float *du, *gpart, *gpart2, *split;
 };
 
-size_t bitlinear_bwd_plan(Carver &c, int64_t m, int n, int k, mmf_dtype dyt, BitlinearBwdWs *o) {
+// rows of the dW product's operands, zero-padded to whole 16-byte pieces
+int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }
+
+// floats of the dW product's per-split partial blocks for an n x k weight over m rows (0: no split)
+size_t dw_split_floats(int64_t m, int n, int k) {
+    const int sp = m > 0 ? gemm_bf16_splits(n, k, (int)pad8(m)) : 1;
+    return sp > 1 ? (size_t)sp * n * k : 0;
+}
+
+size_t bitlinear_bwd_plan(Carver &c, int64_t m, int n, int k, mmf_dtype dyt, BitlinearBwdWs *o,
+                          size_t split_floats = SIZE_MAX) {
     BitlinearBwdWs w;
     w.q = c.take<int8_t>((size_t)m * k);
     w.s = c.take<float>((size_t)m);
-    w.t16 = c.take<uint16_t>((size_t)n * k);
+    w.tT = c.take<uint16_t>((size_t)n * k);
     w.dy16 = dyt == MMF_F32 ? c.take<uint16_t>((size_t)m * n) : nullptr;
-    w.u16 = c.take<uint16_t>((size_t)m * k);
+    w.dyT = c.take<uint16_t>((size_t)n * pad8(m));
+    w.qT = c.take<uint16_t>((size_t)k * pad8(m));
     w.du = c.take<float>((size_t)m * k);
     const int64_t nblk = m > 0 ? (m + rmsnorm_bwd_rows(m) - 1) / rmsnorm_bwd_rows(m) : 0;
     w.gpart = c.take<float>((size_t)nblk * k);
     w.gpart2 = c.take<float>((size_t)gain_reduce_splits((int)nblk) * k);
+    // partial blocks of the dW product when it is split along the rows
+    if (split_floats == SIZE_MAX) split_floats = dw_split_floats(m, n, k);
+    w.split = split_floats ? c.take<float>(split_floats) : nullptr;
     if (o) *o = w;
     return c.off;
 }
 
 // One FusedBitLinear derivative (m > 0) on a carved workspace sized for at
-// least (m, n, k) with an fp32 dy: codes from the forward's quantiser, bf16
-// products through rocBLAS, the RMSNorm derivative and the gain's sums.
+// least (m, n, k) with an fp32 dy: codes from the forward's quantiser, the two
+// bf16 products (du before 1 / sw: dy t over n; dW: (dy / s)^T q over the rows),
+// the RMSNorm derivative and the gain's sums.
 hipError_t bitlinear_bwd_run(const void *x, ActType xt, int64_t m, const mmf_ternary_weight *w, float eps,
                              const void *dy, ActType dyt, void *dx, ActType dxt, float *dw, float *dgain,
-                             const BitlinearBwdWs &B, hipStream_t stream, std::string *path, std::string *err) {
+                             const BitlinearBwdWs &B, hipStream_t stream, std::string *path) {
     const int n = w->n, k = w->k;
     hipError_t e = t_norm_quant(x, xt, m, k, w->norm_w, eps, B.q, B.s, nullptr, stream, path);
-    const uint16_t *dy16 = dyt == ACT_F32 ? B.dy16 : static_cast<const uint16_t *>(dy);
-    if (e == hipSuccess && dyt == ACT_F32)
-        e = timed("to_bf16", m, n, n, stream,
-                  [&] { return launch_to_bf16(static_cast<const float *>(dy), m * n, B.dy16, stream); });
     if (e == hipSuccess && (dx || dgain)) {
-        e = timed("expand_ternary", n, k, k, stream, [&] { return launch_expand_ternary(w->packed, n, k, B.t16, stream); });
-        if (e == hipSuccess)  // du (before 1 / sw) = dy t
+        const uint16_t *dy16 = static_cast<const uint16_t *>(dy);
+        if (dyt == ACT_F32) {
+            e = timed("to_bf16", m, n, n, stream,
+                      [&] { return launch_to_bf16(static_cast<const float *>(dy), m * n, B.dy16, stream); });
+            dy16 = B.dy16;
+        }
+        if (e == hipSuccess)
+            e = timed("expand_ternary_t", n, k, k, stream,
+                      [&] { return launch_expand_ternary_t(w->packed, n, k, B.tT, n, stream); });
+        if (e == hipSuccess)  // du (before 1 / sw) [m][k] = dy [m][n] t^T [k][n]^T
             e = timed("gemm_bf16<du>", m, k, n, stream,
-                      [&] { return gemm_bf16_f32(dy16, false, B.t16, m, k, n, B.du, stream, err); });
+                      [&] { return launch_gemm_bf16_nt(dy16, n, B.tT, n, (int)m, k, n, B.du, k, nullptr, stream); });
         if (e == hipSuccess)
             e = timed("rmsnorm_bwd", m, k, k, stream, [&] {
                 return launch_rmsnorm_bwd(x, xt, B.du, w->norm_w, w->mu, eps, m, k, dx, dxt, dgain ? B.gpart : nullptr,
@@ -620,14 +639,21 @@ hipError_t bitlinear_bwd_run(const void *x, ActType xt, int64_t m, const mmf_ter
             e = timed("gain_reduce", nblk, k, k, stream,
                       [&] { return launch_gain_reduce(B.gpart, nblk, k, B.gpart2, dgain, stream); });
         }
-        *path += "expand_ternary;gemm_bf16<du>;rmsnorm_bwd;" + std::string(dgain ? "gain_reduce;" : "");
+        *path += std::string(dyt == ACT_F32 ? "to_bf16;" : "") + "expand_ternary_t;gemm_bf16<du>;rmsnorm_bwd;" +
+                 (dgain ? "gain_reduce;" : "");
     }
     if (e == hipSuccess && dw) {
-        e = timed("scaled_codes", m, k, k, stream, [&] { return launch_scaled_codes(B.q, B.s, m, k, B.u16, stream); });
-        if (e == hipSuccess)  // dW = dy^T (q / s)
-            e = timed("gemm_bf16<dw>", n, k, m, stream,
-                      [&] { return gemm_bf16_f32(dy16, true, B.u16, n, k, m, dw, stream, err); });
-        *path += "scaled_codes;gemm_bf16<dw>;";
+        const int64_t mp = pad8(m);
+        e = timed("transpose_bf16<dy/s>", m, n, n, stream, [&] {
+            return launch_transpose_bf16(dy, dyt == ACT_F32 ? 0 : 1, B.s, m, n, B.dyT, mp, stream);
+        });
+        if (e == hipSuccess)
+            e = timed("transpose_bf16<q>", m, k, k, stream,
+                      [&] { return launch_transpose_bf16(B.q, 2, nullptr, m, k, B.qT, mp, stream); });
+        if (e == hipSuccess)  // dW [n][k] = (dy / s)^T [n][m] (q^T [k][m])^T
+            e = timed("gemm_bf16<dw>", n, k, (int)mp, stream,
+                      [&] { return launch_gemm_bf16_nt(B.dyT, mp, B.qT, mp, n, k, (int)mp, dw, k, B.split, stream); });
+        *path += "transpose_bf16<dy/s>;transpose_bf16<q>;gemm_bf16<dw>;";
     }
     return e;
 }
@@ -672,9 +698,8 @@ mmf_status mmf_bitlinear_bwd(const void *x, mmf_dtype xt, int64_t m, const mmf_t
     Carver c(ws);
     BitlinearBwdWs B;
     bitlinear_bwd_plan(c, m, n, k, dyt, &B);
-    std::string path, err;
-    hipError_t e = bitlinear_bwd_run(x, act(xt), m, w, eps, dy, act(dyt), dx, act(dxt), dw, dgain, B, stream, &path, &err);
-    if (e != hipSuccess && !err.empty()) return fail(MMF_ERR_HIP, "mmf_bitlinear_bwd: %s", err.c_str());
+    std::string path;
+    hipError_t e = bitlinear_bwd_run(x, act(xt), m, w, eps, dy, act(dyt), dx, act(dxt), dw, dgain, B, stream, &path);
     mmf_status r = hip_status(e, "mmf_bitlinear_bwd");
     if (r == MMF_OK) g_path = path;
     return r;
@@ -951,7 +976,13 @@ size_t layer_bwd_plan(Carver &c, const mmf_layer_weights *w, int64_t b, int64_t 
     L.scan = c.take<char>(scan_workspace_bytes(b, w->d, chunks));
     const int nmax = 2 * w->inner > w->d ? 2 * w->inner : w->d;
     const int kmax = w->inner > w->d ? w->inner : w->d;
-    bitlinear_bwd_plan(c, m, nmax, kmax, MMF_F32, &L.blin);
+    const mmf_ternary_weight *tw[6] = {&w->i, &w->f, &w->g, &w->o, &w->gate, &w->down};
+    size_t split_floats = 0;  // the largest split product of the six projections
+    for (const mmf_ternary_weight *p : tw) {
+        const size_t f = dw_split_floats(m, p->n, p->k);
+        if (f > split_floats) split_floats = f;
+    }
+    bitlinear_bwd_plan(c, m, nmax, kmax, MMF_F32, &L.blin, split_floats);
     if (o) *o = L;
     return c.off;
 }
@@ -987,7 +1018,7 @@ mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *
     if (m > 0 && (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)))
         return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
     const mmf_ternary_weight *tw[6] = {&w->i, &w->f, &w->g, &w->o, &w->gate, &w->down};
-    std::string path, err;
+    std::string path;
     hipError_t e = hipSuccess;
     if (m == 0) {
         // no tokens: h_last is h0, and every weight and gain sees nothing
@@ -1046,15 +1077,15 @@ mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *
     // ---- derivatives, last step first
     if (e == hipSuccess)  // down_proj: dz
         e = bitlinear_bwd_run(L.z, ACT_F32, m, &w->down, eps, dout, at, L.dz, ACT_F32, gr->dw[5], gr->dgain[5],
-                              L.blin, stream, &path, &err);
+                              L.blin, stream, &path);
     if (e == hipSuccess) e = launch_glu_bwd(L.dz, L.ab, m, inner, L.dab, stream);
     if (e == hipSuccess)  // gate_proj: into x1
         e = bitlinear_bwd_run(L.x1, ACT_F32, m, &w->gate, eps, L.dab, ACT_F32, L.dx1g, ACT_F32, gr->dw[4], gr->dgain[4],
-                              L.blin, stream, &path, &err);
+                              L.blin, stream, &path);
     if (e == hipSuccess) e = launch_sum(dout, at, L.dx1g, nullptr, nullptr, md, L.dx1, stream);  // + the residual
     if (e == hipSuccess)  // o_proj: du
         e = bitlinear_bwd_run(L.u, ACT_F32, m, &w->o, eps, L.dx1, ACT_F32, L.du, ACT_F32, gr->dw[3], gr->dgain[3], L.blin,
-                              stream, &path, &err);
+                              stream, &path);
     if (e == hipSuccess)  // g_norm: dh, dg^ and the weight's partial sums
         e = launch_gnorm_bwd(L.h, L.g, ACT_F32, L.du, w->g_norm_w, eps, m, d, L.dh, L.dg,
                              gr->dg_norm_w ? L.wpart : nullptr, stream);
@@ -1070,9 +1101,8 @@ mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *
     float *dxq[3] = {L.dxi, L.dxf, L.dxg};
     for (int q = 0; q < 3 && e == hipSuccess; ++q)
         e = bitlinear_bwd_run(x, at, m, tw[q], eps, dpre[q], ACT_F32, dxq[q], ACT_F32, gr->dw[q], gr->dgain[q], L.blin,
-                              stream, &path, &err);
+                              stream, &path);
     if (e == hipSuccess) e = launch_sum(L.dx1, ACT_F32, L.dxi, L.dxf, L.dxg, md, gr->dx, stream);
-    if (e != hipSuccess && !err.empty()) return fail(MMF_ERR_HIP, "mmf_layer_bwd: %s", err.c_str());
     mmf_status r = hip_status(e, "mmf_layer_bwd");
     if (r == MMF_OK) g_path = path;
     return r;

@@ -363,7 +363,7 @@ def test_layer_bwd_parity(gpu, d, inner, b, t, act, gains, mode):
     """Every derivative of the block (straight-through quantisers) against the oracle's chain,
     evaluated at the GPU forward's own stage values (a probed forward call runs the kernels the
     derivative's recompute runs), so that both sides' quantisers see the same inputs. The
-    products run in bf16 (rocBLAS): the bf16 bar applies (rtol 2e-2)."""
+    products run in bf16: the bf16 bar applies (rtol 2e-2)."""
     mmf = _mmf()
     L, P = make_pair(d, inner, 860 + t, gpu, gains)
     x = synth.activations((b, t, d), 861, act)
