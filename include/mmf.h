@@ -378,18 +378,20 @@ mmf_status mmf_timing_enable(int on);
 mmf_status mmf_timing_collect(mmf_kernel_timing *out, int32_t capacity, int32_t *count);
 
 /*
- * mmf_hbm_ceiling -- measured HBM roof (measurement support): streams `bytes`
- * of device memory in the access pattern of the library's bandwidth-bound
- * kernels (16-byte loads by consecutive lanes, four in flight per lane,
- * 2048 workgroups of 256 threads).
- *  mode 0 : read src only (the packed-weight stream of a GEMV); dst receives
- *           one uint32 per workgroup (at least MMF_HBM_CEILING_SINK_BYTES).
- *  mode 1 : copy src to dst (a read stream and a write stream, as the scan).
+ * mmf_hbm_ceiling -- measured HBM roof (measurement support): streams device
+ * memory in the access pattern of the library's bandwidth-bound kernels
+ * (16-byte loads by consecutive lanes, eight in flight per lane, 8192
+ * workgroups of 256 threads, non-temporal).
+ *  mode 0 : read `bytes` of src (the packed-weight stream of a GEMV); dst
+ *           receives one uint32 per workgroup (MMF_HBM_CEILING_SINK_BYTES).
+ *  mode 1 : copy `bytes` from src to dst (one read and one write stream).
+ *  mode 2 : dst = src[0:bytes) ^ src[bytes:2*bytes) (two read streams and one
+ *           write stream: the scan's pattern); src holds 2 * bytes.
  *  bytes % 16 == 0; src and dst 16-byte aligned and not overlapping.
  *  Timed like every other launch while mmf_timing_enable is on ("stream_read",
- *  "stream_copy"). Errors: INVALID_ARG.
+ *  "stream_copy", "stream_2r1w"). Errors: INVALID_ARG.
  */
-#define MMF_HBM_CEILING_SINK_BYTES 8192
+#define MMF_HBM_CEILING_SINK_BYTES 32768
 mmf_status mmf_hbm_ceiling(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -158,10 +158,12 @@ def timing_collect() -> list:
 
 
 def hbm_ceiling(src, dst, mode: str = "read"):
-    """Measured HBM roof (mmf_hbm_ceiling): stream src (read) or copy it into dst (copy).
-    For "read", dst is a sink of at least 8192 bytes."""
+    """Measured HBM roof (mmf_hbm_ceiling): "read" streams src (dst: a sink of at least 32768
+    bytes); "copy" copies src into dst; "2r1w" writes dst = first half of src ^ second half
+    (src twice dst's size)."""
     n = src.numel() * src.element_size()
-    _check(load().mmf_hbm_ceiling(0 if mode == "read" else 1, _ptr(src), _ptr(dst), n, _stream()))
+    m = {"read": 0, "copy": 1, "2r1w": 2}[mode]
+    _check(load().mmf_hbm_ceiling(m, _ptr(src), _ptr(dst), n // 2 if m == 2 else n, _stream()))
 
 
 def _check(status: int):

@@ -155,11 +155,11 @@ hipError_t launch_gnorm_bwd(const float *h, const void *g, ActType gt, const flo
                             int64_t m, int d, float *dh, float *dg, float *wpart, hipStream_t st);
 
 // Measured HBM ceilings (k_ceiling.hip): a streaming read of `bytes` (a
-// multiple of 16; one word per workgroup to sink, ceiling_blocks() words) and
-// a streaming copy.
+// multiple of 16; one word per workgroup to sink, ceiling_blocks() words), a
+// streaming copy, and with src2 two read streams into one write stream.
 int ceiling_blocks();
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t st);
-hipError_t launch_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t st);
+hipError_t launch_stream_copy(const void *src, const void *src2, void *dst, int64_t bytes, hipStream_t st);
 
 // Generation (k_generate.hip): embedding rows (16-byte pieces of a row of
 // row_bytes; zero rows for ids outside [0, vocab)), and per row of an int32

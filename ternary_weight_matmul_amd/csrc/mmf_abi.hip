@@ -1109,7 +1109,7 @@ mmf_status mmf_layer_bwd(const mmf_layer_weights *w, const void *x, const void *
 }
 
 mmf_status mmf_hbm_ceiling(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream) {
-    if (mode != 0 && mode != 1) return fail(MMF_ERR_INVALID_ARG, "mode %d (0 read, 1 copy)", mode);
+    if (mode < 0 || mode > 2) return fail(MMF_ERR_INVALID_ARG, "mode %d (0 read, 1 copy, 2 two reads one write)", mode);
     if (bytes <= 0 || bytes % 16) return fail(MMF_ERR_INVALID_ARG, "bytes=%lld must be a positive multiple of 16",
                                              (long long)bytes);
     if (!src || !dst || !aligned16(src) || !aligned16(dst))
@@ -1117,12 +1117,14 @@ mmf_status mmf_hbm_ceiling(int mode, const void *src, void *dst, int64_t bytes, 
     if (ceiling_blocks() * 4 > MMF_HBM_CEILING_SINK_BYTES) return fail(MMF_ERR_INVALID_ARG, "sink too small");
     const char *s = static_cast<const char *>(src);
     const char *d = static_cast<const char *>(dst);
+    const int64_t slen = mode == 2 ? 2 * bytes : bytes;
     const int64_t dlen = mode == 0 ? MMF_HBM_CEILING_SINK_BYTES : bytes;
-    if (s < d + dlen && d < s + bytes) return fail(MMF_ERR_INVALID_ARG, "src and dst overlap");
-    std::string path = mode == 0 ? "stream_read;" : "stream_copy;";
-    const hipError_t e = timed(mode == 0 ? "stream_read" : "stream_copy", bytes, 0, 0, stream, [&] {
-        return mode == 0 ? launch_stream_read(src, bytes, static_cast<uint32_t *>(dst), stream)
-                         : launch_stream_copy(src, dst, bytes, stream);
+    if (s < d + dlen && d < s + slen) return fail(MMF_ERR_INVALID_ARG, "src and dst overlap");
+    static const char *names[] = {"stream_read", "stream_copy", "stream_2r1w"};
+    std::string path = std::string(names[mode]) + ";";
+    const hipError_t e = timed(names[mode], bytes, 0, 0, stream, [&] {
+        if (mode == 0) return launch_stream_read(src, bytes, static_cast<uint32_t *>(dst), stream);
+        return launch_stream_copy(src, mode == 2 ? s + bytes : nullptr, dst, bytes, stream);
     });
     mmf_status r = hip_status(e, "mmf_hbm_ceiling");
     if (r == MMF_OK) g_path = path;

@@ -212,3 +212,15 @@ def test_decode_kernel_modes(lib):
     for name, mode in B.DECODE_KERNELS.items():
         B.set_decode_kernel(name)
     B.set_decode_kernel("auto")
+
+
+def test_hbm_ceiling_rejects_bad_arguments(lib):
+    """mmf_hbm_ceiling validates on the host before any HIP call."""
+    import ctypes as C
+    p = C.c_void_p(FAKE)
+    q = C.c_void_p(FAKE + (1 << 30))
+    assert lib.mmf_hbm_ceiling(3, p, q, 4096, None) == INVALID
+    assert lib.mmf_hbm_ceiling(0, p, q, 4100, None) == INVALID
+    assert lib.mmf_hbm_ceiling(1, p, C.c_void_p(FAKE + 8), 4096, None) == INVALID  # overlap
+    assert lib.mmf_hbm_ceiling(2, p, C.c_void_p(FAKE + 4096), 4096, None) == INVALID  # overlaps the second source
+    assert lib.mmf_hbm_ceiling(1, None, q, 4096, None) == INVALID
