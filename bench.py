@@ -399,8 +399,9 @@ def hbm_ceilings(mmf, torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> dict:
     return dict(bytes_per_stream=nbytes, read_GBs=round(rd, 1), copy_GBs=round(cp, 1), two_read_one_write_GBs=round(r2, 1),
                 read_frac=round(rd / HBM_PEAK_GBS, 4), copy_frac=round(cp / HBM_PEAK_GBS, 4),
                 two_read_one_write_frac=round(r2 / HBM_PEAK_GBS, 4),
-                note="hand-written streaming kernels (mmf_hbm_ceiling): 8192 x 256 threads, 8 non-temporal 16-byte "
-                     "loads in flight per lane")
+                note="hand-written streaming kernels (mmf_hbm_ceiling): 256-thread workgroups each streaming a "
+                     "contiguous range, 8 16-byte loads in flight per lane (read: 8192 workgroups, cached loads; "
+                     "copy and 2r1w: 16384, non-temporal)")
 
 
 def with_ceiling(roof: dict, ceil: dict) -> dict:

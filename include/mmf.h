@@ -380,8 +380,10 @@ mmf_status mmf_timing_collect(mmf_kernel_timing *out, int32_t capacity, int32_t 
 /*
  * mmf_hbm_ceiling -- measured HBM roof (measurement support): streams device
  * memory in the access pattern of the library's bandwidth-bound kernels
- * (16-byte loads by consecutive lanes, eight in flight per lane, 8192
- * workgroups of 256 threads, non-temporal).
+ * (16-byte loads by consecutive lanes, eight in flight per lane, each
+ * workgroup of 256 threads streaming its own contiguous range; 8192
+ * workgroups and cached loads for the read stream, 16384 and non-temporal
+ * accesses for the others).
  *  mode 0 : read `bytes` of src (the packed-weight stream of a GEMV); dst
  *           receives one uint32 per workgroup (MMF_HBM_CEILING_SINK_BYTES).
  *  mode 1 : copy `bytes` from src to dst (one read and one write stream).

@@ -1111,17 +1111,21 @@ static void run_gemm_dma(const ContractArgs &a, hipStream_t st) {
     launch_k(tgemm_dma_kernel<NG, JN, EPI>, (unsigned)(tiles_m * tiles_n), 256, 0, st, a, tiles_n);
 }
 
-// Channel blocks per workgroup for one row block: the most (1, 2 or 4, with
-// ng * cb <= 4) that still leaves kGemvMinGroups workgroups; fewer, wider
-// workgroups read the codes less often but leave the latency-bound small
+// Channel blocks per workgroup for one row block: the most (1, 2, 4, or 8 for a
+// single group, with ng * cb <= 4 otherwise) that still leaves kGemvMinGroups
+// workgroups. Every workgroup reads the codes of all its rows over the whole
+// K, as many bytes as a 64-channel block of packed weights, so wider
+// workgroups cut that traffic; too few of them leave the latency-bound small
 // shapes with too few CUs pulling weights (measured on MI355X: 2048 outputs
-// keep 16-channel workgroups, 5632 x 2 take two blocks, 11264 x 1 four).
+// keep 16-channel workgroups, 5632 x 2 take two blocks, 11264 x 1 four; a
+// 32768 x 32768 weight streams at 4.4 TB/s with eight blocks against 3.75 with
+// four, and at 5.4 with the codes traffic removed in a timing-only copy).
 constexpr int kGemvMinGroups = 160;
 static int gemv_channel_blocks(int nc, int ng, int k, int row_blocks) {
     int cb = 1;
     if (k < 1024) return cb;  // fewer than 4 slices: too few waves for the wider epilogue
-    for (int c = 2; c <= 4; c *= 2)
-        if (ng * c <= 4 && (nc + 16 * c - 1) / (16 * c) * row_blocks >= kGemvMinGroups) cb = c;
+    for (int c = 2; c <= 8; c *= 2)
+        if (ng * c <= (ng == 1 ? 8 : 4) && (nc + 16 * c - 1) / (16 * c) * row_blocks >= kGemvMinGroups) cb = c;
     return cb;
 }
 
@@ -1132,6 +1136,9 @@ static void run_gemv_t(const ContractArgs &a, hipStream_t st) {
     // share each activation fragment (a workgroup reads its rows' codes once,
     // 4x the bytes of a 16-channel block of weights)
     switch (gemv_channel_blocks(a.nc, NG, a.k, (int)((a.m + 15) / 16))) {
+        case 8:
+            if constexpr (NG == 1) { run_gemv_cb<NG, SH, EPI, 4, RT, 8>(a, st); break; }
+            [[fallthrough]];
         case 4:
             if constexpr (NG == 1) { run_gemv_cb<NG, SH, EPI, 4, RT, 4>(a, st); break; }
             [[fallthrough]];
@@ -1399,6 +1406,7 @@ static hipError_t run_row_in(const ContractArgs &a, const RowSrc &src, float eps
     // at most 8192 wide) or with a gain, whose registers would not fit them
     constexpr bool CB4 = NG == 1 && IN == ROW_X;
     switch (gemv_channel_blocks(a.nc, NG, a.k, 1)) {
+        case 8:  // the row kernels stop at four channel blocks
         case 4:
             if constexpr (CB4) return run_row_cb<NG, EPI, XT, RT, 4, IN>(a, src, eps, st);
             [[fallthrough]];

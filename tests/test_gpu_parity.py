@@ -59,6 +59,9 @@ BITLINEAR_CASES = [
     (8, 2048, 10250, "bf16", False),
     (16, 16384, 64, "bf16", False),
     (2, 8208, 100, "f32", True),
+    # eight channel blocks per workgroup (single group, 20480 outputs or more), ragged last block
+    (4, 1024, 20500, "bf16", True),
+    (16, 2048, 32768, "f32", False),
 ]
 
 
