@@ -33,6 +33,9 @@ the derivative of the recurrence (reverse time), and ``bitlinear_bwd``, the
 derivative of FusedBitLinear with both quantisers passed straight through;
 and for the token-to-token loop of generation, ``embed`` and ``greedy_head``
 (a FusedBitLinear head whose largest exact sum picks the next token).
+``hgrn2_scan`` widens the recurrence's state from a vector to a matrix per head
+(HGRN2, which [R1] names without printing its equations: a reading, stated
+in its docstring).
 
 Precision: every step is binary64 except the two quantisers, which decide
 integers and therefore run in the kernel's precision (binary32 operations,
@@ -300,6 +303,43 @@ def hgrn_scan_bwd(f: np.ndarray, h: np.ndarray, dh: np.ndarray, h0: Optional[np.
                                     _ptr(dh0)) != 0:
         raise ValueError("oracle_hgrn_scan_bwd failed")
     return dx, df, dh0
+
+
+def hgrn2_scan(f: np.ndarray, i: np.ndarray, o: np.ndarray, e: int, s0: Optional[np.ndarray] = None):
+    """The HGRN recurrence with an expanded state (HGRN2), binary64, sequential.
+
+    [R1] names HGRN2 as the gated linear recurrence that replaces attention (section
+    "核心价值提炼", table "创新之处" and list "关键设计决策") and prints only its elementwise form
+    h_t = g_t * h_{t-1} + x_t. The expanded state is a reading: the channels split into heads of e,
+    each head's state is an e x e matrix, the forget gate acts on its rows, the input is the outer
+    product of (1 - f) with the input vector and the output gate reads the state out:
+
+        S_t[a][c] = f_t[a] * S_{t-1}[a][c] + (1 - f_t[a]) * i_t[c]
+        y_t[c]    = sum_a o_t[a] * S_t[a][c]
+
+    (a, c index the head's e channels). With e = 1 this is [R1]'s recurrence with
+    x~ = (1 - f) * i, read out as y = o * h.
+    f, i, o: [b, t, d] with d a multiple of e; s0: [b, d / e, e, e] or None (zeros).
+    Returns (y [b, t, d], s_last [b, d / e, e, e])."""
+    f = np.asarray(f, dtype=np.float64)
+    i = np.asarray(i, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    if f.shape != i.shape or f.shape != o.shape or f.ndim != 3:
+        raise ValueError("f, i and o must all be [b, t, d]")
+    b, t, d = f.shape
+    if e < 1 or d % e:
+        raise ValueError("d must be a multiple of e")
+    nh = d // e
+    fh = f.reshape(b, t, nh, e)
+    ih = i.reshape(b, t, nh, e)
+    oh = o.reshape(b, t, nh, e)
+    s = np.zeros((b, nh, e, e)) if s0 is None else np.array(s0, dtype=np.float64).reshape(b, nh, e, e)
+    y = np.empty((b, t, nh, e))
+    for step in range(t):
+        fa = fh[:, step][..., :, None]                  # forget gate on the rows
+        s = fa * s + (1.0 - fa) * ih[:, step][..., None, :]
+        y[:, step] = np.einsum("bna,bnac->bnc", oh[:, step], s)
+    return y.reshape(b, t, d), s
 
 
 def gnorm_swish(h, g, weight=None, eps: float = 1e-8):

@@ -75,5 +75,16 @@ def scan_inputs(b: int, t: int, d: int, seed: int, f_loc: float = 2.0, f_scale: 
     return x, f
 
 
+def hgrn2_inputs(b: int, t: int, d: int, seed: int, f_loc: float = 2.0, f_scale: float = 1.0):
+    """Inputs of the expanded-state recurrence: f as in ``scan_inputs`` (logit-normal), the input
+    vector i and the output gate o ~ N(0, 1); all fp32 [b, t, d]."""
+    g = rng(seed)
+    logit = g.standard_normal(size=(b, t, d), dtype=np.float32) * np.float32(f_scale) + np.float32(f_loc)
+    f = (1.0 / (1.0 + np.exp(-logit.astype(np.float64)))).astype(np.float32)
+    i = g.standard_normal(size=(b, t, d), dtype=np.float32)
+    o = g.standard_normal(size=(b, t, d), dtype=np.float32)
+    return f, i, o
+
+
 def layer_seed(config_seed: int, layer: int) -> int:
     return config_seed * 1000 + layer
