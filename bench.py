@@ -21,8 +21,10 @@ Also printed in the same JSON line:
   cpu_baseline -- the CPU oracle on a bounded sample of the same workload;
   configs      -- with --extras (default): every other config of the workload
                   (370M layer fp32; 370M and 2.7B stack prefills; the 1.3B
-                  decode step at batch 1, 16, 64; the long-sequence scan), each
-                  with its own roofline, next to a measured HBM ceiling.
+                  decode step at batch 1, 16, 64; the long-sequence scan; the
+                  expanded-state recurrence, prefill and decode step), each
+                  with its own roofline (the fp32 vector ALU for the
+                  expanded-state prefill), next to a measured HBM ceiling.
 --only LEG runs one config leg alone, for profiling it.
 """
 from __future__ import annotations
@@ -38,6 +40,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed, 256 CUs at 2.4 GHz)
 INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
@@ -56,7 +59,7 @@ def parse():
     ap.add_argument("--extras", type=int, default=1,
                     help="0 skips the figures measured outside the timed steps (the other configs, the "
                          "measured HBM ceiling, derivatives, generation)")
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "prefill_b8", "ceiling", "bwd"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "prefill_b8", "ceiling", "bwd", "hgrn2"],
                     help="run one config leg alone and print its JSON (for profiling a config)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (for scaling HBM counters)")
@@ -161,9 +164,17 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
     norm_quant<T> (m rows of k): x read (sizeof T) + codes written (1 B) per element, 8 B per row.
     gnorm_quant<T>: h (fp32) and g (sizeof T) read + codes written per element, 8 B per row.
     scan (m = b t, k = d): f and x~ read, h written, 12 B per element.
+    hgrn2_scan<e> / hgrn2_step<e> (m = b t, n = d, k = e, the expanded-state recurrence): per
+      token and head of e, 5 e^2 + e flops (the state's multiply, multiply-add and readout
+      multiply-add, and 1 - f); f, i, o read and y written, 16 B per (b, t, channel); a step
+      (t = 1, m = b) also reads and writes the state, 8 e bytes per (b, channel).
     scan_bwd (m = b t, k = d): dh, f and h read, dx and df written, 20 B per element.
     """
     base, args = _kind(kernel)
+    if base in ("hgrn2_scan", "hgrn2_step"):
+        e = int(args[0])
+        nbytes = 16.0 * m * n + (8.0 * m * n * e if base == "hgrn2_step" else 0.0)
+        return m * n * (5.0 * e + 1.0), nbytes
     if base in ("tgemm", "tgemm_dma", "tgemv", "tgemv_row"):
         epi = args[0]
         na = 3 if "split_a" in args else 1
@@ -199,6 +210,8 @@ KERNEL_SOURCES = {
     "norm_quant": ["k_quant.hip", "row_quant.hpp"] + _COMMON,
     "gnorm_quant": ["k_quant.hip", "row_quant.hpp"] + _COMMON,
     "scan": ["k_scan.hip"] + _COMMON,
+    "hgrn2_scan": ["k_hgrn2.hip"] + _COMMON,
+    "hgrn2_step": ["k_hgrn2.hip"] + _COMMON,
 }
 
 
@@ -287,6 +300,9 @@ class KernelTable:
         if e["name"].startswith("tgemm"):
             roof = dict(bound="mfma", achieved=round(e["ops"] / avg_s / 1e12, 2), peak=INT8_MFMA_PEAK_TOPS,
                         unit="TFLOP/s")
+        elif e["name"].startswith("hgrn2_scan"):
+            roof = dict(bound="alu", achieved=round(e["ops"] / avg_s / 1e12, 2), peak=FP32_VECTOR_PEAK_TFLOPS,
+                        unit="TFLOP/s")
         else:
             roof = dict(bound="hbm", achieved=round(e["bytes"] / avg_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
         roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
@@ -295,14 +311,15 @@ class KernelTable:
         roof["phase"] = e["phase"]
         roof["avg_launch_us"] = round(e["avg_ms"] * 1000.0, 2)
         roof["launches_per_step"] = round(e["launches"], 1)
-        roof["algorithmic_per_launch"] = e["ops"] if roof["bound"] == "mfma" else e["bytes"]
+        roof["algorithmic_per_launch"] = e["ops"] if roof["bound"] in ("mfma", "alu") else e["bytes"]
         roof["share_of_step"] = round(e["ms"] / step_ms, 3)
         tr = stored_trace_us(key)
         if tr:  # the same kernel's average in a committed rocprofv3 trace of these sources
             us, fname = tr
             work = roof["algorithmic_per_launch"]
             roof["trace_avg_launch_us"] = us
-            roof["trace_frac"] = round(work / (us / 1e6) / (1e12 if roof["bound"] == "mfma" else 1e9) / roof["peak"], 4)
+            scale = 1e9 if roof["bound"] == "hbm" else 1e12
+            roof["trace_frac"] = round(work / (us / 1e6) / scale / roof["peak"], 4)
             roof["trace_file"] = "profiles/" + fname
         return roof
 
@@ -326,7 +343,10 @@ class KernelTable:
             t = e["avg_ms"] / 1000.0
             row = dict(phase=e["phase"], launches_per_step=round(e["launches"], 1), avg_us=round(e["avg_ms"] * 1000, 2),
                        ms_per_step=round(e["ms"], 3))
-            if e["ops"]:
+            if e["ops"] and e["name"].startswith("hgrn2"):
+                row["fp32_tflops"] = round(e["ops"] / t / 1e12, 2)
+                row["frac_fp32_vector"] = round(e["ops"] / t / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4)
+            elif e["ops"]:
                 row["int8_tops"] = round(e["ops"] / t / 1e12, 1)
                 row["frac_mfma"] = round(e["ops"] / t / 1e12 / INT8_MFMA_PEAK_TOPS, 4)
             row["gbs"] = round(e["bytes"] / t / 1e9, 1)
@@ -558,6 +578,59 @@ def leg_c5(mmf, torch, dev, reps: int = 10, ceil=None, cpu: bool = True) -> dict
     return res
 
 
+def leg_hgrn2(mmf, torch, dev, reps: int = 5, ceil=None, cpu: bool = True) -> dict:
+    """The expanded-state recurrence at 1.3B width, heads of 128: a 16 x 2048-token prefill
+    (value = tokens/s, bound by the fp32 vector ALU) and a decode step at batch 16 (one token,
+    the state read and written in place, HBM-bound). f = sigmoid(N(2,1)), i, o ~ N(0,1), the
+    initial state ~ N(0,1). The oracle runs one (sequence, head) pair of the prefill."""
+    b, t, d, e = 16, 2048, 2048, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    f = torch.sigmoid(torch.randn((b, t, d), device=dev, generator=gen) + 2.0)
+    i = torch.randn((b, t, d), device=dev, generator=gen)
+    o = torch.randn((b, t, d), device=dev, generator=gen)
+    s0 = torch.randn((b, d // e, e, e), device=dev, generator=gen)
+    s_last = torch.empty_like(s0)
+    y = torch.empty_like(f)
+
+    def run():
+        mmf.hgrn2_scan_fwd(f, i, o, e, s0, out=y, s_last=s_last)
+
+    ms = event_ms(torch, run, reps)
+    kt = KernelTable().add(timed_records(mmf, run, reps), "prefill", 1.0 / reps)
+    res = dict(workload="HGRN2 expanded-state recurrence: d=2048, heads of 128, B=16 x T=2048, fp32",
+               value=round(b * t / (ms / 1000), 1), unit="tokens/s", ms=round(ms, 3),
+               roofline=kt.roofline(ms), kernels=kt.breakdown())
+    # decode: one token per sequence, the state updated in place
+    f1, i1, o1 = f[:, :1].contiguous(), i[:, :1].contiguous(), o[:, :1].contiguous()
+    st = s0.clone()
+    y1 = torch.empty_like(f1)
+    steps = 50
+
+    def step():
+        mmf.hgrn2_scan_fwd(f1, i1, o1, e, st, out=y1, s_last=st)
+
+    sms = event_ms(torch, step, steps)
+    kd = KernelTable().add(timed_records(mmf, step, steps), "decode", 1.0 / steps)
+    res["decode_step"] = dict(workload="one token at B=16, state in place", us=round(sms * 1000, 2),
+                              roofline=with_ceiling(kd.roofline(sms), ceil))
+    if cpu:
+        import oracle
+        fs = f[0, :, :e].double().cpu().numpy()[None]
+        is_ = i[0, :, :e].double().cpu().numpy()[None]
+        os_ = o[0, :, :e].double().cpu().numpy()[None]
+        s0s = s0[0, :1].double().cpu().numpy()[None]
+        t0 = time.perf_counter()
+        oracle.hgrn2_scan(fs, is_, os_, e, s0s)
+        dt = time.perf_counter() - t0
+        res["cpu_oracle"] = dict(value=round(t / (d // e) / dt, 1), unit="tokens/s (full-width equivalent)",
+                                 cores=1, cpu=cpu_model(),
+                                 sample="one sequence x one head of 16 (2048 tokens, %.2f s), scaled to the "
+                                        "full width" % dt)
+    del f, i, o, s0, s_last, y, st
+    return res
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -589,6 +662,8 @@ def run_only(args):
         res = leg_decode(mmf, torch, dev)
     elif args.only == "c5":
         res = leg_c5(mmf, torch, dev, cpu=cpu)
+    elif args.only == "hgrn2":
+        res = leg_hgrn2(mmf, torch, dev, cpu=cpu)
     elif args.only == "bwd":
         from ternary_weight_matmul_amd import synth
         d, inner, _ = synth.SHAPES["1.3B"]
@@ -767,6 +842,8 @@ def main():
         configs["prefill_1p3b_b8"] = leg_prefill(mmf, torch, dev, "1.3B", 8, 2048, 3, 3, ceil)
         torch.cuda.empty_cache()
         configs["c5"] = leg_c5(mmf, torch, dev, ceil=ceil, cpu=args.cpu_baseline != 0)
+        torch.cuda.empty_cache()
+        configs["hgrn2"] = leg_hgrn2(mmf, torch, dev, ceil=ceil, cpu=args.cpu_baseline != 0)
         torch.cuda.empty_cache()
         if T > 0:
             scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev)

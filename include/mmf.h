@@ -276,6 +276,29 @@ mmf_status mmf_hgrn_scan_bwd(const float *f, const float *h, const float *h0, co
                              int64_t t, int64_t d, mmf_scan_mode mode, hipStream_t stream);
 
 /*
+ * mmf_hgrn2_scan_fwd -- the recurrence with an expanded state (HGRN2), fp32.
+ * [R1] (section "核心价值提炼", table "创新之处" and list "关键设计决策") names
+ * HGRN2 as the gated linear recurrence that replaces attention and prints only
+ * the elementwise h_t = gate_t * h_{t-1} + x_t; the expanded state is a
+ * reading: the d channels split into d/e heads of e channels, each head's state
+ * is an e x e matrix S (row a, column c), the forget gate acts on its rows, the
+ * input is the outer product of (1 - f) with i, and the output gate reads it:
+ *   S_t[a][c] = f_t[a] * S_{t-1}[a][c] + (1 - f_t[a]) * i_t[c]
+ *   y_t[c]    = sum_a o_t[a] * S_t[a][c]
+ * (with e = 1 it is mmf_hgrn_scan_fwd with x = (1 - f) i, read out as o h).
+ *  f, i, o, y : [b][t][d] fp32 (head n owns channels n*e .. n*e+e-1);
+ *  s0, s_last : [b][d/e][e][e] fp32 or NULL (s0 NULL: zeros; s_last NULL: not
+ *  written). s_last may equal s0 (in place: a decode step is t = 1); y and
+ *  s_last may not alias anything else. The tokens run in order, each state
+ *  block held in registers, so a call over t tokens and t calls of one token
+ *  give the same bits. No workspace. t may be 0 (s_last = s0).
+ *  e in {16, 32, 64, 128}, d a multiple of e; every tensor 16-byte aligned.
+ *  Errors: INVALID_ARG, UNSUPPORTED (e), HIP.
+ */
+mmf_status mmf_hgrn2_scan_fwd(const float *f, const float *i, const float *o, const float *s0, float *y,
+                              float *s_last, int64_t b, int64_t t, int64_t d, int64_t e, hipStream_t stream);
+
+/*
  * mmf_layer_fwd -- one HGRNBit block over b sequences of t tokens ([R3]):
  *   i^, f^, g^ = BitLinear_{i,f,g}(x)
  *   f  = sigmoid(f^);  x~ = (1 - f) * SiLU(i^)

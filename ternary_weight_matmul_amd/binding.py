@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmmf.so")
 __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
     "ternary_pack", "bitlinear_fwd", "bitlinear_bwd", "embed", "greedy_head", "hgrn_scan_fwd", "hgrn_scan_bwd",
-    "layer_fwd", "layer_bwd",
+    "hgrn2_scan_fwd", "layer_fwd", "layer_bwd",
     "layer_decode_step", "layer_decode_step_noalloc",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
     "set_decode_kernel", "DECODE_KERNELS", "hbm_ceiling",
@@ -31,7 +31,7 @@ SYMBOLS = [
     "mmf_bitlinear_workspace_size", "mmf_bitlinear_fwd",
     "mmf_bitlinear_bwd_workspace_size", "mmf_bitlinear_bwd",
     "mmf_embed", "mmf_greedy_head_workspace_size", "mmf_greedy_head",
-    "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd", "mmf_hgrn_scan_bwd",
+    "mmf_hgrn_scan_workspace_size", "mmf_hgrn_scan_fwd", "mmf_hgrn_scan_bwd", "mmf_hgrn2_scan_fwd",
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step", "mmf_layer_decode_step_noalloc",
     "mmf_layer_bwd_workspace_size", "mmf_layer_bwd",
     "mmf_set_decode_kernel",
@@ -106,6 +106,7 @@ def load():
     lib.mmf_hgrn_scan_workspace_size.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.mmf_hgrn_scan_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P, SZ, P]
     lib.mmf_hgrn_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
+    lib.mmf_hgrn2_scan_fwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
     lib.mmf_layer_workspace_size.argtypes = [ctypes.POINTER(CLayerWeights), I64, I64, ctypes.POINTER(SZ)]
     lib.mmf_layer_fwd.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, I64, P, P,
                                   ctypes.c_int, P, SZ, ctypes.POINTER(CLayerProbe), P]
@@ -345,6 +346,23 @@ def hgrn_scan_bwd(f, h, dh, h0=None, dh_last=None, mode: str = "auto", dx=None, 
     _check(lib.mmf_hgrn_scan_bwd(_ptr(f), _ptr(h), _ptr(h0), _ptr(dh), _ptr(dh_last), _ptr(dx), _ptr(df),
                                  _ptr(dh0), b, t, d, SCAN_MODES[mode], _stream()))
     return dx, df, dh0
+
+
+def hgrn2_scan_fwd(f, i, o, e: int, s0=None, out=None, s_last=None):
+    """The expanded-state recurrence (mmf_hgrn2_scan_fwd) over f, i, o [b, t, d] fp32 with heads
+    of e channels; s0 / s_last [b, d / e, e, e] fp32 or None (s_last may be s0). Returns y."""
+    torch = _torch()
+    lib = load()
+    if f.shape != i.shape or f.shape != o.shape or f.dim() != 3:
+        raise ValueError("f, i and o must all be [b, t, d]")
+    for t_ in (f, i, o) + tuple(x for x in (s0, s_last) if x is not None):
+        if t_.dtype != torch.float32 or not t_.is_contiguous():
+            raise TypeError("f, i, o and the states must be contiguous float32")
+    b, t, d = f.shape
+    y = out if out is not None else torch.empty_like(f)
+    _check(lib.mmf_hgrn2_scan_fwd(_ptr(f), _ptr(i), _ptr(o), _ptr(s0), _ptr(y), _ptr(s_last), b, t, d, e,
+                                  _stream()))
+    return y
 
 
 @dataclass

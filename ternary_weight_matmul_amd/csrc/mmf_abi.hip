@@ -816,6 +816,34 @@ mmf_status mmf_hgrn_scan_fwd(const float *x, const float *f, const float *h0, fl
     return r;
 }
 
+mmf_status mmf_hgrn2_scan_fwd(const float *f, const float *i, const float *o, const float *s0, float *y,
+                              float *s_last, int64_t b, int64_t t, int64_t d, int64_t e, hipStream_t stream) {
+    if (b < 0 || t < 0 || d <= 0) return fail(MMF_ERR_INVALID_ARG, "b, t >= 0 and d > 0 required");
+    if (e != 16 && e != 32 && e != 64 && e != 128)
+        return fail(MMF_ERR_UNSUPPORTED, "head width e = %lld: 16, 32, 64 or 128 supported", (long long)e);
+    if (d % e) return fail(MMF_ERR_INVALID_ARG, "d = %lld is not a multiple of e = %lld", (long long)d, (long long)e);
+    if (b > 0 && t > 0 && (!f || !i || !o || !y)) return fail(MMF_ERR_INVALID_ARG, "f, i, o and y must be non-NULL");
+    const void *ins[] = {f, i, o, s0};
+    for (const void *p : ins)
+        if (p && (p == y || p == s_last) && !(p == s0 && p == s_last))
+            return fail(MMF_ERR_INVALID_ARG, "y and s_last may not alias an input (s_last may equal s0)");
+    if (y && y == s_last) return fail(MMF_ERR_INVALID_ARG, "y and s_last may not alias");
+    const void *all[] = {f, i, o, s0, y, s_last};
+    for (const void *p : all)
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return fail(MMF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    const int64_t blocks = b * (d / e) * (e < 32 ? 1 : e / 32);
+    if (blocks > INT32_MAX) return fail(MMF_ERR_UNSUPPORTED, "b * d / min(e, 32) too large");
+    if (b == 0) return MMF_OK;
+    const char *name = "hgrn2_scan";
+    // timing label: a one-token call (a decode step) streams the state, a longer one computes
+    const std::string label = std::string(t == 1 ? "hgrn2_step<" : "hgrn2_scan<") + std::to_string(e) + ">";
+    hipError_t err = timed(label, b * t, (int)d, (int)e, stream,
+                           [&] { return launch_hgrn2_scan(f, i, o, s0, y, s_last, b, t, d, (int)e, stream, &name); });
+    mmf_status r = hip_status(err, "mmf_hgrn2_scan_fwd");
+    if (r == MMF_OK) g_path = name;
+    return r;
+}
+
 mmf_status mmf_hgrn_scan_bwd(const float *f, const float *h, const float *h0, const float *dh, const float *dh_last,
                              float *dx, float *df, float *dh0, int64_t b, int64_t t, int64_t d, mmf_scan_mode mode,
                              hipStream_t stream) {

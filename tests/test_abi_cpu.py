@@ -109,6 +109,25 @@ def test_scan_validation(lib):
     assert lib.mmf_hgrn_scan_fwd(FAKE, FAKE, None, FAKE, None, 1, 4096, 64, 2, None, 0, None) == WORKSPACE
 
 
+def test_hgrn2_scan_validation(lib):
+    """mmf_hgrn2_scan_fwd rejects unsupported head widths, ragged heads, missing and aliased
+    buffers on the host."""
+    F = [FAKE + k * (1 << 24) for k in range(6)]
+    f, i, o, s0, y, sl = F
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, 1, 4, 256, 48, None) == UNSUPPORTED
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, 1, 4, 256, 8, None) == UNSUPPORTED
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, 1, 4, 96, 64, None) == INVALID
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, -1, 4, 256, 64, None) == INVALID
+    assert lib.mmf_hgrn2_scan_fwd(None, i, o, s0, y, sl, 1, 4, 256, 64, None) == INVALID
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, None, sl, 1, 4, 256, 64, None) == INVALID
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, i, sl, 1, 4, 256, 64, None) == INVALID   # y aliases i
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, f, 1, 4, 256, 64, None) == INVALID   # s_last aliases f
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, y, 1, 4, 256, 64, None) == INVALID   # s_last aliases y
+    assert "alias" in B.last_error()
+    assert lib.mmf_hgrn2_scan_fwd(f + 4, i, o, s0, y, sl, 1, 4, 256, 64, None) == INVALID  # misaligned
+    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, 0, 4, 256, 64, None) == OK       # nothing to do
+
+
 def test_bitlinear_bwd_validation(lib):
     sz = ctypes.c_size_t(0)
     w = _weight(64, 128)
