@@ -12,14 +12,16 @@
 // (sequence, head, block of BC columns) and keeps its E x BC block of the
 // state in registers for the whole sequence: thread (ta, tc) holds rows
 // ta*RA .. ta*RA+RA-1 and columns tc*RC .. tc*RC+RC-1, with ta the lane's low
-// four bits, so the sum over rows of the readout is a DPP reduction within a
-// row of 16 lanes (every lane ends with the row total; fixed order). Per token
-// a thread does 3 RA*RC multiply-adds and 4 RC DPP adds: the recurrence is
+// four bits. The sum over rows of the readout runs as a DPP sum over each quad
+// of lanes per token and a sum of the four quads' partials, in LDS, once per
+// chunk of tokens (fixed order). Per token a thread does 3 RA*RC vector
+// operations (S - v, then f (S - v) + v, then the readout's multiply-add) and
+// 2 DPP adds per column: the recurrence is
 // bound by the vector ALU (about 5 e^2 flops per token and head against 16 e
 // bytes of HBM traffic). The gates of TT tokens are staged through LDS with
 // coalesced loads issued one chunk ahead; the outputs of a chunk leave as
-// 16-byte stores. The state block enters and leaves through LDS as 16-byte
-// row pieces, so a decode step (one token) streams the state at full width.
+// 16-byte stores. The state block goes straight between HBM and registers as
+// one RC-float piece per row and thread (16 bytes for heads of 64 and 128).
 // Workgroups that share a (sequence, head) are dealt to the same XCD, so its f
 // and o rows come from that XCD's L2 after the first reader.
 #include "device_common.hpp"
@@ -27,21 +29,22 @@
 
 namespace mmf {
 
+template <int N>
+using fvec = float __attribute__((ext_vector_type(N)));
+
 template <int E>
 struct H2Shape {
-    static constexpr int BC = E < 32 ? E : 32;  // state columns per workgroup
-    static constexpr int RA = E / 16;           // rows per thread
-    static constexpr int RC = BC / 16;          // columns per thread
+    static constexpr int BC = E < 64 ? E : 64;  // state columns per workgroup
+    static constexpr int TA = 16;               // lanes that share a column (a DPP row)
+    static constexpr int RA = E / TA;           // rows per thread
+    static constexpr int RC = BC * TA / 256;    // columns per thread
     static constexpr int TT = 16;               // tokens per LDS chunk
     static constexpr int GATE_FL = 2 * TT * E;  // f and o of a chunk (floats)
-    static constexpr int STATE_FL = E * BC;     // the state block (floats)
-    static constexpr int STAGE_FL = GATE_FL > STATE_FL ? GATE_FL : STATE_FL;
     static constexpr int G4 = TT * E / 4;       // float4s of one gate per chunk
     static constexpr int I4 = TT * BC / 4;      // float4s of i per chunk
     static constexpr int GL = (G4 + 255) / 256; // float4 slots per thread per gate
     static constexpr int IL = (I4 + 255) / 256;
-    static constexpr int S4 = E * BC / 4;       // float4s of the state block
-    static constexpr int SL = (S4 + 255) / 256;
+    static_assert(TA * RA == E && RC * (256 / TA) == BC, "256 threads tile the E x BC block");
 };
 
 template <int E>
@@ -49,11 +52,12 @@ __global__ __launch_bounds__(256) void hgrn2_scan_kernel(const float *__restrict
                                                          const float *__restrict__ o, const float *s0, float *y,
                                                          float *s_last, int64_t t, int64_t d, int heads) {
     using Sh = H2Shape<E>;
-    constexpr int BC = Sh::BC, RA = Sh::RA, RC = Sh::RC, TT = Sh::TT;
+    constexpr int BC = Sh::BC, RA = Sh::RA, RC = Sh::RC, TT = Sh::TT, TA = Sh::TA;
     constexpr int CBK = E / BC;
-    __shared__ __attribute__((aligned(16))) float stage[Sh::STAGE_FL];  // f, o of a chunk; the state block
+    __shared__ __attribute__((aligned(16))) float stage[Sh::GATE_FL];  // f and o of a chunk
     __shared__ __attribute__((aligned(16))) float si[TT * BC];
-    __shared__ __attribute__((aligned(16))) float sy[TT * BC];
+    constexpr int NQ = TA / 4;  // quads of lanes per column
+    __shared__ __attribute__((aligned(16))) float sq[TT * NQ * BC];  // per-quad sums of the readout
 
     // workgroup -> (pair, column block); with a grid of whole XCD rounds, the
     // CBK workgroups of a pair get consecutive slots of one XCD
@@ -62,149 +66,166 @@ __global__ __launch_bounds__(256) void hgrn2_scan_kernel(const float *__restrict
     const int pair = lin / CBK, cblk = lin - pair * CBK;
     const int64_t bi = pair / heads;
     const int head = pair - (int)bi * heads;
-    const int tid = threadIdx.x, ta = tid & 15, tc = tid >> 4;
+    const int tid = threadIdx.x, ta = tid & (TA - 1), tc = tid / TA;
     const int64_t col0 = (int64_t)head * E;         // first channel of the head
     const int64_t ccol0 = col0 + (int64_t)cblk * BC; // first channel of the column block
     const int64_t row_base = bi * t * d;             // element (bi, 0, 0)
     const int64_t sbase = ((int64_t)pair * E) * E + (int64_t)cblk * BC;  // state (pair, 0, cblk*BC)
 
-    // ---- the state block: coalesced rows of BC floats through LDS
-    float S[RA][RC];
-#pragma unroll
-    for (int j = 0; j < Sh::SL; ++j) {
-        const int q = tid + 256 * j;
-        if (q < Sh::S4) {
-            const int a = q / (BC / 4), c4 = q - a * (BC / 4);
-            const float4 v = s0 ? *reinterpret_cast<const float4 *>(s0 + sbase + (int64_t)a * E + 4 * c4)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-            *reinterpret_cast<float4 *>(stage + a * BC + 4 * c4) = v;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < RA; ++r)
-#pragma unroll
-        for (int c = 0; c < RC; ++c) S[r][c] = stage[(ta * RA + r) * BC + tc * RC + c];
-    __syncthreads();
-
     // ---- chunks of TT tokens: loads of chunk n+1 in flight while chunk n runs
-    float4 pf[Sh::GL], po[Sh::GL], pi[Sh::IL];
-    auto fetch = [&](int64_t t0) {
-#pragma unroll
-        for (int j = 0; j < Sh::GL; ++j) {
-            const int q = tid + 256 * j;
-            const int k = q / (E / 4), c4 = q - k * (E / 4);
-            const int64_t tk = t0 + k < t ? t0 + k : t - 1;  // rows past t: any valid row, unused
-            const int64_t off = row_base + tk * d + col0 + 4 * c4;
-            if (q < Sh::G4) {
-                pf[j] = *reinterpret_cast<const float4 *>(f + off);
-                po[j] = *reinterpret_cast<const float4 *>(o + off);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < Sh::IL; ++j) {
-            const int q = tid + 256 * j;
-            const int k = q / (BC / 4), c4 = q - k * (BC / 4);
-            const int64_t tk = t0 + k < t ? t0 + k : t - 1;
-            if (q < Sh::I4) pi[j] = *reinterpret_cast<const float4 *>(xi + row_base + tk * d + ccol0 + 4 * c4);
-        }
+    // (a gate of a chunk is at most 512 float4s and i at most 256, so a thread
+    // holds at most two slots of each gate and one of i, in named registers;
+    // slots past a gate's float4 count -- only when it is not a multiple of 256
+    // -- load a clamped, valid element and are never parked)
+    static_assert(Sh::GL <= 2 && Sh::IL == 1, "prefetch slots");
+    float4 pf0, pf1, po0, po1, pi0;
+    auto gate_off = [&](int64_t t0, int j) __attribute__((always_inline)) {
+        const int q = min(tid + 256 * j, Sh::G4 - 1);
+        const int k = q / (E / 4), c4 = q - k * (E / 4);
+        const int64_t tk = t0 + k < t ? t0 + k : t - 1;  // rows past t: any valid row, unused
+        return row_base + tk * d + col0 + 4 * c4;
     };
-    auto park = [&]() {
-#pragma unroll
-        for (int j = 0; j < Sh::GL; ++j) {
-            const int q = tid + 256 * j;
-            if (q < Sh::G4) {
-                *reinterpret_cast<float4 *>(stage + 4 * q) = pf[j];
-                *reinterpret_cast<float4 *>(stage + TT * E + 4 * q) = po[j];
+    auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
+        const int64_t off0 = gate_off(t0, 0);
+        pf0 = *reinterpret_cast<const float4 *>(f + off0);
+        po0 = *reinterpret_cast<const float4 *>(o + off0);
+        if constexpr (Sh::GL == 2) {
+            const int64_t off1 = gate_off(t0, 1);
+            pf1 = *reinterpret_cast<const float4 *>(f + off1);
+            po1 = *reinterpret_cast<const float4 *>(o + off1);
+        }
+        const int q = min(tid, Sh::I4 - 1);
+        const int k = q / (BC / 4), c4 = q - k * (BC / 4);
+        const int64_t tk = t0 + k < t ? t0 + k : t - 1;
+        pi0 = *reinterpret_cast<const float4 *>(xi + row_base + tk * d + ccol0 + 4 * c4);
+    };
+    auto park = [&]() __attribute__((always_inline)) {
+        if (Sh::G4 % 256 == 0 || tid < Sh::G4) {
+            *reinterpret_cast<float4 *>(stage + 4 * tid) = pf0;
+            *reinterpret_cast<float4 *>(stage + TT * E + 4 * tid) = po0;
+        }
+        if constexpr (Sh::GL == 2) {
+            const int q = tid + 256;
+            if (Sh::G4 % 256 == 0 || q < Sh::G4) {
+                *reinterpret_cast<float4 *>(stage + 4 * q) = pf1;
+                *reinterpret_cast<float4 *>(stage + TT * E + 4 * q) = po1;
             }
         }
-#pragma unroll
-        for (int j = 0; j < Sh::IL; ++j) {
-            const int q = tid + 256 * j;
-            if (q < Sh::I4) *reinterpret_cast<float4 *>(si + 4 * q) = pi[j];
-        }
+        if (Sh::I4 % 256 == 0 || tid < Sh::I4) *reinterpret_cast<float4 *>(si + 4 * tid) = pi0;
     };
 
-    if (t > 0) {
-        fetch(0);
-        park();
-        __syncthreads();
+    if (t > 0) fetch(0);
+
+    // ---- the state block, straight into registers: each of a thread's RA rows is
+    // one RC-float vector (one load instruction of a wave covers 16 rows x 4 RC
+    // contiguous floats); these loads are in flight with the first chunk's
+    float S[RA][RC];
+    {
+        fvec<RC> sv[RA];
+        if (s0) {  // one uniform branch around all the loads: no wait between them
+#pragma unroll
+            for (int r = 0; r < RA; ++r)
+                sv[r] = *reinterpret_cast<const fvec<RC> *>(s0 + sbase + (int64_t)(ta * RA + r) * E + tc * RC);
+        } else {
+#pragma unroll
+            for (int r = 0; r < RA; ++r) sv[r] = fvec<RC>{};
+        }
+#pragma unroll
+        for (int r = 0; r < RA; ++r)
+#pragma unroll
+            for (int c = 0; c < RC; ++c) S[r][c] = sv[r][c];
     }
+
+    // one token: S <- f (S - v) + v (= f S + (1 - f) v), y = sum over rows of o S
+    auto token = [&](int k) __attribute__((always_inline)) {
+        float fa[RA], oa[RA], vc[RC];
+#pragma unroll
+        for (int r = 0; r < RA; ++r) {
+            fa[r] = stage[k * E + ta * RA + r];
+            oa[r] = stage[TT * E + k * E + ta * RA + r];
+        }
+#pragma unroll
+        for (int c = 0; c < RC; ++c) vc[c] = si[k * BC + tc * RC + c];
+        float part[RC];
+#pragma unroll
+        for (int c = 0; c < RC; ++c) part[c] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RA; ++r)
+#pragma unroll
+            for (int c = 0; c < RC; ++c) {
+                S[r][c] = fmaf(fa[r], S[r][c] - vc[c], vc[c]);
+                part[c] = fmaf(oa[r], S[r][c], part[c]);
+            }
+        // sums over each quad of lanes (DPP); the quads meet when the chunk is written
+        fvec<RC> qs;
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            float v = part[c];
+            v += dpp_f<kDppXor1>(v);
+            v += dpp_f<kDppXor2>(v);
+            qs[c] = v;
+        }
+        if ((ta & 3) == 0) *reinterpret_cast<fvec<RC> *>(sq + (k * NQ + (ta >> 2)) * BC + tc * RC) = qs;
+    };
+
+    if (t > 0) park();
+    // every load so far (the state, the first chunk) has landed before the loop:
+    // otherwise the loop's first use of the state would have to wait for the
+    // prefetch issued in front of it too
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt unconstrained
+    __syncthreads();
     for (int64_t t0 = 0; t0 < t; t0 += TT) {
         const int nk = t - t0 < TT ? (int)(t - t0) : TT;
         const bool more = t0 + TT < t;
         if (more) fetch(t0 + TT);
-        for (int k = 0; k < nk; ++k) {
-            float fa[RA], oa[RA], vc[RC];
+        if (nk == TT) {
 #pragma unroll
-            for (int r = 0; r < RA; ++r) {
-                fa[r] = stage[k * E + ta * RA + r];
-                oa[r] = stage[TT * E + k * E + ta * RA + r];
-            }
-#pragma unroll
-            for (int c = 0; c < RC; ++c) vc[c] = si[k * BC + tc * RC + c];
-            float part[RC];
-#pragma unroll
-            for (int c = 0; c < RC; ++c) part[c] = 0.0f;
-#pragma unroll
-            for (int r = 0; r < RA; ++r) {
-                const float kr = 1.0f - fa[r];
-#pragma unroll
-                for (int c = 0; c < RC; ++c) {
-                    S[r][c] = fmaf(fa[r], S[r][c], kr * vc[c]);
-                    part[c] = fmaf(oa[r], S[r][c], part[c]);
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < RC; ++c) {
-                float v = part[c];
-                v += dpp_f<kDppXor1>(v);
-                v += dpp_f<kDppXor2>(v);
-                v += dpp_f<kDppHalfMirror>(v);
-                v += dpp_f<kDppMirror>(v);
-                part[c] = v;
-            }
-            if (ta == 0) {
-#pragma unroll
-                for (int c = 0; c < RC; ++c) sy[k * BC + tc * RC + c] = part[c];
-            }
+            for (int k = 0; k < TT; ++k) token(k);
+        } else {
+            for (int k = 0; k < nk; ++k) token(k);
         }
-        __syncthreads();  // sy complete; stage and si no longer read
+        __syncthreads();  // sq complete; stage and si no longer read
         for (int q = tid; q < nk * (BC / 4); q += 256) {
             const int k = q / (BC / 4), c4 = q - k * (BC / 4);
-            *reinterpret_cast<float4 *>(y + row_base + (t0 + k) * d + ccol0 + 4 * c4) =
-                *reinterpret_cast<const float4 *>(sy + 4 * q);
+            const float *pq = sq + k * NQ * BC + 4 * c4;
+            float4 acc = *reinterpret_cast<const float4 *>(pq);
+#pragma unroll
+            for (int g = 1; g < NQ; ++g) {
+                const float4 v = *reinterpret_cast<const float4 *>(pq + g * BC);
+                acc.x += v.x;
+                acc.y += v.y;
+                acc.z += v.z;
+                acc.w += v.w;
+            }
+            *reinterpret_cast<float4 *>(y + row_base + (t0 + k) * d + ccol0 + 4 * c4) = acc;
         }
         if (more) park();
-        __syncthreads();  // the next chunk is in LDS; sy free again
+        __syncthreads();  // the next chunk is in LDS; sq free again
     }
 
-    // ---- the state block out, through LDS
+    // ---- the state block out, as it came in
     if (s_last) {
 #pragma unroll
-        for (int r = 0; r < RA; ++r)
+        for (int r = 0; r < RA; ++r) {
+            fvec<RC> v;
 #pragma unroll
-            for (int c = 0; c < RC; ++c) stage[(ta * RA + r) * BC + tc * RC + c] = S[r][c];
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < Sh::SL; ++j) {
-            const int q = tid + 256 * j;
-            if (q < Sh::S4) {
-                const int a = q / (BC / 4), c4 = q - a * (BC / 4);
-                *reinterpret_cast<float4 *>(s_last + sbase + (int64_t)a * E + 4 * c4) =
-                    *reinterpret_cast<const float4 *>(stage + a * BC + 4 * c4);
-            }
+            for (int c = 0; c < RC; ++c) v[c] = S[r][c];
+            *reinterpret_cast<fvec<RC> *>(s_last + sbase + (int64_t)(ta * RA + r) * E + tc * RC) = v;
         }
     }
+}
+
+int64_t hgrn2_workgroups(int64_t b, int64_t d, int e) {
+    const int bc = e == 16 ? H2Shape<16>::BC : e == 32 ? H2Shape<32>::BC : e == 64 ? H2Shape<64>::BC
+                                                                                 : H2Shape<128>::BC;
+    return b * (d / e) * (e / bc);
 }
 
 hipError_t launch_hgrn2_scan(const float *f, const float *i, const float *o, const float *s0, float *y,
                              float *s_last, int64_t b, int64_t t, int64_t d, int e, hipStream_t st,
                              const char **name) {
     const int heads = (int)(d / e);
-    const int64_t pairs = b * heads;
-    const int cbk = e < 32 ? 1 : e / 32;
-    const unsigned grid = (unsigned)(pairs * cbk);
+    const unsigned grid = (unsigned)hgrn2_workgroups(b, d, e);
     if (grid == 0) return hipSuccess;
     switch (e) {
         case 16: launch_k(hgrn2_scan_kernel<16>, grid, 256, 0, st, f, i, o, s0, y, s_last, t, d, heads); break;

@@ -831,8 +831,7 @@ mmf_status mmf_hgrn2_scan_fwd(const float *f, const float *i, const float *o, co
     const void *all[] = {f, i, o, s0, y, s_last};
     for (const void *p : all)
         if (reinterpret_cast<uintptr_t>(p) & 15u) return fail(MMF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-    const int64_t blocks = b * (d / e) * (e < 32 ? 1 : e / 32);
-    if (blocks > INT32_MAX) return fail(MMF_ERR_UNSUPPORTED, "b * d / min(e, 32) too large");
+    if (hgrn2_workgroups(b, d, (int)e) > INT32_MAX) return fail(MMF_ERR_UNSUPPORTED, "b * d too large");
     if (b == 0) return MMF_OK;
     const char *name = "hgrn2_scan";
     // timing label: a one-token call (a decode step) streams the state, a longer one computes
