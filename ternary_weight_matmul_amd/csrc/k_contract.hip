@@ -731,9 +731,11 @@ __global__ __launch_bounds__((gemv_bound<NG, SHARED_A, EPT>())) void tgemv_kerne
             load_slice(wave, bw, a, whole);
             mma_slice(bw, a, wave);
         }
-    } else if constexpr (MB > 2 || EPT > 2 || (EPT == 2 && CB * NG >= 4)) {
+    } else if constexpr (MB > 2 || (EPT > 2 && CB * NG > 8) || (EPT == 2 && CB * NG >= 4)) {
         // no registers for a second set (with two outputs per thread and four
-        // channel blocks a launch has fewer than 16 slices: one per wave, above)
+        // channel blocks a launch has fewer than 16 slices: one per wave, above;
+        // three or four outputs per thread come with a 512-thread bound, whose
+        // registers hold two sets for up to eight channel blocks)
         for (int sl = wave; sl < nslices; sl += nw) {
             uint32_t bw[CB][NG][WPL];
             i32x4 a[MB][NA][WPL];

@@ -59,9 +59,13 @@ BITLINEAR_CASES = [
     (8, 2048, 10250, "bf16", False),
     (16, 16384, 64, "bf16", False),
     (2, 8208, 100, "f32", True),
-    # eight channel blocks per workgroup (single group, 20480 outputs or more), ragged last block
+    # eight channel blocks per workgroup (single group, 20480 outputs or more), ragged last block;
+    # with more slices than its eight waves, the double-buffered slice loop (32 slices; 17 with
+    # the last one partial)
     (4, 1024, 20500, "bf16", True),
     (16, 2048, 32768, "f32", False),
+    (16, 8192, 20480, "f32", False),
+    (5, 4112, 20496, "bf16", True),
 ]
 
 
