@@ -22,7 +22,8 @@ Also printed in the same JSON line:
   configs      -- with --extras (default): every other config of the workload
                   (370M layer fp32; 370M and 2.7B stack prefills; the 1.3B
                   decode step at batch 1, 16, 64; the long-sequence scan; the
-                  expanded-state recurrence, prefill and decode step), each
+                  expanded-state recurrence, prefill and decode step; the
+                  decode GEMV streaming 67 and 268 MB of weights), each
                   with its own roofline (the fp32 vector ALU for the
                   expanded-state prefill), next to a measured HBM ceiling.
 --only LEG runs one config leg alone, for profiling it.
@@ -59,7 +60,8 @@ def parse():
     ap.add_argument("--extras", type=int, default=1,
                     help="0 skips the figures measured outside the timed steps (the other configs, the "
                          "measured HBM ceiling, derivatives, generation)")
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "prefill_b8", "ceiling", "bwd", "hgrn2"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "prefill_b8", "ceiling", "bwd", "hgrn2",
+                                       "gemv"],
                     help="run one config leg alone and print its JSON (for profiling a config)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (for scaling HBM counters)")
@@ -631,6 +633,33 @@ def leg_hgrn2(mmf, torch, dev, reps: int = 5, ceil=None, cpu: bool = True) -> di
     return res
 
 
+def leg_gemv(mmf, torch, dev, ceil=None, reps: int = 10) -> dict:
+    """Large FusedBitLinear products at 16 rows (bf16 in and out): the decode GEMV's streaming
+    rate on 67 MB (16384 x 16384) and 268 MB (32768 x 32768) of packed ternary weights, from
+    latent weights ~ N(0, 0.02) and x ~ N(0, 1). Roofline of the GEMV kernel itself (the row
+    quantiser in front of it is timed too, apart)."""
+    out = {}
+    for n, k in ((16384, 16384), (32768, 32768)):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        w = torch.randn((n, k), device=dev, generator=gen) * 0.02
+        pl = mmf.ternary_pack(w)
+        del w
+        x = torch.randn((16, k), device=dev, generator=gen).to(torch.bfloat16)
+
+        def run():
+            mmf.bitlinear_fwd(x, pl)
+
+        ms = event_ms(torch, run, reps)
+        kt = KernelTable().add(timed_records(mmf, run, reps), "decode", 1.0 / reps)
+        key = [kk for kk in kt.k if kk.startswith("tgemv")][0]
+        out["%dx%d" % (n, k)] = dict(weight_MB=round(n * k / 4 / 1e6, 1), us_per_call=round(ms * 1000, 2),
+                                     roofline=with_ceiling(kt.roofline(ms, key), ceil))
+        del pl, x
+        torch.cuda.empty_cache()
+    return dict(workload="FusedBitLinear at 16 rows, bf16, packed ternary weights of 67 and 268 MB", shapes=out)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -664,6 +693,8 @@ def run_only(args):
         res = leg_c5(mmf, torch, dev, cpu=cpu)
     elif args.only == "hgrn2":
         res = leg_hgrn2(mmf, torch, dev, cpu=cpu)
+    elif args.only == "gemv":
+        res = leg_gemv(mmf, torch, dev)
     elif args.only == "bwd":
         from ternary_weight_matmul_amd import synth
         d, inner, _ = synth.SHAPES["1.3B"]
@@ -844,6 +875,8 @@ def main():
         configs["c5"] = leg_c5(mmf, torch, dev, ceil=ceil, cpu=args.cpu_baseline != 0)
         torch.cuda.empty_cache()
         configs["hgrn2"] = leg_hgrn2(mmf, torch, dev, ceil=ceil, cpu=args.cpu_baseline != 0)
+        torch.cuda.empty_cache()
+        configs["gemv_stream"] = leg_gemv(mmf, torch, dev, ceil=ceil)
         torch.cuda.empty_cache()
         if T > 0:
             scan_bwd = measure_scan_bwd(mmf, torch, B, T, d, dev)

@@ -169,6 +169,100 @@ __global__ __launch_bounds__(256) void norm_quant_row_kernel(const T *__restrict
                             sumq ? sumq + row : nullptr, sh);
 }
 
+// Few rows too long for a 256-thread workgroup's registers (k > 8192): one
+// 1024-thread workgroup per row walks it in 4-element chunks, three passes at
+// most (Σx² and max |x| together, then max |y| only with a gain, then the
+// codes, stored four to a word); the later passes hit L2. The sixteen waves'
+// partial results meet in LDS in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(1024) void norm_quant_longrow_kernel(const T *__restrict__ x, int64_t m, int k,
+                                                                 const float *__restrict__ gain, float eps,
+                                                                 int8_t *__restrict__ q, float *__restrict__ s,
+                                                                 int32_t *__restrict__ sumq) {
+    __shared__ double shd[16];
+    __shared__ float shf[16];
+    __shared__ int shi[16];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t row = blockIdx.x;
+    const T *xr = x + row * (int64_t)k;
+    const int nch = k >> 2;
+    double ss = 0.0;
+    float xm = 0.0f;
+    for (int c = tid; c < nch; c += 1024) {
+        const float4 v = load_act4(xr, 4 * (int64_t)c);
+        ss += (double)v.x * (double)v.x;
+        ss += (double)v.y * (double)v.y;
+        ss += (double)v.z * (double)v.z;
+        ss += (double)v.w * (double)v.w;
+        xm = fmaxf(fmaxf(xm, fabsf(v.x)), fmaxf(fabsf(v.y), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    ss = wave_sum(ss);
+    xm = wave_max(xm);
+    if (lane == 0) {
+        shd[wave] = ss;
+        shf[wave] = xm;
+    }
+    __syncthreads();
+    double tot_ss = 0.0;
+    float tot_xm = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        tot_ss += shd[w];
+        tot_xm = fmaxf(tot_xm, shf[w]);
+    }
+    const float r = rms_factor(tot_ss, k, eps);
+    float amax;
+    if (!gain) {
+        amax = __fmul_rn(tot_xm, r);  // r > 0: max |x r| = (max |x|) r exactly
+    } else {
+        float ym = 0.0f;
+        for (int c = tid; c < nch; c += 1024) {
+            const float4 v = load_act4(xr, 4 * (int64_t)c);
+            const float4 g = *reinterpret_cast<const float4 *>(gain + 4 * (int64_t)c);
+            ym = fmaxf(ym, fabsf(__fmul_rn(__fmul_rn(v.x, r), g.x)));
+            ym = fmaxf(ym, fabsf(__fmul_rn(__fmul_rn(v.y, r), g.y)));
+            ym = fmaxf(ym, fabsf(__fmul_rn(__fmul_rn(v.z, r), g.z)));
+            ym = fmaxf(ym, fabsf(__fmul_rn(__fmul_rn(v.w, r), g.w)));
+        }
+        ym = wave_max(ym);
+        __syncthreads();  // shf is reused
+        if (lane == 0) shf[wave] = ym;
+        __syncthreads();
+        amax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) amax = fmaxf(amax, shf[w]);
+    }
+    const float sc = quant_scale(amax);
+    uint32_t *qw = reinterpret_cast<uint32_t *>(q + row * (int64_t)k);
+    int tot = 0;
+    for (int c = tid; c < nch; c += 1024) {
+        const float4 v = load_act4(xr, 4 * (int64_t)c);
+        float y0 = __fmul_rn(v.x, r), y1 = __fmul_rn(v.y, r), y2 = __fmul_rn(v.z, r), y3 = __fmul_rn(v.w, r);
+        if (gain) {
+            const float4 g = *reinterpret_cast<const float4 *>(gain + 4 * (int64_t)c);
+            y0 = __fmul_rn(y0, g.x);
+            y1 = __fmul_rn(y1, g.y);
+            y2 = __fmul_rn(y2, g.z);
+            y3 = __fmul_rn(y3, g.w);
+        }
+        const int a0 = quant_code(y0, sc), a1 = quant_code(y1, sc), a2 = quant_code(y2, sc), a3 = quant_code(y3, sc);
+        tot += a0 + a1 + a2 + a3;
+        qw[c] = pack_codes4(a0, a1, a2, a3);
+    }
+    if (sumq) {
+        tot = wave_sum_int(tot);
+        if (lane == 0) shi[wave] = tot;
+        __syncthreads();
+        if (tid == 0) {
+            int t = 0;
+#pragma unroll
+            for (int w = 0; w < 16; ++w) t += shi[w];
+            sumq[row] = t;
+        }
+    }
+    if (tid == 0) s[row] = sc;
+}
+
 constexpr int kFewRows = 2048;  // below this many rows a row gets a whole workgroup
 
 constexpr int kMaxCachedChunks = 32;  // 64 lanes * 32 chunks of 16 bytes per row in registers
@@ -201,6 +295,11 @@ static void norm_quant_dispatch(const T *x, int64_t m, int k, const float *gain,
 #undef MMF_NQB
         }
         if (path) *path += std::string("norm_quant_row<") + tn + "," + std::to_string(nvb) + ">;";
+        return;
+    }
+    if (m < kFewRows && k % 4 == 0) {
+        launch_k(norm_quant_longrow_kernel<T>, (unsigned)m, 1024, 0, st, x, m, k, gain, eps, q, s, sumq);
+        if (path) *path += std::string("norm_quant_longrow<") + tn + ">;";
         return;
     }
     const dim3 grid((unsigned)((m + 3) / 4)), block(256);

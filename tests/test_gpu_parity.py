@@ -66,6 +66,9 @@ BITLINEAR_CASES = [
     (16, 2048, 32768, "f32", False),
     (16, 8192, 20480, "f32", False),
     (5, 4112, 20496, "bf16", True),
+    # rows longer than 8192 at few rows: a 1024-thread quantiser workgroup per row
+    (3, 12288, 40, "f32", True),
+    (2, 9008, 24, "bf16", True),
 ]
 
 
