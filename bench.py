@@ -637,13 +637,19 @@ def leg_gemv(mmf, torch, dev, ceil=None, reps: int = 10) -> dict:
     """Large FusedBitLinear products at 16 rows (bf16 in and out): the decode GEMV's streaming
     rate on 67 MB (16384 x 16384) and 268 MB (32768 x 32768) of packed ternary weights, from
     latent weights ~ N(0, 0.02) and x ~ N(0, 1). Roofline of the GEMV kernel itself (the row
-    quantiser in front of it is timed too, apart)."""
+    quantiser in front of it is timed too, apart); the packing of those weights is timed once."""
     out = {}
     for n, k in ((16384, 16384), (32768, 32768)):
         gen = torch.Generator(device=dev)
         gen.manual_seed(7)
         w = torch.randn((n, k), device=dev, generator=gen) * 0.02
-        pl = mmf.ternary_pack(w)
+        pl = mmf.ternary_pack(w)  # warm-up (and the weights used below)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        mmf.ternary_pack(w)
+        b.record()
+        torch.cuda.synchronize()
+        pack_ms = a.elapsed_time(b)
         del w
         x = torch.randn((16, k), device=dev, generator=gen).to(torch.bfloat16)
 
@@ -653,8 +659,13 @@ def leg_gemv(mmf, torch, dev, ceil=None, reps: int = 10) -> dict:
         ms = event_ms(torch, run, reps)
         kt = KernelTable().add(timed_records(mmf, run, reps), "decode", 1.0 / reps)
         key = [kk for kk in kt.k if kk.startswith("tgemv")][0]
+        # the packer reads the fp32 latent weights twice (mean |W|, then the codes) and writes 2 bits each
+        pack_bytes = n * k * 8.25
         out["%dx%d" % (n, k)] = dict(weight_MB=round(n * k / 4 / 1e6, 1), us_per_call=round(ms * 1000, 2),
-                                     roofline=with_ceiling(kt.roofline(ms, key), ceil))
+                                     roofline=with_ceiling(kt.roofline(ms, key), ceil),
+                                     pack=dict(ms=round(pack_ms, 3), GBs=round(pack_bytes / (pack_ms / 1e3) / 1e9, 1),
+                                               frac_hbm=round(pack_bytes / (pack_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                               note="two passes over the fp32 weights: 8.25 B per weight"))
         del pl, x
         torch.cuda.empty_cache()
     return dict(workload="FusedBitLinear at 16 rows, bf16, packed ternary weights of 67 and 268 MB", shapes=out)

@@ -473,13 +473,30 @@ constexpr int kPackPartials = 512;
 
 size_t pack_workspace_bytes() { return kPackPartials * sizeof(double); }
 
+// Sum of |w| over one block's range of the weights (a multiple of 256 elements;
+// the whole tensor a multiple of 16): 16-byte loads, four of them in flight per
+// thread, four binary64 accumulators, then a fixed-order tree over the block.
 __global__ __launch_bounds__(256) void abs_sum_partial_kernel(const float *__restrict__ w, int64_t count,
                                                               int64_t per_block, double *__restrict__ partial) {
     __shared__ double red[256];
     const int64_t lo = (int64_t)blockIdx.x * per_block;
     const int64_t hi = lo + per_block < count ? lo + per_block : count;
-    double acc = 0.0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) acc += fabs((double)w[i]);
+    const float4 *w4 = reinterpret_cast<const float4 *>(w);
+    const int64_t hi4 = hi >> 2;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    auto add4 = [](double acc, float4 v) {
+        return acc + (((double)fabsf(v.x) + (double)fabsf(v.y)) + ((double)fabsf(v.z) + (double)fabsf(v.w)));
+    };
+    int64_t i = (lo >> 2) + threadIdx.x;
+    for (; i + 768 < hi4; i += 1024) {
+        const float4 v0 = w4[i], v1 = w4[i + 256], v2 = w4[i + 512], v3 = w4[i + 768];
+        a0 = add4(a0, v0);
+        a1 = add4(a1, v1);
+        a2 = add4(a2, v2);
+        a3 = add4(a3, v3);
+    }
+    for (; i < hi4; i += 256) a0 = add4(a0, w4[i]);
+    const double acc = (a0 + a1) + (a2 + a3);
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
