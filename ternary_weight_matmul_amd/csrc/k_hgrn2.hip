@@ -16,9 +16,9 @@
 // of lanes per token and a sum of the four quads' partials, in LDS, once per
 // chunk of tokens (fixed order). Per token a thread does 3 RA*RC vector
 // operations (S - v, then f (S - v) + v, then the readout's multiply-add) and
-// 2 DPP adds per column: the recurrence is
-// bound by the vector ALU (about 5 e^2 flops per token and head against 16 e
-// bytes of HBM traffic). The gates of TT tokens are staged through LDS with
+// 2 DPP adds per column: the recurrence is bound by the vector ALU (about
+// 5 e^2 flops per token and head against 16 e bytes of HBM traffic). The
+// gates of TT tokens are staged through LDS with
 // coalesced loads issued one chunk ahead; the outputs of a chunk leave as
 // 16-byte stores. The state block goes straight between HBM and registers as
 // one RC-float piece per row and thread (16 bytes for heads of 64 and 128).
@@ -190,8 +190,8 @@ __global__ __launch_bounds__(256) void hgrn2_scan_kernel(const float *__restrict
             const float *pq = sq + k * NQ * BC + 4 * c4;
             float4 acc = *reinterpret_cast<const float4 *>(pq);
 #pragma unroll
-            for (int g = 1; g < NQ; ++g) {
-                const float4 v = *reinterpret_cast<const float4 *>(pq + g * BC);
+            for (int qd = 1; qd < NQ; ++qd) {
+                const float4 v = *reinterpret_cast<const float4 *>(pq + qd * BC);
                 acc.x += v.x;
                 acc.y += v.y;
                 acc.z += v.z;
