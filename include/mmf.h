@@ -49,22 +49,27 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Enumerated values travel as plain 32-bit integers, so any value a caller
+ * passes is well defined and is checked (an unknown one is INVALID_ARG). */
+typedef int32_t mmf_status;
+enum {
     MMF_OK = 0,
     MMF_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad enum value      */
     MMF_ERR_UNSUPPORTED = 2,   /* valid but not handled (e.g. k % 16 != 0)     */
     MMF_ERR_WORKSPACE = 3,     /* workspace missing, too small or misaligned   */
     MMF_ERR_HIP = 4            /* a HIP launch or runtime call failed          */
-} mmf_status;
+};
 
-typedef enum { MMF_F32 = 0, MMF_BF16 = 1 } mmf_dtype;
+typedef int32_t mmf_dtype;
+enum { MMF_F32 = 0, MMF_BF16 = 1 };
 
 /* [R1] the recurrence has a step-wise and a chunked implementation. */
-typedef enum {
+typedef int32_t mmf_scan_mode;
+enum {
     MMF_SCAN_AUTO = 0,         /* library picks from b*d and t                 */
     MMF_SCAN_RECURRENT = 1,    /* sequential in t per channel: same order as the definition */
     MMF_SCAN_CHUNK = 2         /* t split in chunks, carries composed as (a,b) pairs */
-} mmf_scan_mode;
+};
 
 /*
  * One packed ternary weight ([R1] weight_quant; [R4] section 5.1 packing).

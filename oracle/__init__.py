@@ -52,7 +52,8 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libmmf_oracle.so")
+# MMF_ORACLE_LIB: another build of the same C source (the sanitizer check loads one)
+_LIB_PATH = os.environ.get("MMF_ORACLE_LIB") or os.path.join(_HERE, "libmmf_oracle.so")
 _lib = None
 
 

@@ -13,7 +13,8 @@ from dataclasses import dataclass
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmmf.so")
+# MMF_LIB: another build of the same sources (the host-sanitizer check loads one)
+LIB_PATH = os.environ.get("MMF_LIB") or os.path.join(_HERE, "libmmf.so")
 
 __all__ = [
     "MMFError", "load", "LIB_PATH", "SYMBOLS", "PackedLinear", "LayerParams", "LayerProbe",
