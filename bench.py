@@ -42,6 +42,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed, 256 CUs at 2.4 GHz)
+FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
@@ -166,14 +167,16 @@ def algorithmic(kernel: str, m: int, n: int, k: int):
     norm_quant<T> (m rows of k): x read (sizeof T) + codes written (1 B) per element, 8 B per row.
     gnorm_quant<T>: h (fp32) and g (sizeof T) read + codes written per element, 8 B per row.
     scan (m = b t, k = d): f and x~ read, h written, 12 B per element.
-    hgrn2_scan<e> / hgrn2_step<e> (m = b t, n = d, k = e, the expanded-state recurrence): per
-      token and head of e, 5 e^2 + e flops (the state's multiply, multiply-add and readout
-      multiply-add, and 1 - f); f, i, o read and y written, 16 B per (b, t, channel); a step
-      (t = 1, m = b) also reads and writes the state, 8 e bytes per (b, channel).
+    hgrn2_scan<e> / hgrn2_chunk<e> / hgrn2_step<e> (m = b t, n = d, k = e, the expanded-state
+      recurrence, step-wise / chunked / one token): per token and head of e, 5 e^2 + e flops of
+      the definition (the state's multiply, multiply-add and readout multiply-add, and 1 - f;
+      the chunked form's own products are not counted); f, i, o read and y written, 16 B per
+      (b, t, channel); a step (t = 1, m = b) also reads and writes the state, 8 e bytes per
+      (b, channel).
     scan_bwd (m = b t, k = d): dh, f and h read, dx and df written, 20 B per element.
     """
     base, args = _kind(kernel)
-    if base in ("hgrn2_scan", "hgrn2_step"):
+    if base in ("hgrn2_scan", "hgrn2_step", "hgrn2_chunk"):
         e = int(args[0])
         nbytes = 16.0 * m * n + (8.0 * m * n * e if base == "hgrn2_step" else 0.0)
         return m * n * (5.0 * e + 1.0), nbytes
@@ -213,6 +216,7 @@ KERNEL_SOURCES = {
     "gnorm_quant": ["k_quant.hip", "row_quant.hpp"] + _COMMON,
     "scan": ["k_scan.hip"] + _COMMON,
     "hgrn2_scan": ["k_hgrn2.hip"] + _COMMON,
+    "hgrn2_chunk": ["k_hgrn2.hip"] + _COMMON,
     "hgrn2_step": ["k_hgrn2.hip"] + _COMMON,
 }
 
@@ -304,6 +308,9 @@ class KernelTable:
                         unit="TFLOP/s")
         elif e["name"].startswith("hgrn2_scan"):
             roof = dict(bound="alu", achieved=round(e["ops"] / avg_s / 1e12, 2), peak=FP32_VECTOR_PEAK_TFLOPS,
+                        unit="TFLOP/s")
+        elif e["name"].startswith("hgrn2_chunk"):
+            roof = dict(bound="mfma", achieved=round(e["ops"] / avg_s / 1e12, 2), peak=FP32_MFMA_PEAK_TFLOPS,
                         unit="TFLOP/s")
         else:
             roof = dict(bound="hbm", achieved=round(e["bytes"] / avg_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
@@ -582,9 +589,10 @@ def leg_c5(mmf, torch, dev, reps: int = 10, ceil=None, cpu: bool = True) -> dict
 
 def leg_hgrn2(mmf, torch, dev, reps: int = 5, ceil=None, cpu: bool = True) -> dict:
     """The expanded-state recurrence at 1.3B width, heads of 128: a 16 x 2048-token prefill
-    (value = tokens/s, bound by the fp32 vector ALU) and a decode step at batch 16 (one token,
-    the state read and written in place, HBM-bound). f = sigmoid(N(2,1)), i, o ~ N(0,1), the
-    initial state ~ N(0,1). The oracle runs one (sequence, head) pair of the prefill."""
+    (value = tokens/s; the chunked form on fp32 MFMA, with the step-wise form, bound by the fp32
+    vector ALU, timed beside it) and a decode step at batch 16 (one token, the state read and
+    written in place, HBM-bound). f = sigmoid(N(2,1)), i, o ~ N(0,1), the initial state ~ N(0,1).
+    The oracle runs one (sequence, head) pair of the prefill."""
     b, t, d, e = 16, 2048, 2048, 128
     gen = torch.Generator(device=dev)
     gen.manual_seed(6)
@@ -603,6 +611,13 @@ def leg_hgrn2(mmf, torch, dev, reps: int = 5, ceil=None, cpu: bool = True) -> di
     res = dict(workload="HGRN2 expanded-state recurrence: d=2048, heads of 128, B=16 x T=2048, fp32",
                value=round(b * t / (ms / 1000), 1), unit="tokens/s", ms=round(ms, 3),
                roofline=kt.roofline(ms), kernels=kt.breakdown())
+
+    def run_steps():
+        mmf.hgrn2_scan_fwd(f, i, o, e, s0, out=y, s_last=s_last, mode="recurrent")
+
+    rms = event_ms(torch, run_steps, reps)
+    kr = KernelTable().add(timed_records(mmf, run_steps, reps), "prefill", 1.0 / reps)
+    res["prefill_step_wise"] = dict(ms=round(rms, 3), roofline=kr.roofline(rms))
     # decode: one token per sequence, the state updated in place
     f1, i1, o1 = f[:, :1].contiguous(), i[:, :1].contiguous(), o[:, :1].contiguous()
     st = s0.clone()

@@ -294,14 +294,20 @@ mmf_status mmf_hgrn_scan_bwd(const float *f, const float *h, const float *h0, co
  *  f, i, o, y : [b][t][d] fp32 (head n owns channels n*e .. n*e+e-1);
  *  s0, s_last : [b][d/e][e][e] fp32 or NULL (s0 NULL: zeros; s_last NULL: not
  *  written). s_last may equal s0 (in place: a decode step is t = 1); y and
- *  s_last may not alias anything else. The tokens run in order, each state
- *  block held in registers, so a call over t tokens and t calls of one token
- *  give the same bits. No workspace. t may be 0 (s_last = s0).
+ *  s_last may not alias anything else. No workspace. t may be 0 (s_last = s0).
+ *  RECURRENT runs the tokens in order, each state block held in registers, so
+ *  a call over t tokens and t calls of one token give the same bits. CHUNK
+ *  (heads of 64 or 128) takes 16 tokens at a time: with every decay a product
+ *  of gates, Y = Q~ S0 + A V and S1 = diag(prod f) S0 + K^T V, where
+ *  Q~[t][a] = o_t[a] prod_{r<=t} f_r[a], K^[s][a] = (1 - f_s[a]) prod_{r>s} f_r[a]
+ *  and A[t][s] = sum_a o_t[a] (1 - f_s[a]) prod_{s<r<=t} f_r[a] (s <= t): the
+ *  same value up to rounding. AUTO takes CHUNK from 64 tokens on where it can.
  *  e in {16, 32, 64, 128}, d a multiple of e; every tensor 16-byte aligned.
- *  Errors: INVALID_ARG, UNSUPPORTED (e), HIP.
+ *  Errors: INVALID_ARG, UNSUPPORTED (e; CHUNK with e < 64), HIP.
  */
 mmf_status mmf_hgrn2_scan_fwd(const float *f, const float *i, const float *o, const float *s0, float *y,
-                              float *s_last, int64_t b, int64_t t, int64_t d, int64_t e, hipStream_t stream);
+                              float *s_last, int64_t b, int64_t t, int64_t d, int64_t e, mmf_scan_mode mode,
+                              hipStream_t stream);
 
 /*
  * mmf_layer_fwd -- one HGRNBit block over b sequences of t tokens ([R3]):

@@ -107,7 +107,7 @@ def load():
     lib.mmf_hgrn_scan_workspace_size.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
     lib.mmf_hgrn_scan_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, ctypes.c_int, P, SZ, P]
     lib.mmf_hgrn_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
-    lib.mmf_hgrn2_scan_fwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.mmf_hgrn2_scan_fwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_int, P]
     lib.mmf_layer_workspace_size.argtypes = [ctypes.POINTER(CLayerWeights), I64, I64, ctypes.POINTER(SZ)]
     lib.mmf_layer_fwd.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, I64, P, P,
                                   ctypes.c_int, P, SZ, ctypes.POINTER(CLayerProbe), P]
@@ -349,9 +349,10 @@ def hgrn_scan_bwd(f, h, dh, h0=None, dh_last=None, mode: str = "auto", dx=None, 
     return dx, df, dh0
 
 
-def hgrn2_scan_fwd(f, i, o, e: int, s0=None, out=None, s_last=None):
+def hgrn2_scan_fwd(f, i, o, e: int, s0=None, out=None, s_last=None, mode: str = "auto"):
     """The expanded-state recurrence (mmf_hgrn2_scan_fwd) over f, i, o [b, t, d] fp32 with heads
-    of e channels; s0 / s_last [b, d / e, e, e] fp32 or None (s_last may be s0). Returns y."""
+    of e channels; s0 / s_last [b, d / e, e, e] fp32 or None (s_last may be s0); mode "auto",
+    "recurrent" or "chunk". Returns y."""
     torch = _torch()
     lib = load()
     if f.shape != i.shape or f.shape != o.shape or f.dim() != 3:
@@ -362,7 +363,7 @@ def hgrn2_scan_fwd(f, i, o, e: int, s0=None, out=None, s_last=None):
     b, t, d = f.shape
     y = out if out is not None else torch.empty_like(f)
     _check(lib.mmf_hgrn2_scan_fwd(_ptr(f), _ptr(i), _ptr(o), _ptr(s0), _ptr(y), _ptr(s_last), b, t, d, e,
-                                  _stream()))
+                                  SCAN_MODES[mode], _stream()))
     return y
 
 

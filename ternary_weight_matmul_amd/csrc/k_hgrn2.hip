@@ -31,6 +31,7 @@ namespace mmf {
 
 template <int N>
 using fvec = float __attribute__((ext_vector_type(N)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <int E>
 struct H2Shape {
@@ -215,6 +216,287 @@ __global__ __launch_bounds__(256) void hgrn2_scan_kernel(const float *__restrict
     }
 }
 
+// ----------------------------------------------------------------------------
+// Chunked form (the pages name a step-wise and a chunked implementation of the
+// recurrence). Over a chunk of C tokens starting from the state S0, with every
+// decay a plain product of gates (no logarithms or divisions, so nothing can
+// overflow however small f gets):
+//   Q~[t][a]  = o_t[a] * prod_{r<=t} f_r[a]             (decay from the chunk start)
+//   K^[s][a]  = (1 - f_s[a]) * prod_{s<r<C} f_r[a]      (decay to the chunk end)
+//   A[t][s]   = sum_a o_t[a] (1 - f_s[a]) prod_{s<r<=t} f_r[a]   (s <= t, else 0)
+//             = (Q~ K~^T)[t][s], K~[s][a] = (1 - f_s[a]) / prod_{r<=s} f_r[a], on MFMA when every
+//               gate of the chunk is at least 2^-6 (1 / prod f then stays below 2^96), else
+//               as running products of the gates
+//   Y  = Q~ S0 + A V                  (C x BC: the chunk's outputs)
+//   S1 = diag(prod_{r<C} f_r) S0 + K^T V
+// (V = the chunk's input rows of the block's columns). The products run on
+// fp32 MFMA (v_mfma_f32_16x16x4_f32); wave w owns the block's columns
+// 16w .. 16w+15, holds their E x 16 slice of the state as E/16 accumulator
+// tiles, and moves it through its own LDS region to use it as an operand.
+// Gates of the next chunk load into registers during the current one, as in
+// the step-wise kernel. Tokens past the sequence end act as f = 1, o = 0, i = 0.
+// Below this gate the chunk's A sums run with the decays as running products:
+// from it up, 1 / prod f over 16 tokens stays below 2^96.
+constexpr float kChunkMinGate = 0.015625f;  // 2^-6
+
+template <int E>
+struct H2Chunk {
+    static constexpr int C = 16;          // tokens per chunk
+    static constexpr int BC = 64;         // state columns per workgroup: 4 waves x 16
+    static constexpr int AT = E / 16;     // 16-row tiles of a wave's state slice
+    static constexpr int RA = E / 16;     // rows per thread in the A sums (16 threads per s)
+    static constexpr int G4 = C * E / 4;  // float4s of one gate per chunk
+    static constexpr int I4 = C * BC / 4; // float4s of i per chunk
+    static constexpr int GL = (G4 + 255) / 256;
+    // LDS row strides chosen so that the MFMA operand reads (16 lanes along one index, 4 lane
+    // groups along the other) spread over the banks
+    static constexpr int QS = C + 1;       // Q~, K~ / K^ and A stored transposed: [a][t], [s][t]
+    static constexpr int VS = BC + 16;     // V [t][column]
+    static_assert(E == 64 || E == 128, "chunked form: heads of 64 or 128");
+    static_assert(I4 == 256 && GL <= 2, "prefetch slots");
+};
+
+template <int E>
+__global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__restrict__ f, const float *__restrict__ xi,
+                                                          const float *__restrict__ o, const float *s0, float *y,
+                                                          float *s_last, int64_t t, int64_t d, int heads) {
+    using Sh = H2Chunk<E>;
+    constexpr int C = Sh::C, BC = Sh::BC, AT = Sh::AT, RA = Sh::RA, CBK = E / BC;
+    constexpr int QS = Sh::QS, VS = Sh::VS;
+    __shared__ __attribute__((aligned(16))) float sf[C * E];   // f of the chunk, [t][a]
+    __shared__ __attribute__((aligned(16))) float so[C * E];   // o of the chunk, [t][a]
+    __shared__ __attribute__((aligned(16))) float sv[C * VS];  // i of the chunk, [t][column]
+    __shared__ __attribute__((aligned(16))) float sq[E * QS];  // Q~, [a][t]
+    __shared__ __attribute__((aligned(16))) float sa[C * QS];  // A, [s][t]
+    __shared__ __attribute__((aligned(16))) float skt[E * QS]; // K~ or K^, [a][t]
+    // the waves' partial A tiles, [t][s]: in the o buffer, no longer read once Q~ is formed
+    float (*spart)[C * C] = reinterpret_cast<float (*)[C * C]>(so);
+    static_assert(4 * C * C <= C * E, "partial A tiles fit in the o buffer");
+    __shared__ float sdec[E];                                  // prod f over the chunk
+    __shared__ __attribute__((aligned(16))) float ss[4][E * 16];  // each wave's state slice, [a][16]
+
+    const int G = gridDim.x, g = blockIdx.x;
+    const int lin = (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g;
+    const int pair = lin / CBK, cblk = lin - pair * CBK;
+    const int64_t bi = pair / heads;
+    const int head = pair - (int)bi * heads;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+    const int64_t col0 = (int64_t)head * E;
+    const int64_t ccol0 = col0 + (int64_t)cblk * BC;
+    const int64_t row_base = bi * t * d;
+    const int64_t sbase = ((int64_t)pair * E) * E + (int64_t)cblk * BC + 16 * wave;  // state (pair, 0, wave's first column)
+
+    float4 pf0, pf1, po0, po1, pi0;
+    auto gate_off = [&](int64_t t0, int j) __attribute__((always_inline)) {
+        const int q = min(tid + 256 * j, Sh::G4 - 1);
+        const int k = q / (E / 4), c4 = q - k * (E / 4);
+        const int64_t tk = t0 + k < t ? t0 + k : t - 1;  // rows past t: any valid row, replaced below
+        return row_base + tk * d + col0 + 4 * c4;
+    };
+    auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
+        const int64_t off0 = gate_off(t0, 0);
+        pf0 = *reinterpret_cast<const float4 *>(f + off0);
+        po0 = *reinterpret_cast<const float4 *>(o + off0);
+        if constexpr (Sh::GL == 2) {
+            const int64_t off1 = gate_off(t0, 1);
+            pf1 = *reinterpret_cast<const float4 *>(f + off1);
+            po1 = *reinterpret_cast<const float4 *>(o + off1);
+        }
+        const int k = tid / (BC / 4), c4 = tid - k * (BC / 4);
+        const int64_t tk = t0 + k < t ? t0 + k : t - 1;
+        pi0 = *reinterpret_cast<const float4 *>(xi + row_base + tk * d + ccol0 + 4 * c4);
+    };
+    // tokens at or past `nk` of the chunk become f = 1, o = 0, i = 0 (selected per
+    // component: a select of whole float4 values would go through memory)
+    auto or4 = [](bool in, float4 v, float w) __attribute__((always_inline)) {
+        return make_float4(in ? v.x : w, in ? v.y : w, in ? v.z : w, in ? v.w : w);
+    };
+    auto park = [&](int nk) __attribute__((always_inline)) {
+        {
+            const bool in = tid / (E / 4) < nk;
+            *reinterpret_cast<float4 *>(sf + 4 * tid) = or4(in, pf0, 1.0f);
+            *reinterpret_cast<float4 *>(so + 4 * tid) = or4(in, po0, 0.0f);
+        }
+        if constexpr (Sh::GL == 2) {
+            const int q = tid + 256;
+            const bool in = q / (E / 4) < nk;
+            *reinterpret_cast<float4 *>(sf + 4 * q) = or4(in, pf1, 1.0f);
+            *reinterpret_cast<float4 *>(so + 4 * q) = or4(in, po1, 0.0f);
+        }
+        *reinterpret_cast<float4 *>(sv + (tid / (BC / 4)) * VS + 4 * (tid % (BC / 4))) =
+            or4(tid / (BC / 4) < nk, pi0, 0.0f);
+    };
+
+    if (t > 0) fetch(0);
+    // the wave's state slice: tile i holds rows 16i + 4 lg + j, column 16 wave + l16 (accumulator layout)
+    float st[AT][4];
+    if (s0) {
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st[i][j] = s0[sbase + (int64_t)(16 * i + 4 * lg + j) * E + l16];
+    } else {
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st[i][j] = 0.0f;
+    }
+    if (t > 0) park(t < C ? (int)t : C);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state and the first chunk have landed
+    __syncthreads();
+
+    float *myss = ss[wave];
+    for (int64_t t0 = 0; t0 < t; t0 += C) {
+        const bool more = t0 + C < t;
+        if (more) fetch(t0 + C);
+
+        // -- decays, one thread per row a: Q~ and the chunk's total decay; K~ = (1 - f_s) /
+        // prod_{r<=s} f_r and K^ held in registers until the workgroup knows whether any gate of
+        // the chunk is small enough for 1 / prod f to leave the range that keeps K~ exact to a
+        // few ulp; then skt holds K~ (A on MFMA, K^ = K~ * total decay) or K^ (the direct sums)
+        bool tiny = false;
+        float kt[C];
+        if (tid < E) {
+            const int a = tid;
+            float p = 1.0f;
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const float fk = sf[k * E + a];
+                tiny |= fk < kChunkMinGate;
+                p *= fk;
+                sq[a * QS + k] = so[k * E + a] * p;
+                kt[k] = __fdiv_rn(1.0f - fk, p);
+            }
+            sdec[a] = p;
+        }
+        const bool direct = __syncthreads_or(tiny);
+        if (tid < E) {
+            const int a = tid;
+            if (!direct) {
+#pragma unroll
+                for (int k = 0; k < C; ++k) skt[a * QS + k] = kt[k];
+            } else {
+                float suf = 1.0f;  // K^ as suffix products of the gates
+#pragma unroll
+                for (int k = C - 1; k >= 0; --k) {
+                    const float fk = sf[k * E + a];
+                    skt[a * QS + k] = (1.0f - fk) * suf;
+                    suf *= fk;
+                }
+            }
+        }
+        __syncthreads();  // Q~, skt and the decays are in LDS
+        if (!direct) {
+            // -- A = Q~ K~^T on MFMA (A[t][s] = sum_a Q~[t][a] K~[s][a] = sum_a o_t (1 - f_s)
+            // prod_{s<r<=t} f_r), the E rows split over the four waves, the partial tiles
+            // summed in a fixed order; entries with s > t are dropped
+            f32x4v pa = {0.f, 0.f, 0.f, 0.f};
+            float qa[E / 16], kb[E / 16];
+#pragma unroll
+            for (int q = 0; q < E / 16; ++q) {
+                const int row = wave * (E / 4) + 4 * q + lg;
+                qa[q] = sq[row * QS + l16];
+                kb[q] = skt[row * QS + l16];
+            }
+#pragma unroll
+            for (int q = 0; q < E / 16; ++q) pa = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[q], kb[q], pa, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) spart[wave][(4 * lg + j) * 16 + l16] = pa[j];  // [t][s]
+            __syncthreads();
+            const int tI = tid >> 4, sI = tid & 15;
+            const float v = ((spart[0][tI * 16 + sI] + spart[1][tI * 16 + sI]) + spart[2][tI * 16 + sI]) +
+                            spart[3][tI * 16 + sI];
+            sa[sI * QS + tI] = sI <= tI ? v : 0.0f;
+        } else {
+            // -- A[t][s] with the decays as running products: thread (s, ac) sums rows
+            // ac*RA .. ac*RA+RA-1; the 16 ac meet by DPP
+            const int sI = tid >> 4, ac = tid & 15;
+            float dk[RA];
+#pragma unroll
+            for (int r = 0; r < RA; ++r) dk[r] = 1.0f - sf[sI * E + ac * RA + r];
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                float pk = 0.0f;
+#pragma unroll
+                for (int r = 0; r < RA; ++r) {
+                    if (k > sI) dk[r] *= sf[k * E + ac * RA + r];
+                    pk = fmaf(so[k * E + ac * RA + r], dk[r], pk);
+                }
+                pk = k >= sI ? pk : 0.0f;
+                pk += dpp_f<kDppXor1>(pk);
+                pk += dpp_f<kDppXor2>(pk);
+                pk += dpp_f<kDppHalfMirror>(pk);
+                pk += dpp_f<kDppMirror>(pk);
+                if (ac == 0) sa[sI * QS + k] = pk;
+            }
+        }
+        // -- the wave's state slice into its LDS region, [a][16]
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) myss[(16 * i + 4 * lg + j) * 16 + l16] = st[i][j];
+        __syncthreads();  // sq, sk, sa, sdec and every slice written
+
+        // -- Y = Q~ S0 + A V for the wave's 16 columns: every operand is read from LDS
+        // first, then the MFMAs run back to back on two accumulators
+        f32x4v y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int q = 0; q < E / 4; q += 2) {
+            y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[(4 * q + lg) * QS + l16], myss[(4 * q + lg) * 16 + l16], y0,
+                                                      0, 0, 0);
+            y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[(4 * q + 4 + lg) * QS + l16],
+                                                      myss[(4 * q + 4 + lg) * 16 + l16], y1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < C / 4; q += 2) {
+            y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[(4 * q + lg) * QS + l16], sv[(4 * q + lg) * VS + 16 * wave + l16],
+                                                      y0, 0, 0, 0);
+            y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[(4 * q + 4 + lg) * QS + l16],
+                                                      sv[(4 * q + 4 + lg) * VS + 16 * wave + l16], y1, 0, 0, 0);
+        }
+        const f32x4v yacc = y0 + y1;
+        // -- S1 = diag(decay) S0 + K^T V (the V operands serve every tile)
+        float kv[C / 4], ka[AT][C / 4];
+#pragma unroll
+        for (int i = 0; i < AT; ++i) {
+            const float ks = direct ? 1.0f : sdec[16 * i + l16];  // K^ = K~ * total decay
+#pragma unroll
+            for (int q = 0; q < C / 4; ++q) ka[i][q] = skt[(16 * i + l16) * QS + 4 * q + lg] * ks;
+        }
+#pragma unroll
+        for (int q = 0; q < C / 4; ++q) kv[q] = sv[(4 * q + lg) * VS + 16 * wave + l16];
+        f32x4v acc[AT];
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = st[i][j] * sdec[16 * i + 4 * lg + j];
+#pragma unroll
+        for (int q = 0; q < C / 4; ++q)
+#pragma unroll
+            for (int i = 0; i < AT; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[i][q], kv[q], acc[i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st[i][j] = acc[i][j];
+        // -- the chunk's outputs: row 4 lg + j, column 16 wave + l16
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t tk = t0 + 4 * lg + j;
+            if (tk < t) y[row_base + tk * d + ccol0 + 16 * wave + l16] = yacc[j];
+        }
+        __syncthreads();  // every read of this chunk's LDS done
+        if (more) park(t - (t0 + C) < C ? (int)(t - (t0 + C)) : C);
+        __syncthreads();
+    }
+
+    if (s_last) {
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s_last[sbase + (int64_t)(16 * i + 4 * lg + j) * E + l16] = st[i][j];
+    }
+}
+
 int64_t hgrn2_workgroups(int64_t b, int64_t d, int e) {
     const int bc = e == 16 ? H2Shape<16>::BC : e == 32 ? H2Shape<32>::BC : e == 64 ? H2Shape<64>::BC
                                                                                  : H2Shape<128>::BC;
@@ -222,11 +504,20 @@ int64_t hgrn2_workgroups(int64_t b, int64_t d, int e) {
 }
 
 hipError_t launch_hgrn2_scan(const float *f, const float *i, const float *o, const float *s0, float *y,
-                             float *s_last, int64_t b, int64_t t, int64_t d, int e, hipStream_t st,
+                             float *s_last, int64_t b, int64_t t, int64_t d, int e, bool chunk, hipStream_t st,
                              const char **name) {
     const int heads = (int)(d / e);
     const unsigned grid = (unsigned)hgrn2_workgroups(b, d, e);
     if (grid == 0) return hipSuccess;
+    if (chunk) {
+        switch (e) {
+            case 64: launch_k(hgrn2_chunk_kernel<64>, grid, 256, 0, st, f, i, o, s0, y, s_last, t, d, heads); break;
+            case 128: launch_k(hgrn2_chunk_kernel<128>, grid, 256, 0, st, f, i, o, s0, y, s_last, t, d, heads); break;
+            default: return hipErrorInvalidValue;
+        }
+        if (name) *name = e == 64 ? "hgrn2_chunk<64>" : "hgrn2_chunk<128>";
+        return hipGetLastError();
+    }
     switch (e) {
         case 16: launch_k(hgrn2_scan_kernel<16>, grid, 256, 0, st, f, i, o, s0, y, s_last, t, d, heads); break;
         case 32: launch_k(hgrn2_scan_kernel<32>, grid, 256, 0, st, f, i, o, s0, y, s_last, t, d, heads); break;

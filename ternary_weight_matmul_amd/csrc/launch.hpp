@@ -107,10 +107,11 @@ hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h
                        std::string *path);
 
 // The expanded-state recurrence (k_hgrn2.hip): e in {16, 32, 64, 128}, d % e == 0;
-// s0 NULL means zeros, s_last may equal s0; name gets the variant.
+// s0 NULL means zeros, s_last may equal s0; chunk picks the chunked kernel (e of 64
+// or 128), else the step-wise one; name gets the variant.
 int64_t hgrn2_workgroups(int64_t b, int64_t d, int e);
 hipError_t launch_hgrn2_scan(const float *f, const float *i, const float *o, const float *s0, float *y,
-                             float *s_last, int64_t b, int64_t t, int64_t d, int e, hipStream_t st,
+                             float *s_last, int64_t b, int64_t t, int64_t d, int e, bool chunk, hipStream_t st,
                              const char **name);
 
 // Backward of the HGRN scan: 1 = recurrent, kScanTiled = single-pass tiled

@@ -816,11 +816,18 @@ mmf_status mmf_hgrn_scan_fwd(const float *x, const float *f, const float *h0, fl
     return r;
 }
 
+constexpr int64_t kHgrn2ChunkFrom = 64;  // tokens from which AUTO takes the chunked form
+
 mmf_status mmf_hgrn2_scan_fwd(const float *f, const float *i, const float *o, const float *s0, float *y,
-                              float *s_last, int64_t b, int64_t t, int64_t d, int64_t e, hipStream_t stream) {
+                              float *s_last, int64_t b, int64_t t, int64_t d, int64_t e, mmf_scan_mode mode,
+                              hipStream_t stream) {
     if (b < 0 || t < 0 || d <= 0) return fail(MMF_ERR_INVALID_ARG, "b, t >= 0 and d > 0 required");
+    if (mode != MMF_SCAN_AUTO && mode != MMF_SCAN_RECURRENT && mode != MMF_SCAN_CHUNK)
+        return fail(MMF_ERR_INVALID_ARG, "bad scan mode %d", (int)mode);
     if (e != 16 && e != 32 && e != 64 && e != 128)
         return fail(MMF_ERR_UNSUPPORTED, "head width e = %lld: 16, 32, 64 or 128 supported", (long long)e);
+    if (mode == MMF_SCAN_CHUNK && e < 64)
+        return fail(MMF_ERR_UNSUPPORTED, "the chunked form takes heads of 64 or 128, not %lld", (long long)e);
     if (d % e) return fail(MMF_ERR_INVALID_ARG, "d = %lld is not a multiple of e = %lld", (long long)d, (long long)e);
     if (b > 0 && t > 0 && (!f || !i || !o || !y)) return fail(MMF_ERR_INVALID_ARG, "f, i, o and y must be non-NULL");
     const void *ins[] = {f, i, o, s0};
@@ -834,10 +841,14 @@ mmf_status mmf_hgrn2_scan_fwd(const float *f, const float *i, const float *o, co
     if (hgrn2_workgroups(b, d, (int)e) > INT32_MAX) return fail(MMF_ERR_UNSUPPORTED, "b * d too large");
     if (b == 0) return MMF_OK;
     const char *name = "hgrn2_scan";
+    // the chunked kernel from 64 tokens on (heads of 64 or 128), else the step-wise one
+    const bool chunk = mode == MMF_SCAN_CHUNK || (mode == MMF_SCAN_AUTO && e >= 64 && t >= kHgrn2ChunkFrom);
     // timing label: a one-token call (a decode step) streams the state, a longer one computes
-    const std::string label = std::string(t == 1 ? "hgrn2_step<" : "hgrn2_scan<") + std::to_string(e) + ">";
-    hipError_t err = timed(label, b * t, (int)d, (int)e, stream,
-                           [&] { return launch_hgrn2_scan(f, i, o, s0, y, s_last, b, t, d, (int)e, stream, &name); });
+    const std::string label = std::string(chunk ? "hgrn2_chunk<" : t == 1 ? "hgrn2_step<" : "hgrn2_scan<") +
+                              std::to_string(e) + ">";
+    hipError_t err = timed(label, b * t, (int)d, (int)e, stream, [&] {
+        return launch_hgrn2_scan(f, i, o, s0, y, s_last, b, t, d, (int)e, chunk, stream, &name);
+    });
     mmf_status r = hip_status(err, "mmf_hgrn2_scan_fwd");
     if (r == MMF_OK) g_path = name;
     return r;

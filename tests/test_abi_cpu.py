@@ -114,18 +114,23 @@ def test_hgrn2_scan_validation(lib):
     buffers on the host."""
     F = [FAKE + k * (1 << 24) for k in range(6)]
     f, i, o, s0, y, sl = F
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, 1, 4, 256, 48, None) == UNSUPPORTED
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, 1, 4, 256, 8, None) == UNSUPPORTED
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, 1, 4, 96, 64, None) == INVALID
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, -1, 4, 256, 64, None) == INVALID
-    assert lib.mmf_hgrn2_scan_fwd(None, i, o, s0, y, sl, 1, 4, 256, 64, None) == INVALID
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, None, sl, 1, 4, 256, 64, None) == INVALID
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, i, sl, 1, 4, 256, 64, None) == INVALID   # y aliases i
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, f, 1, 4, 256, 64, None) == INVALID   # s_last aliases f
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, y, 1, 4, 256, 64, None) == INVALID   # s_last aliases y
+
+    def h2(*a, mode=0):
+        return lib.mmf_hgrn2_scan_fwd(*a[:10], mode, a[10])
+    assert h2(f, i, o, s0, y, sl, 1, 4, 256, 64, None, mode=7) == INVALID
+    assert h2(f, i, o, s0, y, sl, 1, 4, 256, 32, None, mode=2) == UNSUPPORTED  # chunked: heads of 64 or 128
+    assert h2(f, i, o, s0, y, sl, 1, 4, 256, 48, None) == UNSUPPORTED
+    assert h2(f, i, o, s0, y, sl, 1, 4, 256, 8, None) == UNSUPPORTED
+    assert h2(f, i, o, s0, y, sl, 1, 4, 96, 64, None) == INVALID
+    assert h2(f, i, o, s0, y, sl, -1, 4, 256, 64, None) == INVALID
+    assert h2(None, i, o, s0, y, sl, 1, 4, 256, 64, None) == INVALID
+    assert h2(f, i, o, s0, None, sl, 1, 4, 256, 64, None) == INVALID
+    assert h2(f, i, o, s0, i, sl, 1, 4, 256, 64, None) == INVALID   # y aliases i
+    assert h2(f, i, o, s0, y, f, 1, 4, 256, 64, None) == INVALID   # s_last aliases f
+    assert h2(f, i, o, s0, y, y, 1, 4, 256, 64, None) == INVALID   # s_last aliases y
     assert "alias" in B.last_error()
-    assert lib.mmf_hgrn2_scan_fwd(f + 4, i, o, s0, y, sl, 1, 4, 256, 64, None) == INVALID  # misaligned
-    assert lib.mmf_hgrn2_scan_fwd(f, i, o, s0, y, sl, 0, 4, 256, 64, None) == OK       # nothing to do
+    assert h2(f + 4, i, o, s0, y, sl, 1, 4, 256, 64, None) == INVALID  # misaligned
+    assert h2(f, i, o, s0, y, sl, 0, 4, 256, 64, None) == OK       # nothing to do
 
 
 def test_bitlinear_bwd_validation(lib):
