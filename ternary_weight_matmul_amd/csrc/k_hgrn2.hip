@@ -273,7 +273,6 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
     float (*spart)[C * C] = reinterpret_cast<float (*)[C * C]>(so);
     static_assert(4 * C * C <= C * E, "partial A tiles fit in the o buffer");
     __shared__ float sdec[E];                                  // prod f over the chunk
-    __shared__ __attribute__((aligned(16))) float ss[4][E * 16];  // each wave's state slice, [a][16]
 
     const int G = gridDim.x, g = blockIdx.x;
     const int lin = (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g;
@@ -328,13 +327,16 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
     };
 
     if (t > 0) fetch(0);
-    // the wave's state slice: tile i holds rows 16i + 4 lg + j, column 16 wave + l16 (accumulator layout)
+    // the wave's state slice in accumulator layout, column 16 wave + l16: st[i][j] holds row
+    // 16i + lg + 4j. The update's output row m = 4 lg + j of tile i is taken to be state row
+    // 16i + (m >> 2) + 4 (m & 3) (the order of its K~/K^ operand rows), so that for Q~ S0 the
+    // register st[i][j] is the B operand of the K step whose lane group lg is row 16i + 4j + lg
     float st[AT][4];
     if (s0) {
 #pragma unroll
         for (int i = 0; i < AT; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) st[i][j] = s0[sbase + (int64_t)(16 * i + 4 * lg + j) * E + l16];
+            for (int j = 0; j < 4; ++j) st[i][j] = s0[sbase + (int64_t)(16 * i + lg + 4 * j) * E + l16];
     } else {
 #pragma unroll
         for (int i = 0; i < AT; ++i)
@@ -345,7 +347,6 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state and the first chunk have landed
     __syncthreads();
 
-    float *myss = ss[wave];
     for (int64_t t0 = 0; t0 < t; t0 += C) {
         const bool more = t0 + C < t;
         if (more) fetch(t0 + C);
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
                 tiny |= fk < kChunkMinGate;
                 p *= fk;
                 sq[a * QS + k] = so[k * E + a] * p;
-                kt[k] = __fdiv_rn(1.0f - fk, p);
+                kt[k] = (1.0f - fk) * __builtin_amdgcn_rcpf(p);
             }
             sdec[a] = p;
         }
@@ -430,23 +431,19 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
                 if (ac == 0) sa[sI * QS + k] = pk;
             }
         }
-        // -- the wave's state slice into its LDS region, [a][16]
+        __syncthreads();  // sq, skt, sa and sdec written
+
+        // -- Y = Q~ S0 + A V for the wave's 16 columns on two accumulators; the state operand
+        // comes from registers (K step (i, j): row 16i + 4j + lg)
+        f32x4v y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < AT; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) myss[(16 * i + 4 * lg + j) * 16 + l16] = st[i][j];
-        __syncthreads();  // sq, sk, sa, sdec and every slice written
-
-        // -- Y = Q~ S0 + A V for the wave's 16 columns: every operand is read from LDS
-        // first, then the MFMAs run back to back on two accumulators
-        f32x4v y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int q = 0; q < E / 4; q += 2) {
-            y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[(4 * q + lg) * QS + l16], myss[(4 * q + lg) * 16 + l16], y0,
-                                                      0, 0, 0);
-            y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[(4 * q + 4 + lg) * QS + l16],
-                                                      myss[(4 * q + 4 + lg) * 16 + l16], y1, 0, 0, 0);
-        }
+            for (int j = 0; j < 4; j += 2) {
+                y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[(16 * i + 4 * j + lg) * QS + l16], st[i][j], y0, 0, 0, 0);
+                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[(16 * i + 4 * j + 4 + lg) * QS + l16], st[i][j + 1], y1,
+                                                          0, 0, 0);
+            }
 #pragma unroll
         for (int q = 0; q < C / 4; q += 2) {
             y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[(4 * q + lg) * QS + l16], sv[(4 * q + lg) * VS + 16 * wave + l16],
@@ -457,11 +454,12 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
         const f32x4v yacc = y0 + y1;
         // -- S1 = diag(decay) S0 + K^T V (the V operands serve every tile)
         float kv[C / 4], ka[AT][C / 4];
+        const int prow = (l16 >> 2) + 4 * (l16 & 3);  // state row of operand row l16 within a tile
 #pragma unroll
         for (int i = 0; i < AT; ++i) {
-            const float ks = direct ? 1.0f : sdec[16 * i + l16];  // K^ = K~ * total decay
+            const float ks = direct ? 1.0f : sdec[16 * i + prow];  // K^ = K~ * total decay
 #pragma unroll
-            for (int q = 0; q < C / 4; ++q) ka[i][q] = skt[(16 * i + l16) * QS + 4 * q + lg] * ks;
+            for (int q = 0; q < C / 4; ++q) ka[i][q] = skt[(16 * i + prow) * QS + 4 * q + lg] * ks;
         }
 #pragma unroll
         for (int q = 0; q < C / 4; ++q) kv[q] = sv[(4 * q + lg) * VS + 16 * wave + l16];
@@ -469,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
 #pragma unroll
         for (int i = 0; i < AT; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = st[i][j] * sdec[16 * i + 4 * lg + j];
+            for (int j = 0; j < 4; ++j) acc[i][j] = st[i][j] * sdec[16 * i + lg + 4 * j];
 #pragma unroll
         for (int q = 0; q < C / 4; ++q)
 #pragma unroll
@@ -493,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
 #pragma unroll
         for (int i = 0; i < AT; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s_last[sbase + (int64_t)(16 * i + 4 * lg + j) * E + l16] = st[i][j];
+            for (int j = 0; j < 4; ++j) s_last[sbase + (int64_t)(16 * i + lg + 4 * j) * E + l16] = st[i][j];
     }
 }
 
