@@ -218,33 +218,44 @@ __global__ __launch_bounds__(256) void hgrn2_scan_kernel(const float *__restrict
 
 // ----------------------------------------------------------------------------
 // Chunked form (the pages name a step-wise and a chunked implementation of the
-// recurrence). Over a chunk of C tokens starting from the state S0, with every
-// decay a plain product of gates (no logarithms or divisions, so nothing can
-// overflow however small f gets):
+// recurrence). Over a chunk of C tokens starting from the state S0:
 //   Q~[t][a]  = o_t[a] * prod_{r<=t} f_r[a]             (decay from the chunk start)
 //   K^[s][a]  = (1 - f_s[a]) * prod_{s<r<C} f_r[a]      (decay to the chunk end)
 //   A[t][s]   = sum_a o_t[a] (1 - f_s[a]) prod_{s<r<=t} f_r[a]   (s <= t, else 0)
-//             = (Q~ K~^T)[t][s], K~[s][a] = (1 - f_s[a]) / prod_{r<=s} f_r[a], on MFMA when every
-//               gate of the chunk is at least 2^-6 (1 / prod f then stays below 2^96), else
-//               as running products of the gates
 //   Y  = Q~ S0 + A V                  (C x BC: the chunk's outputs)
 //   S1 = diag(prod_{r<C} f_r) S0 + K^T V
-// (V = the chunk's input rows of the block's columns). The products run on
-// fp32 MFMA (v_mfma_f32_16x16x4_f32); wave w owns the block's columns
-// 16w .. 16w+15, holds their E x 16 slice of the state as E/16 accumulator
-// tiles, and moves it through its own LDS region to use it as an operand.
-// Gates of the next chunk load into registers during the current one, as in
-// the step-wise kernel. Tokens past the sequence end act as f = 1, o = 0, i = 0.
-// Below this gate the chunk's A sums run with the decays as running products:
-// from it up, 1 / prod f over 16 tokens stays below 2^96.
+// (V = the chunk's input rows of the block's columns). When every gate of the
+// chunk is at least 2^-6, 1 / prod_{r<=s} f_r stays below 2^96 and A is the
+// product Q~ K~^T with K~[s][a] = (1 - f_s[a]) / prod_{r<=s} f_r[a] (and
+// K^ = K~ * prod_{r<C} f_r); a chunk with a smaller gate takes A as sums of
+// running products of the gates and K^ as suffix products, with no division.
+// The products run on fp32 MFMA (v_mfma_f32_16x16x4_f32); wave w owns the
+// block's columns 16w .. 16w+15 and holds their E x 16 slice of the state as
+// E/16 accumulator tiles, which serve as the B operand of Q~ S0 as they are.
+//
+// The loop is pipelined over three chunks, two barriers per chunk: while the
+// waves read out chunk k (Y and the state update, the only steps that need
+// the state), they form chunk k+1's A, and between the barriers the decays of
+// chunk k+2 (Q~, K~, the total decay) are prepared from its gates, which were
+// parked in LDS during the same iteration. Gates load into registers one
+// iteration before they are parked. Tokens past the sequence end act as
+// f = 1, o = 0, i = 0.
+//
+// The gates, the input and the outputs move through buffer resources that
+// span the workgroup's sequence: rows past its end read as zeros and are not
+// written. So every iteration issues the same loads and stores whatever its
+// chunk (the prefetches past the last chunk read nothing), and each wait for
+// a prefetch counts only what was issued after it, never this chunk's output
+// stores. A sequence's rows must span less than 2^31 bytes.
 constexpr float kChunkMinGate = 0.015625f;  // 2^-6
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw 32-bit buffer access, range-checked
 
 template <int E>
 struct H2Chunk {
     static constexpr int C = 16;          // tokens per chunk
     static constexpr int BC = 64;         // state columns per workgroup: 4 waves x 16
     static constexpr int AT = E / 16;     // 16-row tiles of a wave's state slice
-    static constexpr int RA = E / 16;     // rows per thread in the A sums (16 threads per s)
+    static constexpr int RA = E / 16;     // rows per thread in the direct A sums (16 threads per s)
     static constexpr int G4 = C * E / 4;  // float4s of one gate per chunk
     static constexpr int I4 = C * BC / 4; // float4s of i per chunk
     static constexpr int GL = (G4 + 255) / 256;
@@ -263,16 +274,14 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
     using Sh = H2Chunk<E>;
     constexpr int C = Sh::C, BC = Sh::BC, AT = Sh::AT, RA = Sh::RA, CBK = E / BC;
     constexpr int QS = Sh::QS, VS = Sh::VS;
-    __shared__ __attribute__((aligned(16))) float sf[C * E];   // f of the chunk, [t][a]
-    __shared__ __attribute__((aligned(16))) float so[C * E];   // o of the chunk, [t][a]
-    __shared__ __attribute__((aligned(16))) float sv[C * VS];  // i of the chunk, [t][column]
-    __shared__ __attribute__((aligned(16))) float sq[E * QS];  // Q~, [a][t]
-    __shared__ __attribute__((aligned(16))) float sa[C * QS];  // A, [s][t]
-    __shared__ __attribute__((aligned(16))) float skt[E * QS]; // K~ or K^, [a][t]
-    // the waves' partial A tiles, [t][s]: in the o buffer, no longer read once Q~ is formed
-    float (*spart)[C * C] = reinterpret_cast<float (*)[C * C]>(so);
-    static_assert(4 * C * C <= C * E, "partial A tiles fit in the o buffer");
-    __shared__ float sdec[E];                                  // prod f over the chunk
+    __shared__ __attribute__((aligned(16))) float sf[C * E];      // f of the chunk being prepared, [t][a]
+    __shared__ __attribute__((aligned(16))) float so[C * E];      // o of that chunk, [t][a]
+    __shared__ __attribute__((aligned(16))) float sv[C * VS];     // i of the chunk being read out, [t][column]
+    __shared__ __attribute__((aligned(16))) float sq[2][E * QS];  // Q~, [a][t]
+    __shared__ __attribute__((aligned(16))) float skt[2][E * QS]; // K~ or K^, [a][t]
+    __shared__ __attribute__((aligned(16))) float sa[2][C * QS];  // A, [s][t]
+    __shared__ float sdec[2][E];                                   // prod f over the chunk
+    __shared__ __attribute__((aligned(16))) float spart[4][C * C]; // the waves' partial A tiles, [t][s]
 
     const int G = gridDim.x, g = blockIdx.x;
     const int lin = (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g;
@@ -284,33 +293,48 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
     const int64_t ccol0 = col0 + (int64_t)cblk * BC;
     const int64_t row_base = bi * t * d;
     const int64_t sbase = ((int64_t)pair * E) * E + (int64_t)cblk * BC + 16 * wave;  // state (pair, 0, wave's first column)
+    const int64_t nch = (t + C - 1) / C;
+    auto tokens = [&](int64_t c) __attribute__((always_inline)) { return t - c * C < C ? (int)(t - c * C) : C; };
 
-    float4 pf0, pf1, po0, po1, pi0;
-    auto gate_off = [&](int64_t t0, int j) __attribute__((always_inline)) {
-        const int q = min(tid + 256 * j, Sh::G4 - 1);
-        const int k = q / (E / 4), c4 = q - k * (E / 4);
-        const int64_t tk = t0 + k < t ? t0 + k : t - 1;  // rows past t: any valid row, replaced below
-        return row_base + tk * d + col0 + 4 * c4;
+    // ---- gate and input traffic: loads into registers, parked in LDS an iteration later;
+    // byte offsets within the sequence, rows past its end read as zeros
+    const int seq_bytes = (int)(t * d * 4);
+    const auto rf = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(f + row_base), 0, seq_bytes, kBufferWord3);
+    const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(o + row_base), 0, seq_bytes, kBufferWord3);
+    const auto ri = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(xi + row_base), 0, seq_bytes, kBufferWord3);
+    const auto ry = __builtin_amdgcn_make_buffer_rsrc(y + row_base, 0, seq_bytes, kBufferWord3);
+    const int row_bytes = (int)d * 4;
+    auto ld4 = [](__amdgpu_buffer_rsrc_t r, int off) __attribute__((always_inline)) {
+        return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
     };
-    auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
-        const int64_t off0 = gate_off(t0, 0);
-        pf0 = *reinterpret_cast<const float4 *>(f + off0);
-        po0 = *reinterpret_cast<const float4 *>(o + off0);
-        if constexpr (Sh::GL == 2) {
-            const int64_t off1 = gate_off(t0, 1);
-            pf1 = *reinterpret_cast<const float4 *>(f + off1);
-            po1 = *reinterpret_cast<const float4 *>(o + off1);
+    float4 pf0, pf1, po0, po1, pi0;
+    auto fetch_gates = [&](int64_t c) __attribute__((always_inline)) {
+        // chunks past the last read as zeros; the offset stays in int range for any c the loop reaches
+        const int crow = (int)(c < nch ? c : nch) * C;
+        {
+            const int k = tid / (E / 4), c4 = tid - k * (E / 4);
+            const int off = (crow + k) * row_bytes + (int)(col0 + 4 * c4) * 4;
+            pf0 = ld4(rf, off);
+            po0 = ld4(ro, off);
         }
+        if constexpr (Sh::GL == 2) {
+            const int q = tid + 256, k = q / (E / 4), c4 = q - k * (E / 4);
+            const int off = (crow + k) * row_bytes + (int)(col0 + 4 * c4) * 4;
+            pf1 = ld4(rf, off);
+            po1 = ld4(ro, off);
+        }
+    };
+    auto fetch_input = [&](int64_t c) __attribute__((always_inline)) {
+        const int crow = (int)(c < nch ? c : nch) * C;
         const int k = tid / (BC / 4), c4 = tid - k * (BC / 4);
-        const int64_t tk = t0 + k < t ? t0 + k : t - 1;
-        pi0 = *reinterpret_cast<const float4 *>(xi + row_base + tk * d + ccol0 + 4 * c4);
+        pi0 = ld4(ri, (crow + k) * row_bytes + (int)(ccol0 + 4 * c4) * 4);
     };
     // tokens at or past `nk` of the chunk become f = 1, o = 0, i = 0 (selected per
     // component: a select of whole float4 values would go through memory)
     auto or4 = [](bool in, float4 v, float w) __attribute__((always_inline)) {
         return make_float4(in ? v.x : w, in ? v.y : w, in ? v.z : w, in ? v.w : w);
     };
-    auto park = [&](int nk) __attribute__((always_inline)) {
+    auto park_gates = [&](int nk) __attribute__((always_inline)) {
         {
             const bool in = tid / (E / 4) < nk;
             *reinterpret_cast<float4 *>(sf + 4 * tid) = or4(in, pf0, 1.0f);
@@ -322,16 +346,149 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
             *reinterpret_cast<float4 *>(sf + 4 * q) = or4(in, pf1, 1.0f);
             *reinterpret_cast<float4 *>(so + 4 * q) = or4(in, po1, 0.0f);
         }
+    };
+    auto park_input = [&](int nk) __attribute__((always_inline)) {
         *reinterpret_cast<float4 *>(sv + (tid / (BC / 4)) * VS + 4 * (tid % (BC / 4))) =
             or4(tid / (BC / 4) < nk, pi0, 0.0f);
     };
 
-    if (t > 0) fetch(0);
+    // ---- decays of the parked chunk, one thread per row a: Q~, K~ (into skt) and the total
+    // decay; returns whether a gate is below the floor that keeps 1 / prod f in range
+    auto prepare = [&](int bf) __attribute__((always_inline)) {
+        bool tiny = false;
+        if (tid < E) {
+            const int a = tid;
+            float p = 1.0f;
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const float fk = sf[k * E + a];
+                tiny |= fk < kChunkMinGate;
+                p *= fk;
+                sq[bf][a * QS + k] = so[k * E + a] * p;
+                skt[bf][a * QS + k] = (1.0f - fk) * __builtin_amdgcn_rcpf(p);
+            }
+            sdec[bf][a] = p;
+        }
+        return tiny;
+    };
+    // A = Q~ K~^T on MFMA, the E rows split over the four waves; each wave's partial tile,
+    // entries with s > t dropped, goes to spart
+    auto a_partial = [&](int bf) __attribute__((always_inline)) {
+        f32x4v pa = {0.f, 0.f, 0.f, 0.f};
+        float qa[E / 16], kb[E / 16];
+#pragma unroll
+        for (int q = 0; q < E / 16; ++q) {
+            const int row = wave * (E / 4) + 4 * q + lg;
+            qa[q] = sq[bf][row * QS + l16];
+            kb[q] = skt[bf][row * QS + l16];
+        }
+#pragma unroll
+        for (int q = 0; q < E / 16; ++q) pa = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[q], kb[q], pa, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) spart[wave][(4 * lg + j) * 16 + l16] = pa[j];  // [t][s]
+    };
+    // the partial tiles summed in a fixed order, s > t set to 0
+    auto a_reduce = [&](int bf) __attribute__((always_inline)) {
+        const int tI = tid >> 4, sI = tid & 15;
+        const float v =
+            ((spart[0][tI * 16 + sI] + spart[1][tI * 16 + sI]) + spart[2][tI * 16 + sI]) + spart[3][tI * 16 + sI];
+        sa[bf][sI * QS + tI] = sI <= tI ? v : 0.0f;
+    };
+    // a chunk with a small gate: A[t][s] from running products of its gates (thread (s, ac)
+    // sums rows ac*RA .. ac*RA+RA-1, the 16 ac meet by DPP) and K^ as suffix products, both
+    // from the gates still parked in sf / so
+    auto a_direct = [&](int bf) __attribute__((always_inline)) {
+        const int sI = tid >> 4, ac = tid & 15;
+        float dk[RA];
+#pragma unroll
+        for (int r = 0; r < RA; ++r) dk[r] = 1.0f - sf[sI * E + ac * RA + r];
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            float pk = 0.0f;
+#pragma unroll
+            for (int r = 0; r < RA; ++r) {
+                if (k > sI) dk[r] *= sf[k * E + ac * RA + r];
+                pk = fmaf(so[k * E + ac * RA + r], dk[r], pk);
+            }
+            pk = k >= sI ? pk : 0.0f;
+            pk += dpp_f<kDppXor1>(pk);
+            pk += dpp_f<kDppXor2>(pk);
+            pk += dpp_f<kDppHalfMirror>(pk);
+            pk += dpp_f<kDppMirror>(pk);
+            if (ac == 0) sa[bf][sI * QS + k] = pk;
+        }
+        if (tid < E) {
+            float suf = 1.0f;
+#pragma unroll
+            for (int k = C - 1; k >= 0; --k) {
+                const float fk = sf[k * E + tid];
+                skt[bf][tid * QS + k] = (1.0f - fk) * suf;
+                suf *= fk;
+            }
+        }
+    };
+
     // the wave's state slice in accumulator layout, column 16 wave + l16: st[i][j] holds row
     // 16i + lg + 4j. The update's output row m = 4 lg + j of tile i is taken to be state row
     // 16i + (m >> 2) + 4 (m & 3) (the order of its K~/K^ operand rows), so that for Q~ S0 the
     // register st[i][j] is the B operand of the K step whose lane group lg is row 16i + 4j + lg
     float st[AT][4];
+    // ---- Y = Q~ S0 + A V for the wave's 16 columns, then S1 = diag(decay) S0 + K^T V
+    auto read_out = [&](int bf, bool direct, int64_t t0) __attribute__((always_inline)) {
+        f32x4v y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[bf][(16 * i + 4 * j + lg) * QS + l16], st[i][j], y0, 0, 0,
+                                                          0);
+                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[bf][(16 * i + 4 * j + 4 + lg) * QS + l16], st[i][j + 1],
+                                                          y1, 0, 0, 0);
+            }
+#pragma unroll
+        for (int q = 0; q < C / 4; q += 2) {
+            y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[bf][(4 * q + lg) * QS + l16],
+                                                      sv[(4 * q + lg) * VS + 16 * wave + l16], y0, 0, 0, 0);
+            y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[bf][(4 * q + 4 + lg) * QS + l16],
+                                                      sv[(4 * q + 4 + lg) * VS + 16 * wave + l16], y1, 0, 0, 0);
+        }
+        const f32x4v yacc = y0 + y1;
+        // S1 = diag(decay) S0 + K^T V; K^ = K~ * total decay (skt holds K^ itself in a direct chunk)
+        float kv[C / 4], ka[AT][C / 4];
+        const int prow = (l16 >> 2) + 4 * (l16 & 3);  // state row of operand row l16 within a tile
+#pragma unroll
+        for (int i = 0; i < AT; ++i) {
+            const float ks = direct ? 1.0f : sdec[bf][16 * i + prow];
+#pragma unroll
+            for (int q = 0; q < C / 4; ++q) ka[i][q] = skt[bf][(16 * i + prow) * QS + 4 * q + lg] * ks;
+        }
+#pragma unroll
+        for (int q = 0; q < C / 4; ++q) kv[q] = sv[(4 * q + lg) * VS + 16 * wave + l16];
+        f32x4v acc[AT];
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = st[i][j] * sdec[bf][16 * i + lg + 4 * j];
+#pragma unroll
+        for (int q = 0; q < C / 4; ++q)
+#pragma unroll
+            for (int i = 0; i < AT; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[i][q], kv[q], acc[i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < AT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st[i][j] = acc[i][j];
+        // the chunk's outputs: row 4 lg + j, column 16 wave + l16 (rows past the end are dropped)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yacc[j]), ry,
+                                                  ((int)t0 + 4 * lg + j) * row_bytes + (int)(ccol0 + 16 * wave + l16) * 4,
+                                                  0, 0);
+    };
+
+    if (nch > 0) {
+        fetch_gates(0);
+        fetch_input(0);
+    }
     if (s0) {
 #pragma unroll
         for (int i = 0; i < AT; ++i)
@@ -343,148 +500,59 @@ __global__ __launch_bounds__(256, 2) void hgrn2_chunk_kernel(const float *__rest
 #pragma unroll
             for (int j = 0; j < 4; ++j) st[i][j] = 0.0f;
     }
-    if (t > 0) park(t < C ? (int)t : C);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state and the first chunk have landed
-    __syncthreads();
 
-    for (int64_t t0 = 0; t0 < t; t0 += C) {
-        const bool more = t0 + C < t;
-        if (more) fetch(t0 + C);
-
-        // -- decays, one thread per row a: Q~ and the chunk's total decay; K~ = (1 - f_s) /
-        // prod_{r<=s} f_r and K^ held in registers until the workgroup knows whether any gate of
-        // the chunk is small enough for 1 / prod f to leave the range that keeps K~ exact to a
-        // few ulp; then skt holds K~ (A on MFMA, K^ = K~ * total decay) or K^ (the direct sums)
-        bool tiny = false;
-        float kt[C];
-        if (tid < E) {
-            const int a = tid;
-            float p = 1.0f;
-#pragma unroll
-            for (int k = 0; k < C; ++k) {
-                const float fk = sf[k * E + a];
-                tiny |= fk < kChunkMinGate;
-                p *= fk;
-                sq[a * QS + k] = so[k * E + a] * p;
-                kt[k] = (1.0f - fk) * __builtin_amdgcn_rcpf(p);
-            }
-            sdec[a] = p;
-        }
-        const bool direct = __syncthreads_or(tiny);
-        if (tid < E) {
-            const int a = tid;
-            if (!direct) {
-#pragma unroll
-                for (int k = 0; k < C; ++k) skt[a * QS + k] = kt[k];
-            } else {
-                float suf = 1.0f;  // K^ as suffix products of the gates
-#pragma unroll
-                for (int k = C - 1; k >= 0; --k) {
-                    const float fk = sf[k * E + a];
-                    skt[a * QS + k] = (1.0f - fk) * suf;
-                    suf *= fk;
-                }
-            }
-        }
-        __syncthreads();  // Q~, skt and the decays are in LDS
-        if (!direct) {
-            // -- A = Q~ K~^T on MFMA (A[t][s] = sum_a Q~[t][a] K~[s][a] = sum_a o_t (1 - f_s)
-            // prod_{s<r<=t} f_r), the E rows split over the four waves, the partial tiles
-            // summed in a fixed order; entries with s > t are dropped
-            f32x4v pa = {0.f, 0.f, 0.f, 0.f};
-            float qa[E / 16], kb[E / 16];
-#pragma unroll
-            for (int q = 0; q < E / 16; ++q) {
-                const int row = wave * (E / 4) + 4 * q + lg;
-                qa[q] = sq[row * QS + l16];
-                kb[q] = skt[row * QS + l16];
-            }
-#pragma unroll
-            for (int q = 0; q < E / 16; ++q) pa = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[q], kb[q], pa, 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) spart[wave][(4 * lg + j) * 16 + l16] = pa[j];  // [t][s]
-            __syncthreads();
-            const int tI = tid >> 4, sI = tid & 15;
-            const float v = ((spart[0][tI * 16 + sI] + spart[1][tI * 16 + sI]) + spart[2][tI * 16 + sI]) +
-                            spart[3][tI * 16 + sI];
-            sa[sI * QS + tI] = sI <= tI ? v : 0.0f;
-        } else {
-            // -- A[t][s] with the decays as running products: thread (s, ac) sums rows
-            // ac*RA .. ac*RA+RA-1; the 16 ac meet by DPP
-            const int sI = tid >> 4, ac = tid & 15;
-            float dk[RA];
-#pragma unroll
-            for (int r = 0; r < RA; ++r) dk[r] = 1.0f - sf[sI * E + ac * RA + r];
-#pragma unroll
-            for (int k = 0; k < C; ++k) {
-                float pk = 0.0f;
-#pragma unroll
-                for (int r = 0; r < RA; ++r) {
-                    if (k > sI) dk[r] *= sf[k * E + ac * RA + r];
-                    pk = fmaf(so[k * E + ac * RA + r], dk[r], pk);
-                }
-                pk = k >= sI ? pk : 0.0f;
-                pk += dpp_f<kDppXor1>(pk);
-                pk += dpp_f<kDppXor2>(pk);
-                pk += dpp_f<kDppHalfMirror>(pk);
-                pk += dpp_f<kDppMirror>(pk);
-                if (ac == 0) sa[sI * QS + k] = pk;
-            }
-        }
-        __syncthreads();  // sq, skt, sa and sdec written
-
-        // -- Y = Q~ S0 + A V for the wave's 16 columns on two accumulators; the state operand
-        // comes from registers (K step (i, j): row 16i + 4j + lg)
-        f32x4v y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < AT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; j += 2) {
-                y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[(16 * i + 4 * j + lg) * QS + l16], st[i][j], y0, 0, 0, 0);
-                y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[(16 * i + 4 * j + 4 + lg) * QS + l16], st[i][j + 1], y1,
-                                                          0, 0, 0);
-            }
-#pragma unroll
-        for (int q = 0; q < C / 4; q += 2) {
-            y0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[(4 * q + lg) * QS + l16], sv[(4 * q + lg) * VS + 16 * wave + l16],
-                                                      y0, 0, 0, 0);
-            y1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[(4 * q + 4 + lg) * QS + l16],
-                                                      sv[(4 * q + 4 + lg) * VS + 16 * wave + l16], y1, 0, 0, 0);
-        }
-        const f32x4v yacc = y0 + y1;
-        // -- S1 = diag(decay) S0 + K^T V (the V operands serve every tile)
-        float kv[C / 4], ka[AT][C / 4];
-        const int prow = (l16 >> 2) + 4 * (l16 & 3);  // state row of operand row l16 within a tile
-#pragma unroll
-        for (int i = 0; i < AT; ++i) {
-            const float ks = direct ? 1.0f : sdec[16 * i + prow];  // K^ = K~ * total decay
-#pragma unroll
-            for (int q = 0; q < C / 4; ++q) ka[i][q] = skt[(16 * i + prow) * QS + 4 * q + lg] * ks;
-        }
-#pragma unroll
-        for (int q = 0; q < C / 4; ++q) kv[q] = sv[(4 * q + lg) * VS + 16 * wave + l16];
-        f32x4v acc[AT];
-#pragma unroll
-        for (int i = 0; i < AT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = st[i][j] * sdec[16 * i + lg + 4 * j];
-#pragma unroll
-        for (int q = 0; q < C / 4; ++q)
-#pragma unroll
-            for (int i = 0; i < AT; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[i][q], kv[q], acc[i], 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < AT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) st[i][j] = acc[i][j];
-        // -- the chunk's outputs: row 4 lg + j, column 16 wave + l16
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t tk = t0 + 4 * lg + j;
-            if (tk < t) y[row_base + tk * d + ccol0 + 16 * wave + l16] = yacc[j];
-        }
-        __syncthreads();  // every read of this chunk's LDS done
-        if (more) park(t - (t0 + C) < C ? (int)(t - (t0 + C)) : C);
+    // prologue: chunk 0 parked and prepared; its A, chunk 1 parked and prepared, chunk 0's input
+    // parked. `direct0` / `direct1` say how chunks k and k+1 were prepared
+    bool direct0 = false, direct1 = false;
+    if (nch > 0) {
+        park_gates(tokens(0));
+        fetch_gates(1);
         __syncthreads();
+        direct1 = __syncthreads_or(prepare(0));
+        if (direct1) a_direct(0);
+        else a_partial(0);
+        if (nch > 1) {
+            if (direct1) __syncthreads();  // the direct sums read chunk 0's gates in sf / so
+            park_gates(tokens(1));
+        }
+        fetch_gates(2);
+        __syncthreads();
+        if (!direct1) a_reduce(0);
+        park_input(tokens(0));
+        fetch_input(1);
+        const bool tiny = nch > 1 ? prepare(1) : false;
+        direct0 = direct1;
+        direct1 = __syncthreads_or(tiny);
+        // vmcnt(0), once: the loop is entered with nothing in flight, so the waits in its body
+        // count only the loop's own loads and stores
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    // iteration k: A of chunk k+1 and chunk k+2 parked, chunk k read out; then chunk k+1's A
+    // summed and its input parked, chunk k+2 prepared. Every iteration issues the same loads
+    // and stores; only LDS and MFMA work depends on which chunks exist
+    for (int64_t k = 0; k < nch; ++k) {
+        const bool has1 = k + 1 < nch, has2 = k + 2 < nch;
+        if (has1) {
+            if (direct1) a_direct((int)((k + 1) & 1));
+            else a_partial((int)((k + 1) & 1));
+        }
+        if (has2) {
+            if (has1 && direct1) __syncthreads();  // the direct sums read chunk k+1's gates in sf / so
+            park_gates(tokens(k + 2));
+        }
+        fetch_gates(k + 3);
+        read_out((int)(k & 1), direct0, k * C);
+        __syncthreads();  // spart, the parked gates; every read of chunk k's buffers and of sv done
+        if (has1) {
+            if (!direct1) a_reduce((int)((k + 1) & 1));
+            park_input(tokens(k + 1));
+        }
+        fetch_input(k + 2);
+        const bool tiny = has2 ? prepare((int)((k + 2) & 1)) : false;
+        const bool direct2 = __syncthreads_or(tiny);  // chunk k+1's A and V, chunk k+2's decays in LDS
+        direct0 = direct1;
+        direct1 = direct2;
     }
 
     if (s_last) {

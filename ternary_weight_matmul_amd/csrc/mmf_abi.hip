@@ -828,6 +828,12 @@ mmf_status mmf_hgrn2_scan_fwd(const float *f, const float *i, const float *o, co
         return fail(MMF_ERR_UNSUPPORTED, "head width e = %lld: 16, 32, 64 or 128 supported", (long long)e);
     if (mode == MMF_SCAN_CHUNK && e < 64)
         return fail(MMF_ERR_UNSUPPORTED, "the chunked form takes heads of 64 or 128, not %lld", (long long)e);
+    // the chunked kernel addresses a sequence's rows (and up to two chunks past its end) with
+    // 32-bit byte offsets
+    const bool chunk_fits = (t + 32) <= (int64_t)INT32_MAX / 4 / d;
+    if (mode == MMF_SCAN_CHUNK && !chunk_fits)
+        return fail(MMF_ERR_UNSUPPORTED, "the chunked form takes sequences of under 2 GiB of rows: t = %lld, d = %lld",
+                    (long long)t, (long long)d);
     if (d % e) return fail(MMF_ERR_INVALID_ARG, "d = %lld is not a multiple of e = %lld", (long long)d, (long long)e);
     if (b > 0 && t > 0 && (!f || !i || !o || !y)) return fail(MMF_ERR_INVALID_ARG, "f, i, o and y must be non-NULL");
     const void *ins[] = {f, i, o, s0};
@@ -841,8 +847,10 @@ mmf_status mmf_hgrn2_scan_fwd(const float *f, const float *i, const float *o, co
     if (hgrn2_workgroups(b, d, (int)e) > INT32_MAX) return fail(MMF_ERR_UNSUPPORTED, "b * d too large");
     if (b == 0) return MMF_OK;
     const char *name = "hgrn2_scan";
-    // the chunked kernel from 64 tokens on (heads of 64 or 128), else the step-wise one
-    const bool chunk = mode == MMF_SCAN_CHUNK || (mode == MMF_SCAN_AUTO && e >= 64 && t >= kHgrn2ChunkFrom);
+    // the chunked kernel from 64 tokens on (heads of 64 or 128, sequences under 2 GiB of rows),
+    // else the step-wise one
+    const bool chunk =
+        mode == MMF_SCAN_CHUNK || (mode == MMF_SCAN_AUTO && e >= 64 && t >= kHgrn2ChunkFrom && chunk_fits);
     // timing label: a one-token call (a decode step) streams the state, a longer one computes
     const std::string label = std::string(chunk ? "hgrn2_chunk<" : t == 1 ? "hgrn2_step<" : "hgrn2_scan<") +
                               std::to_string(e) + ">";

@@ -131,6 +131,11 @@ def test_hgrn2_scan_validation(lib):
     assert "alias" in B.last_error()
     assert h2(f + 4, i, o, s0, y, sl, 1, 4, 256, 64, None) == INVALID  # misaligned
     assert h2(f, i, o, s0, y, sl, 0, 4, 256, 64, None) == OK       # nothing to do
+    # the chunked form addresses a sequence with 32-bit byte offsets: (t + 32) * d * 4 < 2^31
+    t_max = (2 ** 31 - 1) // 4 // 2048 - 32
+    assert h2(f, i, o, s0, y, sl, 1, t_max + 1, 2048, 128, None, mode=2) == UNSUPPORTED
+    assert "2 GiB" in B.last_error()
+    assert h2(f, i, o, s0, y, sl, 0, t_max, 2048, 128, None, mode=2) == OK
 
 
 def test_bitlinear_bwd_validation(lib):
