@@ -354,7 +354,10 @@ class KernelTable:
                        ms_per_step=round(e["ms"], 3))
             if e["ops"] and e["name"].startswith("hgrn2"):
                 row["fp32_tflops"] = round(e["ops"] / t / 1e12, 2)
-                row["frac_fp32_vector"] = round(e["ops"] / t / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4)
+                if e["name"].startswith("hgrn2_chunk"):  # the chunked form runs on fp32 MFMA
+                    row["frac_fp32_mfma"] = round(e["ops"] / t / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)
+                else:
+                    row["frac_fp32_vector"] = round(e["ops"] / t / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4)
             elif e["ops"]:
                 row["int8_tops"] = round(e["ops"] / t / 1e12, 1)
                 row["frac_mfma"] = round(e["ops"] / t / 1e12 / INT8_MFMA_PEAK_TOPS, 4)
