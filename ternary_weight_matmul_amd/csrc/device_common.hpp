@@ -32,6 +32,33 @@ __device__ __forceinline__ float4 load_act4(const uint16_t *p, int64_t i) {
                        __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
 }
 
+// ---- LDS-DMA (global_load_lds_dwordx4) -----------------------------------------
+// One 16-byte LDS-DMA load: lane L copies 16 bytes from src to LDS byte
+// lds_base + 16 L (lds_base is wave-uniform). Written in asm so that the
+// compiler's own wait insertion, which cannot tell which LDS bytes the load
+// fills and so waits for it before any LDS read, leaves it alone; the kernel
+// waits for it with an explicit vmcnt. The load has no register result, and
+// M0 and the address registers are read when it issues. One wait state
+// between the M0 write and the load.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void vmcnt_wait(int n) {
+    // s_waitcnt with only the vector-memory counter constrained (expcnt 7, lgkmcnt 15 = no wait)
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
 // ---- wave reductions (wave64) -------------------------------------------------
 // Within each row of 16 lanes: DPP quad permutes (xor 1, xor 2), half-row
 // mirror and row mirror leave the row total in every lane of the row; the four

@@ -425,31 +425,6 @@ struct DmaShape {
 };
 constexpr int kStages = 3;
 
-// One 16-byte LDS-DMA load: lane L copies 16 bytes from src to LDS byte
-// lds_base + 16 L (lds_base is wave-uniform). Written in asm so that the
-// compiler's own wait insertion, which cannot tell which LDS bytes the load
-// fills and so waits for it before any LDS read, leaves it alone; the kernel
-// waits for it with an explicit vmcnt. The load has no register result, and
-// M0 and the address registers are read when it issues. One wait state
-// between the M0 write and the load.
-__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds_base), "v"(src)
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void vmcnt_wait(int n) {
-    // s_waitcnt with only the vector-memory counter constrained (expcnt 7, lgkmcnt 15 = no wait)
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-}
-
 template <int NG, int JN, int EPI>
 __global__ __launch_bounds__(256, 2) void tgemm_dma_kernel(const ContractArgs p, const int tiles_n) {
     using S = DmaShape<NG, JN>;

@@ -12,7 +12,12 @@
 // end of this file: t^T [k][n] from the packed words for du; (dy / s)^T [n][m]
 // and q^T [k][m] for dW (zero-padded along m to the K step).
 //
-// Tiling: a workgroup of four waves owns a 128 x 128 block of C; each wave a
+// Two kernels share the MFMA tiling and the LDS row layout: where K is a whole
+// number of K steps and rows are 16-byte aligned (both products at the layer
+// shapes), an LDS-DMA kernel with three stages (gemm_bf16_nt_dma_kernel, below);
+// otherwise the register-staged kernel described here.
+//
+// Tiling of the staged kernel: a workgroup of four waves owns a 128 x 128 block of C; each wave a
 // 64 x 64 block (2 x 2 tiles of 32 x 32, 64 accumulators per lane), two
 // workgroups per CU. K moves 64 bf16 (128 bytes) per step through two LDS
 // stages; the next step's tiles are loaded into registers while the current
@@ -155,6 +160,151 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt_kernel(const uint16_t *__
         }
 }
 
+// ----------------------------------------------------------------------------
+// K a multiple of 64, 16-byte aligned rows: LDS stages filled by LDS-DMA
+// ----------------------------------------------------------------------------
+// A BM x BN block of C per workgroup of eight waves, each wave a block of TI x TJ
+// tiles of 32 x 32; NS LDS stages are filled straight from memory by 16-byte
+// LDS-DMA loads (global_load_lds_dwordx4) NS - 1 K steps ahead of the MFMAs, with
+// no staging registers and one barrier per step. Each lane picks the source chunk
+// of the LDS slot it fills, which is how the rows get the same XOR swizzle as
+// above; rows past M or N read a clamped valid row (their outputs are never
+// stored).
+template <int BM, int BN, int NS, int TI, int TJ>
+struct DmaGemm {
+    static constexpr int WN = BN / (32 * TJ);                  // waves along N
+    static constexpr int NW = (BM / (32 * TI)) * WN;           // waves
+    static constexpr int NT = NW * 64;
+    static constexpr int STAGE = (BM + BN) * kGRowBytes;       // A rows, then B rows
+    static constexpr int A_INS = BM * (kGRowBytes / 16) / NT;  // 16-byte A slots per thread and step
+    static constexpr int B_INS = BN * (kGRowBytes / 16) / NT;
+    static constexpr int LOADS = A_INS + B_INS;                // DMA loads per wave and step
+    static_assert(A_INS * NT == BM * (kGRowBytes / 16) && B_INS * NT == BN * (kGRowBytes / 16), "whole slots");
+    static_assert(NS == 2 || LOADS == 6 || LOADS == 8, "vmcnt_wait covers the steps in flight");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS");
+};
+
+template <int BM, int BN, int NS, int TI, int TJ>
+__global__ __launch_bounds__((DmaGemm<BM, BN, NS, TI, TJ>::NT)) void gemm_bf16_nt_dma_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, float *__restrict__ C, int M, int N, int64_t lda,
+    int64_t ldb, int64_t ldc, int tiles_n, int all_steps, int steps_per_split, int64_t split_stride) {
+    using S = DmaGemm<BM, BN, NS, TI, TJ>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NS * S::STAGE];
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int per = G >> 3, rem = G & 7;
+    const int tile = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int tiles_m = G / tiles_n;
+    const int group = tile / (kGGroupM * tiles_n);
+    const int first_m = group * kGGroupM;
+    const int gsz = tiles_m - first_m < kGGroupM ? tiles_m - first_m : kGGroupM;
+    const int in_group = tile - group * kGGroupM * tiles_n;
+    const int tm = first_m + in_group % gsz, tn = in_group / gsz;
+    const int m0 = tm * BM, n0 = tn * BN;
+    C += (int64_t)blockIdx.y * split_stride;
+
+    constexpr int NW = S::NW;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / S::WN, wn = wave % S::WN;  // wave block: rows wm*32*TI + ..., columns wn*32*TJ + ...
+    const int lr = lane & 31, lg = lane >> 5;
+    const int s0 = blockIdx.y * steps_per_split;
+    const int s1 = s0 + steps_per_split < all_steps ? s0 + steps_per_split : all_steps;
+
+    // the source of each of the lane's LDS slots: slot -> (row, position), position holds
+    // chunk position ^ ((row >> 1) & 7) of the row's 64 elements of the step
+    const uint16_t *asrc[S::A_INS];
+#pragma unroll
+    for (int i = 0; i < S::A_INS; ++i) {
+        const int slot = (i * NW + wave) * 64 + lane, row = slot >> 3, c16 = (slot & 7) ^ ((row >> 1) & 7);
+        const int gr = m0 + row < M ? m0 + row : M - 1;
+        asrc[i] = A + (int64_t)gr * lda + 8 * c16;
+    }
+    const uint16_t *bsrc[S::B_INS];
+#pragma unroll
+    for (int i = 0; i < S::B_INS; ++i) {
+        const int slot = (i * NW + wave) * 64 + lane, row = slot >> 3, c16 = (slot & 7) ^ ((row >> 1) & 7);
+        const int gr = n0 + row < N ? n0 + row : N - 1;
+        bsrc[i] = B + (int64_t)gr * ldb + 8 * c16;
+    }
+    auto issue = [&](int ks) {
+        // LDS byte offset of the step's stage (low half of its generic address) plus the wave's slots
+        const uint8_t *base = smem + (ks % NS) * S::STAGE;
+        const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base + wave * 64 * 16);
+#pragma unroll
+        for (int i = 0; i < S::A_INS; ++i) lds_dma16(asrc[i] + ks * kGK, lds + i * NW * 64 * 16);
+#pragma unroll
+        for (int i = 0; i < S::B_INS; ++i) lds_dma16(bsrc[i] + ks * kGK, lds + BM * kGRowBytes + i * NW * 64 * 16);
+    };
+
+    f32x16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+
+    auto compute = [&](const uint8_t *sa) {
+        const uint8_t *sb = sa + BM * kGRowBytes;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {  // 16 of K per MFMA: chunk 2 kk + lg of the row
+            const int c16 = 2 * kk + lg;
+            bf16x8 af[TI], bfr[TJ];
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const int row = wm * 32 * TI + i * 32 + lr;
+                af[i] = *reinterpret_cast<const bf16x8 *>(sa + row * kGRowBytes + swz(row, c16));
+            }
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int row = wn * 32 * TJ + j * 32 + lr;
+                bfr[j] = *reinterpret_cast<const bf16x8 *>(sb + row * kGRowBytes + swz(row, c16));
+            }
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // step ks: wait for its loads (this wave's: they retire in order; the barrier then covers
+    // every wave's, and every wave has finished with the stage the next loads reuse), start the
+    // loads of step ks + NS - 1, multiply
+    if (s0 < s1) {
+#pragma unroll
+        for (int p = 0; p < NS - 1; ++p)
+            if (s0 + p < s1) issue(s0 + p);
+        for (int ks = s0; ks < s1; ++ks) {
+            vmcnt_wait(NS == 3 && ks + 1 < s1 ? S::LOADS : 0);
+            asm volatile("" ::: "memory");  // keep LDS accesses on their side of the barrier
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (ks + NS - 1 < s1) issue(ks + NS - 1);
+            compute(smem + (ks % NS) * S::STAGE);
+        }
+    }
+
+    // register r of lane l holds row (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32 of its tile
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int col = n0 + wn * 32 * TJ + j * 32 + lr;
+            if (col >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 32 * TI + i * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+                if (row < M) C[(int64_t)row * ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
+// the LDS-DMA configuration the products run with: 256 x 256 blocks, eight waves of 128 x 64,
+// two 64 KB stages (measured on MI355X at the 1.3B layer's products, du 32768 x 2048 x 2048
+// and dW 2048 x 2048 x 32768: 36-37 % of the dense bf16 peak; 256 x 128 blocks of 64 x 64
+// waves with three stages 31-32 %, 256 x 256 of 64 x 128 waves 34 %, of four 128 x 128 waves
+// (one wave per SIMD) 32 %, 128 x 128 blocks 27-31 %)
+constexpr int kDmaBM = 256, kDmaBN = 256, kDmaNS = 2, kDmaTI = 4, kDmaTJ = 2;
+using DmaConfig = DmaGemm<kDmaBM, kDmaBN, kDmaNS, kDmaTI, kDmaTJ>;
+
 // C[r][c] = sum over the splits in order of part[split][r][c] (row stride ldc in both)
 __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ part, int splits,
                                                         int64_t split_stride, int M, int N, int64_t ldc,
@@ -168,27 +318,41 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict_
     C[o] = v;
 }
 
-// Splits along K for a product of few tiles: enough workgroups for two per CU,
-// each split at least 8 K steps.
+// Splits along K for a product of few tiles: enough workgroups for two rounds of
+// the CUs' resident workgroups (one per CU for the LDS-DMA kernel, which runs when
+// K is a whole number of K steps; two for the staged one), each split at least 8 K steps.
 int gemm_bf16_splits(int m, int n, int k) {
-    const int tiles = ((m + kGM - 1) / kGM) * ((n + kGN - 1) / kGN);
+    const bool dma = k % kGK == 0;
+    const int tiles = dma ? ((m + kDmaBM - 1) / kDmaBM) * ((n + kDmaBN - 1) / kDmaBN)
+                          : ((m + kGM - 1) / kGM) * ((n + kGN - 1) / kGN);
+    const int want = dma ? 256 : 512;
     const int steps = (k + kGK - 1) / kGK;
     int sp = 1;
-    while (sp < 16 && tiles * sp < 512 && steps / (2 * sp) >= 8) sp *= 2;
+    while (sp < 16 && tiles * sp < want && steps / (2 * sp) >= 8) sp *= 2;
     return sp;
 }
 
 hipError_t launch_gemm_bf16_nt(const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb, int m, int n, int k,
                                float *c, int64_t ldc, float *part, hipStream_t st) {
     if (m <= 0 || n <= 0) return hipSuccess;
-    const int tiles_m = (m + kGM - 1) / kGM, tiles_n = (n + kGN - 1) / kGN;
     const int steps = (k + kGK - 1) / kGK;
     const int sp = part ? gemm_bf16_splits(m, n, k) : 1;
     const int per_split = (steps + sp - 1) / sp;
     const int64_t stride = (int64_t)m * ldc;
-    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)sp);
-    launch_k(gemm_bf16_nt_kernel, grid, 256, 0, st, a, b, sp > 1 ? part : c, m, n, k, lda, ldb, ldc, tiles_n,
-             per_split, stride);
+    // the LDS-DMA kernel wherever every 16-byte slot it fills is whole and aligned
+    const bool dma = k % kGK == 0 && lda % 8 == 0 && ldb % 8 == 0 && (reinterpret_cast<uintptr_t>(a) & 15u) == 0 &&
+                     (reinterpret_cast<uintptr_t>(b) & 15u) == 0;
+    if (dma) {
+        const int tiles_m = (m + kDmaBM - 1) / kDmaBM, tiles_n = (n + kDmaBN - 1) / kDmaBN;
+        const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)sp);
+        launch_k(gemm_bf16_nt_dma_kernel<kDmaBM, kDmaBN, kDmaNS, kDmaTI, kDmaTJ>, grid, DmaConfig::NT, 0, st, a, b,
+                 sp > 1 ? part : c, m, n, lda, ldb, ldc, tiles_n, steps, per_split, stride);
+    } else {
+        const int tiles_m = (m + kGM - 1) / kGM, tiles_n = (n + kGN - 1) / kGN;
+        const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)sp);
+        launch_k(gemm_bf16_nt_kernel, grid, 256, 0, st, a, b, sp > 1 ? part : c, m, n, k, lda, ldb, ldc, tiles_n,
+                 per_split, stride);
+    }
     if (sp > 1)
         launch_k(split_sum_kernel, (unsigned)(((int64_t)m * n + 255) / 256), 256, 0, st, part, sp, stride, m, n, ldc,
                  c);

@@ -577,12 +577,13 @@ struct BitlinearBwdWs {
     float *du, *gpart, *gpart2, *split;
 };
 
-// rows of the dW product's operands, zero-padded to whole 16-byte pieces
-int64_t pad8(int64_t m) { return (m + 7) / 8 * 8; }
+// rows of the dW product's operands (its contraction), zero-padded to whole K steps of the
+// products (64), so that the product runs on its LDS-DMA kernel at any row count
+int64_t pad_k(int64_t m) { return (m + 63) / 64 * 64; }
 
 // floats of the dW product's per-split partial blocks for an n x k weight over m rows (0: no split)
 size_t dw_split_floats(int64_t m, int n, int k) {
-    const int sp = m > 0 ? gemm_bf16_splits(n, k, (int)pad8(m)) : 1;
+    const int sp = m > 0 ? gemm_bf16_splits(n, k, (int)pad_k(m)) : 1;
     return sp > 1 ? (size_t)sp * n * k : 0;
 }
 
@@ -593,8 +594,8 @@ size_t bitlinear_bwd_plan(Carver &c, int64_t m, int n, int k, mmf_dtype dyt, Bit
     w.s = c.take<float>((size_t)m);
     w.tT = c.take<uint16_t>((size_t)n * k);
     w.dy16 = dyt == MMF_F32 ? c.take<uint16_t>((size_t)m * n) : nullptr;
-    w.dyT = c.take<uint16_t>((size_t)n * pad8(m));
-    w.qT = c.take<uint16_t>((size_t)k * pad8(m));
+    w.dyT = c.take<uint16_t>((size_t)n * pad_k(m));
+    w.qT = c.take<uint16_t>((size_t)k * pad_k(m));
     w.du = c.take<float>((size_t)m * k);
     const int64_t nblk = m > 0 ? (m + rmsnorm_bwd_rows(m) - 1) / rmsnorm_bwd_rows(m) : 0;
     w.gpart = c.take<float>((size_t)nblk * k);
@@ -643,7 +644,7 @@ hipError_t bitlinear_bwd_run(const void *x, ActType xt, int64_t m, const mmf_ter
                  (dgain ? "gain_reduce;" : "");
     }
     if (e == hipSuccess && dw) {
-        const int64_t mp = pad8(m);
+        const int64_t mp = pad_k(m);
         e = timed("transpose_bf16<dy/s>", m, n, n, stream, [&] {
             return launch_transpose_bf16(dy, dyt == ACT_F32 ? 0 : 1, B.s, m, n, B.dyT, mp, stream);
         });
