@@ -106,11 +106,14 @@ def test_hgrn2_decode_step_full_width(gpu):
     assert_close(host(st), rs, 1e-4, "state")
 
 
-def test_hgrn2_chunk_saturated_gates_and_in_place(gpu):
-    """The chunked form with gates of exactly 0 and 1 (every decay product 0 or 1, nothing
-    divided) and with the state updated in place, against the oracle."""
+@pytest.mark.parametrize("e", [64, 128])
+def test_hgrn2_chunk_saturated_gates_and_in_place(gpu, e):
+    """The chunked form with gates of exactly 0 and 1 and with the state updated in place,
+    against the oracle. Chunks 0 and 2 hold zero gates (their A and K^ come from running
+    products, by the workgroup's vote), chunk 1 has gates of 1 on half the channels, the
+    others are ordinary (A = Q~ K~^T): both paths alternate within one sequence."""
     mmf = _mmf()
-    b, t, d, e = 2, 70, 256, 128
+    b, t, d = 2, 70, 256
     f, i, o = synth.hgrn2_inputs(b, t, d, 918)
     f = f.copy()
     f[:, 5:9] = 0.0
@@ -119,7 +122,7 @@ def test_hgrn2_chunk_saturated_gates_and_in_place(gpu):
     s0 = _state(b, d, e, 919)
     st = dev(s0, gpu)
     y = mmf.hgrn2_scan_fwd(dev(f, gpu), dev(i, gpu), dev(o, gpu), e, st, s_last=st, mode="chunk")
-    assert mmf.last_path() == "hgrn2_chunk<128>"
+    assert mmf.last_path() == "hgrn2_chunk<%d>" % e
     ry, rs = oracle.hgrn2_scan(f, i, o, e, s0)
     assert_close(host(y), ry, 1e-4, "y")
     assert_close(host(st), rs, 1e-4, "state")
