@@ -233,11 +233,12 @@ __global__ __launch_bounds__(256) void hgrn2_scan_kernel(const float *__restrict
 // block's columns 16w .. 16w+15 and holds their E x 16 slice of the state as
 // E/16 accumulator tiles, which serve as the B operand of Q~ S0 as they are.
 //
-// The loop is pipelined over three chunks, two barriers per chunk: while the
-// waves read out chunk k (Y and the state update, the only steps that need
-// the state), they form chunk k+1's A, and between the barriers the decays of
-// chunk k+2 (Q~, K~, the total decay) are prepared from its gates, which were
-// parked in LDS during the same iteration. Gates load into registers one
+// The loop is pipelined over three chunks, with two synchronisations per
+// chunk (a barrier, and the workgroup's vote on small gates, a block-wide OR
+// that also orders LDS): while the waves read out chunk k (Y and the state
+// update, the only steps that need the state), they form chunk k+1's A, and
+// between the two the decays of chunk k+2 (Q~, K~, the total decay) are
+// prepared from its gates, which were parked in LDS during the same iteration. Gates load into registers one
 // iteration before they are parked. Tokens past the sequence end act as
 // f = 1, o = 0, i = 0.
 //
