@@ -302,8 +302,8 @@ mmf_status mmf_hgrn_scan_bwd(const float *f, const float *h, const float *h0, co
  *  Q~[t][a] = o_t[a] prod_{r<=t} f_r[a], K^[s][a] = (1 - f_s[a]) prod_{r>s} f_r[a]
  *  and A[t][s] = sum_a o_t[a] (1 - f_s[a]) prod_{s<r<=t} f_r[a] (s <= t): the
  *  same value up to rounding. CHUNK needs (t + 32) * d * 4 < 2^31 (a sequence's
- *  rows are addressed with 32-bit byte offsets). AUTO takes CHUNK from 64
- *  tokens on where it can.
+ *  rows are addressed with 32-bit byte offsets). AUTO takes CHUNK from 16
+ *  tokens on where it can (RECURRENT below, the one-token step included).
  *  e in {16, 32, 64, 128}, d a multiple of e; every tensor 16-byte aligned.
  *  Errors: INVALID_ARG, UNSUPPORTED (e; CHUNK with e < 64 or a sequence too
  *  long for it), HIP.
