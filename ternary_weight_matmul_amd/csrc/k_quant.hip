@@ -268,8 +268,12 @@ constexpr int kFewRows = 2048;  // below this many rows a row gets a whole workg
 constexpr int kMaxCachedChunks = 32;  // 64 lanes * 32 chunks of 16 bytes per row in registers
 
 // 16-byte chunks of e elements per lane when a wave owns the row
+// (powers of two up to 8, then 12, 16, 24, 32: a row of 5632 fp32 values takes 24, not 32,
+// and the registers of the 8 chunk slots it would never fill)
 static int chunk_bucket(int k, int e = 4) {
     const int nch = (k / e + kWave - 1) / kWave;
+    if (nch > 16) return nch <= 24 ? 24 : 32;
+    if (nch > 8) return nch <= 12 ? 12 : 16;
     int b = 1;
     while (b < nch) b *= 2;
     return b;
@@ -311,7 +315,7 @@ static void norm_quant_dispatch(const T *x, int64_t m, int k, const float *gain,
     }
     switch (nv) {
 #define MMF_NQ(NV) case NV: launch_k(norm_quant_kernel<T, NV>, grid, block, 0, st, x, m, k, gain, eps, q, s, sumq); break;
-        MMF_NQ(1) MMF_NQ(2) MMF_NQ(4) MMF_NQ(8) MMF_NQ(16) MMF_NQ(32)
+        MMF_NQ(1) MMF_NQ(2) MMF_NQ(4) MMF_NQ(8) MMF_NQ(12) MMF_NQ(16) MMF_NQ(24) MMF_NQ(32)
 #undef MMF_NQ
     }
     if (path) *path += std::string("norm_quant<") + tn + "," + std::to_string(nv) + ">;";
@@ -448,7 +452,7 @@ static hipError_t gnorm_dispatch(const float *h, const TG *g, int64_t m, int d, 
     const int nv = chunk_bucket(d);
     switch (nv) {
 #define MMF_GQ(NV) case NV: launch_k(gnorm_quant_kernel<TG, NV>, grid, block, 0, stream, h, g, m, d, g_norm_w, o_gain, eps, q, s, sumq, u_out); break;
-        MMF_GQ(1) MMF_GQ(2) MMF_GQ(4) MMF_GQ(8) MMF_GQ(16) MMF_GQ(32)
+        MMF_GQ(1) MMF_GQ(2) MMF_GQ(4) MMF_GQ(8) MMF_GQ(12) MMF_GQ(16) MMF_GQ(24) MMF_GQ(32)
 #undef MMF_GQ
         default: return hipErrorInvalidValue;  // d > 8192 is rejected by the ABI layer
     }
