@@ -51,6 +51,7 @@ __device__ __forceinline__ void vmcnt_wait(int n) {
     // s_waitcnt with only the vector-memory counter constrained (expcnt 7, lgkmcnt 15 = no wait)
     switch (n) {
         case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
         case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
         case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
         case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;

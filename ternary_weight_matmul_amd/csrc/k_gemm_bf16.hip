@@ -170,25 +170,34 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_nt_kernel(const uint16_t *__
 // of the LDS slot it fills, which is how the rows get the same XOR swizzle as
 // above; rows past M or N read a clamped valid row (their outputs are never
 // stored).
-template <int BM, int BN, int NS, int TI, int TJ>
+template <int BM, int BN, int NS, int TI, int TJ, int BK>
 struct DmaGemm {
     static constexpr int WN = BN / (32 * TJ);                  // waves along N
     static constexpr int NW = (BM / (32 * TI)) * WN;           // waves
     static constexpr int NT = NW * 64;
-    static constexpr int STAGE = (BM + BN) * kGRowBytes;       // A rows, then B rows
-    static constexpr int A_INS = BM * (kGRowBytes / 16) / NT;  // 16-byte A slots per thread and step
-    static constexpr int B_INS = BN * (kGRowBytes / 16) / NT;
+    static constexpr int RB = BK * 2;                          // bytes of a row per K step
+    static constexpr int CH = RB / 16;                         // 16-byte chunks of a row
+    static constexpr int STAGE = (BM + BN) * RB;               // A rows, then B rows
+    static constexpr int A_INS = BM * CH / NT;                 // 16-byte A slots per thread and step
+    static constexpr int B_INS = BN * CH / NT;
     static constexpr int LOADS = A_INS + B_INS;                // DMA loads per wave and step
-    static_assert(A_INS * NT == BM * (kGRowBytes / 16) && B_INS * NT == BN * (kGRowBytes / 16), "whole slots");
-    static_assert(NS == 2 || LOADS == 6 || LOADS == 8, "vmcnt_wait covers the steps in flight");
-    static_assert(NS * STAGE <= 160 * 1024, "LDS");
+    static_assert(BK == 64 || BK == 32, "K step");
+    static_assert(A_INS * NT == BM * CH && B_INS * NT == BN * CH, "whole slots");
+    static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS");
+    // position of chunk c of a row: XOR-swizzled by the row so that the 16 rows one quarter of
+    // a wave reads at the same chunk fall in different banks (128-byte rows: pairs of rows share
+    // a bank group; 64-byte rows: quadruples)
+    static __device__ __forceinline__ int pos(int row, int c) {
+        return CH == 8 ? c ^ ((row >> 1) & 7) : c ^ ((row >> 2) & 3);
+    }
 };
 
-template <int BM, int BN, int NS, int TI, int TJ>
-__global__ __launch_bounds__((DmaGemm<BM, BN, NS, TI, TJ>::NT)) void gemm_bf16_nt_dma_kernel(
+template <int BM, int BN, int NS, int TI, int TJ, int BK>
+__global__ __launch_bounds__((DmaGemm<BM, BN, NS, TI, TJ, BK>::NT)) void gemm_bf16_nt_dma_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, float *__restrict__ C, int M, int N, int64_t lda,
     int64_t ldb, int64_t ldc, int tiles_n, int all_steps, int steps_per_split, int64_t split_stride) {
-    using S = DmaGemm<BM, BN, NS, TI, TJ>;
+    using S = DmaGemm<BM, BN, NS, TI, TJ, BK>;
+    constexpr int RB = S::RB, CH = S::CH;
     __shared__ __attribute__((aligned(16))) uint8_t smem[NS * S::STAGE];
     const int G = gridDim.x, bid = blockIdx.x;
     const int xcd = bid & 7, idx = bid >> 3;
@@ -210,19 +219,19 @@ __global__ __launch_bounds__((DmaGemm<BM, BN, NS, TI, TJ>::NT)) void gemm_bf16_n
     const int s0 = blockIdx.y * steps_per_split;
     const int s1 = s0 + steps_per_split < all_steps ? s0 + steps_per_split : all_steps;
 
-    // the source of each of the lane's LDS slots: slot -> (row, position), position holds
-    // chunk position ^ ((row >> 1) & 7) of the row's 64 elements of the step
+    // the source of each of the lane's LDS slots: slot -> (row, position), position p holds
+    // the chunk whose swizzled position is p (the swizzle is its own inverse)
     const uint16_t *asrc[S::A_INS];
 #pragma unroll
     for (int i = 0; i < S::A_INS; ++i) {
-        const int slot = (i * NW + wave) * 64 + lane, row = slot >> 3, c16 = (slot & 7) ^ ((row >> 1) & 7);
+        const int slot = (i * NW + wave) * 64 + lane, row = slot / CH, c16 = S::pos(row, slot % CH);
         const int gr = m0 + row < M ? m0 + row : M - 1;
         asrc[i] = A + (int64_t)gr * lda + 8 * c16;
     }
     const uint16_t *bsrc[S::B_INS];
 #pragma unroll
     for (int i = 0; i < S::B_INS; ++i) {
-        const int slot = (i * NW + wave) * 64 + lane, row = slot >> 3, c16 = (slot & 7) ^ ((row >> 1) & 7);
+        const int slot = (i * NW + wave) * 64 + lane, row = slot / CH, c16 = S::pos(row, slot % CH);
         const int gr = n0 + row < N ? n0 + row : N - 1;
         bsrc[i] = B + (int64_t)gr * ldb + 8 * c16;
     }
@@ -231,9 +240,9 @@ __global__ __launch_bounds__((DmaGemm<BM, BN, NS, TI, TJ>::NT)) void gemm_bf16_n
         const uint8_t *base = smem + (ks % NS) * S::STAGE;
         const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base + wave * 64 * 16);
 #pragma unroll
-        for (int i = 0; i < S::A_INS; ++i) lds_dma16(asrc[i] + ks * kGK, lds + i * NW * 64 * 16);
+        for (int i = 0; i < S::A_INS; ++i) lds_dma16(asrc[i] + ks * BK, lds + i * NW * 64 * 16);
 #pragma unroll
-        for (int i = 0; i < S::B_INS; ++i) lds_dma16(bsrc[i] + ks * kGK, lds + BM * kGRowBytes + i * NW * 64 * 16);
+        for (int i = 0; i < S::B_INS; ++i) lds_dma16(bsrc[i] + ks * BK, lds + BM * RB + i * NW * 64 * 16);
     };
 
     f32x16 acc[TI][TJ];
@@ -243,20 +252,20 @@ __global__ __launch_bounds__((DmaGemm<BM, BN, NS, TI, TJ>::NT)) void gemm_bf16_n
         for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
 
     auto compute = [&](const uint8_t *sa) {
-        const uint8_t *sb = sa + BM * kGRowBytes;
+        const uint8_t *sb = sa + BM * RB;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {  // 16 of K per MFMA: chunk 2 kk + lg of the row
+        for (int kk = 0; kk < BK / 16; ++kk) {  // 16 of K per MFMA: chunk 2 kk + lg of the row
             const int c16 = 2 * kk + lg;
             bf16x8 af[TI], bfr[TJ];
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
                 const int row = wm * 32 * TI + i * 32 + lr;
-                af[i] = *reinterpret_cast<const bf16x8 *>(sa + row * kGRowBytes + swz(row, c16));
+                af[i] = *reinterpret_cast<const bf16x8 *>(sa + row * RB + (S::pos(row, c16) << 4));
             }
 #pragma unroll
             for (int j = 0; j < TJ; ++j) {
                 const int row = wn * 32 * TJ + j * 32 + lr;
-                bfr[j] = *reinterpret_cast<const bf16x8 *>(sb + row * kGRowBytes + swz(row, c16));
+                bfr[j] = *reinterpret_cast<const bf16x8 *>(sb + row * RB + (S::pos(row, c16) << 4));
             }
 #pragma unroll
             for (int i = 0; i < TI; ++i)
@@ -265,15 +274,17 @@ __global__ __launch_bounds__((DmaGemm<BM, BN, NS, TI, TJ>::NT)) void gemm_bf16_n
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
     };
-    // step ks: wait for its loads (this wave's: they retire in order; the barrier then covers
-    // every wave's, and every wave has finished with the stage the next loads reuse), start the
-    // loads of step ks + NS - 1, multiply
+    // step ks: wait for its loads (this wave's: they retire in order, and those of the steps
+    // after it that are already in flight may stay; the barrier then covers every wave's, and
+    // every wave has finished with the stage the next loads reuse), start the loads of step
+    // ks + NS - 1, multiply
     if (s0 < s1) {
 #pragma unroll
         for (int p = 0; p < NS - 1; ++p)
             if (s0 + p < s1) issue(s0 + p);
         for (int ks = s0; ks < s1; ++ks) {
-            vmcnt_wait(NS == 3 && ks + 1 < s1 ? S::LOADS : 0);
+            const int ahead = s1 - 1 - ks < NS - 2 ? s1 - 1 - ks : NS - 2;  // later steps already issued
+            vmcnt_wait(ahead * S::LOADS);
             asm volatile("" ::: "memory");  // keep LDS accesses on their side of the barrier
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
@@ -301,9 +312,10 @@ __global__ __launch_bounds__((DmaGemm<BM, BN, NS, TI, TJ>::NT)) void gemm_bf16_n
 // two 64 KB stages (measured on MI355X at the 1.3B layer's products, du 32768 x 2048 x 2048
 // and dW 2048 x 2048 x 32768: 36-37 % of the dense bf16 peak; 256 x 128 blocks of 64 x 64
 // waves with three stages 31-32 %, 256 x 256 of 64 x 128 waves 34 %, of four 128 x 128 waves
-// (one wave per SIMD) 32 %, 128 x 128 blocks 27-31 %)
-constexpr int kDmaBM = 256, kDmaBN = 256, kDmaNS = 2, kDmaTI = 4, kDmaTJ = 2;
-using DmaConfig = DmaGemm<kDmaBM, kDmaBN, kDmaNS, kDmaTI, kDmaTJ>;
+// (one wave per SIMD) 32 %, 128 x 128 blocks 27-31 %; K steps of 32 with four 32 KB stages, three
+// steps of loads in flight, 34-35 %: the barrier every 16 MFMAs costs more than the cover gains)
+constexpr int kDmaBM = 256, kDmaBN = 256, kDmaNS = 2, kDmaTI = 4, kDmaTJ = 2, kDmaBK = 64;
+using DmaConfig = DmaGemm<kDmaBM, kDmaBN, kDmaNS, kDmaTI, kDmaTJ, kDmaBK>;
 
 // C[r][c] = sum over the splits in order of part[split][r][c] (row stride ldc in both)
 __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ part, int splits,
@@ -345,8 +357,9 @@ hipError_t launch_gemm_bf16_nt(const uint16_t *a, int64_t lda, const uint16_t *b
     if (dma) {
         const int tiles_m = (m + kDmaBM - 1) / kDmaBM, tiles_n = (n + kDmaBN - 1) / kDmaBN;
         const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)sp);
-        launch_k(gemm_bf16_nt_dma_kernel<kDmaBM, kDmaBN, kDmaNS, kDmaTI, kDmaTJ>, grid, DmaConfig::NT, 0, st, a, b,
-                 sp > 1 ? part : c, m, n, lda, ldb, ldc, tiles_n, steps, per_split, stride);
+        const int dsteps = k / kDmaBK, dper = per_split * (kGK / kDmaBK);  // the same K range per split
+        launch_k(gemm_bf16_nt_dma_kernel<kDmaBM, kDmaBN, kDmaNS, kDmaTI, kDmaTJ, kDmaBK>, grid, DmaConfig::NT, 0, st,
+                 a, b, sp > 1 ? part : c, m, n, lda, ldb, ldc, tiles_n, dsteps, dper, stride);
     } else {
         const int tiles_m = (m + kGM - 1) / kGM, tiles_n = (n + kGN - 1) / kGN;
         const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)sp);
