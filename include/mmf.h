@@ -387,6 +387,46 @@ mmf_status mmf_layer_decode_step_noalloc(const mmf_layer_weights *w, const void 
 mmf_status mmf_set_decode_kernel(int mode);
 
 /*
+ * mmf_stack_decode_step -- one decode step (one new token per sequence)
+ * through a whole stack of n_layers HGRNBit blocks in a single persistent
+ * kernel ([R3] section "HGRNBitBlock 的結構": the blocks are stacked; [R1] list
+ * "可复用的模式与技巧": the step-wise recurrence used for generation). Block l
+ * takes block l-1's output (block 0 takes x) and updates its state h[l] in
+ * place; the result is that of n_layers mmf_layer_decode_step calls chained
+ * through buffers of the activation dtype, bit for bit.
+ *  layers : [n_layers] host array; every block has the same d and inner, and
+ *           i/f/g share one gain tensor (or none) in each block.
+ *  x, out : [b][d] device, activation dtype act; they must not overlap.
+ *  b      : 1..16. d and inner multiples of 256 whose 16 rows of codes fit
+ *           in LDS (the 370M, 1.3B and 2.7B widths do); else UNSUPPORTED.
+ *  The kernel is launched cooperatively with one workgroup per CU (the launch
+ *  fails with MMF_ERR_HIP if they cannot all be resident); the phases of
+ *  every block are separated by barriers across the grid, and each
+ *  contraction's packed weights are loaded during the barrier before the
+ *  quantiser that precedes it. Every barrier wait is bounded (about a
+ *  second): a wait that expires aborts the launch, every workgroup writes NaN
+ *  over `out` (the states h are then undefined) and the count read by
+ *  mmf_stack_decode_expired grows. A cooperative launch cannot be captured
+ *  into a HIP graph.
+ *  Workspace: mmf_stack_decode_workspace_size bytes, bound to the stack and
+ *  its states by mmf_stack_decode_bind, which copies a table of the blocks'
+ *  device pointers into it and SYNCHRONISES with `stream` (call it once,
+ *  outside graph capture); every later mmf_stack_decode_step on that
+ *  workspace must pass the same layers, n_layers and b. The workspace holds
+ *  the step's intermediate values: calls that share it must not overlap.
+ *  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+mmf_status mmf_stack_decode_workspace_size(const mmf_layer_weights *layers, int32_t n_layers, int64_t b,
+                                           size_t *bytes);
+mmf_status mmf_stack_decode_bind(const mmf_layer_weights *layers, int32_t n_layers, int64_t b, float *const *h,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
+mmf_status mmf_stack_decode_step(const mmf_layer_weights *layers, int32_t n_layers, const void *x, void *out,
+                                 mmf_dtype act, int64_t b, void *ws, size_t ws_bytes, hipStream_t stream);
+/* Barrier waits of mmf_stack_decode_step that expired since the library was
+ * loaded, on the current device (synchronous; 0 in a healthy process). */
+mmf_status mmf_stack_decode_expired(uint32_t *count);
+
+/*
  * Measurement support (not part of the computation). While enabled on a
  * thread, every kernel launch made by the entry points above on that thread
  * is bracketed by two HIP events recorded on the call's stream, and one

@@ -22,6 +22,7 @@ __all__ = [
     "hgrn2_scan_fwd", "layer_fwd", "layer_bwd",
     "layer_decode_step", "layer_decode_step_noalloc",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
+    "StackDecoder", "stack_decode_expired",
     "set_decode_kernel", "DECODE_KERNELS", "hbm_ceiling",
 ]
 
@@ -36,6 +37,7 @@ SYMBOLS = [
     "mmf_layer_workspace_size", "mmf_layer_fwd", "mmf_layer_decode_step", "mmf_layer_decode_step_noalloc",
     "mmf_layer_bwd_workspace_size", "mmf_layer_bwd",
     "mmf_set_decode_kernel",
+    "mmf_stack_decode_workspace_size", "mmf_stack_decode_bind", "mmf_stack_decode_step", "mmf_stack_decode_expired",
     "mmf_timing_enable", "mmf_timing_collect", "mmf_hbm_ceiling",
 ]
 
@@ -119,6 +121,10 @@ def load():
     lib.mmf_layer_bwd.argtypes = [ctypes.POINTER(CLayerWeights), P, P, ctypes.c_int, I64, I64, P, P, ctypes.c_int,
                                   ctypes.POINTER(CLayerGrads), P, SZ, P]
     lib.mmf_set_decode_kernel.argtypes = [ctypes.c_int]
+    lib.mmf_stack_decode_workspace_size.argtypes = [ctypes.POINTER(CLayerWeights), I32, I64, ctypes.POINTER(SZ)]
+    lib.mmf_stack_decode_bind.argtypes = [ctypes.POINTER(CLayerWeights), I32, I64, ctypes.POINTER(P), P, SZ, P]
+    lib.mmf_stack_decode_step.argtypes = [ctypes.POINTER(CLayerWeights), I32, P, P, ctypes.c_int, I64, P, SZ, P]
+    lib.mmf_stack_decode_expired.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     lib.mmf_timing_enable.argtypes = [ctypes.c_int]
     lib.mmf_timing_collect.argtypes = [ctypes.POINTER(CKernelTiming), I32, ctypes.POINTER(I32)]
     lib.mmf_hbm_ceiling.argtypes = [ctypes.c_int, P, P, I64, P]
@@ -536,3 +542,41 @@ def layer_decode_step_noalloc(params: LayerParams, x, h, out, probe: Optional[La
     _check(load().mmf_layer_decode_step_noalloc(ctypes.byref(cw), _ptr(x), _ptr(out), _dtype_code(x.dtype), b,
                                                 _ptr(h), ctypes.byref(cp) if cp is not None else None, _stream()))
     return out
+
+
+class StackDecoder:
+    """A stack of blocks and their states bound to one workspace (mmf_stack_decode_bind, which
+    synchronises once); step(x) runs one token per sequence through every block in one
+    persistent kernel (mmf_stack_decode_step) and updates the states in place."""
+
+    def __init__(self, layers: list, states: list, b: int, ws=None):
+        torch = _torch()
+        lib = load()
+        if len(layers) != len(states) or not layers:
+            raise ValueError("one state per block, at least one block")
+        for h in states:
+            if h.dtype != torch.float32 or not h.is_contiguous() or tuple(h.shape) != (b, layers[0].d):
+                raise ValueError("each state must be a contiguous float32 [b, d] tensor")
+        self.layers, self.states, self.b = list(layers), list(states), b
+        self._cw = (CLayerWeights * len(layers))(*[p.c() for p in layers])
+        need = SZ(0)
+        _check(lib.mmf_stack_decode_workspace_size(self._cw, len(layers), b, ctypes.byref(need)))
+        self.ws = _workspace(need.value, states[0].device, ws)
+        hp = (P * len(states))(*[_ptr(h) for h in states])
+        _check(lib.mmf_stack_decode_bind(self._cw, len(layers), b, hp, _ptr(self.ws), self.ws.numel(), _stream()))
+
+    def step(self, x, out=None):
+        torch = _torch()
+        if x.dim() != 2 or not x.is_contiguous() or x.shape[0] != self.b:
+            raise ValueError("x must be a contiguous [b, d] tensor")
+        out = out if out is not None else torch.empty_like(x)
+        _check(load().mmf_stack_decode_step(self._cw, len(self.layers), _ptr(x), _ptr(out), _dtype_code(x.dtype),
+                                            self.b, _ptr(self.ws), self.ws.numel(), _stream()))
+        return out
+
+
+def stack_decode_expired() -> int:
+    """Barrier waits of the stack decode kernel that expired since the library was loaded (synchronous)."""
+    c = ctypes.c_uint32(0)
+    _check(load().mmf_stack_decode_expired(ctypes.byref(c)))
+    return c.value

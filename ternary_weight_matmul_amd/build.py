@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmmf.so")
-SOURCES = ["k_quant.hip", "k_scan.hip", "k_contract.hip", "k_bwd.hip", "k_gemm_bf16.hip", "k_generate.hip", "k_ceiling.hip", "k_hgrn2.hip", "mmf_abi.hip"]
+SOURCES = ["k_quant.hip", "k_scan.hip", "k_contract.hip", "k_bwd.hip", "k_gemm_bf16.hip", "k_generate.hip", "k_ceiling.hip", "k_hgrn2.hip", "k_stack.hip", "mmf_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -60,7 +60,9 @@ __device__ __forceinline__ void epilogue_vals(const ContractArgs &p, int64_t m, 
         const float f = sigmoid_fast(y[1]);
         const float xt = (1.0f - f) * silu_fast(y[0]);
         float *h = static_cast<float *>(p.out0);
-        h[o] = f * (PRE ? pre : h[o]) + xt;
+        // one fused multiply-add on the rounded x~, as the scan's step does: written out so that
+        // every kernel instantiating this epilogue rounds the same way
+        h[o] = __fmaf_rn(f, PRE ? pre : h[o], xt);
         store_aux(p, p.out1, o, y[2]);
         if (p.out2) static_cast<float *>(p.out2)[o] = f;
         if (p.out3) static_cast<float *>(p.out3)[o] = xt;

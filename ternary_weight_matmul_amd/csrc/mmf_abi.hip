@@ -19,6 +19,7 @@
 
 #include "mmf.h"
 #include "launch.hpp"
+#include "stack.hpp"
 
 using namespace mmf;
 
@@ -982,6 +983,142 @@ mmf_status mmf_layer_decode_step_noalloc(const mmf_layer_weights *w, const void 
     void *ws = nullptr;
     if ((st = scratch_for_current_device(&ws)) != MMF_OK) return st;
     return decode_step_run(w, x, out, actt, b, h, ws, probe, stream);
+}
+
+// ------------------------------------------------------ whole-stack decode --
+struct StackWs {
+    StackLayer *table;
+    unsigned *bar;
+    void *act[2];
+    float *g, *x1, *z;
+    int8_t *codes;
+    float *s;
+    int32_t *sumq;
+};
+
+static size_t stack_plan(Carver &c, int32_t n, int64_t b, int d, int inner, StackWs *o) {
+    StackWs w;
+    w.table = c.take<StackLayer>((size_t)n);
+    w.bar = c.take<unsigned>(kStackBarWords);
+    w.act[0] = c.take<float>((size_t)b * d);  // fp32-sized: holds either activation dtype
+    w.act[1] = c.take<float>((size_t)b * d);
+    w.g = c.take<float>((size_t)b * d);
+    w.x1 = c.take<float>((size_t)b * d);
+    w.z = c.take<float>((size_t)b * inner);
+    w.codes = c.take<int8_t>((size_t)16 * (d > inner ? d : inner));
+    w.s = c.take<float>(16);
+    w.sumq = c.take<int32_t>(16);
+    if (o) *o = w;
+    return c.off;
+}
+
+static mmf_status check_stack(const mmf_layer_weights *layers, int32_t n, int64_t b) {
+    if (!layers) return fail(MMF_ERR_INVALID_ARG, "layers is NULL");
+    if (n <= 0) return fail(MMF_ERR_INVALID_ARG, "n_layers=%d must be positive", (int)n);
+    for (int32_t l = 0; l < n; ++l) {
+        mmf_status st = check_layer(&layers[l]);
+        if (st != MMF_OK) return st;
+        if (layers[l].d != layers[0].d || layers[l].inner != layers[0].inner)
+            return fail(MMF_ERR_INVALID_ARG, "layer %d: d/inner differ from layer 0", (int)l);
+        if (!shared_ifg(&layers[l]))
+            return fail(MMF_ERR_UNSUPPORTED, "layer %d: i/f/g gains must be one tensor (or none)", (int)l);
+    }
+    if (const char *why = stack_decode_unsupported(b, layers[0].d, layers[0].inner))
+        return fail(MMF_ERR_UNSUPPORTED, "stack decode: %s", why);
+    return MMF_OK;
+}
+
+mmf_status mmf_stack_decode_workspace_size(const mmf_layer_weights *layers, int32_t n_layers, int64_t b,
+                                           size_t *bytes) {
+    if (!bytes) return fail(MMF_ERR_INVALID_ARG, "bytes is NULL");
+    mmf_status st = check_stack(layers, n_layers, b);
+    if (st != MMF_OK) return st;
+    Carver c(nullptr);
+    *bytes = stack_plan(c, n_layers, b, layers[0].d, layers[0].inner, nullptr);
+    return MMF_OK;
+}
+
+static mmf_status check_stack_ws(const mmf_layer_weights *layers, int32_t n_layers, int64_t b, void *ws, size_t ws_bytes) {
+    size_t need = 0;
+    mmf_status st = mmf_stack_decode_workspace_size(layers, n_layers, b, &need);
+    if (st != MMF_OK) return st;
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u))
+        return fail(MMF_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    return MMF_OK;
+}
+
+mmf_status mmf_stack_decode_bind(const mmf_layer_weights *layers, int32_t n_layers, int64_t b, float *const *h,
+                                 void *ws, size_t ws_bytes, hipStream_t stream) {
+    mmf_status st = check_stack_ws(layers, n_layers, b, ws, ws_bytes);
+    if (st != MMF_OK) return st;
+    if (!h) return fail(MMF_ERR_INVALID_ARG, "h is NULL");
+    std::vector<StackLayer> table((size_t)n_layers);
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const mmf_layer_weights &w = layers[l];
+        if (!h[l] || !aligned16(h[l])) return fail(MMF_ERR_INVALID_ARG, "h[%d] must be non-NULL and 16-byte aligned", (int)l);
+        const mmf_ternary_weight *tw[6] = {&w.i, &w.f, &w.g, &w.o, &w.gate, &w.down};
+        StackLayer &t = table[l];
+        for (int q = 0; q < 6; ++q) {
+            t.w[q] = tw[q]->packed;
+            t.mu[q] = tw[q]->mu;
+            t.gain[q] = tw[q]->norm_w;
+        }
+        t.g_norm_w = w.g_norm_w;
+        t.h = h[l];
+        t.eps = w.eps;
+        t.pad = 0;
+    }
+    Carver c(ws);
+    StackWs W;
+    stack_plan(c, n_layers, b, layers[0].d, layers[0].inner, &W);
+    hipError_t e = hipMemcpyAsync(W.table, table.data(), table.size() * sizeof(StackLayer), hipMemcpyHostToDevice,
+                                  stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);  // the host table goes out of scope
+    return hip_status(e, "mmf_stack_decode_bind");
+}
+
+mmf_status mmf_stack_decode_step(const mmf_layer_weights *layers, int32_t n_layers, const void *x, void *out,
+                                 mmf_dtype actt, int64_t b, void *ws, size_t ws_bytes, hipStream_t stream) {
+    mmf_status st = check_stack_ws(layers, n_layers, b, ws, ws_bytes);
+    if (st != MMF_OK) return st;
+    if (!valid_dtype(actt)) return fail(MMF_ERR_INVALID_ARG, "bad activation dtype");
+    if (!x || !out) return fail(MMF_ERR_INVALID_ARG, "x and out must be non-NULL");
+    if (!aligned16(x) || !aligned16(out)) return fail(MMF_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+    if (x == out) return fail(MMF_ERR_INVALID_ARG, "x and out must not overlap");
+    Carver c(ws);
+    StackWs W;
+    stack_plan(c, n_layers, b, layers[0].d, layers[0].inner, &W);
+    StackArgs a{};
+    a.layers = W.table;
+    a.n_layers = n_layers;
+    a.d = layers[0].d;
+    a.inner = layers[0].inner;
+    a.b = (int)b;
+    a.act_type = act(actt);
+    a.x = x;
+    a.out = out;
+    a.act[0] = W.act[0];
+    a.act[1] = W.act[1];
+    a.g = W.g;
+    a.x1 = W.x1;
+    a.z = W.z;
+    a.codes = W.codes;
+    a.s = W.s;
+    a.sumq = W.sumq;
+    a.bar = W.bar;
+    std::string path;
+    hipError_t e = timed("stack_decode", b, n_layers, a.d, stream, [&] { return launch_stack_decode(a, stream, &path); });
+    mmf_status r = hip_status(e, "mmf_stack_decode_step");
+    if (r == MMF_OK) g_path = path;
+    return r;
+}
+
+mmf_status mmf_stack_decode_expired(uint32_t *count) {
+    if (!count) return fail(MMF_ERR_INVALID_ARG, "count is NULL");
+    unsigned c = 0;
+    mmf_status r = hip_status(stack_decode_expired_waits(&c), "mmf_stack_decode_expired");
+    if (r == MMF_OK) *count = c;
+    return r;
 }
 
 // --------------------------------------------------------- block derivative --

@@ -253,3 +253,41 @@ def test_hbm_ceiling_rejects_bad_arguments(lib):
     assert lib.mmf_hbm_ceiling(1, p, C.c_void_p(FAKE + 8), 4096, None) == INVALID  # overlap
     assert lib.mmf_hbm_ceiling(2, p, C.c_void_p(FAKE + 4096), 4096, None) == INVALID  # overlaps the second source
     assert lib.mmf_hbm_ceiling(1, None, q, 4096, None) == INVALID
+
+
+def test_stack_decode_validation(lib):
+    SZ = ctypes.c_size_t
+    n = 3
+    layers = (B.CLayerWeights * n)(*[_layer(256, 512) for _ in range(n)])
+    need = SZ(0)
+    assert lib.mmf_stack_decode_workspace_size(layers, n, 16, ctypes.byref(need)) == OK
+    assert need.value > 0
+    big = SZ(0)
+    assert lib.mmf_stack_decode_workspace_size(layers, n, 8, ctypes.byref(big)) == OK and big.value < need.value
+    # batch outside 1..16, widths that are not multiples of 256, no blocks
+    assert lib.mmf_stack_decode_workspace_size(layers, n, 17, ctypes.byref(need)) == UNSUPPORTED
+    assert "1..16" in _err(lib)
+    assert lib.mmf_stack_decode_workspace_size(layers, n, 0, ctypes.byref(need)) == UNSUPPORTED
+    odd = (B.CLayerWeights * 1)(_layer(64, 96))
+    assert lib.mmf_stack_decode_workspace_size(odd, 1, 4, ctypes.byref(need)) == UNSUPPORTED
+    assert "256" in _err(lib)
+    assert lib.mmf_stack_decode_workspace_size(layers, 0, 4, ctypes.byref(need)) == INVALID
+    assert lib.mmf_stack_decode_workspace_size(None, 1, 4, ctypes.byref(need)) == INVALID
+    # blocks of different widths; i/f/g with different gains
+    mixed = (B.CLayerWeights * 2)(_layer(256, 512), _layer(512, 512))
+    assert lib.mmf_stack_decode_workspace_size(mixed, 2, 4, ctypes.byref(need)) == INVALID
+    split = _layer(256, 512)
+    split.f.norm_w = FAKE + 8192
+    gains = (B.CLayerWeights * 1)(split)
+    assert lib.mmf_stack_decode_workspace_size(gains, 1, 4, ctypes.byref(need)) == UNSUPPORTED
+    # bind: no states, a NULL state, a short workspace; step: aliasing, bad dtype, short workspace
+    assert lib.mmf_stack_decode_workspace_size(layers, n, 4, ctypes.byref(need)) == OK
+    hs = (ctypes.c_void_p * n)(FAKE, None, FAKE)
+    assert lib.mmf_stack_decode_bind(layers, n, 4, None, FAKE, need.value, None) == INVALID
+    assert lib.mmf_stack_decode_bind(layers, n, 4, hs, FAKE, need.value, None) == INVALID
+    assert lib.mmf_stack_decode_bind(layers, n, 4, hs, FAKE, need.value - 1, None) == WORKSPACE
+    assert lib.mmf_stack_decode_step(layers, n, FAKE, FAKE, 0, 4, FAKE, need.value, None) == INVALID
+    assert "overlap" in _err(lib)
+    assert lib.mmf_stack_decode_step(layers, n, FAKE, FAKE + 65536, 7, 4, FAKE, need.value, None) == INVALID
+    assert lib.mmf_stack_decode_step(layers, n, FAKE, FAKE + 65536, 0, 4, FAKE, 256, None) == WORKSPACE
+    assert lib.mmf_stack_decode_expired(None) == INVALID

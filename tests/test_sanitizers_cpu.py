@@ -15,7 +15,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ROCM = "/opt/rocm"
-KERNEL_OBJECTS = ["k_quant", "k_scan", "k_contract", "k_bwd", "k_gemm_bf16", "k_generate", "k_ceiling", "k_hgrn2"]
+KERNEL_OBJECTS = ["k_quant", "k_scan", "k_contract", "k_bwd", "k_gemm_bf16", "k_generate", "k_ceiling", "k_hgrn2", "k_stack"]
 SANITIZERS = ["-fsanitize=address", "-fsanitize=undefined", "-fsanitize-trap=undefined"]
 
 
