@@ -521,7 +521,8 @@ def leg_c1(mmf, torch, dev, reps: int = 100, cpu: bool = True) -> dict:
 def leg_decode(mmf, torch, dev, batches=(1, 16, 64), steps: int = 32, ceil=None) -> dict:
     """The 1.3B decode step (24 layers, bf16 x, fp32 carried state h ~ N(0,1)) at each batch:
     one step of every layer captured in a HIP graph and replayed; per-kernel durations from an
-    eager copy of 4 steps (events bound to each dispatch)."""
+    eager copy of 4 steps (events bound to each dispatch). At up to 16 rows the same step as one
+    persistent kernel over the whole stack (mmf_stack_decode_step) is timed beside it."""
     from ternary_weight_matmul_amd import synth
     d, inner, L = synth.SHAPES["1.3B"]
     layers = device_layers(mmf, torch, d, inner, L, 3, dev)
@@ -550,6 +551,13 @@ def leg_decode(mmf, torch, dev, batches=(1, 16, 64), steps: int = 32, ceil=None)
                            layer_tokens_per_s=round(b * L / (us / 1e6), 1),
                            launches_per_layer=round(sum(e["launches"] for e in kt.k.values()) / L, 1),
                            roofline=with_ceiling(kt.roofline(us / 1000.0), ceil), kernels=kt.breakdown(4))
+        if b <= 16:
+            # the same step as one persistent kernel over all 24 layers (cooperative launches, eager)
+            dec = mmf.StackDecoder(layers, [hs[l] for l in range(L)], b)
+            sus = event_ms(torch, lambda: dec.step(xin, out=outs[0]), steps, warmup=3) * 1000.0
+            res[str(b)]["stack_kernel"] = dict(us_per_layer=round(sus / L, 2), us_per_token_step=round(sus, 2),
+                                               launches_per_token_step=2, expired_waits=mmf.stack_decode_expired())
+            del dec
         del hs, xin, outs, ws, g
     del layers
     return dict(workload="1.3B decode step: 24 layers d=2048 inner=5632, bf16 x, fp32 state, HIP graph", by_batch=res)
