@@ -449,14 +449,19 @@ hipError_t launch_stack_decode(const StackArgs &a, hipStream_t st, std::string *
     const int vi = (int)(v - kStackVariants) * 2 + (a.act_type == ACT_F32 ? 0 : 1);
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (!raised[dev][vi].load(std::memory_order_acquire)) {
+        // the kernel's dynamic LDS limit goes to all that its static LDS leaves of a CU's 160 KB,
+        // once per device, so every width the variant serves can launch
         std::lock_guard<std::mutex> lock(mu);
-        if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) return e;
-        int per_cu = 0;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStkThreads, lds)) != hipSuccess) return e;
-        if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
+        hipFuncAttributes attr{};
+        if ((e = hipFuncGetAttributes(&attr, fn)) != hipSuccess) return e;
+        const int limit = 160 * 1024 - (int)attr.sharedSizeBytes;
+        if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, limit)) != hipSuccess) return e;
         if ((e = hipDeviceGetAttribute(&ncu[dev], hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
         raised[dev][vi].store(true, std::memory_order_release);
     }
+    int per_cu = 0;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStkThreads, lds)) != hipSuccess) return e;
+    if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
     const int nwg = ncu[dev] < 16 * kStkGroup ? ncu[dev] : 16 * kStkGroup;  // 16 arrival groups at most
     launch_k(stack_barrier_reset, dim3(1), dim3(256), 0, st, a.bar);
     if ((e = hipGetLastError()) != hipSuccess) return e;
