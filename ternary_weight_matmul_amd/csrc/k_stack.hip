@@ -9,9 +9,10 @@
 // the state update -> g_norm + quantise -> o_proj + residual -> quantise ->
 // gate_proj + SiLU product -> quantise -> down_proj + residual. Here all of
 // them, for every block, run in one launch: the phases are separated by
-// barriers across the whole grid, and before each barrier every wave that
-// will take part in the next contraction issues the loads of its packed
-// weights, so the weight stream of a phase overlaps the barrier before it.
+// barriers across the whole grid. A barrier is split into an arrival and a
+// wait; between the two halves of the barrier that ends a contraction, every
+// wave issues the loads of its packed weights for the next contraction, so
+// they stream in during that barrier and the quantiser phase after it.
 //
 // The launch is cooperative: all workgroups (one per CU) are resident
 // together, or the launch fails, so a barrier cannot wait for a workgroup that
