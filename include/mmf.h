@@ -407,7 +407,8 @@ mmf_status mmf_set_decode_kernel(int mode);
  *  second): a wait that expires aborts the launch, every workgroup writes NaN
  *  over `out` (the states h are then undefined) and the count read by
  *  mmf_stack_decode_expired grows. A cooperative launch cannot be captured
- *  into a HIP graph.
+ *  into a HIP graph: on a stream that is being captured the call returns
+ *  UNSUPPORTED and enqueues nothing.
  *  Workspace: mmf_stack_decode_workspace_size bytes, bound to the stack and
  *  its states by mmf_stack_decode_bind, which copies a table of the blocks'
  *  device pointers into it and SYNCHRONISES with `stream` (call it once,

@@ -1085,6 +1085,9 @@ mmf_status mmf_stack_decode_step(const mmf_layer_weights *layers, int32_t n_laye
     if (!x || !out) return fail(MMF_ERR_INVALID_ARG, "x and out must be non-NULL");
     if (!aligned16(x) || !aligned16(out)) return fail(MMF_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
     if (x == out) return fail(MMF_ERR_INVALID_ARG, "x and out must not overlap");
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return fail(MMF_ERR_UNSUPPORTED, "a cooperative launch cannot be captured into a HIP graph");
     Carver c(ws);
     StackWs W;
     stack_plan(c, n_layers, b, layers[0].d, layers[0].inner, &W);

@@ -116,3 +116,38 @@ def test_stack_rejects_and_reports(gpu):
     with pytest.raises(mmf.MMFError) as e:
         mmf.StackDecoder(Pd, [torch.zeros((4, 1024), dtype=torch.float32, device=gpu)], 4)
     assert e.value.status == 2 and "gain" in str(e.value)
+
+
+def test_stack_refuses_graph_capture(gpu):
+    """A cooperative launch cannot be captured: on a capturing stream the call is refused before
+    anything is enqueued, and the captured graph holds only the caller's own work."""
+    import torch
+    mmf = _mmf()
+    _, P = _stack(1024, 2816, 2, 2950, gpu, None)
+    h0 = [synth.activations((2, 1024), 2960 + l) for l in range(2)]
+    hs = [dev(h, gpu) for h in h0]
+    dec = mmf.StackDecoder(P, hs, 2)
+    x = _act(synth.activations((2, 1024), 2970, "bf16"), "bf16", gpu)
+    out = torch.zeros_like(x)
+    y = torch.zeros(4, device=gpu)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    refused = None
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            y.add_(1.0)
+            try:
+                dec.step(x, out=out)
+            except mmf.MMFError as e:
+                refused = e
+    assert refused is not None and refused.status == 2 and "captured" in str(refused)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(y, torch.ones(4, device=gpu))
+    assert torch.equal(out, torch.zeros_like(x))
+    for l in range(2):
+        assert np.array_equal(host(hs[l]), h0[l])
+    dec.step(x, out=out)  # outside capture it runs
+    torch.cuda.synchronize()
+    assert mmf.stack_decode_expired() == 0
