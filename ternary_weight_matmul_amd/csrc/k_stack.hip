@@ -14,7 +14,7 @@
 // wave issues the loads of its packed weights for the next contraction, so
 // they stream in during that barrier and the quantiser phase after it.
 //
-// The launch is cooperative: all workgroups (one per CU) are resident
+// The launch is cooperative: all workgroups (64, one per CU) are resident
 // together, or the launch fails, so a barrier cannot wait for a workgroup that
 // was never scheduled. Every wait is still bounded: a wait that expires
 // raises the launch's abort word and a library-wide count
@@ -49,6 +49,18 @@ constexpr int kStkThreads = kStkWaves * 64;
 constexpr int kStkPartBytes = kStkWaves * 3 * 256 * 4;  // per-wave partial sums, up to three groups
 constexpr int kStkGroup = 32;                            // workgroups per arrival counter
 constexpr long kStkSpinLimit = 1L << 21;                 // polls before a wait is given up (about a second)
+// Workgroups of a launch: 8 per XCD on MI355X. A barrier's cost grows with the
+// arrivals (measured with release and acquire: 1.9 / 3.0 / 3.9 / 5.8 us at 32 /
+// 64 / 128 / 256 workgroups), and the 1.3B stack step was fastest at 64 (60 / 64
+// us per layer at batch 1 / 16, against 80 with a workgroup on every CU): fewer
+// workgroups stream the weights more slowly, more wait longer at each barrier.
+constexpr int kStkGrid = 64;
+// 16-channel blocks per workgroup and round in the contractions (i/f/g and
+// o_proj, gate_proj, down_proj). More blocks per workgroup (every contraction
+// of the 1.3B block in one round at 64 workgroups) held more weight registers
+// across the quantiser phases than a 512-thread workgroup has: the kernel
+// spilled to scratch in every such geometry tried.
+constexpr int kSlotsD = 1, kSlotsG = 2, kSlotsI = 1;
 
 // Barrier words, each on its own 256-byte line (zeroed before every launch).
 enum { BAR_GROUPS = 0, BAR_TOP = 16 * 64, BAR_GEN = 17 * 64, BAR_ABORT = 18 * 64 };
@@ -134,12 +146,14 @@ struct PhaseGeom {
     }
 };
 
-// Issue the weight loads of this wave for the first round of a contraction
-// phase (block wg * SLOTS + slot); nothing is loaded for a block past the end.
+// Issue the weight loads of this wave for the round of a contraction phase
+// that workgroup position wg takes (block wg * SLOTS + slot; wg + round * nwg
+// in later rounds); nothing is loaded for a block past the end.
 template <int NG, int CPW, int SLOTS>
 __device__ __forceinline__ void load_weights(WeightRegs<NG, CPW> &r, const uint32_t *const (&W)[3], int nc, int K,
-                                             int blk) {
+                                             int wg) {
     const PhaseGeom<SLOTS> gm;
+    const int blk = wg * SLOTS + gm.slot;
     constexpr int WPB = PhaseGeom<SLOTS>::WPB;
     const int nblk = (nc + 15) >> 4, nchunk = K >> 8, KW = K >> 4;
     if (blk >= nblk) return;
@@ -200,7 +214,7 @@ __device__ __forceinline__ void gemv_phase(const ContractArgs &c, const uint32_t
         const bool has = blk < nblk;
         WeightRegs<NG, CPW> r;
         if (first_round) r = first;
-        else load_weights<NG, CPW, SLOTS>(r, W, nc, K, blk);
+        else load_weights<NG, CPW, SLOTS>(r, W, nc, K, base / SLOTS);  // base = (wg + round * nwg) * SLOTS
         first_round = false;
         i32x4 acc[NG];
 #pragma unroll
@@ -262,10 +276,11 @@ __device__ void poison_output(T *out, int64_t n) {
     }
 }
 
-// Phase geometry of the four contractions: i/f/g and o_proj one 16-channel
-// block per workgroup (8 waves over K = d), gate_proj two (4 waves each),
-// down_proj one (8 waves over K = inner). CDA, CDH, CIA: 256-k chunks per
-// wave for K = d over 8 and 4 waves and for K = inner over 8 waves. The
+// Phase geometry of the four contractions: i/f/g and o_proj kSlotsD 16-channel
+// blocks per workgroup, gate_proj kSlotsG, down_proj kSlotsI, the waves of a
+// workgroup split evenly between its blocks. CDA, CDH, CIA: 256-k chunks per
+// wave for K = d in i/f/g and o_proj, K = d in gate_proj and K = inner in
+// down_proj. The
 // weights of a contraction are loaded between the two halves of the barrier
 // that ends the contraction before it, so they arrive during the quantiser
 // phase in between.
@@ -288,13 +303,12 @@ __global__ __launch_bounds__(kStkThreads) void stack_decode_kernel(const StackAr
         return false;
     };
     auto arrive = [&]() { barrier_arrive(a.bar, nwg, gen_local); };
-    const int gate_blk = wg * 2 + PhaseGeom<2>().slot;
 
     WeightRegs<3, CDA> wifg;
     {
         const StackLayer &L0 = a.layers[0];
         const uint32_t *W[3] = {L0.w[0], L0.w[1], L0.w[2]};
-        load_weights<3, CDA, 1>(wifg, W, d, d, wg);
+        load_weights<3, CDA, kSlotsD>(wifg, W, d, d, wg);
     }
     for (int l = 0; l < a.n_layers; ++l) {
         const StackLayer &L = a.layers[l];
@@ -322,12 +336,12 @@ __global__ __launch_bounds__(kStkThreads) void stack_decode_kernel(const StackAr
             ContractArgs c{};
             c.nc = d;
             c.out0 = L.h; c.out1 = a.g; c.out_type = ACT_F32; c.aux_type = ACT_F32;
-            gemv_phase<3, EPI_GATES_STEP, 1, CDA>(c, Wifg, Mifg, codes, a.s, a.sumq, d, b, wg, nwg, lds_a, part,
+            gemv_phase<3, EPI_GATES_STEP, kSlotsD, CDA>(c, Wifg, Mifg, codes, a.s, a.sumq, d, b, wg, nwg, lds_a, part,
                                                    PreFrom<float>{L.h}, wifg);
         }
         arrive();
         WeightRegs<1, CDA> wo;
-        load_weights<1, CDA, 1>(wo, Wo, d, d, wg);
+        load_weights<1, CDA, kSlotsD>(wo, Wo, d, d, wg);
         if (!wait()) return;
         // 3. g_norm gate + o_proj's quantiser
         if (wg < b)
@@ -341,12 +355,12 @@ __global__ __launch_bounds__(kStkThreads) void stack_decode_kernel(const StackAr
             ContractArgs c{};
             c.nc = d;
             c.out0 = a.x1; c.out_type = ACT_F32;
-            gemv_phase<1, EPI_RESID, 1, CDA>(c, Wo, Mo, codes, a.s, a.sumq, d, b, wg, nwg, lds_a, part,
+            gemv_phase<1, EPI_RESID, kSlotsD, CDA>(c, Wo, Mo, codes, a.s, a.sumq, d, b, wg, nwg, lds_a, part,
                                               PreFrom<T>{x}, wo);
         }
         arrive();
         WeightRegs<2, CDH> wgt;
-        load_weights<2, CDH, 2>(wgt, Wg, inner, d, gate_blk);
+        load_weights<2, CDH, kSlotsG>(wgt, Wg, inner, d, wg);
         if (!wait()) return;
         // 5. quantise x1
         if (wg < b)
@@ -359,12 +373,12 @@ __global__ __launch_bounds__(kStkThreads) void stack_decode_kernel(const StackAr
             ContractArgs c{};
             c.nc = inner;
             c.out0 = a.z; c.aux_type = ACT_F32;
-            gemv_phase<2, EPI_GLU, 2, CDH>(c, Wg, Mg, codes, a.s, a.sumq, d, b, wg, nwg, lds_a, part, NoPre{},
+            gemv_phase<2, EPI_GLU, kSlotsG, CDH>(c, Wg, Mg, codes, a.s, a.sumq, d, b, wg, nwg, lds_a, part, NoPre{},
                                            wgt);
         }
         arrive();
         WeightRegs<1, CIA> wdn;
-        load_weights<1, CIA, 1>(wdn, Wd, d, inner, wg);
+        load_weights<1, CIA, kSlotsI>(wdn, Wd, d, inner, wg);
         if (!wait()) return;
         // 7. quantise z
         if (wg < b)
@@ -377,14 +391,14 @@ __global__ __launch_bounds__(kStkThreads) void stack_decode_kernel(const StackAr
             ContractArgs c{};
             c.nc = d;
             c.out0 = out; c.out_type = at;
-            gemv_phase<1, EPI_RESID, 1, CIA>(c, Wd, Md, codes, a.s, a.sumq, inner, b, wg, nwg, lds_a, part,
+            gemv_phase<1, EPI_RESID, kSlotsI, CIA>(c, Wd, Md, codes, a.s, a.sumq, inner, b, wg, nwg, lds_a, part,
                                               PreFrom<float>{a.x1}, wdn);
         }
         if (l + 1 < a.n_layers) {
             arrive();
             const StackLayer &N = a.layers[l + 1];
             const uint32_t *W[3] = {N.w[0], N.w[1], N.w[2]};
-            load_weights<3, CDA, 1>(wifg, W, d, d, wg);
+            load_weights<3, CDA, kSlotsD>(wifg, W, d, d, wg);
             if (!wait()) return;
         }
     }
@@ -416,8 +430,8 @@ static const StackVariant kStackVariants[] = {
 static const StackVariant *pick_stack_variant(int d, int inner) {
     const int nvx = (d / 4 + 255) / 256, nvz = (inner / 4 + 255) / 256;
     const int nd = d / 256, ni = inner / 256;
-    const int cda = (nd + kStkWaves - 1) / kStkWaves, cdh = (nd + kStkWaves / 2 - 1) / (kStkWaves / 2),
-              cia = (ni + kStkWaves - 1) / kStkWaves;
+    constexpr int wd = kStkWaves / kSlotsD, wgp = kStkWaves / kSlotsG, wi = kStkWaves / kSlotsI;
+    const int cda = (nd + wd - 1) / wd, cdh = (nd + wgp - 1) / wgp, cia = (ni + wi - 1) / wi;
     for (const auto &v : kStackVariants)
         if (v.nvx >= nvx && v.nvz >= nvz && v.cda >= cda && v.cdh >= cdh && v.cia >= cia) return &v;
     return nullptr;
@@ -463,7 +477,7 @@ hipError_t launch_stack_decode(const StackArgs &a, hipStream_t st, std::string *
     int per_cu = 0;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStkThreads, lds)) != hipSuccess) return e;
     if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
-    const int nwg = ncu[dev] < 16 * kStkGroup ? ncu[dev] : 16 * kStkGroup;  // 16 arrival groups at most
+    const int nwg = ncu[dev] < kStkGrid ? ncu[dev] : kStkGrid;
     launch_k(stack_barrier_reset, dim3(1), dim3(256), 0, st, a.bar);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     StackArgs args = a;
