@@ -25,6 +25,8 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <atomic>
+
 namespace mmf {
 
 constexpr int kScanU = 8;
@@ -138,15 +140,23 @@ __device__ __forceinline__ void st_stream(float *p, float v) {
     if (NT) __builtin_nontemporal_store(v, p); else *p = v;
 }
 
-template <int W, int S, int P, bool NT>
+// CW channels per workgroup (64, or 32 when the (sequence, channel-group) pairs
+// are too few to fill the GPU at 64): with 32, the two half-waves share their
+// wave's S steps of a chunk, SL = S / 2 each, and the 2W segments of a chunk
+// fold in time order (wave, half).
+template <int W, int S, int P, bool NT, int CW = 64>
 __global__ __launch_bounds__(W * 64) void scan_tiled_kernel(const float *x, const float *f, const float *h0,
                                                             float *h, float *h_last, int64_t t, int64_t d,
                                                             int64_t groups) {
-    constexpr int CH = W * S;  // steps per chunk; P chunks of loads run ahead of the arithmetic
+    constexpr int CH = W * S;    // steps per chunk; P chunks of loads run ahead of the arithmetic
+    constexpr int HS = 64 / CW;  // lanes per channel, each with SL consecutive steps of its wave's S
+    constexpr int SL = S / HS;
+    static_assert(CW * HS == 64 && SL * HS == S, "a wave covers CW channels x S steps");
     __shared__ float2 pairs[2][W][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lc = lane % CW, hs = lane / CW;
     const int64_t bi = blockIdx.x / groups;
-    const int64_t c = (blockIdx.x % groups) * 64 + lane;
+    const int64_t c = (blockIdx.x % groups) * CW + lc;
     const bool live = c < d;
     const int64_t cl = live ? c : d - 1;  // loads of idle lanes stay in bounds
     const float *xp = x + bi * t * d + cl;
@@ -154,20 +164,20 @@ __global__ __launch_bounds__(W * 64) void scan_tiled_kernel(const float *x, cons
     float *hp = h + bi * t * d + c;
     float carry = (h0 && live) ? h0[bi * d + c] : 0.0f;
     const int64_t nchunks = (t + CH - 1) / CH;
-    float fa[P + 1][S], xa[P + 1][S];  // [0] = current chunk, [1..P] = chunks in flight
+    float fa[P + 1][SL], xa[P + 1][SL];  // [0] = current chunk, [1..P] = chunks in flight
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const int64_t ts = min((int64_t)(p * CH + w * S + s), t - 1);
+        for (int s = 0; s < SL; ++s) {
+            const int64_t ts = min((int64_t)(p * CH + w * S + hs * SL + s), t - 1);
             fa[p][s] = ld_stream<NT>(fp + ts * d);
             xa[p][s] = ld_stream<NT>(xp + ts * d);
         }
     for (int64_t ch = 0; ch < nchunks; ++ch) {
-        const int64_t t0 = ch * CH + w * S;
+        const int64_t t0 = ch * CH + w * S + hs * SL;
         if (ch + P < nchunks) {
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
+            for (int s = 0; s < SL; ++s) {
                 const int64_t ts = min(t0 + P * CH + s, t - 1);
                 fa[P][s] = ld_stream<NT>(fp + ts * d);
                 xa[P][s] = ld_stream<NT>(xp + ts * d);
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(W * 64) void scan_tiled_kernel(const float *x, cons
         // steps past the end act as the identity (f = 1, x = 0)
         float a = 1.0f, bb = 0.0f;
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
+        for (int s = 0; s < SL; ++s) {
             const bool in = t0 + s < t;
             fa[0][s] = in ? fa[0][s] : 1.0f;
             xa[0][s] = in ? xa[0][s] : 0.0f;
@@ -185,30 +195,32 @@ __global__ __launch_bounds__(W * 64) void scan_tiled_kernel(const float *x, cons
         }
         pairs[ch & 1][w][lane] = make_float2(a, bb);
         __syncthreads();
-        // fold: the state entering wave w, and the state after the whole chunk
+        // fold: the state entering this lane's segment, and the state after the whole chunk
         float hin = carry, cn = carry;
 #pragma unroll
-        for (int v = 0; v < W; ++v) {
-            if (v == w) hin = cn;
-            const float2 pr = pairs[ch & 1][v][lane];
-            cn = pr.x * cn + pr.y;
-        }
-        float hs = hin;
+        for (int v = 0; v < W; ++v)
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            hs = fa[0][s] * hs + xa[0][s];
-            if (live && t0 + s < t) st_stream<NT>(hp + (t0 + s) * d, hs);
+            for (int u = 0; u < HS; ++u) {
+                if (v == w && u == hs) hin = cn;
+                const float2 pr = pairs[ch & 1][v][u * CW + lc];
+                cn = pr.x * cn + pr.y;
+            }
+        float hv = hin;
+#pragma unroll
+        for (int s = 0; s < SL; ++s) {
+            hv = fa[0][s] * hv + xa[0][s];
+            if (live && t0 + s < t) st_stream<NT>(hp + (t0 + s) * d, hv);
         }
         carry = cn;
 #pragma unroll
         for (int p = 0; p < P; ++p)
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
+            for (int s = 0; s < SL; ++s) {
                 fa[p][s] = fa[p + 1][s];
                 xa[p][s] = xa[p + 1][s];
             }
     }
-    if (h_last && live) h_last[bi * d + c] = carry;
+    if (h_last && live && hs == 0) h_last[bi * d + c] = carry;
 }
 
 // ----------------------------------------------------------------------------
@@ -426,6 +438,19 @@ hipError_t launch_scan_bwd(const float *f, const float *h, const float *h0, cons
     return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h, float *h_last, int64_t b,
                        int64_t t, int64_t d, int chunks, void *ws, hipStream_t stream, std::string *path) {
     if (b <= 0) return hipSuccess;
@@ -439,15 +464,22 @@ hipError_t launch_scan(const float *x, const float *f, const float *h0, float *h
         // ahead) while (sequence, channel-group) pairs are few; 4-wave
         // workgroups with 2 chunks ahead once they fill the GPU (72 % of 8 TB/s
         // at 16 x 2048 x 2048 against 69 % with 4 ahead)
-        const int64_t groups = (d + 63) / 64;
-        const unsigned grid = (unsigned)(b * groups);
+        // fewer pairs than that, but twice as many 32-channel pairs still no more than
+        // one workgroup per CU: groups of 32 channels, 16 steps per wave (the 370M
+        // prefill, 8 x 2048 x 1024: 68.7 -> 51.3 us; at 4 x 4096 x 2560 the 320
+        // workgroups took two rounds on 256 CUs and were slower, 130 -> 140 us)
         const bool nt = 12 * b * t * d > kStreamBytes;
-        const bool many = b * groups >= kTiledManyGroups;
+        const bool many = b * ((d + 63) / 64) >= kTiledManyGroups;
+        const bool half = !many && b * ((d + 31) / 32) <= cu_count();
+        const int64_t groups = half ? (d + 31) / 32 : (d + 63) / 64;
+        const unsigned grid = (unsigned)(b * groups);
         if (many && nt) launch_k(scan_tiled_kernel<4, 8, 2, true>, grid, 256, 0, stream, x, f, h0, h, h_last, t, d, groups);
         else if (many) launch_k(scan_tiled_kernel<4, 8, 2, false>, grid, 256, 0, stream, x, f, h0, h, h_last, t, d, groups);
+        else if (half && nt) launch_k(scan_tiled_kernel<16, 16, 1, true, 32>, grid, 1024, 0, stream, x, f, h0, h, h_last, t, d, groups);
+        else if (half) launch_k(scan_tiled_kernel<16, 16, 1, false, 32>, grid, 1024, 0, stream, x, f, h0, h, h_last, t, d, groups);
         else if (nt) launch_k(scan_tiled_kernel<16, 8, 1, true>, grid, 1024, 0, stream, x, f, h0, h, h_last, t, d, groups);
         else launch_k(scan_tiled_kernel<16, 8, 1, false>, grid, 1024, 0, stream, x, f, h0, h, h_last, t, d, groups);
-        if (path) *path += std::string("scan_tiled<") + (many ? "4w" : "16w") + (nt ? ",nt" : "") + ">;";
+        if (path) *path += std::string("scan_tiled<") + (many ? "4w" : half ? "16w,32c" : "16w") + (nt ? ",nt" : "") + ">;";
         return hipGetLastError();
     }
     if (chunks <= 1) {
