@@ -478,6 +478,7 @@ hipError_t launch_stack_decode(const StackArgs &a, hipStream_t st, std::string *
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kStkThreads, lds)) != hipSuccess) return e;
     if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
     const int nwg = ncu[dev] < kStkGrid ? ncu[dev] : kStkGrid;
+    if (nwg < a.b) return hipErrorInvalidConfiguration;  // the quantiser phases take a row per workgroup
     launch_k(stack_barrier_reset, dim3(1), dim3(256), 0, st, a.bar);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     StackArgs args = a;
