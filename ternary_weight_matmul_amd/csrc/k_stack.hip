@@ -14,7 +14,7 @@
 // wave issues the loads of its packed weights for the next contraction, so
 // they stream in during that barrier and the quantiser phase after it.
 //
-// The launch is cooperative: all workgroups (64, one per CU) are resident
+// The launch is cooperative: all workgroups (64, one CU each) are resident
 // together, or the launch fails, so a barrier cannot wait for a workgroup that
 // was never scheduled. Every wait is still bounded: a wait that expires
 // raises the launch's abort word and a library-wide count
@@ -131,8 +131,8 @@ struct WeightRegs {
 };
 
 // Geometry of a contraction phase: SLOTS 16-channel blocks per workgroup and
-// round, 16 / SLOTS waves per block, wave q of a block taking the 256-k chunks
-// q, q + 16 / SLOTS, ... (CPW at most).
+// round, WPB = kStkWaves / SLOTS waves per block, wave q of a block taking the
+// 256-k chunks q, q + WPB, ... (CPW at most).
 template <int SLOTS>
 struct PhaseGeom {
     static constexpr int WPB = kStkWaves / SLOTS;
