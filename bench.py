@@ -436,13 +436,39 @@ def hbm_ceilings(mmf, torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> dict:
                      "copy and 2r1w: 16384, non-temporal)")
 
 
+def mfma_ceiling(mmf, torch, dev, iters: int = 16384, reps: int = 3) -> dict:
+    """Measured int8 MFMA roof: mmf_mfma_ceiling's MFMA-only loop (four 256-thread workgroups per
+    CU, four independent 32x32x32 int8 MFMA chains per wave), timed with events."""
+    sink = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    ops = mmf.mfma_ceiling(iters, sink)
+    ms = event_ms(torch, lambda: mmf.mfma_ceiling(iters, sink), reps)
+    del sink
+    tops = ops / (ms / 1000.0) / 1e12
+    return dict(int8_TOPs=round(tops, 1), frac=round(tops / INT8_MFMA_PEAK_TOPS, 4), ms_per_launch=round(ms, 3),
+                note="MFMA-only loop (mmf_mfma_ceiling): v_mfma_i32_32x32x32_i8 on register operands, four "
+                     "independent chains per wave, four waves per SIMD; the rate includes the clock the chip "
+                     "holds under that load")
+
+
 def with_ceiling(roof: dict, ceil: dict) -> dict:
     """An HBM-bound roof also read against the measured streaming roofs: the read stream for a
-    contraction or quantiser, two reads and one write for the scan."""
+    contraction or quantiser, two reads and one write for the scan; an int8 contraction against
+    the measured MFMA-only rate."""
     if ceil and roof.get("bound") == "hbm":
         roof["frac_of_measured_read"] = round(roof["achieved"] / ceil["read_GBs"], 4)
         roof["frac_of_measured_2r1w"] = round(roof["achieved"] / ceil["two_read_one_write_GBs"], 4)
+    if ceil and ceil.get("mfma") and roof.get("bound") == "mfma" and roof.get("kernel", "").startswith("tgemm"):
+        roof["frac_of_measured_mfma"] = round(roof["achieved"] / ceil["mfma"]["int8_TOPs"], 4)
     return roof
+
+
+def contractions_with_ceiling(cr, ceil):
+    """All prefill contractions together, also against the measured MFMA-only rate."""
+    if cr and ceil and ceil.get("mfma"):
+        cr["frac_of_measured_mfma"] = round(cr["achieved"] / ceil["mfma"]["int8_TOPs"], 4)
+        cr["per_kernel_of_measured_mfma"] = {k: round(v * INT8_MFMA_PEAK_TOPS / ceil["mfma"]["int8_TOPs"], 4)
+                                             for k, v in cr["per_kernel"].items()}
+    return cr
 
 
 def leg_prefill(mmf, torch, dev, shape: str, b: int, t: int, seed: int, reps: int, ceil=None) -> dict:
@@ -470,7 +496,8 @@ def leg_prefill(mmf, torch, dev, shape: str, b: int, t: int, seed: int, reps: in
     return dict(workload="%s stack prefill: %d layers d=%d inner=%d, bf16, B=%d x T=%d" % (shape, L, d, inner, b, t),
                 value=round(b * t * L / (ms / 1000), 1), unit="layer-tokens/s", ms=round(ms, 3),
                 stack_tokens_per_s=round(b * t / (ms / 1000), 1),
-                roofline=with_ceiling(kt.roofline(ms), ceil), contraction_roofline=kt.contractions(),
+                roofline=with_ceiling(kt.roofline(ms), ceil),
+                contraction_roofline=contractions_with_ceiling(kt.contractions(), ceil),
                 kernels=kt.breakdown(8))
 
 
@@ -742,6 +769,7 @@ def run_only(args):
                    layer_bwd=measure_layer_bwd(mmf, torch, layer, 16, 2048, d, dev))
     else:
         res = hbm_ceilings(mmf, torch, dev)
+        res["mfma"] = mfma_ceiling(mmf, torch, dev)
     print(json.dumps({"leg": args.only, **res}), flush=True)
 
 
@@ -893,6 +921,8 @@ def main():
         kt.add(drecs, "decode", float(D) / DM)
     ex = args.extras != 0
     ceil = hbm_ceilings(mmf, torch, dev) if ex else None
+    if ceil:
+        ceil["mfma"] = mfma_ceiling(mmf, torch, dev)
     roof = with_ceiling(kt.roofline(ms_per_step), ceil)
 
     # ---- outside the timed region: every other config of the workload, the derivatives and
@@ -956,7 +986,7 @@ def main():
         "decode_us_per_token_step": round(decode_ms * 1000 / D, 2) if D else None,
         "decode_us_per_layer": round(decode_ms * 1000 / D / L, 2) if D else None,
         "decode_kernel_sum_us_per_token_step": round(kt.total_ms("decode") * 1000 / D, 2) if D else None,
-        "prefill_contraction_roofline": kt.contractions(),
+        "prefill_contraction_roofline": contractions_with_ceiling(kt.contractions(), ceil),
         "hbm_ceiling": ceil,
         "configs": configs,
         "scan_bwd": scan_bwd,

@@ -474,6 +474,20 @@ mmf_status mmf_timing_collect(mmf_kernel_timing *out, int32_t capacity, int32_t 
 #define MMF_HBM_CEILING_SINK_BYTES 32768
 mmf_status mmf_hbm_ceiling(int mode, const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
+/*
+ * mmf_mfma_ceiling -- measured int8 MFMA roof (measurement support): four
+ * 256-thread workgroups per CU, every wave running `iters` rounds of four
+ * independent v_mfma_i32_32x32x32_i8 on register operands (the instruction
+ * the prefill contractions use), nothing else in the loop. *ops receives the
+ * operations the launch performs (2 * 32^3 per MFMA); divided by the launch's
+ * duration it is the int8 rate this GPU sustains, clock included, against
+ * which a contraction's rate is read next to the published 5.0 POP/s.
+ *  sink : device memory, one uint32 per workgroup (4 * CUs words; sink_bytes
+ *         checked). Timed as "mfma_loop" while mmf_timing_enable is on.
+ *  Errors: INVALID_ARG, HIP.
+ */
+mmf_status mmf_mfma_ceiling(int64_t iters, void *sink, int64_t sink_bytes, int64_t *ops, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ __all__ = [
     "layer_decode_step", "layer_decode_step_noalloc",
     "layer_workspace_size", "last_path", "last_error", "SCAN_MODES", "timing_enable", "timing_collect",
     "StackDecoder", "stack_decode_expired",
-    "set_decode_kernel", "DECODE_KERNELS", "hbm_ceiling",
+    "set_decode_kernel", "DECODE_KERNELS", "hbm_ceiling", "mfma_ceiling",
 ]
 
 # Every entry point declared in include/mmf.h.
@@ -38,7 +38,7 @@ SYMBOLS = [
     "mmf_layer_bwd_workspace_size", "mmf_layer_bwd",
     "mmf_set_decode_kernel",
     "mmf_stack_decode_workspace_size", "mmf_stack_decode_bind", "mmf_stack_decode_step", "mmf_stack_decode_expired",
-    "mmf_timing_enable", "mmf_timing_collect", "mmf_hbm_ceiling",
+    "mmf_timing_enable", "mmf_timing_collect", "mmf_hbm_ceiling", "mmf_mfma_ceiling",
 ]
 
 SCAN_MODES = {"auto": 0, "recurrent": 1, "chunk": 2}
@@ -128,6 +128,7 @@ def load():
     lib.mmf_timing_enable.argtypes = [ctypes.c_int]
     lib.mmf_timing_collect.argtypes = [ctypes.POINTER(CKernelTiming), I32, ctypes.POINTER(I32)]
     lib.mmf_hbm_ceiling.argtypes = [ctypes.c_int, P, P, I64, P]
+    lib.mmf_mfma_ceiling.argtypes = [I64, P, I64, ctypes.POINTER(I64), P]
     for name in SYMBOLS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -172,6 +173,16 @@ def hbm_ceiling(src, dst, mode: str = "read"):
     n = src.numel() * src.element_size()
     m = {"read": 0, "copy": 1, "2r1w": 2}[mode]
     _check(load().mmf_hbm_ceiling(m, _ptr(src), _ptr(dst), n // 2 if m == 2 else n, _stream()))
+
+
+def mfma_ceiling(iters: int, sink) -> int:
+    """Measured int8 MFMA roof (mmf_mfma_ceiling): launches the MFMA-only loop on the current
+    stream with `sink` (a device buffer of at least 4 * CUs uint32) and returns the operations
+    the launch performs; time it with events around the call."""
+    ops = I64(0)
+    _check(load().mmf_mfma_ceiling(iters, _ptr(sink), sink.numel() * sink.element_size(), ctypes.byref(ops),
+                                   _stream()))
+    return ops.value
 
 
 def _check(status: int):

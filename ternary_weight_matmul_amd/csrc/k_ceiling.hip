@@ -94,4 +94,43 @@ hipError_t launch_stream_copy(const void *src, const void *src2, void *dst, int6
     return hipGetLastError();
 }
 
+// Measured int8 MFMA ceiling: every wave runs `iters` rounds of kChains
+// independent v_mfma_i32_32x32x32_i8 on register operands (no memory traffic
+// inside the loop), kMfmaWaves waves per CU, so the matrix pipes stay busy and
+// the clock settles where it does under a contraction's load. One word per
+// workgroup goes to sink (the accumulators must be formed).
+constexpr int kChains = 4;
+constexpr int kMfmaThreads = 256;
+
+__global__ __launch_bounds__(kMfmaThreads) void mfma_loop_kernel(int64_t iters, uint32_t *__restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    const i32x4 a = {lane * 0x01010101, 0x02020202, lane, 0x7f7f7f7f};
+    const i32x4 b = {0x01010101, lane * 0x00010001, 0x03030303, lane};
+    i32x16 acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = i32x16{};
+    for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+        for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[c], 0, 0, 0);
+    int x = 0;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x ^= acc[c][r];
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
+    if (threadIdx.x == 0) sink[blockIdx.x] = (uint32_t)x;
+}
+
+int mfma_ceiling_blocks(int cus) { return 4 * cus; }  // 4 workgroups of 4 waves per CU: 4 waves per SIMD
+
+hipError_t launch_mfma_loop(int64_t iters, int blocks, uint32_t *sink, hipStream_t st) {
+    launch_k(mfma_loop_kernel, blocks, kMfmaThreads, 0, st, iters, sink);
+    return hipGetLastError();
+}
+
+int64_t mfma_loop_ops(int64_t iters, int blocks) {
+    return (int64_t)blocks * (kMfmaThreads / kWave) * iters * kChains * (2LL * 32 * 32 * 32);
+}
+
 }  // namespace mmf

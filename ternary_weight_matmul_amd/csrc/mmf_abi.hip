@@ -1321,6 +1321,24 @@ mmf_status mmf_hbm_ceiling(int mode, const void *src, void *dst, int64_t bytes, 
     return r;
 }
 
+mmf_status mmf_mfma_ceiling(int64_t iters, void *sink, int64_t sink_bytes, int64_t *ops, hipStream_t stream) {
+    if (iters <= 0) return fail(MMF_ERR_INVALID_ARG, "iters=%lld must be positive", (long long)iters);
+    if (!sink || !ops) return fail(MMF_ERR_INVALID_ARG, "sink and ops must be non-NULL");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e, "mmf_mfma_ceiling");
+    const int blocks = mfma_ceiling_blocks(cus);
+    if (sink_bytes < (int64_t)blocks * 4)
+        return fail(MMF_ERR_INVALID_ARG, "sink needs %lld bytes (one word per workgroup)", (long long)blocks * 4);
+    *ops = mfma_loop_ops(iters, blocks);
+    e = timed("mfma_loop", iters, blocks, 0, stream,
+              [&] { return launch_mfma_loop(iters, blocks, static_cast<uint32_t *>(sink), stream); });
+    mmf_status r = hip_status(e, "mmf_mfma_ceiling");
+    if (r == MMF_OK) g_path = "mfma_loop;";
+    return r;
+}
+
 mmf_status mmf_timing_enable(int on) {
     if (on) {
         g_recs.clear();

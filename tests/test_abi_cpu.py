@@ -291,3 +291,10 @@ def test_stack_decode_validation(lib):
     assert lib.mmf_stack_decode_step(layers, n, FAKE, FAKE + 65536, 7, 4, FAKE, need.value, None) == INVALID
     assert lib.mmf_stack_decode_step(layers, n, FAKE, FAKE + 65536, 0, 4, FAKE, 256, None) == WORKSPACE
     assert lib.mmf_stack_decode_expired(None) == INVALID
+
+
+def test_mfma_ceiling_rejects_bad_arguments(lib):
+    ops = ctypes.c_int64(0)
+    assert lib.mmf_mfma_ceiling(0, FAKE, 1 << 20, ctypes.byref(ops), None) == INVALID
+    assert lib.mmf_mfma_ceiling(10, None, 1 << 20, ctypes.byref(ops), None) == INVALID
+    assert lib.mmf_mfma_ceiling(10, FAKE, 1 << 20, None, None) == INVALID

@@ -1072,6 +1072,29 @@ def test_stack_370m_prefill_24_layers_stage_fed(gpu):
     assert np.all(np.isfinite(host(cur)))
 
 
+def test_mfma_ceiling_kernel(gpu):
+    """The MFMA-only roof kernel: it reports the operations of its launch (4 workgroups of 4 waves
+    per CU, each wave iters x 4 MFMAs of 2 * 32^3 operations), and every workgroup, doing the same
+    arithmetic, writes the same sink word (written: two different fills are both overwritten)."""
+    import torch
+    mmf = _mmf()
+    cus = torch.cuda.get_device_properties(gpu).multi_processor_count
+    words = 4 * cus
+    got = []
+    for fill in (0, -1):
+        sink = torch.full((words + 16,), fill, dtype=torch.int32, device=gpu)
+        ops = mmf.mfma_ceiling(64, sink)
+        torch.cuda.synchronize()
+        assert ops == words * 4 * 64 * 4 * 2 * 32 ** 3
+        w = sink.cpu().numpy()
+        assert np.all(w[:words] == w[0]) and np.all(w[words:] == fill)
+        got.append(int(w[0]))
+    assert got[0] == got[1]
+    sink = torch.zeros(words - 1, dtype=torch.int32, device=gpu)
+    with pytest.raises(mmf.MMFError):
+        mmf.mfma_ceiling(64, sink)
+
+
 def test_hbm_ceiling_kernels_move_the_bytes(gpu):
     """The measured-roof kernels do what they time: the copy reproduces its source, the
     two-reads-one-write stream writes the XOR of its two sources, and the read stream's sink
