@@ -11,6 +11,7 @@
 // bandwidth-bound kernels are read against next to the published 8 TB/s.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "ceiling.hpp"
 
 namespace mmf {
 

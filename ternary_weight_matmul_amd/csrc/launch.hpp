@@ -168,12 +168,6 @@ hipError_t launch_gnorm_bwd(const float *h, const void *g, ActType gt, const flo
 int ceiling_blocks();
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_stream_copy(const void *src, const void *src2, void *dst, int64_t bytes, hipStream_t st);
-// Measured int8 MFMA ceiling (k_ceiling.hip): `blocks` workgroups of four waves,
-// each wave `iters` rounds of four independent 32x32x32 int8 MFMAs; one sink
-// word per workgroup; mfma_loop_ops counts the operations of such a launch.
-int mfma_ceiling_blocks(int cus);
-hipError_t launch_mfma_loop(int64_t iters, int blocks, uint32_t *sink, hipStream_t st);
-int64_t mfma_loop_ops(int64_t iters, int blocks);
 
 // Generation (k_generate.hip): embedding rows (16-byte pieces of a row of
 // row_bytes; zero rows for ids outside [0, vocab)), and per row of an int32

@@ -20,6 +20,7 @@
 #include "mmf.h"
 #include "launch.hpp"
 #include "stack.hpp"
+#include "ceiling.hpp"
 
 using namespace mmf;
 
