@@ -363,6 +363,14 @@ class KernelTable:
                 row["frac_mfma"] = round(e["ops"] / t / 1e12 / INT8_MFMA_PEAK_TOPS, 4)
             row["gbs"] = round(e["bytes"] / t / 1e9, 1)
             row["frac_hbm"] = round(e["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4)
+            if e["ops"] and not e["name"].startswith("hgrn2"):
+                # the kernel against its own roof: the longer of its ops at the int8 MFMA peak and
+                # its bytes at the HBM peak
+                t_mfma = e["ops"] / (INT8_MFMA_PEAK_TOPS * 1e12)
+                t_hbm = e["bytes"] / (HBM_PEAK_GBS * 1e9)
+                row["own_roof"] = "mfma" if t_mfma >= t_hbm else "hbm"
+                row["own_roof_us"] = round(max(t_mfma, t_hbm) * 1e6, 2)
+                row["frac_own_roof"] = round(max(t_mfma, t_hbm) / t, 4)
             out[key] = row
         return out
 
