@@ -1164,7 +1164,11 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
     const int lc = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * 16 * CB;
     const int K = p.k, KW = K >> 4, nch = K >> 2, stride = K + 16;
-    const int M = (int)p.m;
+    // a launch may give the rows to two workgroups per channel block (gridDim.y = 2,
+    // 8 rows each): this workgroup's rows are row0 .. row0 + M - 1
+    const int rows_per = 16 / (int)gridDim.y;
+    const int row0 = (int)blockIdx.y * rows_per;
+    const int M = min((int)p.m - row0, rows_per);
     int8_t *codes = reinterpret_cast<int8_t *>(part + nw * PART);
     float *srow = reinterpret_cast<float *>(codes + 16 * stride);
     // 1. this wave's rows (straight-line, clamped)
@@ -1181,7 +1185,7 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
         const int rr = min(wave + i * nw, M - 1);
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
-            load_row_chunk<IN, XT>(src, (int64_t)rr * K, 4 * (int64_t)(FULL ? lane + 64 * j : min(lane + 64 * j, nch - 1)),
+            load_row_chunk<IN, XT>(src, (int64_t)(row0 + rr) * K, 4 * (int64_t)(FULL ? lane + 64 * j : min(lane + 64 * j, nch - 1)),
                                    xv[i][j], unused, unused, GAIN ? ov[j] : unused);
     }
     // 2. the weights of the wave's slices
@@ -1221,7 +1225,7 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
         const int idx = tid + e * (int)blockDim.x;
         const int m = min((idx >> 4) & 15, M - 1);
         const int c = n0 + ((idx >> 8) % CB) * 16 + (idx & 15);
-        pre[e] = PRE ? load_act(pre_src, (int64_t)m * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
+        pre[e] = PRE ? load_act(pre_src, (int64_t)(row0 + m) * p.nc + (c < p.nc ? c : p.nc - 1)) : 0.0f;
     }
     float mu_v[NG];
 #pragma unroll
@@ -1257,7 +1261,7 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
             const float sc = quant_scale(GAIN ? mx : __fmul_rn(mx, rr));
             auto qv = [&](float v) { return (int)code_bits(GAIN ? v : __fmul_rn(v, rr), sc); };
             uint32_t *codes_g = blockIdx.x == 0 && src.codes_out
-                                    ? reinterpret_cast<uint32_t *>(src.codes_out + (int64_t)r * K) : nullptr;
+                                    ? reinterpret_cast<uint32_t *>(src.codes_out + (int64_t)(row0 + r) * K) : nullptr;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = lane + 64 * j;
@@ -1269,7 +1273,7 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
             }
             if (lane == 0) {
                 srow[r] = sc;
-                if (blockIdx.x == 0 && src.scale_out) src.scale_out[r] = sc;
+                if (blockIdx.x == 0 && src.scale_out) src.scale_out[row0 + r] = sc;
             }
         }
     }
@@ -1329,7 +1333,7 @@ __global__ __launch_bounds__(1024) void tgemv_rows_kernel(const ContractArgs p, 
                 v[g] = sum;
                 dq[g] = __builtin_amdgcn_rcpf(srow[r] * sw[g]);
             }
-            epilogue_vals<EPI, NG, true>(p, r, ch, v, dq, pre[e]);
+            epilogue_vals<EPI, NG, true>(p, row0 + r, ch, v, dq, pre[e]);
         }
     }
 }
@@ -1353,6 +1357,19 @@ static hipError_t raise_lds_limit() {
     return e;
 }
 
+// Compute units of the current device (cached per device).
+static int contract_cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <auto KERNEL>
 static hipError_t launch_rows(const ContractArgs &a, const RowSrc &src, float eps, int nslices, dim3 grid, int waves,
                               size_t lds, hipStream_t st) {
@@ -1366,7 +1383,7 @@ template <int NG, int EPI, typename XT, typename RT, int CB, int IN>
 static hipError_t run_row_cb(const ContractArgs &a, const RowSrc &src, float eps, hipStream_t st) {
     const int kw = a.k >> 4;
     const int nslices = (kw + 15) / 16;
-    const dim3 grid((unsigned)((a.nc + 16 * CB - 1) / (16 * CB)));
+    dim3 grid((unsigned)((a.nc + 16 * CB - 1) / (16 * CB)));
     if (a.m == 1) {
         const int waves = nslices < 16 ? nslices : 16;
         const size_t lds = (size_t)waves * CB * NG * 16 * sizeof(int32_t) + (size_t)a.k;
@@ -1379,9 +1396,17 @@ static hipError_t run_row_cb(const ContractArgs &a, const RowSrc &src, float eps
     // 2 to 16 rows of at most 2048, with or without a gain: a wave per row (8
     // chunks of 4 per lane); the gated g_norm runs at one row only
     if constexpr (IN == ROW_X || IN == ROW_GAIN) {
-        const int m = (int)a.m;
+        // more than 8 rows and channel blocks for at most half the CUs: two
+        // workgroups per channel block, 8 rows each, so that each CU quantises
+        // half the rows (every workgroup quantises all of its rows, and that
+        // vector work, not the weights, bounds these kernels; measured on the
+        // 1.3B i/f/g at 16 rows: 31.8 -> 30.5 us per layer; gate_proj, whose
+        // 352 halves would double up on CUs, was slower split: 31.2)
+        const unsigned split = a.m > 8 && 2 * grid.x <= (unsigned)contract_cu_count() ? 2 : 1;
+        const int m = (int)(split == 2 ? 8 : a.m);
         int waves = nslices < 16 ? nslices : 16;
         if (waves < m) waves = m;
+        grid.y = split;
         const size_t lds =
             (size_t)waves * CB * NG * 256 * sizeof(int32_t) + (size_t)16 * (a.k + 16) + 16 * sizeof(float);
         // rows of at most 2048 make at most 8 slices: one per wave
