@@ -911,6 +911,8 @@ ROW_CASES = [
     (12, 2048, 2048, "f32", ("i", "gate", "down")),
     (3, 16, 48, "f32", None),
     (16, 48, 16, "bf16", None),          # 16 rows of three words; down_proj over one word
+    (9, 1024, 2816, "bf16", None),       # i/f/g's rows in two workgroups per channel block: 8 + 1
+    (13, 272, 1040, "f32", None),        # ... 8 + 5, in i/f/g, gate_proj and down_proj, rows not whole chunks
 ]
 
 
